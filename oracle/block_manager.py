@@ -1,0 +1,171 @@
+"""Host block manager of a paged KV cache (test infrastructure; see oracle/__init__).
+
+State, as the pages define it:
+
+* a free list of physical block ids, first-in first-out: allocation takes from
+  the front, release appends to the back ([BT] §05);
+* a reference count per physical block ([KVM] CoW branching; [BT] §08);
+* per sequence, a block table mapping logical block j to a physical block and a
+  length in tokens ([BT] §03, §06).
+
+Operations:
+
+* ``append``: for each new token, j = len // B and r = len % B.  When
+  j == len(table) the previous block is full (r == 0): pop a free block and
+  append it ([BT] §04; [KVM] paged KV allocation, the o = 0 case).  Otherwise the
+  token goes into the existing block T[j]; if that block is shared
+  (ref > 1) it is first replaced by a private copy: pop p_new, record the copy
+  (T[j] -> p_new), drop one reference to the old block and set T[j] = p_new
+  ([KVM] CoW branching; [BT] §08; [INF] §8.3.2).  The slot written is
+  T[j] * B + r.  A batch of appends is all-or-nothing: if the free list runs dry
+  the whole batch is undone and ``MemoryError`` is raised ([BT] §05 raises on an
+  empty free list; [BT] §10 reserves a step's blocks atomically).
+* ``fork``: the child gets a copy of the parent's table, every block in it
+  gains a reference, and the child's length equals the parent's ([KVM] CoW
+  branching, the three constant-time steps).
+* ``release``: every block of the table loses a reference; blocks reaching zero
+  return to the back of the free list in table order ([KVM] host-side
+  reference-counted reclamation; [BT] §05).
+
+Readings where the pages are open: FIFO discipline (the runnable teaching code
+of [BT] §05 is FIFO; [KVM] also says ring buffer or stack/FIFO); within a batch,
+sequences are served in the order given and each sequence's tokens
+consecutively; the copy covers the whole block (the contents beyond the
+sequence's length are never read).
+"""
+
+from __future__ import annotations
+
+import copy
+from collections import deque
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("free_order must be a permutation of the block ids")
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+        self.tables: dict = {}
+        self.lengths: dict = {}
+
+    # -- sequences -------------------------------------------------------
+    def add(self, seq) -> None:
+        if seq in self.tables:
+            raise ValueError(f"sequence {seq} already exists")
+        self.tables[seq] = []
+        self.lengths[seq] = 0
+
+    def fork(self, parent, child) -> None:
+        if parent not in self.tables:
+            raise ValueError(f"unknown parent {parent}")
+        if child in self.tables:
+            raise ValueError(f"sequence {child} already exists")
+        self.tables[child] = list(self.tables[parent])
+        for p in self.tables[child]:
+            self.ref[p] += 1
+        self.lengths[child] = self.lengths[parent]
+
+    def release(self, seq) -> list:
+        """Drop the sequence; return the blocks that went back to the free list."""
+        if seq not in self.tables:
+            raise ValueError(f"unknown sequence {seq}")
+        freed = []
+        for p in self.tables.pop(seq):
+            self.ref[p] -= 1
+            if self.ref[p] == 0:
+                self.free.append(p)
+                freed.append(p)
+        del self.lengths[seq]
+        return freed
+
+    # -- growth ------------------------------------------------------------
+    def _pop_free(self) -> int:
+        if not self.free:
+            raise MemoryError("no free KV block")
+        p = self.free.popleft()
+        self.ref[p] = 1
+        return p
+
+    def _append_one(self, seq, cow_pairs: list) -> int:
+        table = self.tables[seq]
+        length = self.lengths[seq]
+        j, r = divmod(length, self.block_size)
+        if j == len(table):
+            table.append(self._pop_free())
+        elif self.ref[table[j]] > 1:
+            old = table[j]
+            new = self._pop_free()
+            self.ref[old] -= 1
+            table[j] = new
+            cow_pairs.append((old, new))
+        self.lengths[seq] = length + 1
+        return table[j] * self.block_size + r
+
+    def append(self, seq_ids, counts=None):
+        """Append tokens; return (slots, cow_pairs).  All-or-nothing."""
+        seq_ids = list(seq_ids)
+        counts = [1] * len(seq_ids) if counts is None else [int(c) for c in counts]
+        if len(counts) != len(seq_ids):
+            raise ValueError("seq_ids and counts differ in length")
+        for s, c in zip(seq_ids, counts):
+            if s not in self.tables:
+                raise ValueError(f"unknown sequence {s}")
+            if c < 0:
+                raise ValueError("negative token count")
+        saved = (copy.copy(self.free), list(self.ref),
+                 {s: list(t) for s, t in self.tables.items()}, dict(self.lengths))
+        slots, pairs = [], []
+        try:
+            for s, c in zip(seq_ids, counts):
+                for _ in range(c):
+                    slots.append(self._append_one(s, pairs))
+        except MemoryError:
+            self.free, self.ref, self.tables, self.lengths = saved
+            raise
+        return slots, pairs
+
+    # -- queries -------------------------------------------------------------
+    def table(self, seq) -> list:
+        return list(self.tables[seq])
+
+    def length(self, seq) -> int:
+        return self.lengths[seq]
+
+    def n_free(self) -> int:
+        return len(self.free)
+
+    def n_allocated(self) -> int:
+        return sum(1 for r in self.ref if r > 0)
+
+    def n_shared(self) -> int:
+        return sum(1 for r in self.ref if r > 1)
+
+    def check(self) -> None:
+        """Conservation: N_free + N_allocated = N_total and {ref > 0} = allocated ([BT] §13).
+
+        Also: every reference count equals the number of table entries naming
+        the block, no block is both free and referenced, and every table has
+        exactly ceil(len / B) entries.
+        """
+        counted = [0] * self.num_blocks
+        for seq, t in self.tables.items():
+            if len(t) != -(-self.lengths[seq] // self.block_size):
+                raise AssertionError(f"table of {seq} has {len(t)} entries for length {self.lengths[seq]}")
+            for p in t:
+                counted[p] += 1
+        if counted != self.ref:
+            raise AssertionError("reference counts disagree with the tables")
+        free = set(self.free)
+        if len(free) != len(self.free):
+            raise AssertionError("duplicate block in the free list")
+        allocated = {p for p in range(self.num_blocks) if self.ref[p] > 0}
+        if free & allocated:
+            raise AssertionError("a referenced block is on the free list")
+        if len(self.free) + len(allocated) != self.num_blocks:
+            raise AssertionError("N_free + N_allocated != N_total")

@@ -1,0 +1,100 @@
+"""Replay a synthetic workload through the oracle (test infrastructure; see oracle/__init__).
+
+Drives :class:`oracle.block_manager.BlockManager` and :class:`oracle.kv_store.KVStore`
+with the operations of a :class:`synth.workloads.Workload`.  Per append batch the
+block copies requested by copy-on-write are applied first and the new token
+rows written afterwards, which is the order in which the copy must precede the
+divergent write ([KVM] CoW branching; [BT] §08).  Records every batch's slots
+and copy pairs and every decode's block tables and lengths, and evaluates the
+float64 attention of any recorded decode.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from synth import draws
+from synth.draws import TAG_K, TAG_Q, TAG_V
+
+from .attention import decode_attention
+from .block_manager import BlockManager
+from .kv_store import KVStore
+
+
+class OracleReplay:
+    def __init__(self, wl, free_order=None, layers=None, writers=None, background=None):
+        self.wl = wl
+        order = draws.free_order(wl.seed, wl.num_blocks) if free_order is None else free_order
+        self.bm = BlockManager(wl.num_blocks, wl.block_size, order)
+        self.store = KVStore(wl.num_layers, wl.num_blocks, wl.block_size, wl.num_kv_heads,
+                             wl.head_dim, draws.storage_np_dtype(wl.dtype), background, layers)
+        self.layers = list(range(wl.num_layers)) if layers is None else list(layers)
+        self.writers = None if writers is None else set(writers)
+        self.appends = []  # (seq_ids, counts, slots, pairs)
+        self.decodes = []  # {"seq_ids", "tables", "lengths"}
+
+    def run(self, ops=None):
+        for op in (self.wl.ops if ops is None else ops):
+            self.apply(op)
+        return self
+
+    def rows(self, tag, layer, writer, positions):
+        wl = self.wl
+        return draws.token_rows(wl.seed, tag, layer, writer, positions, wl.num_kv_heads,
+                                wl.head_dim, wl.dtype)
+
+    def apply(self, op):
+        kind = op[0]
+        if kind == "add":
+            self.bm.add(op[1])
+        elif kind == "fork":
+            self.bm.fork(op[1], op[2])
+        elif kind == "release":
+            self.bm.release(op[1])
+        elif kind == "append":
+            seq_ids, counts = list(op[1]), list(op[2])
+            running = {}
+            segments = []  # (writer, first position, count)
+            for s, c in zip(seq_ids, counts):
+                start = running.get(s, self.bm.length(s))
+                segments.append((s, start, c))
+                running[s] = start + c
+            slots, pairs = self.bm.append(seq_ids, counts)
+            self.store.copy_blocks(pairs)
+            at = 0
+            for s, start, c in segments:
+                if c and (self.writers is None or s in self.writers):
+                    pos = np.arange(start, start + c)
+                    for layer in self.layers:
+                        self.store.write(layer, slots[at:at + c], self.rows(TAG_K, layer, s, pos),
+                                         self.rows(TAG_V, layer, s, pos))
+                at += c
+            self.appends.append((tuple(seq_ids), tuple(counts), list(slots), list(pairs)))
+        elif kind == "decode":
+            seq_ids = list(op[1])
+            self.decodes.append({
+                "seq_ids": seq_ids,
+                "tables": [self.bm.table(s) for s in seq_ids],
+                "lengths": [self.bm.length(s) for s in seq_ids],
+            })
+        else:
+            raise ValueError(f"unknown op {kind!r}")
+
+    def query_bits(self, decode_index, layer):
+        wl = self.wl
+        n = len(self.decodes[decode_index]["seq_ids"])
+        return draws.normal_bits(wl.seed, TAG_Q, (decode_index, layer),
+                                 (n, wl.num_q_heads, wl.head_dim), wl.dtype)
+
+    def attention(self, decode_index, layer, rows=None, heads=None):
+        """float64 outputs [len(rows), Hq, d] of a recorded decode (rows index its batch)."""
+        wl = self.wl
+        dec = self.decodes[decode_index]
+        rows = range(len(dec["seq_ids"])) if rows is None else rows
+        q = draws.bits_to_f64(self.query_bits(decode_index, layer), wl.dtype)
+        out = []
+        for i in rows:
+            kb, vb = self.store.gather(layer, dec["tables"][i], dec["lengths"][i])
+            out.append(decode_attention(q[i], draws.bits_to_f64(kb, wl.dtype),
+                                        draws.bits_to_f64(vb, wl.dtype)))
+        return np.stack(out)
