@@ -1,0 +1,243 @@
+/*
+ * pagedkv.h -- C ABI of a paged KV cache with single-query decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The library keeps the host-side block manager of a paged KV cache (free
+ * list, per-block reference counts, per-sequence block tables) and launches
+ * HIP kernels that scatter new K/V rows into their slots, copy blocks for
+ * copy-on-write, and compute decode attention by gathering each sequence's
+ * keys and values through its block table.
+ *
+ * Sources, cited by page title:
+ *   [KVM] "KV 缓存管理" (KV cache management chapter of an ML-systems book):
+ *         Eq. 1 (per-token footprint); "Paged KV allocation" and its
+ *         "PagedAttention virtual memory model" (block table T: l -> p,
+ *         l = floor(t/B), o = t mod B, allocation when o = 0, M_block);
+ *         "Zero-copy branching via copy-on-write" (fork, refcounts, CoW,
+ *         reclamation); "Chunked prefill mechanism" (running-max merge).
+ *   [BT]  "KV Cache 还有空间为何新请求却进不来？PagedAttention 的块表与碎片控制"
+ *         (block tables and fragmentation): §03 translation, §04 growth,
+ *         §05 block manager, §06 tensor shapes, §07 decode equation, §08 CoW,
+ *         §10 atomic reservation, §13 conservation.
+ *   [INF] "第 8 章 推理优化" (inference optimisation): §8.3.2 release only
+ *         when no reference remains and no submitted device work reads it.
+ *
+ * Conventions for every call:
+ *   - Status codes; on failure kv_last_error() returns a message (thread
+ *     local) and no state has changed unless the call says otherwise.
+ *   - The library owns host metadata only.  Every device pointer (pools, q,
+ *     out, tables, slot mappings, workspace) is caller-owned device memory.
+ *   - Device operations are enqueued on the given HIP stream (a hipStream_t
+ *     passed as void*; NULL is the default stream) and never synchronise.
+ *   - A pool is not thread safe: use it from one host thread at a time.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KV_OK = 0,
+  KV_ERR_OOM = 1,         /* the free list cannot cover the request ([BT] §05) */
+  KV_ERR_INVALID = 2,     /* bad argument, unknown or duplicate sequence */
+  KV_ERR_STATE = 3,       /* internal invariant violated (kv_pool_check) */
+  KV_ERR_HIP = 4,         /* a HIP runtime call failed; the message names it */
+  KV_ERR_UNSUPPORTED = 5  /* valid but not implemented shape / dtype / kernel */
+} kv_status;
+
+typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
+
+typedef struct {
+  int32_t num_layers;   /* L */
+  int32_t num_blocks;   /* N physical blocks in the pool */
+  int32_t block_size;   /* B tokens per block */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* d; a multiple of 32, at most 256 */
+  int32_t dtype;        /* kv_dtype of K, V, q and out */
+} kv_pool_config;
+
+typedef struct kv_pool kv_pool; /* opaque */
+
+typedef struct {
+  int32_t n_free;      /* blocks on the free list */
+  int32_t n_allocated; /* blocks with reference count > 0 */
+  int32_t n_shared;    /* blocks with reference count > 1 */
+  int32_t n_pending;   /* released blocks waiting for device work to finish */
+  int32_t n_seqs;      /* live sequences */
+  int64_t n_tokens;    /* sum of live sequence lengths */
+  int64_t n_table_refs;/* sum of live block-table lengths */
+} kv_pool_stats_t;
+
+/* ------------------------------------------------------------------------
+ * Pool memory layout (the pages leave the stride open, [BT] §06).
+ *
+ * K and V are two separate caller-owned buffers, each holding, for every
+ * (layer l, physical block p, KV head g), one contiguous tile of B*d
+ * elements:
+ *     tile(l, p, g) = ((l * N + p) * Hkv + g) * B * d          (elements)
+ * Inside a tile, the element of slot r (0 <= r < B) and dimension e
+ * (0 <= e < d) sits at
+ *     K: tile + ((e / X) * B + r) * X + e % X,     X = 16 / sizeof(element)
+ *     V: tile + ((((e / 32) * (B / Q) + r / Q) * 16 + e % 16) * 2
+ *                + (e % 32) / 16) * Q + r % Q,      Q = gcd(B, 4)
+ * so that one 16-byte load brings X dimensions of one key, or 4 slots of
+ * two value dimensions 16 apart; these are the operand orders of the
+ * gfx950 bf16 matrix instructions used by the decode kernel.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes the caller must allocate for the K and the V buffer. */
+kv_status kv_pool_required_bytes(const kv_pool_config* cfg, uint64_t* k_bytes, uint64_t* v_bytes);
+
+/* Create the host block manager over caller-owned device buffers k_cache and
+ * v_cache (each kv_pool_required_bytes large, 256-byte aligned).  The free
+ * list starts as initial_free_order (a permutation of 0..N-1; NULL means
+ * 0, 1, ..., N-1) and is first-in first-out ([BT] §05).  All reference counts
+ * start at zero.  The buffers are not touched and never freed by the library. */
+kv_status kv_pool_create(const kv_pool_config* cfg, void* k_cache, void* v_cache,
+                         const int32_t* initial_free_order, kv_pool** out);
+
+/* Destroy the host state (and any pending release events). */
+void kv_pool_destroy(kv_pool* pool);
+
+/* Register an empty sequence.  KV_ERR_INVALID if seq_id exists. */
+kv_status kv_seq_add(kv_pool* pool, int64_t seq_id);
+
+/* Fork: child gets a copy of parent's block table, each of those blocks gains
+ * one reference, child's length = parent's; no device work ([KVM] copy-on-write
+ * branching, the table copy / refcount increment / registration steps). */
+kv_status kv_seq_fork(kv_pool* pool, int64_t parent, int64_t child);
+
+/* Append n_new[i] tokens to seq_ids[i] for i < n, sequence-major in the given
+ * order, as one all-or-nothing batch ([BT] §10).  For each token, with
+ * j = len / B and r = len % B ([BT] §03-§04):
+ *   - j == table length: pop the front of the free list, append it (ref = 1);
+ *   - else if ref[T[j]] > 1 (shared): pop p_new, emit the pair (T[j], p_new)
+ *     into cow_pairs_out, drop one reference of T[j], set T[j] = p_new
+ *     ([KVM] copy-on-write; [BT] §08);
+ *   - write slot T[j] * B + r into slot_mapping_out; len += 1.
+ * Outputs (host memory): slot_mapping_out[sum n_new] (capacity slot_capacity),
+ * cow_pairs_out[n_cow][2] as (src, dst) (capacity cow_capacity pairs; n pairs
+ * always suffice), *n_cow_out.  The caller must enqueue copy_blocks(pairs)
+ * before reshape_and_cache on the same stream.  KV_ERR_OOM when the free list
+ * runs dry: the whole batch is undone and no state changes.  Released blocks
+ * whose device work has completed are returned to the free list first. */
+kv_status kv_append_slots(kv_pool* pool, int32_t n, const int64_t* seq_ids, const int32_t* n_new,
+                          int64_t* slot_mapping_out, int64_t slot_capacity,
+                          int64_t* cow_pairs_out, int32_t cow_capacity, int32_t* n_cow_out);
+
+/* Host copy of the block tables and lengths of n sequences:
+ * tables_out[n][max_blocks] (row i, entries past ceil(len/B) set to -1) and
+ * context_lens_out[n].  KV_ERR_INVALID if a table is longer than max_blocks. */
+kv_status kv_get_block_tables(const kv_pool* pool, int32_t n, const int64_t* seq_ids,
+                              int32_t max_blocks, int32_t* tables_out, int32_t* context_lens_out);
+
+/* Length in tokens and block-table length of one sequence. */
+kv_status kv_seq_info(const kv_pool* pool, int64_t seq_id, int32_t* length, int32_t* num_blocks);
+
+/* Release a sequence: each block of its table loses a reference.  Blocks that
+ * reach zero return to the back of the free list, in table order, only after
+ * all work enqueued so far on hip_stream has completed ([KVM] reclamation;
+ * [INF] §8.3.2): an event is recorded on the stream and polled at the next
+ * append or kv_pool_reclaim. */
+kv_status kv_seq_release(kv_pool* pool, int64_t seq_id, void* hip_stream);
+
+/* As kv_seq_release, with a caller-managed fence instead of a HIP event: the
+ * freed blocks wait until kv_pool_retire(pool, f) is called with f >= fence.
+ * fence == 0 returns them at once. */
+kv_status kv_seq_release_fenced(kv_pool* pool, int64_t seq_id, uint64_t fence);
+
+/* Declare every fence <= completed_fence done, then reclaim. */
+kv_status kv_pool_retire(kv_pool* pool, uint64_t completed_fence);
+
+/* Return released blocks whose events completed (wait != 0: wait for all
+ * pending events first).  Ready groups go back in release order. */
+kv_status kv_pool_reclaim(kv_pool* pool, int32_t wait);
+
+kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
+
+/* Free list in pop order (out capacity cap; *n_out = its length). */
+kv_status kv_pool_free_list(const kv_pool* pool, int32_t cap, int32_t* out, int32_t* n_out);
+
+/* Reference counts of all N blocks (out[N]). */
+kv_status kv_pool_refcounts(const kv_pool* pool, int32_t* out);
+
+/* Conservation ([BT] §13): N_free + N_allocated + N_pending = N_total, the set
+ * of blocks with ref > 0 is exactly the set named by tables, each count equals
+ * the number of table entries naming the block, and every table has
+ * ceil(len / B) entries.  KV_ERR_STATE names the first violation. */
+kv_status kv_pool_check(const kv_pool* pool);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* kv_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Device operations
+ * ---------------------------------------------------------------------- */
+
+/* Scatter new key/value rows into the pool of one layer ([KVM] paged KV
+ * allocation: the token's K and V go to T[l] at offset o; [BT] §11: decode
+ * appends one KV slot per sequence).  k_new, v_new: device [n_tokens][Hkv][d]
+ * in the pool dtype; d_slot_mapping: device int64[n_tokens], slot = p * B + r.
+ * Slots < 0 or >= N * B are skipped.  Bitwise copy. */
+kv_status reshape_and_cache(kv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                            const int64_t* d_slot_mapping, int32_t n_tokens, void* hip_stream);
+
+/* Copy-on-write block copies ([KVM] CoW: the shared block's B tokens are copied
+ * to p_new): for each pair (src, dst) of device int64[n_pairs][2], in every
+ * layer, K and V tiles of dst become bitwise copies of src.  Pairs naming a
+ * block outside [0, N) are skipped; the dst blocks must be distinct and no dst
+ * may be a src of the same call. */
+kv_status copy_blocks(kv_pool* pool, const int64_t* d_pairs, int32_t n_pairs, void* hip_stream);
+
+typedef enum {
+  KV_KERNEL_AUTO = 0,    /* the matrix-core kernel where it applies, else generic */
+  KV_KERNEL_GENERIC = 1, /* vector-ALU kernel: any dtype, B, d, G <= 16 */
+  KV_KERNEL_MFMA = 2     /* bf16, B = 16, d in {64, 128, 256}, G <= 16 */
+} kv_kernel;
+
+typedef struct {
+  float scale;              /* softmax scale; 0 means 1/sqrt(d) ([BT] §07) */
+  int32_t partition_tokens; /* split-K partition length in tokens; 0 = let the
+                               library choose; else a positive multiple of B */
+  int32_t kernel;           /* kv_kernel */
+} kv_attention_options;
+
+/* Device workspace needed by paged_attention_decode for these arguments. */
+uint64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int32_t num_q_heads,
+                                         int32_t max_blocks_per_seq,
+                                         const kv_attention_options* opts);
+
+/* Decode attention over the paged cache of one layer ([BT] §07): for sequence
+ * s with n = context_lens[s] cached tokens (the query's own token included)
+ * and query head h reading KV head g = h / (Hq / Hkv),
+ *     k_t = K[l][T_s[t / B]][g][t % B],  v_t likewise,   t = 0 .. n-1,
+ *     out[s][h] = sum_t softmax_t(scale * q[s][h] . k_t) v_t.
+ * The context is split into partitions of partition_tokens tokens; each
+ * partition yields its running max m, sum l and unnormalised output, and a
+ * merge kernel folds them with the recurrences of [KVM] (chunked prefill
+ * mechanism) when there is more than one.
+ *   q, out:          device [n_seqs][Hq][d], pool dtype (out rounded to
+ *                    nearest even for bf16); accumulation is fp32.
+ *   d_block_tables:  device int32[n_seqs][max_blocks_per_seq].
+ *   d_context_lens:  device int32[n_seqs]; values are clamped to
+ *                    max_blocks_per_seq * B; n <= 0 yields a zero row.
+ *   d_workspace:     caller-owned device memory of at least
+ *                    paged_attention_workspace_bytes (may be NULL if that is 0).
+ * A table entry outside [0, N) is never dereferenced: the rows of that
+ * sequence are written as NaN.  opts may be NULL (all defaults). */
+kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, void* out,
+                                 const int32_t* d_block_tables, const int32_t* d_context_lens,
+                                 int32_t n_seqs, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                                 const kv_attention_options* opts, void* d_workspace,
+                                 uint64_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,274 @@
+"""ctypes binding of libpagedkv.so (include/pagedkv.h).
+
+Argument marshalling only: every function has the C name, converts torch
+tensors to device pointers (and the current HIP stream when none is given),
+numpy arrays to host pointers, and turns a non-OK status into an exception
+carrying kv_last_error().  All computation happens in the library.  Loading
+fails loudly when the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from .build import LIB_PATH
+
+KV_OK, KV_ERR_OOM, KV_ERR_INVALID, KV_ERR_STATE, KV_ERR_HIP, KV_ERR_UNSUPPORTED = range(6)
+KV_F32, KV_BF16 = 0, 1
+KV_KERNEL_AUTO, KV_KERNEL_GENERIC, KV_KERNEL_MFMA = 0, 1, 2
+
+
+class KVError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+class KVOutOfBlocks(KVError, MemoryError):
+    pass
+
+
+class kv_pool_config(C.Structure):
+    _fields_ = [("num_layers", C.c_int32), ("num_blocks", C.c_int32), ("block_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32)]
+
+
+class kv_pool_stats_t(C.Structure):
+    _fields_ = [("n_free", C.c_int32), ("n_allocated", C.c_int32), ("n_shared", C.c_int32),
+                ("n_pending", C.c_int32), ("n_seqs", C.c_int32), ("n_tokens", C.c_int64),
+                ("n_table_refs", C.c_int64)]
+
+
+class kv_attention_options(C.Structure):
+    _fields_ = [("scale", C.c_float), ("partition_tokens", C.c_int32), ("kernel", C.c_int32)]
+
+
+_P = C.c_void_p
+_I32 = C.c_int32
+_I64 = C.c_int64
+_U64 = C.c_uint64
+
+# name -> (restype, argtypes); the exported surface of include/pagedkv.h
+SIGNATURES = {
+    "kv_pool_required_bytes": (_I32, [C.POINTER(kv_pool_config), C.POINTER(_U64), C.POINTER(_U64)]),
+    "kv_pool_create": (_I32, [C.POINTER(kv_pool_config), _P, _P, _P, C.POINTER(_P)]),
+    "kv_pool_destroy": (None, [_P]),
+    "kv_seq_add": (_I32, [_P, _I64]),
+    "kv_seq_fork": (_I32, [_P, _I64, _I64]),
+    "kv_append_slots": (_I32, [_P, _I32, _P, _P, _P, _I64, _P, _I32, C.POINTER(_I32)]),
+    "kv_get_block_tables": (_I32, [_P, _I32, _P, _I32, _P, _P]),
+    "kv_seq_info": (_I32, [_P, _I64, C.POINTER(_I32), C.POINTER(_I32)]),
+    "kv_seq_release": (_I32, [_P, _I64, _P]),
+    "kv_seq_release_fenced": (_I32, [_P, _I64, _U64]),
+    "kv_pool_retire": (_I32, [_P, _U64]),
+    "kv_pool_reclaim": (_I32, [_P, _I32]),
+    "kv_pool_stats": (_I32, [_P, C.POINTER(kv_pool_stats_t)]),
+    "kv_pool_free_list": (_I32, [_P, _I32, _P, C.POINTER(_I32)]),
+    "kv_pool_refcounts": (_I32, [_P, _P]),
+    "kv_pool_check": (_I32, [_P]),
+    "kv_last_error": (C.c_char_p, []),
+    "reshape_and_cache": (_I32, [_P, _I32, _P, _P, _P, _I32, _P]),
+    "copy_blocks": (_I32, [_P, _P, _I32, _P]),
+    "paged_attention_workspace_bytes": (_U64, [_P, _I32, _I32, _I32, C.POINTER(kv_attention_options)]),
+    "paged_attention_decode": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _I32,
+                                      C.POINTER(kv_attention_options), _P, _U64, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m pagedattention_decode_amd.build`")
+        handle = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != KV_OK:
+        msg = lib().kv_last_error().decode(errors="replace")
+        if status == KV_ERR_OOM:
+            raise KVOutOfBlocks(status, msg)
+        raise KVError(status, msg)
+
+
+def _host(arr, dtype):
+    a = np.ascontiguousarray(arr, dtype=dtype)
+    return a, a.ctypes.data_as(C.c_void_p)
+
+
+def _dev(t):
+    """Device pointer of a contiguous torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("device tensors must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+# -- pool -------------------------------------------------------------------
+
+def make_config(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype):
+    return kv_pool_config(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype)
+
+
+def kv_pool_required_bytes(cfg):
+    kb, vb = _U64(), _U64()
+    _check(lib().kv_pool_required_bytes(C.byref(cfg), C.byref(kb), C.byref(vb)))
+    return kb.value, vb.value
+
+
+def kv_pool_create(cfg, k_cache, v_cache, initial_free_order=None):
+    """k_cache / v_cache: torch tensors (device) or raw integer addresses."""
+    order = None
+    ptr = None
+    if initial_free_order is not None:
+        order, ptr = _host(initial_free_order, np.int32)
+    out = _P()
+    kp = k_cache if isinstance(k_cache, int) or k_cache is None else k_cache.data_ptr()
+    vp = v_cache if isinstance(v_cache, int) or v_cache is None else v_cache.data_ptr()
+    _check(lib().kv_pool_create(C.byref(cfg), kp, vp, ptr, C.byref(out)))
+    del order
+    return out
+
+
+def kv_pool_destroy(pool):
+    lib().kv_pool_destroy(pool)
+
+
+def kv_seq_add(pool, seq_id):
+    _check(lib().kv_seq_add(pool, int(seq_id)))
+
+
+def kv_seq_fork(pool, parent, child):
+    _check(lib().kv_seq_fork(pool, int(parent), int(child)))
+
+
+def kv_append_slots(pool, seq_ids, n_new=None):
+    """Returns (slot_mapping int64[sum n_new], cow_pairs int64[k, 2])."""
+    seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    n = seq_ids.size
+    n_new = np.ones(n, np.int32) if n_new is None else np.ascontiguousarray(n_new, dtype=np.int32)
+    total = int(n_new.sum(dtype=np.int64))
+    slots = np.empty(max(total, 1), np.int64)
+    pairs = np.empty((max(n, 1), 2), np.int64)
+    n_cow = _I32()
+    _check(lib().kv_append_slots(pool, n, seq_ids.ctypes.data_as(_P), n_new.ctypes.data_as(_P),
+                                 slots.ctypes.data_as(_P), total, pairs.ctypes.data_as(_P),
+                                 max(n, 1), C.byref(n_cow)))
+    return slots[:total], pairs[:n_cow.value].copy()
+
+
+def kv_get_block_tables(pool, seq_ids, max_blocks):
+    seq_ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    n = seq_ids.size
+    tables = np.empty((n, max_blocks), np.int32)
+    lens = np.empty(n, np.int32)
+    _check(lib().kv_get_block_tables(pool, n, seq_ids.ctypes.data_as(_P), max_blocks,
+                                     tables.ctypes.data_as(_P), lens.ctypes.data_as(_P)))
+    return tables, lens
+
+
+def kv_seq_info(pool, seq_id):
+    length, nb = _I32(), _I32()
+    _check(lib().kv_seq_info(pool, int(seq_id), C.byref(length), C.byref(nb)))
+    return length.value, nb.value
+
+
+def kv_seq_release(pool, seq_id, stream=None):
+    _check(lib().kv_seq_release(pool, int(seq_id), _stream(stream)))
+
+
+def kv_seq_release_fenced(pool, seq_id, fence):
+    _check(lib().kv_seq_release_fenced(pool, int(seq_id), int(fence)))
+
+
+def kv_pool_retire(pool, completed_fence):
+    _check(lib().kv_pool_retire(pool, int(completed_fence)))
+
+
+def kv_pool_reclaim(pool, wait=False):
+    _check(lib().kv_pool_reclaim(pool, 1 if wait else 0))
+
+
+def kv_pool_stats(pool):
+    s = kv_pool_stats_t()
+    _check(lib().kv_pool_stats(pool, C.byref(s)))
+    return {f: getattr(s, f) for f, _ in kv_pool_stats_t._fields_}
+
+
+def kv_pool_free_list(pool, num_blocks):
+    out = np.empty(max(num_blocks, 1), np.int32)
+    n = _I32()
+    _check(lib().kv_pool_free_list(pool, num_blocks, out.ctypes.data_as(_P), C.byref(n)))
+    return out[:n.value].copy()
+
+
+def kv_pool_refcounts(pool, num_blocks):
+    out = np.empty(num_blocks, np.int32)
+    _check(lib().kv_pool_refcounts(pool, out.ctypes.data_as(_P)))
+    return out
+
+
+def kv_pool_check(pool):
+    _check(lib().kv_pool_check(pool))
+
+
+def kv_last_error():
+    return lib().kv_last_error().decode(errors="replace")
+
+
+# -- device operations ----------------------------------------------------
+
+def reshape_and_cache(pool, layer, k_new, v_new, slot_mapping, stream=None):
+    """k_new, v_new: device [n, Hkv, d]; slot_mapping: device int64 [n]."""
+    n = int(slot_mapping.numel())
+    _check(lib().reshape_and_cache(pool, int(layer), _dev(k_new), _dev(v_new), _dev(slot_mapping), n,
+                                   _stream(stream)))
+
+
+def copy_blocks(pool, pairs, stream=None):
+    """pairs: device int64 [k, 2] of (src, dst)."""
+    n = int(pairs.shape[0]) if pairs is not None else 0
+    _check(lib().copy_blocks(pool, _dev(pairs) if n else None, n, _stream(stream)))
+
+
+def attention_options(scale=0.0, partition_tokens=0, kernel=KV_KERNEL_AUTO):
+    return kv_attention_options(float(scale), int(partition_tokens), int(kernel))
+
+
+def paged_attention_workspace_bytes(pool, n_seqs, num_q_heads, max_blocks_per_seq, opts=None):
+    return int(lib().paged_attention_workspace_bytes(pool, int(n_seqs), int(num_q_heads), int(max_blocks_per_seq),
+                                                     C.byref(opts) if opts is not None else None))
+
+
+def paged_attention_decode(pool, layer, q, out, block_tables, context_lens, num_q_heads, opts=None,
+                           workspace=None, stream=None):
+    """q, out: device [n, Hq, d]; block_tables: device int32 [n, max_blocks]; context_lens int32 [n]."""
+    n_seqs, max_blocks = int(block_tables.shape[0]), int(block_tables.shape[1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attention_decode(pool, int(layer), _dev(q), _dev(out), _dev(block_tables),
+                                        _dev(context_lens), n_seqs, max_blocks, int(num_q_heads),
+                                        C.byref(opts) if opts is not None else None, _dev(workspace),
+                                        ws_bytes, _stream(stream)))

@@ -1,0 +1,857 @@
+// Device side of the paged KV cache for gfx950 (MI355X): slot scatter, block
+// copy, decode attention over block tables (split-K partitions) and the
+// log-sum-exp merge.
+//
+// Sources (by page title):
+//   [BT]  "PagedAttention 的块表与碎片控制": §03 j = t / B, r = t mod B,
+//         p = block_table[j]; §06 caches [layers, blocks, B, Hkv, d] as the
+//         readable form (the stride is left to the kernel); §07 decode
+//         equation s_t = q . k_t / sqrt(d), o = sum softmax(s)_t v_t, combined
+//         blockwise with an online softmax.
+//   [KVM] "KV 缓存管理": paged KV allocation (K/V of a new token written to
+//         T[l] at offset o; the decode kernel takes the block table as an extra
+//         input and walks logical blocks 0 .. floor((S-1)/B)); copy-on-write
+//         (copy the B tokens of the shared block); chunked prefill mechanism
+//         (running max m, sum l and output O folded across blocks).
+//
+// Pool layout: see include/pagedkv.h.  Per (layer, block, kv head) one tile of
+// B*d elements; K tile = [d/X][B][X] (X = 16 bytes of elements), V tile =
+// [d/32][B/Q][16][2][Q] (Q = gcd(B, 4)).  For bf16, B = 16 these are exactly the
+// register operand orders of v_mfma_f32_16x16x32_bf16 (K, as the A operand of
+// S^T = K Q^T) and v_mfma_f32_16x16x16_bf16 (V, as the A operand of
+// O^T = V^T P^T), so every K/V byte is fetched by one 16-byte load per lane and
+// every wave-wide load instruction reads 1 KiB of contiguous memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "pool_internal.h"
+
+namespace pagedkv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// element helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// Round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct elem;
+template <> struct elem<float> {
+  __device__ static float to_f32(float x) { return x; }
+  __device__ static float from_f32(float x) { return x; }
+};
+template <> struct elem<uint16_t> {
+  __device__ static float to_f32(uint16_t x) { return bf16_to_f32(x); }
+  __device__ static uint16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// Element offset of (slot r, dim e) inside a K tile.
+__device__ __forceinline__ int k_offset(int r, int e, int B, int X) { return ((e / X) * B + r) * X + (e % X); }
+
+// Element offset of (slot r, dim e) inside a V tile.
+__device__ __forceinline__ int v_offset(int r, int e, int B, int Q) {
+  return ((((e >> 5) * (B / Q) + r / Q) * 16 + (e & 15)) * 2 + ((e & 31) >> 4)) * Q + r % Q;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// reshape_and_cache: one thread per 16-byte chunk of a new K row; the same
+// thread scatters the matching V elements.
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__global__ void __launch_bounds__(256) reshape_and_cache_kernel(
+    const T* __restrict__ k_new, const T* __restrict__ v_new, const int64_t* __restrict__ slots,
+    T* __restrict__ k_layer, T* __restrict__ v_layer, int64_t n_items, int n_kv_heads, int head_dim,
+    int block_size, int64_t n_slots) {
+  constexpr int X = 16 / sizeof(T);
+  const int Q = (block_size % 4 == 0) ? 4 : ((block_size % 2 == 0) ? 2 : 1);
+  const int chunks_per_head = head_dim / X;
+  const int64_t chunks_per_token = static_cast<int64_t>(n_kv_heads) * chunks_per_head;
+  for (int64_t item = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; item < n_items;
+       item += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t tok = item / chunks_per_token;
+    const int rem = static_cast<int>(item % chunks_per_token);
+    const int g = rem / chunks_per_head;
+    const int c = rem % chunks_per_head;
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= n_slots) continue;
+    const int64_t blk = slot / block_size;
+    const int r = static_cast<int>(slot % block_size);
+    const int64_t tile = (blk * n_kv_heads + g) * static_cast<int64_t>(block_size) * head_dim;
+    const int64_t src = (tok * n_kv_heads + g) * head_dim + static_cast<int64_t>(c) * X;
+    // K: one 16-byte chunk, contiguous in the tile
+    const uint4 kv = *reinterpret_cast<const uint4*>(k_new + src);
+    *reinterpret_cast<uint4*>(k_layer + tile + k_offset(r, c * X, block_size, X)) = kv;
+    // V: X elements, each to its own place
+    const uint4 vv = *reinterpret_cast<const uint4*>(v_new + src);
+    const T* ve = reinterpret_cast<const T*>(&vv);
+#pragma unroll
+    for (int x = 0; x < X; ++x) v_layer[tile + v_offset(r, c * X + x, block_size, Q)] = ve[x];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// copy_blocks: one workgroup per (pair, layer, K or V); copies the Hkv tiles of
+// that block, which are contiguous.
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) copy_blocks_kernel(uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                                          const int64_t* __restrict__ pairs, int num_layers,
+                                                          int num_blocks, int64_t block_vec16) {
+  const int pair = blockIdx.x / (num_layers * 2);
+  const int rem = blockIdx.x % (num_layers * 2);
+  const int layer = rem >> 1;
+  uint4* base = (rem & 1) ? v_pool : k_pool;
+  const int64_t src = pairs[2 * pair];
+  const int64_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const uint4* s = base + (static_cast<int64_t>(layer) * num_blocks + src) * block_vec16;
+  uint4* d = base + (static_cast<int64_t>(layer) * num_blocks + dst) * block_vec16;
+  for (int64_t i = threadIdx.x; i < block_vec16; i += blockDim.x) d[i] = s[i];
+}
+
+// ---------------------------------------------------------------------------
+// Shared by both attention kernels: the work item of a workgroup and the
+// per-partition output (final row when the sequence has one partition, else
+// the partial (m, l, o) of the running-max recurrences, with m in base-2
+// units because scores are pre-multiplied by log2(e)).
+// ---------------------------------------------------------------------------
+
+struct attn_args {
+  const void* q;
+  void* out;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  const void* k_layer;
+  const void* v_layer;
+  float* part_m;  // [n_seqs][Hq][max_parts]
+  float* part_l;  // [n_seqs][Hq][max_parts]
+  float* part_o;  // [n_seqs][Hq][max_parts][d]
+  int n_seqs, max_blocks, n_q_heads, n_kv_heads, head_dim, block_size, num_blocks;
+  int partition_tokens, max_parts;
+  float scale_log2;  // scale * log2(e)
+};
+
+struct work_item {
+  int seq, kv_head, part, n, n_parts, tok_begin, tok_end;
+};
+
+__device__ __forceinline__ bool decode_work(const attn_args& a, work_item& w) {
+  // Workgroups are numbered (part, kv head, seq) with seq fastest, so the
+  // workgroups running together read the same partition index of different
+  // sequences (sequences sharing a prefix then read the same blocks together).
+  int id = blockIdx.x;
+  w.seq = id % a.n_seqs;
+  id /= a.n_seqs;
+  w.kv_head = id % a.n_kv_heads;
+  w.part = id / a.n_kv_heads;
+  int n = a.ctx_lens[w.seq];
+  const int cap = a.max_blocks * a.block_size;
+  w.n = n > cap ? cap : n;
+  w.n_parts = w.n <= 0 ? 1 : (w.n + a.partition_tokens - 1) / a.partition_tokens;
+  if (w.part >= w.n_parts) return false;
+  w.tok_begin = w.part * a.partition_tokens;
+  w.tok_end = min(w.n, w.tok_begin + a.partition_tokens);
+  return true;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_result(const attn_args& a, const work_item& w, int h_local, int e, float m,
+                                             float l, float o, bool poisoned) {
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int h = w.kv_head * G + h_local;
+  if (w.n_parts == 1) {
+    float val = (w.n <= 0) ? 0.f : o / l;
+    if (poisoned) val = __builtin_nanf("");
+    T* out = static_cast<T*>(a.out);
+    out[(static_cast<int64_t>(w.seq) * a.n_q_heads + h) * a.head_dim + e] = elem<T>::from_f32(val);
+  } else {
+    const int64_t ph = (static_cast<int64_t>(w.seq) * a.n_q_heads + h) * a.max_parts + w.part;
+    if (poisoned) {
+      m = l = o = __builtin_nanf("");
+    }
+    if (e == 0) {
+      a.part_m[ph] = m;
+      a.part_l[ph] = l;
+    }
+    a.part_o[ph * a.head_dim + e] = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic decode attention (vector ALU).  Any dtype, block size, head_dim
+// (multiple of 32, <= 256) and group G <= 16.  A workgroup of 4 waves handles
+// one (sequence, kv head, partition); each wave takes 64 tokens at a time, one
+// token per lane for the scores (q in LDS), then one dimension per lane for
+// the weighted sum of values.
+// ---------------------------------------------------------------------------
+
+constexpr int kGenericWaves = 4;
+constexpr int kMaxGroup = 16;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
+  constexpr int X = 16 / sizeof(T);
+  constexpr int DPL = (D + 63) / 64;  // dims per lane in the PV phase
+  __shared__ float q_s[kMaxGroup][D];  // scaled queries; reused for the merged output
+  __shared__ float p_s[kGenericWaves][kMaxGroup][64];
+  __shared__ int64_t base_s[kGenericWaves][64];
+  __shared__ int r_s[kGenericWaves][64];
+  __shared__ float m_s[kGenericWaves][kMaxGroup], l_s[kGenericWaves][kMaxGroup];
+  __shared__ int poison_s;
+
+  work_item w;
+  if (!decode_work(a, w)) return;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int B = a.block_size;
+  const int Q = (B % 4 == 0) ? 4 : ((B % 2 == 0) ? 2 : 1);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const T* qg = static_cast<const T*>(a.q) + (static_cast<int64_t>(w.seq) * a.n_q_heads + w.kv_head * G) * D;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) q_s[i / D][i % D] = elem<T>::to_f32(qg[i]) * a.scale_log2;
+  if (threadIdx.x == 0) poison_s = 0;
+  __syncthreads();
+
+  const T* kl = static_cast<const T*>(a.k_layer);
+  const T* vl = static_cast<const T*>(a.v_layer);
+  const int32_t* table = a.tables + static_cast<int64_t>(w.seq) * a.max_blocks;
+  const int64_t tile_elems = static_cast<int64_t>(B) * D;
+
+  float m_run[kMaxGroup], l_lane[kMaxGroup], acc[kMaxGroup][DPL];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    m_run[h] = -INFINITY;
+    l_lane[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[h][k] = 0.f;
+  }
+  bool poisoned = false;
+
+  const int span = w.tok_end - w.tok_begin;
+  const int rounds = (span + 64 * kGenericWaves - 1) / (64 * kGenericWaves);
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int t0 = w.tok_begin + (rd * kGenericWaves + wave) * 64;
+    const int t = t0 + lane;
+    bool valid = t < w.tok_end;
+    int64_t base = 0;
+    int r = 0;
+    if (valid) {
+      const int p = table[t / B];
+      r = t % B;
+      if (p < 0 || p >= a.num_blocks) {
+        valid = false;
+        poisoned = true;
+      } else {
+        base = (static_cast<int64_t>(p) * a.n_kv_heads + w.kv_head) * tile_elems;
+      }
+    }
+    float s[kMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) s[h] = 0.f;
+    if (valid) {
+      for (int c = 0; c < D / X; ++c) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(kl + base + k_offset(r, c * X, B, X));
+        const T* ke = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+        for (int x = 0; x < X; ++x) {
+          const float kx = elem<T>::to_f32(ke[x]);
+#pragma unroll
+          for (int h = 0; h < kMaxGroup; ++h)
+            if (h < G) s[h] += q_s[h][c * X + x] * kx;
+        }
+      }
+    }
+    base_s[wave][lane] = base;
+    r_s[wave][lane] = valid ? r : -1;
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h >= G) continue;
+      const float sv = valid ? s[h] : -INFINITY;
+      const float mc = wave_max(sv);
+      const float m_new = fmaxf(m_run[h], mc);
+      float alpha = 1.f, pv = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = exp2f(m_run[h] - m_new);
+        pv = valid ? exp2f(sv - m_new) : 0.f;
+      }
+      m_run[h] = m_new;
+      l_lane[h] = l_lane[h] * alpha + pv;
+      p_s[wave][h][lane] = pv;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) acc[h][k] *= alpha;
+    }
+    __syncthreads();
+    const int nvalid = min(64, max(0, w.tok_end - t0));
+    for (int i = 0; i < nvalid; ++i) {
+      const int ri = r_s[wave][i];
+      if (ri < 0) continue;
+      const int64_t bi = base_s[wave][i];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int e = lane + 64 * k;
+        if (e < D) {
+          const float vx = elem<T>::to_f32(vl[bi + v_offset(ri, e, B, Q)]);
+#pragma unroll
+          for (int h = 0; h < kMaxGroup; ++h)
+            if (h < G) acc[h][k] += p_s[wave][h][i] * vx;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // merge the waves of the workgroup: common maximum per head, then every
+  // wave adds its rescaled partial output into q_s (no longer needed)
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h >= G) continue;
+    const float lw = wave_sum(l_lane[h]);
+    if (lane == 0) {
+      m_s[wave][h] = m_run[h];
+      l_s[wave][h] = lw;
+    }
+  }
+  if (poisoned) atomicOr(&poison_s, 1);
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) q_s[i / D][i % D] = 0.f;
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h >= G) continue;
+    float M = -INFINITY;
+    for (int v = 0; v < kGenericWaves; ++v) M = fmaxf(M, m_s[v][h]);
+    const float f = (M == -INFINITY) ? 0.f : exp2f(m_run[h] - M);
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      const int e = lane + 64 * k;
+      if (e < D) atomicAdd(&q_s[h][e], acc[h][k] * f);
+    }
+  }
+  __syncthreads();
+  const bool any_poison = poison_s != 0;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int h = i / D, e = i % D;
+    float M = -INFINITY;
+    for (int v = 0; v < kGenericWaves; ++v) M = fmaxf(M, m_s[v][h]);
+    float L = 0.f;
+    if (M != -INFINITY)
+      for (int v = 0; v < kGenericWaves; ++v) L += exp2f(m_s[v][h] - M) * l_s[v][h];
+    store_result<T>(a, w, h, e, M, L, q_s[h][e], any_poison);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core decode attention: bf16, B = 16, d = D, G <= 16.  A workgroup of W
+// waves handles one (sequence, kv head, partition); wave w takes the
+// partition's blocks w, w + W, ...  Per 16-token block and wave:
+//   S^T[16 tokens][16 heads] = K[16][D] . Q^T[D][16]   (D/32 x mfma 16x16x32)
+//   online softmax on S^T (each lane holds 4 tokens of one head)
+//   O^T[D][16 heads] += V^T[D][16] . P^T[16][16]        (D/16 x mfma 16x16x16)
+// Query heads beyond G are zero rows; their results are discarded.  The P^T
+// operand is exactly the S^T result layout, so no data moves between lanes
+// except the two shuffles of the per-head block maximum.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct kv_regs {
+  uint4 k[D / 32];
+  uint4 v[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(kv_regs<D>& r, const uint4* kt, const uint4* vt, int lane) {
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) r.k[i] = kt[i * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) r.v[i] = vt[i * 64 + lane];
+}
+
+template <int D, int W>
+__global__ void __launch_bounds__(W * 64) attn_mfma_kernel(attn_args a) {
+  extern __shared__ float smem[];  // [W][G][D] outputs, then [W][G] m and l
+  work_item w;
+  if (!decode_work(a, w)) return;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hl = lane & 15;   // head column owned by this lane
+  const int quad = lane >> 4; // 4-token group / 8-dim group of this lane
+
+  // Q^T operand: lane holds q[head hl][kk*32 + quad*8 .. +8]
+  bf16x8_t qop[D / 32];
+  {
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<int64_t>(w.seq) * a.n_q_heads + w.kv_head * G + hl) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (hl < G) raw = *reinterpret_cast<const uint4*>(qg + kk * 32 + quad * 8);
+      qop[kk] = __builtin_bit_cast(bf16x8_t, raw);
+    }
+  }
+
+  const int32_t* table = a.tables + static_cast<int64_t>(w.seq) * a.max_blocks;
+  const int blk_begin = w.tok_begin / 16;
+  const int blk_end = (w.tok_end + 15) / 16;
+  const int n_mine = blk_begin + wave < blk_end ? (blk_end - blk_begin - wave + W - 1) / W : 0;
+  const uint4* kpool = static_cast<const uint4*>(a.k_layer);
+  const uint4* vpool = static_cast<const uint4*>(a.v_layer);
+  constexpr int kTileVec = 16 * D * 2 / 16;  // 16-byte vectors per tile
+  const int64_t head_off = static_cast<int64_t>(w.kv_head) * kTileVec;
+  const int64_t blk_stride = static_cast<int64_t>(a.n_kv_heads) * kTileVec;
+
+  f32x4_t o[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+  bool poisoned = false;
+
+  // The physical ids of this wave's blocks, 64 at a time, one per lane.
+  int tab_vec = 0;
+  auto fetch_table = [&](int first) {
+    const int idx = first + lane;
+    const int j = blk_begin + wave + idx * W;
+    tab_vec = (idx < n_mine) ? table[j] : 0;
+  };
+  auto phys_of = [&](int k) -> int {
+    return __builtin_amdgcn_readlane(tab_vec, k & 63);
+  };
+
+  kv_regs<D> cur, nxt;
+  if (n_mine > 0) {
+    fetch_table(0);
+    int p = phys_of(0);
+    if (p < 0 || p >= a.num_blocks) p = 0;
+    const int64_t t = p * blk_stride + head_off;
+    load_block<D>(cur, kpool + t, vpool + t, lane);
+  }
+  for (int k = 0; k < n_mine; ++k) {
+    int p = phys_of(k);
+    const bool bad = p < 0 || p >= a.num_blocks;
+    poisoned |= bad;
+    if (k + 1 < n_mine) {
+      if (((k + 1) & 63) == 0) fetch_table(k + 1);
+      int pn = phys_of(k + 1);
+      if (pn < 0 || pn >= a.num_blocks) pn = 0;
+      const int64_t t = pn * blk_stride + head_off;
+      load_block<D>(nxt, kpool + t, vpool + t, lane);
+    }
+    const int j = blk_begin + wave + k * W;
+    const int valid = bad ? 0 : min(16, w.tok_end - j * 16);  // tokens of this block in range
+
+    // S^T = K . Q^T
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk], s, 0, 0, 0);
+
+    // online softmax; lane holds tokens quad*4 + i of head hl
+    float sv[4];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = (quad * 4 + i < valid) ? s[i] * a.scale_log2 : -INFINITY;
+      mb = fmaxf(mb, sv[i]);
+    }
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float m_new = fmaxf(m_run, mb);
+    float alpha = 1.f;
+    float pv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m_new != -INFINITY) {
+      alpha = exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = exp2f(sv[i] - m_new);
+    }
+    m_run = m_new;
+    // P^T operand in bf16; the denominator sums the rounded weights
+    s16x4_t pop;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t b = f32_to_bf16(pv[i]);
+      pop[i] = static_cast<short>(b);
+      psum += bf16_to_f32(b);
+    }
+    l_lane = l_lane * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
+
+    // zero the values of out-of-range slots (their memory may hold anything)
+    if (valid < 16) {
+#pragma unroll
+      for (int pp = 0; pp < D / 32; ++pp) {
+        uint32_t* wv = reinterpret_cast<uint32_t*>(&cur.v[pp]);
+        // 16 bytes = [half 0: 4 slots][half 1: 4 slots], 2 slots per dword
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw) {
+          const int slot0 = quad * 4 + (dw & 1) * 2;
+          uint32_t mask = 0;
+          if (slot0 < valid) mask |= 0x0000ffffu;
+          if (slot0 + 1 < valid) mask |= 0xffff0000u;
+          wv[dw] &= mask;
+        }
+      }
+    }
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int pp = 0; pp < D / 32; ++pp) {
+      const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
+      o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop,
+                                                            o[2 * pp], 0, 0, 0);
+      o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[1]), pop,
+                                                                o[2 * pp + 1], 0, 0, 0);
+    }
+    cur = nxt;
+  }
+
+  // per-head denominators: sum over the four token groups
+  l_lane += __shfl_xor(l_lane, 16);
+  l_lane += __shfl_xor(l_lane, 32);
+
+  // stage this wave's (m, l, O) in LDS; lane holds O^T[16*nt + quad*4 + i][hl]
+  float* o_s = smem;                               // [W][G][D]
+  float* m_s = smem + W * G * D;                   // [W][G]
+  float* l_s = m_s + W * G;                        // [W][G]
+  __shared__ int poison_s;
+  if (threadIdx.x == 0) poison_s = 0;
+  if (hl < G) {
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o_s[(wave * G + hl) * D + nt * 16 + quad * 4 + i] = o[nt][i];
+    if (quad == 0) {
+      m_s[wave * G + hl] = m_run;
+      l_s[wave * G + hl] = l_lane;
+    }
+  }
+  __syncthreads();
+  if (poisoned) atomicOr(&poison_s, 1);
+  __syncthreads();
+  const bool any_poison = poison_s != 0;
+  for (int i = threadIdx.x; i < G * D; i += W * 64) {
+    const int h = i / D, e = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < W; ++v) M = fmaxf(M, m_s[v * G + h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int v = 0; v < W; ++v) {
+        const float f = exp2f(m_s[v * G + h] - M);
+        L += f * l_s[v * G + h];
+        O += f * o_s[(v * G + h) * D + e];
+      }
+    }
+    store_result<uint16_t>(a, w, h, e, M, L, O, any_poison);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the partitions of a sequence with the running-max recurrences:
+// M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// One workgroup per (sequence, query head); sequences with one partition were
+// finished by the partition kernel.
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__global__ void __launch_bounds__(256) merge_kernel(attn_args a) {
+  const int seq = blockIdx.x / a.n_q_heads;
+  const int h = blockIdx.x % a.n_q_heads;
+  int n = a.ctx_lens[seq];
+  const int cap = a.max_blocks * a.block_size;
+  n = n > cap ? cap : n;
+  const int n_parts = n <= 0 ? 1 : (n + a.partition_tokens - 1) / a.partition_tokens;
+  if (n_parts == 1) return;
+  const int64_t ph = (static_cast<int64_t>(seq) * a.n_q_heads + h) * a.max_parts;
+  __shared__ float w_s[1024];
+  __shared__ float red[4];
+  // maximum over partitions
+  float M = -INFINITY;
+  for (int p = threadIdx.x; p < n_parts; p += blockDim.x) M = fmaxf(M, a.part_m[ph + p]);
+  M = wave_max(M);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  // weights and denominator
+  float L = 0.f;
+  for (int p = threadIdx.x; p < n_parts; p += blockDim.x) {
+    const float m = a.part_m[ph + p];
+    float f = exp2f(m - M);
+    if (m != m) f = __builtin_nanf("");
+    if (p < 1024) w_s[p] = f;
+    L += f * a.part_l[ph + p];
+  }
+  L = wave_sum(L);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = L;
+  __syncthreads();
+  L = red[0] + red[1] + red[2] + red[3];
+  const float inv = 1.f / L;
+  T* out = static_cast<T*>(a.out) + (static_cast<int64_t>(seq) * a.n_q_heads + h) * a.head_dim;
+  for (int e = threadIdx.x; e < a.head_dim; e += blockDim.x) {
+    float acc = 0.f;
+    for (int p = 0; p < n_parts; ++p) {
+      const float f = p < 1024 ? w_s[p] : exp2f(a.part_m[ph + p] - M);
+      acc += f * a.part_o[(ph + p) * a.head_dim + e];
+    }
+    out[e] = elem<T>::from_f32(acc * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host helpers
+// ---------------------------------------------------------------------------
+
+kv_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KV_OK;
+  return fail(KV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+constexpr int kMfmaWaves = 4;
+
+// LDS staging of the per-wave outputs must fit the 64 KiB a launch may request.
+size_t mfma_lds_bytes(int D, int G) { return static_cast<size_t>(kMfmaWaves) * G * (D + 2) * sizeof(float); }
+
+bool mfma_supported(const kv_pool_config& c, int G) {
+  return c.dtype == KV_BF16 && c.block_size == 16 && (c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256) &&
+         G >= 1 && G <= kMaxGroup && mfma_lds_bytes(c.head_dim, G) <= 65536;
+}
+
+int choose_partition(const kv_pool_config& c, int n_seqs, int max_blocks) {
+  // Aim for a few thousand workgroups so every CU has several resident, with
+  // at least 16 blocks per workgroup (4 per wave) to amortise the prologue.
+  const int64_t max_ctx = static_cast<int64_t>(max_blocks) * c.block_size;
+  const int64_t units = static_cast<int64_t>(n_seqs) * c.num_kv_heads;
+  int part = 16 * c.block_size;
+  while (part < max_ctx && units * ((max_ctx + part - 1) / part) > 4096) part *= 2;
+  return part;
+}
+
+struct resolved {
+  int kernel;
+  int partition;
+  int max_parts;
+  float scale;
+};
+
+kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_blocks, const kv_attention_options* opts,
+                  resolved& r) {
+  const kv_pool_config& c = pool->cfg;
+  if (num_q_heads <= 0 || num_q_heads % c.num_kv_heads != 0)
+    return fail(KV_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+  const int G = num_q_heads / c.num_kv_heads;
+  if (G > kMaxGroup) return fail(KV_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  if (n_seqs < 0 || max_blocks <= 0) return fail(KV_ERR_INVALID, "n_seqs must be >= 0 and max_blocks_per_seq > 0");
+  kv_attention_options o{0.f, 0, KV_KERNEL_AUTO};
+  if (opts) o = *opts;
+  if (o.kernel == KV_KERNEL_MFMA && !mfma_supported(c, G))
+    return fail(KV_ERR_UNSUPPORTED, "the matrix-core kernel needs bf16, B = 16, d in {64, 128, 256} and G * (d + 2) <= 4096");
+  if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_GENERIC && o.kernel != KV_KERNEL_MFMA)
+    return fail(KV_ERR_INVALID, "unknown kernel selector");
+  r.kernel = o.kernel == KV_KERNEL_AUTO ? (mfma_supported(c, G) ? KV_KERNEL_MFMA : KV_KERNEL_GENERIC) : o.kernel;
+  if (o.partition_tokens < 0 || (o.partition_tokens > 0 && o.partition_tokens % c.block_size != 0))
+    return fail(KV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of the block size");
+  r.partition = o.partition_tokens ? o.partition_tokens : choose_partition(c, n_seqs, max_blocks);
+  const int64_t max_ctx = static_cast<int64_t>(max_blocks) * c.block_size;
+  r.max_parts = static_cast<int>((max_ctx + r.partition - 1) / r.partition);
+  if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
+  r.scale = o.scale > 0.f ? o.scale : 1.f / std::sqrt(static_cast<float>(c.head_dim));
+  return KV_OK;
+}
+
+uint64_t workspace_for(const kv_pool_config& c, int n_seqs, int num_q_heads, const resolved& r) {
+  if (r.max_parts <= 1) return 0;
+  const uint64_t rows = static_cast<uint64_t>(n_seqs) * num_q_heads * r.max_parts;
+  auto up = [](uint64_t b) { return (b + 255) & ~uint64_t(255); };
+  return up(rows * 4) * 2 + up(rows * c.head_dim * 4);
+}
+
+template <int D, int W>
+hipError_t launch_mfma(const attn_args& a, int G, int64_t grid, hipStream_t st) {
+  static_assert(W == kMfmaWaves, "LDS sizing assumes kMfmaWaves waves");
+  const size_t shm = mfma_lds_bytes(D, G);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, W>), dim3(static_cast<unsigned>(grid)), dim3(W * 64), shm, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_generic(const attn_args& a, int64_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((attn_generic_kernel<T, D>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace pagedkv
+
+using namespace pagedkv;
+
+extern "C" {
+
+kv_status reshape_and_cache(kv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                            const int64_t* d_slot_mapping, int32_t n_tokens, void* hip_stream) {
+  if (!pool) return fail(KV_ERR_INVALID, "pool is NULL");
+  const kv_pool_config& c = pool->cfg;
+  if (layer < 0 || layer >= c.num_layers) return fail(KV_ERR_INVALID, "layer out of range");
+  if (n_tokens < 0) return fail(KV_ERR_INVALID, "n_tokens < 0");
+  if (n_tokens == 0) return KV_OK;
+  if (!k_new || !v_new || !d_slot_mapping || !pool->k_cache || !pool->v_cache)
+    return fail(KV_ERR_INVALID, "NULL device pointer");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(KV_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
+  const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_elems(c);
+  const int64_t n_slots = static_cast<int64_t>(c.num_blocks) * c.block_size;
+  const int X = 16 / elem_bytes(c.dtype);
+  const int64_t items = static_cast<int64_t>(n_tokens) * c.num_kv_heads * (c.head_dim / X);
+  const int64_t want = (items + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (c.dtype == KV_F32) {
+    hipLaunchKernelGGL(reshape_and_cache_kernel<float>, dim3(grid), dim3(256), 0, st, static_cast<const float*>(k_new),
+                       static_cast<const float*>(v_new), d_slot_mapping, static_cast<float*>(pool->k_cache) + layer_off,
+                       static_cast<float*>(pool->v_cache) + layer_off, items, c.num_kv_heads, c.head_dim, c.block_size,
+                       n_slots);
+  } else {
+    hipLaunchKernelGGL(reshape_and_cache_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), d_slot_mapping,
+                       static_cast<uint16_t*>(pool->k_cache) + layer_off,
+                       static_cast<uint16_t*>(pool->v_cache) + layer_off, items, c.num_kv_heads, c.head_dim,
+                       c.block_size, n_slots);
+  }
+  if (kv_status s = hip_check(hipGetLastError(), "reshape_and_cache launch")) return s;
+  return KV_OK;
+}
+
+kv_status copy_blocks(kv_pool* pool, const int64_t* d_pairs, int32_t n_pairs, void* hip_stream) {
+  if (!pool) return fail(KV_ERR_INVALID, "pool is NULL");
+  if (n_pairs < 0) return fail(KV_ERR_INVALID, "n_pairs < 0");
+  if (n_pairs == 0) return KV_OK;
+  if (!d_pairs || !pool->k_cache || !pool->v_cache) return fail(KV_ERR_INVALID, "NULL device pointer");
+  const kv_pool_config& c = pool->cfg;
+  const int64_t grid = static_cast<int64_t>(n_pairs) * c.num_layers * 2;
+  if (grid > 0x7fffffff) return fail(KV_ERR_INVALID, "too many pairs");
+  const int64_t block_bytes = static_cast<int64_t>(c.num_kv_heads) * tile_elems(c) * elem_bytes(c.dtype);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                     static_cast<hipStream_t>(hip_stream), static_cast<uint4*>(pool->k_cache),
+                     static_cast<uint4*>(pool->v_cache), d_pairs, c.num_layers, c.num_blocks, block_bytes / 16);
+  return hip_check(hipGetLastError(), "copy_blocks launch");
+}
+
+uint64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int32_t num_q_heads,
+                                         int32_t max_blocks_per_seq, const kv_attention_options* opts) {
+  if (!pool) return 0;
+  resolved r;
+  if (resolve(pool, n_seqs, num_q_heads, max_blocks_per_seq, opts, r) != KV_OK) return 0;
+  return workspace_for(pool->cfg, n_seqs, num_q_heads, r);
+}
+
+kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, void* out,
+                                 const int32_t* d_block_tables, const int32_t* d_context_lens, int32_t n_seqs,
+                                 int32_t max_blocks_per_seq, int32_t num_q_heads, const kv_attention_options* opts,
+                                 void* d_workspace, uint64_t workspace_bytes, void* hip_stream) {
+  if (!pool) return fail(KV_ERR_INVALID, "pool is NULL");
+  const kv_pool_config& c = pool->cfg;
+  if (layer < 0 || layer >= c.num_layers) return fail(KV_ERR_INVALID, "layer out of range");
+  resolved r;
+  if (kv_status s = resolve(pool, n_seqs, num_q_heads, max_blocks_per_seq, opts, r)) return s;
+  if (n_seqs == 0) return KV_OK;
+  if (!q || !out || !d_block_tables || !d_context_lens || !pool->k_cache || !pool->v_cache)
+    return fail(KV_ERR_INVALID, "NULL device pointer");
+  if (reinterpret_cast<uintptr_t>(q) & 15) return fail(KV_ERR_INVALID, "q must be 16-byte aligned");
+  const uint64_t need = workspace_for(c, n_seqs, num_q_heads, r);
+  if (need > 0 && (!d_workspace || workspace_bytes < need))
+    return fail(KV_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
+  const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * r.max_parts;
+  if (grid > 0x7fffffff) return fail(KV_ERR_INVALID, "grid too large");
+
+  attn_args a{};
+  a.q = q;
+  a.out = out;
+  a.tables = d_block_tables;
+  a.ctx_lens = d_context_lens;
+  const int64_t layer_off =
+      static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_elems(c) * elem_bytes(c.dtype);
+  a.k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
+  a.v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
+  if (need > 0) {
+    const uint64_t rows = static_cast<uint64_t>(n_seqs) * num_q_heads * r.max_parts;
+    auto up = [](uint64_t b) { return (b + 255) & ~uint64_t(255); };
+    char* ws = static_cast<char*>(d_workspace);
+    a.part_m = reinterpret_cast<float*>(ws);
+    a.part_l = reinterpret_cast<float*>(ws + up(rows * 4));
+    a.part_o = reinterpret_cast<float*>(ws + 2 * up(rows * 4));
+  }
+  a.n_seqs = n_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.n_q_heads = num_q_heads;
+  a.n_kv_heads = c.num_kv_heads;
+  a.head_dim = c.head_dim;
+  a.block_size = c.block_size;
+  a.num_blocks = c.num_blocks;
+  a.partition_tokens = r.partition;
+  a.max_parts = r.max_parts;
+  a.scale_log2 = r.scale * kLog2e;
+
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const int G = num_q_heads / c.num_kv_heads;
+  hipError_t e = hipSuccess;
+  if (r.kernel == KV_KERNEL_MFMA) {
+    switch (c.head_dim) {
+      case 64: e = launch_mfma<64, kMfmaWaves>(a, G, grid, st); break;
+      case 128: e = launch_mfma<128, kMfmaWaves>(a, G, grid, st); break;
+      default: e = launch_mfma<256, kMfmaWaves>(a, G, grid, st); break;
+    }
+  } else {
+    const bool f32 = c.dtype == KV_F32;
+    switch (c.head_dim) {
+      case 32: e = f32 ? launch_generic<float, 32>(a, grid, st) : launch_generic<uint16_t, 32>(a, grid, st); break;
+      case 64: e = f32 ? launch_generic<float, 64>(a, grid, st) : launch_generic<uint16_t, 64>(a, grid, st); break;
+      case 96: e = f32 ? launch_generic<float, 96>(a, grid, st) : launch_generic<uint16_t, 96>(a, grid, st); break;
+      case 128: e = f32 ? launch_generic<float, 128>(a, grid, st) : launch_generic<uint16_t, 128>(a, grid, st); break;
+      case 160: e = f32 ? launch_generic<float, 160>(a, grid, st) : launch_generic<uint16_t, 160>(a, grid, st); break;
+      case 192: e = f32 ? launch_generic<float, 192>(a, grid, st) : launch_generic<uint16_t, 192>(a, grid, st); break;
+      case 224: e = f32 ? launch_generic<float, 224>(a, grid, st) : launch_generic<uint16_t, 224>(a, grid, st); break;
+      default: e = f32 ? launch_generic<float, 256>(a, grid, st) : launch_generic<uint16_t, 256>(a, grid, st); break;
+    }
+  }
+  if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
+  if (r.max_parts > 1) {
+    const int64_t mgrid = static_cast<int64_t>(n_seqs) * num_q_heads;
+    if (c.dtype == KV_F32)
+      hipLaunchKernelGGL(merge_kernel<float>, dim3(static_cast<unsigned>(mgrid)), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(static_cast<unsigned>(mgrid)), dim3(256), 0, st, a);
+    if (kv_status s = hip_check(hipGetLastError(), "paged attention merge launch")) return s;
+  }
+  return KV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal view of a kv_pool shared by the host block manager (pool.cpp) and
+// the device entry points (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <deque>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pagedkv.h"
+
+struct kv_seq_state {
+  std::vector<int32_t> table;  // logical block j -> physical block
+  int32_t length = 0;          // tokens
+};
+
+struct kv_pending_group {
+  void* event = nullptr;  // hipEvent_t, or nullptr for a fence group
+  uint64_t fence = 0;     // used when event == nullptr
+  bool ready = false;
+  std::vector<int32_t> blocks;
+};
+
+struct kv_pool {
+  kv_pool_config cfg;
+  void* k_cache = nullptr;
+  void* v_cache = nullptr;
+  std::deque<int32_t> free_list;             // pop front, push back
+  std::vector<int32_t> ref;                  // per physical block
+  std::unordered_map<int64_t, kv_seq_state> seqs;
+  std::deque<kv_pending_group> pending;      // released, waiting for the device
+  int32_t n_pending = 0;
+};
+
+namespace pagedkv {
+
+// Element size of the pool dtype.
+inline int elem_bytes(int32_t dtype) { return dtype == KV_F32 ? 4 : 2; }
+
+// Elements of one (layer, block, kv head) tile.
+inline int64_t tile_elems(const kv_pool_config& c) {
+  return static_cast<int64_t>(c.block_size) * c.head_dim;
+}
+
+// Elements of the whole K (or V) buffer.
+inline int64_t pool_elems(const kv_pool_config& c) {
+  return static_cast<int64_t>(c.num_layers) * c.num_blocks * c.num_kv_heads * tile_elems(c);
+}
+
+// Sets the thread-local error message and returns the status.
+kv_status fail(kv_status st, const std::string& msg);
+
+}  // namespace pagedkv

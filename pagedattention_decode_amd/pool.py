@@ -1,0 +1,105 @@
+"""Owner object for one pool: torch allocates the K/V buffers, the library keeps
+the host block manager.  Marshalling only; see include/pagedkv.h for semantics.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as B
+
+
+class PagedKVPool:
+    def __init__(self, num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype="bf16",
+                 free_order=None, device="cuda", allocate=True):
+        self.dtype = dtype
+        code = B.KV_BF16 if dtype == "bf16" else B.KV_F32
+        self.cfg = B.make_config(num_layers, num_blocks, block_size, num_kv_heads, head_dim, code)
+        self.num_layers, self.num_blocks, self.block_size = num_layers, num_blocks, block_size
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        kb, vb = B.kv_pool_required_bytes(self.cfg)
+        self.k_cache = self.v_cache = None
+        if allocate:
+            import torch
+            # raw storage; elements are viewed per dtype by the caller when needed
+            self.k_cache = torch.empty(kb, dtype=torch.uint8, device=device)
+            self.v_cache = torch.empty(vb, dtype=torch.uint8, device=device)
+        self.handle = B.kv_pool_create(self.cfg, self.k_cache if allocate else 0,
+                                       self.v_cache if allocate else 0, free_order)
+
+    def close(self):
+        if self.handle is not None:
+            B.kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- host block manager ----------------------------------------------
+    def add(self, seq):
+        B.kv_seq_add(self.handle, seq)
+
+    def fork(self, parent, child):
+        B.kv_seq_fork(self.handle, parent, child)
+
+    def append(self, seq_ids, counts=None):
+        return B.kv_append_slots(self.handle, seq_ids, counts)
+
+    def tables(self, seq_ids, max_blocks):
+        return B.kv_get_block_tables(self.handle, seq_ids, max_blocks)
+
+    def info(self, seq):
+        return B.kv_seq_info(self.handle, seq)
+
+    def release(self, seq, stream=None):
+        B.kv_seq_release(self.handle, seq, stream)
+
+    def release_fenced(self, seq, fence):
+        B.kv_seq_release_fenced(self.handle, seq, fence)
+
+    def retire(self, completed):
+        B.kv_pool_retire(self.handle, completed)
+
+    def reclaim(self, wait=False):
+        B.kv_pool_reclaim(self.handle, wait)
+
+    def stats(self):
+        return B.kv_pool_stats(self.handle)
+
+    def free_list(self):
+        return B.kv_pool_free_list(self.handle, self.num_blocks)
+
+    def refcounts(self):
+        return B.kv_pool_refcounts(self.handle, self.num_blocks)
+
+    def check(self):
+        B.kv_pool_check(self.handle)
+
+    # -- device operations ---------------------------------------------------
+    def cache(self, layer, k_new, v_new, slot_mapping, stream=None):
+        B.reshape_and_cache(self.handle, layer, k_new, v_new, slot_mapping, stream)
+
+    def copy(self, pairs, stream=None):
+        B.copy_blocks(self.handle, pairs, stream)
+
+    def workspace_bytes(self, n_seqs, num_q_heads, max_blocks, opts=None):
+        return B.paged_attention_workspace_bytes(self.handle, n_seqs, num_q_heads, max_blocks, opts)
+
+    def decode(self, layer, q, out, block_tables, context_lens, num_q_heads, opts=None, workspace=None,
+               stream=None):
+        B.paged_attention_decode(self.handle, layer, q, out, block_tables, context_lens, num_q_heads, opts,
+                                 workspace, stream)
+
+    # -- raw views for tests -------------------------------------------------
+    def raw(self, which):
+        """The K or V buffer as a flat tensor of stored bit patterns."""
+        import torch
+        buf = self.k_cache if which == "k" else self.v_cache
+        return buf.view(torch.int16 if self.dtype == "bf16" else torch.int32)
+
+
+def np_storage(dtype):
+    return np.uint16 if dtype == "bf16" else np.uint32

@@ -1,0 +1,187 @@
+"""Replays a synthetic workload through the HIP library (C++ block manager +
+device kernels), optionally checking every allocator result against an
+oracle replay of the same workload bit for bit.
+
+Used by the GPU tests and by ``__graft_entry__.smoke``.  Inputs come from
+:mod:`synth` only; nothing here computes attention.
+"""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+from pagedattention_decode_amd import binding as B
+from pagedattention_decode_amd.pool import PagedKVPool
+from synth import draws
+from synth.draws import TAG_K, TAG_Q, TAG_V
+
+
+_EXECUTOR = None
+
+
+def _pool():
+    global _EXECUTOR
+    if _EXECUTOR is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _EXECUTOR = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4))
+    return _EXECUTOR
+
+
+def to_device_bits(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    if bits.dtype == np.uint16:
+        return torch.from_numpy(bits.view(np.int16)).to(device)
+    return torch.from_numpy(bits.view(np.int32)).to(device)
+
+
+def bits_to_float_tensor(t: torch.Tensor, dtype: str) -> torch.Tensor:
+    return t.view(torch.bfloat16).float() if dtype == draws.BF16 else t.view(torch.float32)
+
+
+class GpuRun:
+    def __init__(self, wl, layers=None, writers=None, opts=None, free_order=None, fill=None,
+                 max_blocks=None, ref=None, decode_layers=None):
+        self.wl = wl
+        self.layers = list(range(wl.num_layers)) if layers is None else list(layers)
+        self.decode_layers = self.layers if decode_layers is None else list(decode_layers)
+        self.writers = None if writers is None else set(writers)
+        self.opts = opts
+        self.ref = ref
+        order = draws.free_order(wl.seed, wl.num_blocks) if free_order is None else free_order
+        self.pool = PagedKVPool(wl.num_layers, wl.num_blocks, wl.block_size, wl.num_kv_heads,
+                                wl.head_dim, wl.dtype, free_order=order)
+        if fill is not None:
+            # a known background: every unwritten element holds this bit pattern
+            self.pool.raw("k").fill_(fill)
+            self.pool.raw("v").fill_(fill)
+        final = wl.final_lengths()
+        longest = max(final.values()) if final else 1
+        self.max_blocks = max_blocks or max(1, -(-longest // wl.block_size))
+        self.appends = []
+        self.decodes = []
+        self.decode_outputs = []  # per decode op: {layer: tensor [S, Hq, d] float32}
+        self.n_append = 0
+        self.n_decode = 0
+
+    def rows(self, tag, layer, writer, positions):
+        wl = self.wl
+        return draws.token_rows(wl.seed, tag, layer, writer, positions, wl.num_kv_heads, wl.head_dim, wl.dtype)
+
+    def run(self, ops=None):
+        for op in (self.wl.ops if ops is None else ops):
+            self.apply(op)
+        torch.cuda.synchronize()
+        return self
+
+    def apply(self, op):
+        kind = op[0]
+        pool = self.pool
+        if kind == "add":
+            pool.add(op[1])
+        elif kind == "fork":
+            pool.fork(op[1], op[2])
+        elif kind == "release":
+            pool.release(op[1])
+        elif kind == "append":
+            seq_ids, counts = list(op[1]), list(op[2])
+            segments, running = [], {}
+            for s, c in zip(seq_ids, counts):
+                start = running.get(s, pool.info(s)[0])
+                segments.append((s, start, c))
+                running[s] = start + c
+            slots, pairs = pool.append(seq_ids, counts)
+            if self.ref is not None:
+                r_seq, r_cnt, r_slots, r_pairs = self.ref.appends[self.n_append]
+                assert list(r_seq) == seq_ids and list(r_cnt) == counts
+                assert np.array_equal(slots, np.asarray(r_slots, np.int64)), "slot mapping differs from the oracle"
+                assert [tuple(p) for p in pairs.tolist()] == [tuple(p) for p in r_pairs], "CoW pairs differ"
+            self.appends.append((slots, pairs))
+            self.n_append += 1
+            if len(pairs):
+                pool.copy(torch.from_numpy(pairs).cuda())
+            write_slots = slots.copy()
+            at = 0
+            keep = []
+            for s, start, c in segments:
+                if self.writers is not None and s not in self.writers:
+                    write_slots[at:at + c] = -1
+                else:
+                    keep.append((s, start, c, at))
+                at += c
+            if not keep or len(slots) == 0:
+                return
+            d_slots = torch.from_numpy(write_slots).cuda()
+            # split every kept segment at generator-chunk boundaries and draw in parallel
+            tasks = []
+            for s, start, c, at in keep:
+                pos = start
+                while pos < start + c:
+                    end = min(start + c, (pos // draws.CHUNK + 1) * draws.CHUNK)
+                    tasks.append((s, pos, end - pos, at + pos - start))
+                    pos = end
+            for layer in self.layers:
+                kb = np.zeros((len(slots), self.wl.num_kv_heads, self.wl.head_dim),
+                              dtype=draws.storage_np_dtype(self.wl.dtype))
+                vb = np.zeros_like(kb)
+
+                def fill(task, layer=layer, kb=kb, vb=vb):
+                    s, p0, c, at = task
+                    pos = np.arange(p0, p0 + c)
+                    kb[at:at + c] = self.rows(TAG_K, layer, s, pos)
+                    vb[at:at + c] = self.rows(TAG_V, layer, s, pos)
+
+                if len(tasks) > 4:
+                    list(_pool().map(fill, tasks))
+                else:
+                    for t in tasks:
+                        fill(t)
+                pool.cache(layer, to_device_bits(kb), to_device_bits(vb), d_slots)
+        elif kind == "decode":
+            seq_ids = list(op[1])
+            tables, lens = pool.tables(seq_ids, self.max_blocks)
+            if self.ref is not None:
+                rd = self.ref.decodes[self.n_decode]
+                assert rd["seq_ids"] == seq_ids
+                assert list(lens) == rd["lengths"], "context lengths differ from the oracle"
+                for i, t in enumerate(rd["tables"]):
+                    assert list(tables[i, :len(t)]) == t, "block table differs from the oracle"
+            self.decodes.append({"seq_ids": seq_ids, "tables": tables, "lengths": lens})
+            d_tables = torch.from_numpy(tables).cuda()
+            d_lens = torch.from_numpy(lens).cuda()
+            outs = {}
+            for layer in self.decode_layers:
+                outs[layer] = self.decode(self.n_decode, layer, d_tables, d_lens, len(seq_ids))
+            self.decode_outputs.append(outs)
+            self.n_decode += 1
+        else:
+            raise ValueError(kind)
+
+    def query_bits(self, decode_index, layer, n):
+        wl = self.wl
+        return draws.normal_bits(wl.seed, TAG_Q, (decode_index, layer), (n, wl.num_q_heads, wl.head_dim), wl.dtype)
+
+    def decode(self, decode_index, layer, d_tables, d_lens, n, opts=None):
+        wl = self.wl
+        q = to_device_bits(self.query_bits(decode_index, layer, n))
+        out = torch.empty_like(q)
+        opts = opts if opts is not None else self.opts
+        ws_bytes = self.pool.workspace_bytes(n, wl.num_q_heads, d_tables.shape[1], opts)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+        self.pool.decode(layer, q, out, d_tables, d_lens, wl.num_q_heads, opts, ws)
+        return bits_to_float_tensor(out, wl.dtype)
+
+
+def run_workload_on_gpu(wl, **kw):
+    return GpuRun(wl, **kw).run()
+
+
+def attention_errors(got: np.ndarray, expect: np.ndarray):
+    """(max abs error, max over rows of the relative L2 error) of [S, Hq, d] outputs."""
+    diff = got - expect
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    num = np.sqrt((diff ** 2).sum(axis=-1))
+    den = np.sqrt((expect ** 2).sum(axis=-1))
+    rel = float((num / np.maximum(den, 1e-30)).max()) if diff.size else 0.0
+    return max_abs, rel

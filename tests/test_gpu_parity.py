@@ -1,0 +1,319 @@
+"""GPU parity: the HIP library against the CPU oracle.
+
+* slot scatter (reshape_and_cache) and copy-on-write block copies: bit-exact
+  against the oracle's logical pool, with every unwritten element unchanged;
+* decode attention: fp32 within 1e-5 (max abs); bf16 within max abs 2e-2 and a
+  per-row relative L2 error of 5e-3 against the float64 oracle;
+* the workloads at their full sizes (config 4 and the fork workload on sampled
+  sequences), ragged lengths, edge cases and both kernels.
+
+Every test prints the case it runs before touching the GPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import decode_attention
+from oracle.runner import OracleReplay
+from pagedattention_decode_amd import binding as B
+from synth import draws, workloads
+from tests.gpu_harness import GpuRun, attention_errors, bits_to_float_tensor, to_device_bits
+
+pytestmark = pytest.mark.gpu
+
+BF16_ABS, BF16_REL, F32_ABS = 2e-2, 5e-3, 1e-5
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def check_outputs(got, expect, dtype, what):
+    max_abs, rel = attention_errors(got, expect)
+    print(f"  {what}: max abs {max_abs:.3e}, max row rel-L2 {rel:.3e}", flush=True)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    if dtype == draws.F32:
+        assert max_abs <= F32_ABS, what
+    else:
+        assert max_abs <= BF16_ABS and rel <= BF16_REL, what
+
+
+# ---------------------------------------------------------------------------
+# pool layout decoding (independent restatement of the documented index map)
+# ---------------------------------------------------------------------------
+
+def layout_index(num_blocks, block_size, num_kv_heads, head_dim, dtype, which):
+    """Flat element index of [N][B][Hkv][d] (one layer) in the device buffer."""
+    X = 16 // (4 if dtype == draws.F32 else 2)
+    Q = math.gcd(block_size, 4)
+    p = np.arange(num_blocks)[:, None, None, None]
+    r = np.arange(block_size)[None, :, None, None]
+    g = np.arange(num_kv_heads)[None, None, :, None]
+    e = np.arange(head_dim)[None, None, None, :]
+    tile = (p * num_kv_heads + g) * block_size * head_dim
+    if which == "k":
+        inner = ((e // X) * block_size + r) * X + e % X
+    else:
+        inner = ((((e // 32) * (block_size // Q) + r // Q) * 16 + e % 16) * 2 + (e % 32) // 16) * Q + r % Q
+    return tile + inner
+
+
+def device_pool_logical(run: GpuRun, which, layer):
+    wl = run.wl
+    raw = run.pool.raw(which).cpu().numpy().view(draws.storage_np_dtype(wl.dtype))
+    per_layer = wl.num_blocks * wl.block_size * wl.num_kv_heads * wl.head_dim
+    idx = layout_index(wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.dtype, which)
+    return raw[layer * per_layer:(layer + 1) * per_layer][idx]
+
+
+# ---------------------------------------------------------------------------
+# scatter and copy: bit-exact
+# ---------------------------------------------------------------------------
+
+def small_fork_workload(dtype, block_size, head_dim, num_kv_heads=2, layers=2, num_blocks=48, seed=21):
+    ops = [("add", 0), ("append", (0,), (3 * block_size + 1,)), ("add", 1),
+           ("append", (1, 0), (5, 2)), ("fork", 0, 2), ("fork", 0, 3),
+           ("append", (2, 3, 0, 1), (1, 2, 1, block_size)), ("decode", (0, 1, 2, 3)),
+           ("append", (2, 3), (block_size + 3, 1)), ("decode", (0, 1, 2, 3))]
+    return workloads.Workload("small_fork", seed, dtype, layers, num_kv_heads * 2, num_kv_heads, head_dim,
+                              block_size, num_blocks, ops)
+
+
+@pytest.mark.parametrize("dtype,block_size,head_dim", [(draws.BF16, 16, 128), (draws.F32, 4, 64),
+                                                       (draws.BF16, 2, 32), (draws.F32, 6, 96)])
+def test_scatter_and_copy_bit_exact(dtype, block_size, head_dim):
+    announce(f"reshape_and_cache + copy_blocks bitwise: {dtype} B={block_size} d={head_dim}")
+    wl = small_fork_workload(dtype, block_size, head_dim)
+    fill = 0x5A5A if dtype == draws.BF16 else 0x5A5A5A5A
+    bg_val = np.array(fill, dtype=draws.storage_np_dtype(dtype))
+    bg = lambda layer, which, block: np.full((block_size, 2, head_dim), bg_val)  # noqa: E731
+    ref = OracleReplay(wl, background=bg).run()
+    run = GpuRun(wl, fill=fill if dtype == draws.F32 else np.int16(fill), ref=ref).run()
+    assert any(len(p) for _, _, _, p in ref.appends), "the workload must exercise copy-on-write"
+    for layer in range(wl.num_layers):
+        for which in "kv":
+            dev = device_pool_logical(run, which, layer)
+            expect = np.stack([ref.store.block(which, layer, p) for p in range(wl.num_blocks)])
+            assert np.array_equal(dev, expect), f"{which} pool of layer {layer} differs"
+
+
+def test_negative_and_out_of_range_slots_are_skipped():
+    announce("reshape_and_cache skips slots < 0 and >= N*B")
+    wl = small_fork_workload(draws.BF16, 16, 128, num_blocks=8)
+    run = GpuRun(wl, fill=np.int16(0x1111))
+    before = run.pool.raw("k").clone()
+    n = 4
+    k = torch.full((n, 2, 128), 7, dtype=torch.int16, device="cuda")
+    slots = torch.tensor([-1, 8 * 16, 8 * 16 + 5, -100], dtype=torch.int64, device="cuda")
+    run.pool.cache(0, k, k, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(before, run.pool.raw("k"))
+
+
+# ---------------------------------------------------------------------------
+# attention on the workloads
+# ---------------------------------------------------------------------------
+
+def compare_all_decodes(run, ref, layers=None):
+    wl = run.wl
+    for i in range(len(ref.decodes)):
+        for layer in (layers or range(wl.num_layers)):
+            got = run.decode_outputs[i][layer].double().cpu().numpy()
+            check_outputs(got, ref.attention(i, layer), wl.dtype, f"decode {i} layer {layer}")
+
+
+def test_config1_tiny_fp32():
+    announce("config 1: tiny fp32, B=4, lengths 5/7/9, generic kernel, NaN background")
+    wl = workloads.tiny_fp32()
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()  # 0xFFFFFFFF is a NaN: unwritten slots must never count
+    compare_all_decodes(run, ref)
+
+
+@pytest.mark.parametrize("kernel", [B.KV_KERNEL_GENERIC, B.KV_KERNEL_MFMA])
+@pytest.mark.parametrize("dtype", [draws.BF16, draws.F32])
+def test_small_fork_workload(kernel, dtype):
+    if kernel == B.KV_KERNEL_MFMA and dtype == draws.F32:
+        pytest.skip("the matrix-core kernel is bf16 only")
+    announce(f"small fork workload with CoW: {dtype}, kernel {kernel}")
+    wl = small_fork_workload(dtype, 16, 128)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1, opts=B.attention_options(kernel=kernel)).run()
+    compare_all_decodes(run, ref)
+
+
+def ragged_workload(hq, hkv, d, lengths, seed=31, num_blocks=None, dtype=draws.BF16):
+    seqs = tuple(range(len(lengths)))
+    ops = [("add", s) for s in seqs]
+    ops.append(("append", seqs, tuple(lengths)))
+    ops.append(("decode", seqs))
+    need = sum(-(-n // 16) for n in lengths)
+    return workloads.Workload("ragged", seed, dtype, 1, hq, hkv, d, 16, num_blocks or need + 7, ops)
+
+
+RAGGED = [1, 2, 15, 16, 17, 31, 100, 257, 511, 512, 513, 1000, 2049]
+
+
+@pytest.mark.parametrize("kernel", [B.KV_KERNEL_MFMA, B.KV_KERNEL_GENERIC])
+@pytest.mark.parametrize("partition", [0, 16, 48, 256, 512, 4096])
+def test_ragged_lengths_and_partitions(kernel, partition):
+    announce(f"ragged lengths {RAGGED}, kernel {kernel}, partition {partition}")
+    wl = ragged_workload(32, 8, 128, RAGGED)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1,
+                 opts=B.attention_options(partition_tokens=partition, kernel=kernel)).run()
+    compare_all_decodes(run, ref)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (64, 8, 128), (48, 3, 128), (16, 1, 128),
+                                      (32, 8, 64), (16, 4, 256), (12, 4, 64)])
+def test_head_shapes(hq, hkv, d):
+    announce(f"head shapes Hq={hq} Hkv={hkv} d={d}, both kernels")
+    wl = ragged_workload(hq, hkv, d, [1, 7, 16, 33, 300, 700])
+    ref = OracleReplay(wl).run()
+    for kernel in (B.KV_KERNEL_MFMA, B.KV_KERNEL_GENERIC):
+        run = GpuRun(wl, ref=ref, fill=-1, opts=B.attention_options(partition_tokens=128, kernel=kernel)).run()
+        compare_all_decodes(run, ref)
+
+
+def test_config2_qwen_full():
+    announce("config 2: 37 x 2304 tokens, bf16, default launch")
+    wl = workloads.qwen_independent()
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref).run()
+    compare_all_decodes(run, ref)
+
+
+def test_config3_shared_prefix_full():
+    announce("config 3: 16 x 8448 tokens sharing 6144, bf16, default launch")
+    wl = workloads.shared_prefix()
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref).run()
+    compare_all_decodes(run, ref)
+    # forks share before divergence: the prefix blocks of all 16 tables coincide
+    tables = run.decodes[0]["tables"]
+    assert (tables[:, :384] == tables[0, :384]).all()
+
+
+def test_config4_long_context_sampled():
+    announce("config 4: 12 x 131072 tokens, Hq=64, split-K 512; sequences 0, 5, 11 checked")
+    wl = workloads.gqa70b_128k()
+    sample = [0, 5, 11]
+    ref = OracleReplay(wl, writers=sample).run()
+    run = GpuRun(wl, ref=ref, writers=sample, opts=B.attention_options(partition_tokens=512)).run()
+    got = run.decode_outputs[0][0].double().cpu().numpy()
+    expect = ref.attention(0, 0, rows=sample)
+    check_outputs(got[sample], expect, wl.dtype, "config 4 sampled")
+
+
+def test_agentic_fork_sampled():
+    announce("fork workload: 4 roots x 32769, 16 forks each, 20 steps, layers {0, 1} of 36 written")
+    wl = workloads.agentic_fork(steps=20, layers=36)
+    sample_seqs = [0, 1, 15, 16, 47, 63]
+    writers = set(sample_seqs) | {0, 16, 32, 48}
+    layers = [0, 1]
+    ref = OracleReplay(wl, layers=layers, writers=writers).run()
+    run = GpuRun(wl, ref=ref, layers=layers, writers=writers).run()
+    for i in (0, 1, 15, 16, 19):
+        for layer in layers:
+            got = run.decode_outputs[i][layer].double().cpu().numpy()[sample_seqs]
+            check_outputs(got, ref.attention(i, layer, rows=sample_seqs), wl.dtype, f"step {i} layer {layer}")
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def test_zero_length_context_gives_zero_row_and_bad_entry_gives_nan():
+    announce("context_len 0 -> zero row; out-of-range table entry -> NaN row; empty batch")
+    wl = ragged_workload(32, 8, 128, [40, 40, 40])
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()
+    tables = torch.from_numpy(run.decodes[0]["tables"]).cuda()
+    lens = torch.from_numpy(run.decodes[0]["lengths"]).cuda()
+    lens[1] = 0
+    tables[2, 1] = wl.num_blocks + 5
+    for kernel in (B.KV_KERNEL_MFMA, B.KV_KERNEL_GENERIC):
+        for part in (16, 0):
+            out = run.decode(0, 0, tables, lens, 3, opts=B.attention_options(partition_tokens=part, kernel=kernel))
+            o = out.double().cpu().numpy()
+            check_outputs(o[:1], ref.attention(0, 0, rows=[0]), wl.dtype, "row 0 unaffected")
+            assert (o[1] == 0).all()
+            assert np.isnan(o[2]).all()
+    # an empty batch is a no-op
+    empty_t = torch.zeros((0, 4), dtype=torch.int32, device="cuda")
+    empty_l = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    q = torch.zeros((0, 32, 128), dtype=torch.int16, device="cuda")
+    run.pool.decode(0, q, q.clone(), empty_t, empty_l, 32)
+    torch.cuda.synchronize()
+
+
+def test_single_token_context_returns_its_value():
+    announce("n = 1: the output equals v_0 rounded to bf16")
+    wl = ragged_workload(32, 8, 128, [1, 1])
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()
+    got = run.decode_outputs[0][0].cpu().numpy()
+    for s in range(2):
+        _, vb = ref.store.gather(0, ref.decodes[0]["tables"][s], 1)
+        v = draws.bits_to_f64(vb, wl.dtype)[0]  # [Hkv, d]
+        expect = np.repeat(v, 4, axis=0)
+        assert np.array_equal(got[s].astype(np.float64), expect)
+
+
+def test_split_and_single_pass_agree():
+    announce("split-K partitions vs one partition vs generic kernel on 2049 tokens")
+    wl = ragged_workload(32, 8, 128, [2049, 1500])
+    ref = OracleReplay(wl).run()
+    outs = []
+    for kernel, part in ((B.KV_KERNEL_MFMA, 4096), (B.KV_KERNEL_MFMA, 64), (B.KV_KERNEL_GENERIC, 4096),
+                         (B.KV_KERNEL_GENERIC, 32)):
+        run = GpuRun(wl, ref=ref, opts=B.attention_options(partition_tokens=part, kernel=kernel)).run()
+        outs.append(run.decode_outputs[0][0].double().cpu().numpy())
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 2 * BF16_ABS
+
+
+def test_invalid_arguments_are_rejected():
+    announce("argument validation of the device entry points")
+    wl = ragged_workload(32, 8, 128, [20])
+    run = GpuRun(wl).run()
+    t = torch.from_numpy(run.decodes[0]["tables"]).cuda()
+    l_ = torch.from_numpy(run.decodes[0]["lengths"]).cuda()
+    q = torch.zeros((1, 32, 128), dtype=torch.int16, device="cuda")
+    with pytest.raises(B.KVError):
+        run.pool.decode(0, q, q.clone(), t, l_, 30)  # Hq not a multiple of Hkv
+    with pytest.raises(B.KVError):
+        run.pool.decode(3, q, q.clone(), t, l_, 32)  # layer out of range
+    with pytest.raises(B.KVError):
+        run.pool.decode(0, q, q.clone(), t, l_, 32, opts=B.attention_options(partition_tokens=24))
+    with pytest.raises(B.KVError):  # needs a workspace
+        run.pool.decode(0, q, q.clone(), t, l_, 32, opts=B.attention_options(partition_tokens=16))
+    with pytest.raises(B.KVError):
+        run.pool.decode(0, q, q.clone(), t, l_, 8 * 17)  # G = 17
+    f32 = small_fork_workload(draws.F32, 4, 64)
+    r2 = GpuRun(f32)
+    with pytest.raises(B.KVError) as e:
+        r2.pool.decode(0, torch.zeros((1, 4, 64), dtype=torch.int32, device="cuda"),
+                       torch.zeros((1, 4, 64), dtype=torch.int32, device="cuda"),
+                       torch.zeros((1, 2), dtype=torch.int32, device="cuda"),
+                       torch.ones((1,), dtype=torch.int32, device="cuda"), 4,
+                       opts=B.attention_options(kernel=B.KV_KERNEL_MFMA))
+    assert e.value.status == B.KV_ERR_UNSUPPORTED
+
+
+def test_release_waits_for_stream_event():
+    announce("kv_seq_release defers reuse until the stream's work completes")
+    wl = ragged_workload(32, 8, 128, [64, 64], num_blocks=8)
+    run = GpuRun(wl).run()
+    stream = torch.cuda.current_stream()
+    run.pool.release(0, stream)
+    st = run.pool.stats()
+    assert st["n_pending"] + st["n_free"] == 4 and st["n_allocated"] == 4
+    run.pool.reclaim(wait=True)
+    st = run.pool.stats()
+    assert st["n_pending"] == 0 and st["n_free"] == 4
+    run.pool.check()
