@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Throughput of the paged decode-attention hot path on one MI355X.
+
+A step is one decode step of the workload through the whole path:
+  host:   kv_append_slots (one token per sequence; copy-on-write pairs),
+          kv_get_block_tables, upload of slot mapping and tables;
+  device: copy_blocks (only when the allocator asked for copies),
+          then for every layer reshape_and_cache + paged_attention_decode
+          (partition kernel + log-sum-exp merge).
+Inputs (queries, new K/V rows) for every timed step are resident in HBM
+before the timed region; the pool is filled once, before warm-up.
+
+Workloads (synthetic, seeded; see synth/workloads.py):
+  2  Qwen3-8B-shaped layer: 37 sequences x 2304 tokens, Hq=32, Hkv=8, d=128,
+     B=16, bf16; 4 layer buffers rotated so the 256 MB last-level cache
+     cannot hold the working set (1.4 GB per step).       (default)
+  3  16 x 8448 tokens sharing a 6144-token prefix, same shapes, 4 layers.
+  4  70B-GQA-shaped layer: 12 x 131072 tokens, Hq=64, split-K 512.
+  5  agentic fork: 64 sequences (4 roots x 16 forks) x ~33K tokens, 36 layers.
+
+Prints one JSON line (rank 0, one GPU).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, public specification
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--layers", type=int, default=0, help="layer buffers (0 = workload default)")
+    ap.add_argument("--partition", type=int, default=-1, help="partition tokens (-1 = workload default)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "generic"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--seed", type=int, default=0, help="0 = the workload's seed")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU form in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from pagedattention_decode_amd import binding as B
+    from pagedattention_decode_amd.pool import PagedKVPool
+    from synth import draws, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    base = workloads.get_workload(args.config) if args.config != 5 else workloads.agentic_fork(steps=1)
+    default_layers = {2: 4, 3: 4, 4: 1, 5: 36}[args.config]
+    L = args.layers or default_layers
+    seed = args.seed or base.seed
+    partition = base.partition_tokens if args.partition < 0 else args.partition
+    kernel = {"auto": B.KV_KERNEL_AUTO, "mfma": B.KV_KERNEL_MFMA, "generic": B.KV_KERNEL_GENERIC}[args.kernel]
+    opts = B.attention_options(partition_tokens=partition, kernel=kernel)
+    Hq, Hkv, d, Bs = base.num_q_heads, base.num_kv_heads, base.head_dim, base.block_size
+
+    # setup = everything before the per-step ops; a step appends one token per
+    # decoding sequence when the workload does so, then decodes
+    ops = base.ops
+    first_step = next(i for i, op in enumerate(ops)
+                      if op[0] == "decode" or (op[0] == "append" and set(op[2]) == {1}))
+    setup_ops = ops[:first_step]
+    step_ops = ops[first_step:]
+    decode_seqs = list(next(op for op in step_ops if op[0] == "decode")[1])
+    step_appends = any(op[0] == "append" for op in step_ops)
+    S = len(decode_seqs)
+
+    pool = PagedKVPool(L, base.num_blocks, Bs, Hkv, d, "bf16", free_order=draws.free_order(seed, base.num_blocks))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def randn_bf16(*shape):
+        return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    # ---- fill the pool (untimed) -----------------------------------------
+    t_fill = time.time()
+    for op in setup_ops:
+        if op[0] == "add":
+            pool.add(op[1])
+        elif op[0] == "fork":
+            pool.fork(op[1], op[2])
+        elif op[0] == "append":
+            slots, pairs = pool.append(op[1], op[2])
+            assert len(pairs) == 0
+            chunk = 1 << 17
+            for at in range(0, len(slots), chunk):
+                d_slots = torch.from_numpy(slots[at:at + chunk]).to(dev)
+                n = d_slots.numel()
+                for layer in range(L):
+                    pool.cache(layer, randn_bf16(n, Hkv, d), randn_bf16(n, Hkv, d), d_slots)
+    torch.cuda.synchronize()
+    t_fill = time.time() - t_fill
+
+    total_steps = args.warmup + args.steps
+    lens0 = np.array([pool.info(s)[0] for s in decode_seqs])
+    max_blocks = int(math.ceil((lens0.max() + (total_steps if step_appends else 0)) / Bs)) + 1
+    q_in = [[randn_bf16(S, Hq, d) for _ in range(L)] for _ in range(total_steps)]
+    kv_in = [[(randn_bf16(S, Hkv, d), randn_bf16(S, Hkv, d)) for _ in range(L)] for _ in range(total_steps)] \
+        if step_appends else None
+    out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
+    ws_bytes = pool.workspace_bytes(S, Hq, max_blocks, opts)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device=dev)
+    d_lens = torch.empty((S,), dtype=torch.int32, device=dev)
+    d_slots = torch.empty((S,), dtype=torch.int64, device=dev)
+    ring = 4
+    h_tables = [torch.empty((S, max_blocks), dtype=torch.int32).pin_memory() for _ in range(ring)]
+    h_lens = [torch.empty((S,), dtype=torch.int32).pin_memory() for _ in range(ring)]
+    h_slots = [torch.empty((S,), dtype=torch.int64).pin_memory() for _ in range(ring)]
+    ring_ev = [None] * ring
+    seq_arr = np.asarray(decode_seqs, np.int64)
+    stream = torch.cuda.current_stream()
+
+    attn_ev = []  # (start, end) HIP events around every paged_attention_decode
+    logical_bytes = [0]
+    n_copies = [0]
+
+    def step(i, timed):
+        slot = i % ring
+        if ring_ev[slot] is not None:
+            ring_ev[slot].synchronize()
+        pairs = np.zeros((0, 2), np.int64)
+        if step_appends:
+            slots, pairs = pool.append(seq_arr, None)
+            h_slots[slot].numpy()[:] = slots
+            d_slots.copy_(h_slots[slot], non_blocking=True)
+        tables, lens = B.kv_get_block_tables(pool.handle, seq_arr, max_blocks)
+        h_tables[slot].numpy()[:] = tables
+        h_lens[slot].numpy()[:] = lens
+        d_tables.copy_(h_tables[slot], non_blocking=True)
+        d_lens.copy_(h_lens[slot], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        ring_ev[slot] = ev
+        if len(pairs):
+            pool.copy(torch.from_numpy(pairs).to(dev, non_blocking=False))
+            n_copies[0] += len(pairs)
+        for layer in range(L):
+            if step_appends:
+                k_new, v_new = kv_in[i][layer]
+                pool.cache(layer, k_new, v_new, d_slots)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            pool.decode(layer, q_in[i][layer], out, d_tables, d_lens, Hq, opts, ws)
+            if timed:
+                e1.record(stream)
+                attn_ev.append((e0, e1))
+                logical_bytes[0] += int(lens.astype(np.int64).sum()) * 2 * Hkv * d * 2
+        return lens
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    lens_hist = []
+    for i in range(args.warmup, total_steps):
+        lens_hist.append(step(i, True))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    ms_step = wall / args.steps * 1e3
+
+    attn_ms = [a.elapsed_time(b) for a, b in attn_ev]
+    attn_avg_s = float(np.mean(attn_ms)) / 1e3
+    n_launch = len(attn_ms)
+    kv_bytes_per_launch = logical_bytes[0] / n_launch
+    blocks_per_launch = float(np.mean([np.ceil(l / Bs).sum() for l in lens_hist]))
+    ideal_per_launch = kv_bytes_per_launch + 2 * S * Hq * d * 2 + 4 * blocks_per_launch
+    achieved = ideal_per_launch / attn_avg_s / 1e9
+    value = logical_bytes[0] / wall / 1e9
+    tok_per_s_layer = S * L * args.steps / wall
+
+    # unique bytes (shared blocks counted once) per launch, for the sharing workloads
+    tables, lens = B.kv_get_block_tables(pool.handle, seq_arr, max_blocks)
+    uniq = set()
+    for r in range(S):
+        uniq.update(tables[r, :int(math.ceil(lens[r] / Bs))].tolist())
+    unique_kv_bytes = len(uniq) * Bs * 2 * Hkv * d * 2
+
+    result = {
+        "metric": "paged-decode KV GB/s (% of HBM peak) + attention tokens/s per layer",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": base.name,
+            "description": base.description,
+            "layers_per_step": L,
+            "sequences": S,
+            "context_tokens_first_step": int(lens_hist[0].max()) if lens_hist else None,
+            "partition_tokens": partition or "auto",
+            "kernel": args.kernel,
+            "step": (f"append + {L} x (reshape_and_cache + paged_attention_decode)" if step_appends
+                     else f"{L} x paged_attention_decode"),
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "attn_tokens_per_s_per_layer": round(tok_per_s_layer, 1),
+        "attn_kernel_tokens_per_s_per_layer": round(S / attn_avg_s, 1),
+        "attn_call_us": round(attn_avg_s * 1e6, 2),
+        "unique_kv_bytes_per_launch": unique_kv_bytes,
+        "cow_copies": n_copies[0],
+        "fill_seconds": round(t_fill, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "paged_attention_decode (partition + merge kernels)",
+            "algorithmic_bytes_per_launch": int(ideal_per_launch),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args):
+    """The fp64 oracle timed on the host on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.runner import OracleReplay
+    from synth import workloads
+
+    cores = len(os.sched_getaffinity(0))
+    cfg = args.config
+    if cfg == 2:
+        wl = workloads.qwen_independent()
+        layers, writers = None, None
+        sample = "Qwen3-8B-shaped layer: the oracle's decode of all 37 sequences x 2304 tokens, one layer"
+    elif cfg == 3:
+        wl = workloads.shared_prefix()
+        layers, writers = None, None
+        sample = "shared-prefix layer: the oracle's decode of all 16 sequences x 8448 tokens, one layer"
+    elif cfg == 4:
+        wl = workloads.gqa70b_128k()
+        layers, writers = None, {0}
+        sample = "70B-GQA layer: the oracle's decode of sequence 0 (131072 tokens, 64 heads)"
+    else:
+        wl = workloads.agentic_fork(steps=1, layers=1)
+        layers, writers = [0], {0, 1}
+        sample = "fork workload: the oracle's decode of sequences 0 and 1 (32770 tokens), layer 0, step 0"
+    ref = OracleReplay(wl, layers=layers, writers=writers).run()
+    rows = list(range(len(ref.decodes[0]["seq_ids"]))) if writers is None else sorted(writers)
+    kv_per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    bytes_one = sum(ref.decodes[0]["lengths"][r] for r in rows) * kv_per_tok
+    reps = 0
+    c0 = time.process_time()
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while True:
+            ref.attention(0, 0, rows=rows)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return {
+        "value": round(bytes_one * reps / wall / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{sample}; repeated {reps} times in {wall:.1f} s",
+        "tokens_per_s_per_layer": round(len(rows) * reps / wall, 3),
+        "cpu_utilisation": round(cpu / wall, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

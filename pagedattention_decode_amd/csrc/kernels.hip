@@ -23,6 +23,7 @@
 // every wave-wide load instruction reads 1 KiB of contiguous memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <string>
 
@@ -393,39 +394,313 @@ __device__ __forceinline__ void load_block(kv_regs<D>& r, const uint4* kt, const
   for (int i = 0; i < D / 32; ++i) r.v[i] = vt[i * 64 + lane];
 }
 
-template <int D, int W>
-__global__ void __launch_bounds__(W * 64) attn_mfma_kernel(attn_args a) {
-  extern __shared__ float smem[];  // [W][G][D] outputs, then [W][G] m and l
-  work_item w;
-  if (!decode_work(a, w)) return;
-  const int G = a.n_q_heads / a.n_kv_heads;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int hl = lane & 15;   // head column owned by this lane
-  const int quad = lane >> 4; // 4-token group / 8-dim group of this lane
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-  // Q^T operand: lane holds q[head hl][kk*32 + quad*8 .. +8]
-  bf16x8_t qop[D / 32];
-  {
-    const uint16_t* qg = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<int64_t>(w.seq) * a.n_q_heads + w.kv_head * G + hl) * D;
+// The running maximum m is only moved when a block's maximum exceeds it by more
+// than this many binary orders of magnitude; otherwise the block is weighted
+// against the stale m (weights up to 2^kRescaleSlack).  Numerator and
+// denominator use the same m, so the result is unchanged; the rescale of the
+// accumulators is skipped for most blocks.
+constexpr float kRescaleSlack = 8.f;
+
+// One 16-token block: scores, online-softmax update, weighted sum of values.
+// `valid` (wave uniform) is the number of in-range slots of the block.
+template <int D>
+__device__ __forceinline__ void attend_block(kv_regs<D>& cur, const bf16x8_t* qop, int valid, int quad,
+                                             float scale_log2, f32x4_t* o, float& m_run, float& l_lane) {
+  // S^T = K . Q^T
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (hl < G) raw = *reinterpret_cast<const uint4*>(qg + kk * 32 + quad * 8);
-      qop[kk] = __builtin_bit_cast(bf16x8_t, raw);
+  for (int kk = 0; kk < D / 32; ++kk)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk], s, 0, 0, 0);
+
+  // online softmax; the lane holds tokens quad*4 + i of its head
+  float sv[4];
+  float mb = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = (quad * 4 + i < valid) ? s[i] * scale_log2 : -INFINITY;
+    mb = fmaxf(mb, sv[i]);
+  }
+  mb = fmaxf(mb, __shfl_xor(mb, 16));
+  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  const bool grow = mb > m_run + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch
+    const float m_new = grow ? mb : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf, 1 when kept
+    l_lane *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
+    m_run = m_new;
+  }
+  float pv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pv[i] = (sv[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_run);
+  // P^T operand in bf16 (round to nearest even); the denominator sums the
+  // rounded weights so that the weights applied to V are exactly normalised
+  const bf16x2_t p01 = __builtin_convertvector((f32x2_t{pv[0], pv[1]}), bf16x2_t);
+  const bf16x2_t p23 = __builtin_convertvector((f32x2_t{pv[2], pv[3]}), bf16x2_t);
+  const uint32_t w01 = __builtin_bit_cast(uint32_t, p01);
+  const uint32_t w23 = __builtin_bit_cast(uint32_t, p23);
+  l_lane += (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xffff0000u)) +
+            (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xffff0000u));
+  const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(w01, w23));
+
+  // zero the values of out-of-range slots (their memory may hold anything)
+  if (valid < 16) {
+#pragma unroll
+    for (int pp = 0; pp < D / 32; ++pp) {
+      uint32_t* wv = reinterpret_cast<uint32_t*>(&cur.v[pp]);
+      // 16 bytes = [half 0: 4 slots][half 1: 4 slots], 2 slots per dword
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        const int slot0 = quad * 4 + (dw & 1) * 2;
+        uint32_t mask = 0;
+        if (slot0 < valid) mask |= 0x0000ffffu;
+        if (slot0 + 1 < valid) mask |= 0xffff0000u;
+        wv[dw] &= mask;
+      }
     }
   }
 
-  const int32_t* table = a.tables + static_cast<int64_t>(w.seq) * a.max_blocks;
-  const int blk_begin = w.tok_begin / 16;
-  const int blk_end = (w.tok_end + 15) / 16;
-  const int n_mine = blk_begin + wave < blk_end ? (blk_end - blk_begin - wave + W - 1) / W : 0;
+  // O^T += V^T . P^T
+#pragma unroll
+  for (int pp = 0; pp < D / 32; ++pp) {
+    const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
+    o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop, o[2 * pp],
+                                                          0, 0, 0);
+    o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[1]), pop,
+                                                              o[2 * pp + 1], 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K over partitions, one contiguous run of partitions per wave.
+//
+// Units are (sequence, kv head) pairs in sequence-major order; every unit is
+// cut into partitions of `partition_tokens` tokens.  The partitions of the
+// whole batch, laid end to end, are divided evenly among the waves of a
+// persistent grid: wave w takes partitions [w*P/W, (w+1)*P/W).  A wave walks
+// the 16-token blocks of its partitions in order, folding consecutive blocks
+// (and consecutive partitions) of one unit into one running (m, l, O) state,
+// and writes a result only where its run of a unit ends: the final row when
+// the unit lies entirely in this wave, else the partial (m, l, O) in slot
+// (w + unit), which the merge kernel folds with the same recurrences.  The
+// balance is exact for any mix of lengths, and about W + units partials are
+// written in total, so the stream of K/V reads is not interleaved with
+// per-partition writes.
+// ---------------------------------------------------------------------------
+
+constexpr int kSkWaves = 4;     // waves per workgroup
+constexpr int kSkQUnits = 4;    // at most this many units per wave have staged queries
+
+struct sk_args {
+  const void* q;
+  void* out;
+  const void* k_layer;
+  const void* v_layer;
+  float* part_m;   // [slots][G]
+  float* part_l;   // [slots][G]
+  float* part_o;   // [slots][G][D]
+  int32_t* cum_parts;  // [n_seqs + 1] partitions before each sequence (written by group 0)
+  int n_seqs, max_blocks, n_q_heads, n_kv_heads, num_blocks, part_blocks, n_waves;
+  int q_units;  // units per wave whose queries are staged in LDS (<= kSkQUnits)
+  float scale_log2;
+};
+
+__device__ __forceinline__ int blocks_of(const int32_t* __restrict__ ctx_lens, int s, int cap) {
+  const int n = min(ctx_lens[s], cap);
+  return n > 0 ? (n + 15) >> 4 : 0;
+}
+
+// Exclusive prefix sums, over sequences, of blocks (cum_b) and partitions
+// (cum_p); a workgroup-wide scan in LDS.
+__device__ __forceinline__ void sk_prefix(const sk_args& a, const int32_t* __restrict__ ctx_lens, int* cum_b,
+                                          int* cum_p) {
+  __shared__ int wsum_b[kSkWaves], wsum_p[kSkWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cap = a.max_blocks * 16;
+  int carry_b = 0, carry_p = 0;
+  for (int base = 0; base < a.n_seqs; base += kSkWaves * 64) {
+    const int s = base + tid;
+    const int nb = s < a.n_seqs ? blocks_of(ctx_lens, s, cap) : 0;
+    const int np = (nb + a.part_blocks - 1) / a.part_blocks;
+    int ib = nb, ip = np;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int yb = __shfl_up(ib, off), yp = __shfl_up(ip, off);
+      if (lane >= off) {
+        ib += yb;
+        ip += yp;
+      }
+    }
+    if (lane == 63) {
+      wsum_b[wv] = ib;
+      wsum_p[wv] = ip;
+    }
+    __syncthreads();
+    int before_b = carry_b, before_p = carry_p;
+    for (int i = 0; i < wv; ++i) {
+      before_b += wsum_b[i];
+      before_p += wsum_p[i];
+    }
+    if (s < a.n_seqs) {
+      cum_b[s] = before_b + ib - nb;
+      cum_p[s] = before_p + ip - np;
+    }
+    for (int i = 0; i < kSkWaves; ++i) {
+      carry_b += wsum_b[i];
+      carry_p += wsum_p[i];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    cum_b[a.n_seqs] = carry_b;
+    cum_p[a.n_seqs] = carry_p;
+  }
+  __syncthreads();
+}
+
+// Position of a wave's run in (sequence, kv head, block) terms.  All fields
+// are wave uniform.
+struct sk_cursor {
+  int seq, kvh, j, nb, n;
+};
+
+template <int D, int STAGES, int WAVES_PER_SIMD>
+__global__ void __launch_bounds__(kSkWaves * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD)))
+attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ tables) {
+  extern __shared__ __align__(16) int sk_smem[];
+  int* cum_b = sk_smem;                 // n_seqs + 1
+  int* cum_p = sk_smem + a.n_seqs + 1;  // n_seqs + 1
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int Hkv = a.n_kv_heads;
+  uint16_t* q_s = reinterpret_cast<uint16_t*>(sk_smem + ((2 * (a.n_seqs + 1) + 3) & ~3));  // [waves][q_units][G][D]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = (lane & 15) % G;  // query head (within the group) of this lane's column
+  const int quad = lane >> 4;      // 4-token group / 8-dim group of this lane
+  const int cap = a.max_blocks * 16;
+
+  sk_prefix(a, ctx_lens, cum_b, cum_p);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= a.n_seqs; i += kSkWaves * 64) a.cum_parts[i] = cum_p[i];
+  // prefix entries are read at wave-uniform addresses; keep them scalar so that
+  // every branch below is a scalar branch
+  auto cb = [&](int s) { return __builtin_amdgcn_readfirstlane(cum_b[s]); };
+  auto cp = [&](int s) { return __builtin_amdgcn_readfirstlane(cum_p[s]); };
+
+  // this wave's run of partitions
+  const int64_t total_parts = static_cast<int64_t>(Hkv) * cp(a.n_seqs);
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * kSkWaves + wave;
+  const int64_t p_begin = wid * total_parts / a.n_waves;
+  const int64_t p_end = (wid + 1) * total_parts / a.n_waves;
+  if (p_begin >= p_end) return;
+
+  // partition index -> (sequence, kv head, first block)
+  auto locate = [&](int64_t pp, sk_cursor& c) {
+    int lo = 0, hi = a.n_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (static_cast<int64_t>(Hkv) * cp(mid) <= pp) lo = mid; else hi = mid - 1;
+    }
+    c.seq = lo;
+    const int np = cp(lo + 1) - cp(lo);
+    const int64_t r = pp - static_cast<int64_t>(Hkv) * cp(lo);
+    c.kvh = static_cast<int>(r / np);
+    c.j = static_cast<int>(r % np) * a.part_blocks;
+    c.nb = cb(lo + 1) - cb(lo);
+    c.n = min(ctx_lens[lo], cap);
+  };
+  sk_cursor first, last;
+  locate(p_begin, first);
+  locate(p_end - 1, last);
+  last.j = min(last.j + a.part_blocks, last.nb) - 1;
+  auto flat = [&](const sk_cursor& c) -> int64_t {
+    return static_cast<int64_t>(Hkv) * cb(c.seq) + static_cast<int64_t>(c.kvh) * c.nb + c.j;
+  };
+  const int n_blk = static_cast<int>(flat(last) - flat(first)) + 1;  // blocks of this run
+
+  // step a cursor to the next block of the run
+  auto advance = [&](sk_cursor& c) {
+    if (++c.j < c.nb) return;
+    c.j = 0;
+    if (++c.kvh < Hkv) return;
+    c.kvh = 0;
+    do {
+      ++c.seq;
+    } while (c.seq < a.n_seqs - 1 && cb(c.seq + 1) == cb(c.seq));
+    c.nb = cb(c.seq + 1) - cb(c.seq);
+    c.n = min(ctx_lens[c.seq], cap);
+  };
+
   const uint4* kpool = static_cast<const uint4*>(a.k_layer);
   const uint4* vpool = static_cast<const uint4*>(a.v_layer);
   constexpr int kTileVec = 16 * D * 2 / 16;  // 16-byte vectors per tile
-  const int64_t head_off = static_cast<int64_t>(w.kv_head) * kTileVec;
-  const int64_t blk_stride = static_cast<int64_t>(a.n_kv_heads) * kTileVec;
+
+  // load side: the block STAGES ahead of consumption (the last one repeats
+  // past the end of the run and is served by the L2)
+  sk_cursor ld = first;
+  int ld_k = 0;
+  int phys_ring[STAGES];
+  auto issue = [&](kv_regs<D>& buf, int u) {
+    const int phys = tables[static_cast<int64_t>(ld.seq) * a.max_blocks + ld.j];
+    phys_ring[u] = phys;
+    const int p = (phys < 0 || phys >= a.num_blocks) ? 0 : phys;  // never dereferenced out of range
+    const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * kTileVec;
+    load_block<D>(buf, kpool + t, vpool + t, lane);
+    if (++ld_k < n_blk) advance(ld);
+  };
+
+  kv_regs<D> buf[STAGES];
+#pragma unroll
+  for (int u = 0; u < STAGES; ++u) issue(buf[u], u);
+
+  // stage the queries of the first q_units units of the run in LDS (issued
+  // after the first ring loads, so that both wait out one memory latency)
+  uint16_t* q_wave = q_s + static_cast<int64_t>(wave) * a.q_units * G * D;
+  {
+    sk_cursor c = first;
+    for (int i = 0; i < a.q_units; ++i) {
+      const uint16_t* qg = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<int64_t>(c.seq) * a.n_q_heads + c.kvh * G) * D;
+      for (int e = lane * 8; e < G * D; e += 64 * 8)
+        *reinterpret_cast<uint4*>(q_wave + i * G * D + e) = *reinterpret_cast<const uint4*>(qg + e);
+      if (c.seq == last.seq && c.kvh == last.kvh) break;
+      // next unit
+      c.j = c.nb - 1;
+      advance(c);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // consume side
+  sk_cursor cs = first;
+  int unit_idx = 0;   // index of the current unit within the run
+  int seg_j0 = first.j;
+  bf16x8_t qop[D / 32];
+  // queries of the idx-th unit of the run: always read from LDS (a unit past
+  // the staged ones is first copied into the slot of an earlier, finished
+  // unit), so the query registers never wait on global loads in the loop
+  auto fetch_q = [&](int idx) {
+    const int slot = idx % a.q_units;
+    if (idx >= a.q_units) {
+      const uint16_t* qg = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<int64_t>(cs.seq) * a.n_q_heads + cs.kvh * G) * D;
+      for (int e = lane * 8; e < G * D; e += 64 * 8)
+        *reinterpret_cast<uint4*>(q_wave + slot * G * D + e) = *reinterpret_cast<const uint4*>(qg + e);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      qop[kk] = *reinterpret_cast<const bf16x8_t*>(q_wave + slot * G * D + hg * D + kk * 32 + quad * 8);
+  };
+  fetch_q(0);
 
   f32x4_t o[D / 16];
 #pragma unroll
@@ -433,145 +708,169 @@ __global__ void __launch_bounds__(W * 64) attn_mfma_kernel(attn_args a) {
   float m_run = -INFINITY, l_lane = 0.f;
   bool poisoned = false;
 
-  // The physical ids of this wave's blocks, 64 at a time, one per lane.
-  int tab_vec = 0;
-  auto fetch_table = [&](int first) {
-    const int idx = first + lane;
-    const int j = blk_begin + wave + idx * W;
-    tab_vec = (idx < n_mine) ? table[j] : 0;
+  // writes the result of the current unit's run and resets the state
+  auto finish = [&]() {
+    float l = l_lane + __shfl_xor(l_lane, 16);
+    l += __shfl_xor(l, 32);
+    const int h = cs.kvh * G + hg;
+    const float nan = __builtin_nanf("");
+    if (seg_j0 == 0 && cs.j == cs.nb - 1) {  // the whole unit: final row
+      const float inv = poisoned ? 0.f : 1.f / l;
+      uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(cs.seq) * a.n_q_heads + h) * D;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = poisoned ? nan : o[nt][i] * inv;
+        *reinterpret_cast<uint2*>(out + nt * 16 + quad * 4) =
+            make_uint2(static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+                       static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16));
+      }
+    } else {
+      const int64_t slot = wid + static_cast<int64_t>(cs.seq) * Hkv + cs.kvh;
+      const int64_t row = slot * G + hg;
+      float* po = a.part_o + row * D;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt)
+        *reinterpret_cast<float4*>(po + nt * 16 + quad * 4) =
+            poisoned ? make_float4(nan, nan, nan, nan) : make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
+      a.part_m[row] = poisoned ? nan : m_run;
+      a.part_l[row] = poisoned ? nan : l;
+    }
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_lane = 0.f;
+    poisoned = false;
   };
-  auto phys_of = [&](int k) -> int {
-    return __builtin_amdgcn_readlane(tab_vec, k & 63);
-  };
 
-  kv_regs<D> cur, nxt;
-  if (n_mine > 0) {
-    fetch_table(0);
-    int p = phys_of(0);
-    if (p < 0 || p >= a.num_blocks) p = 0;
-    const int64_t t = p * blk_stride + head_off;
-    load_block<D>(cur, kpool + t, vpool + t, lane);
-  }
-  for (int k = 0; k < n_mine; ++k) {
-    int p = phys_of(k);
-    const bool bad = p < 0 || p >= a.num_blocks;
-    poisoned |= bad;
-    if (k + 1 < n_mine) {
-      if (((k + 1) & 63) == 0) fetch_table(k + 1);
-      int pn = phys_of(k + 1);
-      if (pn < 0 || pn >= a.num_blocks) pn = 0;
-      const int64_t t = pn * blk_stride + head_off;
-      load_block<D>(nxt, kpool + t, vpool + t, lane);
-    }
-    const int j = blk_begin + wave + k * W;
-    const int valid = bad ? 0 : min(16, w.tok_end - j * 16);  // tokens of this block in range
-
-    // S^T = K . Q^T
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  // STAGES-deep register ring: block k lives in buf[k % STAGES]; every slot is
+  // refilled right after it is consumed, so STAGES-1 blocks stay in flight.
+  int k0 = 0;
+  do {
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk], s, 0, 0, 0);
-
-    // online softmax; lane holds tokens quad*4 + i of head hl
-    float sv[4];
-    float mb = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (quad * 4 + i < valid) ? s[i] * a.scale_log2 : -INFINITY;
-      mb = fmaxf(mb, sv[i]);
-    }
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float m_new = fmaxf(m_run, mb);
-    float alpha = 1.f;
-    float pv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (m_new != -INFINITY) {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = exp2f(sv[i] - m_new);
-    }
-    m_run = m_new;
-    // P^T operand in bf16; the denominator sums the rounded weights
-    s16x4_t pop;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t b = f32_to_bf16(pv[i]);
-      pop[i] = static_cast<short>(b);
-      psum += bf16_to_f32(b);
-    }
-    l_lane = l_lane * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
-
-    // zero the values of out-of-range slots (their memory may hold anything)
-    if (valid < 16) {
-#pragma unroll
-      for (int pp = 0; pp < D / 32; ++pp) {
-        uint32_t* wv = reinterpret_cast<uint32_t*>(&cur.v[pp]);
-        // 16 bytes = [half 0: 4 slots][half 1: 4 slots], 2 slots per dword
-#pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-          const int slot0 = quad * 4 + (dw & 1) * 2;
-          uint32_t mask = 0;
-          if (slot0 < valid) mask |= 0x0000ffffu;
-          if (slot0 + 1 < valid) mask |= 0xffff0000u;
-          wv[dw] &= mask;
+    for (int u = 0; u < STAGES; ++u) {
+      const int k = k0 + u;
+      if (k < n_blk) {
+        const int phys = phys_ring[u];
+        const bool bad = phys < 0 || phys >= a.num_blocks;
+        poisoned |= bad;
+        const int valid = bad ? 0 : min(16, cs.n - cs.j * 16);
+        attend_block<D>(buf[u], qop, valid, quad, a.scale_log2, o, m_run, l_lane);
+        if (cs.j == cs.nb - 1 || k == n_blk - 1) {  // end of this unit's run
+          finish();
+          if (k + 1 < n_blk) {
+            advance(cs);
+            seg_j0 = 0;
+            fetch_q(++unit_idx);
+          }
+        } else {
+          advance(cs);
         }
       }
+      issue(buf[u], u);
     }
+    k0 += STAGES;
+  } while (k0 < n_blk);
+}
 
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int pp = 0; pp < D / 32; ++pp) {
-      const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
-      o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop,
-                                                            o[2 * pp], 0, 0, 0);
-      o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[1]), pop,
-                                                                o[2 * pp + 1], 0, 0, 0);
-    }
-    cur = nxt;
+// Merge for the split-K kernel: unit (seq, kv head) was covered by waves
+// wF..wL (the waves whose runs hold its first and last partition); unless one
+// wave held it whole, fold the partials of slots w + unit with the
+// running-max recurrences.  Also writes zero rows for empty sequences.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeWeights = 2048;  // partials whose weights are kept in LDS
+
+__global__ void __launch_bounds__(kMergeThreads) merge_sk_kernel(sk_args a, int head_dim) {
+  const int seq = blockIdx.x / a.n_q_heads;
+  const int h = blockIdx.x % a.n_q_heads;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int kvh = h / G, hg = h % G;
+  const int tid = threadIdx.x;
+  uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(seq) * a.n_q_heads + h) * head_dim;
+  const int np = a.cum_parts[seq + 1] - a.cum_parts[seq];
+  if (np == 0) {
+    for (int e = tid; e < head_dim; e += kMergeThreads) out[e] = 0;
+    return;
   }
-
-  // per-head denominators: sum over the four token groups
-  l_lane += __shfl_xor(l_lane, 16);
-  l_lane += __shfl_xor(l_lane, 32);
-
-  // stage this wave's (m, l, O) in LDS; lane holds O^T[16*nt + quad*4 + i][hl]
-  float* o_s = smem;                               // [W][G][D]
-  float* m_s = smem + W * G * D;                   // [W][G]
-  float* l_s = m_s + W * G;                        // [W][G]
-  __shared__ int poison_s;
-  if (threadIdx.x == 0) poison_s = 0;
-  if (hl < G) {
-#pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o_s[(wave * G + hl) * D + nt * 16 + quad * 4 + i] = o[nt][i];
-    if (quad == 0) {
-      m_s[wave * G + hl] = m_run;
-      l_s[wave * G + hl] = l_lane;
+  const int64_t total = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[a.n_seqs];
+  const int64_t W = a.n_waves;
+  const int64_t first = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[seq] + static_cast<int64_t>(kvh) * np;
+  const int64_t lastp = first + np - 1;
+  auto wave_of = [&](int64_t pp) { return ((pp + 1) * W - 1) / total; };
+  auto run_begin = [&](int64_t w) { return w * total / W; };
+  const int64_t wF = wave_of(first), wL = wave_of(lastp);
+  if (wF == wL) return;  // one wave wrote the final row
+  const int n_w = static_cast<int>(wL - wF + 1);
+  const int64_t unit = static_cast<int64_t>(seq) * a.n_kv_heads + kvh;
+  __shared__ float w_s[kMergeWeights];
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float4 acc_s[kMergeThreads];
+  auto row_of = [&](int i) { return (wF + i + unit) * G + hg; };
+  auto live = [&](int i) { return run_begin(wF + i) < run_begin(wF + i + 1); };
+  float M = -INFINITY;
+  for (int i = tid; i < n_w; i += kMergeThreads)
+    if (live(i)) M = fmaxf(M, a.part_m[row_of(i)]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float L = 0.f;
+  for (int i = tid; i < n_w; i += kMergeThreads) {
+    float f = 0.f;
+    if (live(i)) {
+      const float m = a.part_m[row_of(i)];
+      f = (m != m) ? __builtin_nanf("") : exp2f(m - M);
+      L += f * a.part_l[row_of(i)];
     }
+    if (i < kMergeWeights) w_s[i] = f;
   }
+  L = wave_sum(L);
+  if ((tid & 63) == 0) red[tid >> 6] = L;
   __syncthreads();
-  if (poisoned) atomicOr(&poison_s, 1);
-  __syncthreads();
-  const bool any_poison = poison_s != 0;
-  for (int i = threadIdx.x; i < G * D; i += W * 64) {
-    const int h = i / D, e = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < W; ++v) M = fmaxf(M, m_s[v * G + h]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int v = 0; v < W; ++v) {
-        const float f = exp2f(m_s[v * G + h] - M);
-        L += f * l_s[v * G + h];
-        O += f * o_s[(v * G + h) * D + e];
+  L = red[0] + red[1] + red[2] + red[3];
+  const int d4 = head_dim / 4;
+  const int groups = kMergeThreads / d4;
+  const int grp = tid / d4, c = tid % d4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (grp < groups) {
+    for (int i = grp; i < n_w; i += groups) {
+      float f;
+      if (i < kMergeWeights) {
+        f = w_s[i];
+      } else {
+        f = 0.f;
+        if (live(i)) {
+          const float m = a.part_m[row_of(i)];
+          f = (m != m) ? __builtin_nanf("") : exp2f(m - M);
+        }
       }
+      if (f == 0.f) continue;
+      const float4 v = reinterpret_cast<const float4*>(a.part_o + row_of(i) * head_dim)[c];
+      acc.x += f * v.x;
+      acc.y += f * v.y;
+      acc.z += f * v.z;
+      acc.w += f * v.w;
     }
-    store_result<uint16_t>(a, w, h, e, M, L, O, any_poison);
+  }
+  acc_s[tid] = acc;
+  __syncthreads();
+  if (tid < d4) {
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int g = 0; g < groups; ++g) {
+      const float4 v = acc_s[g * d4 + tid];
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
+    const float inv = 1.f / L;
+    uint16_t* o4 = out + 4 * tid;
+    o4[0] = f32_to_bf16(sum.x * inv);
+    o4[1] = f32_to_bf16(sum.y * inv);
+    o4[2] = f32_to_bf16(sum.z * inv);
+    o4[3] = f32_to_bf16(sum.w * inv);
   }
 }
 
@@ -583,7 +882,7 @@ __global__ void __launch_bounds__(W * 64) attn_mfma_kernel(attn_args a) {
 // ---------------------------------------------------------------------------
 
 template <typename T>
-__global__ void __launch_bounds__(256) merge_kernel(attn_args a) {
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(attn_args a) {
   const int seq = blockIdx.x / a.n_q_heads;
   const int h = blockIdx.x % a.n_q_heads;
   int n = a.ctx_lens[seq];
@@ -592,38 +891,63 @@ __global__ void __launch_bounds__(256) merge_kernel(attn_args a) {
   const int n_parts = n <= 0 ? 1 : (n + a.partition_tokens - 1) / a.partition_tokens;
   if (n_parts == 1) return;
   const int64_t ph = (static_cast<int64_t>(seq) * a.n_q_heads + h) * a.max_parts;
-  __shared__ float w_s[1024];
-  __shared__ float red[4];
+  __shared__ float w_s[kMergeWeights];
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float4 acc_s[kMergeThreads];
+  const int tid = threadIdx.x;
   // maximum over partitions
   float M = -INFINITY;
-  for (int p = threadIdx.x; p < n_parts; p += blockDim.x) M = fmaxf(M, a.part_m[ph + p]);
+  for (int p = tid; p < n_parts; p += kMergeThreads) M = fmaxf(M, a.part_m[ph + p]);
   M = wave_max(M);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
+  if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
-  // weights and denominator
+  // weights 2^(m_p - M) and the denominator
   float L = 0.f;
-  for (int p = threadIdx.x; p < n_parts; p += blockDim.x) {
+  for (int p = tid; p < n_parts; p += kMergeThreads) {
     const float m = a.part_m[ph + p];
-    float f = exp2f(m - M);
-    if (m != m) f = __builtin_nanf("");
-    if (p < 1024) w_s[p] = f;
+    const float f = (m != m) ? __builtin_nanf("") : exp2f(m - M);
+    if (p < kMergeWeights) w_s[p] = f;
     L += f * a.part_l[ph + p];
   }
   L = wave_sum(L);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = L;
+  if ((tid & 63) == 0) red[tid >> 6] = L;
   __syncthreads();
   L = red[0] + red[1] + red[2] + red[3];
-  const float inv = 1.f / L;
-  T* out = static_cast<T*>(a.out) + (static_cast<int64_t>(seq) * a.n_q_heads + h) * a.head_dim;
-  for (int e = threadIdx.x; e < a.head_dim; e += blockDim.x) {
-    float acc = 0.f;
-    for (int p = 0; p < n_parts; ++p) {
-      const float f = p < 1024 ? w_s[p] : exp2f(a.part_m[ph + p] - M);
-      acc += f * a.part_o[(ph + p) * a.head_dim + e];
+  // weighted sum of the partial outputs: each thread owns 4 dims of every
+  // groups-th partition, 16-byte loads
+  const int d4 = a.head_dim / 4;
+  const int groups = kMergeThreads / d4;
+  const int grp = tid / d4, c = tid % d4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (grp < groups) {
+    for (int p = grp; p < n_parts; p += groups) {
+      const float f = p < kMergeWeights ? w_s[p] : exp2f(a.part_m[ph + p] - M);
+      const float4 v = reinterpret_cast<const float4*>(a.part_o + (ph + p) * a.head_dim)[c];
+      acc.x += f * v.x;
+      acc.y += f * v.y;
+      acc.z += f * v.z;
+      acc.w += f * v.w;
     }
-    out[e] = elem<T>::from_f32(acc * inv);
+  }
+  acc_s[tid] = acc;
+  __syncthreads();
+  if (tid < d4) {
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int g = 0; g < groups; ++g) {
+      const float4 v = acc_s[g * d4 + tid];
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
+    const float inv = 1.f / L;
+    T* out = static_cast<T*>(a.out) + (static_cast<int64_t>(seq) * a.n_q_heads + h) * a.head_dim + 4 * tid;
+    out[0] = elem<T>::from_f32(sum.x * inv);
+    out[1] = elem<T>::from_f32(sum.y * inv);
+    out[2] = elem<T>::from_f32(sum.z * inv);
+    out[3] = elem<T>::from_f32(sum.w * inv);
   }
 }
 
@@ -636,19 +960,25 @@ kv_status hip_check(hipError_t e, const char* what) {
   return fail(KV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-constexpr int kMfmaWaves = 4;
-
-// LDS staging of the per-wave outputs must fit the 64 KiB a launch may request.
-size_t mfma_lds_bytes(int D, int G) { return static_cast<size_t>(kMfmaWaves) * G * (D + 2) * sizeof(float); }
-
 bool mfma_supported(const kv_pool_config& c, int G) {
   return c.dtype == KV_BF16 && c.block_size == 16 && (c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256) &&
-         G >= 1 && G <= kMaxGroup && mfma_lds_bytes(c.head_dim, G) <= 65536;
+         G >= 1 && G <= kMaxGroup;
 }
 
-int choose_partition(const kv_pool_config& c, int n_seqs, int max_blocks) {
-  // Aim for a few thousand workgroups so every CU has several resident, with
-  // at least 16 blocks per workgroup (4 per wave) to amortise the prologue.
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+// Partition length of the generic kernel: aim for a few thousand workgroups
+// so every CU has several resident, at least 256 tokens each.
+int choose_generic_partition(const kv_pool_config& c, int n_seqs, int max_blocks) {
   const int64_t max_ctx = static_cast<int64_t>(max_blocks) * c.block_size;
   const int64_t units = static_cast<int64_t>(n_seqs) * c.num_kv_heads;
   int part = 16 * c.block_size;
@@ -656,10 +986,25 @@ int choose_partition(const kv_pool_config& c, int n_seqs, int max_blocks) {
   return part;
 }
 
+// The split-K kernel keeps, per workgroup, two prefix arrays over sequences
+// and the staged queries in LDS.
+constexpr int kSkMaxSeqs = 4095;
+constexpr int kSkQBudget = 8192;  // bytes of staged queries per wave
+
+int sk_q_units(int G, int D) { return std::max(1, std::min(kSkQUnits, kSkQBudget / (G * D * 2))); }
+
+size_t sk_lds_bytes(int n_seqs, int G, int D) {
+  const size_t prefix = static_cast<size_t>((2 * (n_seqs + 1) + 3) & ~3) * 4;
+  return prefix + static_cast<size_t>(kSkWaves) * sk_q_units(G, D) * G * D * 2;
+}
+
+constexpr int sk_waves_per_simd(int D) { return D >= 256 ? 1 : 2; }
+
 struct resolved {
   int kernel;
-  int partition;
-  int max_parts;
+  int partition;   // tokens
+  int max_parts;   // generic kernel: partitions of the longest context
+  int64_t groups;  // split-K kernel: persistent workgroups
   float scale;
 };
 
@@ -673,33 +1018,56 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
   if (n_seqs < 0 || max_blocks <= 0) return fail(KV_ERR_INVALID, "n_seqs must be >= 0 and max_blocks_per_seq > 0");
   kv_attention_options o{0.f, 0, KV_KERNEL_AUTO};
   if (opts) o = *opts;
-  if (o.kernel == KV_KERNEL_MFMA && !mfma_supported(c, G))
-    return fail(KV_ERR_UNSUPPORTED, "the matrix-core kernel needs bf16, B = 16, d in {64, 128, 256} and G * (d + 2) <= 4096");
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_GENERIC && o.kernel != KV_KERNEL_MFMA)
     return fail(KV_ERR_INVALID, "unknown kernel selector");
-  r.kernel = o.kernel == KV_KERNEL_AUTO ? (mfma_supported(c, G) ? KV_KERNEL_MFMA : KV_KERNEL_GENERIC) : o.kernel;
+  const bool mfma_ok = mfma_supported(c, G) && n_seqs <= kSkMaxSeqs;
+  if (o.kernel == KV_KERNEL_MFMA && !mfma_ok)
+    return fail(KV_ERR_UNSUPPORTED,
+                "the matrix-core kernel needs bf16, B = 16, d in {64, 128, 256} and at most 4095 sequences");
+  r.kernel = o.kernel == KV_KERNEL_AUTO ? (mfma_ok ? KV_KERNEL_MFMA : KV_KERNEL_GENERIC) : o.kernel;
   if (o.partition_tokens < 0 || (o.partition_tokens > 0 && o.partition_tokens % c.block_size != 0))
     return fail(KV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of the block size");
-  r.partition = o.partition_tokens ? o.partition_tokens : choose_partition(c, n_seqs, max_blocks);
-  const int64_t max_ctx = static_cast<int64_t>(max_blocks) * c.block_size;
-  r.max_parts = static_cast<int>((max_ctx + r.partition - 1) / r.partition);
   if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
   r.scale = o.scale > 0.f ? o.scale : 1.f / std::sqrt(static_cast<float>(c.head_dim));
+  const int64_t max_ctx = static_cast<int64_t>(max_blocks) * c.block_size;
+  if (r.kernel == KV_KERNEL_MFMA) {
+    // default: one block per partition, the finest split (exact balance)
+    r.partition = o.partition_tokens ? o.partition_tokens : c.block_size;
+    r.max_parts = static_cast<int>((max_ctx + r.partition - 1) / r.partition);
+    const int64_t parts_ub = static_cast<int64_t>(n_seqs) * c.num_kv_heads * r.max_parts;
+    r.groups = std::max<int64_t>(
+        1, std::min<int64_t>((parts_ub + kSkWaves - 1) / kSkWaves, sk_waves_per_simd(c.head_dim) * device_cus()));
+  } else {
+    r.partition = o.partition_tokens ? o.partition_tokens : choose_generic_partition(c, n_seqs, max_blocks);
+    r.max_parts = static_cast<int>((max_ctx + r.partition - 1) / r.partition);
+    r.groups = 0;
+  }
   return KV_OK;
 }
 
+uint64_t up256(uint64_t b) { return (b + 255) & ~uint64_t(255); }
+
+// Workspace layout.  Generic kernel: m, l [n_seqs][Hq][max_parts], o [..][d].
+// Split-K kernel: m, l [slots][G], o [slots][G][d], slots = waves + units,
+// then the partition prefix [n_seqs + 1].
 uint64_t workspace_for(const kv_pool_config& c, int n_seqs, int num_q_heads, const resolved& r) {
+  if (r.kernel == KV_KERNEL_MFMA) {
+    const int G = num_q_heads / c.num_kv_heads;
+    const uint64_t slots = static_cast<uint64_t>(r.groups) * kSkWaves + static_cast<uint64_t>(n_seqs) * c.num_kv_heads;
+    return 2 * up256(slots * G * 4) + up256(slots * G * c.head_dim * 4) + up256((n_seqs + 1) * 4ull);
+  }
   if (r.max_parts <= 1) return 0;
   const uint64_t rows = static_cast<uint64_t>(n_seqs) * num_q_heads * r.max_parts;
-  auto up = [](uint64_t b) { return (b + 255) & ~uint64_t(255); };
-  return up(rows * 4) * 2 + up(rows * c.head_dim * 4);
+  return up256(rows * 4) * 2 + up256(rows * c.head_dim * 4);
 }
 
-template <int D, int W>
-hipError_t launch_mfma(const attn_args& a, int G, int64_t grid, hipStream_t st) {
-  static_assert(W == kMfmaWaves, "LDS sizing assumes kMfmaWaves waves");
-  const size_t shm = mfma_lds_bytes(D, G);
-  hipLaunchKernelGGL((attn_mfma_kernel<D, W>), dim3(static_cast<unsigned>(grid)), dim3(W * 64), shm, st, a);
+template <int D>
+hipError_t launch_mfma(const sk_args& a, const int32_t* ctx_lens, const int32_t* tables, int64_t groups, int G,
+                       hipStream_t st) {
+  constexpr int kStages = D >= 256 ? 2 : 4;
+  constexpr int kWps = sk_waves_per_simd(D);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, kWps>), dim3(static_cast<unsigned>(groups)), dim3(kSkWaves * 64),
+                     sk_lds_bytes(a.n_seqs, G, D), st, a, ctx_lens, tables);
   return hipGetLastError();
 }
 
@@ -785,29 +1153,69 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
   if (n_seqs == 0) return KV_OK;
   if (!q || !out || !d_block_tables || !d_context_lens || !pool->k_cache || !pool->v_cache)
     return fail(KV_ERR_INVALID, "NULL device pointer");
-  if (reinterpret_cast<uintptr_t>(q) & 15) return fail(KV_ERR_INVALID, "q must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(KV_ERR_INVALID, "q and out must be 16-byte aligned");
   const uint64_t need = workspace_for(c, n_seqs, num_q_heads, r);
   if (need > 0 && (!d_workspace || workspace_bytes < need))
     return fail(KV_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
+  if (need > 0 && (reinterpret_cast<uintptr_t>(d_workspace) & 255))
+    return fail(KV_ERR_INVALID, "workspace must be 256-byte aligned");
+  const int64_t layer_off =
+      static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_elems(c) * elem_bytes(c.dtype);
+  const void* k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
+  const void* v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const int G = num_q_heads / c.num_kv_heads;
+  hipError_t e = hipSuccess;
+
+  if (r.kernel == KV_KERNEL_MFMA) {
+    sk_args a{};
+    a.q = q;
+    a.out = out;
+    a.k_layer = k_layer;
+    a.v_layer = v_layer;
+    const uint64_t slots = static_cast<uint64_t>(r.groups) * kSkWaves + static_cast<uint64_t>(n_seqs) * c.num_kv_heads;
+    char* ws = static_cast<char*>(d_workspace);
+    a.part_m = reinterpret_cast<float*>(ws);
+    a.part_l = reinterpret_cast<float*>(ws + up256(slots * G * 4));
+    a.part_o = reinterpret_cast<float*>(ws + 2 * up256(slots * G * 4));
+    a.cum_parts = reinterpret_cast<int32_t*>(ws + 2 * up256(slots * G * 4) + up256(slots * G * c.head_dim * 4));
+    a.n_seqs = n_seqs;
+    a.max_blocks = max_blocks_per_seq;
+    a.n_q_heads = num_q_heads;
+    a.n_kv_heads = c.num_kv_heads;
+    a.num_blocks = c.num_blocks;
+    a.part_blocks = r.partition / c.block_size;
+    a.n_waves = static_cast<int>(r.groups * kSkWaves);
+    a.q_units = sk_q_units(G, c.head_dim);
+    a.scale_log2 = r.scale * kLog2e;
+    switch (c.head_dim) {
+      case 64: e = launch_mfma<64>(a, d_context_lens, d_block_tables, r.groups, G, st); break;
+      case 128: e = launch_mfma<128>(a, d_context_lens, d_block_tables, r.groups, G, st); break;
+      default: e = launch_mfma<256>(a, d_context_lens, d_block_tables, r.groups, G, st); break;
+    }
+    if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
+    const int64_t mgrid = static_cast<int64_t>(n_seqs) * num_q_heads;
+    hipLaunchKernelGGL(merge_sk_kernel, dim3(static_cast<unsigned>(mgrid)), dim3(kMergeThreads), 0, st, a,
+                       static_cast<int>(c.head_dim));
+    return hip_check(hipGetLastError(), "paged attention merge launch");
+  }
+
   const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * r.max_parts;
   if (grid > 0x7fffffff) return fail(KV_ERR_INVALID, "grid too large");
-
   attn_args a{};
   a.q = q;
   a.out = out;
   a.tables = d_block_tables;
   a.ctx_lens = d_context_lens;
-  const int64_t layer_off =
-      static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_elems(c) * elem_bytes(c.dtype);
-  a.k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
-  a.v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
+  a.k_layer = k_layer;
+  a.v_layer = v_layer;
   if (need > 0) {
     const uint64_t rows = static_cast<uint64_t>(n_seqs) * num_q_heads * r.max_parts;
-    auto up = [](uint64_t b) { return (b + 255) & ~uint64_t(255); };
     char* ws = static_cast<char*>(d_workspace);
     a.part_m = reinterpret_cast<float*>(ws);
-    a.part_l = reinterpret_cast<float*>(ws + up(rows * 4));
-    a.part_o = reinterpret_cast<float*>(ws + 2 * up(rows * 4));
+    a.part_l = reinterpret_cast<float*>(ws + up256(rows * 4));
+    a.part_o = reinterpret_cast<float*>(ws + 2 * up256(rows * 4));
   }
   a.n_seqs = n_seqs;
   a.max_blocks = max_blocks_per_seq;
@@ -819,36 +1227,24 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
   a.partition_tokens = r.partition;
   a.max_parts = r.max_parts;
   a.scale_log2 = r.scale * kLog2e;
-
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const int G = num_q_heads / c.num_kv_heads;
-  hipError_t e = hipSuccess;
-  if (r.kernel == KV_KERNEL_MFMA) {
-    switch (c.head_dim) {
-      case 64: e = launch_mfma<64, kMfmaWaves>(a, G, grid, st); break;
-      case 128: e = launch_mfma<128, kMfmaWaves>(a, G, grid, st); break;
-      default: e = launch_mfma<256, kMfmaWaves>(a, G, grid, st); break;
-    }
-  } else {
-    const bool f32 = c.dtype == KV_F32;
-    switch (c.head_dim) {
-      case 32: e = f32 ? launch_generic<float, 32>(a, grid, st) : launch_generic<uint16_t, 32>(a, grid, st); break;
-      case 64: e = f32 ? launch_generic<float, 64>(a, grid, st) : launch_generic<uint16_t, 64>(a, grid, st); break;
-      case 96: e = f32 ? launch_generic<float, 96>(a, grid, st) : launch_generic<uint16_t, 96>(a, grid, st); break;
-      case 128: e = f32 ? launch_generic<float, 128>(a, grid, st) : launch_generic<uint16_t, 128>(a, grid, st); break;
-      case 160: e = f32 ? launch_generic<float, 160>(a, grid, st) : launch_generic<uint16_t, 160>(a, grid, st); break;
-      case 192: e = f32 ? launch_generic<float, 192>(a, grid, st) : launch_generic<uint16_t, 192>(a, grid, st); break;
-      case 224: e = f32 ? launch_generic<float, 224>(a, grid, st) : launch_generic<uint16_t, 224>(a, grid, st); break;
-      default: e = f32 ? launch_generic<float, 256>(a, grid, st) : launch_generic<uint16_t, 256>(a, grid, st); break;
-    }
+  const bool f32 = c.dtype == KV_F32;
+  switch (c.head_dim) {
+    case 32: e = f32 ? launch_generic<float, 32>(a, grid, st) : launch_generic<uint16_t, 32>(a, grid, st); break;
+    case 64: e = f32 ? launch_generic<float, 64>(a, grid, st) : launch_generic<uint16_t, 64>(a, grid, st); break;
+    case 96: e = f32 ? launch_generic<float, 96>(a, grid, st) : launch_generic<uint16_t, 96>(a, grid, st); break;
+    case 128: e = f32 ? launch_generic<float, 128>(a, grid, st) : launch_generic<uint16_t, 128>(a, grid, st); break;
+    case 160: e = f32 ? launch_generic<float, 160>(a, grid, st) : launch_generic<uint16_t, 160>(a, grid, st); break;
+    case 192: e = f32 ? launch_generic<float, 192>(a, grid, st) : launch_generic<uint16_t, 192>(a, grid, st); break;
+    case 224: e = f32 ? launch_generic<float, 224>(a, grid, st) : launch_generic<uint16_t, 224>(a, grid, st); break;
+    default: e = f32 ? launch_generic<float, 256>(a, grid, st) : launch_generic<uint16_t, 256>(a, grid, st); break;
   }
   if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
   if (r.max_parts > 1) {
     const int64_t mgrid = static_cast<int64_t>(n_seqs) * num_q_heads;
-    if (c.dtype == KV_F32)
-      hipLaunchKernelGGL(merge_kernel<float>, dim3(static_cast<unsigned>(mgrid)), dim3(256), 0, st, a);
+    if (f32)
+      hipLaunchKernelGGL(merge_kernel<float>, dim3(static_cast<unsigned>(mgrid)), dim3(kMergeThreads), 0, st, a);
     else
-      hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(static_cast<unsigned>(mgrid)), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(static_cast<unsigned>(mgrid)), dim3(kMergeThreads), 0, st, a);
     if (kv_status s = hip_check(hipGetLastError(), "paged attention merge launch")) return s;
   }
   return KV_OK;

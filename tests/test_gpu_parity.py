@@ -158,7 +158,7 @@ RAGGED = [1, 2, 15, 16, 17, 31, 100, 257, 511, 512, 513, 1000, 2049]
 
 
 @pytest.mark.parametrize("kernel", [B.KV_KERNEL_MFMA, B.KV_KERNEL_GENERIC])
-@pytest.mark.parametrize("partition", [0, 16, 48, 256, 512, 4096])
+@pytest.mark.parametrize("partition", [0, 16, 48, 256, 512, 1024, 4096])
 def test_ragged_lengths_and_partitions(kernel, partition):
     announce(f"ragged lengths {RAGGED}, kernel {kernel}, partition {partition}")
     wl = ragged_workload(32, 8, 128, RAGGED)
@@ -269,12 +269,13 @@ def test_split_and_single_pass_agree():
     wl = ragged_workload(32, 8, 128, [2049, 1500])
     ref = OracleReplay(wl).run()
     outs = []
-    for kernel, part in ((B.KV_KERNEL_MFMA, 4096), (B.KV_KERNEL_MFMA, 64), (B.KV_KERNEL_GENERIC, 4096),
-                         (B.KV_KERNEL_GENERIC, 32)):
+    for kernel, part in ((B.KV_KERNEL_GENERIC, 4096), (B.KV_KERNEL_MFMA, 4096), (B.KV_KERNEL_MFMA, 64),
+                         (B.KV_KERNEL_MFMA, 16), (B.KV_KERNEL_GENERIC, 32)):
         run = GpuRun(wl, ref=ref, opts=B.attention_options(partition_tokens=part, kernel=kernel)).run()
         outs.append(run.decode_outputs[0][0].double().cpu().numpy())
     for o in outs[1:]:
         assert np.abs(o - outs[0]).max() <= 2 * BF16_ABS
+
 
 
 def test_invalid_arguments_are_rejected():
