@@ -46,11 +46,29 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--seed", type=int, default=0, help="0 = the workload's seed")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (a plain copy of known size, used to "
+                         "calibrate the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU form in this build)", file=sys.stderr)
@@ -236,7 +254,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(base.name),
             "kernel": "paged_attention_decode (partition + merge kernels)",
             "algorithmic_bytes_per_launch": int(ideal_per_launch),
         },
@@ -245,6 +263,23 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this
+    workload, or None when there is none or the kernel source changed since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    src = os.path.join(ROOT, "pagedattention_decode_amd", "csrc", "kernels.hip")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("kernel_source_sha256"):
+            return None
+    return rec.get("traffic_bytes_per_call")
 
 
 def cpu_baseline(args):

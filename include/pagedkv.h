@@ -197,13 +197,15 @@ kv_status copy_blocks(kv_pool* pool, const int64_t* d_pairs, int32_t n_pairs, vo
 typedef enum {
   KV_KERNEL_AUTO = 0,    /* the matrix-core kernel where it applies, else generic */
   KV_KERNEL_GENERIC = 1, /* vector-ALU kernel: any dtype, B, d, G <= 16 */
-  KV_KERNEL_MFMA = 2     /* bf16, B = 16, d in {64, 128, 256}, G <= 16 */
+  KV_KERNEL_MFMA = 2     /* bf16, B = 16, d in {64, 128, 256}, G <= 16,
+                            at most 4095 sequences per call */
 } kv_kernel;
 
 typedef struct {
   float scale;              /* softmax scale; 0 means 1/sqrt(d) ([BT] §07) */
-  int32_t partition_tokens; /* split-K partition length in tokens; 0 = let the
-                               library choose; else a positive multiple of B */
+  int32_t partition_tokens; /* split-K partition length in tokens, a positive
+                               multiple of B; 0 = the library's choice (one
+                               block for the matrix-core kernel) */
   int32_t kernel;           /* kv_kernel */
 } kv_attention_options;
 
@@ -217,17 +219,22 @@ uint64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t n_seqs, in
  * and query head h reading KV head g = h / (Hq / Hkv),
  *     k_t = K[l][T_s[t / B]][g][t % B],  v_t likewise,   t = 0 .. n-1,
  *     out[s][h] = sum_t softmax_t(scale * q[s][h] . k_t) v_t.
- * The context is split into partitions of partition_tokens tokens; each
- * partition yields its running max m, sum l and unnormalised output, and a
- * merge kernel folds them with the recurrences of [KVM] (chunked prefill
- * mechanism) when there is more than one.
+ * The context of every (sequence, kv head) is split into partitions of
+ * partition_tokens tokens.  Matrix-core kernel: the partitions of the whole
+ * batch are divided evenly, as contiguous runs, among the waves of a
+ * persistent grid; a wave folds its consecutive partitions online and writes
+ * a running max m, sum l and unnormalised output only where its run of a
+ * (sequence, kv head) ends.  Generic kernel: one partial per partition.  A
+ * merge kernel folds the partials with the recurrences of [KVM] (chunked
+ * prefill mechanism).
  *   q, out:          device [n_seqs][Hq][d], pool dtype (out rounded to
  *                    nearest even for bf16); accumulation is fp32.
  *   d_block_tables:  device int32[n_seqs][max_blocks_per_seq].
  *   d_context_lens:  device int32[n_seqs]; values are clamped to
  *                    max_blocks_per_seq * B; n <= 0 yields a zero row.
  *   d_workspace:     caller-owned device memory of at least
- *                    paged_attention_workspace_bytes (may be NULL if that is 0).
+ *                    paged_attention_workspace_bytes, 256-byte aligned (may be
+ *                    NULL if that is 0); its contents need no initialisation.
  * A table entry outside [0, N) is never dereferenced: the rows of that
  * sequence are written as NaN.  opts may be NULL (all defaults). */
 kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, void* out,

@@ -998,7 +998,11 @@ size_t sk_lds_bytes(int n_seqs, int G, int D) {
   return prefix + static_cast<size_t>(kSkWaves) * sk_q_units(G, D) * G * D * 2;
 }
 
-constexpr int sk_waves_per_simd(int D) { return D >= 256 ? 1 : 2; }
+// One wave per SIMD.  With two, the scheduler's oldest-first issue lets one
+// wave of each pair stream ~1.6x faster than the other; with equal shares the
+// slower half then finishes alone with half the loads in flight.  A single
+// wave per SIMD with a deeper ring keeps the same bytes in flight per CU.
+constexpr int sk_waves_per_simd(int) { return 1; }
 
 struct resolved {
   int kernel;
@@ -1064,7 +1068,7 @@ uint64_t workspace_for(const kv_pool_config& c, int n_seqs, int num_q_heads, con
 template <int D>
 hipError_t launch_mfma(const sk_args& a, const int32_t* ctx_lens, const int32_t* tables, int64_t groups, int G,
                        hipStream_t st) {
-  constexpr int kStages = D >= 256 ? 2 : 4;
+  constexpr int kStages = D >= 256 ? 2 : 6;
   constexpr int kWps = sk_waves_per_simd(D);
   hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, kWps>), dim3(static_cast<unsigned>(groups)), dim3(kSkWaves * 64),
                      sk_lds_bytes(a.n_seqs, G, D), st, a, ctx_lens, tables);
