@@ -6,7 +6,7 @@ A step is one decode step of the workload through the whole path:
           kv_get_block_tables, upload of slot mapping and tables;
   device: copy_blocks (only when the allocator asked for copies),
           then for every layer reshape_and_cache + paged_attention_decode
-          (partition kernel + log-sum-exp merge).
+          (split-K kernel, then the log-sum-exp merge of split units).
 Inputs (queries, new K/V rows) for every timed step are resident in HBM
 before the timed region; the pool is filled once, before warm-up.
 
@@ -71,7 +71,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU form in this build)", file=sys.stderr)
+              "(the path has no multi-GPU form)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -255,7 +255,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(base.name),
-            "kernel": "paged_attention_decode (partition + merge kernels)",
+            "kernel": "paged_attention_decode (split-K kernel + merge kernel)",
             "algorithmic_bytes_per_launch": int(ideal_per_launch),
         },
         "cpu_baseline": None,

@@ -165,10 +165,16 @@ class GpuRun:
     def decode(self, decode_index, layer, d_tables, d_lens, n, opts=None):
         wl = self.wl
         q = to_device_bits(self.query_bits(decode_index, layer, n))
+        # outputs and workspace start as all-ones bytes (NaN in both float
+        # types): a row the path forgets to write, or a stale partial or
+        # counter it reads, shows up in the comparison
         out = torch.empty_like(q)
+        out.view(torch.uint8).fill_(0xFF)
         opts = opts if opts is not None else self.opts
         ws_bytes = self.pool.workspace_bytes(n, wl.num_q_heads, d_tables.shape[1], opts)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+        if ws is not None:
+            ws.fill_(0xFF)
         self.pool.decode(layer, q, out, d_tables, d_lens, wl.num_q_heads, opts, ws)
         return bits_to_float_tensor(out, wl.dtype)
 

@@ -145,13 +145,13 @@ def test_small_fork_workload(kernel, dtype):
     compare_all_decodes(run, ref)
 
 
-def ragged_workload(hq, hkv, d, lengths, seed=31, num_blocks=None, dtype=draws.BF16):
+def ragged_workload(hq, hkv, d, lengths, seed=31, num_blocks=None, dtype=draws.BF16, layers=1):
     seqs = tuple(range(len(lengths)))
     ops = [("add", s) for s in seqs]
     ops.append(("append", seqs, tuple(lengths)))
     ops.append(("decode", seqs))
     need = sum(-(-n // 16) for n in lengths)
-    return workloads.Workload("ragged", seed, dtype, 1, hq, hkv, d, 16, num_blocks or need + 7, ops)
+    return workloads.Workload("ragged", seed, dtype, layers, hq, hkv, d, 16, num_blocks or need + 7, ops)
 
 
 RAGGED = [1, 2, 15, 16, 17, 31, 100, 257, 511, 512, 513, 1000, 2049]
@@ -276,6 +276,28 @@ def test_split_and_single_pass_agree():
     for o in outs[1:]:
         assert np.abs(o - outs[0]).max() <= 2 * BF16_ABS
 
+
+
+def test_workspace_reused_across_calls():
+    announce("split-K kernel: one workspace reused by 6 calls (layers 0, 1 alternating), outputs poisoned")
+    lengths = [2304, 17, 1000, 4096, 33, 2304, 700, 1]
+    wl = ragged_workload(32, 8, 128, lengths, layers=2)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()
+    tables = torch.from_numpy(run.decodes[0]["tables"]).cuda()
+    lens = torch.from_numpy(run.decodes[0]["lengths"]).cuda()
+    n = len(lengths)
+    opts = B.attention_options(kernel=B.KV_KERNEL_MFMA)
+    ws = torch.empty(run.pool.workspace_bytes(n, 32, tables.shape[1], opts), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    out = torch.empty((n, 32, 128), dtype=torch.int16, device="cuda")
+    for call in range(6):
+        layer = call % 2
+        q = to_device_bits(run.query_bits(0, layer, n))
+        out.fill_(-1)
+        run.pool.decode(layer, q, out, tables, lens, 32, opts, ws)
+        got = bits_to_float_tensor(out, wl.dtype).double().cpu().numpy()
+        check_outputs(got, ref.attention(0, layer), wl.dtype, f"call {call} layer {layer}")
 
 
 def test_invalid_arguments_are_rejected():
