@@ -31,8 +31,15 @@ Modules:
 * :mod:`oracle.attention`     gathered softmax(q K^T / sqrt(d)) V in float64
                                ([BT] §07) and the split-K merge recurrences
                                ([KVM] chunked prefill mechanism).
+* :mod:`oracle.prefill`       multi-query attention over paged history: a chunk
+                               of c queries over h cached tokens with the
+                               history fully visible and a causal mask inside
+                               the chunk ([KVM] chunked prefill mechanism,
+                               Figure 8; [INF] §8.2.3 pair counts, §8.5.1
+                               verification of draft positions).
 * :mod:`oracle.runner`        replays a :mod:`synth` workload through the above.
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against values the
+Every function is pinned by ``tests/test_oracle_pins.py`` and
+``tests/test_prefill_pins.py`` against values the
 pages print, closed forms, invariants and brute force.  Parity unpinned: none.
 """

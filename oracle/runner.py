@@ -14,11 +14,12 @@ from __future__ import annotations
 import numpy as np
 
 from synth import draws
-from synth.draws import TAG_K, TAG_Q, TAG_V
+from synth.draws import TAG_K, TAG_Q, TAG_QCHUNK, TAG_V
 
 from .attention import decode_attention
 from .block_manager import BlockManager
 from .kv_store import KVStore
+from .prefill import chunk_attention
 
 
 class OracleReplay:
@@ -32,6 +33,7 @@ class OracleReplay:
         self.writers = None if writers is None else set(writers)
         self.appends = []  # (seq_ids, counts, slots, pairs)
         self.decodes = []  # {"seq_ids", "tables", "lengths"}
+        self.prefills = []  # {"seq_ids", "counts", "tables", "lengths"} (lengths after the chunk)
 
     def run(self, ops=None):
         for op in (self.wl.ops if ops is None else ops):
@@ -51,7 +53,7 @@ class OracleReplay:
             self.bm.fork(op[1], op[2])
         elif kind == "release":
             self.bm.release(op[1])
-        elif kind == "append":
+        elif kind in ("append", "prefill"):
             seq_ids, counts = list(op[1]), list(op[2])
             running = {}
             segments = []  # (writer, first position, count)
@@ -70,6 +72,13 @@ class OracleReplay:
                                          self.rows(TAG_V, layer, s, pos))
                 at += c
             self.appends.append((tuple(seq_ids), tuple(counts), list(slots), list(pairs)))
+            if kind == "prefill":
+                self.prefills.append({
+                    "seq_ids": seq_ids,
+                    "counts": counts,
+                    "tables": [self.bm.table(s) for s in seq_ids],
+                    "lengths": [self.bm.length(s) for s in seq_ids],
+                })
         elif kind == "decode":
             seq_ids = list(op[1])
             self.decodes.append({
@@ -96,5 +105,41 @@ class OracleReplay:
         for i in rows:
             kb, vb = self.store.gather(layer, dec["tables"][i], dec["lengths"][i])
             out.append(decode_attention(q[i], draws.bits_to_f64(kb, wl.dtype),
+                                        draws.bits_to_f64(vb, wl.dtype)))
+        return np.stack(out)
+
+    def prefill_query_bits(self, prefill_index, layer):
+        wl = self.wl
+        total = sum(self.prefills[prefill_index]["counts"])
+        return draws.normal_bits(wl.seed, TAG_QCHUNK, (prefill_index, layer),
+                                 (total, wl.num_q_heads, wl.head_dim), wl.dtype)
+
+    def prefill_attention(self, prefill_index, layer, seqs=None):
+        """float64 outputs of a recorded prefill: {batch index: [count, Hq, d]}."""
+        wl = self.wl
+        rec = self.prefills[prefill_index]
+        seqs = range(len(rec["seq_ids"])) if seqs is None else seqs
+        q = draws.bits_to_f64(self.prefill_query_bits(prefill_index, layer), wl.dtype)
+        first = np.concatenate([[0], np.cumsum(rec["counts"])])
+        out = {}
+        for i in seqs:
+            kb, vb = self.store.gather(layer, rec["tables"][i], rec["lengths"][i])
+            out[i] = chunk_attention(q[first[i]:first[i + 1]], draws.bits_to_f64(kb, wl.dtype),
+                                     draws.bits_to_f64(vb, wl.dtype))
+        return out
+
+    def prefill_rows(self, prefill_index, layer, picks):
+        """float64 outputs [len(picks), Hq, d] of single rows (batch index, chunk row) of a
+        recorded prefill; row j of a chunk of c tokens is the decode query of position
+        length - c + j over the cached positions 0 .. length - c + j."""
+        wl = self.wl
+        rec = self.prefills[prefill_index]
+        q = draws.bits_to_f64(self.prefill_query_bits(prefill_index, layer), wl.dtype)
+        first = np.concatenate([[0], np.cumsum(rec["counts"])])
+        out = []
+        for i, j in picks:
+            n = rec["lengths"][i] - rec["counts"][i] + j + 1
+            kb, vb = self.store.gather(layer, rec["tables"][i], n)
+            out.append(decode_attention(q[first[i] + j], draws.bits_to_f64(kb, wl.dtype),
                                         draws.bits_to_f64(vb, wl.dtype)))
         return np.stack(out)

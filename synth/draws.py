@@ -24,6 +24,7 @@ TAG_Q = 1
 TAG_K = 2
 TAG_V = 3
 TAG_BACKGROUND = 4
+TAG_QCHUNK = 5  # queries of multi-query (chunk / verification) attention
 
 # Tokens per generator chunk for K/V rows.
 CHUNK = 1024

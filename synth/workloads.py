@@ -8,11 +8,17 @@ A workload is a model shape plus an ordered list of block-manager operations:
                                          sequence-major, in the given order); every
                                          appended token gets K/V rows in every layer;
 * ``("fork", parent, child)``            the child shares the parent's blocks;
-* ``("decode", seq_ids)``                one query per listed sequence per layer.
+* ``("decode", seq_ids)``                one query per listed sequence per layer;
+* ``("prefill", seq_ids, counts)``       append ``counts[i]`` tokens to ``seq_ids[i]``
+                                         exactly as ``append`` does, then attend one
+                                         query per appended token (chunked prefill
+                                         or verification of draft positions).
 
 The K/V rows of a token are a function of (layer, writing sequence, position)
 only, drawn by :func:`synth.draws.token_rows`; queries of the ``i``-th decode
-op in layer ``l`` are ``normal_bits(seed, TAG_Q, (i, l), (S, Hq, d))``.
+op in layer ``l`` are ``normal_bits(seed, TAG_Q, (i, l), (S, Hq, d))``; queries of
+the ``i``-th prefill op are ``normal_bits(seed, TAG_QCHUNK, (i, l), (sum(counts),
+Hq, d))``, sequence-major.
 
 The shapes follow the pages' workloads: the Qwen3-8B geometry (36 layers,
 8 KV heads of dim 128, 32 query heads), the 70B GQA geometry (64 query heads,
@@ -60,7 +66,7 @@ class Workload:
                 lens[op[1]] = 0
             elif op[0] == "fork":
                 lens[op[2]] = lens[op[1]]
-            elif op[0] == "append":
+            elif op[0] in ("append", "prefill"):
                 for s, c in zip(op[1], op[2]):
                     lens[s] += c
         return lens
@@ -143,6 +149,56 @@ def agentic_fork(steps: int = 512, layers: int = 36) -> Workload:
     return Workload("agentic_fork_64x33281", 5, BF16, layers, 32, 8, 128, 16, POOL_FORK, ops,
                     description=f"bf16 Hq=32 Hkv=8 d=128 B=16, {layers} layers, 4 roots x 16 forks,"
                                 f" {steps} steps")
+
+
+def chunked_prompt(prompts=(2048,), chunk=512, layers=1, seed=6) -> Workload:
+    """Prompts prefilled chunk by chunk over their own paged history.
+
+    With the defaults this is [KVM] Figure 8: one 2048-token prompt, chunks of
+    512 tokens, so iteration k = 3 covers tokens 1024..1535 and attends the
+    1536 tokens of chunks 1..3.  Several prompts advance together, one chunk
+    each per iteration, until the longest is done.
+    """
+    seqs = tuple(range(len(prompts)))
+    ops = [("add", s) for s in seqs]
+    done = [0] * len(prompts)
+    while any(d < p for d, p in zip(done, prompts)):
+        ids = tuple(s for s in seqs if done[s] < prompts[s])
+        counts = tuple(min(chunk, prompts[s] - done[s]) for s in ids)
+        ops.append(("prefill", ids, counts))
+        for s, c in zip(ids, counts):
+            done[s] += c
+    blocks = sum(-(-p // 16) for p in prompts)
+    return Workload(f"chunked_prompt_{'_'.join(map(str, prompts))}_c{chunk}", seed, BF16, layers, 32, 8, 128, 16,
+                    blocks + 16, ops,
+                    description=f"bf16 Hq=32 Hkv=8 d=128 B=16, prompts {list(prompts)} in chunks of {chunk}")
+
+
+# Pool of the chunk workloads: 16 sequences x 8192 tokens = 8192 blocks, plus slack.
+POOL_CHUNK = 8208
+
+
+def prefill_last_chunk() -> Workload:
+    """The last 512-token chunk of 16 8K-token prompts ([INF] section 8.2.3: 7680
+    cached tokens, 4,063,488 query-key pairs per head; batch 16 as in the
+    chapter's 8K-input experiment)."""
+    seqs = tuple(range(16))
+    ops = [("add", s) for s in seqs]
+    ops.append(("append", seqs, tuple(7680 for _ in seqs)))
+    ops.append(("prefill", seqs, tuple(512 for _ in seqs)))
+    return Workload("prefill_16x512_after_7680", 7, BF16, 1, 32, 8, 128, 16, POOL_CHUNK, ops,
+                    description="bf16 Hq=32 Hkv=8 d=128 B=16, 16 x (7680 cached + 512-token chunk)")
+
+
+def verify_drafts(positions=8) -> Workload:
+    """Verification of ``positions`` draft tokens for 16 requests with 8K contexts
+    ([INF] section 8.6.3 plan D: 16 requests, 8 positions each)."""
+    seqs = tuple(range(16))
+    ops = [("add", s) for s in seqs]
+    ops.append(("append", seqs, tuple(8192 - positions for _ in seqs)))
+    ops.append(("prefill", seqs, tuple(positions for _ in seqs)))
+    return Workload(f"verify_16x{positions}_after_{8192 - positions}", 8, BF16, 1, 32, 8, 128, 16, POOL_CHUNK, ops,
+                    description=f"bf16 Hq=32 Hkv=8 d=128 B=16, 16 x ({8192 - positions} cached + {positions} drafts)")
 
 
 CONFIGS = {
