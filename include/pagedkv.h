@@ -20,7 +20,9 @@
  *         §05 block manager, §06 tensor shapes, §07 decode equation, §08 CoW,
  *         §10 atomic reservation, §13 conservation.
  *   [INF] "第 8 章 推理优化" (inference optimisation): §8.3.2 release only
- *         when no reference remains and no submitted device work reads it.
+ *         when no reference remains and no submitted device work reads it;
+ *         §8.2.3 query-key pairs of a chunk; §8.5.1 verification of draft
+ *         positions in one pass.
  *
  * Conventions for every call:
  *   - Status codes; on failure kv_last_error() returns a message (thread
@@ -242,6 +244,45 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
                                  int32_t n_seqs, int32_t max_blocks_per_seq, int32_t num_q_heads,
                                  const kv_attention_options* opts, void* d_workspace,
                                  uint64_t workspace_bytes, void* hip_stream);
+
+/* Device workspace needed by paged_attention_prefill for these arguments. */
+uint64_t paged_prefill_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int32_t total_q, int32_t max_q_len,
+                                       int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                       const kv_attention_options* opts);
+
+/* Multi-query attention over the paged cache of one layer: chunked prefill
+ * ([KVM] chunked prefill mechanism, Figure 8) and verification of draft
+ * positions ([INF] §8.5.1).  Sequence s owns the query rows
+ * q_indptr[s] .. q_indptr[s+1]-1, c of them; its K/V rows for those c
+ * tokens must already be in the pool (reshape_and_cache), so with
+ * n = context_lens[s] the queries sit at positions h = n - c .. n - 1.  The
+ * query of chunk row j sees the cached positions 0 .. h + j: the whole
+ * history and, inside the chunk, itself and the rows before it.  For query
+ * head h reading KV head g = h / (Hq / Hkv):
+ *     out[r][h] = sum_{t <= h_s + j} softmax_t(scale * q[r][h] . k_t) v_t.
+ * A sequence with c = 1 is a decode query.
+ *   q, out:          device [total_q][Hq][d] bf16, rows grouped by sequence
+ *                    as q_indptr says; out rounded to nearest even.
+ *   d_q_indptr:      device int32[n_seqs + 1], non-decreasing, q_indptr[0] = 0,
+ *                    q_indptr[n_seqs] <= total_q.  Rows of a sequence that
+ *                    would fall outside [0, total_q) are not written.
+ *   max_q_len:       an upper bound of every c (sizes the grid); a sequence
+ *                    with c > max_q_len or c > n gets NaN rows.
+ *   d_block_tables, d_context_lens: as for paged_attention_decode (lengths
+ *                    clamped to max_blocks_per_seq * B).
+ *   d_workspace:     at least paged_prefill_workspace_bytes, 256-byte
+ *                    aligned (NULL if that is 0); no initialisation needed.
+ * A table entry outside [0, N) is never dereferenced: the rows of the query
+ * tiles that would read it are written as NaN.  Only the matrix-core kernel
+ * exists (bf16, B = 16, d in {64, 128, 256}, G <= 16); other pools give
+ * KV_ERR_UNSUPPORTED.  opts->partition_tokens splits every tile's keys into
+ * partitions merged with the [KVM] recurrences (0 = the library's choice). */
+kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, void* out,
+                                  const int32_t* d_q_indptr, const int32_t* d_block_tables,
+                                  const int32_t* d_context_lens, int32_t n_seqs, int32_t total_q,
+                                  int32_t max_q_len, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                                  const kv_attention_options* opts, void* d_workspace, uint64_t workspace_bytes,
+                                  void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -1,4 +1,5 @@
-"""Paged KV cache with single-query decode attention for MI355X (gfx950).
+"""Paged KV cache with decode and multi-query (chunked prefill / draft
+verification) attention for MI355X (gfx950).
 
 The work is done by ``libpagedkv.so`` (C ABI in ``include/pagedkv.h``): a C++
 host block manager and hand-written HIP kernels.  :mod:`.binding` exposes the
@@ -27,7 +28,9 @@ from .binding import (  # noqa: F401
     kv_seq_fork,
     kv_seq_release,
     paged_attention_decode,
+    paged_attention_prefill,
     paged_attention_workspace_bytes,
+    paged_prefill_workspace_bytes,
     reshape_and_cache,
 )
 from .pool import PagedKVPool  # noqa: F401

@@ -75,6 +75,9 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (_U64, [_P, _I32, _I32, _I32, C.POINTER(kv_attention_options)]),
     "paged_attention_decode": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _I32,
                                       C.POINTER(kv_attention_options), _P, _U64, _P]),
+    "paged_prefill_workspace_bytes": (_U64, [_P, _I32, _I32, _I32, _I32, _I32, C.POINTER(kv_attention_options)]),
+    "paged_attention_prefill": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                       C.POINTER(kv_attention_options), _P, _U64, _P]),
 }
 
 _lib = None
@@ -272,3 +275,22 @@ def paged_attention_decode(pool, layer, q, out, block_tables, context_lens, num_
                                         _dev(context_lens), n_seqs, max_blocks, int(num_q_heads),
                                         C.byref(opts) if opts is not None else None, _dev(workspace),
                                         ws_bytes, _stream(stream)))
+
+
+def paged_prefill_workspace_bytes(pool, n_seqs, total_q, max_q_len, num_q_heads, max_blocks_per_seq, opts=None):
+    return int(lib().paged_prefill_workspace_bytes(pool, int(n_seqs), int(total_q), int(max_q_len), int(num_q_heads),
+                                                   int(max_blocks_per_seq),
+                                                   C.byref(opts) if opts is not None else None))
+
+
+def paged_attention_prefill(pool, layer, q, out, q_indptr, block_tables, context_lens, max_q_len, num_q_heads,
+                            opts=None, workspace=None, stream=None):
+    """q, out: device [total_q, Hq, d]; q_indptr: device int32 [n + 1]; block_tables: device
+    int32 [n, max_blocks]; context_lens: device int32 [n] (lengths after the chunk)."""
+    n_seqs, max_blocks = int(block_tables.shape[0]), int(block_tables.shape[1])
+    total_q = int(q.shape[0])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attention_prefill(pool, int(layer), _dev(q), _dev(out), _dev(q_indptr), _dev(block_tables),
+                                         _dev(context_lens), n_seqs, total_q, int(max_q_len), max_blocks,
+                                         int(num_q_heads), C.byref(opts) if opts is not None else None,
+                                         _dev(workspace), ws_bytes, _stream(stream)))

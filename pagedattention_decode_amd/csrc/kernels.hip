@@ -27,26 +27,15 @@
 #include <cmath>
 #include <string>
 
+#include "device_common.h"
 #include "pool_internal.h"
 
 namespace pagedkv {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 // ---------------------------------------------------------------------------
 // element helpers
 // ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
-
-// Round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
 
 template <typename T> struct elem;
 template <> struct elem<float> {
@@ -212,7 +201,6 @@ __device__ __forceinline__ void store_result(const attn_args& a, const work_item
 // ---------------------------------------------------------------------------
 
 constexpr int kGenericWaves = 4;
-constexpr int kMaxGroup = 16;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
@@ -376,33 +364,6 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
 // except the two shuffles of the per-head block maximum.
 // ---------------------------------------------------------------------------
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-template <int D>
-struct kv_regs {
-  uint4 k[D / 32];
-  uint4 v[D / 32];
-};
-
-template <int D>
-__device__ __forceinline__ void load_block(kv_regs<D>& r, const uint4* kt, const uint4* vt, int lane) {
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) r.k[i] = kt[i * 64 + lane];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) r.v[i] = vt[i * 64 + lane];
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// The running maximum m is only moved when a block's maximum exceeds it by more
-// than this many binary orders of magnitude; otherwise the block is weighted
-// against the stale m (weights up to 2^kRescaleSlack).  Numerator and
-// denominator use the same m, so the result is unchanged; the rescale of the
-// accumulators is skipped for most blocks.
-constexpr float kRescaleSlack = 8.f;
 
 // One 16-token block: scores, online-softmax update, weighted sum of values.
 // `valid` (wave uniform) is the number of in-range slots of the block.
@@ -448,21 +409,7 @@ __device__ __forceinline__ void attend_block(kv_regs<D>& cur, const bf16x8_t* qo
   const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(w01, w23));
 
   // zero the values of out-of-range slots (their memory may hold anything)
-  if (valid < 16) {
-#pragma unroll
-    for (int pp = 0; pp < D / 32; ++pp) {
-      uint32_t* wv = reinterpret_cast<uint32_t*>(&cur.v[pp]);
-      // 16 bytes = [half 0: 4 slots][half 1: 4 slots], 2 slots per dword
-#pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {
-        const int slot0 = quad * 4 + (dw & 1) * 2;
-        uint32_t mask = 0;
-        if (slot0 < valid) mask |= 0x0000ffffu;
-        if (slot0 + 1 < valid) mask |= 0xffff0000u;
-        wv[dw] &= mask;
-      }
-    }
-  }
+  if (valid < 16) zero_v_tail<D>(cur, valid, quad);
 
   // O^T += V^T . P^T
 #pragma unroll
@@ -955,6 +902,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(attn_args a) {
 // host helpers
 // ---------------------------------------------------------------------------
 
+}  // namespace
+
 kv_status hip_check(hipError_t e, const char* what) {
   if (e == hipSuccess) return KV_OK;
   return fail(KV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -975,6 +924,10 @@ int device_cus() {
   }
   return cus;
 }
+
+uint64_t up256(uint64_t b) { return (b + 255) & ~uint64_t(255); }
+
+namespace {
 
 // Partition length of the generic kernel: aim for a few thousand workgroups
 // so every CU has several resident, at least 256 tokens each.
@@ -1048,8 +1001,6 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
   }
   return KV_OK;
 }
-
-uint64_t up256(uint64_t b) { return (b + 255) & ~uint64_t(255); }
 
 // Workspace layout.  Generic kernel: m, l [n_seqs][Hq][max_parts], o [..][d].
 // Split-K kernel: m, l [slots][G], o [slots][G][d], slots = waves + units,

@@ -2,6 +2,8 @@
 // the device entry points (kernels.hip).  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_runtime_api.h>
+
 #include <cstdint>
 #include <deque>
 #include <string>
@@ -50,5 +52,12 @@ inline int64_t pool_elems(const kv_pool_config& c) {
 
 // Sets the thread-local error message and returns the status.
 kv_status fail(kv_status st, const std::string& msg);
+
+// Shared by the attention entry points (defined with the decode kernels).
+constexpr int kMaxGroup = 16;  // query heads per KV head
+kv_status hip_check(hipError_t e, const char* what);
+bool mfma_supported(const kv_pool_config& c, int G);  // bf16, B = 16, d in {64, 128, 256}, G <= 16
+int device_cus();                                    // compute units of the current device
+uint64_t up256(uint64_t b);                          // rounded up to 256 bytes
 
 }  // namespace pagedkv

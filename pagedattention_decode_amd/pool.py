@@ -93,6 +93,14 @@ class PagedKVPool:
         B.paged_attention_decode(self.handle, layer, q, out, block_tables, context_lens, num_q_heads, opts,
                                  workspace, stream)
 
+    def prefill_workspace_bytes(self, n_seqs, total_q, max_q_len, num_q_heads, max_blocks, opts=None):
+        return B.paged_prefill_workspace_bytes(self.handle, n_seqs, total_q, max_q_len, num_q_heads, max_blocks, opts)
+
+    def prefill(self, layer, q, out, q_indptr, block_tables, context_lens, max_q_len, num_q_heads, opts=None,
+                workspace=None, stream=None):
+        B.paged_attention_prefill(self.handle, layer, q, out, q_indptr, block_tables, context_lens, max_q_len,
+                                  num_q_heads, opts, workspace, stream)
+
     # -- raw views for tests -------------------------------------------------
     def raw(self, which):
         """The K or V buffer as a flat tensor of stored bit patterns."""

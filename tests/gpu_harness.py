@@ -16,7 +16,7 @@ import torch
 from pagedattention_decode_amd import binding as B
 from pagedattention_decode_amd.pool import PagedKVPool
 from synth import draws
-from synth.draws import TAG_K, TAG_Q, TAG_V
+from synth.draws import TAG_K, TAG_Q, TAG_QCHUNK, TAG_V
 
 
 _EXECUTOR = None
@@ -62,8 +62,11 @@ class GpuRun:
         self.appends = []
         self.decodes = []
         self.decode_outputs = []  # per decode op: {layer: tensor [S, Hq, d] float32}
+        self.prefills = []
+        self.prefill_outputs = []  # per prefill op: {layer: tensor [sum(counts), Hq, d] float32}
         self.n_append = 0
         self.n_decode = 0
+        self.n_prefill = 0
 
     def rows(self, tag, layer, writer, positions):
         wl = self.wl
@@ -138,6 +141,25 @@ class GpuRun:
                     for t in tasks:
                         fill(t)
                 pool.cache(layer, to_device_bits(kb), to_device_bits(vb), d_slots)
+        elif kind == "prefill":
+            seq_ids, counts = list(op[1]), list(op[2])
+            self.apply(("append", op[1], op[2]))
+            tables, lens = pool.tables(seq_ids, self.max_blocks)
+            if self.ref is not None:
+                rp = self.ref.prefills[self.n_prefill]
+                assert rp["seq_ids"] == seq_ids and list(rp["counts"]) == counts
+                assert list(lens) == rp["lengths"], "context lengths differ from the oracle"
+                for i, t in enumerate(rp["tables"]):
+                    assert list(tables[i, :len(t)]) == t, "block table differs from the oracle"
+            self.prefills.append({"seq_ids": seq_ids, "counts": counts, "tables": tables, "lengths": lens})
+            d_tables = torch.from_numpy(tables).cuda()
+            d_lens = torch.from_numpy(lens).cuda()
+            d_indptr = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+            outs = {}
+            for layer in self.decode_layers:
+                outs[layer] = self.prefill(self.n_prefill, layer, d_indptr, d_tables, d_lens, max(counts))
+            self.prefill_outputs.append(outs)
+            self.n_prefill += 1
         elif kind == "decode":
             seq_ids = list(op[1])
             tables, lens = pool.tables(seq_ids, self.max_blocks)
@@ -176,6 +198,27 @@ class GpuRun:
         if ws is not None:
             ws.fill_(0xFF)
         self.pool.decode(layer, q, out, d_tables, d_lens, wl.num_q_heads, opts, ws)
+        return bits_to_float_tensor(out, wl.dtype)
+
+
+    def prefill_query_bits(self, prefill_index, layer, total):
+        wl = self.wl
+        return draws.normal_bits(wl.seed, TAG_QCHUNK, (prefill_index, layer), (total, wl.num_q_heads, wl.head_dim),
+                                 wl.dtype)
+
+    def prefill(self, prefill_index, layer, d_indptr, d_tables, d_lens, max_q_len, opts=None):
+        wl = self.wl
+        n = int(d_tables.shape[0])
+        total = int(d_indptr[-1].item())
+        q = to_device_bits(self.prefill_query_bits(prefill_index, layer, total))
+        out = torch.empty_like(q)
+        out.view(torch.uint8).fill_(0xFF)  # NaN: rows the path forgets stay visible
+        opts = opts if opts is not None else self.opts
+        ws_bytes = self.pool.prefill_workspace_bytes(n, total, max_q_len, wl.num_q_heads, d_tables.shape[1], opts)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+        if ws is not None:
+            ws.fill_(0xFF)
+        self.pool.prefill(layer, q, out, d_indptr, d_tables, d_lens, max_q_len, wl.num_q_heads, opts, ws)
         return bits_to_float_tensor(out, wl.dtype)
 
 

@@ -1,0 +1,174 @@
+"""GPU parity of multi-query attention over paged history (chunked prefill and
+draft verification) against the float64 oracle.
+
+bf16 bar as for decode: max abs error 2e-2 and per-row relative L2 error 5e-3.
+Outputs and workspace start as NaN bytes, so an unwritten row fails.  Every
+test prints its case before touching the GPU.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.runner import OracleReplay
+from pagedattention_decode_amd import binding as B
+from synth import draws, workloads
+from tests.gpu_harness import GpuRun, attention_errors, bits_to_float_tensor, to_device_bits
+
+pytestmark = pytest.mark.gpu
+
+BF16_ABS, BF16_REL = 2e-2, 5e-3
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def check(got, expect, what):
+    max_abs, rel = attention_errors(got, expect)
+    print(f"  {what}: max abs {max_abs:.3e}, max row rel-L2 {rel:.3e}", flush=True)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert max_abs <= BF16_ABS and rel <= BF16_REL, what
+
+
+def chunk_workload(prompts, chunk, hq=32, hkv=8, d=128, seed=41, history=None):
+    """Prompts prefilled chunk by chunk; ``history`` tokens per prompt are appended
+    first in bulk (no queries)."""
+    seqs = tuple(range(len(prompts)))
+    ops = [("add", s) for s in seqs]
+    done = [0] * len(prompts)
+    if history:
+        ops.append(("append", seqs, tuple(history)))
+    while any(x < p for x, p in zip(done, prompts)):
+        ids = tuple(s for s in seqs if done[s] < prompts[s])
+        counts = tuple(min(chunk, prompts[s] - done[s]) for s in ids)
+        ops.append(("prefill", ids, counts))
+        for s, c in zip(ids, counts):
+            done[s] += c
+    total = [p + (history[i] if history else 0) for i, p in enumerate(prompts)]
+    blocks = sum(-(-t // 16) for t in total)
+    return workloads.Workload("chunks", seed, draws.BF16, 1, hq, hkv, d, 16, blocks + 9, ops)
+
+
+def compare_all(run, ref, what=""):
+    for i in range(len(ref.prefills)):
+        expect = ref.prefill_attention(i, 0)
+        got = run.prefill_outputs[i][0].double().cpu().numpy()
+        first = np.concatenate([[0], np.cumsum(ref.prefills[i]["counts"])])
+        for b in expect:
+            check(got[first[b]:first[b + 1]], expect[b], f"{what} prefill {i} seq {ref.prefills[i]['seq_ids'][b]}")
+
+
+def test_figure8_prompt_in_chunks_of_512():
+    announce("2048-token prompt in chunks of 512 (Figure 8 of the KV-cache chapter), Hq=32 Hkv=8 d=128")
+    wl = workloads.chunked_prompt()
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref).run()
+    compare_all(run, ref, "fig8")
+
+
+RAGGED_PROMPTS = (700, 33, 1, 517, 16, 130)
+
+
+@pytest.mark.parametrize("partition", [0, 16, 64, 256, 4096])
+def test_ragged_chunks_and_partitions(partition):
+    announce(f"prompts {RAGGED_PROMPTS} in chunks of 100 over 0..40 history tokens, partition {partition}")
+    wl = chunk_workload(RAGGED_PROMPTS, 100, history=[0, 40, 3, 17, 0, 1])
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1, opts=B.attention_options(partition_tokens=partition)).run()
+    compare_all(run, ref, f"P={partition}")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (64, 8, 128), (16, 1, 128), (32, 8, 64), (16, 4, 256),
+                                      (12, 4, 64), (48, 3, 128)])
+def test_head_shapes(hq, hkv, d):
+    announce(f"head shapes Hq={hq} Hkv={hkv} d={d}: prompts (97, 16, 5) in chunks of 40")
+    wl = chunk_workload((97, 16, 5), 40, hq=hq, hkv=hkv, d=d, history=[20, 0, 300])
+    ref = OracleReplay(wl).run()
+    for part in (0, 32):
+        run = GpuRun(wl, ref=ref, fill=-1, opts=B.attention_options(partition_tokens=part)).run()
+        compare_all(run, ref, f"P={part}")
+
+
+def test_last_chunk_of_8k_prompts_sampled():
+    announce("16 x (7680 cached + 512-token chunk), default launch; rows sampled in sequences 0, 7, 15")
+    wl = workloads.prefill_last_chunk()
+    sample = [0, 7, 15]
+    ref = OracleReplay(wl, writers=sample).run()
+    run = GpuRun(wl, ref=ref, writers=sample).run()
+    got = run.prefill_outputs[0][0].double().cpu().numpy()
+    picks = [(b, j) for b in sample for j in (0, 1, 15, 16, 63, 64, 255, 256, 510, 511)]
+    expect = ref.prefill_rows(0, 0, picks)
+    rows = [b * 512 + j for b, j in picks]
+    check(got[rows], expect, "last chunk sampled")
+
+
+def test_verify_8_drafts_full():
+    announce("16 x (8184 cached + 8 draft positions), default launch; every row checked")
+    wl = workloads.verify_drafts()
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref).run()
+    got = run.prefill_outputs[0][0].double().cpu().numpy()
+    picks = [(b, j) for b in range(16) for j in range(8)]
+    check(got, ref.prefill_rows(0, 0, picks), "verify 16 x 8")
+
+
+def test_one_row_chunks_match_decode_kernel():
+    announce("chunks of one query equal the decode kernel on the same pool")
+    wl = chunk_workload((1, 1, 1), 1, history=[300, 17, 2048])
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref).run()
+    compare_all(run, ref, "c=1")
+    rec = run.prefills[0]
+    d_tables = torch.from_numpy(rec["tables"]).cuda()
+    d_lens = torch.from_numpy(rec["lengths"]).cuda()
+    dq = to_device_bits(run.prefill_query_bits(0, 0, 3))
+    out = torch.empty_like(dq)
+    ws = torch.empty(max(run.pool.workspace_bytes(3, 32, d_tables.shape[1]), 1), dtype=torch.uint8, device="cuda")
+    run.pool.decode(0, dq, out, d_tables, d_lens, 32, None, ws)
+    dec = bits_to_float_tensor(out, wl.dtype).double().cpu().numpy()
+    pre = run.prefill_outputs[0][0].double().cpu().numpy()
+    assert np.abs(dec - pre).max() <= 2 * BF16_ABS
+
+
+def test_contract_violations_give_nan_rows_or_errors():
+    announce("chunk longer than its context or than max_q_len -> NaN rows; bad table entry -> NaN; errors")
+    wl = chunk_workload((40, 40, 40), 40, history=[10, 10, 10])
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()
+    rec = run.prefills[0]
+    tables = torch.from_numpy(rec["tables"]).cuda()
+    lens = torch.from_numpy(rec["lengths"]).cuda()
+    indptr = torch.tensor([0, 40, 80, 120], dtype=torch.int32, device="cuda")
+    lens[1] = 30            # 40 queries over 30 tokens: NaN rows
+    tables[2, 1] = wl.num_blocks + 3  # never dereferenced: NaN rows
+    out = run.prefill(0, 0, indptr, tables, lens, 40).double().cpu().numpy()
+    expect = ref.prefill_attention(0, 0)
+    check(out[0:40], expect[0], "sequence 0 unaffected")
+    assert np.isnan(out[40:80]).all()
+    # every query tile of sequence 2 reads block 1 (positions 16..31): NaN rows
+    assert np.isnan(out[80:120]).all()
+    # max_q_len smaller than a chunk: NaN rows for that sequence only
+    lens = torch.from_numpy(rec["lengths"]).cuda()
+    tables = torch.from_numpy(rec["tables"]).cuda()
+    indptr2 = torch.tensor([0, 40, 80, 81], dtype=torch.int32, device="cuda")
+    out = run.prefill(0, 0, indptr2, tables, lens, 1)
+    o = out.double().cpu().numpy()
+    assert np.isnan(o[0:80]).all()
+    # unsupported pool and bad options
+    f32 = workloads.tiny_fp32()
+    r2 = GpuRun(f32)
+    z = torch.zeros((1, 4, 64), dtype=torch.int32, device="cuda")
+    with pytest.raises(B.KVError) as e:
+        r2.pool.prefill(0, z, z.clone(), torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
+                        torch.zeros((1, 2), dtype=torch.int32, device="cuda"),
+                        torch.ones((1,), dtype=torch.int32, device="cuda"), 1, 4)
+    assert e.value.status == B.KV_ERR_UNSUPPORTED
+    q = torch.zeros((40, 32, 128), dtype=torch.int16, device="cuda")
+    with pytest.raises(B.KVError):
+        run.pool.prefill(0, q, q.clone(), indptr[:2].contiguous(), tables[:1].contiguous(), lens[:1].contiguous(),
+                         40, 32, opts=B.attention_options(partition_tokens=24))
+    with pytest.raises(B.KVError):
+        run.pool.prefill(0, q, q.clone(), indptr[:2].contiguous(), tables[:1].contiguous(), lens[:1].contiguous(),
+                         40, 30)
+    torch.cuda.synchronize()
