@@ -18,6 +18,12 @@ Workloads (synthetic, seeded; see synth/workloads.py):
   4  70B-GQA-shaped layer: 12 x 131072 tokens, Hq=64, split-K 512.
   5  agentic fork: 64 sequences (4 roots x 16 forks) x ~33K tokens, 36 layers.
 
+--op prefill / verify time the multi-query path instead (paged_attention_prefill):
+  prefill  the last 512-token chunk of 16 8K-token prompts (7680 cached tokens each),
+           reported in TFLOP/s against the bf16 matrix peak;
+  verify   8 draft positions for 16 requests with 8184 cached tokens, 4 layers,
+           reported in KV GB/s against the HBM peak.
+
 Prints one JSON line (rank 0, one GPU).
 """
 
@@ -32,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, public specification
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, public specification
 
 
 def parse():
@@ -40,6 +47,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--op", default="decode", choices=["decode", "prefill", "verify"],
+                    help="decode: the decode step of --config; prefill: the last 512-token chunk of 16 "
+                         "8K prompts; verify: 8 draft positions for 16 requests with 8K contexts")
     ap.add_argument("--layers", type=int, default=0, help="layer buffers (0 = workload default)")
     ap.add_argument("--partition", type=int, default=-1, help="partition tokens (-1 = workload default)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "generic"])
@@ -73,6 +83,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU form)", file=sys.stderr)
         sys.exit(2)
+
+    if args.op != "decode":
+        multi_query_bench(args)
+        return
 
     import numpy as np
     import torch
@@ -265,13 +279,193 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measured_traffic(workload):
+def multi_query_bench(args):
+    """Chunked prefill or draft verification through paged_attention_prefill.
+
+    A step is, for every layer, reshape_and_cache of the chunk's K/V rows (into
+    the slots the chunk owns) followed by the multi-query attention of the
+    chunk's queries.  The history is written once before warm-up; queries and
+    chunk rows for every timed step are resident in HBM.
+    """
+    import numpy as np
+    import torch
+
+    from pagedattention_decode_amd import binding as B
+    from pagedattention_decode_amd.pool import PagedKVPool
+    from synth import draws, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    prefill = args.op == "prefill"
+    base = workloads.prefill_last_chunk() if prefill else workloads.verify_drafts()
+    L = args.layers or (1 if prefill else 4)
+    seed = args.seed or base.seed
+    Hq, Hkv, d, Bs = base.num_q_heads, base.num_kv_heads, base.head_dim, base.block_size
+    hist_op = next(op for op in base.ops if op[0] == "append")
+    chunk_op = next(op for op in base.ops if op[0] == "prefill")
+    seqs, hist, counts = list(chunk_op[1]), list(hist_op[2]), list(chunk_op[2])
+    S, c = len(seqs), counts[0]
+    opts = B.attention_options(partition_tokens=max(args.partition, 0))
+
+    pool = PagedKVPool(L, base.num_blocks, Bs, Hkv, d, "bf16", free_order=draws.free_order(seed, base.num_blocks))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def randn_bf16(*shape):
+        return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    t_fill = time.time()
+    for s in seqs:
+        pool.add(s)
+    slots, _ = pool.append(seqs, hist)
+    d_hist = torch.from_numpy(slots).to(dev)
+    for layer in range(L):
+        pool.cache(layer, randn_bf16(len(slots), Hkv, d), randn_bf16(len(slots), Hkv, d), d_hist)
+    chunk_slots, _ = pool.append(seqs, counts)
+    d_slots = torch.from_numpy(chunk_slots).to(dev)
+    torch.cuda.synchronize()
+    t_fill = time.time() - t_fill
+
+    total_q = S * c
+    max_blocks = int(math.ceil((max(hist) + c) / Bs))
+    tables, lens = B.kv_get_block_tables(pool.handle, np.asarray(seqs, np.int64), max_blocks)
+    d_tables = torch.from_numpy(tables).to(dev)
+    d_lens = torch.from_numpy(lens).to(dev)
+    d_indptr = torch.arange(0, total_q + 1, c, dtype=torch.int32, device=dev)
+    total_steps = args.warmup + args.steps
+    q_in = [[randn_bf16(total_q, Hq, d) for _ in range(L)] for _ in range(total_steps)]
+    kv_in = [[(randn_bf16(total_q, Hkv, d), randn_bf16(total_q, Hkv, d)) for _ in range(L)]
+             for _ in range(total_steps)]
+    out = torch.empty((total_q, Hq, d), dtype=torch.bfloat16, device=dev)
+    ws_bytes = pool.prefill_workspace_bytes(S, total_q, c, Hq, max_blocks, opts)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    attn_ev = []
+
+    def step(i, timed):
+        for layer in range(L):
+            k_new, v_new = kv_in[i][layer]
+            pool.cache(layer, k_new, v_new, d_slots)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            pool.prefill(layer, q_in[i][layer], out, d_indptr, d_tables, d_lens, c, Hq, opts, ws)
+            if timed:
+                e1.record(stream)
+                attn_ev.append((e0, e1))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in attn_ev]
+    attn_s = float(np.mean(attn_ms)) / 1e3
+    n = lens.astype(np.int64)
+    pairs = int(sum(c * (int(x) - c) + c * (c + 1) // 2 for x in n))  # query-key pairs per head
+    flops = 4 * d * Hq * pairs                                          # QK^T and PV, per layer call
+    kv_bytes = int(n.sum()) * 2 * Hkv * d * 2                           # each sequence's keys and values
+    ideal_bytes = kv_bytes + 2 * total_q * Hq * d * 2 + 4 * int(np.ceil(n / Bs).sum())
+    calls = args.steps * L
+    result = {
+        "metric": ("multi-query paged attention TFLOP/s (chunked prefill)" if prefill
+                   else "paged-verification KV GB/s (% of HBM peak)"),
+        "value": round(flops * calls / wall / 1e12, 2) if prefill else round(kv_bytes * calls / wall / 1e9, 2),
+        "unit": "TFLOP/s" if prefill else "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": base.name,
+            "description": base.description,
+            "layers_per_step": L,
+            "sequences": S,
+            "chunk_tokens": c,
+            "history_tokens": int(hist[0]),
+            "partition_tokens": args.partition if args.partition > 0 else "auto",
+            "step": f"{L} x (reshape_and_cache of the chunk + paged_attention_prefill)",
+        },
+        "attn_call_us": round(attn_s * 1e6, 2),
+        "chunk_tokens_per_s_per_layer": round(total_q / attn_s, 1),
+        "query_key_pairs_per_head": pairs,
+        "fill_seconds": round(t_fill, 2),
+        "roofline": ({
+            "bound": "mfma",
+            "achieved": round(flops / attn_s / 1e12, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / attn_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(base.name, "prefill.hip"),
+            "kernel": "attn_prefill_kernel",
+            "algorithmic_flops_per_launch": flops,
+        } if prefill else {
+            "bound": "hbm",
+            "achieved": round(ideal_bytes / attn_s / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(ideal_bytes / attn_s / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(base.name, "prefill.hip"),
+            "kernel": "attn_prefill_kernel + merge_prefill_kernel",
+            "algorithmic_bytes_per_launch": ideal_bytes,
+        }),
+        "cpu_baseline": None if args.no_cpu_baseline else multi_query_cpu_baseline(args, base),
+    }
+    print(json.dumps(result), flush=True)
+
+
+def multi_query_cpu_baseline(args, wl):
+    """The fp64 oracle's chunk attention of sequence 0 of the workload, repeated."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.runner import OracleReplay
+
+    cores = len(os.sched_getaffinity(0))
+    ref = OracleReplay(wl, writers={0}).run()
+    rec = ref.prefills[0]
+    # the first rows of sequence 0's chunk (all of a verification chunk)
+    rows = min(rec["counts"][0], 32)
+    c, n = rows, rec["lengths"][0] - rec["counts"][0] + rows
+    pairs = c * (n - c) + c * (c + 1) // 2
+    flops = 4 * wl.head_dim * wl.num_q_heads * pairs
+    kv_bytes = n * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    reps = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while True:
+            ref.prefill_attention(0, 0, seqs=[0], first_rows=rows)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+    wall = time.perf_counter() - t0
+    prefill = args.op == "prefill"
+    return {
+        "value": round(flops * reps / wall / 1e12, 6) if prefill else round(kv_bytes * reps / wall / 1e9, 4),
+        "unit": "TFLOP/s" if prefill else "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"the oracle's chunk attention of the first {c} queries of sequence 0's chunk "
+                  f"(keys 0..{n - 1}), repeated {reps} times in {wall:.1f} s",
+        "chunk_tokens_per_s_per_layer": round(c * reps / wall, 3),
+    }
+
+
+def measured_traffic(workload, source="kernels.hip"):
     """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this
     workload, or None when there is none or the kernel source changed since it was taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
-    src = os.path.join(ROOT, "pagedattention_decode_amd", "csrc", "kernels.hip")
+    src = os.path.join(ROOT, "pagedattention_decode_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     with open(path) as f:

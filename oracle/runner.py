@@ -114,8 +114,11 @@ class OracleReplay:
         return draws.normal_bits(wl.seed, TAG_QCHUNK, (prefill_index, layer),
                                  (total, wl.num_q_heads, wl.head_dim), wl.dtype)
 
-    def prefill_attention(self, prefill_index, layer, seqs=None):
-        """float64 outputs of a recorded prefill: {batch index: [count, Hq, d]}."""
+    def prefill_attention(self, prefill_index, layer, seqs=None, first_rows=None):
+        """float64 outputs of a recorded prefill: {batch index: [count, Hq, d]}.
+
+        ``first_rows`` limits each chunk to its first rows; they see no key past
+        position h + first_rows - 1, so the keys are cut there too."""
         wl = self.wl
         rec = self.prefills[prefill_index]
         seqs = range(len(rec["seq_ids"])) if seqs is None else seqs
@@ -123,8 +126,11 @@ class OracleReplay:
         first = np.concatenate([[0], np.cumsum(rec["counts"])])
         out = {}
         for i in seqs:
-            kb, vb = self.store.gather(layer, rec["tables"][i], rec["lengths"][i])
-            out[i] = chunk_attention(q[first[i]:first[i + 1]], draws.bits_to_f64(kb, wl.dtype),
+            c = rec["counts"][i]
+            r = c if first_rows is None else min(c, first_rows)
+            n = rec["lengths"][i] - c + r
+            kb, vb = self.store.gather(layer, rec["tables"][i], n)
+            out[i] = chunk_attention(q[first[i]:first[i] + r], draws.bits_to_f64(kb, wl.dtype),
                                      draws.bits_to_f64(vb, wl.dtype))
         return out
 

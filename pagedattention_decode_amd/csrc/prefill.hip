@@ -17,10 +17,11 @@
 //
 // Work split.  Unit = (sequence, kv head).  Its queries are flattened into
 // columns f = j * G + hg (chunk row j, query head g * G + hg).  A wave owns a
-// tile of NC = 16 * NCG consecutive columns and one partition of the keys; the
-// four waves of a workgroup own four consecutive tiles of one unit and the same
-// partition, so they stream the same K/V blocks (the second to fourth reads hit
-// in L2).  Per 16-token block and 16-column group, as in the decode kernel:
+// tile of NC = 16 * NCG consecutive columns and one partition of the keys.  The
+// four waves of a workgroup own wt consecutive tiles (4 when a unit has that
+// many) times 4 / wt consecutive partitions of one unit; waves on the same
+// partition stream the same K/V blocks, so all but the first read hit in L2.
+// Per 16-token block and 16-column group, as in the decode kernel:
 //   S^T[16 tokens][16 cols] = K[16][D] . Q^T[D][16]   (D/32 x mfma 16x16x32)
 //   causal mask, online softmax (each lane holds 4 tokens of one column)
 //   O^T[D][16 cols] += V^T[D][16] . P^T[16][16]        (D/16 x mfma 16x16x16)
@@ -40,7 +41,7 @@
 namespace pagedkv {
 namespace {
 
-constexpr int kPfWaves = 4;  // waves (tiles) per workgroup
+constexpr int kPfWaves = 4;  // waves per workgroup: wt tiles x (4 / wt) partitions
 
 struct pf_args {
   const void* q;        // [total_q][Hq][D] bf16
@@ -54,59 +55,153 @@ struct pf_args {
   float* part_l;            // [total_q * Hq][max_parts]
   float* part_o;            // [total_q * Hq][max_parts][D]
   int n_seqs, total_q, max_q_len, max_blocks, n_q_heads, n_kv_heads, num_blocks;
-  int part_blocks, max_parts, tile_groups, cols_per_tile;
+  int part_blocks, max_parts, cols_per_tile;
+  int wt;                        // tiles per workgroup (1, 2 or 4); the other factor of 4 is partitions
+  int tile_groups, part_groups;  // workgroups per unit along tiles and along partitions
   float scale_log2;
 };
 
-// One 16-token block for one 16-column group: scores, causal mask, online
-// softmax, weighted values.  `lim` (per lane) is the number of leading slots
-// of the block visible to this lane's column (0 .. 16).  The V tail beyond the
-// context has already been zeroed.
+// Two consecutive 16-token blocks in registers.  K as for the decode kernel
+// (the A operands of S^T = K Q^T); V regrouped for mfma 16x16x32 over the 32
+// tokens: v[t] holds, for d-tile t (16 dims), the lane's 4 tokens of the first
+// block in dwords 0-1 and its 4 tokens of the second block in dwords 2-3, so
+// that it is the A operand of O^T += V^T P^T as loaded (two 8-byte loads from
+// the two blocks' V tiles, same cache lines as one 16-byte load each).
 template <int D>
-__device__ __forceinline__ void attend_cols(const kv_regs<D>& cur, const bf16x8_t* qop, int lim, int quad,
-                                            float scale_log2, f32x4_t* o, float& m_run, float& l_lane) {
-  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk], s, 0, 0, 0);
+struct kv_pair {
+  uint4 ka[D / 32];
+  uint4 kb[D / 32];
+  uint4 v[D / 16];
+};
 
-  float sv[4];
-  float mb = -INFINITY;
+template <int D>
+__device__ __forceinline__ void load_pair(kv_pair<D>& r, const uint4* kta, const uint4* vta, const uint4* ktb,
+                                          const uint4* vtb, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sv[i] = (quad * 4 + i < lim) ? s[i] * scale_log2 : -INFINITY;
-    mb = fmaxf(mb, sv[i]);
+  for (int i = 0; i < D / 32; ++i) r.ka[i] = kta[i * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) r.kb[i] = ktb[i * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const uint2* va = reinterpret_cast<const uint2*>(vta + i * 64 + lane);
+    const uint2* vb = reinterpret_cast<const uint2*>(vtb + i * 64 + lane);
+    const uint2 a0 = va[0], a1 = va[1], b0 = vb[0], b1 = vb[1];
+    r.v[2 * i] = make_uint4(a0.x, a0.y, b0.x, b0.y);
+    r.v[2 * i + 1] = make_uint4(a1.x, a1.y, b1.x, b1.y);
   }
-  mb = fmaxf(mb, __shfl_xor(mb, 16));
-  mb = fmaxf(mb, __shfl_xor(mb, 32));
-  const bool grow = mb > m_run + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch
-    const float m_new = grow ? mb : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf, 1 when kept
-    l_lane *= alpha;
+}
+
+// Zeroes the V values of slots >= valid_a of the first block and >= valid_b
+// of the second (memory past the context may hold anything).
+template <int D>
+__device__ __forceinline__ void zero_pair_tail(kv_pair<D>& r, int valid_a, int valid_b, int quad) {
+  uint32_t ma[2], mb[2];
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
-    m_run = m_new;
+  for (int dw = 0; dw < 2; ++dw) {
+    const int slot0 = quad * 4 + dw * 2;
+    ma[dw] = (slot0 < valid_a ? 0x0000ffffu : 0u) | (slot0 + 1 < valid_a ? 0xffff0000u : 0u);
+    mb[dw] = (slot0 < valid_b ? 0x0000ffffu : 0u) | (slot0 + 1 < valid_b ? 0xffff0000u : 0u);
   }
-  float pv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pv[i] = (sv[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_run);
-  // P^T in bf16 (round to nearest even); the denominator sums the rounded
-  // weights, so the weights applied to V are exactly normalised
-  const bf16x2_t p01 = __builtin_convertvector((f32x2_t{pv[0], pv[1]}), bf16x2_t);
-  const bf16x2_t p23 = __builtin_convertvector((f32x2_t{pv[2], pv[3]}), bf16x2_t);
-  const uint32_t w01 = __builtin_bit_cast(uint32_t, p01);
-  const uint32_t w23 = __builtin_bit_cast(uint32_t, p23);
-  l_lane += (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xffff0000u)) +
-            (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xffff0000u));
-  const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(w01, w23));
+  for (int t = 0; t < D / 16; ++t) {
+    r.v[t].x &= ma[0];
+    r.v[t].y &= ma[1];
+    r.v[t].z &= mb[0];
+    r.v[t].w &= mb[1];
+  }
+}
+
+// Two consecutive 16-token blocks (32 tokens) for all NCG 16-column groups.
+//   1. S^T of both blocks for every group: 2 * NCG independent chains of
+//      D/32 x mfma 16x16x32; the Q^T operands come from LDS (the wave's own
+//      copy, in operand order), which leaves the registers to the K/V ring
+//      and the accumulators.
+//   2. Online softmax per group over the 8 scores a lane holds (tokens
+//      4q..4q+3 of each block, q = lane / 16, for column lane % 16); one vote
+//      over the wave decides whether any group's running maximum moves.  The
+//      scale is applied in the exponent: p = 2^(s * c - m).
+//   3. O^T += V^T P^T with mfma 16x16x32 over the 32 tokens: contraction index
+//      k = 8q + i is token 4q + i of the first block for i < 4 and token
+//      4q + i - 4 of the second for i >= 4 (the order of kv_pair::v), so the B
+//      operand is the two blocks' P^T operands side by side.
+// MASKED: `lim_a`, `lim_b` (per lane and group) are the numbers of leading
+// slots of each block visible to the lane's column; otherwise every slot of
+// both blocks is visible to every column.  V tails beyond the context are
+// already zero.
+template <int D, int NCG, bool MASKED>
+__device__ __forceinline__ void attend_pair(const kv_pair<D>& kv, const bf16x8_t* q_lds, int lane,
+                                            const int* lim_a, const int* lim_b, int quad, float c,
+                                            f32x4_t (&o)[NCG][D / 16], float* m_run, float* l_lane) {
+  f32x4_t sa[NCG], sb[NCG];
 #pragma unroll
-  for (int pp = 0; pp < D / 32; ++pp) {
-    const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
-    o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop, o[2 * pp],
-                                                          0, 0, 0);
-    o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[1]), pop,
-                                                              o[2 * pp + 1], 0, 0, 0);
+  for (int cg = 0; cg < NCG; ++cg) {
+    sa[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sb[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const bf16x8_t qk = q_lds[(cg * (D / 32) + kk) * 64 + lane];
+      sa[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.ka[kk]), qk, sa[cg], 0, 0, 0);
+      sb[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.kb[kk]), qk, sb[cg], 0, 0, 0);
+    }
+  }
+  float mb[NCG];
+  bool grow_any = false;
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    if (MASKED) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (quad * 4 + i >= lim_a[cg]) sa[cg][i] = -INFINITY;
+        if (quad * 4 + i >= lim_b[cg]) sb[cg][i] = -INFINITY;
+      }
+    }
+    float m = fmaxf(fmaxf(fmaxf(sa[cg][0], sa[cg][1]), fmaxf(sa[cg][2], sa[cg][3])),
+                    fmaxf(fmaxf(sb[cg][0], sb[cg][1]), fmaxf(sb[cg][2], sb[cg][3])));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    mb[cg] = m * c;
+    grow_any |= mb[cg] > m_run[cg] + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow_any)) {  // wave-uniform branch, rare after the first blocks
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const float m_new = mb[cg] > m_run[cg] + kRescaleSlack ? mb[cg] : m_run[cg];
+      const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_new);  // 0 when m_run = -inf, 1 when kept
+      l_lane[cg] *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) o[cg][i] *= alpha;
+      m_run[cg] = m_new;
+    }
+  }
+  bf16x8_t pop[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const float nm = -m_run[cg];
+    float pa[4], pb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pa[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[cg][i], c, nm));
+      pb[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[cg][i], c, nm));
+      if (MASKED) {  // a column that has seen no visible key keeps m = -inf
+        pa[i] = sa[cg][i] == -INFINITY ? 0.f : pa[i];
+        pb[i] = sb[cg][i] == -INFINITY ? 0.f : pb[i];
+      }
+    }
+    l_lane[cg] += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
+    const bf16x2_t p0 = __builtin_convertvector((f32x2_t{pa[0], pa[1]}), bf16x2_t);
+    const bf16x2_t p1 = __builtin_convertvector((f32x2_t{pa[2], pa[3]}), bf16x2_t);
+    const bf16x2_t p2 = __builtin_convertvector((f32x2_t{pb[0], pb[1]}), bf16x2_t);
+    const bf16x2_t p3 = __builtin_convertvector((f32x2_t{pb[2], pb[3]}), bf16x2_t);
+    pop[cg] = __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                                      __builtin_bit_cast(uint32_t, p2),
+                                                      __builtin_bit_cast(uint32_t, p3)));
+  }
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      o[cg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.v[t]), pop[cg], o[cg][t], 0,
+                                                         0, 0);
   }
 }
 
@@ -132,26 +227,28 @@ __device__ __forceinline__ int pf_tile_keys(const pf_seq& q, int G, int tile, in
   return q.h + f_last / G + 1;
 }
 
-template <int D, int NCG>
+template <int D, int NCG, int STAGES>
 __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) {
   constexpr int NC = 16 * NCG;
   const int lane = threadIdx.x & 63;
   const int quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int bid = blockIdx.x;
-  const int part = bid % a.max_parts;
-  bid /= a.max_parts;
+  const int pg = bid % a.part_groups;
+  bid /= a.part_groups;
   const int tg = bid % a.tile_groups;
   bid /= a.tile_groups;
   const int g = bid % a.n_kv_heads;
   const int s = bid / a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
-  const int tile = tg * kPfWaves + wave;
+  const int tile = tg * a.wt + wave % a.wt;
+  const int part = pg * (kPfWaves / a.wt) + wave / a.wt;
 
   const pf_seq sq = pf_locate(a, s);
   if (sq.c <= 0 || sq.q0 < 0 || sq.q0 + sq.c > a.total_q) return;  // nothing, or rows outside the output
   const int cols = sq.c * G;
   uint16_t* out = static_cast<uint16_t*>(a.out);
+  if (part >= a.max_parts) return;
   if (sq.bad) {  // one wave per unit marks the unit's rows
     if (part == 0 && tile == 0)
       for (int i = lane; i < cols * D; i += 64) {
@@ -170,10 +267,11 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
   const int b_end = (min(kend, k_begin + P) + 15) >> 4;
   const int f0 = tile * NC;
 
-  // this lane's column in every group, and each group's last visible position
-  bf16x8_t qop[NCG][D / 32];
+  // this lane's column in every group; the Q^T operands of the wave's tile
+  // go to its LDS slice in operand order (lane l's 16 bytes at l * 16)
+  extern __shared__ __align__(16) bf16x8_t pf_q_lds[];
+  bf16x8_t* q_lds = pf_q_lds + wave * (NCG * (D / 32) * 64);
   int pos[NCG];
-  int gmax[NCG];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     const int f = f0 + cg * 16 + (lane & 15);
@@ -181,27 +279,31 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
     const int j = live ? f / G : 0;
     const int hg = live ? f % G : 0;
     pos[cg] = live ? sq.h + j : -1;
-    gmax[cg] = (f0 + cg * 16 < cols) ? sq.h + min(f0 + cg * 16 + 15, cols - 1) / G : -1;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                          (static_cast<int64_t>(sq.q0 + j) * a.n_q_heads + g * G + hg) * D + quad * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
-      qop[cg][kk] = live ? *reinterpret_cast<const bf16x8_t*>(qp + kk * 32) : bf16x8_t{};
+      q_lds[(cg * (D / 32) + kk) * 64 + lane] = live ? *reinterpret_cast<const bf16x8_t*>(qp + kk * 32) : bf16x8_t{};
   }
+  const int pos_min = sq.h + f0 / G;  // position of the tile's first column: older keys are visible to all
 
   const uint4* kpool = static_cast<const uint4*>(a.k_layer);
   const uint4* vpool = static_cast<const uint4*>(a.v_layer);
   constexpr int kTileVec = 16 * D * 2 / 16;  // 16-byte vectors per tile
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
-  // two-deep register ring; loads past the run repeat its last block (L2 hits)
-  kv_regs<D> buf[2];
-  int phys_ring[2];
+  // ring of STAGES block pairs; loads past the run repeat its last block (L2 hits)
+  kv_pair<D> buf[STAGES];
+  int phys_a[STAGES], phys_b[STAGES];
   auto issue = [&](int u, int b) {
-    const int phys = trow[min(b, b_end - 1)];
-    phys_ring[u] = phys;
-    const int p = (phys < 0 || phys >= a.num_blocks) ? 0 : phys;  // never dereferenced out of range
-    const int64_t t = (static_cast<int64_t>(p) * a.n_kv_heads + g) * kTileVec;
-    load_block<D>(buf[u], kpool + t, vpool + t, lane);
+    const int pa = trow[min(b, b_end - 1)];
+    const int pb = trow[min(b + 1, b_end - 1)];
+    phys_a[u] = pa;
+    phys_b[u] = pb;
+    const int qa = (pa < 0 || pa >= a.num_blocks) ? 0 : pa;  // never dereferenced out of range
+    const int qb = (pb < 0 || pb >= a.num_blocks) ? 0 : pb;
+    const int64_t ta = (static_cast<int64_t>(qa) * a.n_kv_heads + g) * kTileVec;
+    const int64_t tb = (static_cast<int64_t>(qb) * a.n_kv_heads + g) * kTileVec;
+    load_pair<D>(buf[u], kpool + ta, vpool + ta, kpool + tb, vpool + tb, lane);
   };
 
   f32x4_t o[NCG][D / 16];
@@ -214,27 +316,37 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
     l_lane[cg] = 0.f;
   }
   bool poisoned = false;
+  const float c = a.scale_log2;
 
-  issue(0, b_begin);
-  issue(1, b_begin + 1);
-  for (int b0 = b_begin; b0 < b_end; b0 += 2) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int b = b0 + u;
+  for (int u = 0; u < STAGES; ++u) issue(u, b_begin + 2 * u);
+  for (int b0 = b_begin; b0 < b_end; b0 += 2 * STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      const int b = b0 + 2 * u;
+      // keeps the LDS reads of Q^T inside the loop instead of hoisted into registers
+      asm volatile("" ::: "memory");
       if (b < b_end) {
-        const int phys = phys_ring[u];
-        const bool bad = phys < 0 || phys >= a.num_blocks;
-        poisoned |= bad;
-        const int valid = bad ? 0 : min(16, sq.n - b * 16);
-        if (valid < 16) zero_v_tail<D>(buf[u], valid, quad);
+        const bool has_b = b + 1 < b_end;  // else the second block is outside the partition: all masked
+        const bool bad_a = phys_a[u] < 0 || phys_a[u] >= a.num_blocks;
+        const bool bad_b = phys_b[u] < 0 || phys_b[u] >= a.num_blocks;
+        poisoned |= bad_a || (has_b && bad_b);
+        const int valid_a = bad_a ? 0 : min(16, sq.n - b * 16);
+        const int valid_b = (!has_b || bad_b) ? 0 : min(16, sq.n - (b + 1) * 16);
+        if (valid_a < 16 || valid_b < 16) zero_pair_tail<D>(buf[u], valid_a, valid_b, quad);
+        if (valid_a == 16 && valid_b == 16 && b * 16 + 31 <= pos_min) {
+          attend_pair<D, NCG, false>(buf[u], q_lds, lane, nullptr, nullptr, quad, c, o, m_run, l_lane);
+        } else {
+          int lim_a[NCG], lim_b[NCG];
 #pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
-          if (b * 16 > gmax[cg]) continue;  // wave-uniform: the whole group is masked
-          const int lim = min(max(min(pos[cg] - b * 16 + 1, valid), 0), 16);
-          attend_cols<D>(buf[u], qop[cg], lim, quad, a.scale_log2, o[cg], m_run[cg], l_lane[cg]);
+          for (int cg = 0; cg < NCG; ++cg) {
+            lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
+            lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
+          }
+          attend_pair<D, NCG, true>(buf[u], q_lds, lane, lim_a, lim_b, quad, c, o, m_run, l_lane);
         }
       }
-      issue(u, b + 2);
+      issue(u, b + 2 * STAGES);
     }
   }
 
@@ -277,7 +389,9 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
 // Folds the partitions of every (query row, head) whose tile had more than one:
 // M = max_p m_p, out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p.  A
 // partition that saw no key of the row has m = -inf and weight 0; a poisoned
-// one carries NaN into the row.  One wave per (row, head).
+// one carries NaN into the row.  One wave per (row, head): lane p holds the
+// weight of partition p (64 at a time), then every lane accumulates its
+// dimensions over the partitions.
 constexpr int kPfMergeWaves = 4;
 
 template <int D>
@@ -304,26 +418,35 @@ __global__ void __launch_bounds__(kPfMergeWaves * 64) merge_prefill_kernel(pf_ar
   const int64_t base = item * a.max_parts;
   float M = -INFINITY;
   bool nan_seen = false;
-  for (int p = 0; p < n_parts; ++p) {
-    const float m = a.part_m[base + p];
-    nan_seen |= m != m;
+  for (int p0 = 0; p0 < n_parts; p0 += 64) {
+    const float m = p0 + lane < n_parts ? a.part_m[base + p0 + lane] : -INFINITY;
+    nan_seen |= __builtin_amdgcn_ballot_w64(m != m) != 0;
     M = fmaxf(M, m);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   constexpr int E = (D + 63) / 64;  // dims per lane
   float acc[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) acc[i] = 0.f;
   float L = 0.f;
-  for (int p = 0; p < n_parts; ++p) {
-    const float m = a.part_m[base + p];
-    if (m == -INFINITY || m != m) continue;
-    const float w = exp2f(m - M);
-    L += w * a.part_l[base + p];
-    const float* po = a.part_o + (base + p) * D;
+  for (int p0 = 0; p0 < n_parts; p0 += 64) {
+    const int p = p0 + lane;
+    const float m = p < n_parts ? a.part_m[base + p] : -INFINITY;
+    const float w = (m == -INFINITY || m != m) ? 0.f : exp2f(m - M);
+    L += w == 0.f ? 0.f : w * a.part_l[base + p];
+    const int np = min(64, n_parts - p0);
+    for (int k = 0; k < np; ++k) {
+      const float wk = __shfl(w, k);
+      if (wk == 0.f) continue;  // wave uniform
+      const float* po = a.part_o + (base + p0 + k) * D;
 #pragma unroll
-    for (int i = 0; i < E; ++i)
-      if (lane + 64 * i < D) acc[i] += w * po[lane + 64 * i];
+      for (int i = 0; i < E; ++i)
+        if (lane + 64 * i < D) acc[i] += wk * po[lane + 64 * i];
+    }
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
   uint16_t* orow = static_cast<uint16_t*>(a.out) + item * D;
 #pragma unroll
   for (int i = 0; i < E; ++i)
@@ -337,7 +460,9 @@ __global__ void __launch_bounds__(kPfMergeWaves * 64) merge_prefill_kernel(pf_ar
 struct pf_plan {
   int ncg;          // 16-column groups per wave
   int tiles;        // tiles per sequence (upper bound)
-  int tile_groups;  // workgroups per (sequence, kv head, partition)
+  int wt;           // tiles per workgroup
+  int tile_groups;  // workgroups per unit along tiles
+  int part_groups;  // workgroups per unit along partitions
   int partition;    // tokens per partition
   int max_parts;
   float scale;
@@ -363,10 +488,10 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
   p.scale = o.scale > 0.f ? o.scale : 1.f / std::sqrt(static_cast<float>(c.head_dim));
   const int64_t cols = static_cast<int64_t>(max_q_len) * G;
-  const int max_ncg = c.head_dim >= 256 ? 2 : 4;
-  p.ncg = cols <= 16 ? 1 : (cols <= 32 || max_ncg == 2 ? 2 : 4);
+  p.ncg = cols <= 16 ? 1 : 2;
   p.tiles = static_cast<int>((cols + 16 * p.ncg - 1) / (16 * p.ncg));
-  p.tile_groups = (p.tiles + kPfWaves - 1) / kPfWaves;
+  p.wt = p.tiles >= 4 ? 4 : (p.tiles >= 2 ? 2 : 1);
+  p.tile_groups = (p.tiles + p.wt - 1) / p.wt;
   const int64_t max_ctx = static_cast<int64_t>(max_blocks) * 16;
   if (o.partition_tokens > 0) {
     p.partition = o.partition_tokens;
@@ -383,7 +508,9 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
     }
   }
   p.max_parts = static_cast<int>((max_ctx + p.partition - 1) / p.partition);
-  const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * p.tile_groups * p.max_parts;
+  const int wp = kPfWaves / p.wt;
+  p.part_groups = (p.max_parts + wp - 1) / wp;
+  const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * p.tile_groups * p.part_groups;
   if (grid > 0x7fffffff) return fail(KV_ERR_INVALID, "grid too large");
   return KV_OK;
 }
@@ -394,9 +521,14 @@ uint64_t pf_workspace(const kv_pool_config& c, int total_q, int num_q_heads, con
   return 2 * up256(rows * 4) + up256(rows * c.head_dim * 4);
 }
 
+// Ring depth in block pairs: the wider tiles hold more accumulators and fewer
+// blocks in flight.
 template <int D, int NCG>
 hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_prefill_kernel<D, NCG>), dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64), 0, st, a);
+  constexpr int kStages = D >= 256 ? 1 : 2;
+  constexpr size_t kLds = static_cast<size_t>(kPfWaves) * NCG * (D / 32) * 64 * 16;  // Q^T operands per wave
+  hipLaunchKernelGGL((attn_prefill_kernel<D, NCG, kStages>), dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64),
+                     kLds, st, a);
   return hipGetLastError();
 }
 
@@ -404,7 +536,6 @@ template <int D>
 hipError_t pf_launch_d(const pf_args& a, int ncg, int64_t grid, hipStream_t st) {
   if (ncg == 1) return pf_launch<D, 1>(a, grid, st);
   if (ncg == 2) return pf_launch<D, 2>(a, grid, st);
-  if constexpr (D < 256) return pf_launch<D, 4>(a, grid, st);
   return hipErrorInvalidValue;
 }
 
@@ -477,11 +608,13 @@ kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, v
   a.num_blocks = c.num_blocks;
   a.part_blocks = p.partition / 16;
   a.max_parts = p.max_parts;
+  a.wt = p.wt;
   a.tile_groups = p.tile_groups;
+  a.part_groups = p.part_groups;
   a.cols_per_tile = 16 * p.ncg;
   a.scale_log2 = p.scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * p.tile_groups * p.max_parts;
+  const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * p.tile_groups * p.part_groups;
   hipError_t e;
   switch (c.head_dim) {
     case 64: e = pf_launch_d<64>(a, p.ncg, grid, st); break;

@@ -241,3 +241,7 @@ def test_prefill_rows_match_chunk_attention():
     rows = ref.prefill_rows(1, 0, picks)
     for r, (b, j) in zip(rows, picks):
         np.testing.assert_allclose(r, full[b][j], rtol=0, atol=1e-13)
+    # the first rows of a chunk see no key past h + rows - 1: cutting the keys there changes nothing
+    head = ref.prefill_attention(1, 0, first_rows=5)
+    for b in head:
+        np.testing.assert_allclose(head[b], full[b][:5], rtol=0, atol=1e-13)
