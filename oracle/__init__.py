@@ -37,9 +37,13 @@ Modules:
                                the chunk ([KVM] chunked prefill mechanism,
                                Figure 8; [INF] §8.2.3 pair counts, §8.5.1
                                verification of draft positions).
+* :mod:`oracle.quant`         grouped 8- and 4-bit KV codes with a half scale
+                               per 32 values (q8_0, q4_0), their byte budget
+                               and read/convert trade-off ([INF] §8.4.2,
+                               Figure 8-23), and a quantised logical pool.
 * :mod:`oracle.runner`        replays a :mod:`synth` workload through the above.
 
-Every function is pinned by ``tests/test_oracle_pins.py`` and
-``tests/test_prefill_pins.py`` against values the
+Every function is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_prefill_pins.py`` and ``tests/test_quant_pins.py`` against values the
 pages print, closed forms, invariants and brute force.  Parity unpinned: none.
 """

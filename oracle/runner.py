@@ -20,6 +20,7 @@ from .attention import decode_attention
 from .block_manager import BlockManager
 from .kv_store import KVStore
 from .prefill import chunk_attention
+from .quant import QuantKVStore
 
 
 class OracleReplay:
@@ -27,8 +28,15 @@ class OracleReplay:
         self.wl = wl
         order = draws.free_order(wl.seed, wl.num_blocks) if free_order is None else free_order
         self.bm = BlockManager(wl.num_blocks, wl.block_size, order)
-        self.store = KVStore(wl.num_layers, wl.num_blocks, wl.block_size, wl.num_kv_heads,
-                             wl.head_dim, draws.storage_np_dtype(wl.dtype), background, layers)
+        self.kv_format = getattr(wl, "kv_format", None)
+        if self.kv_format:
+            if background is not None:
+                raise ValueError("a quantised pool has no background pattern")
+            self.store = QuantKVStore(wl.num_layers, wl.num_blocks, wl.block_size, wl.num_kv_heads,
+                                      wl.head_dim, self.kv_format, wl.dtype, layers)
+        else:
+            self.store = KVStore(wl.num_layers, wl.num_blocks, wl.block_size, wl.num_kv_heads,
+                                 wl.head_dim, draws.storage_np_dtype(wl.dtype), background, layers)
         self.layers = list(range(wl.num_layers)) if layers is None else list(layers)
         self.writers = None if writers is None else set(writers)
         self.appends = []  # (seq_ids, counts, slots, pairs)
@@ -39,6 +47,14 @@ class OracleReplay:
         for op in (self.wl.ops if ops is None else ops):
             self.apply(op)
         return self
+
+    def gather_f64(self, layer, table, n):
+        """K and V [n, Hkv, d] float64 of a sequence: widened stored values, or the
+        dequantised values of a quantised pool."""
+        if self.kv_format:
+            return self.store.gather_f64(layer, table, n)
+        kb, vb = self.store.gather(layer, table, n)
+        return draws.bits_to_f64(kb, self.wl.dtype), draws.bits_to_f64(vb, self.wl.dtype)
 
     def rows(self, tag, layer, writer, positions):
         wl = self.wl
@@ -103,9 +119,8 @@ class OracleReplay:
         q = draws.bits_to_f64(self.query_bits(decode_index, layer), wl.dtype)
         out = []
         for i in rows:
-            kb, vb = self.store.gather(layer, dec["tables"][i], dec["lengths"][i])
-            out.append(decode_attention(q[i], draws.bits_to_f64(kb, wl.dtype),
-                                        draws.bits_to_f64(vb, wl.dtype)))
+            k, v = self.gather_f64(layer, dec["tables"][i], dec["lengths"][i])
+            out.append(decode_attention(q[i], k, v))
         return np.stack(out)
 
     def prefill_query_bits(self, prefill_index, layer):
@@ -129,9 +144,8 @@ class OracleReplay:
             c = rec["counts"][i]
             r = c if first_rows is None else min(c, first_rows)
             n = rec["lengths"][i] - c + r
-            kb, vb = self.store.gather(layer, rec["tables"][i], n)
-            out[i] = chunk_attention(q[first[i]:first[i] + r], draws.bits_to_f64(kb, wl.dtype),
-                                     draws.bits_to_f64(vb, wl.dtype))
+            k, v = self.gather_f64(layer, rec["tables"][i], n)
+            out[i] = chunk_attention(q[first[i]:first[i] + r], k, v)
         return out
 
     def prefill_rows(self, prefill_index, layer, picks):
@@ -145,7 +159,6 @@ class OracleReplay:
         out = []
         for i, j in picks:
             n = rec["lengths"][i] - rec["counts"][i] + j + 1
-            kb, vb = self.store.gather(layer, rec["tables"][i], n)
-            out.append(decode_attention(q[first[i] + j], draws.bits_to_f64(kb, wl.dtype),
-                                        draws.bits_to_f64(vb, wl.dtype)))
+            k, v = self.gather_f64(layer, rec["tables"][i], n)
+            out.append(decode_attention(q[first[i] + j], k, v))
         return np.stack(out)

@@ -49,6 +49,7 @@ class Workload:
     ops: list = field(default_factory=list)
     partition_tokens: int = 0  # 0: let the library choose
     description: str = ""
+    kv_format: str = ""  # "", "q8_0" or "q4_0": the pool stores the rows quantised
 
     @property
     def group(self) -> int:
