@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "q8_0", "q4_0"],
+                    help="storage of the KV pool for --op decode: bf16, or q8_0 / q4_0 codes with one 2-byte "
+                         "scale per 32 values (written by reshape_and_cache, dequantised in the kernel)")
     ap.add_argument("--op", default="decode", choices=["decode", "prefill", "verify"],
                     help="decode: the decode step of --config; prefill: the last 512-token chunk of 16 "
                          "8K prompts; verify: 8 draft positions for 16 requests with 8K contexts")
@@ -118,7 +121,9 @@ def main():
     step_appends = any(op[0] == "append" for op in step_ops)
     S = len(decode_seqs)
 
-    pool = PagedKVPool(L, base.num_blocks, Bs, Hkv, d, "bf16", free_order=draws.free_order(seed, base.num_blocks))
+    pool = PagedKVPool(L, base.num_blocks, Bs, Hkv, d, args.kv, free_order=draws.free_order(seed, base.num_blocks))
+    # bytes of one token's K and V in one layer, as stored (codes + scales when quantised)
+    kv_tok = 2 * Hkv * (d * 2 if args.kv == "bf16" else d * (8 if args.kv == "q8_0" else 4) // 8 + d // 32 * 2)
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
 
@@ -199,7 +204,7 @@ def main():
             if timed:
                 e1.record(stream)
                 attn_ev.append((e0, e1))
-                logical_bytes[0] += int(lens.astype(np.int64).sum()) * 2 * Hkv * d * 2
+                logical_bytes[0] += int(lens.astype(np.int64).sum()) * kv_tok
         return lens
 
     for i in range(args.warmup):
@@ -229,7 +234,7 @@ def main():
     uniq = set()
     for r in range(S):
         uniq.update(tables[r, :int(math.ceil(lens[r] / Bs))].tolist())
-    unique_kv_bytes = len(uniq) * Bs * 2 * Hkv * d * 2
+    unique_kv_bytes = len(uniq) * Bs * kv_tok
 
     result = {
         "metric": "paged-decode KV GB/s (% of HBM peak) + attention tokens/s per layer",
@@ -252,6 +257,8 @@ def main():
             "context_tokens_first_step": int(lens_hist[0].max()) if lens_hist else None,
             "partition_tokens": partition or "auto",
             "kernel": args.kernel,
+            "kv_storage": args.kv,
+            "kv_bytes_per_token_per_layer": kv_tok,
             "step": (f"append + {L} x (reshape_and_cache + paged_attention_decode)" if step_appends
                      else f"{L} x paged_attention_decode"),
         },
@@ -502,9 +509,15 @@ def cpu_baseline(args):
         wl = workloads.agentic_fork(steps=1, layers=1)
         layers, writers = [0], {0, 1}
         sample = "fork workload: the oracle's decode of sequences 0 and 1 (32770 tokens), layer 0, step 0"
+    if args.kv != "bf16":
+        from dataclasses import replace
+
+        wl = replace(wl, kv_format=args.kv)
+        sample += f", {args.kv} pool"
     ref = OracleReplay(wl, layers=layers, writers=writers).run()
     rows = list(range(len(ref.decodes[0]["seq_ids"]))) if writers is None else sorted(writers)
-    kv_per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    kv_per_tok = 2 * wl.num_kv_heads * (wl.head_dim * wl.elem_bytes if args.kv == "bf16" else
+                                        wl.head_dim * (8 if args.kv == "q8_0" else 4) // 8 + wl.head_dim // 16)
     bytes_one = sum(ref.decodes[0]["lengths"][r] for r in rows) * kv_per_tok
     reps = 0
     c0 = time.process_time()

@@ -52,7 +52,11 @@ typedef enum {
   KV_ERR_UNSUPPORTED = 5  /* valid but not implemented shape / dtype / kernel */
 } kv_status;
 
-typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
+/* KV_Q8_0, KV_Q4_0: the pool stores K and V quantised in groups of 32 values
+ * with one 2-byte scale per group ([INF] §8.4.2, Figure 8-23: 34 and 18
+ * bytes per 32 values); new rows, q and out are bf16.  Quantised pools need
+ * B = 16 and d in {64, 128, 256}. */
+typedef enum { KV_F32 = 0, KV_BF16 = 1, KV_Q8_0 = 2, KV_Q4_0 = 3 } kv_dtype;
 
 typedef struct {
   int32_t num_layers;   /* L */
@@ -60,7 +64,7 @@ typedef struct {
   int32_t block_size;   /* B tokens per block */
   int32_t num_kv_heads; /* Hkv */
   int32_t head_dim;     /* d; a multiple of 32, at most 256 */
-  int32_t dtype;        /* kv_dtype of K, V, q and out */
+  int32_t dtype;        /* kv_dtype of K and V (and of q and out unless quantised) */
 } kv_pool_config;
 
 typedef struct kv_pool kv_pool; /* opaque */
@@ -90,6 +94,21 @@ typedef struct {
  * so that one 16-byte load brings X dimensions of one key, or 4 slots of
  * two value dimensions 16 apart; these are the operand orders of the
  * gfx950 bf16 matrix instructions used by the decode kernel.
+ *
+ * Quantised pools (B = 16).  A value x of a group of 32 (32 consecutive
+ * dimensions 32 g .. 32 g + 31 of one slot of one KV head) is stored as a code
+ * c with x ~ c * s: s = max|x| / M (M = 127 for q8_0, 7 for q4_0) in float32,
+ * rounded to the nearest IEEE half (saturating at 65504), and
+ * c = rint(x / s) (float32 quotient, ties to even, clamped to [-M, M]; 0 when
+ * s = 0).  A tile is T = 16 d bits/8 code bytes followed by 16 x d/32 scales
+ * (half, at T + (r * d/32 + g) * 2), tile(l, p, g) = ((l * N + p) * Hkv + g) *
+ * (T + d) bytes.  Codes sit per matrix-core lane L = 16 q + r (q < 4, r < 16),
+ * which owns the d * bits / 32 bytes at L * d * bits / 32:
+ *     K, lane (q, r): slot r, dims 32 k + 8 q + j (k < d/32, j < 8) at
+ *         q8_0 byte 8 k + j; q4_0 byte 4 k + j/2, low nibble for even j;
+ *     V, lane (q, r): dim 16 t + r of slots 4 q + i (t < d/16, i < 4) at
+ *         q8_0 byte 4 t + i; q4_0 byte 4 (t/2) + i, low nibble for even t.
+ * q8_0 codes are two's-complement bytes, q4_0 codes are stored as c + 8.
  * ---------------------------------------------------------------------- */
 
 /* Bytes the caller must allocate for the K and the V buffer. */
@@ -184,8 +203,9 @@ const char* kv_last_error(void);
 /* Scatter new key/value rows into the pool of one layer ([KVM] paged KV
  * allocation: the token's K and V go to T[l] at offset o; [BT] §11: decode
  * appends one KV slot per sequence).  k_new, v_new: device [n_tokens][Hkv][d]
- * in the pool dtype; d_slot_mapping: device int64[n_tokens], slot = p * B + r.
- * Slots < 0 or >= N * B are skipped.  Bitwise copy. */
+ * in the pool dtype (bf16 for a quantised pool); d_slot_mapping: device
+ * int64[n_tokens], slot = p * B + r.  Slots < 0 or >= N * B are skipped.
+ * Bitwise copy, or quantisation as described above for q8_0 / q4_0 pools. */
 kv_status reshape_and_cache(kv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
                             const int64_t* d_slot_mapping, int32_t n_tokens, void* hip_stream);
 
@@ -198,9 +218,11 @@ kv_status copy_blocks(kv_pool* pool, const int64_t* d_pairs, int32_t n_pairs, vo
 
 typedef enum {
   KV_KERNEL_AUTO = 0,    /* the matrix-core kernel where it applies, else generic */
-  KV_KERNEL_GENERIC = 1, /* vector-ALU kernel: any dtype, B, d, G <= 16 */
-  KV_KERNEL_MFMA = 2     /* bf16, B = 16, d in {64, 128, 256}, G <= 16,
-                            at most 4095 sequences per call */
+  KV_KERNEL_GENERIC = 1, /* vector-ALU kernel: f32 or bf16, any B, d; G <= 16 */
+  KV_KERNEL_MFMA = 2     /* bf16, q8_0 or q4_0, B = 16, d in {64, 128, 256},
+                            G <= 16, at most 4095 sequences per call; the only
+                            kernel for quantised pools (codes are dequantised
+                            to bf16 operands in registers) */
 } kv_kernel;
 
 typedef struct {

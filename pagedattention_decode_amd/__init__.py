@@ -11,6 +11,8 @@ from . import binding  # noqa: F401
 from .binding import (  # noqa: F401
     KV_BF16,
     KV_F32,
+    KV_Q4_0,
+    KV_Q8_0,
     KV_KERNEL_AUTO,
     KV_KERNEL_GENERIC,
     KV_KERNEL_MFMA,

@@ -3,6 +3,7 @@
 // block in the pool's MFMA operand order.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -69,6 +70,155 @@ __device__ __forceinline__ void zero_v_tail(kv_regs<D>& cur, int valid, int quad
       wv[dw] &= mask;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Quantised tiles (B = 16, groups of 32 values along d with a half scale).
+//
+// One K or V tile = a code region followed by a scale region of 16 x d/32
+// halves ([slot][group]).  Codes are arranged per MFMA lane: lane l = 16 q + r
+// owns D*bits/32 contiguous bytes at l * D*bits/32.
+//   K, lane (q, r): token r, dims 32 kk + 8 q + j (kk < D/32, j < 8);
+//     q8: byte 8 kk + j; q4: byte 4 kk + j/2, nibble j % 2 (low = even j).
+//   V, lane (q, r): dim 16 t + r of tokens 4 q + i (t < D/16, i < 4);
+//     q8: byte 4 t + i; q4: byte 4 (t/2) + i, nibble t % 2.
+// A q8 code is stored as a two's-complement byte, a q4 code as code + 8.
+// Every byte holds codes of one token only, so a writer owns whole bytes.
+// ---------------------------------------------------------------------------
+
+enum { kFmtBf16 = 0, kFmtQ8 = 1, kFmtQ4 = 2 };
+
+template <int FMT>
+constexpr int fmt_bits() {
+  return FMT == kFmtQ8 ? 8 : 4;
+}
+template <int D, int FMT>
+constexpr int q_code_bytes() {  // per tile
+  return 16 * D * fmt_bits<FMT>() / 8;
+}
+template <int D, int FMT>
+constexpr int q_tile_bytes() {
+  return q_code_bytes<D, FMT>() + 16 * (D / 32) * 2;
+}
+
+// Raw quantised block of one KV head in registers, per lane.
+template <int D, int FMT>
+struct kv_qregs {
+  uint32_t kc[D * fmt_bits<FMT>() / 128];  // K codes
+  uint32_t vc[D * fmt_bits<FMT>() / 128];  // V codes
+  uint32_t ks[D / 64];                     // K scales of the lane's token, one half per group
+  uint32_t vs[D / 16];                     // V scales of the lane's 4 tokens ([token][group])
+};
+
+template <int N>
+__device__ __forceinline__ void load_dwords(uint32_t (&w)[N], const unsigned char* p) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const uint2 v = reinterpret_cast<const uint2*>(p)[i];
+      w[2 * i] = v.x;
+      w[2 * i + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = reinterpret_cast<const uint32_t*>(p)[i];
+  }
+}
+
+// Loads the lane's share of the K and V tiles at kt, vt (byte addresses).
+template <int D, int FMT>
+__device__ __forceinline__ void load_qblock(kv_qregs<D, FMT>& r, const unsigned char* kt, const unsigned char* vt,
+                                            int lane) {
+  constexpr int lane_bytes = D * fmt_bits<FMT>() / 32;
+  constexpr int codes = q_code_bytes<D, FMT>();
+  load_dwords(r.kc, kt + lane * lane_bytes);
+  load_dwords(r.vc, vt + lane * lane_bytes);
+  load_dwords(r.ks, kt + codes + (lane & 15) * (D / 32) * 2);
+  load_dwords(r.vs, vt + codes + (lane >> 4) * 4 * (D / 32) * 2);
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) { return __half2float(__ushort_as_half(static_cast<unsigned short>(w))); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return __half2float(__ushort_as_half(static_cast<unsigned short>(w >> 16))); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+
+// Byte k of w as a float (one v_cvt_f32_ubyte).
+__device__ __forceinline__ float ubyte_f32(uint32_t w, int k) { return static_cast<float>((w >> (8 * k)) & 0xffu); }
+
+// Four codes held as bytes (code + bias) of word w, times scale s, as floats:
+// value = byte * s - bias * s.
+__device__ __forceinline__ void bytes_to_f32(uint32_t w, float s, float bias_s, float* out) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = __builtin_fmaf(ubyte_f32(w, k), s, bias_s);
+}
+
+// Dequantises a raw block into the bf16 operand tile of the decode kernel
+// (value = code * scale, exact in float32, then rounded to nearest-even bf16).
+template <int D, int FMT>
+__device__ __forceinline__ void dequant_block(const kv_qregs<D, FMT>& r, kv_regs<D>& out) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const float s = (kk & 1) ? half_hi(r.ks[kk >> 1]) : half_lo(r.ks[kk >> 1]);
+    float v[8];
+    if constexpr (FMT == kFmtQ8) {
+      // two's-complement bytes, flipped to code + 128
+      bytes_to_f32(r.kc[2 * kk] ^ 0x80808080u, s, -128.f * s, v);
+      bytes_to_f32(r.kc[2 * kk + 1] ^ 0x80808080u, s, -128.f * s, v + 4);
+    } else {
+      float lo[4], hi[4];
+      bytes_to_f32(r.kc[kk] & 0x0f0f0f0fu, s, -8.f * s, lo);         // j = 0, 2, 4, 6
+      bytes_to_f32((r.kc[kk] >> 4) & 0x0f0f0f0fu, s, -8.f * s, hi);  // j = 1, 3, 5, 7
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = lo[i];
+        v[2 * i + 1] = hi[i];
+      }
+    }
+    out.k[kk] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                           pack_bf16x2(v[6], v[7]));
+  }
+  // V: tile t gives the 16x16x16 operand of dims 16 t + r for the lane's 4 tokens
+  uint32_t half_words[D / 16][2];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const int g = t >> 1;  // group of dims 32 g .. 32 g + 31
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = r.vs[(i * (D / 32) + g) >> 1];
+      s[i] = ((i * (D / 32) + g) & 1) ? half_hi(w) : half_lo(w);
+    }
+    uint32_t bytes;
+    float bias;
+    if constexpr (FMT == kFmtQ8) {
+      bytes = r.vc[t] ^ 0x80808080u;
+      bias = -128.f;
+    } else {
+      bytes = (t & 1) ? (r.vc[t >> 1] >> 4) & 0x0f0f0f0fu : r.vc[t >> 1] & 0x0f0f0f0fu;
+      bias = -8.f;
+    }
+    const float v0 = __builtin_fmaf(ubyte_f32(bytes, 0), s[0], bias * s[0]);
+    const float v1 = __builtin_fmaf(ubyte_f32(bytes, 1), s[1], bias * s[1]);
+    const float v2 = __builtin_fmaf(ubyte_f32(bytes, 2), s[2], bias * s[2]);
+    const float v3 = __builtin_fmaf(ubyte_f32(bytes, 3), s[3], bias * s[3]);
+    half_words[t][0] = pack_bf16x2(v0, v1);
+    half_words[t][1] = pack_bf16x2(v2, v3);
+  }
+#pragma unroll
+  for (int pp = 0; pp < D / 32; ++pp)
+    out.v[pp] = make_uint4(half_words[2 * pp][0], half_words[2 * pp][1], half_words[2 * pp + 1][0],
+                           half_words[2 * pp + 1][1]);
 }
 
 }  // namespace pagedkv

@@ -21,9 +21,11 @@
 // S^T = K Q^T) and v_mfma_f32_16x16x16_bf16 (V, as the A operand of
 // O^T = V^T P^T), so every K/V byte is fetched by one 16-byte load per lane and
 // every wave-wide load instruction reads 1 KiB of contiguous memory.
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 #include <string>
 
@@ -101,6 +103,99 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(
     const T* ve = reinterpret_cast<const T*>(&vv);
 #pragma unroll
     for (int x = 0; x < X; ++x) v_layer[tile + v_offset(r, c * X + x, block_size, Q)] = ve[x];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// reshape_and_cache into a quantised pool ([INF] §8.4.2: 32 values share one
+// 2-byte scale): one thread per (token, KV head, group of 32 dims).  It forms
+// the group's half scale max|x| / M and codes rint(x / s) for K and for V and
+// writes them in the tile layout of device_common.h; every byte it writes
+// holds codes of its own token only.
+// ---------------------------------------------------------------------------
+
+template <int D, int FMT>
+__device__ __forceinline__ void quantize_group(const uint16_t* __restrict__ x, float* c, uint16_t& scale_bits) {
+  constexpr float qmax = FMT == kFmtQ8 ? 127.f : 7.f;
+  float f[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = reinterpret_cast<const uint4*>(x)[i];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[8 * i + 2 * k] = __uint_as_float(ws[k] << 16);
+      f[8 * i + 2 * k + 1] = __uint_as_float(ws[k] & 0xffff0000u);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  const __half hs = __float2half_rn(fminf(__fdiv_rn(amax, qmax), 65504.f));
+  scale_bits = __half_as_ushort(hs);
+  const float s = __half2float(hs);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) c[i] = s > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(f[i], s)), -qmax), qmax) : 0.f;
+}
+
+template <int D, int FMT>
+__global__ void __launch_bounds__(256) quantize_cache_kernel(const uint16_t* __restrict__ k_new,
+                                                             const uint16_t* __restrict__ v_new,
+                                                             const int64_t* __restrict__ slots,
+                                                             unsigned char* __restrict__ k_layer,
+                                                             unsigned char* __restrict__ v_layer, int64_t n_items,
+                                                             int n_kv_heads, int64_t n_slots) {
+  constexpr int G32 = D / 32;
+  constexpr int TB = q_tile_bytes<D, FMT>();
+  constexpr int CB = q_code_bytes<D, FMT>();
+  constexpr int LB = D * fmt_bits<FMT>() / 32;  // code bytes per lane
+  for (int64_t item = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; item < n_items;
+       item += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t tok = item / (n_kv_heads * G32);
+    const int rem = static_cast<int>(item % (n_kv_heads * G32));
+    const int h = rem / G32, grp = rem % G32;
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= n_slots) continue;
+    const int r = static_cast<int>(slot & 15);
+    const int64_t tile = ((slot >> 4) * n_kv_heads + h) * TB;
+    const int64_t src = (tok * n_kv_heads + h) * D + grp * 32;
+    float c[32];
+    uint16_t sb;
+    // K: lane (q, r) holds dims 32 grp + 8 q + j
+    quantize_group<D, FMT>(k_new + src, c, sb);
+    unsigned char* kt = k_layer + tile;
+    *reinterpret_cast<uint16_t*>(kt + CB + (r * G32 + grp) * 2) = sb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      unsigned char* dst = kt + (q * 16 + r) * LB;
+      if constexpr (FMT == kFmtQ8) {
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j >> 2] |= (static_cast<uint32_t>(static_cast<int>(c[q * 8 + j])) & 0xffu) << (8 * (j & 3));
+        *reinterpret_cast<uint2*>(dst + grp * 8) = make_uint2(w[0], w[1]);
+      } else {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w |= static_cast<uint32_t>(static_cast<int>(c[q * 8 + j]) + 8) << (4 * j);
+        *reinterpret_cast<uint32_t*>(dst + grp * 4) = w;
+      }
+    }
+    // V: lane (r / 4, rr) holds dim 16 t + rr of this token (slot r % 4 of its four)
+    quantize_group<D, FMT>(v_new + src, c, sb);
+    unsigned char* vt = v_layer + tile;
+    *reinterpret_cast<uint16_t*>(vt + CB + (r * G32 + grp) * 2) = sb;
+    const int qv = r >> 2, i = r & 3;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      unsigned char* dst = vt + (qv * 16 + rr) * LB;
+      if constexpr (FMT == kFmtQ8) {
+        dst[(2 * grp) * 4 + i] = static_cast<unsigned char>(static_cast<int>(c[rr]));
+        dst[(2 * grp + 1) * 4 + i] = static_cast<unsigned char>(static_cast<int>(c[16 + rr]));
+      } else {
+        dst[grp * 4 + i] = static_cast<unsigned char>((static_cast<int>(c[rr]) + 8) |
+                                                      ((static_cast<int>(c[16 + rr]) + 8) << 4));
+      }
+    }
   }
 }
 
@@ -515,7 +610,7 @@ struct sk_cursor {
   int seq, kvh, j, nb, n;
 };
 
-template <int D, int STAGES, int WAVES_PER_SIMD>
+template <int D, int STAGES, int WAVES_PER_SIMD, int FMT>
 __global__ void __launch_bounds__(kSkWaves * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD)))
 attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ tables) {
   extern __shared__ __align__(16) int sk_smem[];
@@ -582,6 +677,8 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     c.n = min(ctx_lens[c.seq], cap);
   };
 
+  // ring entries: bf16 operand tiles, or raw quantised tiles dequantised on use
+  using ring_t = typename std::conditional<FMT == kFmtBf16, kv_regs<D>, kv_qregs<D, FMT>>::type;
   const uint4* kpool = static_cast<const uint4*>(a.k_layer);
   const uint4* vpool = static_cast<const uint4*>(a.v_layer);
   constexpr int kTileVec = 16 * D * 2 / 16;  // 16-byte vectors per tile
@@ -591,16 +688,22 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
   sk_cursor ld = first;
   int ld_k = 0;
   int phys_ring[STAGES];
-  auto issue = [&](kv_regs<D>& buf, int u) {
+  auto issue = [&](ring_t& buf, int u) {
     const int phys = tables[static_cast<int64_t>(ld.seq) * a.max_blocks + ld.j];
     phys_ring[u] = phys;
     const int p = (phys < 0 || phys >= a.num_blocks) ? 0 : phys;  // never dereferenced out of range
-    const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * kTileVec;
-    load_block<D>(buf, kpool + t, vpool + t, lane);
+    if constexpr (FMT == kFmtBf16) {
+      const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * kTileVec;
+      load_block<D>(buf, kpool + t, vpool + t, lane);
+    } else {
+      const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * q_tile_bytes<D, FMT>();
+      load_qblock<D, FMT>(buf, static_cast<const unsigned char*>(a.k_layer) + t,
+                          static_cast<const unsigned char*>(a.v_layer) + t, lane);
+    }
     if (++ld_k < n_blk) advance(ld);
   };
 
-  kv_regs<D> buf[STAGES];
+  ring_t buf[STAGES];
 #pragma unroll
   for (int u = 0; u < STAGES; ++u) issue(buf[u], u);
 
@@ -703,7 +806,13 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
         const bool bad = phys < 0 || phys >= a.num_blocks;
         poisoned |= bad;
         const int valid = bad ? 0 : min(16, cs.n - cs.j * 16);
-        attend_block<D>(buf[u], qop, valid, quad, a.scale_log2, o, m_run, l_lane);
+        if constexpr (FMT == kFmtBf16) {
+          attend_block<D>(buf[u], qop, valid, quad, a.scale_log2, o, m_run, l_lane);
+        } else {
+          kv_regs<D> tile;
+          dequant_block<D, FMT>(buf[u], tile);
+          attend_block<D>(tile, qop, valid, quad, a.scale_log2, o, m_run, l_lane);
+        }
         if (cs.j == cs.nb - 1 || k == n_blk - 1) {  // end of this unit's run
           finish();
           if (k + 1 < n_blk) {
@@ -910,8 +1019,8 @@ kv_status hip_check(hipError_t e, const char* what) {
 }
 
 bool mfma_supported(const kv_pool_config& c, int G) {
-  return c.dtype == KV_BF16 && c.block_size == 16 && (c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256) &&
-         G >= 1 && G <= kMaxGroup;
+  return (c.dtype == KV_BF16 || is_quantized(c.dtype)) && c.block_size == 16 &&
+         (c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256) && G >= 1 && G <= kMaxGroup;
 }
 
 int device_cus() {
@@ -955,7 +1064,19 @@ size_t sk_lds_bytes(int n_seqs, int G, int D) {
 // wave of each pair stream ~1.6x faster than the other; with equal shares the
 // slower half then finishes alone with half the loads in flight.  A single
 // wave per SIMD with a deeper ring keeps the same bytes in flight per CU.
-constexpr int sk_waves_per_simd(int) { return 1; }
+constexpr int fmt_of(int32_t dtype) { return dtype == KV_Q8_0 ? kFmtQ8 : (dtype == KV_Q4_0 ? kFmtQ4 : kFmtBf16); }
+
+// Waves per SIMD and register-ring depth (blocks in flight per wave).  bf16:
+// one wave per SIMD with a deep ring (the waves of one SIMD are issued oldest
+// first, so two waves with equal shares finish far apart).  Quantised: the
+// dequantisation is vector-ALU work that one wave cannot overlap with its own
+// loads; two waves per SIMD with a shorter ring measured 1.25-1.4x faster.
+constexpr int sk_waves_per_simd(int D, int fmt) { return fmt != kFmtBf16 && D < 256 ? 2 : 1; }
+
+template <int D, int FMT>
+constexpr int sk_stages() {
+  return D >= 256 ? 2 : (FMT == kFmtBf16 ? 6 : 4);
+}
 
 struct resolved {
   int kernel;
@@ -980,7 +1101,11 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
   const bool mfma_ok = mfma_supported(c, G) && n_seqs <= kSkMaxSeqs;
   if (o.kernel == KV_KERNEL_MFMA && !mfma_ok)
     return fail(KV_ERR_UNSUPPORTED,
-                "the matrix-core kernel needs bf16, B = 16, d in {64, 128, 256} and at most 4095 sequences");
+                "the matrix-core kernel needs bf16 or q8_0/q4_0, B = 16, d in {64, 128, 256} and at most 4095 "
+                "sequences");
+  if (is_quantized(c.dtype) && (o.kernel == KV_KERNEL_GENERIC || !mfma_ok))
+    return fail(KV_ERR_UNSUPPORTED, "a quantised pool is read by the matrix-core kernel only (at most 4095 "
+                                    "sequences, G <= 16)");
   r.kernel = o.kernel == KV_KERNEL_AUTO ? (mfma_ok ? KV_KERNEL_MFMA : KV_KERNEL_GENERIC) : o.kernel;
   if (o.partition_tokens < 0 || (o.partition_tokens > 0 && o.partition_tokens % c.block_size != 0))
     return fail(KV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of the block size");
@@ -993,7 +1118,7 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
     r.max_parts = static_cast<int>((max_ctx + r.partition - 1) / r.partition);
     const int64_t parts_ub = static_cast<int64_t>(n_seqs) * c.num_kv_heads * r.max_parts;
     r.groups = std::max<int64_t>(
-        1, std::min<int64_t>((parts_ub + kSkWaves - 1) / kSkWaves, sk_waves_per_simd(c.head_dim) * device_cus()));
+        1, std::min<int64_t>((parts_ub + kSkWaves - 1) / kSkWaves, sk_waves_per_simd(c.head_dim, fmt_of(c.dtype)) * device_cus()));
   } else {
     r.partition = o.partition_tokens ? o.partition_tokens : choose_generic_partition(c, n_seqs, max_blocks);
     r.max_parts = static_cast<int>((max_ctx + r.partition - 1) / r.partition);
@@ -1016,12 +1141,12 @@ uint64_t workspace_for(const kv_pool_config& c, int n_seqs, int num_q_heads, con
   return up256(rows * 4) * 2 + up256(rows * c.head_dim * 4);
 }
 
-template <int D>
+template <int D, int FMT>
 hipError_t launch_mfma(const sk_args& a, const int32_t* ctx_lens, const int32_t* tables, int64_t groups, int G,
                        hipStream_t st) {
-  constexpr int kStages = D >= 256 ? 2 : 6;
-  constexpr int kWps = sk_waves_per_simd(D);
-  hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, kWps>), dim3(static_cast<unsigned>(groups)), dim3(kSkWaves * 64),
+  constexpr int kStages = sk_stages<D, FMT>();
+  constexpr int kWps = sk_waves_per_simd(D, FMT);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, kWps, FMT>), dim3(static_cast<unsigned>(groups)), dim3(kSkWaves * 64),
                      sk_lds_bytes(a.n_seqs, G, D), st, a, ctx_lens, tables);
   return hipGetLastError();
 }
@@ -1050,6 +1175,33 @@ kv_status reshape_and_cache(kv_pool* pool, int32_t layer, const void* k_new, con
     return fail(KV_ERR_INVALID, "NULL device pointer");
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
     return fail(KV_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
+  if (is_quantized(c.dtype)) {
+    const int64_t layer_bytes = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
+    unsigned char* kl = static_cast<unsigned char*>(pool->k_cache) + layer_bytes;
+    unsigned char* vl = static_cast<unsigned char*>(pool->v_cache) + layer_bytes;
+    const int64_t items = static_cast<int64_t>(n_tokens) * c.num_kv_heads * (c.head_dim / 32);
+    const int64_t want = (items + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
+    const int64_t n_slots = static_cast<int64_t>(c.num_blocks) * c.block_size;
+    const uint16_t* kn = static_cast<const uint16_t*>(k_new);
+    const uint16_t* vn = static_cast<const uint16_t*>(v_new);
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    auto go = [&](auto d, auto f) {
+      constexpr int D = decltype(d)::value, F = decltype(f)::value;
+      hipLaunchKernelGGL((quantize_cache_kernel<D, F>), dim3(grid), dim3(256), 0, st, kn, vn, d_slot_mapping, kl, vl,
+                         items, c.num_kv_heads, n_slots);
+    };
+    auto go_d = [&](auto f) {
+      switch (c.head_dim) {
+        case 64: go(std::integral_constant<int, 64>{}, f); break;
+        case 128: go(std::integral_constant<int, 128>{}, f); break;
+        default: go(std::integral_constant<int, 256>{}, f); break;
+      }
+    };
+    if (c.dtype == KV_Q8_0) go_d(std::integral_constant<int, kFmtQ8>{});
+    else go_d(std::integral_constant<int, kFmtQ4>{});
+    return hip_check(hipGetLastError(), "reshape_and_cache launch");
+  }
   const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_elems(c);
   const int64_t n_slots = static_cast<int64_t>(c.num_blocks) * c.block_size;
   const int X = 16 / elem_bytes(c.dtype);
@@ -1081,7 +1233,7 @@ kv_status copy_blocks(kv_pool* pool, const int64_t* d_pairs, int32_t n_pairs, vo
   const kv_pool_config& c = pool->cfg;
   const int64_t grid = static_cast<int64_t>(n_pairs) * c.num_layers * 2;
   if (grid > 0x7fffffff) return fail(KV_ERR_INVALID, "too many pairs");
-  const int64_t block_bytes = static_cast<int64_t>(c.num_kv_heads) * tile_elems(c) * elem_bytes(c.dtype);
+  const int64_t block_bytes = static_cast<int64_t>(c.num_kv_heads) * tile_bytes(c);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
                      static_cast<hipStream_t>(hip_stream), static_cast<uint4*>(pool->k_cache),
                      static_cast<uint4*>(pool->v_cache), d_pairs, c.num_layers, c.num_blocks, block_bytes / 16);
@@ -1115,8 +1267,7 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     return fail(KV_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
   if (need > 0 && (reinterpret_cast<uintptr_t>(d_workspace) & 255))
     return fail(KV_ERR_INVALID, "workspace must be 256-byte aligned");
-  const int64_t layer_off =
-      static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_elems(c) * elem_bytes(c.dtype);
+  const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
   const void* k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
   const void* v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -1144,11 +1295,17 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     a.n_waves = static_cast<int>(r.groups * kSkWaves);
     a.q_units = sk_q_units(G, c.head_dim);
     a.scale_log2 = r.scale * kLog2e;
-    switch (c.head_dim) {
-      case 64: e = launch_mfma<64>(a, d_context_lens, d_block_tables, r.groups, G, st); break;
-      case 128: e = launch_mfma<128>(a, d_context_lens, d_block_tables, r.groups, G, st); break;
-      default: e = launch_mfma<256>(a, d_context_lens, d_block_tables, r.groups, G, st); break;
-    }
+    auto launch = [&](auto fmt) {
+      constexpr int F = decltype(fmt)::value;
+      switch (c.head_dim) {
+        case 64: return launch_mfma<64, F>(a, d_context_lens, d_block_tables, r.groups, G, st);
+        case 128: return launch_mfma<128, F>(a, d_context_lens, d_block_tables, r.groups, G, st);
+        default: return launch_mfma<256, F>(a, d_context_lens, d_block_tables, r.groups, G, st);
+      }
+    };
+    if (c.dtype == KV_Q8_0) e = launch(std::integral_constant<int, kFmtQ8>{});
+    else if (c.dtype == KV_Q4_0) e = launch(std::integral_constant<int, kFmtQ4>{});
+    else e = launch(std::integral_constant<int, kFmtBf16>{});
     if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
     const int64_t mgrid = static_cast<int64_t>(n_seqs) * num_q_heads;
     hipLaunchKernelGGL(merge_sk_kernel, dim3(static_cast<unsigned>(mgrid)), dim3(kMergeThreads), 0, st, a,

@@ -44,7 +44,11 @@ static kv_status validate_config(const kv_pool_config* c) {
     return fail(KV_ERR_INVALID, "num_layers, num_blocks, block_size and num_kv_heads must be positive");
   if (c->head_dim <= 0 || c->head_dim % 32 != 0 || c->head_dim > 256)
     return fail(KV_ERR_INVALID, "head_dim must be a positive multiple of 32, at most 256");
-  if (c->dtype != KV_F32 && c->dtype != KV_BF16) return fail(KV_ERR_INVALID, "dtype must be KV_F32 or KV_BF16");
+  if (c->dtype != KV_F32 && c->dtype != KV_BF16 && c->dtype != KV_Q8_0 && c->dtype != KV_Q4_0)
+    return fail(KV_ERR_INVALID, "dtype must be KV_F32, KV_BF16, KV_Q8_0 or KV_Q4_0");
+  if (pagedkv::is_quantized(c->dtype) &&
+      (c->block_size != 16 || (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)))
+    return fail(KV_ERR_UNSUPPORTED, "a quantised pool needs B = 16 and head_dim 64, 128 or 256");
   if (static_cast<int64_t>(c->num_blocks) * c->block_size > INT64_C(1) << 40)
     return fail(KV_ERR_INVALID, "pool too large");
   return KV_OK;
@@ -81,7 +85,7 @@ const char* kv_last_error(void) { return g_last_error.c_str(); }
 kv_status kv_pool_required_bytes(const kv_pool_config* cfg, uint64_t* k_bytes, uint64_t* v_bytes) {
   if (kv_status st = validate_config(cfg)) return st;
   if (!k_bytes || !v_bytes) return fail(KV_ERR_INVALID, "output pointer is NULL");
-  uint64_t b = static_cast<uint64_t>(pool_elems(*cfg)) * elem_bytes(cfg->dtype);
+  uint64_t b = static_cast<uint64_t>(pool_bytes(*cfg));
   *k_bytes = b;
   *v_bytes = b;
   return ok();

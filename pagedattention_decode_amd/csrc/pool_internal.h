@@ -37,17 +37,28 @@ struct kv_pool {
 
 namespace pagedkv {
 
-// Element size of the pool dtype.
+// Element size of an unquantised pool dtype (also of q / out / new rows of a
+// quantised pool, which are bf16).
 inline int elem_bytes(int32_t dtype) { return dtype == KV_F32 ? 4 : 2; }
 
-// Elements of one (layer, block, kv head) tile.
+inline bool is_quantized(int32_t dtype) { return dtype == KV_Q8_0 || dtype == KV_Q4_0; }
+
+// Elements (values) of one (layer, block, kv head) tile.
 inline int64_t tile_elems(const kv_pool_config& c) {
   return static_cast<int64_t>(c.block_size) * c.head_dim;
 }
 
-// Elements of the whole K (or V) buffer.
-inline int64_t pool_elems(const kv_pool_config& c) {
-  return static_cast<int64_t>(c.num_layers) * c.num_blocks * c.num_kv_heads * tile_elems(c);
+// Bytes of one (layer, block, kv head) tile of K (or of V): values, or codes
+// plus one 2-byte scale per 32 values for a quantised pool.
+inline int64_t tile_bytes(const kv_pool_config& c) {
+  if (!is_quantized(c.dtype)) return tile_elems(c) * elem_bytes(c.dtype);
+  const int bits = c.dtype == KV_Q8_0 ? 8 : 4;
+  return tile_elems(c) * bits / 8 + tile_elems(c) / 32 * 2;
+}
+
+// Bytes of the whole K (or V) buffer.
+inline int64_t pool_bytes(const kv_pool_config& c) {
+  return static_cast<int64_t>(c.num_layers) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
 }
 
 // Sets the thread-local error message and returns the status.

@@ -481,8 +481,8 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   if (opts) o = *opts;
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_MFMA)
     return fail(KV_ERR_UNSUPPORTED, "multi-query attention has only the matrix-core kernel");
-  if (!mfma_supported(c, G))
-    return fail(KV_ERR_UNSUPPORTED, "multi-query attention needs bf16, B = 16, d in {64, 128, 256} and G <= 16");
+  if (!mfma_supported(c, G) || c.dtype != KV_BF16)
+    return fail(KV_ERR_UNSUPPORTED, "multi-query attention needs a bf16 pool, B = 16, d in {64, 128, 256} and G <= 16");
   if (o.partition_tokens < 0 || o.partition_tokens % 16 != 0)
     return fail(KV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of the block size");
   if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
@@ -583,7 +583,7 @@ kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, v
   if (need > 0 && (reinterpret_cast<uintptr_t>(d_workspace) & 255))
     return fail(KV_ERR_INVALID, "workspace must be 256-byte aligned");
   const int64_t layer_off =
-      static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_elems(c) * elem_bytes(c.dtype);
+      static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
   pf_args a{};
   a.q = q;
   a.out = out;

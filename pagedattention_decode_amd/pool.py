@@ -13,7 +13,7 @@ class PagedKVPool:
     def __init__(self, num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype="bf16",
                  free_order=None, device="cuda", allocate=True):
         self.dtype = dtype
-        code = B.KV_BF16 if dtype == "bf16" else B.KV_F32
+        code = B.DTYPE_CODES[dtype]
         self.cfg = B.make_config(num_layers, num_blocks, block_size, num_kv_heads, head_dim, code)
         self.num_layers, self.num_blocks, self.block_size = num_layers, num_blocks, block_size
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
@@ -103,9 +103,11 @@ class PagedKVPool:
 
     # -- raw views for tests -------------------------------------------------
     def raw(self, which):
-        """The K or V buffer as a flat tensor of stored bit patterns."""
+        """The K or V buffer as a flat tensor of stored bit patterns (bytes for a quantised pool)."""
         import torch
         buf = self.k_cache if which == "k" else self.v_cache
+        if self.dtype in ("q8_0", "q4_0"):
+            return buf
         return buf.view(torch.int16 if self.dtype == "bf16" else torch.int32)
 
 

@@ -50,12 +50,14 @@ class GpuRun:
         self.opts = opts
         self.ref = ref
         order = draws.free_order(wl.seed, wl.num_blocks) if free_order is None else free_order
+        self.quantized = bool(getattr(wl, "kv_format", ""))
         self.pool = PagedKVPool(wl.num_layers, wl.num_blocks, wl.block_size, wl.num_kv_heads,
-                                wl.head_dim, wl.dtype, free_order=order)
+                                wl.head_dim, wl.kv_format or wl.dtype, free_order=order)
         if fill is not None:
-            # a known background: every unwritten element holds this bit pattern
-            self.pool.raw("k").fill_(fill)
-            self.pool.raw("v").fill_(fill)
+            # a known background: every unwritten element (byte, for a quantised pool) holds this pattern
+            pattern = fill & 0xFF if self.quantized else fill
+            self.pool.raw("k").fill_(pattern)
+            self.pool.raw("v").fill_(pattern)
         final = wl.final_lengths()
         longest = max(final.values()) if final else 1
         self.max_blocks = max_blocks or max(1, -(-longest // wl.block_size))

@@ -250,3 +250,20 @@ def test_empty_batches_and_zero_counts():
     assert slots.size == 0
     assert pool.info(3) == (0, 0)
     pool.check()
+
+
+def test_quantised_pool_sizes_and_shape_limits():
+    """[INF] §8.4.2 budget: per 32 values, 32 (q8_0) or 16 (q4_0) code bytes plus a
+    2-byte scale, so a tile of 16 slots x d dims takes 16 d bits/8 + d bytes."""
+    from oracle import quant as qt
+
+    for fmt, code in (("q8_0", B.KV_Q8_0), ("q4_0", B.KV_Q4_0)):
+        for d in (64, 128, 256):
+            cfg = B.make_config(3, 10, 16, 4, d, code)
+            kb, vb = B.kv_pool_required_bytes(cfg)
+            values = 3 * 10 * 4 * 16 * d
+            assert kb == vb == values // 32 * qt.group_bytes(fmt)
+        for bad in (B.make_config(1, 4, 8, 2, 128, code), B.make_config(1, 4, 16, 2, 96, code)):
+            with pytest.raises(B.KVError) as e:
+                B.kv_pool_required_bytes(bad)
+            assert e.value.status == B.KV_ERR_UNSUPPORTED
