@@ -188,13 +188,64 @@ kv_status kv_pool_free_list(const kv_pool* pool, int32_t cap, int32_t* out, int3
 kv_status kv_pool_refcounts(const kv_pool* pool, int32_t* out);
 
 /* Conservation ([BT] §13): N_free + N_allocated + N_pending = N_total, the set
- * of blocks with ref > 0 is exactly the set named by tables, each count equals
- * the number of table entries naming the block, and every table has
- * ceil(len / B) entries.  KV_ERR_STATE names the first violation. */
+ * of blocks with ref > 0 is exactly the set named by tables and the prefix
+ * cache, each count equals the number of table entries naming the block plus
+ * the prefix cache's reference, and every table has ceil(len / B) entries.
+ * KV_ERR_STATE names the first violation. */
 kv_status kv_pool_check(const kv_pool* pool);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* kv_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Prefix cache ([KVM] cross-turn prefix caching: Table 2, Definition 0.2,
+ * Figure 6).  A radix tree binds runs of prompt tokens to the physical blocks
+ * holding their K/V, so a later request with the same prefix reuses them
+ * instead of recomputing them.  Only completely filled blocks are shared: a
+ * match of S_match tokens gives S_usable = floor(S_match / B) * B cached
+ * tokens and the tail is recomputed (block-aligned truncation).  Every edge
+ * holds whole blocks; a child is keyed by the tokens of its first block.  The
+ * tree holds one reference on each block it caches; a request attached to or
+ * inserted into the tree holds a ref_count on each node of its path until it
+ * is released.  Nodes with ref_count 0 are dormant; eviction takes dormant
+ * leaves oldest last_access first, and a parent left childless and dormant
+ * becomes a candidate in turn.  last_access is a counter advanced by every
+ * lookup, attach and insert (ties go to the node created first).  Tokens are
+ * int32 host arrays; the tree lives on the host.
+ * ---------------------------------------------------------------------- */
+
+/* Longest cached prefix of tokens[0, n): S_match tokens (whole blocks along
+ * the tree plus the longest common run with the next block), of which
+ * S_usable (whole blocks) can be reused.  Marks the walked nodes accessed. */
+kv_status kv_prefix_match(kv_pool* pool, const int32_t* tokens, int32_t n, int32_t* s_match, int32_t* s_usable);
+
+/* Register a new sequence whose table starts with the cached blocks of the
+ * longest block-aligned prefix of tokens[0, n) (each gains a reference);
+ * *cached_tokens = its length (a multiple of B).  The caller then appends and
+ * computes the rest.  KV_ERR_INVALID if seq_id exists. */
+kv_status kv_seq_attach_prefix(kv_pool* pool, int64_t seq_id, const int32_t* tokens, int32_t n,
+                               int32_t* cached_tokens);
+
+/* Cache the first floor(n / B) blocks of sequence seq_id, whose first n
+ * tokens are tokens[0, n) and already hold their K/V.  Nodes the tree lacks
+ * adopt the sequence's blocks (the tree takes a reference); a run diverging
+ * inside an edge splits it at the block boundary.  n <= the sequence length. */
+kv_status kv_prefix_insert(kv_pool* pool, int64_t seq_id, const int32_t* tokens, int32_t n, int32_t* cached_tokens);
+
+/* Evict dormant leaves until the free list (plus blocks this call makes
+ * pending) holds target_free blocks or no dormant leaf is left.  Blocks
+ * whose last reference was the tree's go to the free list once the work
+ * enqueued on hip_stream so far has completed (as kv_seq_release), or, for
+ * the fenced form, once completed_fence >= fence (0 = at once).  The evicted
+ * nodes' blocks, in eviction order, go to blocks_out (at most cap entries;
+ * blocks_out may be NULL) and their number to *n_out. */
+kv_status kv_prefix_evict(kv_pool* pool, int32_t target_free, void* hip_stream, int32_t* blocks_out, int32_t cap,
+                          int32_t* n_out);
+kv_status kv_prefix_evict_fenced(kv_pool* pool, int32_t target_free, uint64_t fence, int32_t* blocks_out,
+                                 int32_t cap, int32_t* n_out);
+
+/* Nodes, blocks cached by the tree, and pinned nodes (ref_count > 0). */
+kv_status kv_prefix_stats(const kv_pool* pool, int32_t* n_nodes, int32_t* n_cached_blocks, int32_t* n_pinned);
 
 /* ------------------------------------------------------------------------
  * Device operations

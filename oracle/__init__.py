@@ -41,9 +41,15 @@ Modules:
                                per 32 values (q8_0, q4_0), their byte budget
                                and read/convert trade-off ([INF] §8.4.2,
                                Figure 8-23), and a quantised logical pool.
+* :mod:`oracle.prefix_cache`  radix-tree prefix cache over the block manager:
+                               longest match with block-aligned truncation,
+                               attach / insert / release, leaf-first LRU
+                               eviction ([KVM] cross-turn prefix caching,
+                               Table 2, Definition 0.2, estimate 0.4).
 * :mod:`oracle.runner`        replays a :mod:`synth` workload through the above.
 
 Every function is pinned by ``tests/test_oracle_pins.py``,
-``tests/test_prefill_pins.py`` and ``tests/test_quant_pins.py`` against values the
+``tests/test_prefill_pins.py``, ``tests/test_quant_pins.py`` and
+``tests/test_prefix_cache.py`` against values the
 pages print, closed forms, invariants and brute force.  Parity unpinned: none.
 """

@@ -51,6 +51,7 @@ class BlockManager:
             raise ValueError("free_order must be a permutation of the block ids")
         self.free = deque(order)
         self.ref = [0] * num_blocks
+        self.held = [0] * num_blocks  # references held outside the tables (a prefix cache)
         self.tables: dict = {}
         self.lengths: dict = {}
 
@@ -82,6 +83,38 @@ class BlockManager:
                 self.free.append(p)
                 freed.append(p)
         del self.lengths[seq]
+        return freed
+
+    def add_with_blocks(self, seq, blocks) -> None:
+        """Register a sequence whose table starts with ``blocks`` (full blocks it shares):
+        each gains a reference; the length is len(blocks) * B."""
+        if seq in self.tables:
+            raise ValueError(f"sequence {seq} already exists")
+        self.tables[seq] = list(blocks)
+        for p in blocks:
+            self.ref[p] += 1
+        self.lengths[seq] = len(blocks) * self.block_size
+
+    def retain(self, blocks) -> None:
+        """A holder outside the tables takes one reference on each block."""
+        for p in blocks:
+            if self.ref[p] <= 0:
+                raise ValueError(f"block {p} is not allocated")
+            self.ref[p] += 1
+            self.held[p] += 1
+
+    def drop(self, blocks) -> list:
+        """The outside holder gives its references back; blocks reaching zero return
+        to the back of the free list in the given order.  Returns those blocks."""
+        freed = []
+        for p in blocks:
+            if self.held[p] <= 0:
+                raise ValueError(f"block {p} is not held")
+            self.held[p] -= 1
+            self.ref[p] -= 1
+            if self.ref[p] == 0:
+                self.free.append(p)
+                freed.append(p)
         return freed
 
     # -- growth ------------------------------------------------------------
@@ -159,8 +192,9 @@ class BlockManager:
                 raise AssertionError(f"table of {seq} has {len(t)} entries for length {self.lengths[seq]}")
             for p in t:
                 counted[p] += 1
+        counted = [c + h for c, h in zip(counted, self.held)]
         if counted != self.ref:
-            raise AssertionError("reference counts disagree with the tables")
+            raise AssertionError("reference counts disagree with the tables and outside holders")
         free = set(self.free)
         if len(free) != len(self.free):
             raise AssertionError("duplicate block in the free list")

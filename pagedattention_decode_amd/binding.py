@@ -76,6 +76,12 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (_U64, [_P, _I32, _I32, _I32, C.POINTER(kv_attention_options)]),
     "paged_attention_decode": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _I32,
                                       C.POINTER(kv_attention_options), _P, _U64, _P]),
+    "kv_prefix_match": (_I32, [_P, _P, _I32, C.POINTER(_I32), C.POINTER(_I32)]),
+    "kv_seq_attach_prefix": (_I32, [_P, _I64, _P, _I32, C.POINTER(_I32)]),
+    "kv_prefix_insert": (_I32, [_P, _I64, _P, _I32, C.POINTER(_I32)]),
+    "kv_prefix_evict": (_I32, [_P, _I32, _P, _P, _I32, C.POINTER(_I32)]),
+    "kv_prefix_evict_fenced": (_I32, [_P, _I32, _U64, _P, _I32, C.POINTER(_I32)]),
+    "kv_prefix_stats": (_I32, [_P, C.POINTER(_I32), C.POINTER(_I32), C.POINTER(_I32)]),
     "paged_prefill_workspace_bytes": (_U64, [_P, _I32, _I32, _I32, _I32, _I32, C.POINTER(kv_attention_options)]),
     "paged_attention_prefill": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                        C.POINTER(kv_attention_options), _P, _U64, _P]),
@@ -295,3 +301,46 @@ def paged_attention_prefill(pool, layer, q, out, q_indptr, block_tables, context
                                          _dev(context_lens), n_seqs, total_q, int(max_q_len), max_blocks,
                                          int(num_q_heads), C.byref(opts) if opts is not None else None,
                                          _dev(workspace), ws_bytes, _stream(stream)))
+
+
+# -- prefix cache ------------------------------------------------------------
+
+def kv_prefix_match(pool, tokens):
+    """(S_match, S_usable) of the longest cached prefix of ``tokens``."""
+    t, tp = _host(tokens, np.int32)
+    m, u = _I32(), _I32()
+    _check(lib().kv_prefix_match(pool, tp, len(t), C.byref(m), C.byref(u)))
+    return m.value, u.value
+
+
+def kv_seq_attach_prefix(pool, seq_id, tokens):
+    t, tp = _host(tokens, np.int32)
+    c = _I32()
+    _check(lib().kv_seq_attach_prefix(pool, int(seq_id), tp, len(t), C.byref(c)))
+    return c.value
+
+
+def kv_prefix_insert(pool, seq_id, tokens):
+    t, tp = _host(tokens, np.int32)
+    c = _I32()
+    _check(lib().kv_prefix_insert(pool, int(seq_id), tp, len(t), C.byref(c)))
+    return c.value
+
+
+def kv_prefix_evict(pool, target_free, stream=None, fence=None, cap=1 << 16):
+    """Evict; with ``fence`` given, the fenced form (0 = blocks free at once).
+    Returns the evicted nodes' blocks in eviction order (at most ``cap``)."""
+    n = _I32()
+    out = np.empty(cap, np.int32)
+    op = out.ctypes.data_as(C.c_void_p)
+    if fence is not None:
+        _check(lib().kv_prefix_evict_fenced(pool, int(target_free), int(fence), op, cap, C.byref(n)))
+    else:
+        _check(lib().kv_prefix_evict(pool, int(target_free), _stream(stream), op, cap, C.byref(n)))
+    return out[:min(n.value, cap)].tolist()
+
+
+def kv_prefix_stats(pool):
+    a, b, c = _I32(), _I32(), _I32()
+    _check(lib().kv_prefix_stats(pool, C.byref(a), C.byref(b), C.byref(c)))
+    return {"n_nodes": a.value, "n_cached_blocks": b.value, "n_pinned": c.value}

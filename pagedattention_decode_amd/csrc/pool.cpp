@@ -122,6 +122,7 @@ void kv_pool_destroy(kv_pool* p) {
   if (!p) return;
   for (auto& g : p->pending)
     if (g.event) (void)hipEventDestroy(static_cast<hipEvent_t>(g.event));
+  prefix_destroy(p);
   delete p;
 }
 
@@ -274,6 +275,7 @@ static kv_status release_common(kv_pool* p, int64_t seq_id, void* event, uint64_
     if (p->ref[b] == 0) g.blocks.push_back(b);
   }
   p->seqs.erase(it);
+  prefix_on_release(p, seq_id);
   if (immediate) {
     for (int32_t b : g.blocks) p->free_list.push_back(b);
     return ok();
@@ -365,7 +367,9 @@ kv_status kv_pool_check(const kv_pool* p) {
     }
   }
   for (int32_t b = 0; b < n; ++b)
-    if (counted[b] != p->ref[b]) return fail(KV_ERR_STATE, "reference count of block " + std::to_string(b) + " disagrees with the tables");
+    if (counted[b] + prefix_held(p, b) != p->ref[b])
+      return fail(KV_ERR_STATE, "reference count of block " + std::to_string(b) +
+                                    " disagrees with the tables and the prefix cache");
   std::vector<char> state(n, 0);  // 1 free, 2 pending
   for (int32_t b : p->free_list) {
     if (b < 0 || b >= n || state[b]) return fail(KV_ERR_STATE, "free list holds a duplicate or invalid block");

@@ -12,6 +12,8 @@
 
 #include "pagedkv.h"
 
+struct kv_prefix_tree;  // prefix_cache.cpp
+
 struct kv_seq_state {
   std::vector<int32_t> table;  // logical block j -> physical block
   int32_t length = 0;          // tokens
@@ -33,6 +35,7 @@ struct kv_pool {
   std::unordered_map<int64_t, kv_seq_state> seqs;
   std::deque<kv_pending_group> pending;      // released, waiting for the device
   int32_t n_pending = 0;
+  kv_prefix_tree* tree = nullptr;            // prefix cache, created on first use
 };
 
 namespace pagedkv {
@@ -63,6 +66,11 @@ inline int64_t pool_bytes(const kv_pool_config& c) {
 
 // Sets the thread-local error message and returns the status.
 kv_status fail(kv_status st, const std::string& msg);
+
+// Prefix cache hooks (prefix_cache.cpp).
+void prefix_on_release(kv_pool* p, int64_t seq);  // the request gives back its nodes' ref_counts
+void prefix_destroy(kv_pool* p);
+int32_t prefix_held(const kv_pool* p, int32_t block);  // references the tree holds on a block
 
 // Shared by the attention entry points (defined with the decode kernels).
 constexpr int kMaxGroup = 16;  // query heads per KV head

@@ -101,6 +101,22 @@ class PagedKVPool:
         B.paged_attention_prefill(self.handle, layer, q, out, q_indptr, block_tables, context_lens, max_q_len,
                                   num_q_heads, opts, workspace, stream)
 
+    # -- prefix cache --------------------------------------------------------
+    def prefix_match(self, tokens):
+        return B.kv_prefix_match(self.handle, tokens)
+
+    def attach_prefix(self, seq, tokens):
+        return B.kv_seq_attach_prefix(self.handle, seq, tokens)
+
+    def prefix_insert(self, seq, tokens):
+        return B.kv_prefix_insert(self.handle, seq, tokens)
+
+    def prefix_evict(self, target_free, stream=None, fence=None):
+        return B.kv_prefix_evict(self.handle, target_free, stream, fence)
+
+    def prefix_stats(self):
+        return B.kv_prefix_stats(self.handle)
+
     # -- raw views for tests -------------------------------------------------
     def raw(self, which):
         """The K or V buffer as a flat tensor of stored bit patterns (bytes for a quantised pool)."""
