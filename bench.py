@@ -17,6 +17,9 @@ Workloads (synthetic, seeded; see synth/workloads.py):
   3  16 x 8448 tokens sharing a 6144-token prefix, same shapes, 4 layers.
   4  70B-GQA-shaped layer: 12 x 131072 tokens, Hq=64, split-K 512.
   5  agentic fork: 64 sequences (4 roots x 16 forks) x ~33K tokens, 36 layers.
+--cascade (configs 3, 5) decodes through paged_attention_decode_cascade: the
+groups come from kv_shared_prefix_plan every step, each group's shared prefix
+is read once; roofline bytes then count the prefix once per group.
 
 --op prefill / verify time the multi-query path instead (paged_attention_prefill):
   prefill  the last 512-token chunk of 16 8K-token prompts (7680 cached tokens each),
@@ -53,6 +56,8 @@ def parse():
     ap.add_argument("--op", default="decode", choices=["decode", "prefill", "verify"],
                     help="decode: the decode step of --config; prefill: the last 512-token chunk of 16 "
                          "8K prompts; verify: 8 draft positions for 16 requests with 8K contexts")
+    ap.add_argument("--cascade", action="store_true",
+                    help="decode through paged_attention_decode_cascade (shared prefixes read once per group)")
     ap.add_argument("--layers", type=int, default=0, help="layer buffers (0 = workload default)")
     ap.add_argument("--partition", type=int, default=-1, help="partition tokens (-1 = workload default)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "generic"])
@@ -156,7 +161,12 @@ def main():
     kv_in = [[(randn_bf16(S, Hkv, d), randn_bf16(S, Hkv, d)) for _ in range(L)] for _ in range(total_steps)] \
         if step_appends else None
     out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
-    ws_bytes = pool.workspace_bytes(S, Hq, max_blocks, opts)
+    if args.cascade:
+        # groups of up to S members, any number of groups (the prefix partition depends on it)
+        ws_bytes = max(pool.cascade_workspace_bytes(S, ng, S, Hq, max_blocks, opts) for ng in range(1, S + 1))
+        d_plan = torch.empty((2 * S + 1,), dtype=torch.int32, device=dev)
+    else:
+        ws_bytes = pool.workspace_bytes(S, Hq, max_blocks, opts)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device=dev)
     d_lens = torch.empty((S,), dtype=torch.int32, device=dev)
@@ -165,6 +175,7 @@ def main():
     h_tables = [torch.empty((S, max_blocks), dtype=torch.int32).pin_memory() for _ in range(ring)]
     h_lens = [torch.empty((S,), dtype=torch.int32).pin_memory() for _ in range(ring)]
     h_slots = [torch.empty((S,), dtype=torch.int64).pin_memory() for _ in range(ring)]
+    h_plan = [torch.empty((2 * S + 1,), dtype=torch.int32).pin_memory() for _ in range(ring)]
     ring_ev = [None] * ring
     seq_arr = np.asarray(decode_seqs, np.int64)
     stream = torch.cuda.current_stream()
@@ -172,6 +183,8 @@ def main():
     attn_ev = []  # (start, end) HIP events around every paged_attention_decode
     logical_bytes = [0]
     n_copies = [0]
+    n_groups = [0]
+    read_bytes = [0]  # KV bytes the path reads (shared prefixes once per group with --cascade)
 
     def step(i, timed):
         slot = i % ring
@@ -187,6 +200,18 @@ def main():
         h_lens[slot].numpy()[:] = lens
         d_tables.copy_(h_tables[slot], non_blocking=True)
         d_lens.copy_(h_lens[slot], non_blocking=True)
+        if args.cascade:
+            gs, sb = pool.shared_prefix_plan(seq_arr)
+            ng = len(sb)
+            h_plan[slot].numpy()[:ng + 1] = gs
+            h_plan[slot].numpy()[ng + 1:2 * ng + 1] = sb
+            d_plan[:2 * ng + 1].copy_(h_plan[slot][:2 * ng + 1], non_blocking=True)
+            n_groups[0] = ng
+            # tokens the cascade reads: each group's shared prefix once, every member's suffix
+            shared_tok = np.repeat(sb.astype(np.int64) * Bs, np.diff(gs))
+            read_tokens = int(sb.astype(np.int64).sum()) * Bs + int((lens.astype(np.int64) - shared_tok).sum())
+        else:
+            read_tokens = int(lens.astype(np.int64).sum())
         ev = torch.cuda.Event()
         ev.record(stream)
         ring_ev[slot] = ev
@@ -200,11 +225,17 @@ def main():
             if timed:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            pool.decode(layer, q_in[i][layer], out, d_tables, d_lens, Hq, opts, ws)
+            if args.cascade:
+                ng = n_groups[0]
+                pool.decode_cascade(layer, q_in[i][layer], out, d_tables, d_lens, Hq, d_plan[:ng + 1],
+                                    d_plan[ng + 1:2 * ng + 1], S, opts, ws)
+            else:
+                pool.decode(layer, q_in[i][layer], out, d_tables, d_lens, Hq, opts, ws)
             if timed:
                 e1.record(stream)
                 attn_ev.append((e0, e1))
                 logical_bytes[0] += int(lens.astype(np.int64).sum()) * kv_tok
+                read_bytes[0] += read_tokens * kv_tok
         return lens
 
     for i in range(args.warmup):
@@ -219,10 +250,11 @@ def main():
     wall = t1 - t0
     ms_step = wall / args.steps * 1e3
 
+    attn_name = "paged_attention_decode_cascade" if args.cascade else "paged_attention_decode"
     attn_ms = [a.elapsed_time(b) for a, b in attn_ev]
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     n_launch = len(attn_ms)
-    kv_bytes_per_launch = logical_bytes[0] / n_launch
+    kv_bytes_per_launch = read_bytes[0] / n_launch
     blocks_per_launch = float(np.mean([np.ceil(l / Bs).sum() for l in lens_hist]))
     ideal_per_launch = kv_bytes_per_launch + 2 * S * Hq * d * 2 + 4 * blocks_per_launch
     achieved = ideal_per_launch / attn_avg_s / 1e9
@@ -259,8 +291,8 @@ def main():
             "kernel": args.kernel,
             "kv_storage": args.kv,
             "kv_bytes_per_token_per_layer": kv_tok,
-            "step": (f"append + {L} x (reshape_and_cache + paged_attention_decode)" if step_appends
-                     else f"{L} x paged_attention_decode"),
+            "step": (f"append + {L} x (reshape_and_cache + {attn_name})" if step_appends
+                     else f"{L} x {attn_name}"),
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "attn_tokens_per_s_per_layer": round(tok_per_s_layer, 1),
@@ -275,8 +307,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(base.name),
-            "kernel": "paged_attention_decode (split-K kernel + merge kernel)",
+            "traffic": measured_traffic(base.name + ("" if args.kv == "bf16" else f"_{args.kv}")
+                                        + ("_cascade" if args.cascade else ""),
+                                        ("kernels.hip", "prefill.hip") if args.cascade else ("kernels.hip",)),
+            "kernel": ("paged_attention_decode_cascade (prefix multi-query kernel + split-K kernel + merge)"
+                       if args.cascade else "paged_attention_decode (split-K kernel + merge kernel)"),
             "algorithmic_bytes_per_launch": int(ideal_per_launch),
         },
         "cpu_baseline": None,
@@ -369,6 +404,7 @@ def multi_query_bench(args):
         step(i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    attn_name = "paged_attention_decode_cascade" if args.cascade else "paged_attention_decode"
     attn_ms = [a.elapsed_time(b) for a, b in attn_ev]
     attn_s = float(np.mean(attn_ms)) / 1e3
     n = lens.astype(np.int64)
@@ -411,7 +447,7 @@ def multi_query_bench(args):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(flops / attn_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(base.name, "prefill.hip"),
+            "traffic": measured_traffic(base.name, ("prefill.hip",)),
             "kernel": "attn_prefill_kernel",
             "algorithmic_flops_per_launch": flops,
         } if prefill else {
@@ -420,7 +456,7 @@ def multi_query_bench(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ideal_bytes / attn_s / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(base.name, "prefill.hip"),
+            "traffic": measured_traffic(base.name, ("prefill.hip",)),
             "kernel": "attn_prefill_kernel + merge_prefill_kernel",
             "algorithmic_bytes_per_launch": ideal_bytes,
         }),
@@ -466,20 +502,26 @@ def multi_query_cpu_baseline(args, wl):
     }
 
 
-def measured_traffic(workload, source="kernels.hip"):
-    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this
-    workload, or None when there is none or the kernel source changed since it was taken."""
+def kernel_source_sha256(sources):
     import hashlib
 
+    h = hashlib.sha256()
+    for name in sources:
+        with open(os.path.join(ROOT, "pagedattention_decode_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, sources=("kernels.hip",)):
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this
+    workload, or None when there is none or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
-    src = os.path.join(ROOT, "pagedattention_decode_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec.get("kernel_source_sha256"):
-            return None
+    if kernel_source_sha256(sources) != rec.get("kernel_source_sha256"):
+        return None
     return rec.get("traffic_bytes_per_call")
 
 

@@ -244,6 +244,15 @@ kv_status kv_prefix_evict(kv_pool* pool, int32_t target_free, void* hip_stream, 
 kv_status kv_prefix_evict_fenced(kv_pool* pool, int32_t target_free, uint64_t fence, int32_t* blocks_out,
                                  int32_t cap, int32_t* n_out);
 
+/* Groups for paged_attention_decode_cascade from the host tables: maximal runs
+ * of consecutive sequences of seq_ids[0, n) that share at least one completely
+ * filled leading block with the run's first member; shared_blocks[g] = the
+ * number of leading blocks every member has in common with it and completely
+ * filled (0 for a run of one).  group_start needs n + 1 entries, shared_blocks
+ * n; *n_groups receives the number of groups. */
+kv_status kv_shared_prefix_plan(const kv_pool* pool, int32_t n, const int64_t* seq_ids, int32_t* group_start,
+                                int32_t* shared_blocks, int32_t* n_groups);
+
 /* Nodes, blocks cached by the tree, and pinned nodes (ref_count > 0). */
 kv_status kv_prefix_stats(const kv_pool* pool, int32_t* n_nodes, int32_t* n_cached_blocks, int32_t* n_pinned);
 
@@ -317,6 +326,37 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
                                  int32_t n_seqs, int32_t max_blocks_per_seq, int32_t num_q_heads,
                                  const kv_attention_options* opts, void* d_workspace,
                                  uint64_t workspace_bytes, void* hip_stream);
+
+/* Read-once decode over shared prefixes (cascade).  Sequences are given in
+ * groups: group g holds the sequences group_start[g] .. group_start[g+1]-1 (in
+ * the order of q, out and the tables), whose tables agree on their first
+ * shared_blocks[g] blocks, each completely filled (every member's context is
+ * at least 16 * shared_blocks[g] tokens) — forks of one request share such
+ * blocks physically ([KVM] CoW branching, cross-turn prefix caching).  The
+ * result equals paged_attention_decode; the shared blocks are read once per
+ * group instead of once per member:
+ *   prefix: the multi-query kernel over the shared blocks, the members'
+ *           queries as its columns, no causal mask;
+ *   suffix: the split-K decode over each member's remaining blocks;
+ *   merge:  both kinds of partials folded with the [KVM] recurrences.
+ * A member whose shared entries differ from the first member's, or whose
+ * context (or the first member's) does not cover them, gets a NaN row (checked
+ * on the device); so do the members of a group larger than max_group.  bf16 pools with the
+ * matrix-core kernel only (KV_ERR_UNSUPPORTED otherwise).
+ *   d_group_start:   device int32[n_groups + 1], group_start[0] = 0,
+ *                    non-decreasing, group_start[n_groups] = n_seqs.
+ *   d_shared_blocks: device int32[n_groups] (0 = no shared prefix).
+ *   max_group:       an upper bound of every group's size (sizes the grid).
+ *   d_workspace:     paged_attention_cascade_workspace_bytes, 256-byte aligned. */
+uint64_t paged_attention_cascade_workspace_bytes(kv_pool* pool, int32_t n_seqs, int32_t n_groups, int32_t max_group,
+                                                 int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                                 const kv_attention_options* opts);
+kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const void* q, void* out,
+                                         const int32_t* d_block_tables, const int32_t* d_context_lens,
+                                         int32_t n_seqs, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                                         const int32_t* d_group_start, const int32_t* d_shared_blocks,
+                                         int32_t n_groups, int32_t max_group, const kv_attention_options* opts,
+                                         void* d_workspace, uint64_t workspace_bytes, void* hip_stream);
 
 /* Device workspace needed by paged_attention_prefill for these arguments. */
 uint64_t paged_prefill_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int32_t total_q, int32_t max_q_len,

@@ -82,6 +82,11 @@ SIGNATURES = {
     "kv_prefix_evict": (_I32, [_P, _I32, _P, _P, _I32, C.POINTER(_I32)]),
     "kv_prefix_evict_fenced": (_I32, [_P, _I32, _U64, _P, _I32, C.POINTER(_I32)]),
     "kv_prefix_stats": (_I32, [_P, C.POINTER(_I32), C.POINTER(_I32), C.POINTER(_I32)]),
+    "kv_shared_prefix_plan": (_I32, [_P, _I32, _P, _P, _P, C.POINTER(_I32)]),
+    "paged_attention_cascade_workspace_bytes": (_U64, [_P, _I32, _I32, _I32, _I32, _I32,
+                                                       C.POINTER(kv_attention_options)]),
+    "paged_attention_decode_cascade": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _I32,
+                                              C.POINTER(kv_attention_options), _P, _U64, _P]),
     "paged_prefill_workspace_bytes": (_U64, [_P, _I32, _I32, _I32, _I32, _I32, C.POINTER(kv_attention_options)]),
     "paged_attention_prefill": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                        C.POINTER(kv_attention_options), _P, _U64, _P]),
@@ -344,3 +349,37 @@ def kv_prefix_stats(pool):
     a, b, c = _I32(), _I32(), _I32()
     _check(lib().kv_prefix_stats(pool, C.byref(a), C.byref(b), C.byref(c)))
     return {"n_nodes": a.value, "n_cached_blocks": b.value, "n_pinned": c.value}
+
+
+# -- cascade decode over shared prefixes ---------------------------------------
+
+def kv_shared_prefix_plan(pool, seq_ids):
+    """(group_start int32 [g + 1], shared_blocks int32 [g]) for the sequences in order."""
+    ids, ip = _host(seq_ids, np.int64)
+    n = len(ids)
+    gs = np.zeros(n + 1, np.int32)
+    sb = np.zeros(max(n, 1), np.int32)
+    ng = _I32()
+    _check(lib().kv_shared_prefix_plan(pool, n, ip, gs.ctypes.data_as(C.c_void_p), sb.ctypes.data_as(C.c_void_p),
+                                       C.byref(ng)))
+    return gs[:ng.value + 1].copy(), sb[:ng.value].copy()
+
+
+def paged_attention_cascade_workspace_bytes(pool, n_seqs, n_groups, max_group, num_q_heads, max_blocks_per_seq,
+                                            opts=None):
+    return int(lib().paged_attention_cascade_workspace_bytes(pool, int(n_seqs), int(n_groups), int(max_group),
+                                                             int(num_q_heads), int(max_blocks_per_seq),
+                                                             C.byref(opts) if opts is not None else None))
+
+
+def paged_attention_decode_cascade(pool, layer, q, out, block_tables, context_lens, num_q_heads, group_start,
+                                   shared_blocks, max_group, opts=None, workspace=None, stream=None):
+    """group_start: device int32 [g + 1]; shared_blocks: device int32 [g]."""
+    n_seqs, max_blocks = int(block_tables.shape[0]), int(block_tables.shape[1])
+    n_groups = int(shared_blocks.shape[0])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().paged_attention_decode_cascade(pool, int(layer), _dev(q), _dev(out), _dev(block_tables),
+                                                _dev(context_lens), n_seqs, max_blocks, int(num_q_heads),
+                                                _dev(group_start), _dev(shared_blocks), n_groups, int(max_group),
+                                                C.byref(opts) if opts is not None else None, _dev(workspace),
+                                                ws_bytes, _stream(stream)))

@@ -549,6 +549,7 @@ struct sk_args {
   int n_seqs, max_blocks, n_q_heads, n_kv_heads, num_blocks, part_blocks, n_waves;
   int q_units;  // units per wave whose queries are staged in LDS (<= kSkQUnits)
   float scale_log2;
+  int force_partial;  // every unit ends in partials (the cascade merge folds them with a prefix)
 };
 
 __device__ __forceinline__ int blocks_of(const int32_t* __restrict__ ctx_lens, int s, int cap) {
@@ -764,7 +765,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     l += __shfl_xor(l, 32);
     const int h = cs.kvh * G + hg;
     const float nan = __builtin_nanf("");
-    if (seg_j0 == 0 && cs.j == cs.nb - 1) {  // the whole unit: final row
+    if (seg_j0 == 0 && cs.j == cs.nb - 1 && !a.force_partial) {  // the whole unit: final row
       const float inv = poisoned ? 0.f : 1.f / l;
       uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(cs.seq) * a.n_q_heads + h) * D;
 #pragma unroll
@@ -928,6 +929,176 @@ __global__ void __launch_bounds__(kMergeThreads) merge_sk_kernel(sk_args a, int 
     o4[2] = f32_to_bf16(sum.z * inv);
     o4[3] = f32_to_bf16(sum.w * inv);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Cascade decode over shared prefixes (read once per group).  Sequences come
+// in groups [group_start[g], group_start[g+1]) whose tables agree on their first
+// shared[g] blocks (forks of one request; the [KVM] CoW branching and prefix
+// caching make such blocks physically shared).  The decode of a member splits
+// into two key ranges merged with the running-max recurrences of [KVM]
+// (chunked prefill mechanism):
+//   prefix: the shared blocks, read once for all members by the multi-query
+//           kernel with the members' queries as columns (no causal mask);
+//   suffix: the member's own blocks, by the split-K decode kernel on a
+//           shifted table (every unit ends in partials);
+// cascade_merge folds both kinds of partials into the output row.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int group_of(const int32_t* __restrict__ group_start, int n_groups, int s) {
+  int lo = 0, hi = n_groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (group_start[mid] <= s) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One workgroup per sequence: checks the member against its group (the shared
+// entries equal the first member's, both contexts cover them), then writes the
+// suffix table row, the suffix length and the member's verdict; the group's
+// first member writes the prefix length.
+__global__ void __launch_bounds__(256) cascade_prep_kernel(
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ ctx, const int32_t* __restrict__ group_start,
+    const int32_t* __restrict__ shared, int n_seqs, int n_groups, int max_blocks, int32_t* __restrict__ tables_sfx,
+    int32_t* __restrict__ ctx_sfx, int32_t* __restrict__ prefix_ctx, int32_t* __restrict__ bad) {
+  __shared__ int mismatch;
+  const int s = blockIdx.x;
+  const int g = group_of(group_start, n_groups, s);
+  const int first = group_start[g];
+  const int skip = shared[g];
+  const int n = min(ctx[s], max_blocks * 16);
+  // the first member's context must cover the prefix too: it alone sets the
+  // prefix length, and every member reads the prefix through its table row
+  bool ok = first >= 0 && first <= s && s < group_start[g + 1] && skip >= 0 && skip <= max_blocks &&
+            16 * skip <= max(n, 0) && 16 * skip <= max(min(ctx[first], max_blocks * 16), 0);
+  if (threadIdx.x == 0) mismatch = 0;
+  __syncthreads();
+  if (ok)
+    for (int j = threadIdx.x; j < skip; j += blockDim.x)
+      if (tables[static_cast<int64_t>(s) * max_blocks + j] != tables[static_cast<int64_t>(first) * max_blocks + j])
+        mismatch = 1;
+  __syncthreads();
+  ok = ok && !mismatch;
+  const int shift = ok ? skip : 0;
+  for (int j = threadIdx.x; j < max_blocks; j += blockDim.x)
+    tables_sfx[static_cast<int64_t>(s) * max_blocks + j] =
+        (ok && j + shift < max_blocks) ? tables[static_cast<int64_t>(s) * max_blocks + j + shift] : -1;
+  if (threadIdx.x == 0) {
+    ctx_sfx[s] = ok ? n - 16 * skip : 0;
+    bad[s] = ok ? 0 : 1;
+    if (s == first) prefix_ctx[g] = ok ? 16 * skip : 0;
+  }
+}
+
+struct cascade_args {
+  sk_args sfx;                 // the suffix decode (cum_parts, slots, n_waves)
+  const int32_t* group_start;  // [n_groups + 1]
+  const int32_t* prefix_ctx;   // [n_groups] tokens of the shared prefix
+  const int32_t* bad;          // [n_seqs]
+  const int32_t* ctx;          // [n_seqs] full contexts
+  const float* pre_m;          // prefix partials [n_seqs * Hq][pre_parts]
+  const float* pre_l;
+  const float* pre_o;          // [..][D]
+  int n_groups, max_group, pre_part_tokens, pre_parts;
+};
+
+// One wave per (sequence, query head): the prefix partitions and the suffix
+// runs of the member, folded with M = max m, out = sum 2^(m - M) O / sum
+// 2^(m - M) l.  A poisoned partial, a member that failed its check, or a
+// group larger than the multi-query grid gives a NaN row; no keys at all give
+// a zero row.
+template <int D>
+__global__ void __launch_bounds__(256) cascade_merge_kernel(cascade_args c) {
+  const sk_args& a = c.sfx;
+  const int lane = threadIdx.x & 63;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (item >= static_cast<int64_t>(a.n_seqs) * a.n_q_heads) return;
+  const int s = static_cast<int>(item / a.n_q_heads);
+  const int head = static_cast<int>(item % a.n_q_heads);
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int kvh = head / G, hg = head % G;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + item * D;
+  constexpr int E = (D + 63) / 64;
+  const int g = group_of(c.group_start, c.n_groups, s);
+  const bool nan_row = c.bad[s] != 0 || c.group_start[g + 1] - c.group_start[g] > c.max_group;
+  const int pre_tokens = c.prefix_ctx[g];
+  const int n_pre = pre_tokens > 0 ? (pre_tokens + c.pre_part_tokens - 1) / c.pre_part_tokens : 0;
+  // suffix runs: waves wF..wL of unit (s, kvh), as the split-K merge finds them
+  const int np = a.cum_parts[s + 1] - a.cum_parts[s];
+  const int64_t total = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[a.n_seqs];
+  const int64_t W = a.n_waves;
+  int64_t wF = 0, wL = -1;
+  if (np > 0) {
+    const int64_t first = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[s] + static_cast<int64_t>(kvh) * np;
+    wF = ((first + 1) * W - 1) / total;
+    wL = ((first + np) * W - 1) / total;
+  }
+  auto run_begin = [&](int64_t w) { return w * total / W; };
+  const int64_t unit = static_cast<int64_t>(s) * a.n_kv_heads + kvh;
+  const int n_suf = static_cast<int>(wL - wF + 1);
+  // entry i < n_pre: prefix partition i; else suffix wave wF + (i - n_pre)
+  auto entry = [&](int i, float& m, float& l, const float*& o) {
+    if (i < n_pre) {
+      const int64_t r = item * c.pre_parts + i;
+      m = c.pre_m[r];
+      l = c.pre_l[r];
+      o = c.pre_o + r * D;
+    } else {
+      const int64_t w = wF + (i - n_pre);
+      if (!(run_begin(w) < run_begin(w + 1))) {  // a wave with an empty run wrote nothing
+        m = -INFINITY;
+        l = 0.f;
+        o = nullptr;
+        return;
+      }
+      const int64_t row = (w + unit) * G + hg;
+      m = a.part_m[row];
+      l = a.part_l[row];
+      o = a.part_o + row * D;
+    }
+  };
+  const int n_ent = n_pre + n_suf;
+  float M = -INFINITY;
+  bool nan_seen = nan_row;
+  for (int i0 = 0; i0 < n_ent; i0 += 64) {
+    float m = -INFINITY, l;
+    const float* o;
+    if (i0 + lane < n_ent) entry(i0 + lane, m, l, o);
+    nan_seen |= __builtin_amdgcn_ballot_w64(m != m) != 0;
+    M = fmaxf(M, m);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float acc[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) acc[i] = 0.f;
+  float L = 0.f;
+  for (int i0 = 0; i0 < n_ent; i0 += 64) {
+    float m = -INFINITY, l = 0.f;
+    const float* o = nullptr;
+    if (i0 + lane < n_ent) entry(i0 + lane, m, l, o);
+    const float w = (m == -INFINITY || m != m) ? 0.f : exp2f(m - M);
+    L += w == 0.f ? 0.f : w * l;
+    const int cnt = min(64, n_ent - i0);
+    for (int k = 0; k < cnt; ++k) {
+      const float wk = __shfl(w, k);
+      if (wk == 0.f) continue;  // wave uniform
+      float mk, lk;
+      const float* ok;
+      entry(i0 + k, mk, lk, ok);
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        if (lane + 64 * i < D) acc[i] += wk * ok[lane + 64 * i];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+  const bool empty = M == -INFINITY && !nan_seen;  // no key at all
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    if (lane + 64 * i < D)
+      orow[lane + 64 * i] = nan_seen ? static_cast<uint16_t>(0x7fc0) : (empty ? 0 : f32_to_bf16(acc[i] / L));
 }
 
 // ---------------------------------------------------------------------------
@@ -1360,6 +1531,138 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     if (kv_status s = hip_check(hipGetLastError(), "paged attention merge launch")) return s;
   }
   return KV_OK;
+}
+
+// ---- cascade decode over shared prefixes ---------------------------------
+
+namespace {
+
+struct cascade_layout {
+  uint64_t decode, tables, ctx, prefix_ctx, bad, pre, total;
+  int pre_part_tokens, pre_parts;
+};
+
+kv_status cascade_plan(kv_pool* pool, int n_seqs, int n_groups, int max_group, int num_q_heads, int max_blocks,
+                       const kv_attention_options* opts, resolved& r, cascade_layout& L) {
+  if (kv_status s = resolve(pool, n_seqs, num_q_heads, max_blocks, opts, r)) return s;
+  if (r.kernel != KV_KERNEL_MFMA || pool->cfg.dtype != KV_BF16)
+    return fail(KV_ERR_UNSUPPORTED, "the cascade decode needs a bf16 pool and the matrix-core kernel");
+  if (n_groups < 1 || n_groups > n_seqs || max_group < 1)
+    return fail(KV_ERR_INVALID, "need 1 <= n_groups <= n_seqs and max_group >= 1");
+  uint64_t pre_bytes = 0;
+  if (kv_status s = prefix_phase_plan(pool, n_groups, n_seqs, max_group, num_q_heads, max_blocks, opts,
+                                      &L.pre_part_tokens, &L.pre_parts, &pre_bytes))
+    return s;
+  L.decode = up256(workspace_for(pool->cfg, n_seqs, num_q_heads, r));
+  L.tables = L.decode;
+  L.ctx = L.tables + up256(static_cast<uint64_t>(n_seqs) * max_blocks * 4);
+  L.prefix_ctx = L.ctx + up256(static_cast<uint64_t>(n_seqs) * 4);
+  L.bad = L.prefix_ctx + up256(static_cast<uint64_t>(n_groups) * 4);
+  L.pre = L.bad + up256(static_cast<uint64_t>(n_seqs) * 4);
+  L.total = L.pre + up256(pre_bytes);
+  return KV_OK;
+}
+
+}  // namespace
+
+uint64_t paged_attention_cascade_workspace_bytes(kv_pool* pool, int32_t n_seqs, int32_t n_groups, int32_t max_group,
+                                                 int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                                 const kv_attention_options* opts) {
+  if (!pool || n_seqs <= 0) return 0;
+  resolved r;
+  cascade_layout L;
+  if (cascade_plan(pool, n_seqs, n_groups, max_group, num_q_heads, max_blocks_per_seq, opts, r, L) != KV_OK) return 0;
+  return L.total;
+}
+
+kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const void* q, void* out,
+                                         const int32_t* d_block_tables, const int32_t* d_context_lens,
+                                         int32_t n_seqs, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                                         const int32_t* d_group_start, const int32_t* d_shared_blocks,
+                                         int32_t n_groups, int32_t max_group, const kv_attention_options* opts,
+                                         void* d_workspace, uint64_t workspace_bytes, void* hip_stream) {
+  if (!pool) return fail(KV_ERR_INVALID, "pool is NULL");
+  const kv_pool_config& c = pool->cfg;
+  if (layer < 0 || layer >= c.num_layers) return fail(KV_ERR_INVALID, "layer out of range");
+  if (n_seqs == 0) return KV_OK;
+  resolved r;
+  cascade_layout L;
+  if (kv_status s = cascade_plan(pool, n_seqs, n_groups, max_group, num_q_heads, max_blocks_per_seq, opts, r, L))
+    return s;
+  if (!q || !out || !d_block_tables || !d_context_lens || !d_group_start || !d_shared_blocks || !pool->k_cache ||
+      !pool->v_cache)
+    return fail(KV_ERR_INVALID, "NULL device pointer");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(KV_ERR_INVALID, "q and out must be 16-byte aligned");
+  if (!d_workspace || workspace_bytes < L.total)
+    return fail(KV_ERR_INVALID, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  if (reinterpret_cast<uintptr_t>(d_workspace) & 255) return fail(KV_ERR_INVALID, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(d_workspace);
+  int32_t* tables_sfx = reinterpret_cast<int32_t*>(ws + L.tables);
+  int32_t* ctx_sfx = reinterpret_cast<int32_t*>(ws + L.ctx);
+  int32_t* prefix_ctx = reinterpret_cast<int32_t*>(ws + L.prefix_ctx);
+  int32_t* bad = reinterpret_cast<int32_t*>(ws + L.bad);
+  hipLaunchKernelGGL(cascade_prep_kernel, dim3(static_cast<unsigned>(n_seqs)), dim3(256), 0, st, d_block_tables,
+                     d_context_lens, d_group_start, d_shared_blocks, n_seqs, n_groups, max_blocks_per_seq,
+                     tables_sfx, ctx_sfx, prefix_ctx, bad);
+  if (kv_status s = hip_check(hipGetLastError(), "cascade prep launch")) return s;
+  // prefix: every group's shared blocks, once, for all members
+  if (kv_status s = prefix_phase_launch(pool, layer, q, out, d_group_start, prefix_ctx, d_block_tables, n_groups,
+                                        n_seqs, max_group, max_blocks_per_seq, num_q_heads, opts, ws + L.pre, st))
+    return s;
+  // suffix: the split-K decode on the shifted tables, partials only
+  const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
+  const int G = num_q_heads / c.num_kv_heads;
+  sk_args a{};
+  a.q = q;
+  a.out = out;
+  a.k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
+  a.v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
+  const uint64_t slots = static_cast<uint64_t>(r.groups) * kSkWaves + static_cast<uint64_t>(n_seqs) * c.num_kv_heads;
+  a.part_m = reinterpret_cast<float*>(ws);
+  a.part_l = reinterpret_cast<float*>(ws + up256(slots * G * 4));
+  a.part_o = reinterpret_cast<float*>(ws + 2 * up256(slots * G * 4));
+  a.cum_parts = reinterpret_cast<int32_t*>(ws + 2 * up256(slots * G * 4) + up256(slots * G * c.head_dim * 4));
+  a.n_seqs = n_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.n_q_heads = num_q_heads;
+  a.n_kv_heads = c.num_kv_heads;
+  a.num_blocks = c.num_blocks;
+  a.part_blocks = r.partition / c.block_size;
+  a.n_waves = static_cast<int>(r.groups * kSkWaves);
+  a.q_units = sk_q_units(G, c.head_dim);
+  a.scale_log2 = r.scale * kLog2e;
+  a.force_partial = 1;
+  hipError_t e;
+  switch (c.head_dim) {
+    case 64: e = launch_mfma<64, kFmtBf16>(a, ctx_sfx, tables_sfx, r.groups, G, st); break;
+    case 128: e = launch_mfma<128, kFmtBf16>(a, ctx_sfx, tables_sfx, r.groups, G, st); break;
+    default: e = launch_mfma<256, kFmtBf16>(a, ctx_sfx, tables_sfx, r.groups, G, st); break;
+  }
+  if (kv_status s = hip_check(e, "cascade suffix launch")) return s;
+  cascade_args m{};
+  m.sfx = a;
+  m.group_start = d_group_start;
+  m.prefix_ctx = prefix_ctx;
+  m.bad = bad;
+  m.ctx = d_context_lens;
+  const uint64_t pre_rows = static_cast<uint64_t>(n_seqs) * num_q_heads * L.pre_parts;
+  m.pre_m = reinterpret_cast<const float*>(ws + L.pre);
+  m.pre_l = reinterpret_cast<const float*>(ws + L.pre + up256(pre_rows * 4));
+  m.pre_o = reinterpret_cast<const float*>(ws + L.pre + 2 * up256(pre_rows * 4));
+  m.n_groups = n_groups;
+  m.max_group = max_group;
+  m.pre_part_tokens = L.pre_part_tokens;
+  m.pre_parts = L.pre_parts;
+  const int64_t items = static_cast<int64_t>(n_seqs) * num_q_heads;
+  const unsigned mgrid = static_cast<unsigned>((items + 3) / 4);
+  switch (c.head_dim) {
+    case 64: hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mgrid), dim3(256), 0, st, m); break;
+    case 128: hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mgrid), dim3(256), 0, st, m); break;
+    default: hipLaunchKernelGGL(cascade_merge_kernel<256>, dim3(mgrid), dim3(256), 0, st, m); break;
+  }
+  return hip_check(hipGetLastError(), "cascade merge launch");
 }
 
 }  // extern "C"

@@ -337,6 +337,44 @@ kv_status kv_pool_stats(const kv_pool* p, kv_pool_stats_t* out) {
   return ok();
 }
 
+kv_status kv_shared_prefix_plan(const kv_pool* p, int32_t n, const int64_t* seq_ids, int32_t* group_start,
+                                int32_t* shared_blocks, int32_t* n_groups) {
+  if (!p || !n_groups || (n > 0 && (!seq_ids || !group_start || !shared_blocks)))
+    return fail(KV_ERR_INVALID, "NULL argument");
+  if (n < 0) return fail(KV_ERR_INVALID, "n < 0");
+  std::vector<const kv_seq_state*> s(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(seq_ids[i]);
+    if (it == p->seqs.end()) return fail(KV_ERR_INVALID, "unknown sequence " + std::to_string(seq_ids[i]));
+    s[i] = &it->second;
+  }
+  const int32_t B = p->cfg.block_size;
+  // leading blocks of b that equal a's and are completely filled in both
+  auto common = [&](const kv_seq_state* a, const kv_seq_state* b) {
+    const int32_t lim = std::min(a->length, b->length) / B;
+    int32_t j = 0;
+    while (j < lim && a->table[j] == b->table[j]) ++j;
+    return j;
+  };
+  int32_t g = 0;
+  for (int32_t i = 0; i < n;) {
+    int32_t shared = 0, k = i + 1;
+    while (k < n) {
+      const int32_t c = common(s[i], s[k]);
+      if (c < 1) break;
+      shared = (k == i + 1) ? c : std::min(shared, c);
+      ++k;
+    }
+    group_start[g] = i;
+    shared_blocks[g] = shared;
+    ++g;
+    i = k;
+  }
+  group_start[g] = n;
+  *n_groups = g;
+  return ok();
+}
+
 kv_status kv_pool_free_list(const kv_pool* p, int32_t cap, int32_t* out, int32_t* n_out) {
   if (!p || !n_out) return fail(KV_ERR_INVALID, "NULL argument");
   const int32_t n = static_cast<int32_t>(p->free_list.size());

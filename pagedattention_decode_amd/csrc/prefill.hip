@@ -59,6 +59,12 @@ struct pf_args {
   int wt;                        // tiles per workgroup (1, 2 or 4); the other factor of 4 is partitions
   int tile_groups, part_groups;  // workgroups per unit along tiles and along partitions
   float scale_log2;
+  // Shared-prefix mode (set by the cascade decode): every query sees all n
+  // keys (no causal mask), "sequence" s reads table row table_rows[s], and
+  // every tile writes partials even when it has one partition.
+  int causal;
+  int force_partial;
+  const int32_t* table_rows;  // nullptr: row s
 };
 
 // Two consecutive 16-token blocks in registers.  K as for the decode kernel
@@ -217,12 +223,14 @@ __device__ __forceinline__ pf_seq pf_locate(const pf_args& a, int s) {
   r.c = a.q_indptr[s + 1] - r.q0;
   r.n = min(a.ctx_lens[s], a.max_blocks * 16);
   r.h = r.n - r.c;
-  r.bad = r.c > a.max_q_len || r.c > r.n;
+  r.bad = r.c > a.max_q_len || (a.causal && r.c > r.n);
   return r;
 }
 
-// Keys [0, kend) of tile `tile` of a sequence: up to the position of its last column.
-__device__ __forceinline__ int pf_tile_keys(const pf_seq& q, int G, int tile, int nc) {
+// Keys [0, kend) of tile `tile` of a sequence: up to the position of its last
+// column (all n keys without the causal mask).
+__device__ __forceinline__ int pf_tile_keys(const pf_args& a, const pf_seq& q, int G, int tile, int nc) {
+  if (!a.causal) return q.n;
   const int f_last = min((tile + 1) * nc, q.c * G) - 1;
   return q.h + f_last / G + 1;
 }
@@ -258,7 +266,7 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
     return;
   }
   if (tile * NC >= cols) return;
-  const int kend = pf_tile_keys(sq, G, tile, NC);
+  const int kend = pf_tile_keys(a, sq, G, tile, NC);
   const int P = a.part_blocks * 16;
   const int k_begin = part * P;
   if (k_begin >= kend) return;
@@ -278,19 +286,20 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
     const bool live = f < cols;
     const int j = live ? f / G : 0;
     const int hg = live ? f % G : 0;
-    pos[cg] = live ? sq.h + j : -1;
+    pos[cg] = live ? (a.causal ? sq.h + j : sq.n - 1) : -1;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                          (static_cast<int64_t>(sq.q0 + j) * a.n_q_heads + g * G + hg) * D + quad * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
       q_lds[(cg * (D / 32) + kk) * 64 + lane] = live ? *reinterpret_cast<const bf16x8_t*>(qp + kk * 32) : bf16x8_t{};
   }
-  const int pos_min = sq.h + f0 / G;  // position of the tile's first column: older keys are visible to all
+  // position of the tile's first column: older keys are visible to all
+  const int pos_min = a.causal ? sq.h + f0 / G : sq.n - 1;
 
   const uint4* kpool = static_cast<const uint4*>(a.k_layer);
   const uint4* vpool = static_cast<const uint4*>(a.v_layer);
   constexpr int kTileVec = 16 * D * 2 / 16;  // 16-byte vectors per tile
-  const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.max_blocks;
+  const int32_t* trow = a.tables + static_cast<int64_t>(a.table_rows ? a.table_rows[s] : s) * a.max_blocks;
   // ring of STAGES block pairs; loads past the run repeat its last block (L2 hits)
   kv_pair<D> buf[STAGES];
   int phys_a[STAGES], phys_b[STAGES];
@@ -324,8 +333,12 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
 #pragma unroll
     for (int u = 0; u < STAGES; ++u) {
       const int b = b0 + 2 * u;
-      // keeps the LDS reads of Q^T inside the loop instead of hoisted into registers
-      asm volatile("" ::: "memory");
+      // an index that, for all the compiler knows, depends on b keeps the LDS
+      // reads of Q^T inside the loop (hoisted, they would hold D/4 * NCG more
+      // registers); unlike a memory clobber or a volatile statement it leaves
+      // the block-table reads scalar
+      int ql;
+      asm("" : "=v"(ql) : "0"(lane), "s"(b));
       if (b < b_end) {
         const bool has_b = b + 1 < b_end;  // else the second block is outside the partition: all masked
         const bool bad_a = phys_a[u] < 0 || phys_a[u] >= a.num_blocks;
@@ -335,7 +348,7 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
         const int valid_b = (!has_b || bad_b) ? 0 : min(16, sq.n - (b + 1) * 16);
         if (valid_a < 16 || valid_b < 16) zero_pair_tail<D>(buf[u], valid_a, valid_b, quad);
         if (valid_a == 16 && valid_b == 16 && b * 16 + 31 <= pos_min) {
-          attend_pair<D, NCG, false>(buf[u], q_lds, lane, nullptr, nullptr, quad, c, o, m_run, l_lane);
+          attend_pair<D, NCG, false>(buf[u], q_lds, ql, nullptr, nullptr, quad, c, o, m_run, l_lane);
         } else {
           int lim_a[NCG], lim_b[NCG];
 #pragma unroll
@@ -343,7 +356,7 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
             lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
             lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
           }
-          attend_pair<D, NCG, true>(buf[u], q_lds, lane, lim_a, lim_b, quad, c, o, m_run, l_lane);
+          attend_pair<D, NCG, true>(buf[u], q_lds, ql, lim_a, lim_b, quad, c, o, m_run, l_lane);
         }
       }
       issue(u, b + 2 * STAGES);
@@ -358,7 +371,7 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
     const int f = f0 + cg * 16 + (lane & 15);
     if (f >= cols) continue;
     const int64_t row = static_cast<int64_t>(sq.q0 + f / G) * a.n_q_heads + g * G + f % G;
-    if (n_parts == 1) {
+    if (n_parts == 1 && !a.force_partial) {
       const float inv = 1.f / l;
       uint16_t* orow = out + row * D;
 #pragma unroll
@@ -411,7 +424,7 @@ __global__ void __launch_bounds__(kPfMergeWaves * 64) merge_prefill_kernel(pf_ar
   if (sq.c <= 0 || r < sq.q0 || r >= sq.q0 + sq.c || sq.bad) return;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int f = (r - sq.q0) * G + head % G;
-  const int kend = pf_tile_keys(sq, G, f / a.cols_per_tile, a.cols_per_tile);
+  const int kend = pf_tile_keys(a, sq, G, f / a.cols_per_tile, a.cols_per_tile);
   const int P = a.part_blocks * 16;
   const int n_parts = (kend + P - 1) / P;
   if (n_parts <= 1) return;
@@ -488,7 +501,8 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
   p.scale = o.scale > 0.f ? o.scale : 1.f / std::sqrt(static_cast<float>(c.head_dim));
   const int64_t cols = static_cast<int64_t>(max_q_len) * G;
-  p.ncg = cols <= 16 ? 1 : 2;
+  // two column groups per wave hold 2 x D/4 accumulators: at d = 256 they no longer fit in registers
+  p.ncg = (cols <= 16 || c.head_dim >= 256) ? 1 : 2;
   p.tiles = static_cast<int>((cols + 16 * p.ncg - 1) / (16 * p.ncg));
   p.wt = p.tiles >= 4 ? 4 : (p.tiles >= 2 ? 2 : 1);
   p.tile_groups = (p.tiles + p.wt - 1) / p.wt;
@@ -535,7 +549,8 @@ hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st) {
 template <int D>
 hipError_t pf_launch_d(const pf_args& a, int ncg, int64_t grid, hipStream_t st) {
   if (ncg == 1) return pf_launch<D, 1>(a, grid, st);
-  if (ncg == 2) return pf_launch<D, 2>(a, grid, st);
+  if constexpr (D < 256)
+    if (ncg == 2) return pf_launch<D, 2>(a, grid, st);
   return hipErrorInvalidValue;
 }
 
@@ -549,6 +564,71 @@ hipError_t pf_merge(const pf_args& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// The prefix phase of the cascade decode (kernels.hip): the members of every
+// group are the query rows of one "sequence" whose keys are the group's shared
+// prefix (table row of the first member, prefix_ctx tokens); no causal mask;
+// every tile writes partials [row * Hq + head][max_parts] into ws.
+kv_status prefix_phase_plan(const kv_pool* pool, int n_groups, int n_rows, int max_group, int num_q_heads,
+                            int max_blocks, const kv_attention_options* opts, int* part_tokens, int* max_parts,
+                            uint64_t* bytes) {
+  pf_plan p;
+  if (kv_status s = pf_resolve(pool, n_groups, n_rows, max_group, num_q_heads, max_blocks, opts, p)) return s;
+  *part_tokens = p.partition;
+  *max_parts = p.max_parts;
+  const uint64_t rows = static_cast<uint64_t>(n_rows) * num_q_heads * p.max_parts;
+  *bytes = 2 * up256(rows * 4) + up256(rows * pool->cfg.head_dim * 4);
+  return KV_OK;
+}
+
+kv_status prefix_phase_launch(kv_pool* pool, int layer, const void* q, void* out, const int32_t* group_start,
+                              const int32_t* prefix_ctx, const int32_t* tables, int n_groups, int n_rows,
+                              int max_group, int max_blocks, int num_q_heads, const kv_attention_options* opts,
+                              void* ws, hipStream_t st) {
+  pf_plan p;
+  if (kv_status s = pf_resolve(pool, n_groups, n_rows, max_group, num_q_heads, max_blocks, opts, p)) return s;
+  const kv_pool_config& c = pool->cfg;
+  const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
+  const uint64_t rows = static_cast<uint64_t>(n_rows) * num_q_heads * p.max_parts;
+  char* w = static_cast<char*>(ws);
+  pf_args a{};
+  a.q = q;
+  a.out = out;
+  a.k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
+  a.v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
+  a.q_indptr = group_start;
+  a.ctx_lens = prefix_ctx;
+  a.tables = tables;
+  a.table_rows = group_start;
+  a.part_m = reinterpret_cast<float*>(w);
+  a.part_l = reinterpret_cast<float*>(w + up256(rows * 4));
+  a.part_o = reinterpret_cast<float*>(w + 2 * up256(rows * 4));
+  a.n_seqs = n_groups;
+  a.total_q = n_rows;
+  a.max_q_len = max_group;
+  a.max_blocks = max_blocks;
+  a.n_q_heads = num_q_heads;
+  a.n_kv_heads = c.num_kv_heads;
+  a.num_blocks = c.num_blocks;
+  a.part_blocks = p.partition / 16;
+  a.max_parts = p.max_parts;
+  a.wt = p.wt;
+  a.tile_groups = p.tile_groups;
+  a.part_groups = p.part_groups;
+  a.cols_per_tile = 16 * p.ncg;
+  a.scale_log2 = p.scale * kLog2e;
+  a.causal = 0;
+  a.force_partial = 1;
+  const int64_t grid = static_cast<int64_t>(n_groups) * c.num_kv_heads * p.tile_groups * p.part_groups;
+  hipError_t e;
+  switch (c.head_dim) {
+    case 64: e = pf_launch_d<64>(a, p.ncg, grid, st); break;
+    case 128: e = pf_launch_d<128>(a, p.ncg, grid, st); break;
+    default: e = pf_launch_d<256>(a, p.ncg, grid, st); break;
+  }
+  return hip_check(e, "cascade prefix launch");
+}
+
 }  // namespace pagedkv
 
 using namespace pagedkv;
@@ -613,6 +693,7 @@ kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, v
   a.part_groups = p.part_groups;
   a.cols_per_tile = 16 * p.ncg;
   a.scale_log2 = p.scale * kLog2e;
+  a.causal = 1;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * p.tile_groups * p.part_groups;
   hipError_t e;

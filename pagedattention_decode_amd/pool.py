@@ -101,6 +101,18 @@ class PagedKVPool:
         B.paged_attention_prefill(self.handle, layer, q, out, q_indptr, block_tables, context_lens, max_q_len,
                                   num_q_heads, opts, workspace, stream)
 
+    def shared_prefix_plan(self, seq_ids):
+        return B.kv_shared_prefix_plan(self.handle, seq_ids)
+
+    def cascade_workspace_bytes(self, n_seqs, n_groups, max_group, num_q_heads, max_blocks, opts=None):
+        return B.paged_attention_cascade_workspace_bytes(self.handle, n_seqs, n_groups, max_group, num_q_heads,
+                                                         max_blocks, opts)
+
+    def decode_cascade(self, layer, q, out, block_tables, context_lens, num_q_heads, group_start, shared_blocks,
+                       max_group, opts=None, workspace=None, stream=None):
+        B.paged_attention_decode_cascade(self.handle, layer, q, out, block_tables, context_lens, num_q_heads,
+                                         group_start, shared_blocks, max_group, opts, workspace, stream)
+
     # -- prefix cache --------------------------------------------------------
     def prefix_match(self, tokens):
         return B.kv_prefix_match(self.handle, tokens)

@@ -224,6 +224,31 @@ class GpuRun:
         return bits_to_float_tensor(out, wl.dtype)
 
 
+    def decode_cascade(self, decode_index, layer, opts=None, plan=None, max_group=None, tables=None, lens=None):
+        """The recorded decode's queries through paged_attention_decode_cascade, with the
+        library's own shared-prefix plan unless one is given."""
+        wl = self.wl
+        rec = self.decodes[decode_index]
+        tables = rec["tables"] if tables is None else tables
+        lens = rec["lengths"] if lens is None else lens
+        n = len(rec["seq_ids"])
+        gs, sb = self.pool.shared_prefix_plan(rec["seq_ids"]) if plan is None else plan
+        max_group = int(np.diff(gs).max()) if max_group is None else max_group
+        q = to_device_bits(self.query_bits(decode_index, layer, n))
+        out = torch.empty_like(q)
+        out.view(torch.uint8).fill_(0xFF)
+        opts = opts if opts is not None else self.opts
+        d_tables = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).cuda()
+        d_lens = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
+        d_gs = torch.from_numpy(np.ascontiguousarray(gs, dtype=np.int32)).cuda()
+        d_sb = torch.from_numpy(np.ascontiguousarray(sb, dtype=np.int32)).cuda()
+        ws_bytes = self.pool.cascade_workspace_bytes(n, len(sb), max_group, wl.num_q_heads, d_tables.shape[1], opts)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF)
+        self.pool.decode_cascade(layer, q, out, d_tables, d_lens, wl.num_q_heads, d_gs, d_sb, max_group, opts, ws)
+        return bits_to_float_tensor(out, wl.dtype)
+
+
 def run_workload_on_gpu(wl, **kw):
     return GpuRun(wl, **kw).run()
 

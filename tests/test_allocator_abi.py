@@ -267,3 +267,77 @@ def test_quantised_pool_sizes_and_shape_limits():
             with pytest.raises(B.KVError) as e:
                 B.kv_pool_required_bytes(bad)
             assert e.value.status == B.KV_ERR_UNSUPPORTED
+
+
+# -- groups for the read-once decode over shared prefixes ----------------------
+
+def brute_plan(tables, lengths, B_):
+    """Maximal runs of consecutive sequences sharing >= 1 completely filled leading block
+    with the run's first member; shared = the fewest such blocks over the run's members."""
+    def common(a, b):
+        lim = min(lengths[a], lengths[b]) // B_
+        j = 0
+        while j < lim and tables[a][j] == tables[b][j]:
+            j += 1
+        return j
+    gs, sb, i, n = [], [], 0, len(tables)
+    while i < n:
+        k, shared = i + 1, None
+        while k < n and common(i, k) >= 1:
+            shared = common(i, k) if shared is None else min(shared, common(i, k))
+            k += 1
+        gs.append(i)
+        sb.append(shared or 0)
+        i = k
+    return gs + [n], sb
+
+
+def plan_of(pool, seqs):
+    tables, lens = pool.tables(seqs, max(1, max(pool.info(s)[1] for s in seqs)))
+    return [list(t) for t in tables], [int(x) for x in lens]
+
+
+def test_shared_prefix_plan_on_workloads():
+    wl = workloads.shared_prefix()
+    pool = host_pool(wl, draws.free_order(wl.seed, wl.num_blocks))
+    seqs = None
+    for op in wl.ops:
+        if op[0] == "add":
+            pool.add(op[1])
+        elif op[0] == "fork":
+            pool.fork(op[1], op[2])
+        elif op[0] == "append":
+            pool.append(op[1], op[2])
+        elif op[0] == "decode":
+            seqs = list(op[1])
+    gs, sb = pool.shared_prefix_plan(seqs)
+    assert list(gs) == [0, 16] and list(sb) == [384]
+    # the members in another order are still one run
+    gs, sb = pool.shared_prefix_plan(seqs[:5] + [seqs[-1]] + seqs[5:-1])
+    assert list(gs) == [0, 16] and list(sb) == [384]
+    tables, lens = plan_of(pool, seqs)
+    assert brute_plan(tables, lens, 16) == ([0, 16], [384])
+
+
+def test_shared_prefix_plan_random_forks():
+    rng = np.random.default_rng(7)
+    for trial in range(30):
+        pool = host_pool((1, 400, 4, 1, 32, "f32"))
+        live, nxt = [], 0
+        for _ in range(int(rng.integers(1, 12))):
+            if live and rng.random() < 0.5:
+                src = int(rng.choice(live))
+                pool.fork(src, nxt)
+            else:
+                pool.add(nxt)
+            live.append(nxt)
+            nxt += 1
+            counts = [int(rng.integers(0, 9)) for _ in live]
+            pool.append(live, counts)
+        order = list(rng.permutation(live)) if trial % 2 else sorted(live, key=lambda s: pool.info(s)[1])
+        gs, sb = pool.shared_prefix_plan(order)
+        tables, lens = plan_of(pool, order)
+        assert (list(gs), list(sb)) == brute_plan(tables, lens, 4), trial
+    assert list(pool.shared_prefix_plan([])[0]) == [0]
+    with pytest.raises(B.KVError):
+        pool.shared_prefix_plan([10 ** 6])
