@@ -20,14 +20,20 @@ Sources.  Citations name the pages by title:
 Modules:
 
 * :mod:`oracle.footprint`     closed forms: per-token footprint, block bytes,
-                               tail waste ([KVM] Eq. 1, block-size trade-off;
-                               [BT] §01, §04; [INF] §8.1.2, §8.3.1).
+                               tail waste, reload and recompute times
+                               ([KVM] Eq. 1, block-size trade-off,
+                               evict-versus-swap analysis; [BT] §01, §04;
+                               [INF] §8.1.2, §8.3.1).
 * :mod:`oracle.block_manager` the host block manager: FIFO free list,
                                refcounts, tables, append with copy-on-write,
-                               fork, release ([BT] §03-§05, §08, §10, §13;
-                               [KVM] paged KV allocation, CoW branching).
+                               fork, release, and the host tier: swap of a
+                               sequence's own blocks to pinned host frames and
+                               back ([BT] §03-§05, §08, §10, §13; [KVM] paged
+                               KV allocation, CoW branching, asynchronous
+                               paged swap).
 * :mod:`oracle.kv_store`      the logical K/V pool ``[layer][block][slot][head][dim]``
-                               ([BT] §06) with slot scatter and block copy.
+                               ([BT] §06) with slot scatter, block copy and
+                               block copies to host frames and back.
 * :mod:`oracle.attention`     gathered softmax(q K^T / sqrt(d)) V in float64
                                ([BT] §07) and the split-K merge recurrences
                                ([KVM] chunked prefill mechanism).
@@ -49,7 +55,7 @@ Modules:
 * :mod:`oracle.runner`        replays a :mod:`synth` workload through the above.
 
 Every function is pinned by ``tests/test_oracle_pins.py``,
-``tests/test_prefill_pins.py``, ``tests/test_quant_pins.py`` and
-``tests/test_prefix_cache.py`` against values the
+``tests/test_prefill_pins.py``, ``tests/test_quant_pins.py``,
+``tests/test_prefix_cache.py`` and ``tests/test_swap_pins.py`` against values the
 pages print, closed forms, invariants and brute force.  Parity unpinned: none.
 """

@@ -27,11 +27,27 @@ Operations:
   return to the back of the free list in table order ([KVM] host-side
   reference-counted reclamation; [BT] §05).
 
+* host tier ([KVM] asynchronous paged swap, Figure 11 and the three
+  migration steps): ``attach_host`` gives the manager a pool of pinned host
+  frames with its own free list; ``swap_out`` moves a sequence's blocks to host
+  frames (the frames are taken, the data is copied, the table entries are
+  re-tagged as host-resident with their frame index, the device blocks go back
+  to the free list); ``swap_in`` takes fresh device blocks for the host entries
+  and gives the frames back.  The table is the pages' extended block table:
+  every entry carries its residency, ``("hbm", block)`` or ``("host", frame)``.
+
 Readings where the pages are open: FIFO discipline (the runnable teaching code
 of [BT] §05 is FIFO; [KVM] also says ring buffer or stack/FIFO); within a batch,
 sequences are served in the order given and each sequence's tokens
 consecutively; the copy covers the whole block (the contents beyond the
-sequence's length are never read).
+sequence's length are never read).  For the host tier: only the blocks the
+sequence holds alone (reference count 1) move, in table order; a block it
+shares with a fork or the prefix cache stays in HBM with the sequence's
+reference, since the other holders still read it; frames come from the front
+of a FIFO host free list and go back to its back; swap_in takes device blocks
+from the front of the free list in table order, all or nothing, like an
+append; a swapped-out sequence (one with a host entry) can be released but
+not appended to, forked or read until it is swapped back in.
 """
 
 from __future__ import annotations
@@ -54,6 +70,9 @@ class BlockManager:
         self.held = [0] * num_blocks  # references held outside the tables (a prefix cache)
         self.tables: dict = {}
         self.lengths: dict = {}
+        self.host_free = None   # FIFO of free host frames once a host tier is attached
+        self.n_frames = 0
+        self.frames: dict = {}  # seq -> {logical block j: host frame} of its host-resident entries
 
     # -- sequences -------------------------------------------------------
     def add(self, seq) -> None:
@@ -67,23 +86,97 @@ class BlockManager:
             raise ValueError(f"unknown parent {parent}")
         if child in self.tables:
             raise ValueError(f"sequence {child} already exists")
+        self._resident(parent)
         self.tables[child] = list(self.tables[parent])
         for p in self.tables[child]:
             self.ref[p] += 1
         self.lengths[child] = self.lengths[parent]
 
     def release(self, seq) -> list:
-        """Drop the sequence; return the blocks that went back to the free list."""
+        """Drop the sequence; return the blocks that went back to the free list.  Frames of
+        host-resident entries go back to the host free list, in table order."""
         if seq not in self.tables:
             raise ValueError(f"unknown sequence {seq}")
         freed = []
-        for p in self.tables.pop(seq):
+        host = self.frames.pop(seq, {})
+        for j, p in enumerate(self.tables.pop(seq)):
+            if j in host:
+                self.host_free.append(host[j])
+                continue
             self.ref[p] -= 1
             if self.ref[p] == 0:
                 self.free.append(p)
                 freed.append(p)
         del self.lengths[seq]
         return freed
+
+    # -- host tier ---------------------------------------------------------
+    def attach_host(self, n_frames: int, free_order=None) -> None:
+        if self.host_free is not None:
+            raise ValueError("a host tier is already attached")
+        if n_frames <= 0:
+            raise ValueError("n_frames must be positive")
+        order = list(range(n_frames)) if free_order is None else [int(f) for f in free_order]
+        if sorted(order) != list(range(n_frames)):
+            raise ValueError("free_order must be a permutation of the frame ids")
+        self.host_free = deque(order)
+        self.n_frames = int(n_frames)
+
+    def swapped(self, seq) -> bool:
+        return bool(self.frames.get(seq))
+
+    def _resident(self, seq) -> None:
+        if seq not in self.tables:
+            raise ValueError(f"unknown sequence {seq}")
+        if self.swapped(seq):
+            raise ValueError(f"sequence {seq} is swapped out")
+
+    def swap_out(self, seq) -> list:
+        """Move the blocks only ``seq`` holds to host frames.  Returns the (block, frame)
+        copies in table order; the blocks go to the back of the free list.  All or
+        nothing: MemoryError when the host free list is too short."""
+        if self.host_free is None:
+            raise ValueError("no host tier attached")
+        self._resident(seq)
+        table = self.tables[seq]
+        moved = [j for j, p in enumerate(table) if self.ref[p] == 1]
+        if len(moved) > len(self.host_free):
+            raise MemoryError("no free host frame")
+        pairs, host = [], {}
+        for j in moved:
+            p, f = table[j], self.host_free.popleft()
+            pairs.append((p, f))
+            host[j] = f
+            self.ref[p] = 0
+            self.free.append(p)
+            table[j] = None
+        if host:
+            self.frames[seq] = host
+        return pairs
+
+    def swap_in(self, seq) -> list:
+        """Give every host-resident entry of ``seq`` a fresh device block.  Returns the
+        (frame, block) copies in table order; the frames go to the back of the host free
+        list.  All or nothing: MemoryError when the free list is too short."""
+        if seq not in self.tables:
+            raise ValueError(f"unknown sequence {seq}")
+        host = self.frames.get(seq, {})
+        if len(host) > len(self.free):
+            raise MemoryError("no free KV block")
+        pairs = []
+        table = self.tables[seq]
+        for j in sorted(host):
+            p = self._pop_free()
+            table[j] = p
+            pairs.append((host[j], p))
+            self.host_free.append(host[j])
+        self.frames.pop(seq, None)
+        return pairs
+
+    def residency(self, seq) -> list:
+        """The extended block table of ``seq``: ("hbm", block) or ("host", frame) per entry."""
+        host = self.frames.get(seq, {})
+        return [("host", host[j]) if j in host else ("hbm", p) for j, p in enumerate(self.tables[seq])]
 
     def add_with_blocks(self, seq, blocks) -> None:
         """Register a sequence whose table starts with ``blocks`` (full blocks it shares):
@@ -147,8 +240,7 @@ class BlockManager:
         if len(counts) != len(seq_ids):
             raise ValueError("seq_ids and counts differ in length")
         for s, c in zip(seq_ids, counts):
-            if s not in self.tables:
-                raise ValueError(f"unknown sequence {s}")
+            self._resident(s)
             if c < 0:
                 raise ValueError("negative token count")
         saved = (copy.copy(self.free), list(self.ref),
@@ -165,6 +257,7 @@ class BlockManager:
 
     # -- queries -------------------------------------------------------------
     def table(self, seq) -> list:
+        self._resident(seq)
         return list(self.tables[seq])
 
     def length(self, seq) -> int:
@@ -187,11 +280,24 @@ class BlockManager:
         exactly ceil(len / B) entries.
         """
         counted = [0] * self.num_blocks
+        used_frames = []
         for seq, t in self.tables.items():
             if len(t) != -(-self.lengths[seq] // self.block_size):
                 raise AssertionError(f"table of {seq} has {len(t)} entries for length {self.lengths[seq]}")
-            for p in t:
-                counted[p] += 1
+            host = self.frames.get(seq, {})
+            for j, p in enumerate(t):
+                if j in host:
+                    if p is not None:
+                        raise AssertionError(f"entry {j} of {seq} is in both tiers")
+                    used_frames.append(host[j])
+                else:
+                    counted[p] += 1
+        if self.host_free is not None:
+            frames = list(self.host_free) + used_frames
+            if sorted(frames) != list(range(self.n_frames)):
+                raise AssertionError("host frames: free + used != all frames, or a frame is used twice")
+        elif used_frames:
+            raise AssertionError("host entries without a host tier")
         counted = [c + h for c, h in zip(counted, self.held)]
         if counted != self.ref:
             raise AssertionError("reference counts disagree with the tables and outside holders")

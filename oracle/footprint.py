@@ -49,3 +49,20 @@ def translate(position: int, block_size: int, table) -> tuple:
     """Logical position t -> (physical block, slot) = (table[t // B], t mod B). [BT] §03."""
     j, r = divmod(position, block_size)
     return table[j], r
+
+
+def reload_seconds(num_tokens: int, bytes_per_token: int, link_bytes_per_s: float) -> float:
+    """Time to stream a sequence's KV state over the host link: S * m_token / B_link.
+
+    [KVM] evict-versus-swap analysis, T_reload; a round trip (out and back) takes twice this.
+    """
+    return num_tokens * bytes_per_token / link_bytes_per_s
+
+
+def recompute_seconds(n_params: float, num_tokens: int, flops_per_s: float) -> float:
+    """Time to rebuild the state by a prefill pass, linear term only: 2 P S / R_prefill.
+
+    [KVM] evict-versus-swap analysis, T_recomp (the 4 L S^2 d_model attention term is
+    dropped there for contexts up to about 32K tokens; so here).
+    """
+    return 2 * n_params * num_tokens / flops_per_s

@@ -13,6 +13,9 @@ by default), so large pools cost only what is written.
               ([KVM] CoW branching: the shared block's B tokens are copied).
 * ``gather``  returns the first ``n`` token rows of a sequence by walking its
               block table ([BT] §06: block_table[seq, t // B], then t % B).
+* ``to_host`` / ``from_host`` copy whole blocks (every layer) to host frames and
+              back ([KVM] asynchronous paged swap: a block's bytes move
+              unchanged between the tiers).
 """
 
 from __future__ import annotations
@@ -73,6 +76,29 @@ class KVStore:
     def block(self, which, layer, block) -> np.ndarray:
         store = self.k if which == "k" else self.v
         return self._block(store, which, layer, block, False)
+
+    def to_host(self, pairs) -> None:
+        """(block, frame) pairs: frame := block, in every tracked layer."""
+        if not hasattr(self, "host_k"):
+            self.host_k, self.host_v = {}, {}
+        for layer in range(self.num_layers):
+            if not self._tracked(layer):
+                continue
+            for block, frame in pairs:
+                self.host_k[(layer, frame)] = self._block(self.k, "k", layer, block, False).copy()
+                self.host_v[(layer, frame)] = self._block(self.v, "v", layer, block, False).copy()
+
+    def from_host(self, pairs) -> None:
+        """(frame, block) pairs: block := frame, in every tracked layer."""
+        for layer in range(self.num_layers):
+            if not self._tracked(layer):
+                continue
+            for frame, block in pairs:
+                self.k[(layer, block)] = self.host_k[(layer, frame)].copy()
+                self.v[(layer, block)] = self.host_v[(layer, frame)].copy()
+
+    def host_block(self, which, layer, frame) -> np.ndarray:
+        return (self.host_k if which == "k" else self.host_v)[(layer, frame)]
 
     def gather(self, layer, table, n):
         """K and V rows [n, Hkv, d] of a sequence of length n with block table ``table``."""

@@ -178,6 +178,31 @@ class QuantKVStore:
         """(codes [B, Hkv, d] int8, scales [B, Hkv, d / 32] half bits) of one block."""
         return self._block(self.k if which == "k" else self.v, layer, block, False)
 
+    def to_host(self, pairs) -> None:
+        """(block, frame) pairs: frame := block (codes and scales), every tracked layer."""
+        if not hasattr(self, "host_k"):
+            self.host_k, self.host_v = {}, {}
+        for layer in range(self.num_layers):
+            if not self._tracked(layer):
+                continue
+            for block, frame in pairs:
+                for store, host in ((self.k, self.host_k), (self.v, self.host_v)):
+                    c, s = self._block(store, layer, block, False)
+                    host[(layer, frame)] = (c.copy(), s.copy())
+
+    def from_host(self, pairs) -> None:
+        """(frame, block) pairs: block := frame, every tracked layer."""
+        for layer in range(self.num_layers):
+            if not self._tracked(layer):
+                continue
+            for frame, block in pairs:
+                for store, host in ((self.k, self.host_k), (self.v, self.host_v)):
+                    c, s = host[(layer, frame)]
+                    store[(layer, block)] = (c.copy(), s.copy())
+
+    def host_block(self, which, layer, frame):
+        return (self.host_k if which == "k" else self.host_v)[(layer, frame)]
+
     def gather_f64(self, layer, table, n):
         """Dequantised K and V rows [n, Hkv, d] float64 of a sequence of length n."""
         k = np.empty((n, self.num_kv_heads, self.head_dim))

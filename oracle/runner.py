@@ -42,6 +42,7 @@ class OracleReplay:
         self.appends = []  # (seq_ids, counts, slots, pairs)
         self.decodes = []  # {"seq_ids", "tables", "lengths"}
         self.prefills = []  # {"seq_ids", "counts", "tables", "lengths"} (lengths after the chunk)
+        self.swaps = []  # ("out", seq, [(block, frame)]) or ("in", seq, [(frame, block)])
 
     def run(self, ops=None):
         for op in (self.wl.ops if ops is None else ops):
@@ -69,6 +70,16 @@ class OracleReplay:
             self.bm.fork(op[1], op[2])
         elif kind == "release":
             self.bm.release(op[1])
+        elif kind == "host":
+            self.bm.attach_host(op[1], draws.host_free_order(self.wl.seed, op[1]))
+        elif kind == "swap_out":
+            pairs = self.bm.swap_out(op[1])
+            self.store.to_host(pairs)
+            self.swaps.append(("out", op[1], pairs))
+        elif kind == "swap_in":
+            pairs = self.bm.swap_in(op[1])
+            self.store.from_host(pairs)
+            self.swaps.append(("in", op[1], pairs))
         elif kind in ("append", "prefill"):
             seq_ids, counts = list(op[1]), list(op[2])
             running = {}

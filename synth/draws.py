@@ -86,3 +86,8 @@ def token_rows(seed: int, tag: int, layer: int, writer: int, positions: np.ndarr
 def free_order(seed: int, num_blocks: int) -> np.ndarray:
     """Initial free-list order: a seeded permutation of the block ids."""
     return np.random.default_rng(int(seed) + 1000).permutation(num_blocks).astype(np.int32)
+
+
+def host_free_order(seed: int, num_frames: int) -> np.ndarray:
+    """Initial order of the host frame free list: a seeded permutation of the frame ids."""
+    return np.random.default_rng(int(seed) + 2000).permutation(num_frames).astype(np.int32)

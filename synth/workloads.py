@@ -202,6 +202,36 @@ def verify_drafts(positions=8) -> Workload:
                     description=f"bf16 Hq=32 Hkv=8 d=128 B=16, 16 x ({8192 - positions} cached + {positions} drafts)")
 
 
+def tool_pause(layers: int = 2, seed: int = 8) -> Workload:
+    """Trajectories paused for a tool call are swapped to host frames and back.
+
+    Eight sequences of mixed lengths (two of them forks of a third, so some of
+    their blocks are shared and stay in HBM); sequences 0 and 3 are swapped out,
+    the others keep decoding and reuse the freed blocks, then 0 and 3 are
+    swapped back in (into other blocks) and everyone decodes.  Hq=32, Hkv=8,
+    d=128, B=16, bf16.
+    """
+    lens = (2304, 37, 16, 1000, 513, 0, 64, 300)
+    seqs = tuple(range(len(lens)))
+    ops = [("host", 256)]
+    ops += [("add", s) for s in seqs if s not in (6, 7)]
+    ops.append(("append", tuple(s for s in seqs if s not in (6, 7)), tuple(lens[s] for s in seqs if s not in (6, 7))))
+    ops += [("fork", 3, 6), ("fork", 3, 7)]
+    ops.append(("append", (6, 7), (64 - 0, 300 - 0)))
+    ops.append(("decode", seqs))
+    ops += [("swap_out", 0), ("swap_out", 3)]
+    others = tuple(s for s in seqs if s not in (0, 3))
+    for _ in range(3):
+        ops.append(("append", others, tuple(40 for _ in others)))
+        ops.append(("decode", others))
+    ops += [("swap_in", 3), ("swap_in", 0)]
+    ops.append(("append", seqs, tuple(1 for _ in seqs)))
+    ops.append(("decode", seqs))
+    blocks = sum(-(-(n + 130) // 16) for n in lens) + 100
+    return Workload("tool_pause_8", seed, BF16, layers, 32, 8, 128, 16, blocks, ops,
+                    description="bf16 Hq=32 Hkv=8 d=128 B=16, 8 sequences, 2 swapped out and back in")
+
+
 CONFIGS = {
     1: tiny_fp32,
     2: qwen_independent,
