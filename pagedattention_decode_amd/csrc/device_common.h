@@ -106,8 +106,8 @@ template <int D, int FMT>
 struct kv_qregs {
   uint32_t kc[D * fmt_bits<FMT>() / 128];  // K codes
   uint32_t vc[D * fmt_bits<FMT>() / 128];  // V codes
-  uint32_t ks[D / 64];                     // K scales of the lane's token, one half per group
-  uint32_t vs[D / 16];                     // V scales of the lane's 4 tokens ([token][group])
+  uint32_t ks[D / 16];                     // K scales of the lane's 4 score tokens ([token][group])
+  uint32_t vs[D / 16];                     // V scales of the same 4 tokens ([token][group])
 };
 
 template <int N>
@@ -142,7 +142,7 @@ __device__ __forceinline__ void load_qblock(kv_qregs<D, FMT>& r, const unsigned 
   constexpr int codes = q_code_bytes<D, FMT>();
   load_dwords(r.kc, kt + lane * lane_bytes);
   load_dwords(r.vc, vt + lane * lane_bytes);
-  load_dwords(r.ks, kt + codes + (lane & 15) * (D / 32) * 2);
+  load_dwords(r.ks, kt + codes + (lane >> 4) * 4 * (D / 32) * 2);
   load_dwords(r.vs, vt + codes + (lane >> 4) * 4 * (D / 32) * 2);
 }
 
@@ -163,22 +163,30 @@ __device__ __forceinline__ void bytes_to_f32(uint32_t w, float s, float bias_s, 
   for (int k = 0; k < 4; ++k) out[k] = __builtin_fmaf(ubyte_f32(w, k), s, bias_s);
 }
 
-// Dequantises a raw block into the bf16 operand tile of the decode kernel
-// (value = code * scale, exact in float32, then rounded to nearest-even bf16).
+// Scale of token i (of the lane's 4) and group g, from a [token][group] list of halves.
+template <int D>
+__device__ __forceinline__ float scale_at(const uint32_t* w, int i, int g) {
+  const int h = i * (D / 32) + g;
+  return (h & 1) ? half_hi(w[h >> 1]) : half_lo(w[h >> 1]);
+}
+
+// The codes of a raw block as the bf16 operand tiles of the decode kernel.
+// Codes are integers of at most 8 bits, exact in bf16; the scales are applied
+// in float32 by the attention step (to the scores for K, to the weights for V).
 template <int D, int FMT>
-__device__ __forceinline__ void dequant_block(const kv_qregs<D, FMT>& r, kv_regs<D>& out) {
+__device__ __forceinline__ void codes_block(const kv_qregs<D, FMT>& r, kv_regs<D>& out) {
+  constexpr float bias = FMT == kFmtQ8 ? -128.f : -8.f;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
-    const float s = (kk & 1) ? half_hi(r.ks[kk >> 1]) : half_lo(r.ks[kk >> 1]);
     float v[8];
     if constexpr (FMT == kFmtQ8) {
       // two's-complement bytes, flipped to code + 128
-      bytes_to_f32(r.kc[2 * kk] ^ 0x80808080u, s, -128.f * s, v);
-      bytes_to_f32(r.kc[2 * kk + 1] ^ 0x80808080u, s, -128.f * s, v + 4);
+      bytes_to_f32(r.kc[2 * kk] ^ 0x80808080u, 1.f, bias, v);
+      bytes_to_f32(r.kc[2 * kk + 1] ^ 0x80808080u, 1.f, bias, v + 4);
     } else {
       float lo[4], hi[4];
-      bytes_to_f32(r.kc[kk] & 0x0f0f0f0fu, s, -8.f * s, lo);         // j = 0, 2, 4, 6
-      bytes_to_f32((r.kc[kk] >> 4) & 0x0f0f0f0fu, s, -8.f * s, hi);  // j = 1, 3, 5, 7
+      bytes_to_f32(r.kc[kk] & 0x0f0f0f0fu, 1.f, bias, lo);         // j = 0, 2, 4, 6
+      bytes_to_f32((r.kc[kk] >> 4) & 0x0f0f0f0fu, 1.f, bias, hi);  // j = 1, 3, 5, 7
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v[2 * i] = lo[i];
@@ -192,28 +200,15 @@ __device__ __forceinline__ void dequant_block(const kv_qregs<D, FMT>& r, kv_regs
   uint32_t half_words[D / 16][2];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    const int g = t >> 1;  // group of dims 32 g .. 32 g + 31
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w = r.vs[(i * (D / 32) + g) >> 1];
-      s[i] = ((i * (D / 32) + g) & 1) ? half_hi(w) : half_lo(w);
-    }
     uint32_t bytes;
-    float bias;
-    if constexpr (FMT == kFmtQ8) {
+    if constexpr (FMT == kFmtQ8)
       bytes = r.vc[t] ^ 0x80808080u;
-      bias = -128.f;
-    } else {
+    else
       bytes = (t & 1) ? (r.vc[t >> 1] >> 4) & 0x0f0f0f0fu : r.vc[t >> 1] & 0x0f0f0f0fu;
-      bias = -8.f;
-    }
-    const float v0 = __builtin_fmaf(ubyte_f32(bytes, 0), s[0], bias * s[0]);
-    const float v1 = __builtin_fmaf(ubyte_f32(bytes, 1), s[1], bias * s[1]);
-    const float v2 = __builtin_fmaf(ubyte_f32(bytes, 2), s[2], bias * s[2]);
-    const float v3 = __builtin_fmaf(ubyte_f32(bytes, 3), s[3], bias * s[3]);
-    half_words[t][0] = pack_bf16x2(v0, v1);
-    half_words[t][1] = pack_bf16x2(v2, v3);
+    float v[4];
+    bytes_to_f32(bytes, 1.f, bias, v);
+    half_words[t][0] = pack_bf16x2(v[0], v[1]);
+    half_words[t][1] = pack_bf16x2(v[2], v[3]);
   }
 #pragma unroll
   for (int pp = 0; pp < D / 32; ++pp)

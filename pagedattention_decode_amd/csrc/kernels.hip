@@ -462,16 +462,13 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
 
 // One 16-token block: scores, online-softmax update, weighted sum of values.
 // `valid` (wave uniform) is the number of in-range slots of the block.
+// Online-softmax step on the 4 scores s of the lane's tokens quad*4 + i:
+// masks the slots past `valid`, raises the running maximum when a score
+// exceeds it by more than the slack (rescaling l and O), and returns the
+// weights 2^(s * scale_log2 - m_run) (0 for masked slots).
 template <int D>
-__device__ __forceinline__ void attend_block(kv_regs<D>& cur, const bf16x8_t* qop, int valid, int quad,
-                                             float scale_log2, f32x4_t* o, float& m_run, float& l_lane) {
-  // S^T = K . Q^T
-  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk], s, 0, 0, 0);
-
-  // online softmax; the lane holds tokens quad*4 + i of its head
+__device__ __forceinline__ void softmax_step(const f32x4_t& s, int valid, int quad, float scale_log2, f32x4_t* o,
+                                             float& m_run, float& l_lane, float (&pv)[4]) {
   float sv[4];
   float mb = -INFINITY;
 #pragma unroll
@@ -490,9 +487,21 @@ __device__ __forceinline__ void attend_block(kv_regs<D>& cur, const bf16x8_t* qo
     for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
     m_run = m_new;
   }
-  float pv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pv[i] = (sv[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_run);
+}
+
+template <int D>
+__device__ __forceinline__ void attend_block(kv_regs<D>& cur, const bf16x8_t* qop, int valid, int quad,
+                                             float scale_log2, f32x4_t* o, float& m_run, float& l_lane) {
+  // S^T = K . Q^T
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk], s, 0, 0, 0);
+
+  float pv[4];
+  softmax_step<D>(s, valid, quad, scale_log2, o, m_run, l_lane, pv);
   // P^T operand in bf16 (round to nearest even); the denominator sums the
   // rounded weights so that the weights applied to V are exactly normalised
   const bf16x2_t p01 = __builtin_convertvector((f32x2_t{pv[0], pv[1]}), bf16x2_t);
@@ -509,6 +518,43 @@ __device__ __forceinline__ void attend_block(kv_regs<D>& cur, const bf16x8_t* qo
   // O^T += V^T . P^T
 #pragma unroll
   for (int pp = 0; pp < D / 32; ++pp) {
+    const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
+    o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop, o[2 * pp],
+                                                          0, 0, 0);
+    o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[1]), pop,
+                                                              o[2 * pp + 1], 0, 0, 0);
+  }
+}
+
+// The same step on a quantised block, with the codes (exact in bf16) as the
+// operands and the group scales applied in float32:
+//   score(r) = sum_g sK(r, g) * (codes_K(r, group g) . q(group g)),
+//   O      += sum_r  p(r) * sV(r, g) * codes_V(r, dims of group g),
+// so the only rounding beyond float32 is that of the weight p * sV to bf16
+// (the unquantised path rounds p alone).  l sums the unrounded weights.
+template <int D, int FMT>
+__device__ __forceinline__ void attend_qblock(const kv_regs<D>& cur, const kv_qregs<D, FMT>& raw,
+                                              const bf16x8_t* qop, int valid, int quad, float scale_log2,
+                                              f32x4_t* o, float& m_run, float& l_lane) {
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {  // one group of 32 dims per instruction
+    const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk],
+                                                               f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(scale_at<D>(raw.ks, i, kk), t[i], s[i]);
+  }
+  float pv[4];
+  softmax_step<D>(s, valid, quad, scale_log2, o, m_run, l_lane, pv);
+  l_lane += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+  // O^T += V^T . (P * sV)^T, one weight operand per group; masked slots get
+  // weight 0 by selection (their scales and codes may be anything)
+#pragma unroll
+  for (int pp = 0; pp < D / 32; ++pp) {
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pv[i] == 0.f ? 0.f : pv[i] * scale_at<D>(raw.vs, i, pp);
+    const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])));
     const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
     o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop, o[2 * pp],
                                                           0, 0, 0);
@@ -811,8 +857,8 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
           attend_block<D>(buf[u], qop, valid, quad, a.scale_log2, o, m_run, l_lane);
         } else {
           kv_regs<D> tile;
-          dequant_block<D, FMT>(buf[u], tile);
-          attend_block<D>(tile, qop, valid, quad, a.scale_log2, o, m_run, l_lane);
+          codes_block<D, FMT>(buf[u], tile);
+          attend_qblock<D, FMT>(tile, buf[u], qop, valid, quad, a.scale_log2, o, m_run, l_lane);
         }
         if (cs.j == cs.nb - 1 || k == n_blk - 1) {  // end of this unit's run
           finish();
