@@ -189,10 +189,92 @@ kv_status kv_pool_refcounts(const kv_pool* pool, int32_t* out);
 
 /* Conservation ([BT] §13): N_free + N_allocated + N_pending = N_total, the set
  * of blocks with ref > 0 is exactly the set named by tables and the prefix
- * cache, each count equals the number of table entries naming the block plus
- * the prefix cache's reference, and every table has ceil(len / B) entries.
- * KV_ERR_STATE names the first violation. */
+ * cache, each count equals the number of HBM-resident table entries naming the
+ * block plus the prefix cache's reference, and every table has ceil(len / B)
+ * entries; with a host tier, free + pending + host-resident frames are every
+ * frame exactly once.  KV_ERR_STATE names the first violation. */
 kv_status kv_pool_check(const kv_pool* pool);
+
+/* ------------------------------------------------------------------------
+ * Host tier: swap of a sequence's blocks to pinned host memory and back
+ * ([KVM] asynchronous paged swap, Figure 11: frames of a pre-allocated pinned
+ * host pool, the copy on a dedicated stream, the block table remapped with a
+ * residency tag per entry, the device frames reused once the copy is done).
+ *
+ * A host frame holds one block of every layer: for l = 0 .. L-1, the block's
+ * K tiles of all Hkv heads (Hkv tile bytes, as laid out in the pool), then its
+ * V tiles; kv_host_frame_bytes = 2 L Hkv tile bytes = B times the per-token
+ * footprint ([KVM] Eq. 1) for an unquantised pool.  Frame f starts at
+ * host_frames + f * kv_host_frame_bytes.
+ *
+ * Only entries whose block the sequence holds alone (reference count 1) move;
+ * a block shared with a fork or held by the prefix cache stays in HBM, still
+ * referenced.  A sequence with a host-resident entry is "swapped out": it can
+ * be released or swapped in, and kv_seq_info / kv_seq_residency answer for it;
+ * append, fork, kv_get_block_tables, kv_shared_prefix_plan and
+ * kv_prefix_insert refuse it (KV_ERR_INVALID).
+ * ---------------------------------------------------------------------- */
+
+typedef enum { KV_TIER_HBM = 0, KV_TIER_HOST = 1 } kv_tier;
+
+/* Bytes of one host frame (0 for a NULL pool). */
+uint64_t kv_host_frame_bytes(const kv_pool* pool);
+
+/* Give the pool n_frames host frames at host_frames (caller-owned page-locked
+ * memory, n_frames * kv_host_frame_bytes bytes, from hipHostMalloc or an
+ * equivalent pinned allocation: pageable memory would stall the copies; NULL
+ * allows host bookkeeping only).  The host free list starts as
+ * initial_free_order (a permutation of 0..n_frames-1; NULL = 0, 1, ...) and is
+ * first-in first-out.  Once per pool. */
+kv_status kv_pool_attach_host(kv_pool* pool, void* host_frames, int32_t n_frames, const int32_t* initial_free_order);
+
+/* Swap out: for every entry of the sequence's table whose block it holds alone,
+ * in table order, take a frame from the front of the host free list, emit the
+ * pair (block, frame) into pairs_out[n][2] (capacity cap pairs; the table
+ * length always suffices), tag the entry as host-resident with that frame and
+ * drop the block's reference.  All or nothing: KV_ERR_OOM when the host free
+ * list is too short (nothing changes).  Enqueues on hip_stream the copies of
+ * the blocks to their frames (through d_staging, a device buffer of at least
+ * one frame, 16-byte aligned, used in chunks of whole frames); the blocks
+ * return to the back of the free list once that work has completed (an event
+ * polled like kv_seq_release's).  The caller orders hip_stream after the work
+ * that wrote the blocks.  *n_out = number of pairs (0: nothing moved). */
+kv_status kv_seq_swap_out(kv_pool* pool, int64_t seq_id, void* d_staging, uint64_t staging_bytes, void* hip_stream,
+                          int32_t* pairs_out, int32_t cap, int32_t* n_out);
+
+/* Swap in: for every host-resident entry, in table order, take a block from the
+ * front of the free list, emit (frame, block), set the entry to the block
+ * (reference 1).  All or nothing: KV_ERR_OOM when the free list is too short.
+ * Enqueues the copies frames -> blocks on hip_stream; the frames return to the
+ * back of the host free list once that work has completed.  Work that reads
+ * the sequence must be ordered after hip_stream. */
+kv_status kv_seq_swap_in(kv_pool* pool, int64_t seq_id, void* d_staging, uint64_t staging_bytes, void* hip_stream,
+                         int32_t* pairs_out, int32_t cap, int32_t* n_out);
+
+/* The same bookkeeping without device work: the blocks (out) or frames (in)
+ * wait for kv_pool_retire(pool, f >= fence) (fence 0: at once).  The caller
+ * moves the bytes with kv_swap_copy and retires the fence after it. */
+kv_status kv_seq_swap_out_fenced(kv_pool* pool, int64_t seq_id, uint64_t fence, int32_t* pairs_out, int32_t cap,
+                                 int32_t* n_out);
+kv_status kv_seq_swap_in_fenced(kv_pool* pool, int64_t seq_id, uint64_t fence, int32_t* pairs_out, int32_t cap,
+                                int32_t* n_out);
+
+/* Device side only: copy n pairs (host memory) on hip_stream; direction 0 =
+ * out, pairs (block, frame); direction 1 = in, pairs (frame, block).  Each
+ * chunk of whole frames is gathered by a kernel into d_staging and moved by
+ * one DMA copy per run of consecutive frames (out), or the reverse (in).
+ * KV_ERR_INVALID for a block or frame out of range. */
+kv_status kv_swap_copy(kv_pool* pool, const int32_t* pairs, int32_t n, int32_t direction, void* d_staging,
+                       uint64_t staging_bytes, void* hip_stream);
+
+/* The extended block table of a sequence: per entry, its tier (kv_tier) and
+ * its block (KV_TIER_HBM) or frame (KV_TIER_HOST); capacity cap entries,
+ * *n_out = table length. */
+kv_status kv_seq_residency(const kv_pool* pool, int64_t seq_id, int32_t cap, int32_t* tier_out, int32_t* index_out,
+                           int32_t* n_out);
+
+/* Host free list in pop order. */
+kv_status kv_host_free_list(const kv_pool* pool, int32_t cap, int32_t* out, int32_t* n_out);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* kv_last_error(void);

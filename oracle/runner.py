@@ -24,7 +24,7 @@ from .quant import QuantKVStore
 
 
 class OracleReplay:
-    def __init__(self, wl, free_order=None, layers=None, writers=None, background=None):
+    def __init__(self, wl, free_order=None, layers=None, writers=None, background=None, eager=False):
         self.wl = wl
         order = draws.free_order(wl.seed, wl.num_blocks) if free_order is None else free_order
         self.bm = BlockManager(wl.num_blocks, wl.block_size, order)
@@ -42,7 +42,11 @@ class OracleReplay:
         self.appends = []  # (seq_ids, counts, slots, pairs)
         self.decodes = []  # {"seq_ids", "tables", "lengths"}
         self.prefills = []  # {"seq_ids", "counts", "tables", "lengths"} (lengths after the chunk)
-        self.swaps = []  # ("out", seq, [(block, frame)]) or ("in", seq, [(frame, block)])
+        self.swaps = []  # {"kind", "seq", "pairs": [(block, frame)] out / [(frame, block)] in, "length", "positions"}
+        # eager: every decode is evaluated when it happens (needed once blocks are reused after a
+        # release or a swap-out; otherwise attention() reads the store at the end of the replay)
+        self.eager = eager
+        self.decode_out = {}  # (decode index, layer) -> [S, Hq, d] float64 (NaN rows for empty sequences)
 
     def run(self, ops=None):
         for op in (self.wl.ops if ops is None else ops):
@@ -71,15 +75,23 @@ class OracleReplay:
         elif kind == "release":
             self.bm.release(op[1])
         elif kind == "host":
-            self.bm.attach_host(op[1], draws.host_free_order(self.wl.seed, op[1]))
-        elif kind == "swap_out":
-            pairs = self.bm.swap_out(op[1])
-            self.store.to_host(pairs)
-            self.swaps.append(("out", op[1], pairs))
-        elif kind == "swap_in":
-            pairs = self.bm.swap_in(op[1])
-            self.store.from_host(pairs)
-            self.swaps.append(("in", op[1], pairs))
+            sequential = len(op) > 2 and op[2] == "sequential"
+            self.bm.attach_host(op[1], None if sequential else draws.host_free_order(self.wl.seed, op[1]))
+        elif kind in ("swap_out", "swap_in"):
+            seq = op[1]
+            if kind == "swap_out":
+                pairs = self.bm.swap_out(seq)
+                self.store.to_host(pairs)
+            else:
+                pairs = self.bm.swap_in(seq)
+                self.store.from_host(pairs)
+            frames = {f: j for j, (tier, f) in enumerate(self.bm.residency(seq)) if tier == "host"} \
+                if kind == "swap_out" else None
+            self.swaps.append({
+                "kind": kind, "seq": seq, "pairs": pairs, "length": self.bm.length(seq),
+                # logical block of every pair (table order)
+                "positions": [frames[f] for _, f in pairs] if frames is not None else None,
+            })
         elif kind in ("append", "prefill"):
             seq_ids, counts = list(op[1]), list(op[2])
             running = {}
@@ -113,6 +125,10 @@ class OracleReplay:
                 "tables": [self.bm.table(s) for s in seq_ids],
                 "lengths": [self.bm.length(s) for s in seq_ids],
             })
+            if self.eager:
+                i = len(self.decodes) - 1
+                for layer in self.layers:
+                    self.decode_out[(i, layer)] = self._evaluate(i, layer, range(len(seq_ids)))
         else:
             raise ValueError(f"unknown op {kind!r}")
 
@@ -124,12 +140,21 @@ class OracleReplay:
 
     def attention(self, decode_index, layer, rows=None, heads=None):
         """float64 outputs [len(rows), Hq, d] of a recorded decode (rows index its batch)."""
-        wl = self.wl
         dec = self.decodes[decode_index]
         rows = range(len(dec["seq_ids"])) if rows is None else rows
+        if self.eager:
+            return self.decode_out[(decode_index, layer)][list(rows)]
+        return self._evaluate(decode_index, layer, rows)
+
+    def _evaluate(self, decode_index, layer, rows):
+        wl = self.wl
+        dec = self.decodes[decode_index]
         q = draws.bits_to_f64(self.query_bits(decode_index, layer), wl.dtype)
         out = []
         for i in rows:
+            if dec["lengths"][i] == 0 and self.eager:
+                out.append(np.full((wl.num_q_heads, wl.head_dim), np.nan))
+                continue
             k, v = self.gather_f64(layer, dec["tables"][i], dec["lengths"][i])
             out.append(decode_attention(q[i], k, v))
         return np.stack(out)

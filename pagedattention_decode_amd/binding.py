@@ -87,6 +87,15 @@ SIGNATURES = {
                                                        C.POINTER(kv_attention_options)]),
     "paged_attention_decode_cascade": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _I32,
                                               C.POINTER(kv_attention_options), _P, _U64, _P]),
+    "kv_host_frame_bytes": (_U64, [_P]),
+    "kv_pool_attach_host": (_I32, [_P, _P, _I32, _P]),
+    "kv_seq_swap_out": (_I32, [_P, _I64, _P, _U64, _P, _P, _I32, C.POINTER(_I32)]),
+    "kv_seq_swap_in": (_I32, [_P, _I64, _P, _U64, _P, _P, _I32, C.POINTER(_I32)]),
+    "kv_seq_swap_out_fenced": (_I32, [_P, _I64, _U64, _P, _I32, C.POINTER(_I32)]),
+    "kv_seq_swap_in_fenced": (_I32, [_P, _I64, _U64, _P, _I32, C.POINTER(_I32)]),
+    "kv_swap_copy": (_I32, [_P, _P, _I32, _I32, _P, _U64, _P]),
+    "kv_seq_residency": (_I32, [_P, _I64, _I32, _P, _P, C.POINTER(_I32)]),
+    "kv_host_free_list": (_I32, [_P, _I32, _P, C.POINTER(_I32)]),
     "paged_prefill_workspace_bytes": (_U64, [_P, _I32, _I32, _I32, _I32, _I32, C.POINTER(kv_attention_options)]),
     "paged_attention_prefill": (_I32, [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                        C.POINTER(kv_attention_options), _P, _U64, _P]),
@@ -383,3 +392,71 @@ def paged_attention_decode_cascade(pool, layer, q, out, block_tables, context_le
                                                 _dev(group_start), _dev(shared_blocks), n_groups, int(max_group),
                                                 C.byref(opts) if opts is not None else None, _dev(workspace),
                                                 ws_bytes, _stream(stream)))
+
+
+# -- host tier: swap to pinned host frames -------------------------------------
+
+KV_TIER_HBM, KV_TIER_HOST = 0, 1
+
+
+def kv_host_frame_bytes(pool):
+    return int(lib().kv_host_frame_bytes(pool))
+
+
+def kv_pool_attach_host(pool, host_frames, n_frames, initial_free_order=None):
+    """host_frames: a pinned torch tensor, a raw address, or None (bookkeeping only)."""
+    order, ptr = (None, None) if initial_free_order is None else _host(initial_free_order, np.int32)
+    hp = host_frames if isinstance(host_frames, int) or host_frames is None else host_frames.data_ptr()
+    _check(lib().kv_pool_attach_host(pool, hp, int(n_frames), ptr))
+    del order
+
+
+def _pairs_call(fn, *args, cap):
+    out = np.empty((max(cap, 1), 2), np.int32)
+    n = _I32()
+    _check(fn(*args, out.ctypes.data_as(_P), int(cap), C.byref(n)))
+    return out[:n.value].copy()
+
+
+def kv_seq_swap_out(pool, seq_id, staging, stream=None, cap=1 << 20):
+    """(block, frame) pairs [n, 2]."""
+    nbytes = 0 if staging is None else staging.numel() * staging.element_size()
+    return _pairs_call(lib().kv_seq_swap_out, pool, int(seq_id), _dev(staging), nbytes, _stream(stream), cap=cap)
+
+
+def kv_seq_swap_in(pool, seq_id, staging, stream=None, cap=1 << 20):
+    """(frame, block) pairs [n, 2]."""
+    nbytes = 0 if staging is None else staging.numel() * staging.element_size()
+    return _pairs_call(lib().kv_seq_swap_in, pool, int(seq_id), _dev(staging), nbytes, _stream(stream), cap=cap)
+
+
+def kv_seq_swap_out_fenced(pool, seq_id, fence, cap=1 << 20):
+    return _pairs_call(lib().kv_seq_swap_out_fenced, pool, int(seq_id), int(fence), cap=cap)
+
+
+def kv_seq_swap_in_fenced(pool, seq_id, fence, cap=1 << 20):
+    return _pairs_call(lib().kv_seq_swap_in_fenced, pool, int(seq_id), int(fence), cap=cap)
+
+
+def kv_swap_copy(pool, pairs, direction, staging, stream=None):
+    arr, ptr = _host(np.asarray(pairs, np.int32).reshape(-1, 2), np.int32)
+    nbytes = 0 if staging is None else staging.numel() * staging.element_size()
+    _check(lib().kv_swap_copy(pool, ptr, len(arr), int(direction), _dev(staging), nbytes, _stream(stream)))
+    del arr
+
+
+def kv_seq_residency(pool, seq_id, cap=1 << 20):
+    """(tiers int32 [n], indices int32 [n]) of the sequence's extended block table."""
+    tiers = np.empty(max(cap, 1), np.int32)
+    idx = np.empty(max(cap, 1), np.int32)
+    n = _I32()
+    _check(lib().kv_seq_residency(pool, int(seq_id), int(cap), tiers.ctypes.data_as(_P), idx.ctypes.data_as(_P),
+                                  C.byref(n)))
+    return tiers[:n.value].copy(), idx[:n.value].copy()
+
+
+def kv_host_free_list(pool, n_frames):
+    out = np.empty(max(n_frames, 1), np.int32)
+    n = _I32()
+    _check(lib().kv_host_free_list(pool, int(n_frames), out.ctypes.data_as(_P), C.byref(n)))
+    return out[:n.value].copy()

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["pool.cpp", "prefix_cache.cpp", "kernels.hip", "prefill.hip"]
+SOURCES = ["pool.cpp", "prefix_cache.cpp", "kernels.hip", "prefill.hip", "swap.hip"]
 ARCH = "gfx950"
 
 

@@ -15,15 +15,18 @@
 struct kv_prefix_tree;  // prefix_cache.cpp
 
 struct kv_seq_state {
-  std::vector<int32_t> table;  // logical block j -> physical block
+  std::vector<int32_t> table;  // logical block j -> physical block (-1 while host-resident)
   int32_t length = 0;          // tokens
+  std::vector<int32_t> host;   // empty, or per entry: host frame of a host-resident entry, else -1
+  int32_t n_host = 0;          // host-resident entries; > 0 means swapped out
 };
 
 struct kv_pending_group {
   void* event = nullptr;  // hipEvent_t, or nullptr for a fence group
   uint64_t fence = 0;     // used when event == nullptr
   bool ready = false;
-  std::vector<int32_t> blocks;
+  std::vector<int32_t> blocks;  // device blocks going back to the free list
+  std::vector<int32_t> frames;  // host frames going back to the host free list
 };
 
 struct kv_pool {
@@ -36,6 +39,11 @@ struct kv_pool {
   std::deque<kv_pending_group> pending;      // released, waiting for the device
   int32_t n_pending = 0;
   kv_prefix_tree* tree = nullptr;            // prefix cache, created on first use
+  // host tier (kv_pool_attach_host): caller-owned pinned frames, FIFO free list
+  void* host_frames = nullptr;
+  int32_t n_frames = 0;
+  std::deque<int32_t> host_free;
+  int32_t n_host_pending = 0;
 };
 
 namespace pagedkv {
@@ -59,6 +67,12 @@ inline int64_t tile_bytes(const kv_pool_config& c) {
   return tile_elems(c) * bits / 8 + tile_elems(c) / 32 * 2;
 }
 
+// Bytes of one host frame: the block's K tiles of every head, then its V
+// tiles, for every layer in turn.
+inline int64_t frame_bytes(const kv_pool_config& c) {
+  return 2LL * c.num_layers * c.num_kv_heads * tile_bytes(c);
+}
+
 // Bytes of the whole K (or V) buffer.
 inline int64_t pool_bytes(const kv_pool_config& c) {
   return static_cast<int64_t>(c.num_layers) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
@@ -80,6 +94,11 @@ kv_status prefix_phase_launch(kv_pool* pool, int layer, const void* q, void* out
                               const int32_t* prefix_ctx, const int32_t* tables, int n_groups, int n_rows,
                               int max_group, int max_blocks, int num_q_heads, const kv_attention_options* opts,
                               void* ws, hipStream_t st);
+
+// Device side of a swap (swap.hip): pairs are (block, frame) for direction 0
+// (out) and (frame, block) for direction 1 (in); checked by the caller.
+kv_status swap_copy(kv_pool* pool, const int32_t* pairs, int32_t n, int32_t direction, void* d_staging,
+                    uint64_t staging_bytes, hipStream_t st);
 
 // Shared by the attention entry points (defined with the decode kernels).
 constexpr int kMaxGroup = 16;  // query heads per KV head

@@ -193,6 +193,7 @@ kv_status kv_prefix_insert(kv_pool* p, int64_t seq_id, const int32_t* tokens, in
   auto sit = p->seqs.find(seq_id);
   if (sit == p->seqs.end()) return fail(KV_ERR_INVALID, "unknown sequence " + std::to_string(seq_id));
   if (n < 0 || n > sit->second.length) return fail(KV_ERR_INVALID, "n must be in [0, sequence length]");
+  if (sit->second.n_host > 0) return fail(KV_ERR_INVALID, "sequence " + std::to_string(seq_id) + " is swapped out");
   kv_prefix_tree* t = tree_of(p);
   const int32_t B = p->cfg.block_size;
   const std::vector<int32_t>& table = sit->second.table;

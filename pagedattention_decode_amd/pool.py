@@ -113,6 +113,41 @@ class PagedKVPool:
         B.paged_attention_decode_cascade(self.handle, layer, q, out, block_tables, context_lens, num_q_heads,
                                          group_start, shared_blocks, max_group, opts, workspace, stream)
 
+    # -- host tier ----------------------------------------------------------
+    def attach_host(self, n_frames, free_order=None, staging_bytes=64 << 20):
+        """Pinned host frames (allocated here when the pool owns device memory) and a
+        device staging buffer of whole frames (at least one)."""
+        self.frame_bytes = B.kv_host_frame_bytes(self.handle)
+        self.n_frames = n_frames
+        self.host_frames = self.staging = None
+        if self.k_cache is not None:
+            import torch
+            self.host_frames = torch.empty(n_frames * self.frame_bytes, dtype=torch.uint8, pin_memory=True)
+            frames = max(1, staging_bytes // self.frame_bytes)
+            self.staging = torch.empty(frames * self.frame_bytes, dtype=torch.uint8, device=self.k_cache.device)
+        B.kv_pool_attach_host(self.handle, self.host_frames, n_frames, free_order)
+
+    def swap_out(self, seq, stream=None):
+        return B.kv_seq_swap_out(self.handle, seq, self.staging, stream)
+
+    def swap_in(self, seq, stream=None):
+        return B.kv_seq_swap_in(self.handle, seq, self.staging, stream)
+
+    def swap_out_fenced(self, seq, fence):
+        return B.kv_seq_swap_out_fenced(self.handle, seq, fence)
+
+    def swap_in_fenced(self, seq, fence):
+        return B.kv_seq_swap_in_fenced(self.handle, seq, fence)
+
+    def swap_copy(self, pairs, direction, stream=None):
+        B.kv_swap_copy(self.handle, pairs, direction, self.staging, stream)
+
+    def residency(self, seq):
+        return B.kv_seq_residency(self.handle, seq)
+
+    def host_free_list(self):
+        return B.kv_host_free_list(self.handle, self.n_frames)
+
     # -- prefix cache --------------------------------------------------------
     def prefix_match(self, tokens):
         return B.kv_prefix_match(self.handle, tokens)

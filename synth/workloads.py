@@ -202,7 +202,7 @@ def verify_drafts(positions=8) -> Workload:
                     description=f"bf16 Hq=32 Hkv=8 d=128 B=16, 16 x ({8192 - positions} cached + {positions} drafts)")
 
 
-def tool_pause(layers: int = 2, seed: int = 8) -> Workload:
+def tool_pause(layers: int = 2, seed: int = 8, frames: str = "shuffled") -> Workload:
     """Trajectories paused for a tool call are swapped to host frames and back.
 
     Eight sequences of mixed lengths (two of them forks of a third, so some of
@@ -213,7 +213,8 @@ def tool_pause(layers: int = 2, seed: int = 8) -> Workload:
     """
     lens = (2304, 37, 16, 1000, 513, 0, 64, 300)
     seqs = tuple(range(len(lens)))
-    ops = [("host", 256)]
+    # "sequential": the host free list starts 0, 1, 2, ... (frames of a swap are consecutive)
+    ops = [("host", 256) if frames == "shuffled" else ("host", 256, "sequential")]
     ops += [("add", s) for s in seqs if s not in (6, 7)]
     ops.append(("append", tuple(s for s in seqs if s not in (6, 7)), tuple(lens[s] for s in seqs if s not in (6, 7))))
     ops += [("fork", 3, 6), ("fork", 3, 7)]

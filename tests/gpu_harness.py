@@ -42,7 +42,7 @@ def bits_to_float_tensor(t: torch.Tensor, dtype: str) -> torch.Tensor:
 
 class GpuRun:
     def __init__(self, wl, layers=None, writers=None, opts=None, free_order=None, fill=None,
-                 max_blocks=None, ref=None, decode_layers=None):
+                 max_blocks=None, ref=None, decode_layers=None, staging_bytes=64 << 20, on_swap=None):
         self.wl = wl
         self.layers = list(range(wl.num_layers)) if layers is None else list(layers)
         self.decode_layers = self.layers if decode_layers is None else list(decode_layers)
@@ -69,6 +69,9 @@ class GpuRun:
         self.n_append = 0
         self.n_decode = 0
         self.n_prefill = 0
+        self.staging_bytes = staging_bytes
+        self.on_swap = on_swap  # called as on_swap(run, swap index) after every swap, once its copies are done
+        self.swaps = []         # (kind, seq, pairs)
 
     def rows(self, tag, layer, writer, positions):
         wl = self.wl
@@ -89,6 +92,24 @@ class GpuRun:
             pool.fork(op[1], op[2])
         elif kind == "release":
             pool.release(op[1])
+            # the blocks return once the stream passes the release; waiting here keeps the free
+            # list in the oracle's order whatever the timing
+            pool.reclaim(True)
+        elif kind == "host":
+            sequential = len(op) > 2 and op[2] == "sequential"
+            pool.attach_host(op[1], None if sequential else draws.host_free_order(self.wl.seed, op[1]),
+                             staging_bytes=self.staging_bytes)
+        elif kind in ("swap_out", "swap_in"):
+            pairs = pool.swap_out(op[1]) if kind == "swap_out" else pool.swap_in(op[1])
+            pool.reclaim(True)  # as for release: freed blocks and frames back in the oracle's order
+            if self.ref is not None:
+                r = self.ref.swaps[len(self.swaps)]
+                assert r["kind"] == kind and r["seq"] == op[1]
+                assert [tuple(p) for p in pairs.tolist()] == [tuple(p) for p in r["pairs"]], "swap pairs differ"
+            self.swaps.append((kind, op[1], pairs))
+            if self.on_swap is not None:
+                torch.cuda.synchronize()
+                self.on_swap(self, len(self.swaps) - 1)
         elif kind == "append":
             seq_ids, counts = list(op[1]), list(op[2])
             segments, running = [], {}

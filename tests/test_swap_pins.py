@@ -196,12 +196,14 @@ def test_tool_pause_workload_round_trip():
     """The paused sequences read exactly their own rows after coming back, in other blocks."""
     wl = workloads.tool_pause(layers=1)
     ref = OracleReplay(wl).run()
-    out0 = next(p for k, s, p in ref.swaps if k == "out" and s == 0)
-    in0 = next(p for k, s, p in ref.swaps if k == "in" and s == 0)
+    def pairs_of(kind, seq):
+        return next(r["pairs"] for r in ref.swaps if r["kind"] == kind and r["seq"] == seq)
+
+    out0, in0 = pairs_of("swap_out", 0), pairs_of("swap_in", 0)
     assert len(out0) == 144 and [f for f, _ in in0] == [f for _, f in out0]
     assert set(b for b, _ in out0) != set(b for _, b in in0)
-    out3 = next(p for k, s, p in ref.swaps if k == "out" and s == 3)
-    assert len(out3) == 1  # the forks share the other 62 blocks of sequence 3
+    assert len(pairs_of("swap_out", 3)) == 1  # the forks share the other 62 blocks of sequence 3
+    assert next(r["positions"] for r in ref.swaps if r["kind"] == "swap_out" and r["seq"] == 3) == [62]
     # the final decode's tables gather the draws each sequence wrote, wherever they live
     from synth import draws
     from synth.draws import TAG_K
@@ -213,3 +215,16 @@ def test_tool_pause_workload_round_trip():
         expect = draws.token_rows(wl.seed, TAG_K, 0, s, np.arange(n), wl.num_kv_heads, wl.head_dim, wl.dtype)
         assert np.array_equal(k, expect), s
     ref.bm.check()
+
+
+def test_eager_decodes_equal_lazy_ones_where_nothing_is_reused():
+    """Eager evaluation (needed once freed blocks are reused) agrees with the end-of-replay
+    evaluation wherever the blocks a decode read are unchanged at the end: the last decode."""
+    wl = workloads.tool_pause(layers=1)
+    eager = OracleReplay(wl, eager=True).run()
+    lazy = OracleReplay(wl).run()
+    last = len(lazy.decodes) - 1
+    np.testing.assert_array_equal(eager.attention(last, 0), lazy.attention(last, 0))
+    # an empty sequence has no defined output: NaN rows in the eager record
+    first = eager.attention(0, 0)
+    assert np.isnan(first[5]).all() and np.isfinite(np.delete(first, 5, axis=0)).all()
