@@ -21,6 +21,10 @@ Workloads (synthetic, seeded; see synth/workloads.py):
 groups come from kv_shared_prefix_plan every step, each group's shared prefix
 is read once; roofline bytes then count the prefix once per group.
 
+--op swap times the host tier: --swap-seqs of the 37 Qwen3-8B-shaped sequences
+(36 layers, 2304 tokens, 340 MB of KV each) swapped out to pinned host frames
+and back in per step; reported in GB/s over the host link (both directions)
+against PCIe Gen5 x16 (64 GB/s per direction).
 --op prefill / verify time the multi-query path instead (paged_attention_prefill):
   prefill  the last 512-token chunk of 16 8K-token prompts (7680 cached tokens each),
            reported in TFLOP/s against the bf16 matrix peak;
@@ -53,7 +57,8 @@ def parse():
     ap.add_argument("--kv", default="bf16", choices=["bf16", "q8_0", "q4_0"],
                     help="storage of the KV pool for --op decode: bf16, or q8_0 / q4_0 codes with one 2-byte "
                          "scale per 32 values (written by reshape_and_cache, dequantised in the kernel)")
-    ap.add_argument("--op", default="decode", choices=["decode", "prefill", "verify"],
+    ap.add_argument("--swap-seqs", type=int, default=8, help="--op swap: sequences swapped out and back in per step")
+    ap.add_argument("--op", default="decode", choices=["decode", "prefill", "verify", "swap"],
                     help="decode: the decode step of --config; prefill: the last 512-token chunk of 16 "
                          "8K prompts; verify: 8 draft positions for 16 requests with 8K contexts")
     ap.add_argument("--cascade", action="store_true",
@@ -92,6 +97,9 @@ def main():
               "(the path has no multi-GPU form)", file=sys.stderr)
         sys.exit(2)
 
+    if args.op == "swap":
+        swap_bench(args)
+        return
     if args.op != "decode":
         multi_query_bench(args)
         return
@@ -499,6 +507,176 @@ def multi_query_cpu_baseline(args, wl):
         "sample": f"the oracle's chunk attention of the first {c} queries of sequence 0's chunk "
                   f"(keys 0..{n - 1}), repeated {reps} times in {wall:.1f} s",
         "chunk_tokens_per_s_per_layer": round(c * reps / wall, 3),
+    }
+
+
+PCIE_GEN5_X16_GBS = 64.0  # per direction, public specification of the MI355X host link
+
+
+def swap_bench(args):
+    """Swap round trips over the host link ([KVM] asynchronous paged swap).
+
+    A step swaps --swap-seqs sequences out (kv_seq_swap_out, one call each,
+    all on one stream) and then back in (kv_seq_swap_in).  The pool is the
+    Qwen3-8B-shaped workload with all 36 layers, so a frame is one block of
+    every layer (16 x 147456 bytes).  HIP events time each direction on the
+    stream; a plain pinned hipMemcpy of the same bytes is timed beside it as
+    the link's practical ceiling.
+    """
+    import numpy as np
+    import torch
+
+    from pagedattention_decode_amd.pool import PagedKVPool
+    from synth import draws, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.qwen_independent()
+    L = args.layers or 36
+    seed = args.seed or wl.seed
+    Hkv, d, Bs = wl.num_kv_heads, wl.head_dim, wl.block_size
+    # headroom of two swap sets: a swap-in takes fresh blocks while the last swap-out's
+    # blocks may still wait for their copies to finish
+    n_blocks = wl.num_blocks + 2 * args.swap_seqs * 144
+    pool = PagedKVPool(L, n_blocks, Bs, Hkv, d, args.kv, free_order=draws.free_order(seed, n_blocks))
+    seqs = list(range(37))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    t_fill = time.time()
+    for s_ in seqs:
+        pool.add(s_)
+    slots, _ = pool.append(seqs, [2304] * len(seqs))
+    d_slots = torch.from_numpy(slots).to(dev)
+    for layer in range(L):
+        k = torch.randn((len(slots), Hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((len(slots), Hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+        pool.cache(layer, k, v, d_slots)
+    torch.cuda.synchronize()
+    t_fill = time.time() - t_fill
+    moved = seqs[:args.swap_seqs]
+    blocks = sum(pool.info(s_)[1] for s_ in moved)
+    pool.attach_host(2 * blocks + 16, staging_bytes=64 << 20)  # headroom as for the blocks
+    F = pool.frame_bytes
+    nbytes = blocks * F
+    stream = torch.cuda.current_stream()
+
+    def step(timed):
+        # the previous step's freed blocks and frames come back once its copies are done
+        # (a host wait: the host runs at most one step ahead of the copies)
+        pool.reclaim(True)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        for s_ in moved:
+            pool.swap_out(s_)
+        e[1].record(stream)
+        for s_ in moved:
+            pool.swap_in(s_)
+        e[2].record(stream)
+        return e
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = [step(True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    out_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    in_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    pool.check()
+
+    # the link's practical ceiling: one plain pinned copy of the same bytes each way
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    devbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        host.copy_(devbuf, non_blocking=True)
+        devbuf.copy_(host, non_blocking=True)
+    torch.cuda.synchronize()
+    c = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    c[0].record(stream)
+    host.copy_(devbuf, non_blocking=True)
+    c[1].record(stream)
+    devbuf.copy_(host, non_blocking=True)
+    c[2].record(stream)
+    torch.cuda.synchronize()
+    plain_out = nbytes / (c[0].elapsed_time(c[1]) / 1e3) / 1e9
+    plain_in = nbytes / (c[1].elapsed_time(c[2]) / 1e3) / 1e9
+
+    gbs_out = nbytes / (out_ms / 1e3) / 1e9
+    gbs_in = nbytes / (in_ms / 1e3) / 1e9
+    value = 2 * nbytes * args.steps / wall / 1e9
+    result = {
+        "metric": "KV swap round trip over the host link, GB/s (both directions)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.kv,
+        "data": "synthetic",
+        "config": {
+            "workload": f"qwen3_8b_37x2304_swap{len(moved)}",
+            "description": f"{args.kv} Hq=32 Hkv=8 d=128 B=16, {L} layers, {len(moved)} of 37 sequences x 2304 "
+                           "tokens swapped out and back in per step",
+            "frame_bytes": F,
+            "frames_per_direction": blocks,
+            "bytes_per_direction": nbytes,
+            "staging_bytes": int(pool.staging.numel()),
+        },
+        "swap_out_ms": round(out_ms, 3),
+        "swap_in_ms": round(in_ms, 3),
+        "swap_out_gbs": round(gbs_out, 2),
+        "swap_in_gbs": round(gbs_in, 2),
+        "plain_pinned_copy_gbs": {"out": round(plain_out, 2), "in": round(plain_in, 2)},
+        "fill_seconds": round(t_fill, 2),
+        "roofline": {
+            "bound": "host-link",
+            "achieved": round(min(gbs_out, gbs_in), 2),
+            "peak": PCIE_GEN5_X16_GBS,
+            "unit": "GB/s",
+            "frac": round(min(gbs_out, gbs_in) / PCIE_GEN5_X16_GBS, 4),
+            "traffic": None,
+            "kernel": "kv_seq_swap_out / kv_seq_swap_in (staging copy kernel + DMA), slower direction",
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = swap_cpu_baseline(args)
+    print(json.dumps(result), flush=True)
+
+
+def swap_cpu_baseline(args):
+    """The oracle's swap of one sequence (bookkeeping plus its store's block copies), repeated."""
+    from synth import workloads
+    from oracle.runner import OracleReplay
+
+    cores = 1
+    wl = workloads.qwen_independent()
+    ref = OracleReplay(wl, writers={0}).run()
+    ref.bm.attach_host(200)
+    n = ref.bm.length(0)
+    nbytes = -(-n // wl.block_size) * wl.block_size * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ref.store.to_host(ref.bm.swap_out(0))
+        ref.store.from_host(ref.bm.swap_in(0))
+        reps += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    wall = time.perf_counter() - t0
+    return {
+        "value": round(2 * nbytes * reps / wall / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"the oracle's swap out and back in of sequence 0 (2304 tokens, one layer), repeated {reps} "
+                  f"times in {wall:.1f} s",
     }
 
 
