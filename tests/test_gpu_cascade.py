@@ -134,3 +134,15 @@ def test_contract_violations_give_nan_rows():
         qrun.decode_cascade(0, 0)
     assert e.value.status == B.KV_ERR_UNSUPPORTED
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 64), (16, 2, 256), (16, 16, 128), (64, 4, 128), (12, 4, 64)])
+def test_head_shapes(hq, hkv, d):
+    announce(f"read-once decode, Hq={hq} Hkv={hkv} d={d}, two groups and a singleton")
+    wl = fork_workload([(96, [0, 5, 40]), (33, [0]), (300, [17, 1])], hq=hq, hkv=hkv, d=d, seed=67)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()
+    gs, sb = run.pool.shared_prefix_plan(run.decodes[0]["seq_ids"])
+    assert list(gs) == [0, 3, 4, 6] and list(sb) == [6, 0, 18]
+    out = run.decode_cascade(0, 0).double().cpu().numpy()
+    check(out, ref.attention(0, 0), f"Hq={hq} Hkv={hkv} d={d}")

@@ -213,3 +213,39 @@ def test_swap_round_trip_of_every_block_of_a_long_sequence():
     assert out["tables"][0] != back["tables"][0]  # other blocks, same values
     check_decodes(run, ref)
     check_blocks_back(run, ref)
+
+
+@pytest.mark.parametrize("dtype,block,hkv,d", [(draws.F32, 4, 2, 64), (draws.BF16, 6, 1, 32), (draws.BF16, 16, 4, 256)])
+def test_other_pool_shapes(dtype, block, hkv, d):
+    announce(f"swap on a {dtype} pool, B={block}, Hkv={hkv}, d={d}: frames and blocks bit-exact")
+    ops = [("host", 64, "sequential"), ("add", 0), ("add", 1), ("append", (0, 1), (5 * block + 1, 3 * block + 2)),
+           ("fork", 1, 2), ("append", (2,), (2,)), ("swap_out", 0), ("swap_out", 1),
+           ("add", 3), ("append", (3,), (7 * block,)), ("swap_in", 1), ("swap_in", 0)]
+    wl = workloads.Workload("swap_shapes", 71, dtype, 2, 2 * hkv, hkv, d, block, 40, ops)
+    bits = np.uint32 if dtype == draws.F32 else np.uint16
+    pattern = 0xFFFFFFFF if dtype == draws.F32 else 0xFFFF
+
+    def bg(layer, which, b):
+        return np.full((block, hkv, d), pattern, bits)
+
+    ref = RecordingReplay(wl, background=bg, eager=True).run()
+    seen = []
+
+    def on_swap(run, i):
+        kind, seq, pairs = run.swaps[i]
+        if kind != "swap_out":
+            return
+        for block_id, frame in pairs.tolist():
+            for layer in range(wl.num_layers):
+                for which in ("k", "v"):
+                    elems = frame_chunk(run, frame, layer, which).view(bits)
+                    idx = layout_index(1, block, hkv, d, dtype, which)
+                    assert np.array_equal(elems[idx][0], ref.swaps[i]["host"][(layer, which, frame)])
+            seen.append(frame)
+
+    run = GpuRun(wl, ref=ref, fill=-1, on_swap=on_swap).run()
+    # sequence 0 moves its 6 blocks; sequence 1 only the block its fork copied away from it,
+    # the other 3 stay shared in HBM
+    assert len(seen) == 6 + 1
+    check_blocks_back(run, ref)
+    run.pool.check()
