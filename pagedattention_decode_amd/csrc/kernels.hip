@@ -880,101 +880,84 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
 // Merge for the split-K kernel: unit (seq, kv head) was covered by waves
 // wF..wL (the waves whose runs hold its first and last partition); unless one
 // wave held it whole, fold the partials of slots w + unit with the
-// running-max recurrences.  Also writes zero rows for empty sequences.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeWeights = 2048;  // partials whose weights are kept in LDS
+// running-max recurrences.  Also writes zero rows for empty sequences.  One
+// wave per (sequence, query head), four per workgroup: lane p holds the weight
+// of partial p (64 at a time) and every lane then accumulates its D/64 dims
+// over the partials, four row loads in flight.
+constexpr int kMergeItems = 4;
 
-__global__ void __launch_bounds__(kMergeThreads) merge_sk_kernel(sk_args a, int head_dim) {
-  const int seq = blockIdx.x / a.n_q_heads;
-  const int h = blockIdx.x % a.n_q_heads;
+template <int D>
+__global__ void __launch_bounds__(kMergeItems * 64) merge_sk_kernel(sk_args a) {
+  constexpr int E = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * kMergeItems + (threadIdx.x >> 6);
+  if (item >= static_cast<int64_t>(a.n_seqs) * a.n_q_heads) return;
+  const int seq = static_cast<int>(item / a.n_q_heads);
+  const int h = static_cast<int>(item % a.n_q_heads);
   const int G = a.n_q_heads / a.n_kv_heads;
   const int kvh = h / G, hg = h % G;
-  const int tid = threadIdx.x;
-  uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(seq) * a.n_q_heads + h) * head_dim;
+  uint16_t* out = static_cast<uint16_t*>(a.out) + item * D + lane * E;
   const int np = a.cum_parts[seq + 1] - a.cum_parts[seq];
   if (np == 0) {
-    for (int e = tid; e < head_dim; e += kMergeThreads) out[e] = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) out[j] = 0;
     return;
   }
   const int64_t total = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[a.n_seqs];
   const int64_t W = a.n_waves;
   const int64_t first = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[seq] + static_cast<int64_t>(kvh) * np;
-  const int64_t lastp = first + np - 1;
   auto wave_of = [&](int64_t pp) { return ((pp + 1) * W - 1) / total; };
   auto run_begin = [&](int64_t w) { return w * total / W; };
-  const int64_t wF = wave_of(first), wL = wave_of(lastp);
+  const int64_t wF = wave_of(first), wL = wave_of(first + np - 1);
   if (wF == wL) return;  // one wave wrote the final row
   const int n_w = static_cast<int>(wL - wF + 1);
   const int64_t unit = static_cast<int64_t>(seq) * a.n_kv_heads + kvh;
-  __shared__ float w_s[kMergeWeights];
-  __shared__ float red[kMergeThreads / 64];
-  __shared__ float4 acc_s[kMergeThreads];
   auto row_of = [&](int i) { return (wF + i + unit) * G + hg; };
   auto live = [&](int i) { return run_begin(wF + i) < run_begin(wF + i + 1); };
   float M = -INFINITY;
-  for (int i = tid; i < n_w; i += kMergeThreads)
-    if (live(i)) M = fmaxf(M, a.part_m[row_of(i)]);
-  M = wave_max(M);
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float L = 0.f;
-  for (int i = tid; i < n_w; i += kMergeThreads) {
-    float f = 0.f;
+  bool nan = false;
+  for (int i = lane; i < n_w; i += 64)
     if (live(i)) {
       const float m = a.part_m[row_of(i)];
-      f = (m != m) ? __builtin_nanf("") : exp2f(m - M);
-      L += f * a.part_l[row_of(i)];
+      nan |= m != m;
+      M = fmaxf(M, m);
     }
-    if (i < kMergeWeights) w_s[i] = f;
+  M = wave_max(M);
+  nan = __builtin_amdgcn_ballot_w64(nan) != 0;
+  float acc[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) acc[j] = 0.f;
+  float L = 0.f;
+  for (int i0 = 0; i0 < n_w; i0 += 64) {
+    float w = 0.f;
+    if (i0 + lane < n_w && live(i0 + lane)) {
+      const float m = a.part_m[row_of(i0 + lane)];
+      w = (m != m) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      L += w * a.part_l[row_of(i0 + lane)];
+    }
+    const int cnt = min(64, n_w - i0);
+#pragma unroll 4
+    for (int k = 0; k < cnt; ++k) {
+      const float wk = __shfl(w, k);
+      const float* o = a.part_o + row_of(i0 + k) * D + lane * E;
+      float v[E];
+      if constexpr (E == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(o);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+      } else if constexpr (E == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(o);
+        v[0] = t.x; v[1] = t.y;
+      } else {
+        v[0] = o[0];
+      }
+#pragma unroll
+      for (int j = 0; j < E; ++j) acc[j] = wk == 0.f ? acc[j] : __builtin_fmaf(wk, v[j], acc[j]);
+    }
   }
   L = wave_sum(L);
-  if ((tid & 63) == 0) red[tid >> 6] = L;
-  __syncthreads();
-  L = red[0] + red[1] + red[2] + red[3];
-  const int d4 = head_dim / 4;
-  const int groups = kMergeThreads / d4;
-  const int grp = tid / d4, c = tid % d4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (grp < groups) {
-    for (int i = grp; i < n_w; i += groups) {
-      float f;
-      if (i < kMergeWeights) {
-        f = w_s[i];
-      } else {
-        f = 0.f;
-        if (live(i)) {
-          const float m = a.part_m[row_of(i)];
-          f = (m != m) ? __builtin_nanf("") : exp2f(m - M);
-        }
-      }
-      if (f == 0.f) continue;
-      const float4 v = reinterpret_cast<const float4*>(a.part_o + row_of(i) * head_dim)[c];
-      acc.x += f * v.x;
-      acc.y += f * v.y;
-      acc.z += f * v.z;
-      acc.w += f * v.w;
-    }
-  }
-  acc_s[tid] = acc;
-  __syncthreads();
-  if (tid < d4) {
-    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int g = 0; g < groups; ++g) {
-      const float4 v = acc_s[g * d4 + tid];
-      sum.x += v.x;
-      sum.y += v.y;
-      sum.z += v.z;
-      sum.w += v.w;
-    }
-    const float inv = 1.f / L;
-    uint16_t* o4 = out + 4 * tid;
-    o4[0] = f32_to_bf16(sum.x * inv);
-    o4[1] = f32_to_bf16(sum.y * inv);
-    o4[2] = f32_to_bf16(sum.z * inv);
-    o4[3] = f32_to_bf16(sum.w * inv);
-  }
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int j = 0; j < E; ++j) out[j] = nan ? static_cast<uint16_t>(0x7fc0) : f32_to_bf16(acc[j] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -1153,6 +1136,9 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cascade_args c) {
 // One workgroup per (sequence, query head); sequences with one partition were
 // finished by the partition kernel.
 // ---------------------------------------------------------------------------
+
+constexpr int kMergeThreads = 256;
+constexpr int kMergeWeights = 2048;  // partitions whose weights are kept in LDS
 
 template <typename T>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(attn_args a) {
@@ -1524,9 +1510,13 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     else if (c.dtype == KV_Q4_0) e = launch(std::integral_constant<int, kFmtQ4>{});
     else e = launch(std::integral_constant<int, kFmtBf16>{});
     if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
-    const int64_t mgrid = static_cast<int64_t>(n_seqs) * num_q_heads;
-    hipLaunchKernelGGL(merge_sk_kernel, dim3(static_cast<unsigned>(mgrid)), dim3(kMergeThreads), 0, st, a,
-                       static_cast<int>(c.head_dim));
+    const unsigned mgrid =
+        static_cast<unsigned>((static_cast<int64_t>(n_seqs) * num_q_heads + kMergeItems - 1) / kMergeItems);
+    switch (c.head_dim) {
+      case 64: hipLaunchKernelGGL(merge_sk_kernel<64>, dim3(mgrid), dim3(kMergeItems * 64), 0, st, a); break;
+      case 128: hipLaunchKernelGGL(merge_sk_kernel<128>, dim3(mgrid), dim3(kMergeItems * 64), 0, st, a); break;
+      default: hipLaunchKernelGGL(merge_sk_kernel<256>, dim3(mgrid), dim3(kMergeItems * 64), 0, st, a); break;
+    }
     return hip_check(hipGetLastError(), "paged attention merge launch");
   }
 
