@@ -170,8 +170,13 @@ def main():
         if step_appends else None
     out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
     if args.cascade:
-        # groups of up to S members, any number of groups (the prefix partition depends on it)
-        ws_bytes = max(pool.cascade_workspace_bytes(S, ng, S, Hq, max_blocks, opts) for ng in range(1, S + 1))
+        # max_group sizes the prefix grid: the largest group of the first step's plan (the fork
+        # structure does not change while the sequences decode); the workspace covers any number
+        # of groups, since the prefix partition depends on it
+        gs0, _ = pool.shared_prefix_plan(np.asarray(decode_seqs, np.int64))
+        max_group = int(np.diff(gs0).max())
+        ws_bytes = max(pool.cascade_workspace_bytes(S, ng, max_group, Hq, max_blocks, opts)
+                       for ng in range(1, S + 1))
         d_plan = torch.empty((2 * S + 1,), dtype=torch.int32, device=dev)
     else:
         ws_bytes = pool.workspace_bytes(S, Hq, max_blocks, opts)
@@ -211,6 +216,7 @@ def main():
         if args.cascade:
             gs, sb = pool.shared_prefix_plan(seq_arr)
             ng = len(sb)
+            assert int(np.diff(gs).max()) <= max_group, "a fork group outgrew the first step's plan"
             h_plan[slot].numpy()[:ng + 1] = gs
             h_plan[slot].numpy()[ng + 1:2 * ng + 1] = sb
             d_plan[:2 * ng + 1].copy_(h_plan[slot][:2 * ng + 1], non_blocking=True)
@@ -236,7 +242,7 @@ def main():
             if args.cascade:
                 ng = n_groups[0]
                 pool.decode_cascade(layer, q_in[i][layer], out, d_tables, d_lens, Hq, d_plan[:ng + 1],
-                                    d_plan[ng + 1:2 * ng + 1], S, opts, ws)
+                                    d_plan[ng + 1:2 * ng + 1], max_group, opts, ws)
             else:
                 pool.decode(layer, q_in[i][layer], out, d_tables, d_lens, Hq, opts, ws)
             if timed:

@@ -467,8 +467,9 @@ uint64_t paged_prefill_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int3
  *                    clamped to max_blocks_per_seq * B).
  *   d_workspace:     at least paged_prefill_workspace_bytes, 256-byte
  *                    aligned (NULL if that is 0); no initialisation needed.
- * A table entry outside [0, N) is never dereferenced: the rows of the query
- * tiles that would read it are written as NaN.  Only the matrix-core kernel
+ * A table entry outside [0, N) is never dereferenced: every row whose visible
+ * keys include it is written as NaN, and so may be the other rows of its
+ * query tile (16 consecutive columns of (row, head)).  Only the matrix-core kernel
  * exists (bf16, B = 16, d in {64, 128, 256}, G <= 16); other pools give
  * KV_ERR_UNSUPPORTED.  opts->partition_tokens splits every tile's keys into
  * partitions merged with the [KVM] recurrences (0 = the library's choice). */

@@ -134,10 +134,11 @@ __device__ __forceinline__ void zero_pair_tail(kv_pair<D>& r, int valid_a, int v
 // slots of each block visible to the lane's column; otherwise every slot of
 // both blocks is visible to every column.  V tails beyond the context are
 // already zero.
-template <int D, int NCG, bool MASKED>
-__device__ __forceinline__ void attend_pair(const kv_pair<D>& kv, const bf16x8_t* q_lds, int lane,
-                                            const int* lim_a, const int* lim_b, int quad, float c,
-                                            f32x4_t (&o)[NCG][D / 16], float* m_run, float* l_lane) {
+// qop(cg, kk) gives the Q^T operand of column group cg, k-step kk.
+template <int D, int NCG, bool MASKED, class QOp>
+__device__ __forceinline__ void attend_pair(const kv_pair<D>& kv, const QOp& qop, const int* lim_a,
+                                            const int* lim_b, int quad, float c, f32x4_t (&o)[NCG][D / 16],
+                                            float* m_run, float* l_lane) {
   f32x4_t sa[NCG], sb[NCG];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
@@ -145,7 +146,7 @@ __device__ __forceinline__ void attend_pair(const kv_pair<D>& kv, const bf16x8_t
     sb[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      const bf16x8_t qk = q_lds[(cg * (D / 32) + kk) * 64 + lane];
+      const bf16x8_t qk = qop(cg, kk);
       sa[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.ka[kk]), qk, sa[cg], 0, 0, 0);
       sb[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.kb[kk]), qk, sb[cg], 0, 0, 0);
     }
@@ -347,8 +348,9 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
         const int valid_a = bad_a ? 0 : min(16, sq.n - b * 16);
         const int valid_b = (!has_b || bad_b) ? 0 : min(16, sq.n - (b + 1) * 16);
         if (valid_a < 16 || valid_b < 16) zero_pair_tail<D>(buf[u], valid_a, valid_b, quad);
+        auto qop = [&](int cg, int kk) { return q_lds[(cg * (D / 32) + kk) * 64 + ql]; };
         if (valid_a == 16 && valid_b == 16 && b * 16 + 31 <= pos_min) {
-          attend_pair<D, NCG, false>(buf[u], q_lds, ql, nullptr, nullptr, quad, c, o, m_run, l_lane);
+          attend_pair<D, NCG, false>(buf[u], qop, nullptr, nullptr, quad, c, o, m_run, l_lane);
         } else {
           int lim_a[NCG], lim_b[NCG];
 #pragma unroll
@@ -356,12 +358,251 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
             lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
             lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
           }
-          attend_pair<D, NCG, true>(buf[u], q_lds, ql, lim_a, lim_b, quad, c, o, m_run, l_lane);
+          attend_pair<D, NCG, true>(buf[u], qop, lim_a, lim_b, quad, c, o, m_run, l_lane);
         }
       }
       issue(u, b + 2 * STAGES);
     }
   }
+
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    float l = l_lane[cg] + __shfl_xor(l_lane[cg], 16);
+    l += __shfl_xor(l, 32);
+    const int f = f0 + cg * 16 + (lane & 15);
+    if (f >= cols) continue;
+    const int64_t row = static_cast<int64_t>(sq.q0 + f / G) * a.n_q_heads + g * G + f % G;
+    if (n_parts == 1 && !a.force_partial) {
+      const float inv = 1.f / l;
+      uint16_t* orow = out + row * D;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = poisoned ? nan : o[cg][nt][i] * inv;
+        *reinterpret_cast<uint2*>(orow + nt * 16 + quad * 4) =
+            make_uint2(static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+                       static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16));
+      }
+    } else {
+      const int64_t pi = row * a.max_parts + part;
+      float* po = a.part_o + pi * D;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt)
+        *reinterpret_cast<float4*>(po + nt * 16 + quad * 4) =
+            poisoned ? make_float4(nan, nan, nan, nan)
+                     : make_float4(o[cg][nt][0], o[cg][nt][1], o[cg][nt][2], o[cg][nt][3]);
+      if (quad == 0) {
+        a.part_m[pi] = poisoned ? nan : m_run[cg];
+        a.part_l[pi] = poisoned ? nan : l;
+      }
+    }
+  }
+}
+
+// The same attention with the K/V of each block pair shared through LDS by the
+// WT waves of a partition group (consecutive tiles of one unit, one partition):
+// the group's waves copy disjoint 1 KiB chunks of the pair (K and V tiles of
+// both blocks) from global memory straight into an S-slot LDS ring
+// (global_load_lds, no registers), and every wave reads the whole pair from
+// there.  Each pair crosses the L2 -> CU path once per group instead of once
+// per wave, S - 1 pairs are in flight per group, and the registers hold only
+// Q^T, the accumulators and the pair being consumed.
+// Pipeline per pair k: wait until this wave's chunks of pair k have landed
+// (s_waitcnt on the vector-memory counter, which counts the copies in order);
+// barrier (everyone's chunks of pair k are in, and everyone has finished
+// reading slot (k-1) mod S); issue the copies of pair k + S - 1 into that
+// slot; read pair k and attend.  Every iteration issues the same number of
+// copies (past the group's last pair they repeat it into a slot nobody reads)
+// so the wait count is a constant.  The loop count is uniform over the
+// workgroup (the largest partition of its groups); a wave with no columns or
+// no keys left copies and waits but does not attend.  D <= 128.
+template <int D, int NCG, int WT, int S>
+__global__ void __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_prefill_lds_kernel(pf_args a) {
+  constexpr int NC = 16 * NCG;
+  constexpr int kTileVec = 16 * D * 2 / 16;    // 16-byte vectors per K or V tile
+  constexpr int kChunks = 4 * kTileVec / 64;   // 1 KiB chunks per pair: Ka, Kb, Va, Vb
+  constexpr int kMine = kChunks / WT;          // chunks this wave copies
+  constexpr int kGroups = kPfWaves / WT;       // partition groups per workgroup
+  static_assert(kChunks % WT == 0, "chunks split evenly");
+  static_assert(S >= 2 && (S - 2) * kMine <= 63, "the wait count fits the vector-memory counter");
+  const int lane = threadIdx.x & 63;
+  const int quad = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int bid = blockIdx.x;
+  const int pgi = bid % a.part_groups;
+  bid /= a.part_groups;
+  const int tg = bid % a.tile_groups;
+  bid /= a.tile_groups;
+  const int g = bid % a.n_kv_heads;
+  const int s = bid / a.n_kv_heads;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int tw = wave % WT;    // tile within the workgroup
+  const int grp = wave / WT;   // partition group within the workgroup
+  const int tile = tg * WT + tw;
+  const int part = pgi * kGroups + grp;
+
+  // exits taken by the whole workgroup (they depend on s and tg only)
+  const pf_seq sq = pf_locate(a, s);
+  if (sq.c <= 0 || sq.q0 < 0 || sq.q0 + sq.c > a.total_q) return;
+  const int cols = sq.c * G;
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  if (sq.bad) {
+    if (pgi == 0 && tg == 0 && wave == 0)
+      for (int i = lane; i < cols * D; i += 64) {
+        const int f = i / D, e = i % D;
+        out[(static_cast<int64_t>(sq.q0 + f / G) * a.n_q_heads + g * G + f % G) * D + e] = 0x7fc0;
+      }
+    return;
+  }
+  const int n_tiles = (cols + NC - 1) / NC;
+  if (tg * WT >= n_tiles) return;
+  const int P = a.part_blocks * 16;
+  // the workgroup's last tile sees the most keys: its groups load up to there
+  const int kend_wg = pf_tile_keys(a, sq, G, min(tg * WT + WT, n_tiles) - 1, NC);
+  auto group_pairs = [&](int pt) __attribute__((always_inline)) {  // pairs group partition pt loads
+    if (pt >= a.max_parts || pt * P >= kend_wg) return 0;
+    const int nb = ((min(kend_wg, pt * P + P) + 15) >> 4) - ((pt * P) >> 4);
+    return (nb + 1) >> 1;
+  };
+  int n_iter = 0;
+#pragma unroll
+  for (int gg = 0; gg < kGroups; ++gg) n_iter = max(n_iter, group_pairs(pgi * kGroups + gg));
+  if (n_iter == 0) return;
+  const int my_pairs = group_pairs(part);
+  const int b_begin = (part * P) >> 4;
+  const int grp_b_end = my_pairs > 0 ? ((min(kend_wg, part * P + P) + 15) >> 4) : b_begin;
+
+  // this wave's own tile: keys, block range, partition count
+  const bool live_tile = tile < n_tiles && part < a.max_parts;
+  const int kend = live_tile ? pf_tile_keys(a, sq, G, tile, NC) : 0;
+  const bool computes = live_tile && part * P < kend;
+  const int b_end = computes ? ((min(kend, part * P + P) + 15) >> 4) : b_begin;
+  const int n_parts = (kend + P - 1) / P;
+  const int f0 = tile * NC;
+
+  // Q^T operands of the wave's columns, in registers
+  bf16x8_t qreg[NCG][D / 32];
+  int pos[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int f = f0 + cg * 16 + (lane & 15);
+    const bool live = computes && f < cols;
+    const int j = live ? f / G : 0;
+    const int hg = live ? f % G : 0;
+    pos[cg] = live ? (a.causal ? sq.h + j : sq.n - 1) : -1;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<int64_t>(sq.q0 + j) * a.n_q_heads + g * G + hg) * D + quad * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      qreg[cg][kk] = live ? *reinterpret_cast<const bf16x8_t*>(qp + kk * 32) : bf16x8_t{};
+  }
+  const int pos_min = a.causal ? sq.h + f0 / G : sq.n - 1;
+
+  const uint4* kpool = static_cast<const uint4*>(a.k_layer);
+  const uint4* vpool = static_cast<const uint4*>(a.v_layer);
+  // the table row through the constant address space: read-only for the
+  // kernel's lifetime, so its (uniform) entries stay scalar loads even though
+  // the copies into LDS write memory the compiler cannot tell apart from it
+  typedef const __attribute__((address_space(4))) int32_t ctable_t;
+  ctable_t* trow = (ctable_t*)(a.tables + static_cast<int64_t>(a.table_rows ? a.table_rows[s] : s) * a.max_blocks);
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  extern __shared__ __align__(16) u32x4_t pf_kv_lds[];
+  u32x4_t* ring = pf_kv_lds + grp * S * (kChunks * 64);  // this group's S slots
+
+  // copies of pair kp (clamped to the group's last pair; block 0 of the head
+  // for a group with no pair) into slot kp mod S.  Chunk c of a pair: tile
+  // c / (D/32) (0 Ka, 1 Kb, 2 Va, 3 Vb), 1 KiB piece c % (D/32).
+  auto copy_pair = [&](int kp) __attribute__((always_inline)) {
+    int qa = 0, qb = 0;
+    if (my_pairs > 0) {
+      const int b = b_begin + 2 * min(kp, my_pairs - 1);
+      const int pa = trow[min(b, grp_b_end - 1)];
+      const int pb = trow[min(b + 1, grp_b_end - 1)];
+      qa = (pa < 0 || pa >= a.num_blocks) ? 0 : pa;  // never dereferenced out of range
+      qb = (pb < 0 || pb >= a.num_blocks) ? 0 : pb;
+    }
+    const int64_t ta = (static_cast<int64_t>(qa) * a.n_kv_heads + g) * kTileVec;
+    const int64_t tb = (static_cast<int64_t>(qb) * a.n_kv_heads + g) * kTileVec;
+    u32x4_t* slot = ring + (kp % S) * (kChunks * 64);
+#pragma unroll
+    for (int j = 0; j < kMine; ++j) {
+      const int c = tw + j * WT;
+      const int t = c / (D / 32), i = c % (D / 32);
+      const uint4* src = (t < 2 ? kpool : vpool) + ((t & 1) ? tb : ta) + i * 64 + lane;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                       (__attribute__((address_space(3))) void*)(slot + c * 64), 16, 0, 0);
+    }
+  };
+  // s_waitcnt vmcnt(n), the other counters untouched
+  constexpr int kWait = (S - 2) * kMine;
+  constexpr int kVmWait = (kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (15 << 8);
+  constexpr int kVmDrain = (7 << 4) | (15 << 8);
+
+  f32x4_t o[NCG][D / 16];
+  float m_run[NCG], l_lane[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) o[cg][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[cg] = -INFINITY;
+    l_lane[cg] = 0.f;
+  }
+  bool poisoned = false;
+  const float c = a.scale_log2;
+  auto qop = [&](int cg, int kk) __attribute__((always_inline)) { return qreg[cg][kk]; };
+
+#pragma unroll
+  for (int kp = 0; kp < S - 1; ++kp) copy_pair(kp);
+  for (int k = 0; k < n_iter; ++k) {
+    __builtin_amdgcn_s_waitcnt(kVmWait);  // this wave's chunks of pair k have landed
+    __builtin_amdgcn_s_barrier();         // everyone's have; slot (k - 1) mod S is free
+    copy_pair(k + S - 1);
+    const int b = b_begin + 2 * k;
+    const bool mine = b < b_end;
+    kv_pair<D> kv;
+    if (mine) {
+      const u32x4_t* sl = ring + (k % S) * (kChunks * 64);
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        const u32x4_t ka = sl[(0 * (D / 32) + i) * 64 + lane];
+        const u32x4_t kb = sl[(1 * (D / 32) + i) * 64 + lane];
+        const u32x4_t va = sl[(2 * (D / 32) + i) * 64 + lane];
+        const u32x4_t vb = sl[(3 * (D / 32) + i) * 64 + lane];
+        kv.ka[i] = make_uint4(ka[0], ka[1], ka[2], ka[3]);
+        kv.kb[i] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
+        kv.v[2 * i] = make_uint4(va[0], va[1], vb[0], vb[1]);
+        kv.v[2 * i + 1] = make_uint4(va[2], va[3], vb[2], vb[3]);
+      }
+    }
+    if (mine) {
+      const int pa = trow[b];
+      const int pb = trow[min(b + 1, b_end - 1)];
+      const bool has_b = b + 1 < b_end;
+      const bool bad_a = pa < 0 || pa >= a.num_blocks;
+      const bool bad_b = pb < 0 || pb >= a.num_blocks;
+      poisoned |= bad_a || (has_b && bad_b);
+      const int valid_a = bad_a ? 0 : min(16, sq.n - b * 16);
+      const int valid_b = (!has_b || bad_b) ? 0 : min(16, sq.n - (b + 1) * 16);
+      if (valid_a < 16 || valid_b < 16) zero_pair_tail<D>(kv, valid_a, valid_b, quad);
+      if (valid_a == 16 && valid_b == 16 && b * 16 + 31 <= pos_min) {
+        attend_pair<D, NCG, false>(kv, qop, nullptr, nullptr, quad, c, o, m_run, l_lane);
+      } else {
+        int lim_a[NCG], lim_b[NCG];
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
+          lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
+        }
+        attend_pair<D, NCG, true>(kv, qop, lim_a, lim_b, quad, c, o, m_run, l_lane);
+      }
+    }
+  }
+  // the last copies (repeats nobody reads) must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(kVmDrain);
+  if (!computes) return;
 
   const float nan = __builtin_nanf("");
 #pragma unroll
@@ -501,8 +742,9 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
   p.scale = o.scale > 0.f ? o.scale : 1.f / std::sqrt(static_cast<float>(c.head_dim));
   const int64_t cols = static_cast<int64_t>(max_q_len) * G;
-  // two column groups per wave hold 2 x D/4 accumulators: at d = 256 they no longer fit in registers
-  p.ncg = (cols <= 16 || c.head_dim >= 256) ? 1 : 2;
+  // one 16-column group per wave: with the block pairs shared through LDS, a
+  // second group's accumulators would not leave registers for two waves per SIMD
+  p.ncg = 1;
   p.tiles = static_cast<int>((cols + 16 * p.ncg - 1) / (16 * p.ncg));
   p.wt = p.tiles >= 4 ? 4 : (p.tiles >= 2 ? 2 : 1);
   p.tile_groups = (p.tiles + p.wt - 1) / p.wt;
@@ -537,8 +779,36 @@ uint64_t pf_workspace(const kv_pool_config& c, int total_q, int num_q_heads, con
 
 // Ring depth in block pairs: the wider tiles hold more accumulators and fewer
 // blocks in flight.
+// LDS a workgroup may use on the current device.
+size_t max_lds_per_block() {
+  static int bytes = -1;
+  if (bytes < 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || bytes < 0)
+      bytes = 65536;
+  }
+  return static_cast<size_t>(bytes);
+}
+
 template <int D, int NCG>
 hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st) {
+  constexpr size_t kPair = 4 * 16 * D * 2;  // Ka, Kb, Va, Vb
+  // several tiles per partition: share each block pair through LDS; ring
+  // depth 4 pairs for one partition group (64 KiB at d = 128, two workgroups
+  // per CU), 3 for two groups (96 KiB, one workgroup per CU)
+  if constexpr (D <= 128) {
+    if (a.wt == 2 && (kPfWaves / 2) * 3 * kPair <= max_lds_per_block()) {
+      hipLaunchKernelGGL((attn_prefill_lds_kernel<D, NCG, 2, 3>), dim3(static_cast<unsigned>(grid)),
+                         dim3(kPfWaves * 64), (kPfWaves / 2) * 3 * kPair, st, a);
+      return hipGetLastError();
+    }
+    if (a.wt == 4 && (kPfWaves / 4) * 4 * kPair <= max_lds_per_block()) {
+      hipLaunchKernelGGL((attn_prefill_lds_kernel<D, NCG, 4, 4>), dim3(static_cast<unsigned>(grid)),
+                         dim3(kPfWaves * 64), (kPfWaves / 4) * 4 * kPair, st, a);
+      return hipGetLastError();
+    }
+  }
   constexpr int kStages = D >= 256 ? 1 : 2;
   constexpr size_t kLds = static_cast<size_t>(kPfWaves) * NCG * (D / 32) * 64 * 16;  // Q^T operands per wave
   hipLaunchKernelGGL((attn_prefill_kernel<D, NCG, kStages>), dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64),
@@ -549,8 +819,6 @@ hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st) {
 template <int D>
 hipError_t pf_launch_d(const pf_args& a, int ncg, int64_t grid, hipStream_t st) {
   if (ncg == 1) return pf_launch<D, 1>(a, grid, st);
-  if constexpr (D < 256)
-    if (ncg == 2) return pf_launch<D, 2>(a, grid, st);
   return hipErrorInvalidValue;
 }
 
