@@ -153,16 +153,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
-// Byte k of w as a float (one v_cvt_f32_ubyte).
-__device__ __forceinline__ float ubyte_f32(uint32_t w, int k) { return static_cast<float>((w >> (8 * k)) & 0xffu); }
-
-// Four codes held as bytes (code + bias) of word w, times scale s, as floats:
-// value = byte * s - bias * s.
-__device__ __forceinline__ void bytes_to_f32(uint32_t w, float s, float bias_s, float* out) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) out[k] = __builtin_fmaf(ubyte_f32(w, k), s, bias_s);
-}
-
 // Scale of token i (of the lane's 4) and group g, from a [token][group] list of halves.
 template <int D>
 __device__ __forceinline__ float scale_at(const uint32_t* w, int i, int g) {
@@ -170,27 +160,42 @@ __device__ __forceinline__ float scale_at(const uint32_t* w, int i, int g) {
   return (h & 1) ? half_hi(w[h >> 1]) : half_lo(w[h >> 1]);
 }
 
-// The codes of a raw block as the bf16 operand tiles of the decode kernel.
-// Codes are integers of at most 8 bits, exact in bf16; the scales are applied
-// in float32 by the attention step (to the scores for K, to the weights for V).
+// Byte k of w as a signed integer, converted to float (one SDWA conversion).
+__device__ __forceinline__ float sbyte_f32(uint32_t w, int k) {
+  return static_cast<float>(static_cast<signed char>(w >> (8 * k)));
+}
+
+// Value of one code unit in the operand tiles below: q8_0 tiles hold the codes
+// c, q4_0 tiles hold 16 c (a nibble placed in the top of a byte), so the
+// scale applied to a tile's products is s * kCodeUnit.
+template <int FMT>
+constexpr float code_unit() { return FMT == kFmtQ4 ? 1.f / 16.f : 1.f; }
+
+// The codes of a raw block as the bf16 operand tiles of the decode kernel,
+// exact (integers of at most 8 significant bits).  q8_0: each two's-complement
+// byte converts directly.  q4_0: nibbles hold c + 8; flipping their top bit
+// gives c as a 4-bit two's complement, and moving it to the top of a byte
+// gives the signed byte 16 c; the factor 16 goes into the scale (code_unit).
+// The scales themselves are applied in float32 by the attention step.
 template <int D, int FMT>
 __device__ __forceinline__ void codes_block(const kv_qregs<D, FMT>& r, kv_regs<D>& out) {
-  constexpr float bias = FMT == kFmtQ8 ? -128.f : -8.f;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     float v[8];
     if constexpr (FMT == kFmtQ8) {
-      // two's-complement bytes, flipped to code + 128
-      bytes_to_f32(r.kc[2 * kk] ^ 0x80808080u, 1.f, bias, v);
-      bytes_to_f32(r.kc[2 * kk + 1] ^ 0x80808080u, 1.f, bias, v + 4);
-    } else {
-      float lo[4], hi[4];
-      bytes_to_f32(r.kc[kk] & 0x0f0f0f0fu, 1.f, bias, lo);         // j = 0, 2, 4, 6
-      bytes_to_f32((r.kc[kk] >> 4) & 0x0f0f0f0fu, 1.f, bias, hi);  // j = 1, 3, 5, 7
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = lo[i];
-        v[2 * i + 1] = hi[i];
+      for (int k = 0; k < 4; ++k) {
+        v[k] = sbyte_f32(r.kc[2 * kk], k);
+        v[4 + k] = sbyte_f32(r.kc[2 * kk + 1], k);
+      }
+    } else {
+      const uint32_t x = r.kc[kk] ^ 0x88888888u;
+      const uint32_t lo = (x << 4) & 0xf0f0f0f0u;  // j = 0, 2, 4, 6
+      const uint32_t hi = x & 0xf0f0f0f0u;         // j = 1, 3, 5, 7
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = sbyte_f32(lo, k);
+        v[2 * k + 1] = sbyte_f32(hi, k);
       }
     }
     out.k[kk] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
@@ -201,14 +206,14 @@ __device__ __forceinline__ void codes_block(const kv_qregs<D, FMT>& r, kv_regs<D
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
     uint32_t bytes;
-    if constexpr (FMT == kFmtQ8)
-      bytes = r.vc[t] ^ 0x80808080u;
-    else
-      bytes = (t & 1) ? (r.vc[t >> 1] >> 4) & 0x0f0f0f0fu : r.vc[t >> 1] & 0x0f0f0f0fu;
-    float v[4];
-    bytes_to_f32(bytes, 1.f, bias, v);
-    half_words[t][0] = pack_bf16x2(v[0], v[1]);
-    half_words[t][1] = pack_bf16x2(v[2], v[3]);
+    if constexpr (FMT == kFmtQ8) {
+      bytes = r.vc[t];
+    } else {
+      const uint32_t x = r.vc[t >> 1] ^ 0x88888888u;
+      bytes = (t & 1) ? (x & 0xf0f0f0f0u) : ((x << 4) & 0xf0f0f0f0u);
+    }
+    half_words[t][0] = pack_bf16x2(sbyte_f32(bytes, 0), sbyte_f32(bytes, 1));
+    half_words[t][1] = pack_bf16x2(sbyte_f32(bytes, 2), sbyte_f32(bytes, 3));
   }
 #pragma unroll
   for (int pp = 0; pp < D / 32; ++pp)

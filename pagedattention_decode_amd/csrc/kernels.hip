@@ -542,7 +542,7 @@ __device__ __forceinline__ void attend_qblock(const kv_regs<D>& cur, const kv_qr
     const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk],
                                                                f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(scale_at<D>(raw.ks, i, kk), t[i], s[i]);
+    for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(scale_at<D>(raw.ks, i, kk) * code_unit<FMT>(), t[i], s[i]);
   }
   float pv[4];
   softmax_step<D>(s, valid, quad, scale_log2, o, m_run, l_lane, pv);
@@ -553,7 +553,7 @@ __device__ __forceinline__ void attend_qblock(const kv_regs<D>& cur, const kv_qr
   for (int pp = 0; pp < D / 32; ++pp) {
     float w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pv[i] == 0.f ? 0.f : pv[i] * scale_at<D>(raw.vs, i, pp);
+    for (int i = 0; i < 4; ++i) w[i] = pv[i] == 0.f ? 0.f : pv[i] * (scale_at<D>(raw.vs, i, pp) * code_unit<FMT>());
     const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])));
     const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
     o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop, o[2 * pp],
