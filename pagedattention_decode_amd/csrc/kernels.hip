@@ -1066,34 +1066,33 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cascade_args c) {
   auto run_begin = [&](int64_t w) { return w * total / W; };
   const int64_t unit = static_cast<int64_t>(s) * a.n_kv_heads + kvh;
   const int n_suf = static_cast<int>(wL - wF + 1);
-  // entry i < n_pre: prefix partition i; else suffix wave wF + (i - n_pre)
-  auto entry = [&](int i, float& m, float& l, const float*& o) {
+  // entry i < n_pre: prefix partition i; else suffix wave wF + (i - n_pre).
+  // Gives m, l and the entry's row (of pre_o or part_o); a suffix wave with
+  // an empty run wrote nothing and gets m = -inf.
+  auto entry = [&](int i, float& m, float& l, int64_t& row) {
     if (i < n_pre) {
-      const int64_t r = item * c.pre_parts + i;
-      m = c.pre_m[r];
-      l = c.pre_l[r];
-      o = c.pre_o + r * D;
-    } else {
-      const int64_t w = wF + (i - n_pre);
-      if (!(run_begin(w) < run_begin(w + 1))) {  // a wave with an empty run wrote nothing
-        m = -INFINITY;
-        l = 0.f;
-        o = nullptr;
-        return;
-      }
-      const int64_t row = (w + unit) * G + hg;
-      m = a.part_m[row];
-      l = a.part_l[row];
-      o = a.part_o + row * D;
+      row = item * c.pre_parts + i;
+      m = c.pre_m[row];
+      l = c.pre_l[row];
+      return;
     }
+    const int64_t w = wF + (i - n_pre);
+    row = (w + unit) * G + hg;
+    if (!(run_begin(w) < run_begin(w + 1))) {
+      m = -INFINITY;
+      l = 0.f;
+      return;
+    }
+    m = a.part_m[row];
+    l = a.part_l[row];
   };
   const int n_ent = n_pre + n_suf;
   float M = -INFINITY;
   bool nan_seen = nan_row;
   for (int i0 = 0; i0 < n_ent; i0 += 64) {
     float m = -INFINITY, l;
-    const float* o;
-    if (i0 + lane < n_ent) entry(i0 + lane, m, l, o);
+    int64_t row;
+    if (i0 + lane < n_ent) entry(i0 + lane, m, l, row);
     nan_seen |= __builtin_amdgcn_ballot_w64(m != m) != 0;
     M = fmaxf(M, m);
   }
@@ -1104,18 +1103,20 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cascade_args c) {
   for (int i = 0; i < E; ++i) acc[i] = 0.f;
   float L = 0.f;
   for (int i0 = 0; i0 < n_ent; i0 += 64) {
+    // each lane resolves one entry; its weight and row are then broadcast
     float m = -INFINITY, l = 0.f;
-    const float* o = nullptr;
-    if (i0 + lane < n_ent) entry(i0 + lane, m, l, o);
+    int64_t row = 0;
+    if (i0 + lane < n_ent) entry(i0 + lane, m, l, row);
     const float w = (m == -INFINITY || m != m) ? 0.f : exp2f(m - M);
     L += w == 0.f ? 0.f : w * l;
+    const int row_lo = static_cast<int>(row & 0xffffffff), row_hi = static_cast<int>(row >> 32);
     const int cnt = min(64, n_ent - i0);
     for (int k = 0; k < cnt; ++k) {
       const float wk = __shfl(w, k);
       if (wk == 0.f) continue;  // wave uniform
-      float mk, lk;
-      const float* ok;
-      entry(i0 + k, mk, lk, ok);
+      const int64_t rk = (static_cast<int64_t>(__shfl(row_hi, k)) << 32) |
+                         static_cast<uint32_t>(__shfl(row_lo, k));
+      const float* ok = (i0 + k < n_pre ? c.pre_o : a.part_o) + rk * D;
 #pragma unroll
       for (int i = 0; i < E; ++i)
         if (lane + 64 * i < D) acc[i] += wk * ok[lane + 64 * i];
