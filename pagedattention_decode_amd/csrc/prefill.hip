@@ -722,6 +722,31 @@ struct pf_plan {
   float scale;
 };
 
+// LDS of one CU on the current device.
+int64_t max_lds_per_cu() {
+  static int bytes = -1;
+  if (bytes < 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        bytes <= 0)
+      bytes = 65536;
+  }
+  return bytes;
+}
+
+// LDS a workgroup may use on the current device.
+size_t max_lds_per_block() {
+  static int bytes = -1;
+  if (bytes < 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || bytes < 0)
+      bytes = 65536;
+  }
+  return static_cast<size_t>(bytes);
+}
+
 kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len, int num_q_heads, int max_blocks,
                      const kv_attention_options* opts, pf_plan& p) {
   if (!pool) return fail(KV_ERR_INVALID, "pool is NULL");
@@ -752,9 +777,17 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   if (o.partition_tokens > 0) {
     p.partition = o.partition_tokens;
   } else {
-    // enough waves for two per SIMD; otherwise one partition per tile
+    // enough waves to fill the CUs once: the LDS-sharing kernel (several
+    // tiles per partition, d <= 128) runs as many workgroups per CU as its
+    // ring allows, at most two; the register-ring kernel two waves per SIMD.
+    // Beyond that, one partition per tile.
     const int64_t waves = static_cast<int64_t>(n_seqs) * c.num_kv_heads * p.tiles;
-    const int64_t want = 8LL * device_cus();
+    int64_t want = 8LL * device_cus();
+    if (p.wt >= 2 && c.head_dim <= 128) {
+      const int64_t ring = static_cast<int64_t>(kPfWaves / p.wt) * (p.wt == 2 ? 3 : 4) * 4 * 16 * c.head_dim * 2;
+      const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, max_lds_per_cu() / ring));
+      want = kPfWaves * per_cu * device_cus();
+    }
     if (waves >= want) {
       p.partition = static_cast<int>(max_ctx);
     } else {
@@ -779,18 +812,6 @@ uint64_t pf_workspace(const kv_pool_config& c, int total_q, int num_q_heads, con
 
 // Ring depth in block pairs: the wider tiles hold more accumulators and fewer
 // blocks in flight.
-// LDS a workgroup may use on the current device.
-size_t max_lds_per_block() {
-  static int bytes = -1;
-  if (bytes < 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || bytes < 0)
-      bytes = 65536;
-  }
-  return static_cast<size_t>(bytes);
-}
-
 template <int D, int NCG>
 hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st) {
   constexpr size_t kPair = 4 * 16 * D * 2;  // Ka, Kb, Va, Vb
