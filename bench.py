@@ -312,6 +312,7 @@ def main():
         "attn_tokens_per_s_per_layer": round(tok_per_s_layer, 1),
         "attn_kernel_tokens_per_s_per_layer": round(S / attn_avg_s, 1),
         "attn_call_us": round(attn_avg_s * 1e6, 2),
+        "attn_call_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
         "unique_kv_bytes_per_launch": unique_kv_bytes,
         "cow_copies": n_copies[0],
         "fill_seconds": round(t_fill, 2),
@@ -330,6 +331,10 @@ def main():
         },
         "cpu_baseline": None,
     }
+    traffic = result["roofline"]["traffic"]
+    if traffic:
+        # HBM bytes the counters saw per call, against the algorithmic bytes
+        result["roofline"]["traffic_over_algorithmic"] = round(traffic / ideal_per_launch, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(result), flush=True)
@@ -452,6 +457,7 @@ def multi_query_bench(args):
             "step": f"{L} x (reshape_and_cache of the chunk + paged_attention_prefill)",
         },
         "attn_call_us": round(attn_s * 1e6, 2),
+        "attn_call_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
         "chunk_tokens_per_s_per_layer": round(total_q / attn_s, 1),
         "query_key_pairs_per_head": pairs,
         "fill_seconds": round(t_fill, 2),
