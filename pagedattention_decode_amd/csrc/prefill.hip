@@ -97,25 +97,24 @@ __device__ __forceinline__ void load_pair(kv_pair<D>& r, const uint4* kta, const
   }
 }
 
-// Zeroes the V values of slots >= valid_a of the first block and >= valid_b
-// of the second (memory past the context may hold anything).
-template <int D>
-__device__ __forceinline__ void zero_pair_tail(kv_pair<D>& r, int valid_a, int valid_b, int quad) {
-  uint32_t ma[2], mb[2];
+// Masks that keep the V values of slots < valid_a of the first block and
+// < valid_b of the second in a V operand (dwords 0-1: the lane's 4 slots of
+// the first block, 2-3: of the second); memory past the context may hold
+// anything.
+struct v_tail_mask {
+  uint32_t a[2], b[2];
+  __device__ __forceinline__ v_tail_mask(int valid_a, int valid_b, int quad) {
 #pragma unroll
-  for (int dw = 0; dw < 2; ++dw) {
-    const int slot0 = quad * 4 + dw * 2;
-    ma[dw] = (slot0 < valid_a ? 0x0000ffffu : 0u) | (slot0 + 1 < valid_a ? 0xffff0000u : 0u);
-    mb[dw] = (slot0 < valid_b ? 0x0000ffffu : 0u) | (slot0 + 1 < valid_b ? 0xffff0000u : 0u);
+    for (int dw = 0; dw < 2; ++dw) {
+      const int slot0 = quad * 4 + dw * 2;
+      a[dw] = (slot0 < valid_a ? 0x0000ffffu : 0u) | (slot0 + 1 < valid_a ? 0xffff0000u : 0u);
+      b[dw] = (slot0 < valid_b ? 0x0000ffffu : 0u) | (slot0 + 1 < valid_b ? 0xffff0000u : 0u);
+    }
   }
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    r.v[t].x &= ma[0];
-    r.v[t].y &= ma[1];
-    r.v[t].z &= mb[0];
-    r.v[t].w &= mb[1];
+  __device__ __forceinline__ uint4 apply(uint4 v) const {
+    return make_uint4(v.x & a[0], v.y & a[1], v.z & b[0], v.w & b[1]);
   }
-}
+};
 
 // Two consecutive 16-token blocks (32 tokens) for all NCG 16-column groups.
 //   1. S^T of both blocks for every group: 2 * NCG independent chains of
@@ -134,9 +133,13 @@ __device__ __forceinline__ void zero_pair_tail(kv_pair<D>& r, int valid_a, int v
 // slots of each block visible to the lane's column; otherwise every slot of
 // both blocks is visible to every column.  V tails beyond the context are
 // already zero.
-// qop(cg, kk) gives the Q^T operand of column group cg, k-step kk.
-template <int D, int NCG, bool MASKED, class QOp>
-__device__ __forceinline__ void attend_pair(const kv_pair<D>& kv, const QOp& qop, const int* lim_a,
+// The operands come from callbacks, so that a caller holding the pair in LDS
+// reads each piece only when its matrix instructions need it:
+//   qop(cg, kk)        the Q^T operand of column group cg, k-step kk;
+//   kop(kk, ka, kb)    the K operands of k-step kk of both blocks;
+//   vop(pp, v0, v1)    the V operands of d-tiles 2 pp and 2 pp + 1 (tails masked).
+template <int D, int NCG, bool MASKED, class QOp, class KOp, class VOp>
+__device__ __forceinline__ void attend_pair(const QOp& qop, const KOp& kop, const VOp& vop, const int* lim_a,
                                             const int* lim_b, int quad, float c, f32x4_t (&o)[NCG][D / 16],
                                             float* m_run, float* l_lane) {
   f32x4_t sa[NCG], sb[NCG];
@@ -144,11 +147,16 @@ __device__ __forceinline__ void attend_pair(const kv_pair<D>& kv, const QOp& qop
   for (int cg = 0; cg < NCG; ++cg) {
     sa[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     sb[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
+  for (int kk = 0; kk < D / 32; ++kk) {
+    uint4 ka, kb;
+    kop(kk, ka, kb);
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
       const bf16x8_t qk = qop(cg, kk);
-      sa[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.ka[kk]), qk, sa[cg], 0, 0, 0);
-      sb[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.kb[kk]), qk, sb[cg], 0, 0, 0);
+      sa[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qk, sa[cg], 0, 0, 0);
+      sb[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qk, sb[cg], 0, 0, 0);
     }
   }
   float mb[NCG];
@@ -204,11 +212,16 @@ __device__ __forceinline__ void attend_pair(const kv_pair<D>& kv, const QOp& qop
                                                       __builtin_bit_cast(uint32_t, p3)));
   }
 #pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
+  for (int pp = 0; pp < D / 32; ++pp) {
+    uint4 v0, v1;
+    vop(pp, v0, v1);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      o[cg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv.v[t]), pop[cg], o[cg][t], 0,
-                                                         0, 0);
+    for (int cg = 0; cg < NCG; ++cg) {
+      o[cg][2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v0), pop[cg],
+                                                              o[cg][2 * pp], 0, 0, 0);
+      o[cg][2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v1), pop[cg],
+                                                                  o[cg][2 * pp + 1], 0, 0, 0);
+    }
   }
 }
 
@@ -347,10 +360,18 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
         poisoned |= bad_a || (has_b && bad_b);
         const int valid_a = bad_a ? 0 : min(16, sq.n - b * 16);
         const int valid_b = (!has_b || bad_b) ? 0 : min(16, sq.n - (b + 1) * 16);
-        if (valid_a < 16 || valid_b < 16) zero_pair_tail<D>(buf[u], valid_a, valid_b, quad);
+        const v_tail_mask vm(valid_a, valid_b, quad);
         auto qop = [&](int cg, int kk) { return q_lds[(cg * (D / 32) + kk) * 64 + ql]; };
+        auto kop = [&](int kk, uint4& ka, uint4& kb) {
+          ka = buf[u].ka[kk];
+          kb = buf[u].kb[kk];
+        };
+        auto vop = [&](int pp, uint4& v0, uint4& v1) {
+          v0 = vm.apply(buf[u].v[2 * pp]);
+          v1 = vm.apply(buf[u].v[2 * pp + 1]);
+        };
         if (valid_a == 16 && valid_b == 16 && b * 16 + 31 <= pos_min) {
-          attend_pair<D, NCG, false>(buf[u], qop, nullptr, nullptr, quad, c, o, m_run, l_lane);
+          attend_pair<D, NCG, false>(qop, kop, vop, nullptr, nullptr, quad, c, o, m_run, l_lane);
         } else {
           int lim_a[NCG], lim_b[NCG];
 #pragma unroll
@@ -358,7 +379,7 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
             lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
             lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
           }
-          attend_pair<D, NCG, true>(buf[u], qop, lim_a, lim_b, quad, c, o, m_run, l_lane);
+          attend_pair<D, NCG, true>(qop, kop, vop, lim_a, lim_b, quad, c, o, m_run, l_lane);
         }
       }
       issue(u, b + 2 * STAGES);
@@ -562,22 +583,8 @@ attn_prefill_lds_kernel(pf_args a) {
     copy_pair(k + S - 1);
     const int b = b_begin + 2 * k;
     const bool mine = b < b_end;
-    kv_pair<D> kv;
     if (mine) {
       const u32x4_t* sl = ring + (k % S) * (kChunks * 64);
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        const u32x4_t ka = sl[(0 * (D / 32) + i) * 64 + lane];
-        const u32x4_t kb = sl[(1 * (D / 32) + i) * 64 + lane];
-        const u32x4_t va = sl[(2 * (D / 32) + i) * 64 + lane];
-        const u32x4_t vb = sl[(3 * (D / 32) + i) * 64 + lane];
-        kv.ka[i] = make_uint4(ka[0], ka[1], ka[2], ka[3]);
-        kv.kb[i] = make_uint4(kb[0], kb[1], kb[2], kb[3]);
-        kv.v[2 * i] = make_uint4(va[0], va[1], vb[0], vb[1]);
-        kv.v[2 * i + 1] = make_uint4(va[2], va[3], vb[2], vb[3]);
-      }
-    }
-    if (mine) {
       const int pa = trow[b];
       const int pb = trow[min(b + 1, b_end - 1)];
       const bool has_b = b + 1 < b_end;
@@ -586,9 +593,22 @@ attn_prefill_lds_kernel(pf_args a) {
       poisoned |= bad_a || (has_b && bad_b);
       const int valid_a = bad_a ? 0 : min(16, sq.n - b * 16);
       const int valid_b = (!has_b || bad_b) ? 0 : min(16, sq.n - (b + 1) * 16);
-      if (valid_a < 16 || valid_b < 16) zero_pair_tail<D>(kv, valid_a, valid_b, quad);
+      const v_tail_mask vm(valid_a, valid_b, quad);
+      // operands read from the slot when the matrix instructions need them
+      auto kop = [&](int kk, uint4& ka, uint4& kb) __attribute__((always_inline)) {
+        const u32x4_t x = sl[(0 * (D / 32) + kk) * 64 + lane];
+        const u32x4_t y = sl[(1 * (D / 32) + kk) * 64 + lane];
+        ka = make_uint4(x[0], x[1], x[2], x[3]);
+        kb = make_uint4(y[0], y[1], y[2], y[3]);
+      };
+      auto vop = [&](int pp, uint4& v0, uint4& v1) __attribute__((always_inline)) {
+        const u32x4_t va = sl[(2 * (D / 32) + pp) * 64 + lane];
+        const u32x4_t vb = sl[(3 * (D / 32) + pp) * 64 + lane];
+        v0 = vm.apply(make_uint4(va[0], va[1], vb[0], vb[1]));
+        v1 = vm.apply(make_uint4(va[2], va[3], vb[2], vb[3]));
+      };
       if (valid_a == 16 && valid_b == 16 && b * 16 + 31 <= pos_min) {
-        attend_pair<D, NCG, false>(kv, qop, nullptr, nullptr, quad, c, o, m_run, l_lane);
+        attend_pair<D, NCG, false>(qop, kop, vop, nullptr, nullptr, quad, c, o, m_run, l_lane);
       } else {
         int lim_a[NCG], lim_b[NCG];
 #pragma unroll
@@ -596,7 +616,7 @@ attn_prefill_lds_kernel(pf_args a) {
           lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
           lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
         }
-        attend_pair<D, NCG, true>(kv, qop, lim_a, lim_b, quad, c, o, m_run, l_lane);
+        attend_pair<D, NCG, true>(qop, kop, vop, lim_a, lim_b, quad, c, o, m_run, l_lane);
       }
     }
   }
@@ -767,9 +787,10 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
   p.scale = o.scale > 0.f ? o.scale : 1.f / std::sqrt(static_cast<float>(c.head_dim));
   const int64_t cols = static_cast<int64_t>(max_q_len) * G;
-  // one 16-column group per wave: with the block pairs shared through LDS, a
-  // second group's accumulators would not leave registers for two waves per SIMD
-  p.ncg = 1;
+  // 16-column groups per wave: two when there are enough columns for several
+  // two-group tiles (the LDS-sharing kernel then reads each pair from LDS once
+  // per 32 columns instead of 16); one otherwise, and at d = 256
+  p.ncg = (c.head_dim <= 128 && cols > 64) ? 2 : 1;
   p.tiles = static_cast<int>((cols + 16 * p.ncg - 1) / (16 * p.ncg));
   p.wt = p.tiles >= 4 ? 4 : (p.tiles >= 2 ? 2 : 1);
   p.tile_groups = (p.tiles + p.wt - 1) / p.wt;
@@ -840,6 +861,8 @@ hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st) {
 template <int D>
 hipError_t pf_launch_d(const pf_args& a, int ncg, int64_t grid, hipStream_t st) {
   if (ncg == 1) return pf_launch<D, 1>(a, grid, st);
+  if constexpr (D <= 128)
+    if (ncg == 2) return pf_launch<D, 2>(a, grid, st);
   return hipErrorInvalidValue;
 }
 
