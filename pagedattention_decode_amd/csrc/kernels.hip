@@ -974,35 +974,40 @@ __global__ void __launch_bounds__(kMergeItems * 64) merge_sk_kernel(sk_args a) {
 // cascade_merge folds both kinds of partials into the output row.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int group_of(const int32_t* __restrict__ group_start, int n_groups, int s) {
-  int lo = 0, hi = n_groups - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (group_start[mid] <= s) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// One workgroup per sequence: checks the member against its group (the shared
-// entries equal the first member's, both contexts cover them), then writes the
-// suffix table row, the suffix length and the member's verdict; the group's
-// first member writes the prefix length.
+// One workgroup per sequence: finds the member's group (one pass over
+// group_start by the workgroup's threads, not a chain of dependent loads),
+// checks the member against it (the shared entries equal the first member's,
+// both contexts cover them, the group fits max_group), then writes the suffix
+// table row, the suffix length and the member's record for the merge
+// (NaN-row flag, prefix tokens); the group's first member writes the prefix
+// length for the prefix phase.
 __global__ void __launch_bounds__(256) cascade_prep_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ ctx, const int32_t* __restrict__ group_start,
-    const int32_t* __restrict__ shared, int n_seqs, int n_groups, int max_blocks, int32_t* __restrict__ tables_sfx,
-    int32_t* __restrict__ ctx_sfx, int32_t* __restrict__ prefix_ctx, int32_t* __restrict__ bad) {
+    const int32_t* __restrict__ shared, int n_seqs, int n_groups, int max_group, int max_blocks,
+    int32_t* __restrict__ tables_sfx, int32_t* __restrict__ ctx_sfx, int32_t* __restrict__ prefix_ctx,
+    int2* __restrict__ info) {
+  __shared__ int grp;  // the member's group
   __shared__ int mismatch;
   const int s = blockIdx.x;
-  const int g = group_of(group_start, n_groups, s);
-  const int first = group_start[g];
-  const int skip = shared[g];
+  if (threadIdx.x == 0) {
+    grp = -1;
+    mismatch = 0;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n_groups; t += blockDim.x)
+    if (group_start[t] <= s && s < group_start[t + 1]) atomicMax(&grp, t);  // one match when well formed
+  __syncthreads();
+  const int g = grp;
+  const int first = g >= 0 ? group_start[g] : -1;
+  const int end = g >= 0 ? group_start[g + 1] : -1;
+  const bool in_group = g >= 0 && first >= 0 && first <= s && s < end;
+  const int skip = in_group ? shared[g] : 0;
   const int n = min(ctx[s], max_blocks * 16);
   // the first member's context must cover the prefix too: it alone sets the
   // prefix length, and every member reads the prefix through its table row
-  bool ok = first >= 0 && first <= s && s < group_start[g + 1] && skip >= 0 && skip <= max_blocks &&
-            16 * skip <= max(n, 0) && 16 * skip <= max(min(ctx[first], max_blocks * 16), 0);
-  if (threadIdx.x == 0) mismatch = 0;
-  __syncthreads();
+  const bool group_ok = in_group && skip >= 0 && skip <= max_blocks &&
+                        16 * skip <= max(min(ctx[first], max_blocks * 16), 0) && end - first <= max_group;
+  bool ok = group_ok && 16 * skip <= max(n, 0);
   if (ok)
     for (int j = threadIdx.x; j < skip; j += blockDim.x)
       if (tables[static_cast<int64_t>(s) * max_blocks + j] != tables[static_cast<int64_t>(first) * max_blocks + j])
@@ -1015,21 +1020,18 @@ __global__ void __launch_bounds__(256) cascade_prep_kernel(
         (ok && j + shift < max_blocks) ? tables[static_cast<int64_t>(s) * max_blocks + j + shift] : -1;
   if (threadIdx.x == 0) {
     ctx_sfx[s] = ok ? n - 16 * skip : 0;
-    bad[s] = ok ? 0 : 1;
-    if (s == first) prefix_ctx[g] = ok ? 16 * skip : 0;
+    info[s] = make_int2(ok ? 0 : 1, group_ok ? 16 * skip : 0);
+    if (in_group && s == first) prefix_ctx[g] = group_ok ? 16 * skip : 0;
   }
 }
 
 struct cascade_args {
-  sk_args sfx;                 // the suffix decode (cum_parts, slots, n_waves)
-  const int32_t* group_start;  // [n_groups + 1]
-  const int32_t* prefix_ctx;   // [n_groups] tokens of the shared prefix
-  const int32_t* bad;          // [n_seqs]
-  const int32_t* ctx;          // [n_seqs] full contexts
-  const float* pre_m;          // prefix partials [n_seqs * Hq][pre_parts]
+  sk_args sfx;         // the suffix decode (cum_parts, slots, n_waves)
+  const int2* info;    // [n_seqs]: NaN-row flag, prefix tokens
+  const float* pre_m;  // prefix partials [n_seqs * Hq][pre_parts]
   const float* pre_l;
-  const float* pre_o;          // [..][D]
-  int n_groups, max_group, pre_part_tokens, pre_parts;
+  const float* pre_o;  // [..][D]
+  int pre_part_tokens, pre_parts;
 };
 
 // One wave per (sequence, query head): the prefix partitions and the suffix
@@ -1049,9 +1051,9 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cascade_args c) {
   const int kvh = head / G, hg = head % G;
   uint16_t* orow = static_cast<uint16_t*>(a.out) + item * D;
   constexpr int E = (D + 63) / 64;
-  const int g = group_of(c.group_start, c.n_groups, s);
-  const bool nan_row = c.bad[s] != 0 || c.group_start[g + 1] - c.group_start[g] > c.max_group;
-  const int pre_tokens = c.prefix_ctx[g];
+  const int2 inf = c.info[s];
+  const bool nan_row = inf.x != 0;
+  const int pre_tokens = inf.y;
   const int n_pre = pre_tokens > 0 ? (pre_tokens + c.pre_part_tokens - 1) / c.pre_part_tokens : 0;
   // suffix runs: waves wF..wL of unit (s, kvh), as the split-K merge finds them
   const int np = a.cum_parts[s + 1] - a.cum_parts[s];
@@ -1575,7 +1577,7 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
 namespace {
 
 struct cascade_layout {
-  uint64_t decode, tables, ctx, prefix_ctx, bad, pre, total;
+  uint64_t decode, tables, ctx, prefix_ctx, info, pre, total;
   int pre_part_tokens, pre_parts;
 };
 
@@ -1594,8 +1596,8 @@ kv_status cascade_plan(kv_pool* pool, int n_seqs, int n_groups, int max_group, i
   L.tables = L.decode;
   L.ctx = L.tables + up256(static_cast<uint64_t>(n_seqs) * max_blocks * 4);
   L.prefix_ctx = L.ctx + up256(static_cast<uint64_t>(n_seqs) * 4);
-  L.bad = L.prefix_ctx + up256(static_cast<uint64_t>(n_groups) * 4);
-  L.pre = L.bad + up256(static_cast<uint64_t>(n_seqs) * 4);
+  L.info = L.prefix_ctx + up256(static_cast<uint64_t>(n_groups) * 4);
+  L.pre = L.info + up256(static_cast<uint64_t>(n_seqs) * 8);
   L.total = L.pre + up256(pre_bytes);
   return KV_OK;
 }
@@ -1639,10 +1641,10 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   int32_t* tables_sfx = reinterpret_cast<int32_t*>(ws + L.tables);
   int32_t* ctx_sfx = reinterpret_cast<int32_t*>(ws + L.ctx);
   int32_t* prefix_ctx = reinterpret_cast<int32_t*>(ws + L.prefix_ctx);
-  int32_t* bad = reinterpret_cast<int32_t*>(ws + L.bad);
+  int2* info = reinterpret_cast<int2*>(ws + L.info);
   hipLaunchKernelGGL(cascade_prep_kernel, dim3(static_cast<unsigned>(n_seqs)), dim3(256), 0, st, d_block_tables,
-                     d_context_lens, d_group_start, d_shared_blocks, n_seqs, n_groups, max_blocks_per_seq,
-                     tables_sfx, ctx_sfx, prefix_ctx, bad);
+                     d_context_lens, d_group_start, d_shared_blocks, n_seqs, n_groups, max_group, max_blocks_per_seq,
+                     tables_sfx, ctx_sfx, prefix_ctx, info);
   if (kv_status s = hip_check(hipGetLastError(), "cascade prep launch")) return s;
   // prefix: every group's shared blocks, once, for all members
   if (kv_status s = prefix_phase_launch(pool, layer, q, out, d_group_start, prefix_ctx, d_block_tables, n_groups,
@@ -1680,16 +1682,11 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   if (kv_status s = hip_check(e, "cascade suffix launch")) return s;
   cascade_args m{};
   m.sfx = a;
-  m.group_start = d_group_start;
-  m.prefix_ctx = prefix_ctx;
-  m.bad = bad;
-  m.ctx = d_context_lens;
+  m.info = info;
   const uint64_t pre_rows = static_cast<uint64_t>(n_seqs) * num_q_heads * L.pre_parts;
   m.pre_m = reinterpret_cast<const float*>(ws + L.pre);
   m.pre_l = reinterpret_cast<const float*>(ws + L.pre + up256(pre_rows * 4));
   m.pre_o = reinterpret_cast<const float*>(ws + L.pre + 2 * up256(pre_rows * 4));
-  m.n_groups = n_groups;
-  m.max_group = max_group;
   m.pre_part_tokens = L.pre_part_tokens;
   m.pre_parts = L.pre_parts;
   const int64_t items = static_cast<int64_t>(n_seqs) * num_q_heads;
