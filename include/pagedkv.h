@@ -363,8 +363,10 @@ typedef enum {
   KV_KERNEL_GENERIC = 1, /* vector-ALU kernel: f32 or bf16, any B, d; G <= 16 */
   KV_KERNEL_MFMA = 2     /* bf16, q8_0 or q4_0, B = 16, d in {64, 128, 256},
                             G <= 16, at most 4095 sequences per call; the only
-                            kernel for quantised pools (codes are dequantised
-                            to bf16 operands in registers) */
+                            kernel for quantised pools (the codes, exact in bf16,
+                            are the matrix operands and the group scales are
+                            applied in float32: the result is the attention over
+                            code x scale) */
 } kv_kernel;
 
 typedef struct {

@@ -724,7 +724,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     c.n = min(ctx_lens[c.seq], cap);
   };
 
-  // ring entries: bf16 operand tiles, or raw quantised tiles dequantised on use
+  // ring entries: bf16 operand tiles, or raw quantised tiles (codes and scales) converted on use
   using ring_t = typename std::conditional<FMT == kFmtBf16, kv_regs<D>, kv_qregs<D, FMT>>::type;
   const uint4* kpool = static_cast<const uint4*>(a.k_layer);
   const uint4* vpool = static_cast<const uint4*>(a.v_layer);
@@ -1274,9 +1274,9 @@ constexpr int fmt_of(int32_t dtype) { return dtype == KV_Q8_0 ? kFmtQ8 : (dtype 
 
 // Waves per SIMD and register-ring depth (blocks in flight per wave).  bf16:
 // one wave per SIMD with a deep ring (the waves of one SIMD are issued oldest
-// first, so two waves with equal shares finish far apart).  Quantised: the
-// dequantisation is vector-ALU work that one wave cannot overlap with its own
-// loads; two waves per SIMD with a shorter ring measured 1.25-1.4x faster.
+// first, so two waves with equal shares finish far apart).  Quantised: code
+// conversion and scaling are vector-ALU work that one wave cannot overlap with
+// its own loads; two waves per SIMD with a shorter ring measured 1.25-1.4x faster.
 constexpr int sk_waves_per_simd(int D, int fmt) { return fmt != kFmtBf16 && D < 256 ? 2 : 1; }
 
 template <int D, int FMT>
