@@ -35,6 +35,7 @@ Prints one JSON line (rank 0, one GPU).
 """
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -46,6 +47,19 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, public specification
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, public specification
+
+
+class no_gc:
+    """Python's cyclic garbage collector paused for a timed region (a full
+    collection over torch's object graph takes tens of milliseconds and would
+    land inside some step at random); one collection runs just before."""
+
+    def __enter__(self):
+        gc.collect()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        gc.enable()
 
 
 def parse():
@@ -254,13 +268,14 @@ def main():
 
     for i in range(args.warmup):
         step(i, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     lens_hist = []
-    for i in range(args.warmup, total_steps):
-        lens_hist.append(step(i, True))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warmup, total_steps):
+            lens_hist.append(step(i, True))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     wall = t1 - t0
     ms_step = wall / args.steps * 1e3
 
@@ -417,12 +432,13 @@ def multi_query_bench(args):
 
     for i in range(args.warmup):
         step(i, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.warmup, total_steps):
-        step(i, True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.warmup, total_steps):
+            step(i, True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     attn_name = "paged_attention_decode_cascade" if args.cascade else "paged_attention_decode"
     attn_ms = [a.elapsed_time(b) for a, b in attn_ev]
     attn_s = float(np.mean(attn_ms)) / 1e3
@@ -588,11 +604,12 @@ def swap_bench(args):
 
     for _ in range(args.warmup):
         step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs = [step(True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs = [step(True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     out_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     in_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     pool.check()

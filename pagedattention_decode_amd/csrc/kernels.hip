@@ -598,22 +598,24 @@ struct sk_args {
   int force_partial;  // every unit ends in partials (the cascade merge folds them with a prefix)
 };
 
-__device__ __forceinline__ int blocks_of(const int32_t* __restrict__ ctx_lens, int s, int cap) {
-  const int n = min(ctx_lens[s], cap);
-  return n > 0 ? (n + 15) >> 4 : 0;
-}
+// LDS ints before the staged queries: cum_b, cum_p (n + 1 each) and ctx_n
+// (n), rounded up to 16 bytes.
+__host__ __device__ constexpr int sk_prefix_ints(int n_seqs) { return (3 * n_seqs + 2 + 3) & ~3; }
+
 
 // Exclusive prefix sums, over sequences, of blocks (cum_b) and partitions
-// (cum_p); a workgroup-wide scan in LDS.
+// (cum_p), and the clamped context lengths (ctx_n); a workgroup-wide scan in
+// LDS, so that the kernel reads the lengths from global memory once.
 __device__ __forceinline__ void sk_prefix(const sk_args& a, const int32_t* __restrict__ ctx_lens, int* cum_b,
-                                          int* cum_p) {
+                                          int* cum_p, int* ctx_n) {
   __shared__ int wsum_b[kSkWaves], wsum_p[kSkWaves];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int cap = a.max_blocks * 16;
   int carry_b = 0, carry_p = 0;
   for (int base = 0; base < a.n_seqs; base += kSkWaves * 64) {
     const int s = base + tid;
-    const int nb = s < a.n_seqs ? blocks_of(ctx_lens, s, cap) : 0;
+    const int n = s < a.n_seqs ? min(ctx_lens[s], cap) : 0;
+    const int nb = n > 0 ? (n + 15) >> 4 : 0;
     const int np = (nb + a.part_blocks - 1) / a.part_blocks;
     int ib = nb, ip = np;
 #pragma unroll
@@ -637,6 +639,7 @@ __device__ __forceinline__ void sk_prefix(const sk_args& a, const int32_t* __res
     if (s < a.n_seqs) {
       cum_b[s] = before_b + ib - nb;
       cum_p[s] = before_p + ip - np;
+      ctx_n[s] = n;
     }
     for (int i = 0; i < kSkWaves; ++i) {
       carry_b += wsum_b[i];
@@ -661,24 +664,26 @@ template <int D, int STAGES, int WAVES_PER_SIMD, int FMT>
 __global__ void __launch_bounds__(kSkWaves * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD)))
 attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ tables) {
   extern __shared__ __align__(16) int sk_smem[];
-  int* cum_b = sk_smem;                 // n_seqs + 1
-  int* cum_p = sk_smem + a.n_seqs + 1;  // n_seqs + 1
+  int* cum_b = sk_smem;                       // n_seqs + 1
+  int* cum_p = sk_smem + a.n_seqs + 1;        // n_seqs + 1
+  int* ctx_n = sk_smem + 2 * (a.n_seqs + 1);  // n_seqs
   const int G = a.n_q_heads / a.n_kv_heads;
   const int Hkv = a.n_kv_heads;
-  uint16_t* q_s = reinterpret_cast<uint16_t*>(sk_smem + ((2 * (a.n_seqs + 1) + 3) & ~3));  // [waves][q_units][G][D]
+  uint16_t* q_s = reinterpret_cast<uint16_t*>(sk_smem + sk_prefix_ints(a.n_seqs));  // [waves][q_units][G][D]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = (lane & 15) % G;  // query head (within the group) of this lane's column
   const int quad = lane >> 4;      // 4-token group / 8-dim group of this lane
   const int cap = a.max_blocks * 16;
 
-  sk_prefix(a, ctx_lens, cum_b, cum_p);
+  sk_prefix(a, ctx_lens, cum_b, cum_p, ctx_n);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= a.n_seqs; i += kSkWaves * 64) a.cum_parts[i] = cum_p[i];
   // prefix entries are read at wave-uniform addresses; keep them scalar so that
   // every branch below is a scalar branch
   auto cb = [&](int s) { return __builtin_amdgcn_readfirstlane(cum_b[s]); };
   auto cp = [&](int s) { return __builtin_amdgcn_readfirstlane(cum_p[s]); };
+  auto cn = [&](int s) { return __builtin_amdgcn_readfirstlane(ctx_n[s]); };
 
   // this wave's run of partitions
   const int64_t total_parts = static_cast<int64_t>(Hkv) * cp(a.n_seqs);
@@ -687,20 +692,26 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
   const int64_t p_end = (wid + 1) * total_parts / a.n_waves;
   if (p_begin >= p_end) return;
 
-  // partition index -> (sequence, kv head, first block)
+  // partition index -> (sequence, kv head, first block).  The sequence is the
+  // last one whose first partition is <= pp: the lanes test 64 sequences at a
+  // time and count the passes (the test holds for a prefix of the sequences).
   auto locate = [&](int64_t pp, sk_cursor& c) {
-    int lo = 0, hi = a.n_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (static_cast<int64_t>(Hkv) * cp(mid) <= pp) lo = mid; else hi = mid - 1;
+    int passed = 0;
+    for (int base = 0; base < a.n_seqs; base += 64) {
+      const int s = base + lane;
+      const bool ok = s < a.n_seqs && static_cast<int64_t>(Hkv) * cum_p[s] <= pp;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+      passed += __builtin_popcountll(m);
+      if (m != ~0ull) break;
     }
+    const int lo = max(passed - 1, 0);
     c.seq = lo;
     const int np = cp(lo + 1) - cp(lo);
     const int64_t r = pp - static_cast<int64_t>(Hkv) * cp(lo);
     c.kvh = static_cast<int>(r / np);
     c.j = static_cast<int>(r % np) * a.part_blocks;
     c.nb = cb(lo + 1) - cb(lo);
-    c.n = min(ctx_lens[lo], cap);
+    c.n = cn(lo);
   };
   sk_cursor first, last;
   locate(p_begin, first);
@@ -721,7 +732,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
       ++c.seq;
     } while (c.seq < a.n_seqs - 1 && cb(c.seq + 1) == cb(c.seq));
     c.nb = cb(c.seq + 1) - cb(c.seq);
-    c.n = min(ctx_lens[c.seq], cap);
+    c.n = cn(c.seq);
   };
 
   // ring entries: bf16 operand tiles, or raw quantised tiles (codes and scales) converted on use
@@ -885,6 +896,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
 // of partial p (64 at a time) and every lane then accumulates its D/64 dims
 // over the partials, four row loads in flight.
 constexpr int kMergeItems = 4;
+constexpr int kMergeFast = 8;  // partials per item loaded all at once
 
 template <int D>
 __global__ void __launch_bounds__(kMergeItems * 64) merge_sk_kernel(sk_args a) {
@@ -914,6 +926,50 @@ __global__ void __launch_bounds__(kMergeItems * 64) merge_sk_kernel(sk_args a) {
   const int64_t unit = static_cast<int64_t>(seq) * a.n_kv_heads + kvh;
   auto row_of = [&](int i) { return (wF + i + unit) * G + hg; };
   auto live = [&](int i) { return run_begin(wF + i) < run_begin(wF + i + 1); };
+  auto load_row = [&](int i, float (&v)[E]) {
+    const float* o = a.part_o + row_of(i) * D + lane * E;
+    if constexpr (E == 4) {
+      const float4 t = *reinterpret_cast<const float4*>(o);
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else if constexpr (E == 2) {
+      const float2 t = *reinterpret_cast<const float2*>(o);
+      v[0] = t.x; v[1] = t.y;
+    } else {
+      v[0] = o[0];
+    }
+  };
+  if (n_w <= kMergeFast) {
+    // few partials (the usual case): every load of the item is issued at
+    // once -- each lane's (m, l) and all rows -- so the merge waits out one
+    // memory latency after the prefix read
+    float m = -INFINITY, l = 0.f;
+    if (lane < n_w && live(lane)) {
+      m = a.part_m[row_of(lane)];
+      l = a.part_l[row_of(lane)];
+    }
+    float v[kMergeFast][E];
+#pragma unroll
+    for (int k = 0; k < kMergeFast; ++k)
+      if (k < n_w && live(k)) load_row(k, v[k]);
+    const bool nan = __builtin_amdgcn_ballot_w64(m != m) != 0;
+    const float M = wave_max(m != m ? -INFINITY : m);
+    const float w = (m != m) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    const float L = wave_sum(w * l);
+    float acc[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeFast; ++k) {
+      const float wk = __shfl(w, k);
+      if (k < n_w && wk != 0.f)
+#pragma unroll
+        for (int j = 0; j < E; ++j) acc[j] = __builtin_fmaf(wk, v[k][j], acc[j]);
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int j = 0; j < E; ++j) out[j] = nan ? static_cast<uint16_t>(0x7fc0) : f32_to_bf16(acc[j] * inv);
+    return;
+  }
   float M = -INFINITY;
   bool nan = false;
   for (int i = lane; i < n_w; i += 64)
@@ -1240,6 +1296,18 @@ int device_cus() {
   return cus;
 }
 
+// LDS a workgroup may use on the current device.
+size_t max_lds_per_block() {
+  static int bytes = -1;
+  if (bytes < 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || bytes < 0)
+      bytes = 65536;
+  }
+  return static_cast<size_t>(bytes);
+}
+
 uint64_t up256(uint64_t b) { return (b + 255) & ~uint64_t(255); }
 
 namespace {
@@ -1259,11 +1327,19 @@ int choose_generic_partition(const kv_pool_config& c, int n_seqs, int max_blocks
 constexpr int kSkMaxSeqs = 4095;
 constexpr int kSkQBudget = 8192;  // bytes of staged queries per wave
 
-int sk_q_units(int G, int D) { return std::max(1, std::min(kSkQUnits, kSkQBudget / (G * D * 2))); }
+// Units per wave with staged queries: up to kSkQUnits within the per-wave
+// budget and what the prefix arrays leave of the workgroup's LDS; 0 when not
+// even one unit fits (then the kernel cannot run).
+int sk_q_units(int n_seqs, int G, int D) {
+  const int64_t unit = static_cast<int64_t>(G) * D * 2;
+  const int64_t left = static_cast<int64_t>(max_lds_per_block()) - static_cast<int64_t>(sk_prefix_ints(n_seqs)) * 4;
+  const int64_t fit = left > 0 ? left / (kSkWaves * unit) : 0;
+  return static_cast<int>(std::min<int64_t>({kSkQUnits, std::max<int64_t>(1, kSkQBudget / unit), fit}));
+}
 
 size_t sk_lds_bytes(int n_seqs, int G, int D) {
-  const size_t prefix = static_cast<size_t>((2 * (n_seqs + 1) + 3) & ~3) * 4;
-  return prefix + static_cast<size_t>(kSkWaves) * sk_q_units(G, D) * G * D * 2;
+  const size_t prefix = static_cast<size_t>(sk_prefix_ints(n_seqs)) * 4;
+  return prefix + static_cast<size_t>(kSkWaves) * sk_q_units(n_seqs, G, D) * G * D * 2;
 }
 
 // One wave per SIMD.  With two, the scheduler's oldest-first issue lets one
@@ -1304,7 +1380,7 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
   if (opts) o = *opts;
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_GENERIC && o.kernel != KV_KERNEL_MFMA)
     return fail(KV_ERR_INVALID, "unknown kernel selector");
-  const bool mfma_ok = mfma_supported(c, G) && n_seqs <= kSkMaxSeqs;
+  const bool mfma_ok = mfma_supported(c, G) && n_seqs <= kSkMaxSeqs && sk_q_units(n_seqs, G, c.head_dim) >= 1;
   if (o.kernel == KV_KERNEL_MFMA && !mfma_ok)
     return fail(KV_ERR_UNSUPPORTED,
                 "the matrix-core kernel needs bf16 or q8_0/q4_0, B = 16, d in {64, 128, 256} and at most 4095 "
@@ -1499,7 +1575,7 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     a.num_blocks = c.num_blocks;
     a.part_blocks = r.partition / c.block_size;
     a.n_waves = static_cast<int>(r.groups * kSkWaves);
-    a.q_units = sk_q_units(G, c.head_dim);
+    a.q_units = sk_q_units(n_seqs, G, c.head_dim);
     a.scale_log2 = r.scale * kLog2e;
     auto launch = [&](auto fmt) {
       constexpr int F = decltype(fmt)::value;
@@ -1670,7 +1746,7 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   a.num_blocks = c.num_blocks;
   a.part_blocks = r.partition / c.block_size;
   a.n_waves = static_cast<int>(r.groups * kSkWaves);
-  a.q_units = sk_q_units(G, c.head_dim);
+  a.q_units = sk_q_units(n_seqs, G, c.head_dim);
   a.scale_log2 = r.scale * kLog2e;
   a.force_partial = 1;
   hipError_t e;

@@ -105,6 +105,7 @@ constexpr int kMaxGroup = 16;  // query heads per KV head
 kv_status hip_check(hipError_t e, const char* what);
 bool mfma_supported(const kv_pool_config& c, int G);  // bf16, B = 16, d in {64, 128, 256}, G <= 16
 int device_cus();                                    // compute units of the current device
+size_t max_lds_per_block();                          // LDS bytes a workgroup may use on the current device
 uint64_t up256(uint64_t b);                          // rounded up to 256 bytes
 
 }  // namespace pagedkv

@@ -755,18 +755,6 @@ int64_t max_lds_per_cu() {
   return bytes;
 }
 
-// LDS a workgroup may use on the current device.
-size_t max_lds_per_block() {
-  static int bytes = -1;
-  if (bytes < 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || bytes < 0)
-      bytes = 65536;
-  }
-  return static_cast<size_t>(bytes);
-}
-
 kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len, int num_q_heads, int max_blocks,
                      const kv_attention_options* opts, pf_plan& p) {
   if (!pool) return fail(KV_ERR_INVALID, "pool is NULL");
