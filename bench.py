@@ -62,6 +62,37 @@ class no_gc:
         gc.enable()
 
 
+# GPU cycles of the spin kernel that gives the host a head start before the
+# attention calls are timed one by one
+HEAD_START_CYCLES = 2_000_000
+
+
+def time_calls(torch, B, stream, n, call, **opt_kwargs):
+    """Per-call timing of n attention calls, call(j, opts) for j < n, issued
+    back to back behind a short GPU spin so that the host is ahead and no call
+    waits for its own enqueue.  Each call carries kv_timing_events, which the
+    library attaches to its own kernel launches: start .. kernel_stop is the
+    kernel streaming the K/V cache, start .. stop the whole call.  Returns
+    (kernel ms, call ms) per call."""
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(n)]
+    for t in evs:
+        for e in t:
+            e.record(stream)  # gives each its HIP event
+    opts = [B.attention_options(timing=t, **opt_kwargs) for t in evs]
+    torch.cuda.synchronize()
+    with no_gc():
+        torch.cuda._sleep(HEAD_START_CYCLES)
+        for j in range(n):
+            call(j, opts[j])
+        torch.cuda.synchronize()
+    return [s.elapsed_time(k) for s, k, _ in evs], [s.elapsed_time(e) for s, _, e in evs]
+
+
+def pcts(ms):
+    import numpy as np
+    return [round(float(np.percentile(ms, q)) * 1e3, 2) for q in (10, 50, 90)]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,11 +238,18 @@ def main():
     seq_arr = np.asarray(decode_seqs, np.int64)
     stream = torch.cuda.current_stream()
 
-    attn_ev = []  # (start, end) HIP events around every paged_attention_decode
     logical_bytes = [0]
     n_copies = [0]
     n_groups = [0]
     read_bytes = [0]  # KV bytes the path reads (shared prefixes once per group with --cascade)
+
+    def attention(layer, q, o):
+        if args.cascade:
+            ng = n_groups[0]
+            pool.decode_cascade(layer, q, out, d_tables, d_lens, Hq, d_plan[:ng + 1], d_plan[ng + 1:2 * ng + 1],
+                                max_group, o, ws)
+        else:
+            pool.decode(layer, q, out, d_tables, d_lens, Hq, o, ws)
 
     def step(i, timed):
         slot = i % ring
@@ -250,18 +288,8 @@ def main():
             if step_appends:
                 k_new, v_new = kv_in[i][layer]
                 pool.cache(layer, k_new, v_new, d_slots)
+            attention(layer, q_in[i][layer], opts)
             if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            if args.cascade:
-                ng = n_groups[0]
-                pool.decode_cascade(layer, q_in[i][layer], out, d_tables, d_lens, Hq, d_plan[:ng + 1],
-                                    d_plan[ng + 1:2 * ng + 1], max_group, opts, ws)
-            else:
-                pool.decode(layer, q_in[i][layer], out, d_tables, d_lens, Hq, opts, ws)
-            if timed:
-                e1.record(stream)
-                attn_ev.append((e0, e1))
                 logical_bytes[0] += int(lens.astype(np.int64).sum()) * kv_tok
                 read_bytes[0] += read_tokens * kv_tok
         return lens
@@ -280,13 +308,21 @@ def main():
     ms_step = wall / args.steps * 1e3
 
     attn_name = "paged_attention_decode_cascade" if args.cascade else "paged_attention_decode"
-    attn_ms = [a.elapsed_time(b) for a, b in attn_ev]
+    # the timed steps' attention calls once more, each timed on its own (the
+    # tables and lengths of the last step, layers in turn)
+    kern_ms, attn_ms = time_calls(torch, B, stream, args.steps * L,
+                                  lambda j, o: attention(j % L, q_in[args.warmup + j // L][j % L], o),
+                                  partition_tokens=partition, kernel=kernel)
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
-    n_launch = len(attn_ms)
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    n_launch = args.steps * L
     kv_bytes_per_launch = read_bytes[0] / n_launch
     blocks_per_launch = float(np.mean([np.ceil(l / Bs).sum() for l in lens_hist]))
     ideal_per_launch = kv_bytes_per_launch + 2 * S * Hq * d * 2 + 4 * blocks_per_launch
-    achieved = ideal_per_launch / attn_avg_s / 1e9
+    # the roofline is that of the kernel streaming the cache (the split-K
+    # partition kernel); the cascade's bytes are only defined for the whole call
+    roof_s = attn_avg_s if args.cascade else kern_avg_s
+    achieved = ideal_per_launch / roof_s / 1e9
     value = logical_bytes[0] / wall / 1e9
     tok_per_s_layer = S * L * args.steps / wall
 
@@ -325,9 +361,13 @@ def main():
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "attn_tokens_per_s_per_layer": round(tok_per_s_layer, 1),
-        "attn_kernel_tokens_per_s_per_layer": round(S / attn_avg_s, 1),
+        "attn_call_tokens_per_s_per_layer": round(S / attn_avg_s, 1),
         "attn_call_us": round(attn_avg_s * 1e6, 2),
-        "attn_call_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "attn_call_us_p10_p50_p90": pcts(attn_ms),
+        "attn_kernel_us": round(kern_avg_s * 1e6, 2),
+        "attn_kernel_us_p10_p50_p90": pcts(kern_ms),
+        "call_achieved_gbs": round(ideal_per_launch / attn_avg_s / 1e9, 1),
+        "call_frac": round(ideal_per_launch / attn_avg_s / 1e9 / HBM_PEAK_GBS, 4),
         "unique_kv_bytes_per_launch": unique_kv_bytes,
         "cow_copies": n_copies[0],
         "fill_seconds": round(t_fill, 2),
@@ -340,8 +380,9 @@ def main():
             "traffic": measured_traffic(base.name + ("" if args.kv == "bf16" else f"_{args.kv}")
                                         + ("_cascade" if args.cascade else ""),
                                         ("kernels.hip", "prefill.hip") if args.cascade else ("kernels.hip",)),
-            "kernel": ("paged_attention_decode_cascade (prefix multi-query kernel + split-K kernel + merge)"
-                       if args.cascade else "paged_attention_decode (split-K kernel + merge kernel)"),
+            "kernel": ("paged_attention_decode_cascade (whole call: preparation, prefix multi-query kernel, "
+                       "split-K kernel, merge)" if args.cascade else "attn_mfma_kernel (split-K partition kernel)"),
+            "duration_us": round(roof_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(ideal_per_launch),
         },
         "cpu_baseline": None,
@@ -416,19 +457,12 @@ def multi_query_bench(args):
     ws_bytes = pool.prefill_workspace_bytes(S, total_q, c, Hq, max_blocks, opts)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    attn_ev = []
 
     def step(i, timed):
         for layer in range(L):
             k_new, v_new = kv_in[i][layer]
             pool.cache(layer, k_new, v_new, d_slots)
-            if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
             pool.prefill(layer, q_in[i][layer], out, d_indptr, d_tables, d_lens, c, Hq, opts, ws)
-            if timed:
-                e1.record(stream)
-                attn_ev.append((e0, e1))
 
     for i in range(args.warmup):
         step(i, False)
@@ -439,9 +473,13 @@ def multi_query_bench(args):
             step(i, True)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    attn_name = "paged_attention_decode_cascade" if args.cascade else "paged_attention_decode"
-    attn_ms = [a.elapsed_time(b) for a, b in attn_ev]
+    kern_ms, attn_ms = time_calls(
+        torch, B, stream, args.steps * L,
+        lambda j, o: pool.prefill(j % L, q_in[args.warmup + j // L][j % L], out, d_indptr, d_tables, d_lens, c, Hq,
+                                  o, ws),
+        partition_tokens=max(args.partition, 0))
     attn_s = float(np.mean(attn_ms)) / 1e3
+    kern_s = float(np.mean(kern_ms)) / 1e3
     n = lens.astype(np.int64)
     pairs = int(sum(c * (int(x) - c) + c * (c + 1) // 2 for x in n))  # query-key pairs per head
     flops = 4 * d * Hq * pairs                                          # QK^T and PV, per layer call
@@ -473,29 +511,35 @@ def multi_query_bench(args):
             "step": f"{L} x (reshape_and_cache of the chunk + paged_attention_prefill)",
         },
         "attn_call_us": round(attn_s * 1e6, 2),
-        "attn_call_us_p10_p50_p90": [round(float(np.percentile(attn_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "attn_call_us_p10_p50_p90": pcts(attn_ms),
+        "attn_kernel_us": round(kern_s * 1e6, 2),
+        "attn_kernel_us_p10_p50_p90": pcts(kern_ms),
         "chunk_tokens_per_s_per_layer": round(total_q / attn_s, 1),
         "query_key_pairs_per_head": pairs,
         "fill_seconds": round(t_fill, 2),
         "roofline": ({
             "bound": "mfma",
-            "achieved": round(flops / attn_s / 1e12, 2),
+            "achieved": round(flops / kern_s / 1e12, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(flops / attn_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac": round(flops / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": measured_traffic(base.name, ("prefill.hip",)),
-            "kernel": "attn_prefill_kernel",
+            "kernel": "attn_prefill_lds_kernel (multi-query kernel)",
+            "duration_us": round(kern_s * 1e6, 2),
             "algorithmic_flops_per_launch": flops,
         } if prefill else {
             "bound": "hbm",
-            "achieved": round(ideal_bytes / attn_s / 1e9, 1),
+            "achieved": round(ideal_bytes / kern_s / 1e9, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(ideal_bytes / attn_s / 1e9 / HBM_PEAK_GBS, 4),
+            "frac": round(ideal_bytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(base.name, ("prefill.hip",)),
-            "kernel": "attn_prefill_kernel + merge_prefill_kernel",
+            "kernel": "attn_prefill_lds_kernel (multi-query kernel)",
+            "duration_us": round(kern_s * 1e6, 2),
             "algorithmic_bytes_per_launch": ideal_bytes,
         }),
+        "call_frac": round((flops / attn_s / 1e12 / MFMA_BF16_PEAK_TFLOPS) if prefill
+                           else (ideal_bytes / attn_s / 1e9 / HBM_PEAK_GBS), 4),
         "cpu_baseline": None if args.no_cpu_baseline else multi_query_cpu_baseline(args, base),
     }
     print(json.dumps(result), flush=True)

@@ -369,12 +369,35 @@ typedef enum {
                             code x scale) */
 } kv_kernel;
 
+/* Optional timing of an attention call.  Each field is a hipEvent_t that
+ * already exists (created by the caller, e.g. a torch.cuda.Event recorded
+ * once), or NULL.  The library attaches the events to its own kernel launches
+ * (hipExtLaunchKernel), so they carry the GPU timestamps of the kernels
+ * themselves and add no marker between kernels:
+ *   start        start of the call's first kernel;
+ *   kernel_stop  end of the kernel that streams the K/V cache -- the split-K
+ *                partition kernel of paged_attention_decode and the
+ *                multi-query kernel of paged_attention_prefill (both the
+ *                call's first kernel, so start .. kernel_stop is that kernel
+ *                alone), the prefix-phase kernel of the cascade (start ..
+ *                kernel_stop then also spans the preparation kernel);
+ *   stop         end of the call's last kernel.
+ * Where the last kernel is also the one that streams the cache (one-kernel
+ * calls), stop is recorded right after it as an ordinary event.  The caller
+ * owns the events; the library only records them. */
+typedef struct {
+  void* start;
+  void* kernel_stop;
+  void* stop;
+} kv_timing_events;
+
 typedef struct {
   float scale;              /* softmax scale; 0 means 1/sqrt(d) ([BT] §07) */
   int32_t partition_tokens; /* split-K partition length in tokens, a positive
                                multiple of B; 0 = the library's choice (one
                                block for the matrix-core kernel) */
   int32_t kernel;           /* kv_kernel */
+  const kv_timing_events* timing; /* NULL: no timing */
 } kv_attention_options;
 
 /* Device workspace needed by paged_attention_decode for these arguments. */

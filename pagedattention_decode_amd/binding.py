@@ -43,8 +43,13 @@ class kv_pool_stats_t(C.Structure):
                 ("n_table_refs", C.c_int64)]
 
 
+class kv_timing_events(C.Structure):
+    _fields_ = [("start", C.c_void_p), ("kernel_stop", C.c_void_p), ("stop", C.c_void_p)]
+
+
 class kv_attention_options(C.Structure):
-    _fields_ = [("scale", C.c_float), ("partition_tokens", C.c_int32), ("kernel", C.c_int32)]
+    _fields_ = [("scale", C.c_float), ("partition_tokens", C.c_int32), ("kernel", C.c_int32),
+                ("timing", C.POINTER(kv_timing_events))]
 
 
 _P = C.c_void_p
@@ -278,8 +283,26 @@ def copy_blocks(pool, pairs, stream=None):
     _check(lib().copy_blocks(pool, _dev(pairs) if n else None, n, _stream(stream)))
 
 
-def attention_options(scale=0.0, partition_tokens=0, kernel=KV_KERNEL_AUTO):
-    return kv_attention_options(float(scale), int(partition_tokens), int(kernel))
+def _event_handle(ev):
+    if ev is None:
+        return None
+    if isinstance(ev, int):
+        return ev
+    h = int(ev.cuda_event)  # torch.cuda.Event: exists once it has been recorded
+    if not h:
+        raise ValueError("timing event has no HIP event yet: record it once before passing it")
+    return h
+
+
+def attention_options(scale=0.0, partition_tokens=0, kernel=KV_KERNEL_AUTO, timing=None):
+    """timing: None or (start, kernel_stop, stop), each a torch.cuda.Event
+    (already recorded once), a raw hipEvent_t or None (kv_timing_events)."""
+    o = kv_attention_options(float(scale), int(partition_tokens), int(kernel))
+    if timing is not None:
+        start, kernel_stop, stop = timing
+        o.timing = C.pointer(kv_timing_events(_event_handle(start), _event_handle(kernel_stop),
+                                              _event_handle(stop)))
+    return o
 
 
 def paged_attention_workspace_bytes(pool, n_seqs, num_q_heads, max_blocks_per_seq, opts=None):

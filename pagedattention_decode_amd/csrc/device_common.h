@@ -3,6 +3,7 @@
 // block in the pool's MFMA operand order.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -219,6 +220,19 @@ __device__ __forceinline__ void codes_block(const kv_qregs<D, FMT>& r, kv_regs<D
   for (int pp = 0; pp < D / 32; ++pp)
     out.v[pp] = make_uint4(half_words[2 * pp][0], half_words[2 * pp][1], half_words[2 * pp + 1][0],
                            half_words[2 * pp + 1][1]);
+}
+
+// Launches a kernel; with a start or stop event, through hipExtLaunchKernel so
+// that the events take the kernel's own timestamps.
+template <typename F, typename... Args>
+hipError_t launch_timed(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, hipEvent_t ev_start,
+                        hipEvent_t ev_stop, Args... args) {
+  if (ev_start || ev_stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev_start, ev_stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace pagedkv

@@ -1425,18 +1425,17 @@ uint64_t workspace_for(const kv_pool_config& c, int n_seqs, int num_q_heads, con
 
 template <int D, int FMT>
 hipError_t launch_mfma(const sk_args& a, const int32_t* ctx_lens, const int32_t* tables, int64_t groups, int G,
-                       hipStream_t st) {
+                       hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
   constexpr int kStages = sk_stages<D, FMT>();
   constexpr int kWps = sk_waves_per_simd(D, FMT);
-  hipLaunchKernelGGL((attn_mfma_kernel<D, kStages, kWps, FMT>), dim3(static_cast<unsigned>(groups)), dim3(kSkWaves * 64),
-                     sk_lds_bytes(a.n_seqs, G, D), st, a, ctx_lens, tables);
-  return hipGetLastError();
+  return launch_timed(attn_mfma_kernel<D, kStages, kWps, FMT>, dim3(static_cast<unsigned>(groups)),
+                      dim3(kSkWaves * 64), static_cast<uint32_t>(sk_lds_bytes(a.n_seqs, G, D)), st, ev0, ev1, a,
+                      ctx_lens, tables);
 }
 
 template <typename T, int D>
-hipError_t launch_generic(const attn_args& a, int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_generic_kernel<T, D>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, a);
-  return hipGetLastError();
+hipError_t launch_generic(const attn_args& a, int64_t grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  return launch_timed(attn_generic_kernel<T, D>, dim3(static_cast<unsigned>(grid)), dim3(256), 0u, st, ev0, ev1, a);
 }
 
 }  // namespace
@@ -1554,6 +1553,7 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
   const void* v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const int G = num_q_heads / c.num_kv_heads;
+  const call_events ev = events_of(opts);
   hipError_t e = hipSuccess;
 
   if (r.kernel == KV_KERNEL_MFMA) {
@@ -1580,9 +1580,9 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     auto launch = [&](auto fmt) {
       constexpr int F = decltype(fmt)::value;
       switch (c.head_dim) {
-        case 64: return launch_mfma<64, F>(a, d_context_lens, d_block_tables, r.groups, G, st);
-        case 128: return launch_mfma<128, F>(a, d_context_lens, d_block_tables, r.groups, G, st);
-        default: return launch_mfma<256, F>(a, d_context_lens, d_block_tables, r.groups, G, st);
+        case 64: return launch_mfma<64, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
+        case 128: return launch_mfma<128, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
+        default: return launch_mfma<256, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
       }
     };
     if (c.dtype == KV_Q8_0) e = launch(std::integral_constant<int, kFmtQ8>{});
@@ -1592,11 +1592,11 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     const unsigned mgrid =
         static_cast<unsigned>((static_cast<int64_t>(n_seqs) * num_q_heads + kMergeItems - 1) / kMergeItems);
     switch (c.head_dim) {
-      case 64: hipLaunchKernelGGL(merge_sk_kernel<64>, dim3(mgrid), dim3(kMergeItems * 64), 0, st, a); break;
-      case 128: hipLaunchKernelGGL(merge_sk_kernel<128>, dim3(mgrid), dim3(kMergeItems * 64), 0, st, a); break;
-      default: hipLaunchKernelGGL(merge_sk_kernel<256>, dim3(mgrid), dim3(kMergeItems * 64), 0, st, a); break;
+      case 64: e = launch_timed(merge_sk_kernel<64>, dim3(mgrid), dim3(kMergeItems * 64), 0u, st, nullptr, ev.stop, a); break;
+      case 128: e = launch_timed(merge_sk_kernel<128>, dim3(mgrid), dim3(kMergeItems * 64), 0u, st, nullptr, ev.stop, a); break;
+      default: e = launch_timed(merge_sk_kernel<256>, dim3(mgrid), dim3(kMergeItems * 64), 0u, st, nullptr, ev.stop, a); break;
     }
-    return hip_check(hipGetLastError(), "paged attention merge launch");
+    return hip_check(e, "paged attention merge launch");
   }
 
   const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * r.max_parts;
@@ -1626,25 +1626,29 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
   a.max_parts = r.max_parts;
   a.scale_log2 = r.scale * kLog2e;
   const bool f32 = c.dtype == KV_F32;
+  auto gen = [&](auto d) {
+    constexpr int Dv = decltype(d)::value;
+    return f32 ? launch_generic<float, Dv>(a, grid, st, ev.start, ev.kernel_stop)
+               : launch_generic<uint16_t, Dv>(a, grid, st, ev.start, ev.kernel_stop);
+  };
   switch (c.head_dim) {
-    case 32: e = f32 ? launch_generic<float, 32>(a, grid, st) : launch_generic<uint16_t, 32>(a, grid, st); break;
-    case 64: e = f32 ? launch_generic<float, 64>(a, grid, st) : launch_generic<uint16_t, 64>(a, grid, st); break;
-    case 96: e = f32 ? launch_generic<float, 96>(a, grid, st) : launch_generic<uint16_t, 96>(a, grid, st); break;
-    case 128: e = f32 ? launch_generic<float, 128>(a, grid, st) : launch_generic<uint16_t, 128>(a, grid, st); break;
-    case 160: e = f32 ? launch_generic<float, 160>(a, grid, st) : launch_generic<uint16_t, 160>(a, grid, st); break;
-    case 192: e = f32 ? launch_generic<float, 192>(a, grid, st) : launch_generic<uint16_t, 192>(a, grid, st); break;
-    case 224: e = f32 ? launch_generic<float, 224>(a, grid, st) : launch_generic<uint16_t, 224>(a, grid, st); break;
-    default: e = f32 ? launch_generic<float, 256>(a, grid, st) : launch_generic<uint16_t, 256>(a, grid, st); break;
+    case 32: e = gen(std::integral_constant<int, 32>{}); break;
+    case 64: e = gen(std::integral_constant<int, 64>{}); break;
+    case 96: e = gen(std::integral_constant<int, 96>{}); break;
+    case 128: e = gen(std::integral_constant<int, 128>{}); break;
+    case 160: e = gen(std::integral_constant<int, 160>{}); break;
+    case 192: e = gen(std::integral_constant<int, 192>{}); break;
+    case 224: e = gen(std::integral_constant<int, 224>{}); break;
+    default: e = gen(std::integral_constant<int, 256>{}); break;
   }
   if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
   if (r.max_parts > 1) {
-    const int64_t mgrid = static_cast<int64_t>(n_seqs) * num_q_heads;
-    if (f32)
-      hipLaunchKernelGGL(merge_kernel<float>, dim3(static_cast<unsigned>(mgrid)), dim3(kMergeThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(static_cast<unsigned>(mgrid)), dim3(kMergeThreads), 0, st, a);
-    if (kv_status s = hip_check(hipGetLastError(), "paged attention merge launch")) return s;
+    const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(n_seqs) * num_q_heads));
+    e = f32 ? launch_timed(merge_kernel<float>, mgrid, dim3(kMergeThreads), 0u, st, nullptr, ev.stop, a)
+            : launch_timed(merge_kernel<uint16_t>, mgrid, dim3(kMergeThreads), 0u, st, nullptr, ev.stop, a);
+    return hip_check(e, "paged attention merge launch");
   }
+  if (ev.stop) return hip_check(hipEventRecord(ev.stop, st), "timing event");
   return KV_OK;
 }
 
@@ -1718,13 +1722,17 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   int32_t* ctx_sfx = reinterpret_cast<int32_t*>(ws + L.ctx);
   int32_t* prefix_ctx = reinterpret_cast<int32_t*>(ws + L.prefix_ctx);
   int2* info = reinterpret_cast<int2*>(ws + L.info);
-  hipLaunchKernelGGL(cascade_prep_kernel, dim3(static_cast<unsigned>(n_seqs)), dim3(256), 0, st, d_block_tables,
-                     d_context_lens, d_group_start, d_shared_blocks, n_seqs, n_groups, max_group, max_blocks_per_seq,
-                     tables_sfx, ctx_sfx, prefix_ctx, info);
-  if (kv_status s = hip_check(hipGetLastError(), "cascade prep launch")) return s;
+  const call_events ev = events_of(opts);
+  if (kv_status s = hip_check(
+          launch_timed(cascade_prep_kernel, dim3(static_cast<unsigned>(n_seqs)), dim3(256), 0u, st, ev.start, nullptr,
+                       d_block_tables, d_context_lens, d_group_start, d_shared_blocks, n_seqs, n_groups, max_group,
+                       max_blocks_per_seq, tables_sfx, ctx_sfx, prefix_ctx, info),
+          "cascade prep launch"))
+    return s;
   // prefix: every group's shared blocks, once, for all members
   if (kv_status s = prefix_phase_launch(pool, layer, q, out, d_group_start, prefix_ctx, d_block_tables, n_groups,
-                                        n_seqs, max_group, max_blocks_per_seq, num_q_heads, opts, ws + L.pre, st))
+                                        n_seqs, max_group, max_blocks_per_seq, num_q_heads, opts, ws + L.pre, st,
+                                        ev.kernel_stop))
     return s;
   // suffix: the split-K decode on the shifted tables, partials only
   const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
@@ -1768,11 +1776,11 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   const int64_t items = static_cast<int64_t>(n_seqs) * num_q_heads;
   const unsigned mgrid = static_cast<unsigned>((items + 3) / 4);
   switch (c.head_dim) {
-    case 64: hipLaunchKernelGGL(cascade_merge_kernel<64>, dim3(mgrid), dim3(256), 0, st, m); break;
-    case 128: hipLaunchKernelGGL(cascade_merge_kernel<128>, dim3(mgrid), dim3(256), 0, st, m); break;
-    default: hipLaunchKernelGGL(cascade_merge_kernel<256>, dim3(mgrid), dim3(256), 0, st, m); break;
+    case 64: e = launch_timed(cascade_merge_kernel<64>, dim3(mgrid), dim3(256), 0u, st, nullptr, ev.stop, m); break;
+    case 128: e = launch_timed(cascade_merge_kernel<128>, dim3(mgrid), dim3(256), 0u, st, nullptr, ev.stop, m); break;
+    default: e = launch_timed(cascade_merge_kernel<256>, dim3(mgrid), dim3(256), 0u, st, nullptr, ev.stop, m); break;
   }
-  return hip_check(hipGetLastError(), "cascade merge launch");
+  return hip_check(e, "cascade merge launch");
 }
 
 }  // extern "C"

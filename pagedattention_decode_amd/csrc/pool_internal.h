@@ -93,7 +93,7 @@ kv_status prefix_phase_plan(const kv_pool* pool, int n_groups, int n_rows, int m
 kv_status prefix_phase_launch(kv_pool* pool, int layer, const void* q, void* out, const int32_t* group_start,
                               const int32_t* prefix_ctx, const int32_t* tables, int n_groups, int n_rows,
                               int max_group, int max_blocks, int num_q_heads, const kv_attention_options* opts,
-                              void* ws, hipStream_t st);
+                              void* ws, hipStream_t st, hipEvent_t ev_stop);
 
 // Device side of a swap (swap.hip): pairs are (block, frame) for direction 0
 // (out) and (frame, block) for direction 1 (in); checked by the caller.
@@ -107,5 +107,20 @@ bool mfma_supported(const kv_pool_config& c, int G);  // bf16, B = 16, d in {64,
 int device_cus();                                    // compute units of the current device
 size_t max_lds_per_block();                          // LDS bytes a workgroup may use on the current device
 uint64_t up256(uint64_t b);                          // rounded up to 256 bytes
+
+// Timing events of a call (kv_timing_events), all null when none were given.
+struct call_events {
+  hipEvent_t start = nullptr, kernel_stop = nullptr, stop = nullptr;
+};
+inline call_events events_of(const kv_attention_options* o) {
+  call_events e;
+  if (o && o->timing) {
+    e.start = static_cast<hipEvent_t>(o->timing->start);
+    e.kernel_stop = static_cast<hipEvent_t>(o->timing->kernel_stop);
+    e.stop = static_cast<hipEvent_t>(o->timing->stop);
+  }
+  return e;
+}
+
 
 }  // namespace pagedkv

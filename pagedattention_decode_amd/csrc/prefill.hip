@@ -822,45 +822,41 @@ uint64_t pf_workspace(const kv_pool_config& c, int total_q, int num_q_heads, con
 // Ring depth in block pairs: the wider tiles hold more accumulators and fewer
 // blocks in flight.
 template <int D, int NCG>
-hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st) {
+hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr size_t kPair = 4 * 16 * D * 2;  // Ka, Kb, Va, Vb
   // several tiles per partition: share each block pair through LDS; ring
   // depth 4 pairs for one partition group (64 KiB at d = 128, two workgroups
   // per CU), 3 for two groups (96 KiB, one workgroup per CU)
   if constexpr (D <= 128) {
     if (a.wt == 2 && (kPfWaves / 2) * 3 * kPair <= max_lds_per_block()) {
-      hipLaunchKernelGGL((attn_prefill_lds_kernel<D, NCG, 2, 3>), dim3(static_cast<unsigned>(grid)),
-                         dim3(kPfWaves * 64), (kPfWaves / 2) * 3 * kPair, st, a);
-      return hipGetLastError();
+      return launch_timed(attn_prefill_lds_kernel<D, NCG, 2, 3>, dim3(static_cast<unsigned>(grid)),
+                          dim3(kPfWaves * 64), (kPfWaves / 2) * 3 * kPair, st, ev0, ev1, a);
     }
     if (a.wt == 4 && (kPfWaves / 4) * 4 * kPair <= max_lds_per_block()) {
-      hipLaunchKernelGGL((attn_prefill_lds_kernel<D, NCG, 4, 4>), dim3(static_cast<unsigned>(grid)),
-                         dim3(kPfWaves * 64), (kPfWaves / 4) * 4 * kPair, st, a);
-      return hipGetLastError();
+      return launch_timed(attn_prefill_lds_kernel<D, NCG, 4, 4>, dim3(static_cast<unsigned>(grid)),
+                          dim3(kPfWaves * 64), (kPfWaves / 4) * 4 * kPair, st, ev0, ev1, a);
     }
   }
   constexpr int kStages = D >= 256 ? 1 : 2;
   constexpr size_t kLds = static_cast<size_t>(kPfWaves) * NCG * (D / 32) * 64 * 16;  // Q^T operands per wave
-  hipLaunchKernelGGL((attn_prefill_kernel<D, NCG, kStages>), dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64),
-                     kLds, st, a);
-  return hipGetLastError();
+  return launch_timed(attn_prefill_kernel<D, NCG, kStages>, dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64),
+                      static_cast<uint32_t>(kLds), st, ev0, ev1, a);
 }
 
 template <int D>
-hipError_t pf_launch_d(const pf_args& a, int ncg, int64_t grid, hipStream_t st) {
-  if (ncg == 1) return pf_launch<D, 1>(a, grid, st);
+hipError_t pf_launch_d(const pf_args& a, int ncg, int64_t grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (ncg == 1) return pf_launch<D, 1>(a, grid, st, ev0, ev1);
   if constexpr (D <= 128)
-    if (ncg == 2) return pf_launch<D, 2>(a, grid, st);
+    if (ncg == 2) return pf_launch<D, 2>(a, grid, st, ev0, ev1);
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t pf_merge(const pf_args& a, hipStream_t st) {
+hipError_t pf_merge(const pf_args& a, hipStream_t st, hipEvent_t ev1) {
   const int64_t items = static_cast<int64_t>(a.total_q) * a.n_q_heads;
   const int64_t grid = (items + kPfMergeWaves - 1) / kPfMergeWaves;
-  hipLaunchKernelGGL((merge_prefill_kernel<D>), dim3(static_cast<unsigned>(grid)), dim3(kPfMergeWaves * 64), 0, st,
-                     a);
-  return hipGetLastError();
+  return launch_timed(merge_prefill_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kPfMergeWaves * 64), 0u, st,
+                      nullptr, ev1, a);
 }
 
 }  // namespace
@@ -884,7 +880,7 @@ kv_status prefix_phase_plan(const kv_pool* pool, int n_groups, int n_rows, int m
 kv_status prefix_phase_launch(kv_pool* pool, int layer, const void* q, void* out, const int32_t* group_start,
                               const int32_t* prefix_ctx, const int32_t* tables, int n_groups, int n_rows,
                               int max_group, int max_blocks, int num_q_heads, const kv_attention_options* opts,
-                              void* ws, hipStream_t st) {
+                              void* ws, hipStream_t st, hipEvent_t ev_stop) {
   pf_plan p;
   if (kv_status s = pf_resolve(pool, n_groups, n_rows, max_group, num_q_heads, max_blocks, opts, p)) return s;
   const kv_pool_config& c = pool->cfg;
@@ -922,9 +918,9 @@ kv_status prefix_phase_launch(kv_pool* pool, int layer, const void* q, void* out
   const int64_t grid = static_cast<int64_t>(n_groups) * c.num_kv_heads * p.tile_groups * p.part_groups;
   hipError_t e;
   switch (c.head_dim) {
-    case 64: e = pf_launch_d<64>(a, p.ncg, grid, st); break;
-    case 128: e = pf_launch_d<128>(a, p.ncg, grid, st); break;
-    default: e = pf_launch_d<256>(a, p.ncg, grid, st); break;
+    case 64: e = pf_launch_d<64>(a, p.ncg, grid, st, nullptr, ev_stop); break;
+    case 128: e = pf_launch_d<128>(a, p.ncg, grid, st, nullptr, ev_stop); break;
+    default: e = pf_launch_d<256>(a, p.ncg, grid, st, nullptr, ev_stop); break;
   }
   return hip_check(e, "cascade prefix launch");
 }
@@ -996,21 +992,23 @@ kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, v
   a.causal = 1;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * p.tile_groups * p.part_groups;
+  const call_events ev = events_of(opts);
   hipError_t e;
   switch (c.head_dim) {
-    case 64: e = pf_launch_d<64>(a, p.ncg, grid, st); break;
-    case 128: e = pf_launch_d<128>(a, p.ncg, grid, st); break;
-    default: e = pf_launch_d<256>(a, p.ncg, grid, st); break;
+    case 64: e = pf_launch_d<64>(a, p.ncg, grid, st, ev.start, ev.kernel_stop); break;
+    case 128: e = pf_launch_d<128>(a, p.ncg, grid, st, ev.start, ev.kernel_stop); break;
+    default: e = pf_launch_d<256>(a, p.ncg, grid, st, ev.start, ev.kernel_stop); break;
   }
   if (kv_status s = hip_check(e, "paged_attention_prefill launch")) return s;
   if (p.max_parts > 1) {
     switch (c.head_dim) {
-      case 64: e = pf_merge<64>(a, st); break;
-      case 128: e = pf_merge<128>(a, st); break;
-      default: e = pf_merge<256>(a, st); break;
+      case 64: e = pf_merge<64>(a, st, ev.stop); break;
+      case 128: e = pf_merge<128>(a, st, ev.stop); break;
+      default: e = pf_merge<256>(a, st, ev.stop); break;
     }
     return hip_check(e, "paged_attention_prefill merge launch");
   }
+  if (ev.stop) return hip_check(hipEventRecord(ev.stop, st), "timing event");
   return KV_OK;
 }
 

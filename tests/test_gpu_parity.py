@@ -340,3 +340,35 @@ def test_release_waits_for_stream_event():
     st = run.pool.stats()
     assert st["n_pending"] == 0 and st["n_free"] == 4
     run.pool.check()
+
+
+@pytest.mark.parametrize("kernel", [B.KV_KERNEL_MFMA, B.KV_KERNEL_GENERIC])
+def test_timing_events_leave_results_unchanged(kernel):
+    announce(f"kv_timing_events on decode calls (kernel {kernel}): outputs as without them, times ordered")
+    lengths = [2304, 17, 1000, 33]
+    wl = ragged_workload(32, 8, 128, lengths)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref).run()
+    tables = torch.from_numpy(run.decodes[0]["tables"]).cuda()
+    lens = torch.from_numpy(run.decodes[0]["lengths"]).cuda()
+    n = len(lengths)
+    stream = torch.cuda.current_stream()
+    q = to_device_bits(run.query_bits(0, 0, n))
+    plain = B.attention_options(kernel=kernel)
+    ws = torch.empty(max(run.pool.workspace_bytes(n, 32, tables.shape[1], plain), 1), dtype=torch.uint8,
+                     device="cuda")
+    out0 = torch.empty((n, 32, 128), dtype=torch.int16, device="cuda")
+    run.pool.decode(0, q, out0, tables, lens, 32, plain, ws)
+    for _ in range(3):
+        evs = tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+        for e in evs:
+            e.record(stream)
+        out = torch.full((n, 32, 128), -1, dtype=torch.int16, device="cuda")
+        run.pool.decode(0, q, out, tables, lens, 32, B.attention_options(kernel=kernel, timing=evs), ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out0)
+        k_ms, c_ms = evs[0].elapsed_time(evs[1]), evs[0].elapsed_time(evs[2])
+        print(f"  kernel {k_ms * 1e3:.1f} us, call {c_ms * 1e3:.1f} us", flush=True)
+        assert 0.0 < k_ms <= c_ms
+    got = bits_to_float_tensor(out0, wl.dtype).double().cpu().numpy()
+    check_outputs(got, ref.attention(0, 0), wl.dtype, "decode")
