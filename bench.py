@@ -117,6 +117,19 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (a plain copy of known size, used to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    g = ap.add_argument_group("summaries of rocprofv3 output for profiles/ (no GPU needed)")
+    g.add_argument("--summarize-trace", metavar="DIR", help="a --kernel-trace --stats output directory")
+    g.add_argument("--summarize-counters", metavar="DIR",
+                   help="directory with pmc_<name>_FETCH_SIZE/, pmc_<name>_WRITE_SIZE/, pmc_cal_FETCH_SIZE/, "
+                        "pmc_cal_WRITE_SIZE/ and their .log files")
+    g.add_argument("--summary-name", default="", help="<name> of the pmc_<name>_* runs")
+    g.add_argument("--summary-workload", default="", help="workload name of hbm_traffic_<workload>.json")
+    g.add_argument("--summary-kernels", default="attn_mfma_kernel,merge_sk_kernel",
+                   help="kernels of one call, the one streaming the cache first")
+    g.add_argument("--summary-sources", default="kernels.hip", help="csrc files whose hash the summary records")
+    g.add_argument("--summary-file", default="", help="markdown file name in profiles/ (without .md)")
+    g.add_argument("--summary-title", default="")
+    g.add_argument("--summary-command", default="", help="bench.py arguments of the profiled run")
     return ap.parse_args()
 
 
@@ -136,6 +149,12 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -763,9 +782,11 @@ def kernel_source_sha256(sources):
     return h.hexdigest()
 
 
-def measured_traffic(workload, sources=("kernels.hip",)):
-    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this
-    workload, or None when there is none or the kernel sources changed since it was taken."""
+def measured_traffic(workload, sources=("kernels.hip",), key="traffic_bytes_per_launch"):
+    """HBM bytes per launch of the kernel streaming the cache (key
+    traffic_bytes_per_launch) or per whole call (traffic_bytes_per_call) from
+    the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload;
+    None when there is none or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -773,7 +794,156 @@ def measured_traffic(workload, sources=("kernels.hip",)):
         rec = json.load(f)
     if kernel_source_sha256(sources) != rec.get("kernel_source_sha256"):
         return None
-    return rec.get("traffic_bytes_per_call")
+    return rec.get(key)
+
+
+# ---- summaries of rocprofv3 output for profiles/ ---------------------------
+
+def short_kernel_name(name):
+    """attn_mfma_kernel from 'void pagedkv::(anonymous namespace)::attn_mfma_kernel<...>(...)'."""
+    head = name.replace("(anonymous namespace)::", "")
+    head = head[5:] if head.startswith("void ") else head
+    head = head.split("<", 1)[0].split("(", 1)[0]
+    return head.rsplit("::", 1)[-1]
+
+
+def read_csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def find_csv(run_dir, suffix):
+    for dirpath, _, files in os.walk(run_dir):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(dirpath, fn)
+    raise FileNotFoundError(f"no *{suffix} under {run_dir}")
+
+
+def bench_line(log_path):
+    with open(log_path) as f:
+        lines = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+    return json.loads(lines[-1]) if lines else None
+
+
+def counter_kib_per_dispatch(run_dir, counter):
+    """Mean counter value per dispatch, by short kernel name."""
+    per = {}
+    for r in read_csv_rows(find_csv(run_dir, "counter_collection.csv")):
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in per.items()}
+
+
+def summary_command():
+    """This summary's own command line, with the output directory shown as <dir>."""
+    import shlex
+    args = sys.argv[1:]
+    for i, x in enumerate(args[:-1]):
+        if x in ("--summarize-counters", "--summarize-trace"):
+            args[i + 1] = "<dir>" if x == "--summarize-counters" else "<out>"
+    return "python3 bench.py " + " ".join(shlex.quote(x) for x in args)
+
+
+def summarize_counters(a):
+    """--summarize-counters: FETCH_SIZE / WRITE_SIZE runs of a workload and of
+    the plain-copy calibration -> profiles/hbm_traffic_<workload>.json and a
+    markdown table.  Reads a directory holding pmc_<name>_{FETCH,WRITE}_SIZE/
+    and pmc_cal_{FETCH,WRITE}_SIZE/ (with their .log files)."""
+    d, name, wl = a.summarize_counters, a.summary_name, a.summary_workload
+    kernels = a.summary_kernels.split(",")
+    sources = tuple(a.summary_sources.split(","))
+    fetch = counter_kib_per_dispatch(os.path.join(d, f"pmc_{name}_FETCH_SIZE"), "FETCH_SIZE")
+    write = counter_kib_per_dispatch(os.path.join(d, f"pmc_{name}_WRITE_SIZE"), "WRITE_SIZE")
+    cal_f = counter_kib_per_dispatch(os.path.join(d, "pmc_cal_FETCH_SIZE"), "FETCH_SIZE")
+    cal_w = counter_kib_per_dispatch(os.path.join(d, "pmc_cal_WRITE_SIZE"), "WRITE_SIZE")
+    cal = bench_line(os.path.join(d, "pmc_cal_FETCH_SIZE.log"))["copy_calibration_bytes_per_copy"]
+    copy_f = max(cal_f.values())[0]
+    copy_w = max(cal_w.values())[0]
+    f_scale = cal / (copy_f * 1024)  # the copy reads cal bytes
+    w_scale = cal / (copy_w * 1024)  # and writes cal bytes
+    line = bench_line(os.path.join(d, f"pmc_{name}_FETCH_SIZE.log"))
+    alg = line["roofline"].get("algorithmic_bytes_per_launch")
+    per_kernel = {k: (fetch[k][0] * 1024 * f_scale, write.get(k, (0.0, 0))[0] * 1024 * w_scale) for k in kernels}
+    main_k = kernels[0]
+    rec = {
+        "workload": wl,
+        "kernel_source_sha256": kernel_source_sha256(sources),
+        "sources": list(sources),
+        "kernel": main_k,
+        "traffic_bytes_per_launch": int(round(sum(per_kernel[main_k]))),
+        "traffic_bytes_per_call": int(round(sum(sum(v) for v in per_kernel.values()))),
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "fetch_kib": {k: fetch[k][0] for k in kernels},
+        "write_kib": {k: write.get(k, (0.0, 0))[0] for k in kernels},
+        "algorithmic_bytes_per_launch": alg,
+    }
+    out_json = os.path.join(ROOT, "profiles", f"hbm_traffic_{wl}.json")
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    bench_args = a.summary_command
+    md = [f"# HBM traffic counters: {a.summary_title}", "",
+          "Commands (from the repository root, one pass per counter, each in a run of its own):", "", "```"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        md.append(f"timeout -s KILL 150 rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- "
+                  f"python3 bench.py {bench_args}")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        md.append(f"timeout -s KILL 150 rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- "
+                  f"python3 bench.py --copy-calibration {cal >> 20}")
+    md += ["```", "", "Summarised from the four output directories (as `<dir>/pmc_<name>_<counter>/`, with each "
+           f"run's stdout in `<dir>/pmc_<name>_<counter>.log`) by `{summary_command()}`.", "",
+           f"Kernel sources sha256 ({', '.join(sources)}): `{rec['kernel_source_sha256']}`", "",
+           f"Calibration with a plain device copy of {cal >> 20} MiB (`__amd_rocclr_copyBuffer`, as many bytes "
+           f"read as written): FETCH_SIZE reads {copy_f:.1f} KiB per copy, WRITE_SIZE {copy_w:.1f} KiB, so bytes = "
+           f"KiB x 1024 x {f_scale:.4f} (fetch) and x {w_scale:.4f} (write).", "",
+           "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched bytes (calibrated) | "
+           "written bytes (calibrated) |", "|---|---|---|---|---|---|"]
+    for k in kernels:
+        md.append(f"| `{k}` | {fetch[k][1]} | {fetch[k][0]:.1f} | {write.get(k, (0.0, 0))[0]:.1f} | "
+                  f"{per_kernel[k][0]:,.0f} | {per_kernel[k][1]:,.0f} |")
+    md += ["", f"Algorithmic bytes per launch in the FETCH_SIZE run (K/V as stored, q, out, table entries): "
+           f"{alg:,} B.  `{main_k}` moves {rec['traffic_bytes_per_launch']:,} B per launch "
+           f"({rec['traffic_bytes_per_launch'] / alg:.4f} x algorithmic); the whole call "
+           f"({', '.join(kernels)}) {rec['traffic_bytes_per_call']:,} B "
+           f"({rec['traffic_bytes_per_call'] / alg:.4f} x)."]
+    out_md = os.path.join(ROOT, "profiles", f"{a.summary_file}.md")
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(out_json)
+    print(out_md)
+
+
+def summarize_trace(a):
+    """--summarize-trace: a rocprofv3 --kernel-trace --stats run (and the bench
+    line it printed, <dir>.json) -> a markdown table in profiles/."""
+    d = a.summarize_trace
+    rows = read_csv_rows(find_csv(d, "kernel_stats.csv"))
+    sources = tuple(a.summary_sources.split(","))
+    md = [f"# Kernel trace: {a.summary_title}", "", "Command (from the repository root, on one MI355X):", "", "```",
+          f"rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- python3 bench.py "
+          f"{a.summary_command}", "```", "",
+          f"Summarised from `<out>` (the run's stdout in `<out>.json`) by `{summary_command()}`.", "",
+          f"Kernel sources sha256 ({', '.join(sources)}): `{kernel_source_sha256(sources)}`", "",
+          "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        md.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    line = bench_line(d.rstrip("/") + ".json")
+    if line:
+        r = line["roofline"]
+        md += ["", "Bench line of the same run (under the tracer, which slows launches): "
+               f"value {line['value']} {line['unit']}; "
+               f"kernel {line.get('attn_kernel_us')} us and call {line.get('attn_call_us')} us by the library's "
+               f"timing events; roofline {r['kernel']}: {r['achieved']} {r['unit']} of {r['peak']} "
+               f"({r['frac']})."]
+    out_md = os.path.join(ROOT, "profiles", f"{a.summary_file}.md")
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(out_md)
 
 
 def cpu_baseline(args):
