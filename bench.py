@@ -241,18 +241,27 @@ def main():
         max_group = int(np.diff(gs0).max())
         ws_bytes = max(pool.cascade_workspace_bytes(S, ng, max_group, Hq, max_blocks, opts)
                        for ng in range(1, S + 1))
-        d_plan = torch.empty((2 * S + 1,), dtype=torch.int32, device=dev)
     else:
         ws_bytes = pool.workspace_bytes(S, Hq, max_blocks, opts)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device=dev)
-    d_lens = torch.empty((S,), dtype=torch.int32, device=dev)
-    d_slots = torch.empty((S,), dtype=torch.int64, device=dev)
+    # one upload per step: slot mapping (int64), tables, lengths and the cascade plan (int32)
+    # packed in one pinned buffer and copied to one device buffer in a single transfer
+    off_t = 8 * S
+    off_l = off_t + 4 * S * max_blocks
+    off_p = off_l + 4 * S
+    up_bytes = off_p + 4 * (2 * S + 1)
+    d_up = torch.empty((up_bytes,), dtype=torch.uint8, device=dev)
+    d_slots = d_up[:off_t].view(torch.int64)
+    d_tables = d_up[off_t:off_l].view(torch.int32).view(S, max_blocks)
+    d_lens = d_up[off_l:off_p].view(torch.int32)
+    d_plan = d_up[off_p:].view(torch.int32)
     ring = 4
-    h_tables = [torch.empty((S, max_blocks), dtype=torch.int32).pin_memory() for _ in range(ring)]
-    h_lens = [torch.empty((S,), dtype=torch.int32).pin_memory() for _ in range(ring)]
-    h_slots = [torch.empty((S,), dtype=torch.int64).pin_memory() for _ in range(ring)]
-    h_plan = [torch.empty((2 * S + 1,), dtype=torch.int32).pin_memory() for _ in range(ring)]
+    h_up = [torch.empty((up_bytes,), dtype=torch.uint8).pin_memory() for _ in range(ring)]
+    h_np = [h.numpy() for h in h_up]
+    h_slots = [h[:off_t].view(np.int64) for h in h_np]
+    h_tables = [h[off_t:off_l].view(np.int32).reshape(S, max_blocks) for h in h_np]
+    h_lens = [h[off_l:off_p].view(np.int32) for h in h_np]
+    h_plan = [h[off_p:].view(np.int32) for h in h_np]
     ring_ev = [None] * ring
     seq_arr = np.asarray(decode_seqs, np.int64)
     stream = torch.cuda.current_stream()
@@ -277,26 +286,23 @@ def main():
         pairs = np.zeros((0, 2), np.int64)
         if step_appends:
             slots, pairs = pool.append(seq_arr, None)
-            h_slots[slot].numpy()[:] = slots
-            d_slots.copy_(h_slots[slot], non_blocking=True)
+            h_slots[slot][:] = slots
         tables, lens = B.kv_get_block_tables(pool.handle, seq_arr, max_blocks)
-        h_tables[slot].numpy()[:] = tables
-        h_lens[slot].numpy()[:] = lens
-        d_tables.copy_(h_tables[slot], non_blocking=True)
-        d_lens.copy_(h_lens[slot], non_blocking=True)
+        h_tables[slot][:] = tables
+        h_lens[slot][:] = lens
         if args.cascade:
             gs, sb = pool.shared_prefix_plan(seq_arr)
             ng = len(sb)
             assert int(np.diff(gs).max()) <= max_group, "a fork group outgrew the first step's plan"
-            h_plan[slot].numpy()[:ng + 1] = gs
-            h_plan[slot].numpy()[ng + 1:2 * ng + 1] = sb
-            d_plan[:2 * ng + 1].copy_(h_plan[slot][:2 * ng + 1], non_blocking=True)
+            h_plan[slot][:ng + 1] = gs
+            h_plan[slot][ng + 1:2 * ng + 1] = sb
             n_groups[0] = ng
             # tokens the cascade reads: each group's shared prefix once, every member's suffix
             shared_tok = np.repeat(sb.astype(np.int64) * Bs, np.diff(gs))
             read_tokens = int(sb.astype(np.int64).sum()) * Bs + int((lens.astype(np.int64) - shared_tok).sum())
         else:
             read_tokens = int(lens.astype(np.int64).sum())
+        d_up.copy_(h_up[slot], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record(stream)
         ring_ev[slot] = ev

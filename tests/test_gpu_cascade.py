@@ -146,3 +146,21 @@ def test_head_shapes(hq, hkv, d):
     assert list(gs) == [0, 3, 4, 6] and list(sb) == [6, 0, 18]
     out = run.decode_cascade(0, 0).double().cpu().numpy()
     check(out, ref.attention(0, 0), f"Hq={hq} Hkv={hkv} d={d}")
+
+
+def test_timing_events_leave_results_unchanged():
+    announce("kv_timing_events on the cascade (config 3): outputs bit-identical, prefix time <= call time")
+    wl = workloads.shared_prefix()
+    run = GpuRun(wl).run()
+    plain = run.decode_cascade(0, 0)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        evs = tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+        for e in evs:
+            e.record(stream)
+        got = run.decode_cascade(0, 0, opts=B.attention_options(timing=evs))
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), plain.view(torch.int32))
+        k_ms, c_ms = evs[0].elapsed_time(evs[1]), evs[0].elapsed_time(evs[2])
+        print(f"  preparation + prefix {k_ms * 1e3:.1f} us, call {c_ms * 1e3:.1f} us", flush=True)
+        assert 0.0 < k_ms <= c_ms

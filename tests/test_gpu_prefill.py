@@ -177,3 +177,26 @@ def test_contract_violations_give_nan_rows_or_errors():
         run.pool.prefill(0, q, q.clone(), indptr[:2].contiguous(), tables[:1].contiguous(), lens[:1].contiguous(),
                          40, 30)
     torch.cuda.synchronize()
+
+
+def test_timing_events_leave_results_unchanged():
+    announce("kv_timing_events on verification calls: outputs bit-identical, kernel time <= call time")
+    wl = workloads.verify_drafts()
+    run = GpuRun(wl).run()
+    rec = run.prefills[0]
+    d_tables = torch.from_numpy(rec["tables"]).cuda()
+    d_lens = torch.from_numpy(rec["lengths"]).cuda()
+    counts = rec["counts"]
+    d_indptr = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    plain = run.prefill(0, 0, d_indptr, d_tables, d_lens, max(counts))
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        evs = tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+        for e in evs:
+            e.record(stream)
+        got = run.prefill(0, 0, d_indptr, d_tables, d_lens, max(counts), opts=B.attention_options(timing=evs))
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), plain.view(torch.int32))
+        k_ms, c_ms = evs[0].elapsed_time(evs[1]), evs[0].elapsed_time(evs[2])
+        print(f"  kernel {k_ms * 1e3:.1f} us, call {c_ms * 1e3:.1f} us", flush=True)
+        assert 0.0 < k_ms <= c_ms
