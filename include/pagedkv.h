@@ -380,7 +380,9 @@ typedef enum {
  *                multi-query kernel of paged_attention_prefill (both the
  *                call's first kernel, so start .. kernel_stop is that kernel
  *                alone), the prefix-phase kernel of the cascade (start ..
- *                kernel_stop then also spans the preparation kernel);
+ *                kernel_stop then also spans the preparation kernel), the
+ *                last decode kernel of the row-wise prefill path (after its
+ *                row-length kernel and any earlier batches);
  *   stop         end of the call's last kernel.
  * Where the last kernel is also the one that streams the cache (one-kernel
  * calls), stop is recorded right after it as an ordinary event.  The caller
@@ -481,8 +483,9 @@ uint64_t paged_prefill_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int3
  * head h reading KV head g = h / (Hq / Hkv):
  *     out[r][h] = sum_{t <= h_s + j} softmax_t(scale * q[r][h] . k_t) v_t.
  * A sequence with c = 1 is a decode query.
- *   q, out:          device [total_q][Hq][d] bf16, rows grouped by sequence
- *                    as q_indptr says; out rounded to nearest even.
+ *   q, out:          device [total_q][Hq][d], rows grouped by sequence as
+ *                    q_indptr says; bf16 (rounded to nearest even) for bf16
+ *                    and quantised pools, f32 for f32 pools.
  *   d_q_indptr:      device int32[n_seqs + 1], non-decreasing, q_indptr[0] = 0,
  *                    q_indptr[n_seqs] <= total_q.  Rows of a sequence that
  *                    would fall outside [0, total_q) are not written.
@@ -494,10 +497,20 @@ uint64_t paged_prefill_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int3
  *                    aligned (NULL if that is 0); no initialisation needed.
  * A table entry outside [0, N) is never dereferenced: every row whose visible
  * keys include it is written as NaN, and so may be the other rows of its
- * query tile (16 consecutive columns of (row, head)).  Only the matrix-core kernel
- * exists (bf16, B = 16, d in {64, 128, 256}, G <= 16); other pools give
- * KV_ERR_UNSUPPORTED.  opts->partition_tokens splits every tile's keys into
- * partitions merged with the [KVM] recurrences (0 = the library's choice). */
+ * query tile (16 consecutive columns of (row, head)) on the multi-query
+ * kernel.  Two paths:
+ *   multi-query kernel: bf16 pools with B = 16, d in {64, 128, 256}, G <= 16
+ *     (KV_KERNEL_AUTO or KV_KERNEL_MFMA); one tile of columns reads each
+ *     block once for all its rows;
+ *   row-wise: every other pool, and any pool with KV_KERNEL_GENERIC -- each
+ *     chunk row is a decode query over its n - c + j + 1 keys, through the
+ *     decode kernels (the matrix-core split-K kernel for quantised pools,
+ *     batches of at most 4095 rows; the generic kernel for f32 and bf16), so
+ *     the history is read once per row.  Rows no sequence owns are written
+ *     as zero rows.  KV_KERNEL_MFMA on a pool no matrix-core kernel reads
+ *     gives KV_ERR_UNSUPPORTED.
+ * opts->partition_tokens splits every tile's (row's) keys into partitions
+ * merged with the [KVM] recurrences (0 = the library's choice). */
 kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, void* out,
                                   const int32_t* d_q_indptr, const int32_t* d_block_tables,
                                   const int32_t* d_context_lens, int32_t n_seqs, int32_t total_q,

@@ -239,6 +239,9 @@ struct attn_args {
   int n_seqs, max_blocks, n_q_heads, n_kv_heads, head_dim, block_size, num_blocks;
   int partition_tokens, max_parts;
   float scale_log2;  // scale * log2(e)
+  // row of `tables` that sequence s reads (NULL: row s); a negative row has
+  // no valid entry (the sequence's output is NaN)
+  const int32_t* table_rows;
 };
 
 struct work_item {
@@ -322,7 +325,8 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
 
   const T* kl = static_cast<const T*>(a.k_layer);
   const T* vl = static_cast<const T*>(a.v_layer);
-  const int32_t* table = a.tables + static_cast<int64_t>(w.seq) * a.max_blocks;
+  const int trow = a.table_rows ? a.table_rows[w.seq] : w.seq;
+  const int32_t* table = a.tables + static_cast<int64_t>(max(trow, 0)) * a.max_blocks;
   const int64_t tile_elems = static_cast<int64_t>(B) * D;
 
   float m_run[kMaxGroup], l_lane[kMaxGroup], acc[kMaxGroup][DPL];
@@ -344,7 +348,7 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
     int64_t base = 0;
     int r = 0;
     if (valid) {
-      const int p = table[t / B];
+      const int p = trow >= 0 ? table[t / B] : -1;
       r = t % B;
       if (p < 0 || p >= a.num_blocks) {
         valid = false;
@@ -580,6 +584,41 @@ __device__ __forceinline__ void attend_qblock(const kv_regs<D>& cur, const kv_qr
 // per-partition writes.
 // ---------------------------------------------------------------------------
 
+// ---------------------------------------------------------------------------
+// Multi-query attention as one decode query per chunk row, for the pools the
+// multi-query kernel does not read.  Chunk row j of sequence s (c rows,
+// context n) sees the keys 0 .. n - c + j ([KVM] chunked prefill mechanism:
+// the history and the chunk rows up to its own), so it is a decode query over
+// the first n - c + j + 1 keys of s's table.  This kernel writes, per row r,
+// that length and the table row to read; the rows of a sequence with
+// c > max_q_len or c > n get table row -1 (the decode writes NaN), rows no
+// sequence owns get length 0 (a zero row).
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) prefill_rows_kernel(const int32_t* __restrict__ q_indptr,
+                                                           const int32_t* __restrict__ ctx, int n_seqs, int total_q,
+                                                           int max_q_len, int cap, int32_t* __restrict__ row_len,
+                                                           int32_t* __restrict__ row_table) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= total_q) return;
+  int len = 0, trow = 0;
+  if (n_seqs > 0 && r >= q_indptr[0] && r < q_indptr[n_seqs]) {
+    int lo = 0, hi = n_seqs - 1;  // the last sequence whose first row is <= r
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (q_indptr[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    const int q0 = q_indptr[lo];
+    const int c = q_indptr[lo + 1] - q0;
+    const int n = min(ctx[lo], cap);
+    const bool bad = c > max_q_len || c > n;
+    len = bad ? 1 : n - c + (r - q0) + 1;
+    trow = bad ? -1 : lo;
+  }
+  row_len[r] = len;
+  row_table[r] = trow;
+}
+
 constexpr int kSkWaves = 4;     // waves per workgroup
 constexpr int kSkQUnits = 4;    // at most this many units per wave have staged queries
 
@@ -596,6 +635,9 @@ struct sk_args {
   int q_units;  // units per wave whose queries are staged in LDS (<= kSkQUnits)
   float scale_log2;
   int force_partial;  // every unit ends in partials (the cascade merge folds them with a prefix)
+  // row of the tables that sequence s reads (NULL: row s); a negative row has
+  // no valid entry (the sequence's output is NaN)
+  const int32_t* table_rows;
 };
 
 // LDS ints before the staged queries: cum_b, cum_p (n + 1 each) and ctx_n
@@ -657,7 +699,7 @@ __device__ __forceinline__ void sk_prefix(const sk_args& a, const int32_t* __res
 // Position of a wave's run in (sequence, kv head, block) terms.  All fields
 // are wave uniform.
 struct sk_cursor {
-  int seq, kvh, j, nb, n;
+  int seq, kvh, j, nb, n, trow;  // trow: the table row of seq
 };
 
 template <int D, int STAGES, int WAVES_PER_SIMD, int FMT>
@@ -712,6 +754,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     c.j = static_cast<int>(r % np) * a.part_blocks;
     c.nb = cb(lo + 1) - cb(lo);
     c.n = cn(lo);
+    c.trow = a.table_rows ? a.table_rows[lo] : lo;
   };
   sk_cursor first, last;
   locate(p_begin, first);
@@ -733,6 +776,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     } while (c.seq < a.n_seqs - 1 && cb(c.seq + 1) == cb(c.seq));
     c.nb = cb(c.seq + 1) - cb(c.seq);
     c.n = cn(c.seq);
+    c.trow = a.table_rows ? a.table_rows[c.seq] : c.seq;
   };
 
   // ring entries: bf16 operand tiles, or raw quantised tiles (codes and scales) converted on use
@@ -747,7 +791,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
   int ld_k = 0;
   int phys_ring[STAGES];
   auto issue = [&](ring_t& buf, int u) {
-    const int phys = tables[static_cast<int64_t>(ld.seq) * a.max_blocks + ld.j];
+    const int phys = ld.trow >= 0 ? tables[static_cast<int64_t>(ld.trow) * a.max_blocks + ld.j] : -1;
     phys_ring[u] = phys;
     const int p = (phys < 0 || phys >= a.num_blocks) ? 0 : phys;  // never dereferenced out of range
     if constexpr (FMT == kFmtBf16) {
@@ -1438,7 +1482,185 @@ hipError_t launch_generic(const attn_args& a, int64_t grid, hipStream_t st, hipE
   return launch_timed(attn_generic_kernel<T, D>, dim3(static_cast<unsigned>(grid)), dim3(256), 0u, st, ev0, ev1, a);
 }
 
+// The decode kernels and their merge for arguments already checked.  Sequence
+// s reads row table_rows[s] of the tables (row s when table_rows is NULL).
+kv_status decode_launch(const kv_pool* pool, int layer, const void* q, void* out, const int32_t* d_block_tables,
+                        const int32_t* d_context_lens, const int32_t* table_rows, int n_seqs, int max_blocks_per_seq,
+                        int num_q_heads, const resolved& r, void* d_workspace, hipStream_t st,
+                        const call_events& ev) {
+  const kv_pool_config& c = pool->cfg;
+  const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
+  const void* k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
+  const void* v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
+  const int G = num_q_heads / c.num_kv_heads;
+  hipError_t e = hipSuccess;
+
+  if (r.kernel == KV_KERNEL_MFMA) {
+    sk_args a{};
+    a.q = q;
+    a.out = out;
+    a.k_layer = k_layer;
+    a.v_layer = v_layer;
+    const uint64_t slots = static_cast<uint64_t>(r.groups) * kSkWaves + static_cast<uint64_t>(n_seqs) * c.num_kv_heads;
+    char* ws = static_cast<char*>(d_workspace);
+    a.part_m = reinterpret_cast<float*>(ws);
+    a.part_l = reinterpret_cast<float*>(ws + up256(slots * G * 4));
+    a.part_o = reinterpret_cast<float*>(ws + 2 * up256(slots * G * 4));
+    a.cum_parts = reinterpret_cast<int32_t*>(ws + 2 * up256(slots * G * 4) + up256(slots * G * c.head_dim * 4));
+    a.n_seqs = n_seqs;
+    a.max_blocks = max_blocks_per_seq;
+    a.n_q_heads = num_q_heads;
+    a.n_kv_heads = c.num_kv_heads;
+    a.num_blocks = c.num_blocks;
+    a.part_blocks = r.partition / c.block_size;
+    a.table_rows = table_rows;
+    a.n_waves = static_cast<int>(r.groups * kSkWaves);
+    a.q_units = sk_q_units(n_seqs, G, c.head_dim);
+    a.scale_log2 = r.scale * kLog2e;
+    auto launch = [&](auto fmt) {
+      constexpr int F = decltype(fmt)::value;
+      switch (c.head_dim) {
+        case 64: return launch_mfma<64, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
+        case 128: return launch_mfma<128, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
+        default: return launch_mfma<256, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
+      }
+    };
+    if (c.dtype == KV_Q8_0) e = launch(std::integral_constant<int, kFmtQ8>{});
+    else if (c.dtype == KV_Q4_0) e = launch(std::integral_constant<int, kFmtQ4>{});
+    else e = launch(std::integral_constant<int, kFmtBf16>{});
+    if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
+    const unsigned mgrid =
+        static_cast<unsigned>((static_cast<int64_t>(n_seqs) * num_q_heads + kMergeItems - 1) / kMergeItems);
+    switch (c.head_dim) {
+      case 64: e = launch_timed(merge_sk_kernel<64>, dim3(mgrid), dim3(kMergeItems * 64), 0u, st, nullptr, ev.stop, a); break;
+      case 128: e = launch_timed(merge_sk_kernel<128>, dim3(mgrid), dim3(kMergeItems * 64), 0u, st, nullptr, ev.stop, a); break;
+      default: e = launch_timed(merge_sk_kernel<256>, dim3(mgrid), dim3(kMergeItems * 64), 0u, st, nullptr, ev.stop, a); break;
+    }
+    return hip_check(e, "paged attention merge launch");
+  }
+
+  const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * r.max_parts;
+  if (grid > 0x7fffffff) return fail(KV_ERR_INVALID, "grid too large");
+  attn_args a{};
+  a.q = q;
+  a.out = out;
+  a.tables = d_block_tables;
+  a.ctx_lens = d_context_lens;
+  a.k_layer = k_layer;
+  a.v_layer = v_layer;
+  if (r.max_parts > 1) {  // the partials need the workspace (workspace_for)
+    const uint64_t rows = static_cast<uint64_t>(n_seqs) * num_q_heads * r.max_parts;
+    char* ws = static_cast<char*>(d_workspace);
+    a.part_m = reinterpret_cast<float*>(ws);
+    a.part_l = reinterpret_cast<float*>(ws + up256(rows * 4));
+    a.part_o = reinterpret_cast<float*>(ws + 2 * up256(rows * 4));
+  }
+  a.n_seqs = n_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.n_q_heads = num_q_heads;
+  a.n_kv_heads = c.num_kv_heads;
+  a.head_dim = c.head_dim;
+  a.block_size = c.block_size;
+  a.num_blocks = c.num_blocks;
+  a.partition_tokens = r.partition;
+  a.max_parts = r.max_parts;
+  a.scale_log2 = r.scale * kLog2e;
+  a.table_rows = table_rows;
+  const bool f32 = c.dtype == KV_F32;
+  auto gen = [&](auto d) {
+    constexpr int Dv = decltype(d)::value;
+    return f32 ? launch_generic<float, Dv>(a, grid, st, ev.start, ev.kernel_stop)
+               : launch_generic<uint16_t, Dv>(a, grid, st, ev.start, ev.kernel_stop);
+  };
+  switch (c.head_dim) {
+    case 32: e = gen(std::integral_constant<int, 32>{}); break;
+    case 64: e = gen(std::integral_constant<int, 64>{}); break;
+    case 96: e = gen(std::integral_constant<int, 96>{}); break;
+    case 128: e = gen(std::integral_constant<int, 128>{}); break;
+    case 160: e = gen(std::integral_constant<int, 160>{}); break;
+    case 192: e = gen(std::integral_constant<int, 192>{}); break;
+    case 224: e = gen(std::integral_constant<int, 224>{}); break;
+    default: e = gen(std::integral_constant<int, 256>{}); break;
+  }
+  if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
+  if (r.max_parts > 1) {
+    const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(n_seqs) * num_q_heads));
+    e = f32 ? launch_timed(merge_kernel<float>, mgrid, dim3(kMergeThreads), 0u, st, nullptr, ev.stop, a)
+            : launch_timed(merge_kernel<uint16_t>, mgrid, dim3(kMergeThreads), 0u, st, nullptr, ev.stop, a);
+    return hip_check(e, "paged attention merge launch");
+  }
+  if (ev.stop) return hip_check(hipEventRecord(ev.stop, st), "timing event");
+  return KV_OK;
+}
+
+
+// Row-wise multi-query path: rows go to the decode kernels in batches (the
+// split-K kernel takes at most kSkMaxSeqs sequences per launch).  Workspace:
+// per-row lengths and table rows, then the decode workspace of one batch.
+struct rowwise_plan {
+  resolved r;
+  int batch;
+  uint64_t rows_bytes, decode_off, total;
+};
+
+kv_status plan_rowwise(const kv_pool* pool, int total_q, int num_q_heads, int max_blocks,
+                       const kv_attention_options* opts, rowwise_plan& p) {
+  const int first = std::max(1, std::min(total_q, kSkMaxSeqs));
+  if (kv_status s = resolve(pool, first, num_q_heads, max_blocks, opts, p.r)) return s;
+  p.batch = p.r.kernel == KV_KERNEL_MFMA ? first : std::max(total_q, 1);
+  if (p.batch != first)  // the generic kernel takes every row at once; its partition depends on the count
+    if (kv_status s = resolve(pool, p.batch, num_q_heads, max_blocks, opts, p.r)) return s;
+  p.rows_bytes = up256(static_cast<uint64_t>(std::max(total_q, 1)) * 4);
+  p.decode_off = 2 * p.rows_bytes;
+  p.total = p.decode_off + up256(workspace_for(pool->cfg, p.batch, num_q_heads, p.r));
+  return KV_OK;
+}
+
 }  // namespace
+
+uint64_t prefill_rowwise_workspace(const kv_pool* pool, int total_q, int num_q_heads, int max_blocks,
+                                   const kv_attention_options* opts) {
+  rowwise_plan p;
+  if (plan_rowwise(pool, total_q, num_q_heads, max_blocks, opts, p) != KV_OK) return 0;
+  return p.total;
+}
+
+kv_status prefill_rowwise(kv_pool* pool, int layer, const void* q, void* out, const int32_t* q_indptr,
+                          const int32_t* tables, const int32_t* ctx, int n_seqs, int total_q, int max_q_len,
+                          int max_blocks, int num_q_heads, const kv_attention_options* opts, void* ws,
+                          uint64_t ws_bytes, hipStream_t st) {
+  const kv_pool_config& c = pool->cfg;
+  rowwise_plan p;
+  if (kv_status s = plan_rowwise(pool, total_q, num_q_heads, max_blocks, opts, p)) return s;
+  if (!ws || ws_bytes < p.total)
+    return fail(KV_ERR_INVALID, "workspace too small: need " + std::to_string(p.total) + " bytes");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(KV_ERR_INVALID, "workspace must be 256-byte aligned");
+  const call_events ev = events_of(opts);
+  char* w = static_cast<char*>(ws);
+  int32_t* row_len = reinterpret_cast<int32_t*>(w);
+  int32_t* row_table = reinterpret_cast<int32_t*>(w + p.rows_bytes);
+  const unsigned grid = static_cast<unsigned>((total_q + 255) / 256);
+  if (kv_status s = hip_check(launch_timed(prefill_rows_kernel, dim3(grid), dim3(256), 0u, st, ev.start, nullptr,
+                                           q_indptr, ctx, n_seqs, total_q, max_q_len, max_blocks * c.block_size,
+                                           row_len, row_table),
+                              "prefill row lengths launch"))
+    return s;
+  // q and out rows in the pool's element type (bf16 for quantised pools)
+  const int64_t row_bytes = static_cast<int64_t>(num_q_heads) * c.head_dim * (c.dtype == KV_F32 ? 4 : 2);
+  for (int b0 = 0; b0 < total_q; b0 += p.batch) {
+    const int n = std::min(p.batch, total_q - b0);
+    const bool last = b0 + p.batch >= total_q;
+    call_events e;
+    e.kernel_stop = last ? ev.kernel_stop : nullptr;
+    e.stop = last ? ev.stop : nullptr;
+    if (kv_status s = decode_launch(pool, layer, static_cast<const char*>(q) + b0 * row_bytes,
+                                    static_cast<char*>(out) + b0 * row_bytes, tables, row_len + b0, row_table + b0,
+                                    n, max_blocks, num_q_heads, p.r, w + p.decode_off, st, e))
+      return s;
+  }
+  return KV_OK;
+}
+
 }  // namespace pagedkv
 
 using namespace pagedkv;
@@ -1548,108 +1770,8 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     return fail(KV_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
   if (need > 0 && (reinterpret_cast<uintptr_t>(d_workspace) & 255))
     return fail(KV_ERR_INVALID, "workspace must be 256-byte aligned");
-  const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
-  const void* k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
-  const void* v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const int G = num_q_heads / c.num_kv_heads;
-  const call_events ev = events_of(opts);
-  hipError_t e = hipSuccess;
-
-  if (r.kernel == KV_KERNEL_MFMA) {
-    sk_args a{};
-    a.q = q;
-    a.out = out;
-    a.k_layer = k_layer;
-    a.v_layer = v_layer;
-    const uint64_t slots = static_cast<uint64_t>(r.groups) * kSkWaves + static_cast<uint64_t>(n_seqs) * c.num_kv_heads;
-    char* ws = static_cast<char*>(d_workspace);
-    a.part_m = reinterpret_cast<float*>(ws);
-    a.part_l = reinterpret_cast<float*>(ws + up256(slots * G * 4));
-    a.part_o = reinterpret_cast<float*>(ws + 2 * up256(slots * G * 4));
-    a.cum_parts = reinterpret_cast<int32_t*>(ws + 2 * up256(slots * G * 4) + up256(slots * G * c.head_dim * 4));
-    a.n_seqs = n_seqs;
-    a.max_blocks = max_blocks_per_seq;
-    a.n_q_heads = num_q_heads;
-    a.n_kv_heads = c.num_kv_heads;
-    a.num_blocks = c.num_blocks;
-    a.part_blocks = r.partition / c.block_size;
-    a.n_waves = static_cast<int>(r.groups * kSkWaves);
-    a.q_units = sk_q_units(n_seqs, G, c.head_dim);
-    a.scale_log2 = r.scale * kLog2e;
-    auto launch = [&](auto fmt) {
-      constexpr int F = decltype(fmt)::value;
-      switch (c.head_dim) {
-        case 64: return launch_mfma<64, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
-        case 128: return launch_mfma<128, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
-        default: return launch_mfma<256, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
-      }
-    };
-    if (c.dtype == KV_Q8_0) e = launch(std::integral_constant<int, kFmtQ8>{});
-    else if (c.dtype == KV_Q4_0) e = launch(std::integral_constant<int, kFmtQ4>{});
-    else e = launch(std::integral_constant<int, kFmtBf16>{});
-    if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
-    const unsigned mgrid =
-        static_cast<unsigned>((static_cast<int64_t>(n_seqs) * num_q_heads + kMergeItems - 1) / kMergeItems);
-    switch (c.head_dim) {
-      case 64: e = launch_timed(merge_sk_kernel<64>, dim3(mgrid), dim3(kMergeItems * 64), 0u, st, nullptr, ev.stop, a); break;
-      case 128: e = launch_timed(merge_sk_kernel<128>, dim3(mgrid), dim3(kMergeItems * 64), 0u, st, nullptr, ev.stop, a); break;
-      default: e = launch_timed(merge_sk_kernel<256>, dim3(mgrid), dim3(kMergeItems * 64), 0u, st, nullptr, ev.stop, a); break;
-    }
-    return hip_check(e, "paged attention merge launch");
-  }
-
-  const int64_t grid = static_cast<int64_t>(n_seqs) * c.num_kv_heads * r.max_parts;
-  if (grid > 0x7fffffff) return fail(KV_ERR_INVALID, "grid too large");
-  attn_args a{};
-  a.q = q;
-  a.out = out;
-  a.tables = d_block_tables;
-  a.ctx_lens = d_context_lens;
-  a.k_layer = k_layer;
-  a.v_layer = v_layer;
-  if (need > 0) {
-    const uint64_t rows = static_cast<uint64_t>(n_seqs) * num_q_heads * r.max_parts;
-    char* ws = static_cast<char*>(d_workspace);
-    a.part_m = reinterpret_cast<float*>(ws);
-    a.part_l = reinterpret_cast<float*>(ws + up256(rows * 4));
-    a.part_o = reinterpret_cast<float*>(ws + 2 * up256(rows * 4));
-  }
-  a.n_seqs = n_seqs;
-  a.max_blocks = max_blocks_per_seq;
-  a.n_q_heads = num_q_heads;
-  a.n_kv_heads = c.num_kv_heads;
-  a.head_dim = c.head_dim;
-  a.block_size = c.block_size;
-  a.num_blocks = c.num_blocks;
-  a.partition_tokens = r.partition;
-  a.max_parts = r.max_parts;
-  a.scale_log2 = r.scale * kLog2e;
-  const bool f32 = c.dtype == KV_F32;
-  auto gen = [&](auto d) {
-    constexpr int Dv = decltype(d)::value;
-    return f32 ? launch_generic<float, Dv>(a, grid, st, ev.start, ev.kernel_stop)
-               : launch_generic<uint16_t, Dv>(a, grid, st, ev.start, ev.kernel_stop);
-  };
-  switch (c.head_dim) {
-    case 32: e = gen(std::integral_constant<int, 32>{}); break;
-    case 64: e = gen(std::integral_constant<int, 64>{}); break;
-    case 96: e = gen(std::integral_constant<int, 96>{}); break;
-    case 128: e = gen(std::integral_constant<int, 128>{}); break;
-    case 160: e = gen(std::integral_constant<int, 160>{}); break;
-    case 192: e = gen(std::integral_constant<int, 192>{}); break;
-    case 224: e = gen(std::integral_constant<int, 224>{}); break;
-    default: e = gen(std::integral_constant<int, 256>{}); break;
-  }
-  if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
-  if (r.max_parts > 1) {
-    const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(n_seqs) * num_q_heads));
-    e = f32 ? launch_timed(merge_kernel<float>, mgrid, dim3(kMergeThreads), 0u, st, nullptr, ev.stop, a)
-            : launch_timed(merge_kernel<uint16_t>, mgrid, dim3(kMergeThreads), 0u, st, nullptr, ev.stop, a);
-    return hip_check(e, "paged attention merge launch");
-  }
-  if (ev.stop) return hip_check(hipEventRecord(ev.stop, st), "timing event");
-  return KV_OK;
+  return decode_launch(pool, layer, q, out, d_block_tables, d_context_lens, nullptr, n_seqs, max_blocks_per_seq,
+                       num_q_heads, r, d_workspace, static_cast<hipStream_t>(hip_stream), events_of(opts));
 }
 
 // ---- cascade decode over shared prefixes ---------------------------------

@@ -95,6 +95,16 @@ kv_status prefix_phase_launch(kv_pool* pool, int layer, const void* q, void* out
                               int max_group, int max_blocks, int num_q_heads, const kv_attention_options* opts,
                               void* ws, hipStream_t st, hipEvent_t ev_stop);
 
+// Multi-query attention for the pools the multi-query kernel does not read
+// (kernels.hip): one decode query per chunk row, through the decode kernels.
+// q and out rows are in the pool's element type (bf16 for quantised pools).
+uint64_t prefill_rowwise_workspace(const kv_pool* pool, int total_q, int num_q_heads, int max_blocks,
+                                   const kv_attention_options* opts);
+kv_status prefill_rowwise(kv_pool* pool, int layer, const void* q, void* out, const int32_t* q_indptr,
+                          const int32_t* tables, const int32_t* ctx, int n_seqs, int total_q, int max_q_len,
+                          int max_blocks, int num_q_heads, const kv_attention_options* opts, void* ws,
+                          uint64_t ws_bytes, hipStream_t st);
+
 // Device side of a swap (swap.hip): pairs are (block, frame) for direction 0
 // (out) and (frame, block) for direction 1 (in); checked by the caller.
 kv_status swap_copy(kv_pool* pool, const int32_t* pairs, int32_t n, int32_t direction, void* d_staging,

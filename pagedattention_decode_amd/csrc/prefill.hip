@@ -859,6 +859,16 @@ hipError_t pf_merge(const pf_args& a, hipStream_t st, hipEvent_t ev1) {
                       nullptr, ev1, a);
 }
 
+// Whether a call goes to the row-wise path (one decode query per chunk row):
+// the generic kernel asked for, or a pool the multi-query kernel does not read
+// (f32, quantised, B != 16, other head sizes).
+bool rowwise(const kv_pool* pool, int num_q_heads, const kv_attention_options* opts) {
+  if (!pool || num_q_heads <= 0 || num_q_heads % pool->cfg.num_kv_heads != 0) return false;
+  const int G = num_q_heads / pool->cfg.num_kv_heads;
+  if (opts && opts->kernel == KV_KERNEL_GENERIC) return true;
+  return !(mfma_supported(pool->cfg, G) && pool->cfg.dtype == KV_BF16);
+}
+
 }  // namespace
 
 // The prefix phase of the cascade decode (kernels.hip): the members of every
@@ -934,6 +944,10 @@ extern "C" {
 uint64_t paged_prefill_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int32_t total_q, int32_t max_q_len,
                                        int32_t num_q_heads, int32_t max_blocks_per_seq,
                                        const kv_attention_options* opts) {
+  if (rowwise(pool, num_q_heads, opts)) {
+    if (n_seqs < 0 || total_q < 0 || max_q_len <= 0 || max_blocks_per_seq <= 0) return 0;
+    return prefill_rowwise_workspace(pool, total_q, num_q_heads, max_blocks_per_seq, opts);
+  }
   pf_plan p;
   if (pf_resolve(pool, n_seqs, total_q, max_q_len, num_q_heads, max_blocks_per_seq, opts, p) != KV_OK) return 0;
   return pf_workspace(pool->cfg, total_q, num_q_heads, p);
@@ -944,6 +958,20 @@ kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, v
                                   int32_t total_q, int32_t max_q_len, int32_t max_blocks_per_seq,
                                   int32_t num_q_heads, const kv_attention_options* opts, void* d_workspace,
                                   uint64_t workspace_bytes, void* hip_stream) {
+  if (rowwise(pool, num_q_heads, opts)) {
+    const kv_pool_config& c = pool->cfg;
+    if (layer < 0 || layer >= c.num_layers) return fail(KV_ERR_INVALID, "layer out of range");
+    if (n_seqs < 0 || total_q < 0 || max_q_len <= 0 || max_blocks_per_seq <= 0)
+      return fail(KV_ERR_INVALID, "n_seqs, total_q >= 0 and max_q_len, max_blocks_per_seq > 0 required");
+    if (n_seqs == 0 || total_q == 0) return KV_OK;
+    if (!q || !out || !d_q_indptr || !d_block_tables || !d_context_lens || !pool->k_cache || !pool->v_cache)
+      return fail(KV_ERR_INVALID, "NULL device pointer");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+      return fail(KV_ERR_INVALID, "q and out must be 16-byte aligned");
+    return prefill_rowwise(pool, layer, q, out, d_q_indptr, d_block_tables, d_context_lens, n_seqs, total_q,
+                           max_q_len, max_blocks_per_seq, num_q_heads, opts, d_workspace, workspace_bytes,
+                           static_cast<hipStream_t>(hip_stream));
+  }
   pf_plan p;
   if (kv_status s = pf_resolve(pool, n_seqs, total_q, max_q_len, num_q_heads, max_blocks_per_seq, opts, p)) return s;
   const kv_pool_config& c = pool->cfg;

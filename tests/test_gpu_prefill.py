@@ -160,15 +160,7 @@ def test_contract_violations_give_nan_rows_or_errors():
     out = run.prefill(0, 0, indptr2, tables, lens, 1)
     o = out.double().cpu().numpy()
     assert np.isnan(o[0:80]).all()
-    # unsupported pool and bad options
-    f32 = workloads.tiny_fp32()
-    r2 = GpuRun(f32)
-    z = torch.zeros((1, 4, 64), dtype=torch.int32, device="cuda")
-    with pytest.raises(B.KVError) as e:
-        r2.pool.prefill(0, z, z.clone(), torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
-                        torch.zeros((1, 2), dtype=torch.int32, device="cuda"),
-                        torch.ones((1,), dtype=torch.int32, device="cuda"), 1, 4)
-    assert e.value.status == B.KV_ERR_UNSUPPORTED
+    # bad options
     q = torch.zeros((40, 32, 128), dtype=torch.int16, device="cuda")
     with pytest.raises(B.KVError):
         run.pool.prefill(0, q, q.clone(), indptr[:2].contiguous(), tables[:1].contiguous(), lens[:1].contiguous(),

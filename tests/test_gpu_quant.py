@@ -187,7 +187,7 @@ def test_quantised_qwen_layer_full(fmt):
 
 
 def test_quantised_pool_rejects_other_kernels_and_shapes():
-    announce("quantised pools: generic kernel, multi-query path and B != 16 are refused")
+    announce("quantised pools: the generic kernel and B != 16 are refused")
     wl = quant_workload("q8_0", lengths=(20,), layers=1)
     run = GpuRun(wl).run()
     tables, lens = run.pool.tables([0], run.max_blocks)
@@ -198,7 +198,8 @@ def test_quantised_pool_rejects_other_kernels_and_shapes():
         run.pool.decode(0, q, q.clone(), t, l_, 32, opts=B.attention_options(kernel=B.KV_KERNEL_GENERIC))
     assert e.value.status == B.KV_ERR_UNSUPPORTED
     with pytest.raises(B.KVError) as e:
-        run.pool.prefill(0, q, q.clone(), torch.tensor([0, 1], dtype=torch.int32, device="cuda"), t, l_, 1, 32)
+        run.pool.prefill(0, q, q.clone(), torch.tensor([0, 1], dtype=torch.int32, device="cuda"), t, l_, 1, 32,
+                         opts=B.attention_options(kernel=B.KV_KERNEL_GENERIC))
     assert e.value.status == B.KV_ERR_UNSUPPORTED
     with pytest.raises(B.KVError) as e:
         B.kv_pool_required_bytes(B.make_config(1, 4, 8, 2, 128, B.KV_Q8_0))
