@@ -10,14 +10,19 @@ A step is one decode step of the workload through the whole path:
 Inputs (queries, new K/V rows) for every timed step are resident in HBM
 before the timed region; the pool is filled once, before warm-up.
 
-Workloads (synthetic, seeded; see synth/workloads.py):
-  2  Qwen3-8B-shaped layer: 37 sequences x 2304 tokens, Hq=32, Hkv=8, d=128,
-     B=16, bf16; 4 layer buffers rotated so the 256 MB last-level cache
-     cannot hold the working set (1.4 GB per step).       (default)
-  3  16 x 8448 tokens sharing a 6144-token prefix, same shapes, 4 layers.
-  4  70B-GQA-shaped layer: 12 x 131072 tokens, Hq=64, split-K 512.
-  5  agentic fork: 64 sequences (4 roots x 16 forks) x ~33K tokens, 36 layers.
---cascade (configs 3, 5) decodes through paged_attention_decode_cascade: the
+Workloads (--workload; synthetic, seeded; see synth/workloads.py):
+  qwen3_8b_37x2304       Qwen3-8B-shaped layer: 37 sequences x 2304 tokens,
+                         Hq=32, Hkv=8, d=128, B=16, bf16; 4 layer buffers
+                         rotated so the 256 MB last-level cache cannot hold
+                         the working set (1.4 GB per step).   (default)
+  shared_prefix_16x8448  16 x 8448 tokens sharing a 6144-token prefix, same
+                         shapes, 4 layers.
+  gqa70b_12x131072       70B-GQA-shaped layer: 12 x 131072 tokens, Hq=64,
+                         split-K 512.
+  agentic_fork_64x33281  64 sequences (4 roots x 16 forks) x ~33K tokens,
+                         36 layers.
+--cascade (the shared-prefix and fork workloads) decodes through
+paged_attention_decode_cascade: the
 groups come from kv_shared_prefix_plan every step, each group's shared prefix
 is read once; roofline bytes then count the prefix once per group.
 
@@ -93,18 +98,24 @@ def pcts(ms):
     return [round(float(np.percentile(ms, q)) * 1e3, 2) for q in (10, 50, 90)]
 
 
+# layer buffers per step of each decode workload
+DECODE_LAYERS = {"qwen3_8b_37x2304": 4, "shared_prefix_16x8448": 4, "gqa70b_12x131072": 1,
+                 "agentic_fork_64x33281": 36}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", default="qwen3_8b_37x2304", choices=list(DECODE_LAYERS),
+                    help="the decode workload of --op decode")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "q8_0", "q4_0"],
                     help="storage of the KV pool for --op decode: bf16, or q8_0 / q4_0 codes with one 2-byte "
                          "scale per 32 values (written by reshape_and_cache, dequantised in the kernel)")
     ap.add_argument("--swap-seqs", type=int, default=8, help="--op swap: sequences swapped out and back in per step")
     ap.add_argument("--op", default="decode", choices=["decode", "prefill", "verify", "swap"],
-                    help="decode: the decode step of --config; prefill: the last 512-token chunk of 16 "
+                    help="decode: the decode step of --workload; prefill: the last 512-token chunk of 16 "
                          "8K prompts; verify: 8 draft positions for 16 requests with 8K contexts")
     ap.add_argument("--cascade", action="store_true",
                     help="decode through paged_attention_decode_cascade (shared prefixes read once per group)")
@@ -178,9 +189,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    base = workloads.get_workload(args.config) if args.config != 5 else workloads.agentic_fork(steps=1)
-    default_layers = {2: 4, 3: 4, 4: 1, 5: 36}[args.config]
-    L = args.layers or default_layers
+    fork = args.workload == "agentic_fork_64x33281"
+    base = workloads.agentic_fork(steps=1) if fork else workloads.get_workload(args.workload)
+    L = args.layers or DECODE_LAYERS[args.workload]
     seed = args.seed or base.seed
     partition = base.partition_tokens if args.partition < 0 else args.partition
     kernel = {"auto": B.KV_KERNEL_AUTO, "mfma": B.KV_KERNEL_MFMA, "generic": B.KV_KERNEL_GENERIC}[args.kernel]
@@ -404,7 +415,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(base.name + ("" if args.kv == "bf16" else f"_{args.kv}")
                                         + ("_cascade" if args.cascade else ""),
-                                        ("kernels.hip", "prefill.hip") if args.cascade else ("kernels.hip",)),
+                                        ("kernels.hip", "prefill.hip") if args.cascade else ("kernels.hip",),
+                                        "traffic_bytes_per_call" if args.cascade else "traffic_bytes_per_launch"),
             "kernel": ("paged_attention_decode_cascade (whole call: preparation, prefix multi-query kernel, "
                        "split-K kernel, merge)" if args.cascade else "attn_mfma_kernel (split-K partition kernel)"),
             "duration_us": round(roof_s * 1e6, 2),
@@ -961,16 +973,16 @@ def cpu_baseline(args):
     from synth import workloads
 
     cores = len(os.sched_getaffinity(0))
-    cfg = args.config
-    if cfg == 2:
+    name = args.workload
+    if name == "qwen3_8b_37x2304":
         wl = workloads.qwen_independent()
         layers, writers = None, None
         sample = "Qwen3-8B-shaped layer: the oracle's decode of all 37 sequences x 2304 tokens, one layer"
-    elif cfg == 3:
+    elif name == "shared_prefix_16x8448":
         wl = workloads.shared_prefix()
         layers, writers = None, None
         sample = "shared-prefix layer: the oracle's decode of all 16 sequences x 8448 tokens, one layer"
-    elif cfg == 4:
+    elif name == "gqa70b_12x131072":
         wl = workloads.gqa70b_128k()
         layers, writers = None, {0}
         sample = "70B-GQA layer: the oracle's decode of sequence 0 (131072 tokens, 64 heads)"

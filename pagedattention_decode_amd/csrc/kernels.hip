@@ -716,7 +716,6 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = (lane & 15) % G;  // query head (within the group) of this lane's column
   const int quad = lane >> 4;      // 4-token group / 8-dim group of this lane
-  const int cap = a.max_blocks * 16;
 
   sk_prefix(a, ctx_lens, cum_b, cum_p, ctx_n);
   if (blockIdx.x == 0)
@@ -1083,7 +1082,7 @@ __global__ void __launch_bounds__(kMergeItems * 64) merge_sk_kernel(sk_args a) {
 // length for the prefix phase.
 __global__ void __launch_bounds__(256) cascade_prep_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ ctx, const int32_t* __restrict__ group_start,
-    const int32_t* __restrict__ shared, int n_seqs, int n_groups, int max_group, int max_blocks,
+    const int32_t* __restrict__ shared, int n_groups, int max_group, int max_blocks,
     int32_t* __restrict__ tables_sfx, int32_t* __restrict__ ctx_sfx, int32_t* __restrict__ prefix_ctx,
     int2* __restrict__ info) {
   __shared__ int grp;  // the member's group
@@ -1420,7 +1419,7 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
   const int G = num_q_heads / c.num_kv_heads;
   if (G > kMaxGroup) return fail(KV_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
   if (n_seqs < 0 || max_blocks <= 0) return fail(KV_ERR_INVALID, "n_seqs must be >= 0 and max_blocks_per_seq > 0");
-  kv_attention_options o{0.f, 0, KV_KERNEL_AUTO};
+  kv_attention_options o{0.f, 0, KV_KERNEL_AUTO, nullptr};
   if (opts) o = *opts;
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_GENERIC && o.kernel != KV_KERNEL_MFMA)
     return fail(KV_ERR_INVALID, "unknown kernel selector");
@@ -1847,7 +1846,7 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   const call_events ev = events_of(opts);
   if (kv_status s = hip_check(
           launch_timed(cascade_prep_kernel, dim3(static_cast<unsigned>(n_seqs)), dim3(256), 0u, st, ev.start, nullptr,
-                       d_block_tables, d_context_lens, d_group_start, d_shared_blocks, n_seqs, n_groups, max_group,
+                       d_block_tables, d_context_lens, d_group_start, d_shared_blocks, n_groups, max_group,
                        max_blocks_per_seq, tables_sfx, ctx_sfx, prefix_ctx, info),
           "cascade prep launch"))
     return s;

@@ -764,7 +764,7 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   const int G = num_q_heads / c.num_kv_heads;
   if (n_seqs < 0 || total_q < 0 || max_blocks <= 0 || max_q_len <= 0)
     return fail(KV_ERR_INVALID, "n_seqs, total_q >= 0 and max_q_len, max_blocks_per_seq > 0 required");
-  kv_attention_options o{0.f, 0, KV_KERNEL_AUTO};
+  kv_attention_options o{0.f, 0, KV_KERNEL_AUTO, nullptr};
   if (opts) o = *opts;
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_MFMA)
     return fail(KV_ERR_UNSUPPORTED, "multi-query attention has only the matrix-core kernel");

@@ -23,4 +23,4 @@ from .draws import (  # noqa: F401
     normal_bits,
     token_rows,
 )
-from .workloads import CONFIGS, Workload, get_workload  # noqa: F401
+from .workloads import WORKLOADS, Workload, get_workload  # noqa: F401

@@ -94,12 +94,14 @@ def tiny_fp32() -> Workload:
                     description="fp32 Hq=4 Hkv=1 d=64 B=4, lengths 5/7/9, pool 16")
 
 
-# Pool of configs 2 and 3: floor(12 GiB / 36 layers / 64 KiB per block-layer).
+# Pool of the Qwen3-8B-shaped workloads (37 x 2304 and 16 x 8448 tokens):
+# floor(12 GiB / 36 layers / 64 KiB per block-layer).
 POOL_QWEN = 5461
-# Pool of config 4: 12 sequences x 8192 blocks, the 60 GiB B=16 pool of the
-# 70B example.
+# Pool of the 70B-GQA workload: 12 sequences x 8192 blocks, the 60 GiB B=16
+# pool of the 70B example.
 POOL_70B = 98304
-# Pool of config 5: 10,304 blocks needed at the end plus ~16 % headroom.
+# Pool of the agentic fork workload: 10,304 blocks needed at the end plus ~16 %
+# headroom.
 POOL_FORK = 12288
 
 
@@ -233,14 +235,15 @@ def tool_pause(layers: int = 2, seed: int = 8, frames: str = "shuffled") -> Work
                     description="bf16 Hq=32 Hkv=8 d=128 B=16, 8 sequences, 2 swapped out and back in")
 
 
-CONFIGS = {
-    1: tiny_fp32,
-    2: qwen_independent,
-    3: shared_prefix,
-    4: gqa70b_128k,
-    5: agentic_fork,
+# The decode workloads by name (the name each builds).
+WORKLOADS = {
+    "tiny_fp32": tiny_fp32,
+    "qwen3_8b_37x2304": qwen_independent,
+    "shared_prefix_16x8448": shared_prefix,
+    "gqa70b_12x131072": gqa70b_128k,
+    "agentic_fork_64x33281": agentic_fork,
 }
 
 
-def get_workload(config: int, **kw) -> Workload:
-    return CONFIGS[config](**kw)
+def get_workload(name: str, **kw) -> Workload:
+    return WORKLOADS[name](**kw)

@@ -90,12 +90,13 @@ def replay_both(wl):
     return bm, n_checked
 
 
-@pytest.mark.parametrize("config", [1, 2, 3, 4])
-def test_workload_allocator_bit_exact(config):
-    wl = workloads.get_workload(config)
+@pytest.mark.parametrize("name, tokens", [("tiny_fp32", 21), ("qwen3_8b_37x2304", 37 * 2304),
+                                          ("shared_prefix_16x8448", 6144 + 16 * 2304),
+                                          ("gqa70b_12x131072", 12 * 131072)])
+def test_workload_allocator_bit_exact(name, tokens):
+    wl = workloads.get_workload(name)
     bm, n = replay_both(wl)
-    expect = {1: 21, 2: 37 * 2304, 3: 6144 + 16 * 2304, 4: 12 * 131072}[config]
-    assert n == expect
+    assert n == tokens
 
 
 def test_agentic_fork_allocator_bit_exact():

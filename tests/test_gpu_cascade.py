@@ -49,15 +49,15 @@ def fork_workload(groups, layers=1, seed=61, hq=32, hkv=8, d=128):
     return workloads.Workload("forks", seed, draws.BF16, layers, hq, hkv, d, 16, blocks + 16, ops)
 
 
-def test_shared_prefix_config3_full():
-    announce("config 3: 16 x 8448 sharing 6144, cascade decode vs oracle")
+def test_shared_prefix_16x8448_full():
+    announce("16 x 8448 tokens sharing 6144: cascade decode vs oracle")
     wl = workloads.shared_prefix()
     ref = OracleReplay(wl).run()
     run = GpuRun(wl, ref=ref).run()
     gs, sb = run.pool.shared_prefix_plan(run.decodes[0]["seq_ids"])
     assert list(gs) == [0, 16] and list(sb) == [384]
     out = run.decode_cascade(0, 0).double().cpu().numpy()
-    check(out, ref.attention(0, 0), "config 3 cascade")
+    check(out, ref.attention(0, 0), "16 x 8448 cascade")
 
 
 @pytest.mark.parametrize("partition", [0, 64, 512])
@@ -149,7 +149,7 @@ def test_head_shapes(hq, hkv, d):
 
 
 def test_timing_events_leave_results_unchanged():
-    announce("kv_timing_events on the cascade (config 3): outputs bit-identical, prefix time <= call time")
+    announce("kv_timing_events on the cascade (16 x 8448 sharing 6144): outputs bit-identical, prefix time <= call time")
     wl = workloads.shared_prefix()
     run = GpuRun(wl).run()
     plain = run.decode_cascade(0, 0)

@@ -4,7 +4,7 @@
   against the oracle's logical pool, with every unwritten element unchanged;
 * decode attention: fp32 within 1e-5 (max abs); bf16 within max abs 2e-2 and a
   per-row relative L2 error of 5e-3 against the float64 oracle;
-* the workloads at their full sizes (config 4 and the fork workload on sampled
+* the workloads at their full sizes (the 12 x 131072 and fork workloads on sampled
   sequences), ragged lengths, edge cases and both kernels.
 
 Every test prints the case it runs before touching the GPU.
@@ -125,8 +125,8 @@ def compare_all_decodes(run, ref, layers=None):
             check_outputs(got, ref.attention(i, layer), wl.dtype, f"decode {i} layer {layer}")
 
 
-def test_config1_tiny_fp32():
-    announce("config 1: tiny fp32, B=4, lengths 5/7/9, generic kernel, NaN background")
+def test_tiny_fp32_5_7_9():
+    announce("tiny fp32, B=4, lengths 5/7/9, generic kernel, NaN background")
     wl = workloads.tiny_fp32()
     ref = OracleReplay(wl).run()
     run = GpuRun(wl, ref=ref, fill=-1).run()  # 0xFFFFFFFF is a NaN: unwritten slots must never count
@@ -179,16 +179,16 @@ def test_head_shapes(hq, hkv, d):
         compare_all_decodes(run, ref)
 
 
-def test_config2_qwen_full():
-    announce("config 2: 37 x 2304 tokens, bf16, default launch")
+def test_qwen3_8b_37x2304_full():
+    announce("Qwen3-8B-shaped layer, 37 x 2304 tokens, bf16, default launch")
     wl = workloads.qwen_independent()
     ref = OracleReplay(wl).run()
     run = GpuRun(wl, ref=ref).run()
     compare_all_decodes(run, ref)
 
 
-def test_config3_shared_prefix_full():
-    announce("config 3: 16 x 8448 tokens sharing 6144, bf16, default launch")
+def test_shared_prefix_16x8448_full():
+    announce("16 x 8448 tokens sharing 6144, bf16, default launch")
     wl = workloads.shared_prefix()
     ref = OracleReplay(wl).run()
     run = GpuRun(wl, ref=ref).run()
@@ -198,15 +198,15 @@ def test_config3_shared_prefix_full():
     assert (tables[:, :384] == tables[0, :384]).all()
 
 
-def test_config4_long_context_sampled():
-    announce("config 4: 12 x 131072 tokens, Hq=64, split-K 512; sequences 0, 5, 11 checked")
+def test_gqa70b_12x131072_sampled():
+    announce("70B-GQA layer, 12 x 131072 tokens, Hq=64, split-K 512; sequences 0, 5, 11 checked")
     wl = workloads.gqa70b_128k()
     sample = [0, 5, 11]
     ref = OracleReplay(wl, writers=sample).run()
     run = GpuRun(wl, ref=ref, writers=sample, opts=B.attention_options(partition_tokens=512)).run()
     got = run.decode_outputs[0][0].double().cpu().numpy()
     expect = ref.attention(0, 0, rows=sample)
-    check_outputs(got[sample], expect, wl.dtype, "config 4 sampled")
+    check_outputs(got[sample], expect, wl.dtype, "12 x 131072 sampled")
 
 
 def test_agentic_fork_sampled():

@@ -183,7 +183,7 @@ def test_quantised_qwen_layer_full(fmt):
     wl = replace(workloads.qwen_independent(), kv_format=fmt)
     ref = OracleReplay(wl).run()
     run = GpuRun(wl, ref=ref).run()
-    check(run.decode_outputs[0][0].double().cpu().numpy(), ref.attention(0, 0), f"{fmt} config 2")
+    check(run.decode_outputs[0][0].double().cpu().numpy(), ref.attention(0, 0), f"{fmt} 37 x 2304 layer")
 
 
 def test_quantised_pool_rejects_other_kernels_and_shapes():
