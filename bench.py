@@ -884,6 +884,7 @@ def summarize_counters(a):
     w_scale = cal / (copy_w * 1024)  # and writes cal bytes
     line = bench_line(os.path.join(d, f"pmc_{name}_FETCH_SIZE.log"))
     alg = line["roofline"].get("algorithmic_bytes_per_launch")
+    flops = line["roofline"].get("algorithmic_flops_per_launch")
     per_kernel = {k: (fetch[k][0] * 1024 * f_scale, write.get(k, (0.0, 0))[0] * 1024 * w_scale) for k in kernels}
     main_k = kernels[0]
     rec = {
@@ -923,11 +924,16 @@ def summarize_counters(a):
     for k in kernels:
         md.append(f"| `{k}` | {fetch[k][1]} | {fetch[k][0]:.1f} | {write.get(k, (0.0, 0))[0]:.1f} | "
                   f"{per_kernel[k][0]:,.0f} | {per_kernel[k][1]:,.0f} |")
-    md += ["", f"Algorithmic bytes per launch in the FETCH_SIZE run (K/V as stored, q, out, table entries): "
-           f"{alg:,} B.  `{main_k}` moves {rec['traffic_bytes_per_launch']:,} B per launch "
-           f"({rec['traffic_bytes_per_launch'] / alg:.4f} x algorithmic); the whole call "
-           f"({', '.join(kernels)}) {rec['traffic_bytes_per_call']:,} B "
-           f"({rec['traffic_bytes_per_call'] / alg:.4f} x)."]
+    if alg:
+        md += ["", f"Algorithmic bytes per launch in the FETCH_SIZE run (K/V as stored, q, out, table entries): "
+               f"{alg:,} B.  `{main_k}` moves {rec['traffic_bytes_per_launch']:,} B per launch "
+               f"({rec['traffic_bytes_per_launch'] / alg:.4f} x algorithmic); the whole call "
+               f"({', '.join(kernels)}) {rec['traffic_bytes_per_call']:,} B "
+               f"({rec['traffic_bytes_per_call'] / alg:.4f} x)."]
+    else:  # a matrix-bound launch: its roofline counts flops
+        md += ["", f"`{main_k}` moves {rec['traffic_bytes_per_launch']:,} B per launch for {flops:,} flops "
+               f"({flops / rec['traffic_bytes_per_launch']:.0f} flop/B); the whole call "
+               f"({', '.join(kernels)}) {rec['traffic_bytes_per_call']:,} B."]
     out_md = os.path.join(ROOT, "profiles", f"{a.summary_file}.md")
     with open(out_md, "w") as f:
         f.write("\n".join(md) + "\n")
