@@ -1,0 +1,72 @@
+"""CPU checks of bench.py's measurement helpers: the rocprofv3 summaries that
+profiles/ holds and the traffic lookup that bench lines report."""
+
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("name, short", [
+    ("void pagedkv::(anonymous namespace)::attn_mfma_kernel<128, 6, 1, 0>(pagedkv::(anonymous namespace)::sk_args,"
+     " int const*, int const*)", "attn_mfma_kernel"),
+    ("void pagedkv::(anonymous namespace)::merge_sk_kernel<128>(pagedkv::(anonymous namespace)::sk_args)",
+     "merge_sk_kernel"),
+    ("__amd_rocclr_copyBuffer", "__amd_rocclr_copyBuffer"),
+    ("at::cuda::(anonymous namespace)::spin_kernel(long)", "spin_kernel"),
+])
+def test_short_kernel_name(name, short):
+    assert bench.short_kernel_name(name) == short
+
+
+def test_counter_mean_per_dispatch(tmp_path):
+    d = tmp_path / "run"
+    d.mkdir()
+    rows = [
+        ("void pagedkv::(anonymous namespace)::attn_mfma_kernel<128, 6, 1, 0>(x)", "FETCH_SIZE", 100.0),
+        ("void pagedkv::(anonymous namespace)::attn_mfma_kernel<128, 6, 1, 0>(x)", "FETCH_SIZE", 300.0),
+        ("void pagedkv::(anonymous namespace)::merge_sk_kernel<128>(x)", "FETCH_SIZE", 7.0),
+        ("void pagedkv::(anonymous namespace)::merge_sk_kernel<128>(x)", "WRITE_SIZE", 9.0),
+    ]
+    with open(d / "run_counter_collection.csv", "w") as f:
+        f.write('"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"\n')
+        for i, (k, c, v) in enumerate(rows):
+            f.write(f'{i},"{k}","{c}",{v}\n')
+    got = bench.counter_kib_per_dispatch(str(d), "FETCH_SIZE")
+    assert got == {"attn_mfma_kernel": (200.0, 2), "merge_sk_kernel": (7.0, 1)}
+
+
+def test_traffic_lookup_follows_the_kernel_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    csrc = tmp_path / "pagedattention_decode_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "kernels.hip").write_text("// kernels, version 1\n")
+    rec = {"kernel_source_sha256": bench.kernel_source_sha256(("kernels.hip",)),
+           "traffic_bytes_per_launch": 123, "traffic_bytes_per_call": 456}
+    (tmp_path / "profiles" / "hbm_traffic_w.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("w") == 123
+    assert bench.measured_traffic("w", key="traffic_bytes_per_call") == 456
+    assert bench.measured_traffic("other") is None
+    (csrc / "kernels.hip").write_text("// kernels, version 2\n")  # the counters no longer describe it
+    assert bench.measured_traffic("w") is None
+
+
+def test_committed_traffic_summaries_are_consistent():
+    """Every committed summary: traffic per call >= per launch, both near or below
+    the algorithmic bytes' order, and a source hash of the right form."""
+    prof = os.path.join(ROOT, "profiles")
+    names = [n for n in os.listdir(prof) if n.startswith("hbm_traffic_") and n.endswith(".json")]
+    assert names
+    for n in names:
+        with open(os.path.join(prof, n)) as f:
+            rec = json.load(f)
+        assert len(rec["kernel_source_sha256"]) == 64
+        assert rec["traffic_bytes_per_call"] >= rec["traffic_bytes_per_launch"] > 0, n
+        assert 1.9 < rec["fetch_scale"] < 2.1 and 0.9 < rec["write_scale"] < 1.1, n
