@@ -57,18 +57,6 @@ __device__ __forceinline__ int v_offset(int r, int e, int B, int Q) {
   return ((((e >> 5) * (B / Q) + r / Q) * 16 + (e & 15)) * 2 + ((e & 31) >> 4)) * Q + r % Q;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 // ---------------------------------------------------------------------------
 // reshape_and_cache: one thread per 16-byte chunk of a new K row; the same
 // thread scatters the matching V elements.
@@ -1138,6 +1126,8 @@ struct cascade_args {
 // 2^(m - M) l.  A poisoned partial, a member that failed its check, or a
 // group larger than the multi-query grid gives a NaN row; no keys at all give
 // a zero row.
+constexpr int kCascadeBatch = 8;  // partial rows per batch of loads
+
 template <int D>
 __global__ void __launch_bounds__(256) cascade_merge_kernel(cascade_args c) {
   const sk_args& a = c.sfx;
@@ -1188,6 +1178,46 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cascade_args c) {
     l = a.part_l[row];
   };
   const int n_ent = n_pre + n_suf;
+  if (n_ent <= 64) {
+    // the usual case: every lane resolves one entry once, and the rows are
+    // loaded kCascadeBatch at a time with no branch between the loads, so a
+    // batch waits out one memory latency (entries of weight 0 -- empty runs,
+    // NaN -- are loaded, the row lies inside the workspace, but not added)
+    float m = -INFINITY, l = 0.f;
+    int64_t row = 0;
+    if (lane < n_ent) entry(lane, m, l, row);
+    const bool nan_seen = nan_row || __builtin_amdgcn_ballot_w64(m != m) != 0;
+    const float M = wave_max(m != m ? -INFINITY : m);
+    const float w = (m == -INFINITY || m != m) ? 0.f : exp2f(m - M);
+    const float L = wave_sum(w == 0.f ? 0.f : w * l);
+    const int row_lo = static_cast<int>(row & 0xffffffff), row_hi = static_cast<int>(row >> 32);
+    float acc[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] = 0.f;
+    for (int k0 = 0; k0 < n_ent; k0 += kCascadeBatch) {
+      float v[kCascadeBatch][E];
+#pragma unroll
+      for (int k = 0; k < kCascadeBatch; ++k) {
+        const int kk = min(k0 + k, n_ent - 1);  // past the end: a repeat, weight 0 below
+        const int64_t rk = (static_cast<int64_t>(__shfl(row_hi, kk)) << 32) | static_cast<uint32_t>(__shfl(row_lo, kk));
+        const float* ok = (kk < n_pre ? c.pre_o : a.part_o) + rk * D;
+#pragma unroll
+        for (int i = 0; i < E; ++i) v[k][i] = lane + 64 * i < D ? ok[lane + 64 * i] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kCascadeBatch; ++k) {
+        const float wk = k0 + k < n_ent ? __shfl(w, k0 + k) : 0.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] = wk == 0.f ? acc[i] : __builtin_fmaf(wk, v[k][i], acc[i]);
+      }
+    }
+    const bool empty = M == -INFINITY && !nan_seen;  // no key at all
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (lane + 64 * i < D)
+        orow[lane + 64 * i] = nan_seen ? static_cast<uint16_t>(0x7fc0) : (empty ? 0 : f32_to_bf16(acc[i] / L));
+    return;
+  }
   float M = -INFINITY;
   bool nan_seen = nan_row;
   for (int i0 = 0; i0 < n_ent; i0 += 64) {

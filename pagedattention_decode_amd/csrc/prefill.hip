@@ -667,6 +667,7 @@ attn_prefill_lds_kernel(pf_args a) {
 // weight of partition p (64 at a time), then every lane accumulates its
 // dimensions over the partitions.
 constexpr int kPfMergeWaves = 4;
+constexpr int kPfMergeBatch = 8;  // partial rows per batch of loads
 
 template <int D>
 __global__ void __launch_bounds__(kPfMergeWaves * 64) merge_prefill_kernel(pf_args a) {
@@ -675,13 +676,16 @@ __global__ void __launch_bounds__(kPfMergeWaves * 64) merge_prefill_kernel(pf_ar
   if (item >= static_cast<int64_t>(a.total_q) * a.n_q_heads) return;
   const int r = static_cast<int>(item / a.n_q_heads);
   const int head = static_cast<int>(item % a.n_q_heads);
-  // sequence of row r: the last s with q_indptr[s] <= r
-  int lo = 0, hi = a.n_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.q_indptr[mid] <= r) lo = mid; else hi = mid - 1;
+  // sequence of row r: the last s with q_indptr[s] <= r; the lanes test 64
+  // sequences at a time and count the passes (q_indptr is non-decreasing)
+  int passed = 0;
+  for (int base = 0; base < a.n_seqs; base += 64) {
+    const int s = base + lane;
+    const uint64_t ok = __builtin_amdgcn_ballot_w64(s < a.n_seqs && a.q_indptr[s] <= r);
+    passed += __builtin_popcountll(ok);
+    if (ok != ~0ull) break;
   }
-  const pf_seq sq = pf_locate(a, lo);
+  const pf_seq sq = pf_locate(a, max(passed - 1, 0));
   if (sq.c <= 0 || r < sq.q0 || r >= sq.q0 + sq.c || sq.bad) return;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int f = (r - sq.q0) * G + head % G;
@@ -690,6 +694,41 @@ __global__ void __launch_bounds__(kPfMergeWaves * 64) merge_prefill_kernel(pf_ar
   const int n_parts = (kend + P - 1) / P;
   if (n_parts <= 1) return;
   const int64_t base = item * a.max_parts;
+  constexpr int E = (D + 63) / 64;  // dims per lane
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + item * D;
+  if (n_parts <= 64) {
+    // the usual case: lane p holds partition p's (m, l), read once, and the
+    // rows are loaded kPfMergeBatch at a time with no branch between the
+    // loads (rows of weight 0 are loaded but not added)
+    const float m = lane < n_parts ? a.part_m[base + lane] : -INFINITY;
+    const float l = lane < n_parts ? a.part_l[base + lane] : 0.f;
+    const bool nan_seen = __builtin_amdgcn_ballot_w64(m != m) != 0;
+    const float M = wave_max(m != m ? -INFINITY : m);
+    const float w = (m == -INFINITY || m != m) ? 0.f : exp2f(m - M);
+    const float L = wave_sum(w == 0.f ? 0.f : w * l);
+    float acc[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] = 0.f;
+    for (int k0 = 0; k0 < n_parts; k0 += kPfMergeBatch) {
+      float v[kPfMergeBatch][E];
+#pragma unroll
+      for (int k = 0; k < kPfMergeBatch; ++k) {
+        const float* po = a.part_o + (base + min(k0 + k, n_parts - 1)) * D;
+#pragma unroll
+        for (int i = 0; i < E; ++i) v[k][i] = lane + 64 * i < D ? po[lane + 64 * i] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kPfMergeBatch; ++k) {
+        const float wk = k0 + k < n_parts ? __shfl(w, k0 + k) : 0.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] = wk == 0.f ? acc[i] : __builtin_fmaf(wk, v[k][i], acc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (lane + 64 * i < D) orow[lane + 64 * i] = f32_to_bf16(nan_seen ? __builtin_nanf("") : acc[i] / L);
+    return;
+  }
   float M = -INFINITY;
   bool nan_seen = false;
   for (int p0 = 0; p0 < n_parts; p0 += 64) {
@@ -699,7 +738,6 @@ __global__ void __launch_bounds__(kPfMergeWaves * 64) merge_prefill_kernel(pf_ar
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  constexpr int E = (D + 63) / 64;  // dims per lane
   float acc[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) acc[i] = 0.f;
@@ -721,7 +759,6 @@ __global__ void __launch_bounds__(kPfMergeWaves * 64) merge_prefill_kernel(pf_ar
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-  uint16_t* orow = static_cast<uint16_t*>(a.out) + item * D;
 #pragma unroll
   for (int i = 0; i < E; ++i)
     if (lane + 64 * i < D) orow[lane + 64 * i] = f32_to_bf16(nan_seen ? __builtin_nanf("") : acc[i] / L);
