@@ -106,7 +106,8 @@ DECODE_LAYERS = {"qwen3_8b_37x2304": 4, "shared_prefix_16x8448": 4, "gqa70b_12x1
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (0 = 100 for the decode workloads, 20 for the fork workload and the other ops)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_8b_37x2304", choices=list(DECODE_LAYERS),
                     help="the decode workload of --op decode")
@@ -171,6 +172,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU form)", file=sys.stderr)
         sys.exit(2)
+    if args.steps <= 0:
+        # a decode step of the 37 x 2304 workload is ~0.35 ms: 100 of them keep the timed region
+        # long against the host's occasional stalls of a few milliseconds
+        args.steps = 100 if args.op == "decode" and args.workload != "agentic_fork_64x33281" else 20
 
     if args.op == "swap":
         swap_bench(args)
@@ -209,7 +214,11 @@ def main():
     step_appends = any(op[0] == "append" for op in step_ops)
     S = len(decode_seqs)
 
-    pool = PagedKVPool(L, base.num_blocks, Bs, Hkv, d, args.kv, free_order=draws.free_order(seed, base.num_blocks))
+    total_steps = args.warmup + args.steps
+    # room for the tokens the steps append (and one copy-on-write block per sequence) on top of
+    # the workload's pool; the per-step work does not depend on the pool's size
+    num_blocks = base.num_blocks + (S * (-(-total_steps // Bs) + 2) if step_appends else 0)
+    pool = PagedKVPool(L, num_blocks, Bs, Hkv, d, args.kv, free_order=draws.free_order(seed, num_blocks))
     # bytes of one token's K and V in one layer, as stored (codes + scales when quantised)
     kv_tok = 2 * Hkv * (d * 2 if args.kv == "bf16" else d * (8 if args.kv == "q8_0" else 4) // 8 + d // 32 * 2)
     gen = torch.Generator(device=dev)
@@ -237,12 +246,23 @@ def main():
     torch.cuda.synchronize()
     t_fill = time.time() - t_fill
 
-    total_steps = args.warmup + args.steps
     lens0 = np.array([pool.info(s)[0] for s in decode_seqs])
     max_blocks = int(math.ceil((lens0.max() + (total_steps if step_appends else 0)) / Bs)) + 1
-    q_in = [[randn_bf16(S, Hq, d) for _ in range(L)] for _ in range(total_steps)]
-    kv_in = [[(randn_bf16(S, Hkv, d), randn_bf16(S, Hkv, d)) for _ in range(L)] for _ in range(total_steps)] \
-        if step_appends else None
+    # every step's inputs, resident in HBM before the timed region: per layer the queries and,
+    # when the workload appends, the new K and V rows; one flat buffer per step
+    n_q, n_kv = S * Hq * d, (S * Hkv * d if step_appends else 0)
+    per_layer = n_q + 2 * n_kv
+    inputs = randn_bf16(total_steps, L * per_layer)
+
+    def layer_inputs(buf, layer):
+        at = layer * per_layer
+        q = buf[at:at + n_q].view(S, Hq, d)
+        if not n_kv:
+            return q, None, None
+        k = buf[at + n_q:at + n_q + n_kv].view(S, Hkv, d)
+        v = buf[at + n_q + n_kv:at + per_layer].view(S, Hkv, d)
+        return q, k, v
+
     out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=dev)
     if args.cascade:
         # max_group sizes the prefix grid: the largest group of the first step's plan (the fork
@@ -266,7 +286,9 @@ def main():
     d_tables = d_up[off_t:off_l].view(torch.int32).view(S, max_blocks)
     d_lens = d_up[off_l:off_p].view(torch.int32)
     d_plan = d_up[off_p:].view(torch.int32)
-    ring = 4
+    # pinned upload buffers in flight: the host may run this many steps ahead of the device, so
+    # that a stall of a few milliseconds on the host leaves the device's queue non-empty
+    ring = 32
     h_up = [torch.empty((up_bytes,), dtype=torch.uint8).pin_memory() for _ in range(ring)]
     h_np = [h.numpy() for h in h_up]
     h_slots = [h[:off_t].view(np.int64) for h in h_np]
@@ -289,6 +311,13 @@ def main():
                                 max_group, o, ws)
         else:
             pool.decode(layer, q, out, d_tables, d_lens, Hq, o, ws)
+
+    def layers(buf):
+        for layer in range(L):
+            q, k, v = layer_inputs(buf, layer)
+            if step_appends:
+                pool.cache(layer, k, v, d_slots)
+            attention(layer, q, opts)
 
     def step(i, timed):
         slot = i % ring
@@ -320,14 +349,10 @@ def main():
         if len(pairs):
             pool.copy(torch.from_numpy(pairs).to(dev, non_blocking=False))
             n_copies[0] += len(pairs)
-        for layer in range(L):
-            if step_appends:
-                k_new, v_new = kv_in[i][layer]
-                pool.cache(layer, k_new, v_new, d_slots)
-            attention(layer, q_in[i][layer], opts)
-            if timed:
-                logical_bytes[0] += int(lens.astype(np.int64).sum()) * kv_tok
-                read_bytes[0] += read_tokens * kv_tok
+        layers(inputs[i])
+        if timed:
+            logical_bytes[0] += L * int(lens.astype(np.int64).sum()) * kv_tok
+            read_bytes[0] += L * read_tokens * kv_tok
         return lens
 
     for i in range(args.warmup):
@@ -347,7 +372,7 @@ def main():
     # the timed steps' attention calls once more, each timed on its own (the
     # tables and lengths of the last step, layers in turn)
     kern_ms, attn_ms = time_calls(torch, B, stream, args.steps * L,
-                                  lambda j, o: attention(j % L, q_in[args.warmup + j // L][j % L], o),
+                                  lambda j, o: attention(j % L, layer_inputs(inputs[args.warmup + j // L], j % L)[0], o),
                                   partition_tokens=partition, kernel=kernel)
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
@@ -392,6 +417,7 @@ def main():
             "kernel": args.kernel,
             "kv_storage": args.kv,
             "kv_bytes_per_token_per_layer": kv_tok,
+            "pool_blocks": num_blocks,
             "step": (f"append + {L} x (reshape_and_cache + {attn_name})" if step_appends
                      else f"{L} x {attn_name}"),
         },
