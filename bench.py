@@ -452,8 +452,10 @@ def main():
     }
     traffic = result["roofline"]["traffic"]
     if traffic:
-        # HBM bytes the counters saw per call, against the algorithmic bytes
+        # HBM bytes the counters saw per call, against the algorithmic bytes, and the HBM rate
+        # they make over the measured duration
         result["roofline"]["traffic_over_algorithmic"] = round(traffic / ideal_per_launch, 4)
+        result["roofline"]["traffic_gbs"] = round(traffic / roof_s / 1e9, 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(result), flush=True)
