@@ -394,6 +394,9 @@ def main():
         uniq.update(tables[r, :int(math.ceil(lens[r] / Bs))].tolist())
     unique_kv_bytes = len(uniq) * Bs * kv_tok
 
+    traffic_key = (base.name + ("" if args.kv == "bf16" else f"_{args.kv}") + ("_cascade" if args.cascade else ""),
+                   ("kernels.hip", "prefill.hip") if args.cascade else ("kernels.hip",),
+                   "traffic_bytes_per_call" if args.cascade else "traffic_bytes_per_launch")
     result = {
         "metric": "paged-decode KV GB/s (% of HBM peak) + attention tokens/s per layer",
         "value": round(value, 2),
@@ -439,10 +442,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(base.name + ("" if args.kv == "bf16" else f"_{args.kv}")
-                                        + ("_cascade" if args.cascade else ""),
-                                        ("kernels.hip", "prefill.hip") if args.cascade else ("kernels.hip",),
-                                        "traffic_bytes_per_call" if args.cascade else "traffic_bytes_per_launch"),
+            "traffic": measured_traffic(*traffic_key),
             "kernel": ("paged_attention_decode_cascade (whole call: preparation, prefix multi-query kernel, "
                        "split-K kernel, merge)" if args.cascade else "attn_mfma_kernel (split-K partition kernel)"),
             "duration_us": round(roof_s * 1e6, 2),
@@ -450,12 +450,12 @@ def main():
         },
         "cpu_baseline": None,
     }
-    traffic = result["roofline"]["traffic"]
-    if traffic:
-        # HBM bytes the counters saw per call, against the algorithmic bytes, and the HBM rate
-        # they make over the measured duration
-        result["roofline"]["traffic_over_algorithmic"] = round(traffic / ideal_per_launch, 4)
-        result["roofline"]["traffic_gbs"] = round(traffic / roof_s / 1e9, 1)
+    ratio = traffic_ratio(*traffic_key)
+    if ratio:
+        # HBM bytes the counters saw against the algorithmic bytes of the same run, and the HBM
+        # rate that ratio gives over this run's bytes and measured duration
+        result["roofline"]["traffic_over_algorithmic"] = round(ratio, 4)
+        result["roofline"]["traffic_gbs"] = round(ratio * ideal_per_launch / roof_s / 1e9, 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(result), flush=True)
@@ -833,6 +833,13 @@ def measured_traffic(workload, sources=("kernels.hip",), key="traffic_bytes_per_
     traffic_bytes_per_launch) or per whole call (traffic_bytes_per_call) from
     the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload;
     None when there is none or the kernel sources changed since it was taken."""
+    rec = traffic_record(workload, sources)
+    return rec.get(key) if rec else None
+
+
+def traffic_record(workload, sources=("kernels.hip",)):
+    """The committed counter summary of this workload (profiles/hbm_traffic_<workload>.json),
+    or None when there is none or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -840,7 +847,16 @@ def measured_traffic(workload, sources=("kernels.hip",), key="traffic_bytes_per_
         rec = json.load(f)
     if kernel_source_sha256(sources) != rec.get("kernel_source_sha256"):
         return None
-    return rec.get(key)
+    return rec
+
+
+def traffic_ratio(workload, sources=("kernels.hip",), key="traffic_bytes_per_launch"):
+    """HBM bytes over algorithmic bytes, both from the counter run itself (its contexts may be
+    shorter than those of a longer bench run, so the ratio is the size-independent figure)."""
+    rec = traffic_record(workload, sources)
+    if not rec or not rec.get(key) or not rec.get("algorithmic_bytes_per_launch"):
+        return None
+    return rec[key] / rec["algorithmic_bytes_per_launch"]
 
 
 # ---- summaries of rocprofv3 output for profiles/ ---------------------------

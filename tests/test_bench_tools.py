@@ -49,13 +49,17 @@ def test_traffic_lookup_follows_the_kernel_sources(tmp_path, monkeypatch):
     csrc.mkdir(parents=True)
     (csrc / "kernels.hip").write_text("// kernels, version 1\n")
     rec = {"kernel_source_sha256": bench.kernel_source_sha256(("kernels.hip",)),
-           "traffic_bytes_per_launch": 123, "traffic_bytes_per_call": 456}
+           "traffic_bytes_per_launch": 123, "traffic_bytes_per_call": 456, "algorithmic_bytes_per_launch": 100}
     (tmp_path / "profiles" / "hbm_traffic_w.json").write_text(json.dumps(rec))
     assert bench.measured_traffic("w") == 123
     assert bench.measured_traffic("w", key="traffic_bytes_per_call") == 456
     assert bench.measured_traffic("other") is None
+    # the ratio comes from the counter run's own algorithmic bytes
+    assert bench.traffic_ratio("w") == 1.23
+    assert bench.traffic_ratio("w", key="traffic_bytes_per_call") == 4.56
     (csrc / "kernels.hip").write_text("// kernels, version 2\n")  # the counters no longer describe it
     assert bench.measured_traffic("w") is None
+    assert bench.traffic_ratio("w") is None
 
 
 def test_committed_traffic_summaries_are_consistent():
