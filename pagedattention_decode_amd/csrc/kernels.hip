@@ -77,17 +77,19 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(
     const int rem = static_cast<int>(item % chunks_per_token);
     const int g = rem / chunks_per_head;
     const int c = rem % chunks_per_head;
+    // the new rows are read together with the slot (they are in bounds whatever the slot is),
+    // so the two loads wait out one memory latency, not two
+    const int64_t src = (tok * n_kv_heads + g) * head_dim + static_cast<int64_t>(c) * X;
+    const uint4 kv = *reinterpret_cast<const uint4*>(k_new + src);
+    const uint4 vv = *reinterpret_cast<const uint4*>(v_new + src);
     const int64_t slot = slots[tok];
     if (slot < 0 || slot >= n_slots) continue;
     const int64_t blk = slot / block_size;
     const int r = static_cast<int>(slot % block_size);
     const int64_t tile = (blk * n_kv_heads + g) * static_cast<int64_t>(block_size) * head_dim;
-    const int64_t src = (tok * n_kv_heads + g) * head_dim + static_cast<int64_t>(c) * X;
     // K: one 16-byte chunk, contiguous in the tile
-    const uint4 kv = *reinterpret_cast<const uint4*>(k_new + src);
     *reinterpret_cast<uint4*>(k_layer + tile + k_offset(r, c * X, block_size, X)) = kv;
     // V: X elements, each to its own place
-    const uint4 vv = *reinterpret_cast<const uint4*>(v_new + src);
     const T* ve = reinterpret_cast<const T*>(&vv);
 #pragma unroll
     for (int x = 0; x < X; ++x) v_layer[tile + v_offset(r, c * X + x, block_size, Q)] = ve[x];
