@@ -3,6 +3,7 @@ profiles/ holds and the traffic lookup that bench lines report."""
 
 import json
 import os
+import subprocess
 import sys
 
 import pytest
@@ -74,3 +75,9 @@ def test_committed_traffic_summaries_are_consistent():
         assert len(rec["kernel_source_sha256"]) == 64
         assert rec["traffic_bytes_per_call"] >= rec["traffic_bytes_per_launch"] > 0, n
         assert 1.9 < rec["fetch_scale"] < 2.1 and 0.9 < rec["write_scale"] < 1.1, n
+
+
+def test_more_than_one_gpu_is_refused():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], cwd=ROOT,
+                         capture_output=True, text=True, timeout=120)
+    assert out.returncode == 2 and "one GPU" in out.stderr
