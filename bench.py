@@ -11,14 +11,16 @@ Inputs (queries, new K/V rows) for every timed step are resident in HBM
 before the timed region; the pool is filled once, before warm-up.
 
 Workloads (--workload; synthetic, seeded; see synth/workloads.py):
+  gqa70b_12x131072       70B-GQA-shaped layer: 12 x 131072 tokens (6.4 GB of
+                         KV), Hq=64, Hkv=8, d=128, B=16, bf16, split-K over
+                         512-token partitions.   (default: the long-context
+                         workload, the largest that fits one GPU)
   qwen3_8b_37x2304       Qwen3-8B-shaped layer: 37 sequences x 2304 tokens,
                          Hq=32, Hkv=8, d=128, B=16, bf16; 4 layer buffers
                          rotated so the 256 MB last-level cache cannot hold
-                         the working set (1.4 GB per step).   (default)
+                         the working set (1.4 GB per step).
   shared_prefix_16x8448  16 x 8448 tokens sharing a 6144-token prefix, same
                          shapes, 4 layers.
-  gqa70b_12x131072       70B-GQA-shaped layer: 12 x 131072 tokens, Hq=64,
-                         split-K 512.
   agentic_fork_64x33281  64 sequences (4 roots x 16 forks) x ~33K tokens,
                          36 layers.
 --cascade (the shared-prefix and fork workloads) decodes through
@@ -51,6 +53,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, public specification
+
+# sources whose hash decides whether a committed counter summary still describes
+# the kernels: the kernel file and the headers its device code includes
+DECODE_SOURCES = ("kernels.hip", "device_common.h", "pool_internal.h")
+CASCADE_SOURCES = DECODE_SOURCES + ("prefill.hip",)
+PREFILL_SOURCES = ("prefill.hip", "device_common.h", "pool_internal.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, public specification
 
 
@@ -109,7 +117,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=0,
                     help="timed steps (0 = 100 for the decode workloads, 20 for the fork workload and the other ops)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_8b_37x2304", choices=list(DECODE_LAYERS),
+    ap.add_argument("--workload", default="gqa70b_12x131072", choices=list(DECODE_LAYERS),
                     help="the decode workload of --op decode")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "q8_0", "q4_0"],
                     help="storage of the KV pool for --op decode: bf16, or q8_0 / q4_0 codes with one 2-byte "
@@ -138,7 +146,8 @@ def parse():
     g.add_argument("--summary-workload", default="", help="workload name of hbm_traffic_<workload>.json")
     g.add_argument("--summary-kernels", default="attn_mfma_kernel,merge_sk_kernel",
                    help="kernels of one call, the one streaming the cache first")
-    g.add_argument("--summary-sources", default="kernels.hip", help="csrc files whose hash the summary records")
+    g.add_argument("--summary-sources", default=",".join(DECODE_SOURCES),
+                   help="csrc files whose hash the summary records")
     g.add_argument("--summary-file", default="", help="markdown file name in profiles/ (without .md)")
     g.add_argument("--summary-title", default="")
     g.add_argument("--summary-command", default="", help="bench.py arguments of the profiled run")
@@ -173,8 +182,8 @@ def main():
               "(the path has no multi-GPU form)", file=sys.stderr)
         sys.exit(2)
     if args.steps <= 0:
-        # a decode step of the 37 x 2304 workload is ~0.35 ms: 100 of them keep the timed region
-        # long against the host's occasional stalls of a few milliseconds
+        # a decode step is ~0.35 ms (37 x 2304, 4 layers) to ~1.1 ms (12 x 131072): 100 of them
+        # keep the timed region long against the host's occasional stalls of a few milliseconds
         args.steps = 100 if args.op == "decode" and args.workload != "agentic_fork_64x33281" else 20
 
     if args.op == "swap":
@@ -300,6 +309,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     logical_bytes = [0]
+    first_tables = []  # the first timed step's tables and lengths (for its unique bytes)
     n_copies = [0]
     n_groups = [0]
     read_bytes = [0]  # KV bytes the path reads (shared prefixes once per group with --cascade)
@@ -353,6 +363,8 @@ def main():
         if timed:
             logical_bytes[0] += L * int(lens.astype(np.int64).sum()) * kv_tok
             read_bytes[0] += L * read_tokens * kv_tok
+            if not first_tables:
+                first_tables.append((tables.copy(), lens.copy()))
         return lens
 
     for i in range(args.warmup):
@@ -377,9 +389,17 @@ def main():
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
     n_launch = args.steps * L
-    kv_bytes_per_launch = read_bytes[0] / n_launch
     blocks_per_launch = float(np.mean([np.ceil(l / Bs).sum() for l in lens_hist]))
-    ideal_per_launch = kv_bytes_per_launch + 2 * S * Hq * d * 2 + 4 * blocks_per_launch
+    qo_tab = 2 * S * Hq * d * 2 + 4 * blocks_per_launch  # queries, outputs, table entries
+    # KV bytes a launch must read at least: every physical block once, as far as the longest
+    # context reading it reaches (sharing sequences read a shared block once between them);
+    # the contexts grow by one token per step, so the mean of the first and last timed steps
+    last_tables = B.kv_get_block_tables(pool.handle, seq_arr, max_blocks)
+    unique_kv_bytes = 0.5 * (unique_tokens(*first_tables[0], Bs) + unique_tokens(*last_tables, Bs)) * kv_tok
+    logical_per_launch = logical_bytes[0] / n_launch + qo_tab
+    # the cascade reads each group's shared prefix once (read_bytes), the plain decode is held to
+    # the unique bytes; without sharing both equal the logical bytes
+    ideal_per_launch = (read_bytes[0] / n_launch if args.cascade else unique_kv_bytes) + qo_tab
     # the roofline is that of the kernel streaming the cache (the split-K
     # partition kernel); the cascade's bytes are only defined for the whole call
     roof_s = attn_avg_s if args.cascade else kern_avg_s
@@ -387,15 +407,8 @@ def main():
     value = logical_bytes[0] / wall / 1e9
     tok_per_s_layer = S * L * args.steps / wall
 
-    # unique bytes (shared blocks counted once) per launch, for the sharing workloads
-    tables, lens = B.kv_get_block_tables(pool.handle, seq_arr, max_blocks)
-    uniq = set()
-    for r in range(S):
-        uniq.update(tables[r, :int(math.ceil(lens[r] / Bs))].tolist())
-    unique_kv_bytes = len(uniq) * Bs * kv_tok
-
     traffic_key = (base.name + ("" if args.kv == "bf16" else f"_{args.kv}") + ("_cascade" if args.cascade else ""),
-                   ("kernels.hip", "prefill.hip") if args.cascade else ("kernels.hip",),
+                   CASCADE_SOURCES if args.cascade else DECODE_SOURCES,
                    "traffic_bytes_per_call" if args.cascade else "traffic_bytes_per_launch")
     result = {
         "metric": "paged-decode KV GB/s (% of HBM peak) + attention tokens/s per layer",
@@ -433,7 +446,10 @@ def main():
         "attn_kernel_us_p10_p50_p90": pcts(kern_ms),
         "call_achieved_gbs": round(ideal_per_launch / attn_avg_s / 1e9, 1),
         "call_frac": round(ideal_per_launch / attn_avg_s / 1e9 / HBM_PEAK_GBS, 4),
-        "unique_kv_bytes_per_launch": unique_kv_bytes,
+        "unique_kv_bytes_per_launch": int(unique_kv_bytes),
+        # logical bytes (every sequence's context through its own table) over the kernel's time:
+        # above the HBM peak where sequences share blocks that the caches serve
+        "logical_achieved_gbs": round(logical_per_launch / roof_s / 1e9, 1),
         "cow_copies": n_copies[0],
         "fill_seconds": round(t_fill, 2),
         "roofline": {
@@ -447,6 +463,10 @@ def main():
                        "split-K kernel, merge)" if args.cascade else "attn_mfma_kernel (split-K partition kernel)"),
             "duration_us": round(roof_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(ideal_per_launch),
+            "algorithmic_bytes": ("each group's shared prefix once, every member's own blocks, q, out, table "
+                                  "entries" if args.cascade else
+                                  "every physical block read once (as far as the longest context reading it "
+                                  "reaches), q, out, table entries"),
         },
         "cpu_baseline": None,
     }
@@ -459,6 +479,23 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(result), flush=True)
+
+
+def unique_tokens(tables, lens, block_size):
+    """Tokens of the distinct physical blocks the batch reads: each block counted
+    once, with the most slots any of its readers sees."""
+    import numpy as np
+    lens = np.asarray(lens, np.int64)
+    nb = -(-lens // block_size)
+    j = np.arange(tables.shape[1])[None, :]
+    live = j < nb[:, None]
+    valid = np.minimum(block_size, lens[:, None] - j * block_size)
+    blocks, valid = tables[live].astype(np.int64), valid[live]
+    if blocks.size == 0:
+        return 0
+    best = np.zeros(int(blocks.max()) + 1, np.int64)
+    np.maximum.at(best, blocks, valid)
+    return int(best.sum())
 
 
 def multi_query_bench(args):
@@ -588,7 +625,7 @@ def multi_query_bench(args):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(flops / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(base.name, ("prefill.hip",)),
+            "traffic": measured_traffic(base.name, PREFILL_SOURCES),
             "kernel": "attn_prefill_lds_kernel (multi-query kernel)",
             "duration_us": round(kern_s * 1e6, 2),
             "algorithmic_flops_per_launch": flops,
@@ -598,7 +635,7 @@ def multi_query_bench(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ideal_bytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(base.name, ("prefill.hip",)),
+            "traffic": measured_traffic(base.name, PREFILL_SOURCES),
             "kernel": "attn_prefill_lds_kernel (multi-query kernel)",
             "duration_us": round(kern_s * 1e6, 2),
             "algorithmic_bytes_per_launch": ideal_bytes,
@@ -828,7 +865,7 @@ def kernel_source_sha256(sources):
     return h.hexdigest()
 
 
-def measured_traffic(workload, sources=("kernels.hip",), key="traffic_bytes_per_launch"):
+def measured_traffic(workload, sources=DECODE_SOURCES, key="traffic_bytes_per_launch"):
     """HBM bytes per launch of the kernel streaming the cache (key
     traffic_bytes_per_launch) or per whole call (traffic_bytes_per_call) from
     the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload;
@@ -837,7 +874,7 @@ def measured_traffic(workload, sources=("kernels.hip",), key="traffic_bytes_per_
     return rec.get(key) if rec else None
 
 
-def traffic_record(workload, sources=("kernels.hip",)):
+def traffic_record(workload, sources=DECODE_SOURCES):
     """The committed counter summary of this workload (profiles/hbm_traffic_<workload>.json),
     or None when there is none or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
@@ -850,7 +887,7 @@ def traffic_record(workload, sources=("kernels.hip",)):
     return rec
 
 
-def traffic_ratio(workload, sources=("kernels.hip",), key="traffic_bytes_per_launch"):
+def traffic_ratio(workload, sources=DECODE_SOURCES, key="traffic_bytes_per_launch"):
     """HBM bytes over algorithmic bytes, both from the counter run itself (its contexts may be
     shorter than those of a longer bench run, so the ratio is the size-independent figure)."""
     rec = traffic_record(workload, sources)
@@ -1014,61 +1051,92 @@ def summarize_trace(a):
     print(out_md)
 
 
-def cpu_baseline(args):
-    """The fp64 oracle timed on the host on a bounded sample of the same workload."""
-    import numpy as np
+# threads of the CPU baseline: the host cores available to this process, at most this many
+# (one GPU's share of its box)
+CPU_BASELINE_MAX_WORKERS = 16
+
+
+def _decode_workload(name, kv):
+    """The oracle's workload for the CPU baseline and its rows (batch indices)."""
+    from dataclasses import replace
+
+    from synth import workloads
+
+    if name == "agentic_fork_64x33281":
+        wl = workloads.agentic_fork(steps=1, layers=1)
+        rows = list(range(16))  # the 16 branches of root 0 (32770 tokens each at step 0)
+    else:
+        wl = workloads.get_workload(name)
+        rows = None
+    if kv != "bf16":
+        wl = replace(wl, kv_format=kv)
+    return wl, rows
+
+
+def _cpu_baseline_worker(task):
+    """One single-threaded oracle: the fp64 decode attention of `rows` of the
+    workload's first decode (layer 0), repeated for `seconds`.  Runs in a fresh
+    interpreter (spawn), which never touches the GPU."""
+    name, kv, rows, writers, seconds = task
+    import time as _t
+
     from threadpoolctl import threadpool_limits
 
     from oracle.runner import OracleReplay
-    from synth import workloads
 
-    cores = len(os.sched_getaffinity(0))
-    name = args.workload
-    if name == "qwen3_8b_37x2304":
-        wl = workloads.qwen_independent()
-        layers, writers = None, None
-        sample = "Qwen3-8B-shaped layer: the oracle's decode of all 37 sequences x 2304 tokens, one layer"
-    elif name == "shared_prefix_16x8448":
-        wl = workloads.shared_prefix()
-        layers, writers = None, None
-        sample = "shared-prefix layer: the oracle's decode of all 16 sequences x 8448 tokens, one layer"
-    elif name == "gqa70b_12x131072":
-        wl = workloads.gqa70b_128k()
-        layers, writers = None, {0}
-        sample = "70B-GQA layer: the oracle's decode of sequence 0 (131072 tokens, 64 heads)"
-    else:
-        wl = workloads.agentic_fork(steps=1, layers=1)
-        layers, writers = [0], {0, 1}
-        sample = "fork workload: the oracle's decode of sequences 0 and 1 (32770 tokens), layer 0, step 0"
-    if args.kv != "bf16":
-        from dataclasses import replace
-
-        wl = replace(wl, kv_format=args.kv)
-        sample += f", {args.kv} pool"
-    ref = OracleReplay(wl, layers=layers, writers=writers).run()
-    rows = list(range(len(ref.decodes[0]["seq_ids"]))) if writers is None else sorted(writers)
-    kv_per_tok = 2 * wl.num_kv_heads * (wl.head_dim * wl.elem_bytes if args.kv == "bf16" else
-                                        wl.head_dim * (8 if args.kv == "q8_0" else 4) // 8 + wl.head_dim // 16)
-    bytes_one = sum(ref.decodes[0]["lengths"][r] for r in rows) * kv_per_tok
-    reps = 0
-    c0 = time.process_time()
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=cores):
+    wl, _ = _decode_workload(name, kv)
+    with threadpool_limits(limits=1):
+        ref = OracleReplay(wl, layers=[0], writers=set(writers)).run()
+        lens = ref.decodes[0]["lengths"]
+        tokens = sum(lens[r] for r in rows)
+        reps = 0
+        c0 = _t.process_time()
+        t0 = _t.perf_counter()
         while True:
             ref.attention(0, 0, rows=rows)
             reps += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
+            if _t.perf_counter() - t0 >= seconds:
                 break
-    wall = time.perf_counter() - t0
-    cpu = time.process_time() - c0
+        wall = _t.perf_counter() - t0
+        cpu = _t.process_time() - c0
+    return {"tokens": tokens, "rows": len(rows), "reps": reps, "wall": wall, "cpu": cpu}
+
+
+def cpu_baseline(args):
+    """The fp64 oracle (unchanged) timed on the host: the workload's sequences are
+    dealt to single-threaded oracle processes, one per available core (at most
+    one per sequence), which decode their sequences in parallel for
+    --cpu-seconds; the rate is the sum of the processes' rates."""
+    import multiprocessing as mp
+
+    name = args.workload
+    wl, rows = _decode_workload(name, args.kv)
+    n_seqs = len(next(op for op in wl.ops if op[0] == "decode")[1])
+    rows = list(range(n_seqs)) if rows is None else rows
+    workers = max(1, min(len(os.sched_getaffinity(0)), CPU_BASELINE_MAX_WORKERS, len(rows)))
+    shares = [rows[w::workers] for w in range(workers)]
+    roots = {0} if name == "agentic_fork_64x33281" else set()  # branches read their root's blocks
+    tasks = [(name, args.kv, share, sorted(set(share) | roots), args.cpu_seconds) for share in shares]
+    with mp.get_context("spawn").Pool(workers) as pool:
+        res = pool.map(_cpu_baseline_worker, tasks)
+    kv_per_tok = 2 * wl.num_kv_heads * (wl.head_dim * wl.elem_bytes if args.kv == "bf16" else
+                                        wl.head_dim * (8 if args.kv == "q8_0" else 4) // 8 + wl.head_dim // 16)
+    gbs = sum(r["tokens"] * kv_per_tok * r["reps"] / r["wall"] for r in res) / 1e9
+    tok_s = sum(r["rows"] * r["reps"] / r["wall"] for r in res)
+    wall = max(r["wall"] for r in res)
+    util = sum(r["cpu"] for r in res) / wall
     return {
-        "value": round(bytes_one * reps / wall / 1e9, 4),
+        "value": round(gbs, 4),
         "unit": "GB/s",
-        "cores": cores,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{sample}; repeated {reps} times in {wall:.1f} s",
-        "tokens_per_s_per_layer": round(len(rows) * reps / wall, 3),
-        "cpu_utilisation": round(cpu / wall, 2),
+        "sample": f"{wl.name}{'' if args.kv == 'bf16' else ' (' + args.kv + ' pool)'}: the oracle's decode "
+                  f"attention (layer 0, first decode step) of {len(rows)} sequences dealt to {workers} "
+                  f"single-threaded processes, each repeating its share for {wall:.1f} s "
+                  f"({sum(r['reps'] for r in res)} repetitions in all)",
+        "tokens_per_s_per_layer": round(tok_s, 3),
+        "cpu_utilisation": round(util, 2),
+        "cores_available": len(os.sched_getaffinity(0)),
     }
 
 

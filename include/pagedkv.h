@@ -125,7 +125,14 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* k_cache, void* v_cache
 /* Destroy the host state (and any pending release events). */
 void kv_pool_destroy(kv_pool* pool);
 
-/* Register an empty sequence.  KV_ERR_INVALID if seq_id exists. */
+/* The configuration the pool was created with (for callers that check tensor
+ * shapes and element types against it). */
+kv_status kv_pool_get_config(const kv_pool* pool, kv_pool_config* out);
+
+/* Register an empty sequence: length 0 and an empty block table; its first
+ * append allocates its first block ([BT] §05: a new request starts with no
+ * blocks and a block is taken when the first token's offset is 0; [KVM] paged
+ * KV allocation, allocation at o = 0).  KV_ERR_INVALID if seq_id exists. */
 kv_status kv_seq_add(kv_pool* pool, int64_t seq_id);
 
 /* Fork: child gets a copy of parent's block table, each of those blocks gains
@@ -151,9 +158,13 @@ kv_status kv_append_slots(kv_pool* pool, int32_t n, const int64_t* seq_ids, cons
                           int64_t* slot_mapping_out, int64_t slot_capacity,
                           int64_t* cow_pairs_out, int32_t cow_capacity, int32_t* n_cow_out);
 
-/* Host copy of the block tables and lengths of n sequences:
- * tables_out[n][max_blocks] (row i, entries past ceil(len/B) set to -1) and
- * context_lens_out[n].  KV_ERR_INVALID if a table is longer than max_blocks. */
+/* Host copy of the block tables and lengths of n sequences, the per-sequence
+ * logical -> physical block maps the decode kernel reads ([BT] §06: the
+ * block_tables [num_seqs, max_blocks] and context_lens inputs of the decode;
+ * [KVM] PagedAttention virtual memory model: T maps logical block l to
+ * physical block p): tables_out[n][max_blocks] (row i, entries past
+ * ceil(len/B) set to -1) and context_lens_out[n].  KV_ERR_INVALID if a table
+ * is longer than max_blocks or a sequence is unknown or swapped out. */
 kv_status kv_get_block_tables(const kv_pool* pool, int32_t n, const int64_t* seq_ids,
                               int32_t max_blocks, int32_t* tables_out, int32_t* context_lens_out);
 
@@ -179,6 +190,14 @@ kv_status kv_pool_retire(kv_pool* pool, uint64_t completed_fence);
  * pending events first).  Ready groups go back in release order. */
 kv_status kv_pool_reclaim(kv_pool* pool, int32_t wait);
 
+/* Occupancy of the pool: the counts the conservation law of [BT] §13 relates
+ * (N_free + N_allocated + N_pending = N_total), so that the KV-cache
+ * utilisation U_KV = N_allocated / N_total of [KVM] (serving telemetry, Eq. 8)
+ * can be monitored; the blocks held more than once ([KVM] copy-on-write
+ * branching: shared blocks have a reference count above one); and the live
+ * sequences' tokens and table entries (tokens / (entries * B) is the slot
+ * occupancy, whose complement is the tail waste of [BT] §04).  Host memory; no
+ * device work. */
 kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
 
 /* Free list in pop order (out capacity cap; *n_out = its length). */

@@ -32,6 +32,14 @@ class KVOutOfBlocks(KVError, MemoryError):
     pass
 
 
+class KVArgumentError(KVError, ValueError):
+    """A tensor argument whose device, element type, shape or layout does not
+    match the call (found by the binding before the library is called)."""
+
+    def __init__(self, message):
+        super().__init__(KV_ERR_INVALID, message)
+
+
 class kv_pool_config(C.Structure):
     _fields_ = [("num_layers", C.c_int32), ("num_blocks", C.c_int32), ("block_size", C.c_int32),
                 ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32)]
@@ -72,6 +80,7 @@ SIGNATURES = {
     "kv_pool_retire": (_I32, [_P, _U64]),
     "kv_pool_reclaim": (_I32, [_P, _I32]),
     "kv_pool_stats": (_I32, [_P, C.POINTER(kv_pool_stats_t)]),
+    "kv_pool_get_config": (_I32, [_P, C.POINTER(kv_pool_config)]),
     "kv_pool_free_list": (_I32, [_P, _I32, _P, C.POINTER(_I32)]),
     "kv_pool_refcounts": (_I32, [_P, _P]),
     "kv_pool_check": (_I32, [_P]),
@@ -109,14 +118,22 @@ SIGNATURES = {
 _lib = None
 
 
+def lib_path():
+    """The library to load: libpagedkv.so, or the file named by PAGEDKV_LIBRARY
+    (the host-only sanitizer build of the CPU tests, whose device entry points
+    all fail with KV_ERR_UNSUPPORTED)."""
+    return os.environ.get("PAGEDKV_LIBRARY") or LIB_PATH
+
+
 def lib():
     """The loaded library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m pagedattention_decode_amd.build`")
-        handle = C.CDLL(LIB_PATH)
+        handle = C.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)
             fn.restype = res
@@ -143,8 +160,78 @@ def _dev(t):
     if t is None:
         return None
     if not t.is_contiguous():
-        raise ValueError("device tensors must be contiguous")
+        raise KVArgumentError("device tensors must be contiguous")
     return C.c_void_p(t.data_ptr())
+
+
+# -- argument checks ----------------------------------------------------------
+# The C ABI takes raw pointers, so a tensor of the wrong element type or shape
+# would be read out of bounds or misread; these checks refuse such arguments
+# before the call.  Tensors holding bf16 / f32 values may be given in any
+# torch type of the same element size (the tests pass raw bit patterns as
+# int16 / int32).
+
+_configs = {}
+
+
+def kv_pool_get_config(pool):
+    key = pool.value if isinstance(pool, C.c_void_p) else int(pool)
+    cfg = _configs.get(key)
+    if cfg is None:
+        cfg = kv_pool_config()
+        _check(lib().kv_pool_get_config(pool, C.byref(cfg)))
+        _configs[key] = cfg
+    return cfg
+
+
+def _forget_config(pool):
+    _configs.pop(pool.value if isinstance(pool, C.c_void_p) else int(pool), None)
+
+
+def _row_bytes(cfg):
+    """Element size of new K/V rows, queries and outputs for this pool: 4 for an
+    f32 pool, 2 (bf16) otherwise."""
+    return 4 if cfg.dtype == KV_F32 else 2
+
+
+def _need(cond, msg):
+    if not cond:
+        raise KVArgumentError(msg)
+
+
+def _device_tensor(t, name, ndim=None, elem=None, dtype=None, shape=None):
+    import torch
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.is_cuda, f"{name} must be on the GPU (it is on {t.device})")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype} (it is {t.dtype})")
+    if elem is not None:
+        _need(t.element_size() == elem and not t.is_complex(),
+              f"{name} must have {elem}-byte elements (it has {t.dtype})")
+    if ndim is not None:
+        _need(t.dim() == ndim, f"{name} must have {ndim} dimensions (shape {tuple(t.shape)})")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)} (it has {tuple(t.shape)})")
+
+
+def _rows(pool, t, name, n, heads):
+    """A [n, heads, d] tensor of the pool's row element type."""
+    cfg = kv_pool_get_config(pool)
+    _device_tensor(t, name, ndim=3, elem=_row_bytes(cfg), shape=(n, heads, cfg.head_dim))
+
+
+def _tables(block_tables, context_lens, n=None):
+    import torch
+    _device_tensor(block_tables, "block_tables", ndim=2, dtype=torch.int32)
+    n = block_tables.shape[0] if n is None else n
+    _need(block_tables.shape[0] == n, f"block_tables must have {n} rows")
+    _device_tensor(context_lens, "context_lens", dtype=torch.int32, shape=(n,))
+
+
+def _workspace(ws):
+    if ws is not None:
+        _device_tensor(ws, "workspace")
 
 
 def _stream(stream):
@@ -183,6 +270,7 @@ def kv_pool_create(cfg, k_cache, v_cache, initial_free_order=None):
 
 
 def kv_pool_destroy(pool):
+    _forget_config(pool)
     lib().kv_pool_destroy(pool)
 
 
@@ -272,13 +360,22 @@ def kv_last_error():
 
 def reshape_and_cache(pool, layer, k_new, v_new, slot_mapping, stream=None):
     """k_new, v_new: device [n, Hkv, d]; slot_mapping: device int64 [n]."""
+    import torch
+    _device_tensor(slot_mapping, "slot_mapping", ndim=1, dtype=torch.int64)
     n = int(slot_mapping.numel())
+    cfg = kv_pool_get_config(pool)
+    _rows(pool, k_new, "k_new", n, cfg.num_kv_heads)
+    _rows(pool, v_new, "v_new", n, cfg.num_kv_heads)
     _check(lib().reshape_and_cache(pool, int(layer), _dev(k_new), _dev(v_new), _dev(slot_mapping), n,
                                    _stream(stream)))
 
 
 def copy_blocks(pool, pairs, stream=None):
     """pairs: device int64 [k, 2] of (src, dst)."""
+    if pairs is not None:
+        import torch
+        _device_tensor(pairs, "pairs", ndim=2, dtype=torch.int64)
+        _need(pairs.shape[1] == 2, "pairs must have shape [k, 2]")
     n = int(pairs.shape[0]) if pairs is not None else 0
     _check(lib().copy_blocks(pool, _dev(pairs) if n else None, n, _stream(stream)))
 
@@ -313,7 +410,11 @@ def paged_attention_workspace_bytes(pool, n_seqs, num_q_heads, max_blocks_per_se
 def paged_attention_decode(pool, layer, q, out, block_tables, context_lens, num_q_heads, opts=None,
                            workspace=None, stream=None):
     """q, out: device [n, Hq, d]; block_tables: device int32 [n, max_blocks]; context_lens int32 [n]."""
+    _tables(block_tables, context_lens)
     n_seqs, max_blocks = int(block_tables.shape[0]), int(block_tables.shape[1])
+    _rows(pool, q, "q", n_seqs, num_q_heads)
+    _rows(pool, out, "out", n_seqs, num_q_heads)
+    _workspace(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().paged_attention_decode(pool, int(layer), _dev(q), _dev(out), _dev(block_tables),
                                         _dev(context_lens), n_seqs, max_blocks, int(num_q_heads),
@@ -331,8 +432,15 @@ def paged_attention_prefill(pool, layer, q, out, q_indptr, block_tables, context
                             opts=None, workspace=None, stream=None):
     """q, out: device [total_q, Hq, d]; q_indptr: device int32 [n + 1]; block_tables: device
     int32 [n, max_blocks]; context_lens: device int32 [n] (lengths after the chunk)."""
+    import torch
+    _tables(block_tables, context_lens)
     n_seqs, max_blocks = int(block_tables.shape[0]), int(block_tables.shape[1])
+    _device_tensor(q, "q", ndim=3)
     total_q = int(q.shape[0])
+    _rows(pool, q, "q", total_q, num_q_heads)
+    _rows(pool, out, "out", total_q, num_q_heads)
+    _device_tensor(q_indptr, "q_indptr", dtype=torch.int32, shape=(n_seqs + 1,))
+    _workspace(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().paged_attention_prefill(pool, int(layer), _dev(q), _dev(out), _dev(q_indptr), _dev(block_tables),
                                          _dev(context_lens), n_seqs, total_q, int(max_q_len), max_blocks,
@@ -407,8 +515,15 @@ def paged_attention_cascade_workspace_bytes(pool, n_seqs, n_groups, max_group, n
 def paged_attention_decode_cascade(pool, layer, q, out, block_tables, context_lens, num_q_heads, group_start,
                                    shared_blocks, max_group, opts=None, workspace=None, stream=None):
     """group_start: device int32 [g + 1]; shared_blocks: device int32 [g]."""
+    import torch
+    _tables(block_tables, context_lens)
     n_seqs, max_blocks = int(block_tables.shape[0]), int(block_tables.shape[1])
+    _rows(pool, q, "q", n_seqs, num_q_heads)
+    _rows(pool, out, "out", n_seqs, num_q_heads)
+    _device_tensor(shared_blocks, "shared_blocks", ndim=1, dtype=torch.int32)
     n_groups = int(shared_blocks.shape[0])
+    _device_tensor(group_start, "group_start", dtype=torch.int32, shape=(n_groups + 1,))
+    _workspace(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().paged_attention_decode_cascade(pool, int(layer), _dev(q), _dev(out), _dev(block_tables),
                                                 _dev(context_lens), n_seqs, max_blocks, int(num_q_heads),

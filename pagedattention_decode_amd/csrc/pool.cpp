@@ -285,6 +285,12 @@ kv_status kv_get_block_tables(const kv_pool* p, int32_t n, const int64_t* seq_id
   return ok();
 }
 
+kv_status kv_pool_get_config(const kv_pool* p, kv_pool_config* out) {
+  if (!p || !out) return fail(KV_ERR_INVALID, "NULL argument");
+  *out = p->cfg;
+  return ok();
+}
+
 kv_status kv_seq_info(const kv_pool* p, int64_t seq_id, int32_t* length, int32_t* num_blocks) {
   if (!p) return fail(KV_ERR_INVALID, "pool is NULL");
   auto it = p->seqs.find(seq_id);

@@ -42,10 +42,13 @@ def bits_to_float_tensor(t: torch.Tensor, dtype: str) -> torch.Tensor:
 
 class GpuRun:
     def __init__(self, wl, layers=None, writers=None, opts=None, free_order=None, fill=None,
-                 max_blocks=None, ref=None, decode_layers=None, staging_bytes=64 << 20, on_swap=None):
+                 max_blocks=None, ref=None, decode_layers=None, staging_bytes=64 << 20, on_swap=None,
+                 decode_steps=None):
         self.wl = wl
         self.layers = list(range(wl.num_layers)) if layers is None else list(layers)
         self.decode_layers = self.layers if decode_layers is None else list(decode_layers)
+        # decode ops (by index) whose attention runs; the others only record their tables
+        self.decode_steps = None if decode_steps is None else set(decode_steps)
         self.writers = None if writers is None else set(writers)
         self.opts = opts
         self.ref = ref
@@ -196,8 +199,9 @@ class GpuRun:
             d_tables = torch.from_numpy(tables).cuda()
             d_lens = torch.from_numpy(lens).cuda()
             outs = {}
-            for layer in self.decode_layers:
-                outs[layer] = self.decode(self.n_decode, layer, d_tables, d_lens, len(seq_ids))
+            if self.decode_steps is None or self.n_decode in self.decode_steps:
+                for layer in self.decode_layers:
+                    outs[layer] = self.decode(self.n_decode, layer, d_tables, d_lens, len(seq_ids))
             self.decode_outputs.append(outs)
             self.n_decode += 1
         else:

@@ -342,3 +342,21 @@ def test_shared_prefix_plan_random_forks():
     assert list(pool.shared_prefix_plan([])[0]) == [0]
     with pytest.raises(B.KVError):
         pool.shared_prefix_plan([10 ** 6])
+
+
+def test_pool_config_round_trip_and_host_tensors_refused():
+    """kv_pool_get_config returns the creation config; the binding refuses device
+    arguments that are not GPU tensors before calling the library."""
+    import torch
+
+    cfg = B.make_config(3, 40, 8, 2, 64, B.KV_BF16)
+    pool = B.kv_pool_create(cfg, 0, 0)
+    try:
+        got = B.kv_pool_get_config(pool)
+        assert [getattr(got, f) for f, _ in got._fields_] == [3, 40, 8, 2, 64, B.KV_BF16]
+        rows = torch.zeros((2, 2, 64), dtype=torch.bfloat16)
+        with pytest.raises(B.KVArgumentError) as e:
+            B.reshape_and_cache(pool, 0, rows, rows, torch.zeros(2, dtype=torch.int64))
+        assert "GPU" in str(e.value) and isinstance(e.value, ValueError) and e.value.status == B.KV_ERR_INVALID
+    finally:
+        B.kv_pool_destroy(pool)

@@ -48,8 +48,9 @@ def test_traffic_lookup_follows_the_kernel_sources(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
     csrc = tmp_path / "pagedattention_decode_amd" / "csrc"
     csrc.mkdir(parents=True)
-    (csrc / "kernels.hip").write_text("// kernels, version 1\n")
-    rec = {"kernel_source_sha256": bench.kernel_source_sha256(("kernels.hip",)),
+    for name in bench.DECODE_SOURCES:
+        (csrc / name).write_text(f"// {name}, version 1\n")
+    rec = {"kernel_source_sha256": bench.kernel_source_sha256(bench.DECODE_SOURCES),
            "traffic_bytes_per_launch": 123, "traffic_bytes_per_call": 456, "algorithmic_bytes_per_launch": 100}
     (tmp_path / "profiles" / "hbm_traffic_w.json").write_text(json.dumps(rec))
     assert bench.measured_traffic("w") == 123
@@ -61,6 +62,12 @@ def test_traffic_lookup_follows_the_kernel_sources(tmp_path, monkeypatch):
     (csrc / "kernels.hip").write_text("// kernels, version 2\n")  # the counters no longer describe it
     assert bench.measured_traffic("w") is None
     assert bench.traffic_ratio("w") is None
+    # a header the device code includes counts as much as the kernel file
+    (csrc / "kernels.hip").write_text("// kernels.hip, version 1\n")
+    assert bench.measured_traffic("w") == 123
+    (csrc / "device_common.h").write_text("// operand loads changed\n")
+    assert bench.measured_traffic("w") is None
+    assert set(bench.DECODE_SOURCES) >= {"kernels.hip", "device_common.h", "pool_internal.h"}
 
 
 def test_committed_traffic_summaries_are_consistent():

@@ -1,6 +1,9 @@
 """GPU parity of the read-once decode over shared prefixes (cascade) against the
 float64 oracle, bf16 bar.  The groups come from the library's own plan of the
 host tables unless a test gives them; outputs and workspace start as NaN bytes.
+The fork workload (4 roots x 16 forks, 512 steps, 36 layers) is checked with
+the read-once decode beside the plain one in test_gpu_parity.py
+(test_agentic_fork_sampled), so that its long replay runs once.
 """
 
 import numpy as np
@@ -72,21 +75,6 @@ def test_ragged_groups(partition):
     assert max(sb) > 0 and min(np.diff(gs)) >= 1
     out = run.decode_cascade(0, 0, opts=B.attention_options(partition_tokens=partition)).double().cpu().numpy()
     check(out, ref.attention(0, 0), f"ragged groups P={partition}")
-
-
-def test_agentic_forks_sampled():
-    announce("fork workload: 4 roots x 32769, 16 forks each, 20 steps; cascade on steps 0 and 19")
-    wl = workloads.agentic_fork(steps=20, layers=36)
-    sample = [0, 1, 15, 16, 47, 63]
-    writers = set(sample) | {0, 16, 32, 48}
-    layers = [0]
-    ref = OracleReplay(wl, layers=layers, writers=writers).run()
-    run = GpuRun(wl, ref=ref, layers=layers, writers=writers, decode_layers=[0]).run()
-    for i in (0, 19):
-        gs, sb = run.pool.shared_prefix_plan(run.decodes[i]["seq_ids"])
-        assert len(sb) == 4 and all(b == 2048 for b in sb), (list(gs), list(sb))
-        got = run.decode_cascade(i, 0).double().cpu().numpy()[sample]
-        check(got, ref.attention(i, 0, rows=sample), f"step {i}")
 
 
 def test_no_sharing_equals_plain_decode():

@@ -4,8 +4,9 @@
   against the oracle's logical pool, with every unwritten element unchanged;
 * decode attention: fp32 within 1e-5 (max abs); bf16 within max abs 2e-2 and a
   per-row relative L2 error of 5e-3 against the float64 oracle;
-* the workloads at their full sizes (the 12 x 131072 and fork workloads on sampled
-  sequences), ragged lengths, edge cases and both kernels.
+* the workloads at their full sizes: the 12 x 131072 workload on every sequence,
+  the fork workload over all 512 steps of its 36-layer pool with sampled
+  (step, layer, sequence) points; ragged lengths, edge cases and both kernels.
 
 Every test prints the case it runs before touching the GPU.
 """
@@ -20,6 +21,7 @@ from oracle.attention import decode_attention
 from oracle.runner import OracleReplay
 from pagedattention_decode_amd import binding as B
 from synth import draws, workloads
+from tests import oracle_pool
 from tests.gpu_harness import GpuRun, attention_errors, bits_to_float_tensor, to_device_bits
 
 pytestmark = pytest.mark.gpu
@@ -198,29 +200,79 @@ def test_shared_prefix_16x8448_full():
     assert (tables[:, :384] == tables[0, :384]).all()
 
 
-def test_gqa70b_12x131072_sampled():
-    announce("70B-GQA layer, 12 x 131072 tokens, Hq=64, split-K 512; sequences 0, 5, 11 checked")
+@pytest.mark.timeout(1800)
+def test_gqa70b_12x131072_full():
+    announce("70B-GQA layer, 12 x 131072 tokens, Hq=64: every sequence written and compared, split-K 512 "
+             "(the benchmarked launch) and the automatic partition")
     wl = workloads.gqa70b_128k()
-    sample = [0, 5, 11]
-    ref = OracleReplay(wl, writers=sample).run()
-    run = GpuRun(wl, ref=ref, writers=sample, opts=B.attention_options(partition_tokens=512)).run()
+    S = 12
+    # the oracle's outputs: one process per sequence, each writing that sequence's K/V only
+    res = oracle_pool.evaluate([("gqa70b_128k", {}, [0], [s], [(0, 0, [s])]) for s in range(S)])
+    expect = np.concatenate([r[0] for r in res])
+    # slots and tables of the whole batch are checked against the oracle's block manager
+    ref = OracleReplay(wl, layers=[], writers=set()).run()
+    run = GpuRun(wl, ref=ref, opts=B.attention_options(partition_tokens=512)).run()
     got = run.decode_outputs[0][0].double().cpu().numpy()
-    expect = ref.attention(0, 0, rows=sample)
-    check_outputs(got[sample], expect, wl.dtype, "12 x 131072 sampled")
+    for s in range(S):
+        check_outputs(got[s:s + 1], expect[s:s + 1], wl.dtype, f"sequence {s}, split-K 512")
+    rec = run.decodes[0]
+    d_tables = torch.from_numpy(rec["tables"]).cuda()
+    d_lens = torch.from_numpy(rec["lengths"]).cuda()
+    auto = run.decode(0, 0, d_tables, d_lens, S, opts=B.attention_options()).double().cpu().numpy()
+    check_outputs(auto, expect, wl.dtype, "all sequences, automatic partition")
 
 
+# the fork workload's sampled steps, layers and sequences: the first copy-on-write
+# step, the first block crossings of the divergent suffixes (steps 15 / 16), the
+# middle and the last step; the first, middle and last layer of the 36-layer pool;
+# sequences of every root, roots and forks
+FORK_STEPS = (0, 1, 15, 16, 255, 511)
+FORK_LAYERS = (0, 17, 35)
+FORK_ROWS = (0, 1, 15, 16, 47, 63)
+FORK_ROOT_OF = {0: 0, 1: 0, 15: 0, 16: 16, 47: 32, 63: 48}
+
+
+def fork_oracle():
+    """{(step, layer, sequence): [Hq, d]} of the oracle on the sampled points, replayed
+    per (layer, root) in parallel processes."""
+    by_root = {}
+    for r in FORK_ROWS:
+        by_root.setdefault(FORK_ROOT_OF[r], []).append(r)
+    tasks = []
+    for layer in FORK_LAYERS:
+        for root, rows in by_root.items():
+            step_sets = (FORK_STEPS[:3], FORK_STEPS[3:]) if len(rows) > 1 else (FORK_STEPS,)
+            for steps in step_sets:
+                tasks.append(("agentic_fork", {"steps": 512, "layers": 36}, [layer], sorted(set(rows) | {root}),
+                              [(i, layer, rows) for i in steps]))
+    expect = {}
+    for task, outs in zip(tasks, oracle_pool.evaluate(tasks)):
+        for (i, layer, rows), out in zip(task[4], outs):
+            for r, o in zip(rows, out):
+                expect[(i, layer, r)] = o
+    return expect
+
+
+@pytest.mark.timeout(1800)
 def test_agentic_fork_sampled():
-    announce("fork workload: 4 roots x 32769, 16 forks each, 20 steps, layers {0, 1} of 36 written")
-    wl = workloads.agentic_fork(steps=20, layers=36)
-    sample_seqs = [0, 1, 15, 16, 47, 63]
-    writers = set(sample_seqs) | {0, 16, 32, 48}
-    layers = [0, 1]
-    ref = OracleReplay(wl, layers=layers, writers=writers).run()
-    run = GpuRun(wl, ref=ref, layers=layers, writers=writers).run()
-    for i in (0, 1, 15, 16, 19):
-        for layer in layers:
-            got = run.decode_outputs[i][layer].double().cpu().numpy()[sample_seqs]
-            check_outputs(got, ref.attention(i, layer, rows=sample_seqs), wl.dtype, f"step {i} layer {layer}")
+    announce("fork workload: 4 roots x 32769, 16 forks each, all 512 steps over the 36-layer pool; plain and "
+             f"read-once decode at steps {FORK_STEPS} x layers {FORK_LAYERS}, sequences {FORK_ROWS}")
+    wl = workloads.agentic_fork(steps=512, layers=36)
+    expect = fork_oracle()
+    writers = set(FORK_ROWS) | set(FORK_ROOT_OF.values())
+    ref = OracleReplay(wl, layers=[], writers=set()).run()  # slots, copy pairs and tables, bit for bit
+    run = GpuRun(wl, ref=ref, layers=list(FORK_LAYERS), writers=writers, decode_steps=FORK_STEPS).run()
+    assert sum(len(p) for _, p in run.appends) == 60, "60 copy-on-write copies at the first divergent step"
+    rows = list(FORK_ROWS)
+    for i in FORK_STEPS:
+        gs, sb = run.pool.shared_prefix_plan(run.decodes[i]["seq_ids"])
+        assert len(sb) == 4 and all(b == 2048 for b in sb), (list(gs), list(sb))
+        for layer in FORK_LAYERS:
+            exp = np.stack([expect[(i, layer, r)] for r in rows])
+            got = run.decode_outputs[i][layer].double().cpu().numpy()[rows]
+            check_outputs(got, exp, wl.dtype, f"step {i} layer {layer}")
+            got = run.decode_cascade(i, layer).double().cpu().numpy()[rows]
+            check_outputs(got, exp, wl.dtype, f"step {i} layer {layer}, read-once decode")
 
 
 # ---------------------------------------------------------------------------
@@ -317,6 +369,25 @@ def test_invalid_arguments_are_rejected():
         run.pool.decode(0, q, q.clone(), t, l_, 32, opts=B.attention_options(partition_tokens=16))
     with pytest.raises(B.KVError):
         run.pool.decode(0, q, q.clone(), t, l_, 8 * 17)  # G = 17
+    # the binding refuses tensors of the wrong element type, shape or device before the call
+    slots32 = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    row = torch.zeros((1, 8, 128), dtype=torch.int16, device="cuda")
+    bad_calls = {
+        "int32 slot mapping": lambda: run.pool.cache(0, row, row, slots32),
+        "k rows of 4-byte elements": lambda: run.pool.cache(0, row.float(), row, slots32.long()),
+        "k rows of the wrong head count": lambda: run.pool.cache(0, row[:, :4].contiguous(), row, slots32.long()),
+        "int64 block tables": lambda: run.pool.decode(0, q, q.clone(), t.long(), l_, 32),
+        "int64 context lengths": lambda: run.pool.decode(0, q, q.clone(), t, l_.long(), 32),
+        "float32 queries on a bf16 pool": lambda: run.pool.decode(0, q.float(), q.clone(), t, l_, 32),
+        "queries of the wrong head dim": lambda: run.pool.decode(0, q[:, :, :64].contiguous(), q.clone(), t, l_, 32),
+        "host queries": lambda: run.pool.decode(0, q.cpu(), q.clone(), t, l_, 32),
+        "lengths of another batch": lambda: run.pool.decode(0, q, q.clone(), t, torch.cat([l_, l_]), 32),
+        "int32 copy pairs": lambda: run.pool.copy(torch.zeros((1, 2), dtype=torch.int32, device="cuda")),
+    }
+    for what, call in bad_calls.items():
+        with pytest.raises(B.KVArgumentError):
+            call()
+        print(f"  refused: {what}", flush=True)
     f32 = small_fork_workload(draws.F32, 4, 64)
     r2 = GpuRun(f32)
     with pytest.raises(B.KVError) as e:
