@@ -25,9 +25,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <type_traits>
 #include <cmath>
 #include <string>
+#include <type_traits>
 
 #include "device_common.h"
 #include "pool_internal.h"
@@ -402,8 +402,9 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
     __syncthreads();
   }
 
-  // merge the waves of the workgroup: common maximum per head, then every
-  // wave adds its rescaled partial output into q_s (no longer needed)
+  // merge the waves of the workgroup: common maximum per head, then the waves
+  // add their rescaled partial outputs into q_s (no longer needed) in a fixed
+  // order, one wave at a time, so the result is the same bits on every run
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     if (h >= G) continue;
@@ -416,19 +417,23 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
   if (poisoned) atomicOr(&poison_s, 1);
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) q_s[i / D][i % D] = 0.f;
   __syncthreads();
+  for (int turn = 0; turn < kGenericWaves; ++turn) {
+    if (wave == turn) {
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h >= G) continue;
-    float M = -INFINITY;
-    for (int v = 0; v < kGenericWaves; ++v) M = fmaxf(M, m_s[v][h]);
-    const float f = (M == -INFINITY) ? 0.f : exp2f(m_run[h] - M);
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h >= G) continue;
+        float M = -INFINITY;
+        for (int v = 0; v < kGenericWaves; ++v) M = fmaxf(M, m_s[v][h]);
+        const float f = (M == -INFINITY) ? 0.f : exp2f(m_run[h] - M);
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) {
-      const int e = lane + 64 * k;
-      if (e < D) atomicAdd(&q_s[h][e], acc[h][k] * f);
+        for (int k = 0; k < DPL; ++k) {
+          const int e = lane + 64 * k;
+          if (e < D) q_s[h][e] += acc[h][k] * f;
+        }
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
   const bool any_poison = poison_s != 0;
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
     const int h = i / D, e = i % D;

@@ -330,6 +330,19 @@ def test_split_and_single_pass_agree():
 
 
 
+@pytest.mark.parametrize("kernel", [B.KV_KERNEL_GENERIC, B.KV_KERNEL_MFMA])
+def test_repeated_calls_give_identical_bits(kernel):
+    announce(f"kernel {kernel}: five calls on one input give the same output bits")
+    wl = ragged_workload(32, 8, 128, [2049, 700, 33, 1, 1500], layers=1)
+    run = GpuRun(wl).run()
+    tables = torch.from_numpy(run.decodes[0]["tables"]).cuda()
+    lens = torch.from_numpy(run.decodes[0]["lengths"]).cuda()
+    outs = [run.decode(0, 0, tables, lens, 5, opts=B.attention_options(kernel=kernel, partition_tokens=256))
+            for _ in range(5)]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0]), "the output bits changed between calls"
+
+
 def test_workspace_reused_across_calls():
     announce("split-K kernel: one workspace reused by 6 calls (layers 0, 1 alternating), outputs poisoned")
     lengths = [2304, 17, 1000, 4096, 33, 2304, 700, 1]
