@@ -455,6 +455,23 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
                                  const kv_attention_options* opts, void* d_workspace,
                                  uint64_t workspace_bytes, void* hip_stream);
 
+/* paged_attention_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation): the split-K partials live in a static device array the
+ * library holds on every GPU it runs on (paged_attention_static_scratch_bytes()
+ * bytes, 32 MiB), whose address is looked up on the first call on each device.
+ * Nothing is allocated and nothing is cleared; results equal
+ * paged_attention_decode's bit for bit.  A call whose workspace
+ * (paged_attention_workspace_bytes) would exceed the scratch fails with
+ * KV_ERR_INVALID.  Every call on one GPU uses the same scratch, so calls that
+ * can overlap on one GPU (on different streams, or from several host threads)
+ * race: order them on one stream. */
+uint64_t paged_attention_static_scratch_bytes(void);
+kv_status paged_attention_decode_static(kv_pool* pool, int32_t layer, const void* q, void* out,
+                                        const int32_t* d_block_tables, const int32_t* d_context_lens,
+                                        int32_t n_seqs, int32_t max_blocks_per_seq, int32_t num_q_heads,
+                                        const kv_attention_options* opts, void* hip_stream);
+
 /* Read-once decode over shared prefixes (cascade).  Sequences are given in
  * groups: group g holds the sequences group_start[g] .. group_start[g+1]-1 (in
  * the order of q, out and the tables), whose tables agree on their first

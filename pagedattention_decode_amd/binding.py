@@ -90,6 +90,9 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (_U64, [_P, _I32, _I32, _I32, C.POINTER(kv_attention_options)]),
     "paged_attention_decode": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _I32,
                                       C.POINTER(kv_attention_options), _P, _U64, _P]),
+    "paged_attention_static_scratch_bytes": (_U64, []),
+    "paged_attention_decode_static": (_I32, [_P, _I32, _P, _P, _P, _P, _I32, _I32, _I32,
+                                             C.POINTER(kv_attention_options), _P]),
     "kv_prefix_match": (_I32, [_P, _P, _I32, C.POINTER(_I32), C.POINTER(_I32)]),
     "kv_seq_attach_prefix": (_I32, [_P, _I64, _P, _I32, C.POINTER(_I32)]),
     "kv_prefix_insert": (_I32, [_P, _I64, _P, _I32, C.POINTER(_I32)]),
@@ -420,6 +423,23 @@ def paged_attention_decode(pool, layer, q, out, block_tables, context_lens, num_
                                         _dev(context_lens), n_seqs, max_blocks, int(num_q_heads),
                                         C.byref(opts) if opts is not None else None, _dev(workspace),
                                         ws_bytes, _stream(stream)))
+
+
+def paged_attention_static_scratch_bytes():
+    return int(lib().paged_attention_static_scratch_bytes())
+
+
+def paged_attention_decode_static(pool, layer, q, out, block_tables, context_lens, num_q_heads, opts=None,
+                                  stream=None):
+    """paged_attention_decode with the library's static device scratch instead of a
+    workspace: allocates nothing (arguments as for paged_attention_decode)."""
+    _tables(block_tables, context_lens)
+    n_seqs, max_blocks = int(block_tables.shape[0]), int(block_tables.shape[1])
+    _rows(pool, q, "q", n_seqs, num_q_heads)
+    _rows(pool, out, "out", n_seqs, num_q_heads)
+    _check(lib().paged_attention_decode_static(pool, int(layer), _dev(q), _dev(out), _dev(block_tables),
+                                               _dev(context_lens), n_seqs, max_blocks, int(num_q_heads),
+                                               C.byref(opts) if opts is not None else None, _stream(stream)))
 
 
 def paged_prefill_workspace_bytes(pool, n_seqs, total_q, max_q_len, num_q_heads, max_blocks_per_seq, opts=None):

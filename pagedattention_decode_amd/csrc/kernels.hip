@@ -26,6 +26,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -1701,7 +1702,48 @@ kv_status prefill_rowwise(kv_pool* pool, int layer, const void* q, void* out, co
 
 using namespace pagedkv;
 
+// ---- allocation-free decode -------------------------------------------------
+// Scratch of paged_attention_decode_static: what paged_attention_decode takes as
+// its caller's workspace (the split-K partials m, l, O of the runs that end
+// inside a (sequence, kv head) unit, and the partition prefix), in one static
+// device array that every GPU holds, at its own address, until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// stands for a host-side shadow, not device memory): the device address is
+// looked up once per device with hipGetSymbolAddress and kept per device.
+// Nothing in it needs to start at zero -- every partial a merge reads was
+// written by the same call -- so it is never cleared.
+static constexpr uint64_t kDecodeScratchBytes = 32ull << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device).
+kv_status decode_scratch(void** out) {
+  int dev = -1;
+  if (kv_status s = hip_check(hipGetDevice(&dev), "hipGetDevice")) return s;
+  if (dev < 0 || dev >= kScratchDevices) return fail(KV_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (kv_status s = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))
+      return s;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255)) return fail(KV_ERR_HIP, "scratch address is not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KV_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+uint64_t paged_attention_static_scratch_bytes(void) { return kDecodeScratchBytes; }
 
 kv_status reshape_and_cache(kv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
                             const int64_t* d_slot_mapping, int32_t n_tokens, void* hip_stream) {
@@ -1808,6 +1850,25 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     return fail(KV_ERR_INVALID, "workspace must be 256-byte aligned");
   return decode_launch(pool, layer, q, out, d_block_tables, d_context_lens, nullptr, n_seqs, max_blocks_per_seq,
                        num_q_heads, r, d_workspace, static_cast<hipStream_t>(hip_stream), events_of(opts));
+}
+
+kv_status paged_attention_decode_static(kv_pool* pool, int32_t layer, const void* q, void* out,
+                                        const int32_t* d_block_tables, const int32_t* d_context_lens, int32_t n_seqs,
+                                        int32_t max_blocks_per_seq, int32_t num_q_heads,
+                                        const kv_attention_options* opts, void* hip_stream) {
+  if (!pool) return fail(KV_ERR_INVALID, "pool is NULL");
+  resolved r;
+  if (kv_status s = resolve(pool, n_seqs, num_q_heads, max_blocks_per_seq, opts, r)) return s;
+  const uint64_t need = workspace_for(pool->cfg, n_seqs, num_q_heads, r);
+  if (need > kDecodeScratchBytes)
+    return fail(KV_ERR_INVALID, "the call needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                                    std::to_string(kDecodeScratchBytes) +
+                                    " of the static scratch; use paged_attention_decode with a workspace");
+  void* ws = nullptr;
+  if (need > 0)
+    if (kv_status s = decode_scratch(&ws)) return s;
+  return paged_attention_decode(pool, layer, q, out, d_block_tables, d_context_lens, n_seqs, max_blocks_per_seq,
+                                num_q_heads, opts, ws, need > 0 ? kDecodeScratchBytes : 0, hip_stream);
 }
 
 // ---- cascade decode over shared prefixes ---------------------------------

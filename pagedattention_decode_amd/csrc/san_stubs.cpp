@@ -38,6 +38,13 @@ kv_status paged_attention_decode(kv_pool*, int32_t, const void*, void*, const in
   return no_device();
 }
 
+uint64_t paged_attention_static_scratch_bytes(void) { return 0; }
+
+kv_status paged_attention_decode_static(kv_pool*, int32_t, const void*, void*, const int32_t*, const int32_t*,
+                                        int32_t, int32_t, int32_t, const kv_attention_options*, void*) {
+  return no_device();
+}
+
 uint64_t paged_attention_cascade_workspace_bytes(kv_pool*, int32_t, int32_t, int32_t, int32_t, int32_t,
                                                  const kv_attention_options*) {
   return 0;

@@ -93,6 +93,10 @@ class PagedKVPool:
         B.paged_attention_decode(self.handle, layer, q, out, block_tables, context_lens, num_q_heads, opts,
                                  workspace, stream)
 
+    def decode_static(self, layer, q, out, block_tables, context_lens, num_q_heads, opts=None, stream=None):
+        B.paged_attention_decode_static(self.handle, layer, q, out, block_tables, context_lens, num_q_heads, opts,
+                                        stream)
+
     def prefill_workspace_bytes(self, n_seqs, total_q, max_q_len, num_q_heads, max_blocks, opts=None):
         return B.paged_prefill_workspace_bytes(self.handle, n_seqs, total_q, max_q_len, num_q_heads, max_blocks, opts)
 
