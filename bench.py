@@ -122,6 +122,9 @@ def parse():
     ap.add_argument("--kv", default="bf16", choices=["bf16", "q8_0", "q4_0"],
                     help="storage of the KV pool for --op decode: bf16, or q8_0 / q4_0 codes with one 2-byte "
                          "scale per 32 values (written by reshape_and_cache, dequantised in the kernel)")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="--op decode: tokens per block of the pool (0 = the workload's, 16); bf16 pools of block "
+                         "size 4, 8, 32 and 64 are read by the matrix-core kernel too")
     ap.add_argument("--swap-seqs", type=int, default=8, help="--op swap: sequences swapped out and back in per step")
     ap.add_argument("--op", default="decode", choices=["decode", "prefill", "verify", "swap"],
                     help="decode: the decode step of --workload; prefill: the last 512-token chunk of 16 "
@@ -205,6 +208,12 @@ def main():
 
     fork = args.workload == "agentic_fork_64x33281"
     base = workloads.agentic_fork(steps=1) if fork else workloads.get_workload(args.workload)
+    if args.block_size and args.block_size != base.block_size:
+        from dataclasses import replace
+        # the same tokens in blocks of another size (plus one partly filled block per sequence)
+        n_dec = len(next(op for op in base.ops if op[0] == "decode")[1])
+        base = replace(base, block_size=args.block_size,
+                       num_blocks=-(-base.num_blocks * base.block_size // args.block_size) + n_dec)
     L = args.layers or DECODE_LAYERS[args.workload]
     seed = args.seed or base.seed
     partition = base.partition_tokens if args.partition < 0 else args.partition
@@ -407,7 +416,8 @@ def main():
     value = logical_bytes[0] / wall / 1e9
     tok_per_s_layer = S * L * args.steps / wall
 
-    traffic_key = (base.name + ("" if args.kv == "bf16" else f"_{args.kv}") + ("_cascade" if args.cascade else ""),
+    traffic_key = (base.name + ("" if args.kv == "bf16" else f"_{args.kv}") + ("_cascade" if args.cascade else "") +
+                   ("" if Bs == 16 else f"_b{Bs}"),
                    CASCADE_SOURCES if args.cascade else DECODE_SOURCES,
                    "traffic_bytes_per_call" if args.cascade else "traffic_bytes_per_launch")
     result = {
@@ -432,6 +442,7 @@ def main():
             "partition_tokens": partition or "auto",
             "kernel": args.kernel,
             "kv_storage": args.kv,
+            "block_size": Bs,
             "kv_bytes_per_token_per_layer": kv_tok,
             "pool_blocks": num_blocks,
             "step": (f"append + {L} x (reshape_and_cache + {attn_name})" if step_appends

@@ -380,11 +380,15 @@ kv_status copy_blocks(kv_pool* pool, const int64_t* d_pairs, int32_t n_pairs, vo
 typedef enum {
   KV_KERNEL_AUTO = 0,    /* the matrix-core kernel where it applies, else generic */
   KV_KERNEL_GENERIC = 1, /* vector-ALU kernel: f32 or bf16, any B, d; G <= 16 */
-  KV_KERNEL_MFMA = 2     /* bf16, q8_0 or q4_0, B = 16, d in {64, 128, 256},
-                            G <= 16, at most 4095 sequences per call; the only
-                            kernel for quantised pools (the codes, exact in bf16,
-                            are the matrix operands and the group scales are
-                            applied in float32: the result is the attention over
+  KV_KERNEL_MFMA = 2     /* bf16 with B in {4, 8, 16, 32, 64}, or q8_0 / q4_0
+                            with B = 16; d in {64, 128, 256}, G <= 16, at most
+                            4095 sequences per call.  It works in 16-token
+                            tiles: B/16 tiles per table entry for B > 16, 16/B
+                            entries per tile for B < 16 (entries past a
+                            context are never read).  The only kernel for
+                            quantised pools (the codes, exact in bf16, are the
+                            matrix operands and the group scales are applied in
+                            float32: the result is the attention over
                             code x scale) */
 } kv_kernel;
 
@@ -416,7 +420,8 @@ typedef struct {
   float scale;              /* softmax scale; 0 means 1/sqrt(d) ([BT] §07) */
   int32_t partition_tokens; /* split-K partition length in tokens, a positive
                                multiple of B; 0 = the library's choice (one
-                               block for the matrix-core kernel) */
+                               16-token tile for the matrix-core kernel, which
+                               rounds a requested length up to whole tiles) */
   int32_t kernel;           /* kv_kernel */
   const kv_timing_events* timing; /* NULL: no timing */
 } kv_attention_options;
@@ -540,9 +545,10 @@ uint64_t paged_prefill_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int3
  *     block once for all its rows;
  *   row-wise: every other pool, and any pool with KV_KERNEL_GENERIC -- each
  *     chunk row is a decode query over its n - c + j + 1 keys, through the
- *     decode kernels (the matrix-core split-K kernel for quantised pools,
- *     batches of at most 4095 rows; the generic kernel for f32 and bf16), so
- *     the history is read once per row.  Rows no sequence owns are written
+ *     decode kernels (the matrix-core split-K kernel, in batches of at most
+ *     4095 rows, for quantised pools and bf16 pools of block size 4, 8, 32 or
+ *     64; the generic kernel for f32 pools and other block sizes), so the
+ *     history is read once per row.  Rows no sequence owns are written
  *     as zero rows.  KV_KERNEL_MFMA on a pool no matrix-core kernel reads
  *     gives KV_ERR_UNSUPPORTED.
  * opts->partition_tokens splits every tile's (row's) keys into partitions

@@ -60,6 +60,16 @@ __device__ __forceinline__ void load_block(kv_regs<D>& r, const uint4* kt, const
   for (int i = 0; i < D / 32; ++i) r.v[i] = vt[i * 64 + lane];
 }
 
+// The same for any block size: the lane's first K and V pieces at k and v, its
+// i-th piece STRIDE pieces further (load_block is STRIDE = 64, k = kt + lane).
+template <int D, int STRIDE>
+__device__ __forceinline__ void load_block_strided(kv_regs<D>& r, const uint4* k, const uint4* v) {
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) r.k[i] = k[i * STRIDE];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) r.v[i] = v[i * STRIDE];
+}
+
 // The running maximum m is only moved when a block's maximum exceeds it by more
 // than this many binary orders of magnitude; otherwise the block is weighted
 // against the stale m (weights up to 2^kRescaleSlack).  Numerator and

@@ -628,6 +628,7 @@ struct sk_args {
   float* part_o;   // [slots][G][D]
   int32_t* cum_parts;  // [n_seqs + 1] partitions before each sequence (written by group 0)
   int n_seqs, max_blocks, n_q_heads, n_kv_heads, num_blocks, part_blocks, n_waves;
+  int block_size;  // B: tokens per table entry (the kernel works in 16-token tiles)
   int q_units;  // units per wave whose queries are staged in LDS (<= kSkQUnits)
   float scale_log2;
   int force_partial;  // every unit ends in partials (the cascade merge folds them with a prefix)
@@ -648,7 +649,7 @@ __device__ __forceinline__ void sk_prefix(const sk_args& a, const int32_t* __res
                                           int* cum_p, int* ctx_n) {
   __shared__ int wsum_b[kSkWaves], wsum_p[kSkWaves];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int cap = a.max_blocks * 16;
+  const int cap = a.max_blocks * a.block_size;
   int carry_b = 0, carry_p = 0;
   for (int base = 0; base < a.n_seqs; base += kSkWaves * 64) {
     const int s = base + tid;
@@ -698,9 +699,18 @@ struct sk_cursor {
   int seq, kvh, j, nb, n, trow;  // trow: the table row of seq
 };
 
-template <int D, int STAGES, int WAVES_PER_SIMD, int FMT>
+// BS is the pool's block size B.  The kernel walks 16-token tiles: for B >= 16
+// a table entry holds B/16 tiles (tile j is sub-tile j % (B/16) of entry
+// j / (B/16)); for B < 16 a tile gathers 16/B consecutive entries, each lane
+// reading its pieces from the entry that holds its keys (K) or its 4 value
+// slots (V).  In every case a lane's 16-byte pieces of one tile are exactly its
+// matrix operands (the tile layout of the pool puts, for B >= 16, each
+// quarter-wave's 16 pieces in one 256-byte run).
+template <int D, int STAGES, int WAVES_PER_SIMD, int FMT, int BS>
 __global__ void __launch_bounds__(kSkWaves * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD)))
 attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ tables) {
+  static_assert(FMT == kFmtBf16 || BS == 16, "quantised tiles are 16 tokens");
+  static_assert(BS == 4 || BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size");
   extern __shared__ __align__(16) int sk_smem[];
   int* cum_b = sk_smem;                       // n_seqs + 1
   int* cum_p = sk_smem + a.n_seqs + 1;        // n_seqs + 1
@@ -778,24 +788,62 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
   using ring_t = typename std::conditional<FMT == kFmtBf16, kv_regs<D>, kv_qregs<D, FMT>>::type;
   const uint4* kpool = static_cast<const uint4*>(a.k_layer);
   const uint4* vpool = static_cast<const uint4*>(a.v_layer);
-  constexpr int kTileVec = 16 * D * 2 / 16;  // 16-byte vectors per tile
 
-  // load side: the block STAGES ahead of consumption (the last one repeats
+  // load side: the tile STAGES ahead of consumption (the last one repeats
   // past the end of the run and is served by the L2)
   sk_cursor ld = first;
   int ld_k = 0;
-  int phys_ring[STAGES];
+  bool bad_ring[STAGES];  // a table entry the tile needs lies outside [0, N)
+  // Lane offsets, in 16-byte pieces inside a (block, kv head) tile of BS * D
+  // elements, of the lane's first K and V piece; its i-th piece is 4 BS pieces
+  // further.  With r = lane % 16, a lane holds key r and, for V, value slots
+  // 4 quad .. 4 quad + 3 of the 16-token tile.
+  constexpr int64_t kEntryVec = static_cast<int64_t>(BS) * D * 2 / 16;
+  const int k_lane = quad * BS + (BS >= 16 ? (lane & 15) : (lane & 15) % BS);
+  const int v_lane = BS >= 16 ? lane : ((quad * 4) % BS / 4) * 16 + (lane & 15);
   auto issue = [&](ring_t& buf, int u) {
-    const int phys = ld.trow >= 0 ? tables[static_cast<int64_t>(ld.trow) * a.max_blocks + ld.j] : -1;
-    phys_ring[u] = phys;
-    const int p = (phys < 0 || phys >= a.num_blocks) ? 0 : phys;  // never dereferenced out of range
-    if constexpr (FMT == kFmtBf16) {
-      const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * kTileVec;
-      load_block<D>(buf, kpool + t, vpool + t, lane);
-    } else {
+    const int64_t row = static_cast<int64_t>(ld.trow) * a.max_blocks;
+    if constexpr (FMT != kFmtBf16) {
+      const int phys = ld.trow >= 0 ? tables[row + ld.j] : -1;
+      const bool bad = phys < 0 || phys >= a.num_blocks;
+      bad_ring[u] = bad;
+      const int p = bad ? 0 : phys;  // never dereferenced out of range
       const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * q_tile_bytes<D, FMT>();
       load_qblock<D, FMT>(buf, static_cast<const unsigned char*>(a.k_layer) + t,
                           static_cast<const unsigned char*>(a.v_layer) + t, lane);
+    } else if constexpr (BS >= 16) {
+      // tile j is sub-tile j % (BS/16) of entry j / (BS/16)
+      constexpr int kSub = BS / 16;
+      const int phys = ld.trow >= 0 ? tables[row + ld.j / kSub] : -1;
+      const bool bad = phys < 0 || phys >= a.num_blocks;
+      bad_ring[u] = bad;
+      const int p = bad ? 0 : phys;
+      const int sub = ld.j % kSub;
+      const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * kEntryVec;
+      load_block_strided<D, 4 * BS>(buf, kpool + t + sub * 16 + k_lane, vpool + t + sub * 64 + v_lane);
+    } else {
+      // tile j gathers entries j * (16/BS) + e; only those holding tokens of
+      // the context are read (the others may lie past the table's row)
+      constexpr int kPer = 16 / BS;
+      int phys[kPer];
+      bool bad = false;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const bool needed = ld.j * 16 + e * BS < ld.n;
+        const int ph = !needed ? 0 : (ld.trow >= 0 ? tables[row + ld.j * kPer + e] : -1);
+        const bool b = ph < 0 || ph >= a.num_blocks;
+        bad |= b;
+        phys[e] = b ? 0 : ph;
+      }
+      bad_ring[u] = bad;
+      int pk = phys[0], pv = phys[0];
+#pragma unroll
+      for (int e = 1; e < kPer; ++e) {
+        pk = (lane & 15) / BS == e ? phys[e] : pk;
+        pv = quad * 4 / BS == e ? phys[e] : pv;
+      }
+      load_block_strided<D, 4 * BS>(buf, kpool + (static_cast<int64_t>(pk) * Hkv + ld.kvh) * kEntryVec + k_lane,
+                                    vpool + (static_cast<int64_t>(pv) * Hkv + ld.kvh) * kEntryVec + v_lane);
     }
     if (++ld_k < n_blk) advance(ld);
   };
@@ -899,8 +947,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     for (int u = 0; u < STAGES; ++u) {
       const int k = k0 + u;
       if (k < n_blk) {
-        const int phys = phys_ring[u];
-        const bool bad = phys < 0 || phys >= a.num_blocks;
+        const bool bad = bad_ring[u];
         poisoned |= bad;
         const int valid = bad ? 0 : min(16, cs.n - cs.j * 16);
         if constexpr (FMT == kFmtBf16) {
@@ -1366,6 +1413,14 @@ bool mfma_supported(const kv_pool_config& c, int G) {
          (c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256) && G >= 1 && G <= kMaxGroup;
 }
 
+// The split-K decode kernel also reads bf16 pools of block size 4, 8, 32, 64.
+bool decode_mfma_supported(const kv_pool_config& c, int G) {
+  if (mfma_supported(c, G)) return true;
+  const int b = c.block_size;
+  return c.dtype == KV_BF16 && (b == 4 || b == 8 || b == 32 || b == 64) &&
+         (c.head_dim == 64 || c.head_dim == 128 || c.head_dim == 256) && G >= 1 && G <= kMaxGroup;
+}
+
 int device_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -1461,11 +1516,11 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
   if (opts) o = *opts;
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_GENERIC && o.kernel != KV_KERNEL_MFMA)
     return fail(KV_ERR_INVALID, "unknown kernel selector");
-  const bool mfma_ok = mfma_supported(c, G) && n_seqs <= kSkMaxSeqs && sk_q_units(n_seqs, G, c.head_dim) >= 1;
+  const bool mfma_ok = decode_mfma_supported(c, G) && n_seqs <= kSkMaxSeqs && sk_q_units(n_seqs, G, c.head_dim) >= 1;
   if (o.kernel == KV_KERNEL_MFMA && !mfma_ok)
     return fail(KV_ERR_UNSUPPORTED,
-                "the matrix-core kernel needs bf16 or q8_0/q4_0, B = 16, d in {64, 128, 256} and at most 4095 "
-                "sequences");
+                "the matrix-core kernel needs bf16 with B in {4, 8, 16, 32, 64} or q8_0/q4_0 with B = 16, d in "
+                "{64, 128, 256} and at most 4095 sequences");
   if (is_quantized(c.dtype) && (o.kernel == KV_KERNEL_GENERIC || !mfma_ok))
     return fail(KV_ERR_UNSUPPORTED, "a quantised pool is read by the matrix-core kernel only (at most 4095 "
                                     "sequences, G <= 16)");
@@ -1476,8 +1531,9 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
   r.scale = o.scale > 0.f ? o.scale : 1.f / std::sqrt(static_cast<float>(c.head_dim));
   const int64_t max_ctx = static_cast<int64_t>(max_blocks) * c.block_size;
   if (r.kernel == KV_KERNEL_MFMA) {
-    // default: one block per partition, the finest split (exact balance)
-    r.partition = o.partition_tokens ? o.partition_tokens : c.block_size;
+    // default: one 16-token tile per partition, the finest split (exact
+    // balance); a requested length is rounded up to whole tiles
+    r.partition = o.partition_tokens ? (o.partition_tokens + 15) / 16 * 16 : 16;
     r.max_parts = static_cast<int>((max_ctx + r.partition - 1) / r.partition);
     const int64_t parts_ub = static_cast<int64_t>(n_seqs) * c.num_kv_heads * r.max_parts;
     r.groups = std::max<int64_t>(
@@ -1504,12 +1560,12 @@ uint64_t workspace_for(const kv_pool_config& c, int n_seqs, int num_q_heads, con
   return up256(rows * 4) * 2 + up256(rows * c.head_dim * 4);
 }
 
-template <int D, int FMT>
+template <int D, int FMT, int BS = 16>
 hipError_t launch_mfma(const sk_args& a, const int32_t* ctx_lens, const int32_t* tables, int64_t groups, int G,
                        hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
   constexpr int kStages = sk_stages<D, FMT>();
   constexpr int kWps = sk_waves_per_simd(D, FMT);
-  return launch_timed(attn_mfma_kernel<D, kStages, kWps, FMT>, dim3(static_cast<unsigned>(groups)),
+  return launch_timed(attn_mfma_kernel<D, kStages, kWps, FMT, BS>, dim3(static_cast<unsigned>(groups)),
                       dim3(kSkWaves * 64), static_cast<uint32_t>(sk_lds_bytes(a.n_seqs, G, D)), st, ev0, ev1, a,
                       ctx_lens, tables);
 }
@@ -1549,22 +1605,34 @@ kv_status decode_launch(const kv_pool* pool, int layer, const void* q, void* out
     a.n_q_heads = num_q_heads;
     a.n_kv_heads = c.num_kv_heads;
     a.num_blocks = c.num_blocks;
-    a.part_blocks = r.partition / c.block_size;
+    a.part_blocks = r.partition / 16;  // partitions are whole 16-token tiles
+    a.block_size = c.block_size;
     a.table_rows = table_rows;
     a.n_waves = static_cast<int>(r.groups * kSkWaves);
     a.q_units = sk_q_units(n_seqs, G, c.head_dim);
     a.scale_log2 = r.scale * kLog2e;
-    auto launch = [&](auto fmt) {
+    auto launch = [&](auto fmt, auto bs) {
       constexpr int F = decltype(fmt)::value;
+      constexpr int BS = decltype(bs)::value;
       switch (c.head_dim) {
-        case 64: return launch_mfma<64, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
-        case 128: return launch_mfma<128, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
-        default: return launch_mfma<256, F>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
+        case 64: return launch_mfma<64, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
+        case 128: return launch_mfma<128, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
+        default: return launch_mfma<256, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
       }
     };
-    if (c.dtype == KV_Q8_0) e = launch(std::integral_constant<int, kFmtQ8>{});
-    else if (c.dtype == KV_Q4_0) e = launch(std::integral_constant<int, kFmtQ4>{});
-    else e = launch(std::integral_constant<int, kFmtBf16>{});
+    using B16 = std::integral_constant<int, 16>;
+    if (c.dtype == KV_Q8_0) e = launch(std::integral_constant<int, kFmtQ8>{}, B16{});
+    else if (c.dtype == KV_Q4_0) e = launch(std::integral_constant<int, kFmtQ4>{}, B16{});
+    else {
+      using BF = std::integral_constant<int, kFmtBf16>;
+      switch (c.block_size) {
+        case 4: e = launch(BF{}, std::integral_constant<int, 4>{}); break;
+        case 8: e = launch(BF{}, std::integral_constant<int, 8>{}); break;
+        case 32: e = launch(BF{}, std::integral_constant<int, 32>{}); break;
+        case 64: e = launch(BF{}, std::integral_constant<int, 64>{}); break;
+        default: e = launch(BF{}, B16{}); break;
+      }
+    }
     if (kv_status s = hip_check(e, "paged_attention_decode launch")) return s;
     const unsigned mgrid =
         static_cast<unsigned>((static_cast<int64_t>(n_seqs) * num_q_heads + kMergeItems - 1) / kMergeItems);
@@ -1883,8 +1951,8 @@ struct cascade_layout {
 kv_status cascade_plan(kv_pool* pool, int n_seqs, int n_groups, int max_group, int num_q_heads, int max_blocks,
                        const kv_attention_options* opts, resolved& r, cascade_layout& L) {
   if (kv_status s = resolve(pool, n_seqs, num_q_heads, max_blocks, opts, r)) return s;
-  if (r.kernel != KV_KERNEL_MFMA || pool->cfg.dtype != KV_BF16)
-    return fail(KV_ERR_UNSUPPORTED, "the cascade decode needs a bf16 pool and the matrix-core kernel");
+  if (r.kernel != KV_KERNEL_MFMA || pool->cfg.dtype != KV_BF16 || pool->cfg.block_size != 16)
+    return fail(KV_ERR_UNSUPPORTED, "the cascade decode needs a bf16 pool with B = 16 and the matrix-core kernel");
   if (n_groups < 1 || n_groups > n_seqs || max_group < 1)
     return fail(KV_ERR_INVALID, "need 1 <= n_groups <= n_seqs and max_group >= 1");
   uint64_t pre_bytes = 0;
@@ -1971,7 +2039,8 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   a.n_q_heads = num_q_heads;
   a.n_kv_heads = c.num_kv_heads;
   a.num_blocks = c.num_blocks;
-  a.part_blocks = r.partition / c.block_size;
+  a.part_blocks = r.partition / 16;
+  a.block_size = 16;  // the cascade reads B = 16 pools (cascade_plan)
   a.n_waves = static_cast<int>(r.groups * kSkWaves);
   a.q_units = sk_q_units(n_seqs, G, c.head_dim);
   a.scale_log2 = r.scale * kLog2e;
