@@ -402,8 +402,8 @@ typedef enum {
  *                partition kernel of paged_attention_decode and the
  *                multi-query kernel of paged_attention_prefill (both the
  *                call's first kernel, so start .. kernel_stop is that kernel
- *                alone), the prefix-phase kernel of the cascade (start ..
- *                kernel_stop then also spans the preparation kernel), the
+ *                alone), the fused prefix-and-suffix kernel of the cascade
+ *                (also its first kernel), the
  *                last decode kernel of the row-wise prefill path (after its
  *                row-length kernel and any earlier batches);
  *   stop         end of the call's last kernel.
@@ -484,11 +484,12 @@ kv_status paged_attention_decode_static(kv_pool* pool, int32_t layer, const void
  * at least 16 * shared_blocks[g] tokens) — forks of one request share such
  * blocks physically ([KVM] CoW branching, cross-turn prefix caching).  The
  * result equals paged_attention_decode; the shared blocks are read once per
- * group instead of once per member:
- *   prefix: the multi-query kernel over the shared blocks, the members'
- *           queries as its columns, no causal mask;
- *   suffix: the split-K decode over each member's remaining blocks;
- *   merge:  both kinds of partials folded with the [KVM] recurrences.
+ * group instead of once per member.  One persistent kernel streams a single
+ * work list of prefix units (a group's shared blocks against the queries of
+ * up to 64 query columns: members x their G heads) and suffix units (a
+ * member's remaining blocks against its G heads), cut into per-wave runs by
+ * estimated cost; a second kernel folds each member's prefix and suffix
+ * partials with the [KVM] recurrences.
  * A member whose shared entries differ from the first member's, or whose
  * context (or the first member's) does not cover them, gets a NaN row (checked
  * on the device); so do the members of a group larger than max_group.  bf16 pools with the

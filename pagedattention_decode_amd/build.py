@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["pool.cpp", "prefix_cache.cpp", "kernels.hip", "prefill.hip", "swap.hip"]
+SOURCES = ["pool.cpp", "prefix_cache.cpp", "kernels.hip", "cascade.hip", "prefill.hip", "swap.hip"]
 ARCH = "gfx950"
 
 

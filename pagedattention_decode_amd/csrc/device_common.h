@@ -36,6 +36,28 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Maximum and sum of x over lanes l and l ^ 16, and over l and l ^ 32, without
+// the LDS pipe: v_permlane16_swap exchanges the odd 16-lane rows of its first
+// operand with the even rows of its second, v_permlane32_swap the upper half
+// of its first operand with the lower half of its second, so with x in both
+// every lane ends up holding x[l] and its partner's value.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -93,6 +115,82 @@ __device__ __forceinline__ void zero_v_tail(kv_regs<D>& cur, int valid, int quad
       if (slot0 + 1 < valid) mask |= 0xffff0000u;
       wv[dw] &= mask;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core decode step over one 16-token tile, shared by the split-K decode
+// and the read-once cascade kernels.  A wave computes, for 16 query columns,
+//   S^T[16 tokens][16 columns] = K[16][D] . Q^T[D][16]   (D/32 x mfma 16x16x32)
+//   online softmax on S^T (each lane holds 4 tokens of one column)
+//   O^T[D][16 columns] += V^T[D][16] . P^T[16][16]        (D/16 x mfma 16x16x16)
+// The P^T operand is exactly the S^T result layout, so no data moves between
+// lanes except the two shuffles of the per-column block maximum.
+// ---------------------------------------------------------------------------
+
+// One 16-token block: scores, online-softmax update, weighted sum of values.
+// `valid` (wave uniform) is the number of in-range slots of the block.
+// Online-softmax step on the 4 scores s of the lane's tokens quad*4 + i:
+// masks the slots past `valid`, raises the running maximum when a score
+// exceeds it by more than the slack (rescaling l and O), and returns the
+// weights 2^(s * scale_log2 - m_run) (0 for masked slots).
+template <int D>
+__device__ __forceinline__ void softmax_step(const f32x4_t& s, int valid, int quad, float scale_log2, f32x4_t* o,
+                                             float& m_run, float& l_lane, float (&pv)[4]) {
+  float sv[4];
+  float mb = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = (quad * 4 + i < valid) ? s[i] * scale_log2 : -INFINITY;
+    mb = fmaxf(mb, sv[i]);
+  }
+  mb = fmaxf(mb, __shfl_xor(mb, 16));
+  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  const bool grow = mb > m_run + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch
+    const float m_new = grow ? mb : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf, 1 when kept
+    l_lane *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
+    m_run = m_new;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pv[i] = (sv[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_run);
+}
+
+template <int D>
+__device__ __forceinline__ void attend_block(kv_regs<D>& cur, const bf16x8_t* qop, int valid, int quad,
+                                             float scale_log2, f32x4_t* o, float& m_run, float& l_lane) {
+  // S^T = K . Q^T
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk], s, 0, 0, 0);
+
+  float pv[4];
+  softmax_step<D>(s, valid, quad, scale_log2, o, m_run, l_lane, pv);
+  // P^T operand in bf16 (round to nearest even); the denominator sums the
+  // rounded weights so that the weights applied to V are exactly normalised
+  const bf16x2_t p01 = __builtin_convertvector((f32x2_t{pv[0], pv[1]}), bf16x2_t);
+  const bf16x2_t p23 = __builtin_convertvector((f32x2_t{pv[2], pv[3]}), bf16x2_t);
+  const uint32_t w01 = __builtin_bit_cast(uint32_t, p01);
+  const uint32_t w23 = __builtin_bit_cast(uint32_t, p23);
+  l_lane += (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xffff0000u)) +
+            (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xffff0000u));
+  const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(w01, w23));
+
+  // zero the values of out-of-range slots (their memory may hold anything)
+  if (valid < 16) zero_v_tail<D>(cur, valid, quad);
+
+  // O^T += V^T . P^T
+#pragma unroll
+  for (int pp = 0; pp < D / 32; ++pp) {
+    const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
+    o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop, o[2 * pp],
+                                                          0, 0, 0);
+    o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[1]), pop,
+                                                              o[2 * pp + 1], 0, 0, 0);
   }
 }
 

@@ -448,83 +448,12 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core decode attention: bf16, B = 16, d = D, G <= 16.  A workgroup of W
-// waves handles one (sequence, kv head, partition); wave w takes the
-// partition's blocks w, w + W, ...  Per 16-token block and wave:
-//   S^T[16 tokens][16 heads] = K[16][D] . Q^T[D][16]   (D/32 x mfma 16x16x32)
-//   online softmax on S^T (each lane holds 4 tokens of one head)
-//   O^T[D][16 heads] += V^T[D][16] . P^T[16][16]        (D/16 x mfma 16x16x16)
-// Query heads beyond G are zero rows; their results are discarded.  The P^T
-// operand is exactly the S^T result layout, so no data moves between lanes
-// except the two shuffles of the per-head block maximum.
+// Matrix-core decode attention: bf16 (any B of 4 .. 64) or quantised (B = 16),
+// d = D, G <= 16 query heads as the 16 columns of one tile; heads beyond G are
+// zero columns whose results are discarded.  The per-tile step (attend_block)
+// is in device_common.h; the quantised variant follows.
 // ---------------------------------------------------------------------------
 
-
-// One 16-token block: scores, online-softmax update, weighted sum of values.
-// `valid` (wave uniform) is the number of in-range slots of the block.
-// Online-softmax step on the 4 scores s of the lane's tokens quad*4 + i:
-// masks the slots past `valid`, raises the running maximum when a score
-// exceeds it by more than the slack (rescaling l and O), and returns the
-// weights 2^(s * scale_log2 - m_run) (0 for masked slots).
-template <int D>
-__device__ __forceinline__ void softmax_step(const f32x4_t& s, int valid, int quad, float scale_log2, f32x4_t* o,
-                                             float& m_run, float& l_lane, float (&pv)[4]) {
-  float sv[4];
-  float mb = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sv[i] = (quad * 4 + i < valid) ? s[i] * scale_log2 : -INFINITY;
-    mb = fmaxf(mb, sv[i]);
-  }
-  mb = fmaxf(mb, __shfl_xor(mb, 16));
-  mb = fmaxf(mb, __shfl_xor(mb, 32));
-  const bool grow = mb > m_run + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch
-    const float m_new = grow ? mb : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf, 1 when kept
-    l_lane *= alpha;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
-    m_run = m_new;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pv[i] = (sv[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_run);
-}
-
-template <int D>
-__device__ __forceinline__ void attend_block(kv_regs<D>& cur, const bf16x8_t* qop, int valid, int quad,
-                                             float scale_log2, f32x4_t* o, float& m_run, float& l_lane) {
-  // S^T = K . Q^T
-  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk], s, 0, 0, 0);
-
-  float pv[4];
-  softmax_step<D>(s, valid, quad, scale_log2, o, m_run, l_lane, pv);
-  // P^T operand in bf16 (round to nearest even); the denominator sums the
-  // rounded weights so that the weights applied to V are exactly normalised
-  const bf16x2_t p01 = __builtin_convertvector((f32x2_t{pv[0], pv[1]}), bf16x2_t);
-  const bf16x2_t p23 = __builtin_convertvector((f32x2_t{pv[2], pv[3]}), bf16x2_t);
-  const uint32_t w01 = __builtin_bit_cast(uint32_t, p01);
-  const uint32_t w23 = __builtin_bit_cast(uint32_t, p23);
-  l_lane += (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xffff0000u)) +
-            (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xffff0000u));
-  const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(w01, w23));
-
-  // zero the values of out-of-range slots (their memory may hold anything)
-  if (valid < 16) zero_v_tail<D>(cur, valid, quad);
-
-  // O^T += V^T . P^T
-#pragma unroll
-  for (int pp = 0; pp < D / 32; ++pp) {
-    const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
-    o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop, o[2 * pp],
-                                                          0, 0, 0);
-    o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[1]), pop,
-                                                              o[2 * pp + 1], 0, 0, 0);
-  }
-}
 
 // The same step on a quantised block, with the codes (exact in bf16) as the
 // operands and the group scales applied in float32:
@@ -631,7 +560,6 @@ struct sk_args {
   int block_size;  // B: tokens per table entry (the kernel works in 16-token tiles)
   int q_units;  // units per wave whose queries are staged in LDS (<= kSkQUnits)
   float scale_log2;
-  int force_partial;  // every unit ends in partials (the cascade merge folds them with a prefix)
   // row of the tables that sequence s reads (NULL: row s); a negative row has
   // no valid entry (the sequence's output is NaN)
   const int32_t* table_rows;
@@ -909,7 +837,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     l += __shfl_xor(l, 32);
     const int h = cs.kvh * G + hg;
     const float nan = __builtin_nanf("");
-    if (seg_j0 == 0 && cs.j == cs.nb - 1 && !a.force_partial) {  // the whole unit: final row
+    if (seg_j0 == 0 && cs.j == cs.nb - 1) {  // the whole unit: final row
       const float inv = poisoned ? 0.f : 1.f / l;
       uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(cs.seq) * a.n_q_heads + h) * D;
 #pragma unroll
@@ -1100,221 +1028,6 @@ __global__ void __launch_bounds__(kMergeItems * 64) merge_sk_kernel(sk_args a) {
   const float inv = 1.f / L;
 #pragma unroll
   for (int j = 0; j < E; ++j) out[j] = nan ? static_cast<uint16_t>(0x7fc0) : f32_to_bf16(acc[j] * inv);
-}
-
-// ---------------------------------------------------------------------------
-// Cascade decode over shared prefixes (read once per group).  Sequences come
-// in groups [group_start[g], group_start[g+1]) whose tables agree on their first
-// shared[g] blocks (forks of one request; the [KVM] CoW branching and prefix
-// caching make such blocks physically shared).  The decode of a member splits
-// into two key ranges merged with the running-max recurrences of [KVM]
-// (chunked prefill mechanism):
-//   prefix: the shared blocks, read once for all members by the multi-query
-//           kernel with the members' queries as columns (no causal mask);
-//   suffix: the member's own blocks, by the split-K decode kernel on a
-//           shifted table (every unit ends in partials);
-// cascade_merge folds both kinds of partials into the output row.
-// ---------------------------------------------------------------------------
-
-// One workgroup per sequence: finds the member's group (one pass over
-// group_start by the workgroup's threads, not a chain of dependent loads),
-// checks the member against it (the shared entries equal the first member's,
-// both contexts cover them, the group fits max_group), then writes the suffix
-// table row, the suffix length and the member's record for the merge
-// (NaN-row flag, prefix tokens); the group's first member writes the prefix
-// length for the prefix phase.
-__global__ void __launch_bounds__(256) cascade_prep_kernel(
-    const int32_t* __restrict__ tables, const int32_t* __restrict__ ctx, const int32_t* __restrict__ group_start,
-    const int32_t* __restrict__ shared, int n_groups, int max_group, int max_blocks,
-    int32_t* __restrict__ tables_sfx, int32_t* __restrict__ ctx_sfx, int32_t* __restrict__ prefix_ctx,
-    int2* __restrict__ info) {
-  __shared__ int grp;  // the member's group
-  __shared__ int mismatch;
-  const int s = blockIdx.x;
-  if (threadIdx.x == 0) {
-    grp = -1;
-    mismatch = 0;
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < n_groups; t += blockDim.x)
-    if (group_start[t] <= s && s < group_start[t + 1]) atomicMax(&grp, t);  // one match when well formed
-  __syncthreads();
-  const int g = grp;
-  const int first = g >= 0 ? group_start[g] : -1;
-  const int end = g >= 0 ? group_start[g + 1] : -1;
-  const bool in_group = g >= 0 && first >= 0 && first <= s && s < end;
-  const int skip = in_group ? shared[g] : 0;
-  const int n = min(ctx[s], max_blocks * 16);
-  // the first member's context must cover the prefix too: it alone sets the
-  // prefix length, and every member reads the prefix through its table row
-  const bool group_ok = in_group && skip >= 0 && skip <= max_blocks &&
-                        16 * skip <= max(min(ctx[first], max_blocks * 16), 0) && end - first <= max_group;
-  bool ok = group_ok && 16 * skip <= max(n, 0);
-  if (ok)
-    for (int j = threadIdx.x; j < skip; j += blockDim.x)
-      if (tables[static_cast<int64_t>(s) * max_blocks + j] != tables[static_cast<int64_t>(first) * max_blocks + j])
-        mismatch = 1;
-  __syncthreads();
-  ok = ok && !mismatch;
-  const int shift = ok ? skip : 0;
-  for (int j = threadIdx.x; j < max_blocks; j += blockDim.x)
-    tables_sfx[static_cast<int64_t>(s) * max_blocks + j] =
-        (ok && j + shift < max_blocks) ? tables[static_cast<int64_t>(s) * max_blocks + j + shift] : -1;
-  if (threadIdx.x == 0) {
-    ctx_sfx[s] = ok ? n - 16 * skip : 0;
-    info[s] = make_int2(ok ? 0 : 1, group_ok ? 16 * skip : 0);
-    if (in_group && s == first) prefix_ctx[g] = group_ok ? 16 * skip : 0;
-  }
-}
-
-struct cascade_args {
-  sk_args sfx;         // the suffix decode (cum_parts, slots, n_waves)
-  const int2* info;    // [n_seqs]: NaN-row flag, prefix tokens
-  const float* pre_m;  // prefix partials [n_seqs * Hq][pre_parts]
-  const float* pre_l;
-  const float* pre_o;  // [..][D]
-  int pre_part_tokens, pre_parts;
-};
-
-// One wave per (sequence, query head): the prefix partitions and the suffix
-// runs of the member, folded with M = max m, out = sum 2^(m - M) O / sum
-// 2^(m - M) l.  A poisoned partial, a member that failed its check, or a
-// group larger than the multi-query grid gives a NaN row; no keys at all give
-// a zero row.
-constexpr int kCascadeBatch = 8;  // partial rows per batch of loads
-
-template <int D>
-__global__ void __launch_bounds__(256) cascade_merge_kernel(cascade_args c) {
-  const sk_args& a = c.sfx;
-  const int lane = threadIdx.x & 63;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (item >= static_cast<int64_t>(a.n_seqs) * a.n_q_heads) return;
-  const int s = static_cast<int>(item / a.n_q_heads);
-  const int head = static_cast<int>(item % a.n_q_heads);
-  const int G = a.n_q_heads / a.n_kv_heads;
-  const int kvh = head / G, hg = head % G;
-  uint16_t* orow = static_cast<uint16_t*>(a.out) + item * D;
-  constexpr int E = (D + 63) / 64;
-  const int2 inf = c.info[s];
-  const bool nan_row = inf.x != 0;
-  const int pre_tokens = inf.y;
-  const int n_pre = pre_tokens > 0 ? (pre_tokens + c.pre_part_tokens - 1) / c.pre_part_tokens : 0;
-  // suffix runs: waves wF..wL of unit (s, kvh), as the split-K merge finds them
-  const int np = a.cum_parts[s + 1] - a.cum_parts[s];
-  const int64_t total = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[a.n_seqs];
-  const int64_t W = a.n_waves;
-  int64_t wF = 0, wL = -1;
-  if (np > 0) {
-    const int64_t first = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[s] + static_cast<int64_t>(kvh) * np;
-    wF = ((first + 1) * W - 1) / total;
-    wL = ((first + np) * W - 1) / total;
-  }
-  auto run_begin = [&](int64_t w) { return w * total / W; };
-  const int64_t unit = static_cast<int64_t>(s) * a.n_kv_heads + kvh;
-  const int n_suf = static_cast<int>(wL - wF + 1);
-  // entry i < n_pre: prefix partition i; else suffix wave wF + (i - n_pre).
-  // Gives m, l and the entry's row (of pre_o or part_o); a suffix wave with
-  // an empty run wrote nothing and gets m = -inf.
-  auto entry = [&](int i, float& m, float& l, int64_t& row) {
-    if (i < n_pre) {
-      row = item * c.pre_parts + i;
-      m = c.pre_m[row];
-      l = c.pre_l[row];
-      return;
-    }
-    const int64_t w = wF + (i - n_pre);
-    row = (w + unit) * G + hg;
-    if (!(run_begin(w) < run_begin(w + 1))) {
-      m = -INFINITY;
-      l = 0.f;
-      return;
-    }
-    m = a.part_m[row];
-    l = a.part_l[row];
-  };
-  const int n_ent = n_pre + n_suf;
-  if (n_ent <= 64) {
-    // the usual case: every lane resolves one entry once, and the rows are
-    // loaded kCascadeBatch at a time with no branch between the loads, so a
-    // batch waits out one memory latency (entries of weight 0 -- empty runs,
-    // NaN -- are loaded, the row lies inside the workspace, but not added)
-    float m = -INFINITY, l = 0.f;
-    int64_t row = 0;
-    if (lane < n_ent) entry(lane, m, l, row);
-    const bool nan_seen = nan_row || __builtin_amdgcn_ballot_w64(m != m) != 0;
-    const float M = wave_max(m != m ? -INFINITY : m);
-    const float w = (m == -INFINITY || m != m) ? 0.f : exp2f(m - M);
-    const float L = wave_sum(w == 0.f ? 0.f : w * l);
-    const int row_lo = static_cast<int>(row & 0xffffffff), row_hi = static_cast<int>(row >> 32);
-    float acc[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) acc[i] = 0.f;
-    for (int k0 = 0; k0 < n_ent; k0 += kCascadeBatch) {
-      float v[kCascadeBatch][E];
-#pragma unroll
-      for (int k = 0; k < kCascadeBatch; ++k) {
-        const int kk = min(k0 + k, n_ent - 1);  // past the end: a repeat, weight 0 below
-        const int64_t rk = (static_cast<int64_t>(__shfl(row_hi, kk)) << 32) | static_cast<uint32_t>(__shfl(row_lo, kk));
-        const float* ok = (kk < n_pre ? c.pre_o : a.part_o) + rk * D;
-#pragma unroll
-        for (int i = 0; i < E; ++i) v[k][i] = lane + 64 * i < D ? ok[lane + 64 * i] : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < kCascadeBatch; ++k) {
-        const float wk = k0 + k < n_ent ? __shfl(w, k0 + k) : 0.f;
-#pragma unroll
-        for (int i = 0; i < E; ++i) acc[i] = wk == 0.f ? acc[i] : __builtin_fmaf(wk, v[k][i], acc[i]);
-      }
-    }
-    const bool empty = M == -INFINITY && !nan_seen;  // no key at all
-#pragma unroll
-    for (int i = 0; i < E; ++i)
-      if (lane + 64 * i < D)
-        orow[lane + 64 * i] = nan_seen ? static_cast<uint16_t>(0x7fc0) : (empty ? 0 : f32_to_bf16(acc[i] / L));
-    return;
-  }
-  float M = -INFINITY;
-  bool nan_seen = nan_row;
-  for (int i0 = 0; i0 < n_ent; i0 += 64) {
-    float m = -INFINITY, l;
-    int64_t row;
-    if (i0 + lane < n_ent) entry(i0 + lane, m, l, row);
-    nan_seen |= __builtin_amdgcn_ballot_w64(m != m) != 0;
-    M = fmaxf(M, m);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float acc[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) acc[i] = 0.f;
-  float L = 0.f;
-  for (int i0 = 0; i0 < n_ent; i0 += 64) {
-    // each lane resolves one entry; its weight and row are then broadcast
-    float m = -INFINITY, l = 0.f;
-    int64_t row = 0;
-    if (i0 + lane < n_ent) entry(i0 + lane, m, l, row);
-    const float w = (m == -INFINITY || m != m) ? 0.f : exp2f(m - M);
-    L += w == 0.f ? 0.f : w * l;
-    const int row_lo = static_cast<int>(row & 0xffffffff), row_hi = static_cast<int>(row >> 32);
-    const int cnt = min(64, n_ent - i0);
-    for (int k = 0; k < cnt; ++k) {
-      const float wk = __shfl(w, k);
-      if (wk == 0.f) continue;  // wave uniform
-      const int64_t rk = (static_cast<int64_t>(__shfl(row_hi, k)) << 32) |
-                         static_cast<uint32_t>(__shfl(row_lo, k));
-      const float* ok = (i0 + k < n_pre ? c.pre_o : a.part_o) + rk * D;
-#pragma unroll
-      for (int i = 0; i < E; ++i)
-        if (lane + 64 * i < D) acc[i] += wk * ok[lane + 64 * i];
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-  const bool empty = M == -INFINITY && !nan_seen;  // no key at all
-#pragma unroll
-  for (int i = 0; i < E; ++i)
-    if (lane + 64 * i < D)
-      orow[lane + 64 * i] = nan_seen ? static_cast<uint16_t>(0x7fc0) : (empty ? 0 : f32_to_bf16(acc[i] / L));
 }
 
 // ---------------------------------------------------------------------------
@@ -1937,138 +1650,6 @@ kv_status paged_attention_decode_static(kv_pool* pool, int32_t layer, const void
     if (kv_status s = decode_scratch(&ws)) return s;
   return paged_attention_decode(pool, layer, q, out, d_block_tables, d_context_lens, n_seqs, max_blocks_per_seq,
                                 num_q_heads, opts, ws, need > 0 ? kDecodeScratchBytes : 0, hip_stream);
-}
-
-// ---- cascade decode over shared prefixes ---------------------------------
-
-namespace {
-
-struct cascade_layout {
-  uint64_t decode, tables, ctx, prefix_ctx, info, pre, total;
-  int pre_part_tokens, pre_parts;
-};
-
-kv_status cascade_plan(kv_pool* pool, int n_seqs, int n_groups, int max_group, int num_q_heads, int max_blocks,
-                       const kv_attention_options* opts, resolved& r, cascade_layout& L) {
-  if (kv_status s = resolve(pool, n_seqs, num_q_heads, max_blocks, opts, r)) return s;
-  if (r.kernel != KV_KERNEL_MFMA || pool->cfg.dtype != KV_BF16 || pool->cfg.block_size != 16)
-    return fail(KV_ERR_UNSUPPORTED, "the cascade decode needs a bf16 pool with B = 16 and the matrix-core kernel");
-  if (n_groups < 1 || n_groups > n_seqs || max_group < 1)
-    return fail(KV_ERR_INVALID, "need 1 <= n_groups <= n_seqs and max_group >= 1");
-  uint64_t pre_bytes = 0;
-  if (kv_status s = prefix_phase_plan(pool, n_groups, n_seqs, max_group, num_q_heads, max_blocks, opts,
-                                      &L.pre_part_tokens, &L.pre_parts, &pre_bytes))
-    return s;
-  L.decode = up256(workspace_for(pool->cfg, n_seqs, num_q_heads, r));
-  L.tables = L.decode;
-  L.ctx = L.tables + up256(static_cast<uint64_t>(n_seqs) * max_blocks * 4);
-  L.prefix_ctx = L.ctx + up256(static_cast<uint64_t>(n_seqs) * 4);
-  L.info = L.prefix_ctx + up256(static_cast<uint64_t>(n_groups) * 4);
-  L.pre = L.info + up256(static_cast<uint64_t>(n_seqs) * 8);
-  L.total = L.pre + up256(pre_bytes);
-  return KV_OK;
-}
-
-}  // namespace
-
-uint64_t paged_attention_cascade_workspace_bytes(kv_pool* pool, int32_t n_seqs, int32_t n_groups, int32_t max_group,
-                                                 int32_t num_q_heads, int32_t max_blocks_per_seq,
-                                                 const kv_attention_options* opts) {
-  if (!pool || n_seqs <= 0) return 0;
-  resolved r;
-  cascade_layout L;
-  if (cascade_plan(pool, n_seqs, n_groups, max_group, num_q_heads, max_blocks_per_seq, opts, r, L) != KV_OK) return 0;
-  return L.total;
-}
-
-kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const void* q, void* out,
-                                         const int32_t* d_block_tables, const int32_t* d_context_lens,
-                                         int32_t n_seqs, int32_t max_blocks_per_seq, int32_t num_q_heads,
-                                         const int32_t* d_group_start, const int32_t* d_shared_blocks,
-                                         int32_t n_groups, int32_t max_group, const kv_attention_options* opts,
-                                         void* d_workspace, uint64_t workspace_bytes, void* hip_stream) {
-  if (!pool) return fail(KV_ERR_INVALID, "pool is NULL");
-  const kv_pool_config& c = pool->cfg;
-  if (layer < 0 || layer >= c.num_layers) return fail(KV_ERR_INVALID, "layer out of range");
-  if (n_seqs == 0) return KV_OK;
-  resolved r;
-  cascade_layout L;
-  if (kv_status s = cascade_plan(pool, n_seqs, n_groups, max_group, num_q_heads, max_blocks_per_seq, opts, r, L))
-    return s;
-  if (!q || !out || !d_block_tables || !d_context_lens || !d_group_start || !d_shared_blocks || !pool->k_cache ||
-      !pool->v_cache)
-    return fail(KV_ERR_INVALID, "NULL device pointer");
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
-    return fail(KV_ERR_INVALID, "q and out must be 16-byte aligned");
-  if (!d_workspace || workspace_bytes < L.total)
-    return fail(KV_ERR_INVALID, "workspace too small: need " + std::to_string(L.total) + " bytes");
-  if (reinterpret_cast<uintptr_t>(d_workspace) & 255) return fail(KV_ERR_INVALID, "workspace must be 256-byte aligned");
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  char* ws = static_cast<char*>(d_workspace);
-  int32_t* tables_sfx = reinterpret_cast<int32_t*>(ws + L.tables);
-  int32_t* ctx_sfx = reinterpret_cast<int32_t*>(ws + L.ctx);
-  int32_t* prefix_ctx = reinterpret_cast<int32_t*>(ws + L.prefix_ctx);
-  int2* info = reinterpret_cast<int2*>(ws + L.info);
-  const call_events ev = events_of(opts);
-  if (kv_status s = hip_check(
-          launch_timed(cascade_prep_kernel, dim3(static_cast<unsigned>(n_seqs)), dim3(256), 0u, st, ev.start, nullptr,
-                       d_block_tables, d_context_lens, d_group_start, d_shared_blocks, n_groups, max_group,
-                       max_blocks_per_seq, tables_sfx, ctx_sfx, prefix_ctx, info),
-          "cascade prep launch"))
-    return s;
-  // prefix: every group's shared blocks, once, for all members
-  if (kv_status s = prefix_phase_launch(pool, layer, q, out, d_group_start, prefix_ctx, d_block_tables, n_groups,
-                                        n_seqs, max_group, max_blocks_per_seq, num_q_heads, opts, ws + L.pre, st,
-                                        ev.kernel_stop))
-    return s;
-  // suffix: the split-K decode on the shifted tables, partials only
-  const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
-  const int G = num_q_heads / c.num_kv_heads;
-  sk_args a{};
-  a.q = q;
-  a.out = out;
-  a.k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
-  a.v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
-  const uint64_t slots = static_cast<uint64_t>(r.groups) * kSkWaves + static_cast<uint64_t>(n_seqs) * c.num_kv_heads;
-  a.part_m = reinterpret_cast<float*>(ws);
-  a.part_l = reinterpret_cast<float*>(ws + up256(slots * G * 4));
-  a.part_o = reinterpret_cast<float*>(ws + 2 * up256(slots * G * 4));
-  a.cum_parts = reinterpret_cast<int32_t*>(ws + 2 * up256(slots * G * 4) + up256(slots * G * c.head_dim * 4));
-  a.n_seqs = n_seqs;
-  a.max_blocks = max_blocks_per_seq;
-  a.n_q_heads = num_q_heads;
-  a.n_kv_heads = c.num_kv_heads;
-  a.num_blocks = c.num_blocks;
-  a.part_blocks = r.partition / 16;
-  a.block_size = 16;  // the cascade reads B = 16 pools (cascade_plan)
-  a.n_waves = static_cast<int>(r.groups * kSkWaves);
-  a.q_units = sk_q_units(n_seqs, G, c.head_dim);
-  a.scale_log2 = r.scale * kLog2e;
-  a.force_partial = 1;
-  hipError_t e;
-  switch (c.head_dim) {
-    case 64: e = launch_mfma<64, kFmtBf16>(a, ctx_sfx, tables_sfx, r.groups, G, st); break;
-    case 128: e = launch_mfma<128, kFmtBf16>(a, ctx_sfx, tables_sfx, r.groups, G, st); break;
-    default: e = launch_mfma<256, kFmtBf16>(a, ctx_sfx, tables_sfx, r.groups, G, st); break;
-  }
-  if (kv_status s = hip_check(e, "cascade suffix launch")) return s;
-  cascade_args m{};
-  m.sfx = a;
-  m.info = info;
-  const uint64_t pre_rows = static_cast<uint64_t>(n_seqs) * num_q_heads * L.pre_parts;
-  m.pre_m = reinterpret_cast<const float*>(ws + L.pre);
-  m.pre_l = reinterpret_cast<const float*>(ws + L.pre + up256(pre_rows * 4));
-  m.pre_o = reinterpret_cast<const float*>(ws + L.pre + 2 * up256(pre_rows * 4));
-  m.pre_part_tokens = L.pre_part_tokens;
-  m.pre_parts = L.pre_parts;
-  const int64_t items = static_cast<int64_t>(n_seqs) * num_q_heads;
-  const unsigned mgrid = static_cast<unsigned>((items + 3) / 4);
-  switch (c.head_dim) {
-    case 64: e = launch_timed(cascade_merge_kernel<64>, dim3(mgrid), dim3(256), 0u, st, nullptr, ev.stop, m); break;
-    case 128: e = launch_timed(cascade_merge_kernel<128>, dim3(mgrid), dim3(256), 0u, st, nullptr, ev.stop, m); break;
-    default: e = launch_timed(cascade_merge_kernel<256>, dim3(mgrid), dim3(256), 0u, st, nullptr, ev.stop, m); break;
-  }
-  return hip_check(e, "cascade merge launch");
 }
 
 }  // extern "C"

@@ -86,15 +86,6 @@ void prefix_on_release(kv_pool* p, int64_t seq);  // the request gives back its 
 void prefix_destroy(kv_pool* p);
 int32_t prefix_held(const kv_pool* p, int32_t block);  // references the tree holds on a block
 
-// Prefix phase of the cascade decode (prefill.hip): plan and launch.
-kv_status prefix_phase_plan(const kv_pool* pool, int n_groups, int n_rows, int max_group, int num_q_heads,
-                            int max_blocks, const kv_attention_options* opts, int* part_tokens, int* max_parts,
-                            uint64_t* bytes);
-kv_status prefix_phase_launch(kv_pool* pool, int layer, const void* q, void* out, const int32_t* group_start,
-                              const int32_t* prefix_ctx, const int32_t* tables, int n_groups, int n_rows,
-                              int max_group, int max_blocks, int num_q_heads, const kv_attention_options* opts,
-                              void* ws, hipStream_t st, hipEvent_t ev_stop);
-
 // Multi-query attention for the pools the multi-query kernel does not read
 // (kernels.hip): one decode query per chunk row, through the decode kernels.
 // q and out rows are in the pool's element type (bf16 for quantised pools).

@@ -59,9 +59,10 @@ struct pf_args {
   int wt;                        // tiles per workgroup (1, 2 or 4); the other factor of 4 is partitions
   int tile_groups, part_groups;  // workgroups per unit along tiles and along partitions
   float scale_log2;
-  // Shared-prefix mode (set by the cascade decode): every query sees all n
-  // keys (no causal mask), "sequence" s reads table row table_rows[s], and
-  // every tile writes partials even when it has one partition.
+  // Launch options.  The prefill sets causal = 1 and leaves the other two
+  // off; with causal = 0 every query would see all n keys, table_rows remaps
+  // "sequence" s to table row table_rows[s], and force_partial makes every
+  // tile write partials even when it has one partition.
   int causal;
   int force_partial;
   const int32_t* table_rows;  // nullptr: row s
@@ -907,70 +908,6 @@ bool rowwise(const kv_pool* pool, int num_q_heads, const kv_attention_options* o
 }
 
 }  // namespace
-
-// The prefix phase of the cascade decode (kernels.hip): the members of every
-// group are the query rows of one "sequence" whose keys are the group's shared
-// prefix (table row of the first member, prefix_ctx tokens); no causal mask;
-// every tile writes partials [row * Hq + head][max_parts] into ws.
-kv_status prefix_phase_plan(const kv_pool* pool, int n_groups, int n_rows, int max_group, int num_q_heads,
-                            int max_blocks, const kv_attention_options* opts, int* part_tokens, int* max_parts,
-                            uint64_t* bytes) {
-  pf_plan p;
-  if (kv_status s = pf_resolve(pool, n_groups, n_rows, max_group, num_q_heads, max_blocks, opts, p)) return s;
-  *part_tokens = p.partition;
-  *max_parts = p.max_parts;
-  const uint64_t rows = static_cast<uint64_t>(n_rows) * num_q_heads * p.max_parts;
-  *bytes = 2 * up256(rows * 4) + up256(rows * pool->cfg.head_dim * 4);
-  return KV_OK;
-}
-
-kv_status prefix_phase_launch(kv_pool* pool, int layer, const void* q, void* out, const int32_t* group_start,
-                              const int32_t* prefix_ctx, const int32_t* tables, int n_groups, int n_rows,
-                              int max_group, int max_blocks, int num_q_heads, const kv_attention_options* opts,
-                              void* ws, hipStream_t st, hipEvent_t ev_stop) {
-  pf_plan p;
-  if (kv_status s = pf_resolve(pool, n_groups, n_rows, max_group, num_q_heads, max_blocks, opts, p)) return s;
-  const kv_pool_config& c = pool->cfg;
-  const int64_t layer_off = static_cast<int64_t>(layer) * c.num_blocks * c.num_kv_heads * tile_bytes(c);
-  const uint64_t rows = static_cast<uint64_t>(n_rows) * num_q_heads * p.max_parts;
-  char* w = static_cast<char*>(ws);
-  pf_args a{};
-  a.q = q;
-  a.out = out;
-  a.k_layer = static_cast<const char*>(pool->k_cache) + layer_off;
-  a.v_layer = static_cast<const char*>(pool->v_cache) + layer_off;
-  a.q_indptr = group_start;
-  a.ctx_lens = prefix_ctx;
-  a.tables = tables;
-  a.table_rows = group_start;
-  a.part_m = reinterpret_cast<float*>(w);
-  a.part_l = reinterpret_cast<float*>(w + up256(rows * 4));
-  a.part_o = reinterpret_cast<float*>(w + 2 * up256(rows * 4));
-  a.n_seqs = n_groups;
-  a.total_q = n_rows;
-  a.max_q_len = max_group;
-  a.max_blocks = max_blocks;
-  a.n_q_heads = num_q_heads;
-  a.n_kv_heads = c.num_kv_heads;
-  a.num_blocks = c.num_blocks;
-  a.part_blocks = p.partition / 16;
-  a.max_parts = p.max_parts;
-  a.wt = p.wt;
-  a.tile_groups = p.tile_groups;
-  a.part_groups = p.part_groups;
-  a.cols_per_tile = 16 * p.ncg;
-  a.scale_log2 = p.scale * kLog2e;
-  a.causal = 0;
-  a.force_partial = 1;
-  const int64_t grid = static_cast<int64_t>(n_groups) * c.num_kv_heads * p.tile_groups * p.part_groups;
-  hipError_t e;
-  switch (c.head_dim) {
-    case 64: e = pf_launch_d<64>(a, p.ncg, grid, st, nullptr, ev_stop); break;
-    case 128: e = pf_launch_d<128>(a, p.ncg, grid, st, nullptr, ev_stop); break;
-    default: e = pf_launch_d<256>(a, p.ncg, grid, st, nullptr, ev_stop); break;
-  }
-  return hip_check(e, "cascade prefix launch");
-}
 
 }  // namespace pagedkv
 
