@@ -76,6 +76,8 @@ struct cs_args {
   int32_t* cum_parts;  // [n_a + n_seqs + 1] partitions before each item, per kv head (workgroup 0 writes)
   int32_t* cum_cost;   // [n_a + n_seqs + 1] work-split cost before each item, per kv head (workgroup 0 writes)
   int4* member;    // [n_seqs]: prefix tiles (-1: NaN row), prefix item (-1: none), first column, 0
+  int4* mdesc;     // [n_seqs][Hkv]: first wave and wave count of the member's prefix unit, then of its
+                   // suffix unit (workgroup 0 writes, for the merge)
   int n_seqs, n_groups, cpg, mc, max_group, max_blocks, n_q_heads, n_kv_heads, num_blocks, part_blocks, n_waves;
   int acol;                // columns of a prefix unit's partial rows (column tiles x 16)
   int wa, wb, wu;          // work-split cost of a prefix partition, a suffix partition, a unit's start
@@ -238,25 +240,32 @@ attn_cascade_kernel(cs_args a) {
   const bool publish = blockIdx.x == 0;  // workgroup 0 writes the plan for the merge
 
   // ---- the plan: which members read which prefix, and every unit's tiles ----
-  // Every loop below runs over threads, and each thread's global reads are
-  // independent, so the plan waits out two memory latencies (the group starts,
-  // then the first members' contexts).  gS (in cum_p until the scan) holds each
-  // group's prefix tiles, -1 for a group whose members get NaN rows; j0s holds
-  // each member's group until it holds its prefix tiles.
+  // The first loop reads every global input of the plan (contexts, group
+  // starts, shared block counts) into LDS, all independent loads, so the plan
+  // waits out one memory latency; the rest works in LDS.  gst (in cum_c until
+  // the scan) holds the group starts; gS (in cum_p until the scan) each
+  // group's shared blocks, then its prefix tiles, -1 for a group whose
+  // members get NaN rows; j0s holds each member's group until it holds its
+  // prefix tiles.
   int* gS = cum_p;
-  for (int s = tid; s < n; s += kCsWaves * 64) {
-    j0s[s] = -1;
-    ctx_n[s] = max(min(a.ctx_lens[s], cap), 0);
+  int* gst = cum_c;
+  for (int s = tid; s < max(n, a.n_groups + 1); s += kCsWaves * 64) {
+    if (s < n) {
+      j0s[s] = -1;
+      ctx_n[s] = max(min(a.ctx_lens[s], cap), 0);
+    }
+    if (s <= a.n_groups) gst[s] = a.group_start[s];
+    if (s < a.n_groups) gS[s] = a.shared[s];
   }
   for (int v = tid; v < na; v += kCsWaves * 64) cum_t[v] = 0;  // prefix tiles per chunk
   if (tid == 0) malformed = 0;
   __syncthreads();
   for (int g = tid; g < a.n_groups; g += kCsWaves * 64) {
-    const int first = a.group_start[g], end = a.group_start[g + 1];
+    const int first = gst[g], end = gst[g + 1];
     const bool well = first >= 0 && end <= n && first <= end && (g > 0 || first == 0) &&
                       (g < a.n_groups - 1 || end == n);
     if (!well) malformed = 1;  // every member gets a NaN row
-    const int S = a.shared[g];
+    const int S = gS[g];
     const bool ok = well && first < end && end - first <= a.max_group && S >= 0 && S <= a.max_blocks &&
                     16 * S <= ctx_n[first];
     gS[g] = ok ? S : -1;
@@ -274,7 +283,7 @@ attn_cascade_kernel(cs_args a) {
     const int g = bad_plan ? -1 : j0s[s];
     const int S = g >= 0 ? gS[g] : -1;
     const bool covers = S >= 0 && 16 * S <= ctx_n[s];
-    const int first = g >= 0 ? a.group_start[g] : 0;
+    const int first = g >= 0 ? gst[g] : 0;
     const int4 r = make_int4(covers ? S : -1, covers && S > 0 ? g * a.cpg + (s - first) / a.mc : -1,
                              ((s - first) % a.mc) * G, 0);
     j0s[s] = r.x;
@@ -311,6 +320,29 @@ attn_cascade_kernel(cs_args a) {
     const int cb = rfl(cum_x[item]);
     return split.first_at(c, item, np, cb, rfl(cum_x[item + 1]) - cb, rfl(cum_p[item]));
   };
+  if (publish) {
+    // for the merge: the waves holding each (member, kv head)'s prefix unit
+    // and suffix unit (the members as loop 3 wrote them: same workgroup,
+    // after the barriers above)
+    auto waves_of = [&](int item, int kvh, int& w0, int& cnt) {
+      const int np = cum_p[item + 1] - cum_p[item];
+      w0 = 0;
+      cnt = 0;
+      if (np <= 0) return;
+      const int64_t cb = cum_x[item], uc = cum_x[item + 1] - cb;
+      const int64_t f = split.owner(split.start(item, kvh, 0, cb, uc));
+      w0 = static_cast<int>(f);
+      cnt = static_cast<int>(split.owner(split.start(item, kvh, np - 1, cb, uc)) - f + 1);
+    };
+    for (int i = tid; i < n * Hkv; i += kCsWaves * 64) {
+      const int s = i / Hkv, kvh = i % Hkv;
+      const int4 mi = a.member[s];
+      int4 d = make_int4(0, 0, 0, 0);
+      if (mi.x > 0 && mi.y >= 0) waves_of(mi.y, kvh, d.x, d.y);
+      if (mi.x >= 0) waves_of(na + s, kvh, d.z, d.w);
+      a.mdesc[i] = d;
+    }
+  }
   const int64_t p_begin = first_at(wid * split.C / W), p_end = first_at((wid + 1) * split.C / W);
   if (p_begin >= p_end) return;
 
@@ -398,32 +430,31 @@ attn_cascade_kernel(cs_args a) {
   auto padded = [](int e) __attribute__((always_inline)) { return (e / D) * kQStride + e % D; };
   // copies the first prefix unit's query columns (member-major: column
   // m * G + h) to its slot before the ring is first filled: every piece is
-  // loaded, then all are written, so the copy waits out one memory latency.
-  // (Copies straight from global memory to LDS are avoided everywhere in this
-  // kernel: the compiler would then make every LDS read wait for all loads.)
+  // loaded (at most NT x 16 columns, 16 pieces per lane up to d = 256), then
+  // all are written, so the copy waits out one memory latency.  (Copies
+  // straight from global memory to LDS are avoided everywhere in this kernel:
+  // the compiler would then make every LDS read wait for all loads.)
   auto stage_prefix = [&](const cs_cursor& c) __attribute__((always_inline)) {
     const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-    const int elems = c.cnt * G * D;
-    // the piece of lane `lane` at element offset e0 + (i * 64 + lane) * 8
+    const int elems = c.cnt * G * D;  // <= NT x 16 columns
+    constexpr int kPieces = NT * 16 * D / 512;
+    // the piece of lane `lane` at element offset (i * 64 + lane) * 8
     auto src = [&](int e) __attribute__((always_inline)) {
       const int col = e / D, dim = e % D;
       const int m = col / G, h = col % G;
       return reinterpret_cast<const uint4*>(qg + (static_cast<int64_t>(c.m0 + m) * a.n_q_heads + c.kvh * G + h) * D +
                                             dim);
     };
-    // four pieces per lane in flight at once (named, not an array, so that
-    // they stay in registers)
-    for (int e0 = 0; e0 < elems; e0 += 4 * 512) {
-      const int e1 = e0 + lane * 8, e2 = e1 + 512, e3 = e2 + 512, e4 = e3 + 512;
-      uint4 v1{}, v2{}, v3{}, v4{};
-      if (e1 < elems) v1 = *src(e1);
-      if (e2 < elems) v2 = *src(e2);
-      if (e3 < elems) v3 = *src(e3);
-      if (e4 < elems) v4 = *src(e4);
-      if (e1 < elems) *reinterpret_cast<uint4*>(a_slot + padded(e1)) = v1;
-      if (e2 < elems) *reinterpret_cast<uint4*>(a_slot + padded(e2)) = v2;
-      if (e3 < elems) *reinterpret_cast<uint4*>(a_slot + padded(e3)) = v3;
-      if (e4 < elems) *reinterpret_cast<uint4*>(a_slot + padded(e4)) = v4;
+    uint4 v[kPieces];
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int e = (i * 64 + lane) * 8;
+      v[i] = e < elems ? *src(e) : uint4{};
+    }
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int e = (i * 64 + lane) * 8;
+      if (e < elems) *reinterpret_cast<uint4*>(a_slot + padded(e)) = v[i];
     }
   };
 
@@ -728,42 +759,35 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cs_args a) {
   const int kvh = head / G, hg = head % G;
   constexpr int E = (D + 63) / 64;
   uint16_t* orow = static_cast<uint16_t*>(a.out) + item * D;
+  // the member's plan and its units' waves, loaded together
   const int4 mi = a.member[s];
+  const int4 md = a.mdesc[static_cast<int64_t>(s) * Hkv + kvh];
   const int64_t W = a.n_waves;
   const int na = a.n_groups * a.cpg;
-  const int V = na + a.n_seqs;
-  const cs_split split(a.cum_parts, a.cum_cost, V, na, Hkv, a.wa, a.wb, a.wu, W);
-  const int32_t* cum_x = split.weighted ? a.cum_cost : a.cum_parts;
-  // the waves w0 .. w1 whose runs hold partitions of unit (item, kv head)
-  auto waves_of = [&](int item, int64_t& w0, int64_t& w1) {
-    const int np = a.cum_parts[item + 1] - a.cum_parts[item];
-    w0 = 0;
-    w1 = -1;
-    if (np <= 0) return;
-    const int64_t cb = cum_x[item], uc = cum_x[item + 1] - cb;
-    w0 = split.owner(split.start(item, kvh, 0, cb, uc));
-    w1 = split.owner(split.start(item, kvh, np - 1, cb, uc));
-  };
-  // the prefix unit (none when the member reads no prefix) and the suffix unit
-  int64_t wFA = 0, wLA = -1, wFB = 0, wLB = -1;
-  if (mi.x > 0 && mi.y >= 0) waves_of(mi.y, wFA, wLA);
-  if (mi.x >= 0) waves_of(na + s, wFB, wLB);
+  const cs_split split(a.cum_parts, a.cum_cost, na + a.n_seqs, na, Hkv, a.wa, a.wb, a.wu, W);
+  const int64_t wFA = md.x, wFB = md.z;
   const int64_t uA = static_cast<int64_t>(mi.y) * Hkv + kvh;
-  const int64_t uB = static_cast<int64_t>(na + s) * Hkv + kvh - static_cast<int64_t>(na) * Hkv;
-  const int n_a = static_cast<int>(wLA - wFA + 1);
-  const int n_ent = n_a + static_cast<int>(wLB - wFB + 1);
+  const int64_t uB = static_cast<int64_t>(s) * Hkv + kvh;
+  const int n_a = md.y;
+  const int n_ent = md.y + md.w;
   const int col_a = mi.z + hg;
-  // entry i: prefix wave wFA + i (i < n_a), else suffix wave wFB + i - n_a, as
-  // (m, l, row); a wave with an empty run wrote nothing and has weight 0
-  auto entry = [&](int i, float& m, float& l, int64_t& row) {
+  // entry i: prefix wave wFA + i (i < n_a), else suffix wave wFB + i - n_a:
+  // its partial row, and whether that wave wrote one (a wave without
+  // partitions wrote nothing: only the unweighted split has such waves)
+  auto entry_row = [&](int i, int64_t& row) -> bool {
     const bool pre = i < n_a;
     const int64_t w = pre ? wFA + i : wFB + (i - n_a);
-    row = 0;
+    row = pre ? (w + uA) * a.acol + col_a : (w + uB) * G + hg;
+    return split.weighted || w * split.C / W < (w + 1) * split.C / W;
+  };
+  auto entry = [&](int i, float& m, float& l, int64_t& row) {
+    const bool pre = i < n_a;
     m = -INFINITY;
     l = 0.f;
-    // (a wave without partitions wrote nothing: only the unweighted split has such waves)
-    if (!split.weighted && !(w * split.C / W < (w + 1) * split.C / W)) return;
-    row = pre ? (w + uA) * a.acol + col_a : (w + uB) * G + hg;
+    if (!entry_row(i, row)) {
+      row = 0;
+      return;
+    }
     m = (pre ? a.a_m : a.b_m)[row];
     l = (pre ? a.a_l : a.b_l)[row];
   };
@@ -795,8 +819,38 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cs_args a) {
       }
     }
   };
-  if (n_ent <= 64) {
-    // the usual case: every lane resolves one entry once
+  if (n_ent > 0 && n_ent <= kCsMergeBatch) {
+    // the usual case: lane i loads entry i's (m, l) and every lane its slice
+    // of every entry's row, all at once (one memory latency)
+    float m, l;
+    int64_t row;
+    entry(lane < n_ent ? lane : 0, m, l, row);
+    if (lane >= n_ent) {
+      m = -INFINITY;
+      l = 0.f;
+    }
+    const int row_lo = static_cast<int>(row & 0xffffffff), row_hi = static_cast<int>(row >> 32);
+    float v[kCsMergeBatch][E];
+#pragma unroll
+    for (int k = 0; k < kCsMergeBatch; ++k) {
+      const int kk = min(k, n_ent - 1);  // past the end: a repeat, weight 0 below
+      const int64_t rk = (static_cast<int64_t>(__shfl(row_hi, kk)) << 32) | static_cast<uint32_t>(__shfl(row_lo, kk));
+      const float* src = (kk < n_a ? a.a_o : a.b_o) + rk * D;
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[k][e] = lane + 64 * e < D ? src[lane + 64 * e] : 0.f;
+    }
+    nan_seen |= __builtin_amdgcn_ballot_w64(m != m) != 0;
+    M = wave_max(m != m ? -INFINITY : m);
+    const float w = (m == -INFINITY || m != m) ? 0.f : exp2f(m - M);
+    L = wave_sum(w == 0.f ? 0.f : w * l);
+#pragma unroll
+    for (int k = 0; k < kCsMergeBatch; ++k) {
+      const float wk = k < n_ent ? __shfl(w, k) : 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = wk == 0.f ? acc[e] : __builtin_fmaf(wk, v[k][e], acc[e]);
+    }
+  } else if (n_ent > 0 && n_ent <= 64) {
+    // every lane resolves one entry once
     float m, l;
     int64_t row;
     entry(lane < n_ent ? lane : 0, m, l, row);
@@ -808,8 +862,8 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cs_args a) {
     M = wave_max(m != m ? -INFINITY : m);
     const float w = (m == -INFINITY || m != m) ? 0.f : exp2f(m - M);
     L = wave_sum(w == 0.f ? 0.f : w * l);
-    if (n_ent > 0) accumulate(0, n_ent, w, row);
-  } else {
+    accumulate(0, n_ent, w, row);
+  } else if (n_ent > 64) {
     for (int i0 = 0; i0 < n_ent; i0 += 64) {
       float m = -INFINITY, l = 0.f;
       int64_t row = 0;
@@ -839,7 +893,7 @@ struct cs_plan {
   int nt, acol, mc, cpg, na, aslot, bslot, part_blocks, wa, wb, wu;
   int64_t waves;
   uint64_t lds;
-  uint64_t a_m, a_l, a_o, b_m, b_l, b_o, cum_parts, cum_cost, member, total;  // workspace offsets
+  uint64_t a_m, a_l, a_o, b_m, b_l, b_o, cum_parts, cum_cost, member, mdesc, total;  // workspace offsets
   float scale;
 };
 
@@ -922,6 +976,7 @@ kv_status cs_resolve(const kv_pool* pool, int n_seqs, int n_groups, int max_grou
   p.cum_parts = take((p.na + n_seqs + 1) * 4ull);
   p.cum_cost = take((p.na + n_seqs + 1) * 4ull);
   p.member = take(n_seqs * 16ull);
+  p.mdesc = take(n_seqs * Hkv * 16ull);
   p.total = at;
   return KV_OK;
 }
@@ -1004,6 +1059,7 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   a.cum_parts = reinterpret_cast<int32_t*>(ws + p.cum_parts);
   a.cum_cost = reinterpret_cast<int32_t*>(ws + p.cum_cost);
   a.member = reinterpret_cast<int4*>(ws + p.member);
+  a.mdesc = reinterpret_cast<int4*>(ws + p.mdesc);
   a.n_seqs = n_seqs;
   a.n_groups = n_groups;
   a.cpg = p.cpg;

@@ -23,19 +23,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Maximum and sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 // Maximum and sum of x over lanes l and l ^ 16, and over l and l ^ 32, without
 // the LDS pipe: v_permlane16_swap exchanges the odd 16-lane rows of its first
 // operand with the even rows of its second, v_permlane32_swap the upper half
@@ -56,6 +43,35 @@ __device__ __forceinline__ float sum_xor16(float x) {
 __device__ __forceinline__ float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// x from a partner lane by a DPP pattern within 16-lane rows: quad_perm
+// [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2), the half-row mirror
+// (lane i <-> 7 - i in each 8) and the row mirror (i <-> 15 - i).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum and sum over the 64 lanes of a wave (every lane active; every lane
+// gets the result): a butterfly in which every step pairs disjoint lane
+// groups -- DPP within a row, then the permlane swaps across rows -- so no
+// step goes through the LDS pipe.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f32<kDppXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppMirror>(x));
+  return max_xor32(max_xor16(x));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f32<kDppXor1>(x);
+  x += dpp_f32<kDppXor2>(x);
+  x += dpp_f32<kDppHalfMirror>(x);
+  x += dpp_f32<kDppMirror>(x);
+  return sum_xor32(sum_xor16(x));
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -144,8 +160,7 @@ __device__ __forceinline__ void softmax_step(const f32x4_t& s, int valid, int qu
     sv[i] = (quad * 4 + i < valid) ? s[i] * scale_log2 : -INFINITY;
     mb = fmaxf(mb, sv[i]);
   }
-  mb = fmaxf(mb, __shfl_xor(mb, 16));
-  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  mb = max_xor32(max_xor16(mb));
   const bool grow = mb > m_run + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch
     const float m_new = grow ? mb : m_run;

@@ -833,8 +833,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
 
   // writes the result of the current unit's run and resets the state
   auto finish = [&]() {
-    float l = l_lane + __shfl_xor(l_lane, 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum_xor32(sum_xor16(l_lane));
     const int h = cs.kvh * G + hg;
     const float nan = __builtin_nanf("");
     if (seg_j0 == 0 && cs.j == cs.nb - 1) {  // the whole unit: final row

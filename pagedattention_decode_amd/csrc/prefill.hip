@@ -173,8 +173,7 @@ __device__ __forceinline__ void attend_pair(const QOp& qop, const KOp& kop, cons
     }
     float m = fmaxf(fmaxf(fmaxf(sa[cg][0], sa[cg][1]), fmaxf(sa[cg][2], sa[cg][3])),
                     fmaxf(fmaxf(sb[cg][0], sb[cg][1]), fmaxf(sb[cg][2], sb[cg][3])));
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = max_xor32(max_xor16(m));
     mb[cg] = m * c;
     grow_any |= mb[cg] > m_run[cg] + kRescaleSlack;
   }
@@ -390,8 +389,7 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
   const float nan = __builtin_nanf("");
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    float l = l_lane[cg] + __shfl_xor(l_lane[cg], 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum_xor32(sum_xor16(l_lane[cg]));
     const int f = f0 + cg * 16 + (lane & 15);
     if (f >= cols) continue;
     const int64_t row = static_cast<int64_t>(sq.q0 + f / G) * a.n_q_heads + g * G + f % G;
@@ -628,8 +626,7 @@ attn_prefill_lds_kernel(pf_args a) {
   const float nan = __builtin_nanf("");
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    float l = l_lane[cg] + __shfl_xor(l_lane[cg], 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum_xor32(sum_xor16(l_lane[cg]));
     const int f = f0 + cg * 16 + (lane & 15);
     if (f >= cols) continue;
     const int64_t row = static_cast<int64_t>(sq.q0 + f / G) * a.n_q_heads + g * G + f % G;
