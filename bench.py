@@ -57,7 +57,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, public specification
 # sources whose hash decides whether a committed counter summary still describes
 # the kernels: the kernel file and the headers its device code includes
 DECODE_SOURCES = ("kernels.hip", "device_common.h", "pool_internal.h")
-CASCADE_SOURCES = DECODE_SOURCES + ("prefill.hip",)
+CASCADE_SOURCES = ("cascade.hip", "device_common.h", "pool_internal.h")
 PREFILL_SOURCES = ("prefill.hip", "device_common.h", "pool_internal.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, public specification
 
@@ -470,8 +470,9 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(*traffic_key),
-            "kernel": ("paged_attention_decode_cascade (whole call: preparation, prefix multi-query kernel, "
-                       "split-K kernel, merge)" if args.cascade else "attn_mfma_kernel (split-K partition kernel)"),
+            "kernel": ("paged_attention_decode_cascade (whole call: attn_cascade_kernel over the prefix and "
+                       "suffix units, then cascade_merge_kernel)" if args.cascade
+                       else "attn_mfma_kernel (split-K partition kernel)"),
             "duration_us": round(roof_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(ideal_per_launch),
             "algorithmic_bytes": ("each group's shared prefix once, every member's own blocks, q, out, table "

@@ -472,12 +472,13 @@ attn_cascade_kernel(cs_args a) {
     kv_regs<D> kv;
     uint4 q[QPL];
   };
-  // The table entry of the load cursor's tile is read one issue ahead: the
-  // scalar load for the next tile goes out after this tile's loads, and is
-  // waited for only when that tile is issued, a consumed tile later (a scalar
-  // load waited for at once costs a memory latency per tile).
-  int next_phys = tables_entry(a.tables, ld.trow, a.max_blocks, static_cast<int64_t>(ld.j0) + ld.j);
-  auto issue = [&](stage_regs& sr, int u) __attribute__((always_inline)) {
+  // the table entry of the tile at cursor c; the caller reads it and hands it
+  // to issue (the first STAGES are read together before the ring is first
+  // filled, so the fill waits out one memory latency instead of one per tile)
+  auto entry_of = [&](const cs_cursor& c) __attribute__((always_inline)) {
+    return tables_entry(a.tables, c.trow, a.max_blocks, static_cast<int64_t>(c.j0) + c.j);
+  };
+  auto issue = [&](stage_regs& sr, int u, int phys) __attribute__((always_inline)) {
     if (ld_new && ld.sp == 1) {
       const uint4* qg = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
                                                        (static_cast<int64_t>(ld.m0) * a.n_q_heads + ld.kvh * G) * D);
@@ -487,7 +488,6 @@ attn_cascade_kernel(cs_args a) {
     }
     ld_new = false;
     const int64_t jt = ld.j0 + ld.j;
-    const int phys = next_phys;
     const bool bad = phys < 0 || phys >= a.num_blocks;
     bad_ring[u] = bad;
     phys_ring[u] = phys;
@@ -500,14 +500,22 @@ attn_cascade_kernel(cs_args a) {
       const int item = ld.item, kvh = ld.kvh;
       advance(ld);
       ld_new = ld.item != item || ld.kvh != kvh;
-      next_phys = tables_entry(a.tables, ld.trow, a.max_blocks, static_cast<int64_t>(ld.j0) + ld.j);
     }
   };
 
   if (first.sp == 0) stage_prefix(first);
   stage_regs buf[STAGES];
+  {
+    int pre[STAGES];
+    cs_cursor c = ld;
 #pragma unroll
-  for (int u = 0; u < STAGES; ++u) issue(buf[u], u);
+    for (int u = 0; u < STAGES; ++u) {
+      pre[u] = entry_of(c);
+      if (u + 1 < n_blk) advance(c);
+    }
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) issue(buf[u], u, pre[u]);
+  }
 
   // ---- consume side ----
   cs_cursor cs = first;
@@ -733,7 +741,7 @@ attn_cascade_kernel(cs_args a) {
           advance(cs);
         }
       }
-      issue(buf[u], u);
+      issue(buf[u], u, entry_of(ld));
     }
     k0 += STAGES;
   } while (k0 < n_blk);
