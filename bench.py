@@ -145,6 +145,10 @@ def parse():
     g.add_argument("--summarize-counters", metavar="DIR",
                    help="directory with pmc_<name>_FETCH_SIZE/, pmc_<name>_WRITE_SIZE/, pmc_cal_FETCH_SIZE/, "
                         "pmc_cal_WRITE_SIZE/ and their .log files")
+    g.add_argument("--summarize-activity", metavar="DIR",
+                   help="directory with act_<kind>_1/ and act_<kind>_2/ (vector-ALU and matrix-core activity "
+                        "counters of one workload per KV storage kind) and their .log files")
+    g.add_argument("--summary-kinds", default="bf16,q8_0,q4_0", help="--summarize-activity: the storage kinds")
     g.add_argument("--summary-name", default="", help="<name> of the pmc_<name>_* runs")
     g.add_argument("--summary-workload", default="", help="workload name of hbm_traffic_<workload>.json")
     g.add_argument("--summary-kernels", default="attn_mfma_kernel,merge_sk_kernel",
@@ -179,6 +183,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_activity:
+        summarize_activity(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -953,8 +960,8 @@ def summary_command():
     import shlex
     args = sys.argv[1:]
     for i, x in enumerate(args[:-1]):
-        if x in ("--summarize-counters", "--summarize-trace"):
-            args[i + 1] = "<dir>" if x == "--summarize-counters" else "<out>"
+        if x in ("--summarize-counters", "--summarize-trace", "--summarize-activity"):
+            args[i + 1] = "<out>" if x == "--summarize-trace" else "<dir>"
     return "python3 bench.py " + " ".join(shlex.quote(x) for x in args)
 
 
@@ -1031,6 +1038,60 @@ def summarize_counters(a):
     with open(out_md, "w") as f:
         f.write("\n".join(md) + "\n")
     print(out_json)
+    print(out_md)
+
+
+ACTIVITY_PASSES = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_WAVE_CYCLES SQ_BUSY_CYCLES",
+                   "SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VMEM")
+
+
+def summarize_activity(a):
+    """--summarize-activity: per storage kind, two rocprofv3 --pmc passes of the
+    same bench command (ACTIVITY_PASSES) -> a markdown table in profiles/:
+    vector-ALU and matrix instructions per 16-token tile of the split-K kernel,
+    and the shares of the waves' cycles spent issuing vector-ALU instructions
+    and waiting."""
+    d = a.summarize_activity
+    rows_md = []
+    for kind in a.summary_kinds.split(","):
+        per = {}
+        n_disp = None
+        for i in (1, 2):
+            vals = {}
+            for r in read_csv_rows(find_csv(os.path.join(d, f"act_{kind}_{i}"), "counter_collection.csv")):
+                if short_kernel_name(r["Kernel_Name"]) != "attn_mfma_kernel":
+                    continue
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            for c, v in vals.items():
+                per[c] = sum(v) / len(v)
+                n_disp = len(v)
+        line = bench_line(os.path.join(d, f"act_{kind}_1.log"))
+        cfg = line["config"]
+        tiles = cfg["sequences"] * cfg["context_tokens_first_step"] / 16 * 8  # 8 kv heads
+        wps = 1 if kind == "bf16" else 2
+        valu_share = per["SQ_ACTIVE_INST_VALU"] / per["SQ_WAVE_CYCLES"]
+        rows_md.append(f"| {kind} | {n_disp} | {per['SQ_INSTS_VALU'] / tiles:.1f} | {per['SQ_INSTS_MFMA'] / tiles:.1f} | "
+                       f"{valu_share:.3f} | {wps} | {valu_share * wps:.2f} | "
+                       f"{per['SQ_WAIT_INST_ANY'] / per['SQ_WAVE_CYCLES']:.3f} | {line['attn_kernel_us']} |")
+    bench_args = a.summary_command
+    md = [f"# Vector-ALU and matrix-core activity: {a.summary_title}", "",
+          "Commands (from the repository root; two passes per storage kind <kind>, each a run of its own):", "",
+          "```"]
+    for kind in a.summary_kinds.split(","):
+        for i, pas in enumerate(ACTIVITY_PASSES, 1):
+            md.append(f"timeout -s KILL 200 rocprofv3 --pmc {pas} --output-format csv -d <dir>/act_{kind}_{i} -o run "
+                      f"-- python3 bench.py {bench_args} --kv {kind} --steps 2 --warmup 1")
+    md += ["```", "", f"Summarised by `{summary_command()}` (each run's stdout in `<dir>/act_<kind>_<pass>.log`).", "",
+           "Per 16-token tile of one kv head (a wave's unit of work) in `attn_mfma_kernel`. `SQ_ACTIVE_INST_VALU` "
+           "over `SQ_WAVE_CYCLES` is the share of a wave's cycles spent issuing vector-ALU instructions; times the "
+           "waves per SIMD it estimates how busy each SIMD's vector ALU is. `SQ_WAIT_INST_ANY` over `SQ_WAVE_CYCLES` "
+           "is the share spent waiting (mostly on memory).", "",
+           "| storage | dispatches | VALU instructions per tile | MFMA per tile | VALU share of wave cycles | "
+           "waves per SIMD | SIMD VALU busy (est.) | waiting share | kernel us (this run) |",
+           "|---|---|---|---|---|---|---|---|---|"] + rows_md
+    out_md = os.path.join(ROOT, "profiles", f"{a.summary_file}.md")
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
     print(out_md)
 
 
