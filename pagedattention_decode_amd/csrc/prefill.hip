@@ -130,17 +130,19 @@ struct v_tail_mask {
 //      k = 8q + i is token 4q + i of the first block for i < 4 and token
 //      4q + i - 4 of the second for i >= 4 (the order of kv_pair::v), so the B
 //      operand is the two blocks' P^T operands side by side.
-// MASKED: `lim_a`, `lim_b` (per lane and group) are the numbers of leading
-// slots of each block visible to the lane's column; otherwise every slot of
-// both blocks is visible to every column.  V tails beyond the context are
-// already zero.
+// masked (wave uniform): `lim_a`, `lim_b` (per lane and group) are the
+// numbers of leading slots of each block visible to the lane's column;
+// otherwise every slot of both blocks is visible to every column.  V tails
+// beyond the context are already zero.  (One instance serves both cases, so
+// that the accumulators live in one set of registers: with two, the compiler
+// moved all of them from one set to the other after every pair.)
 // The operands come from callbacks, so that a caller holding the pair in LDS
 // reads each piece only when its matrix instructions need it:
 //   qop(cg, kk)        the Q^T operand of column group cg, k-step kk;
 //   kop(kk, ka, kb)    the K operands of k-step kk of both blocks;
 //   vop(pp, v0, v1)    the V operands of d-tiles 2 pp and 2 pp + 1 (tails masked).
-template <int D, int NCG, bool MASKED, class QOp, class KOp, class VOp>
-__device__ __forceinline__ void attend_pair(const QOp& qop, const KOp& kop, const VOp& vop, const int* lim_a,
+template <int D, int NCG, class QOp, class KOp, class VOp>
+__device__ __forceinline__ void attend_pair(const QOp& qop, const KOp& kop, const VOp& vop, bool masked, const int* lim_a,
                                             const int* lim_b, int quad, float c, f32x4_t (&o)[NCG][D / 16],
                                             float* m_run, float* l_lane) {
   f32x4_t sa[NCG], sb[NCG];
@@ -164,7 +166,7 @@ __device__ __forceinline__ void attend_pair(const QOp& qop, const KOp& kop, cons
   bool grow_any = false;
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    if (MASKED) {
+    if (masked) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (quad * 4 + i >= lim_a[cg]) sa[cg][i] = -INFINITY;
@@ -191,16 +193,15 @@ __device__ __forceinline__ void attend_pair(const QOp& qop, const KOp& kop, cons
   bf16x8_t pop[NCG];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
-    const float nm = -m_run[cg];
+    // a masked slot has s = -inf and weight 2^-inf = 0.  A column that has
+    // seen no visible key yet keeps m = -inf; it is offset by 0 instead (its
+    // slots are all masked then, as any visible one would have raised m)
+    const float nm = m_run[cg] == -INFINITY ? 0.f : -m_run[cg];
     float pa[4], pb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pa[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[cg][i], c, nm));
       pb[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[cg][i], c, nm));
-      if (MASKED) {  // a column that has seen no visible key keeps m = -inf
-        pa[i] = sa[cg][i] == -INFINITY ? 0.f : pa[i];
-        pb[i] = sb[cg][i] == -INFINITY ? 0.f : pb[i];
-      }
     }
     l_lane[cg] += ((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pb[0] + pb[1]) + (pb[2] + pb[3]));
     const bf16x2_t p0 = __builtin_convertvector((f32x2_t{pa[0], pa[1]}), bf16x2_t);
@@ -370,8 +371,10 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
           v0 = vm.apply(buf[u].v[2 * pp]);
           v1 = vm.apply(buf[u].v[2 * pp + 1]);
         };
+        // (two specialised steps here: this kernel streams from HBM, and with
+        // one step the compiler placed the ring's waits earlier)
         if (valid_a == 16 && valid_b == 16 && b * 16 + 31 <= pos_min) {
-          attend_pair<D, NCG, false>(qop, kop, vop, nullptr, nullptr, quad, c, o, m_run, l_lane);
+          attend_pair<D, NCG>(qop, kop, vop, false, nullptr, nullptr, quad, c, o, m_run, l_lane);
         } else {
           int lim_a[NCG], lim_b[NCG];
 #pragma unroll
@@ -379,7 +382,7 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
             lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
             lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
           }
-          attend_pair<D, NCG, true>(qop, kop, vop, lim_a, lim_b, quad, c, o, m_run, l_lane);
+          attend_pair<D, NCG>(qop, kop, vop, true, lim_a, lim_b, quad, c, o, m_run, l_lane);
         }
       }
       issue(u, b + 2 * STAGES);
@@ -600,23 +603,24 @@ attn_prefill_lds_kernel(pf_args a) {
         ka = make_uint4(x[0], x[1], x[2], x[3]);
         kb = make_uint4(y[0], y[1], y[2], y[3]);
       };
+      // (the operands regroup the two blocks' halves, so the registers are
+      // written anyway: the tail mask costs nothing extra.  The slot is read
+      // through the same pointer type the copies write, or the compiler makes
+      // the reads wait for every copy in flight)
       auto vop = [&](int pp, uint4& v0, uint4& v1) __attribute__((always_inline)) {
         const u32x4_t va = sl[(2 * (D / 32) + pp) * 64 + lane];
         const u32x4_t vb = sl[(3 * (D / 32) + pp) * 64 + lane];
         v0 = vm.apply(make_uint4(va[0], va[1], vb[0], vb[1]));
         v1 = vm.apply(make_uint4(va[2], va[3], vb[2], vb[3]));
       };
-      if (valid_a == 16 && valid_b == 16 && b * 16 + 31 <= pos_min) {
-        attend_pair<D, NCG, false>(qop, kop, vop, nullptr, nullptr, quad, c, o, m_run, l_lane);
-      } else {
-        int lim_a[NCG], lim_b[NCG];
+      const bool masked = valid_a < 16 || valid_b < 16 || b * 16 + 31 > pos_min;
+      int lim_a[NCG], lim_b[NCG];
 #pragma unroll
-        for (int cg = 0; cg < NCG; ++cg) {
-          lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
-          lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
-        }
-        attend_pair<D, NCG, true>(qop, kop, vop, lim_a, lim_b, quad, c, o, m_run, l_lane);
+      for (int cg = 0; cg < NCG; ++cg) {
+        lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
+        lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
       }
+      attend_pair<D, NCG>(qop, kop, vop, masked, lim_a, lim_b, quad, c, o, m_run, l_lane);
     }
   }
   // the last copies (repeats nobody reads) must land before the workgroup's LDS is released
