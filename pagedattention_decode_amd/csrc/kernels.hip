@@ -465,24 +465,36 @@ template <int D, int FMT>
 __device__ __forceinline__ void attend_qblock(const kv_regs<D>& cur, const kv_qregs<D, FMT>& raw,
                                               const bf16x8_t* qop, int valid, int quad, float scale_log2,
                                               f32x4_t* o, float& m_run, float& l_lane) {
+  // the scores come out code_unit^-1 times too large (the tiles hold codes in
+  // units of code_unit); that power of two goes into the softmax scale, so
+  // each product is one mixed-precision fma on the half scale
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {  // one group of 32 dims per instruction
     const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk],
                                                                f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(scale_at<D>(raw.ks, i, kk) * code_unit<FMT>(), t[i], s[i]);
+    for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(scale_at<D>(raw.ks, i, kk), t[i], s[i]);
   }
   float pv[4];
-  softmax_step<D>(s, valid, quad, scale_log2, o, m_run, l_lane, pv);
+  softmax_step<D>(s, valid, quad, scale_log2 * code_unit<FMT>(), o, m_run, l_lane, pv);
   l_lane += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-  // O^T += V^T . (P * sV)^T, one weight operand per group; masked slots get
-  // weight 0 by selection (their scales and codes may be anything)
+  // O^T += V^T . (P * sV)^T, one weight operand per group.  The weight is one
+  // mixed-precision fma (p * code_unit) * sV + 0; a masked slot (only in a
+  // partial tile) gets weight 0 by selection, as its scale and codes may be
+  // anything
+  float pu[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pu[i] = pv[i] * code_unit<FMT>();
 #pragma unroll
   for (int pp = 0; pp < D / 32; ++pp) {
     float w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pv[i] == 0.f ? 0.f : pv[i] * (scale_at<D>(raw.vs, i, pp) * code_unit<FMT>());
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_fmaf(scale_at<D>(raw.vs, i, pp), pu[i], 0.f);
+    if (valid < 16) {  // wave uniform
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = pv[i] == 0.f ? 0.f : w[i];
+    }
     const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])));
     const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
     o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop, o[2 * pp],
