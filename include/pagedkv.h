@@ -105,7 +105,7 @@ typedef struct {
  * (T + d) bytes.  Codes sit per matrix-core lane L = 16 q + r (q < 4, r < 16),
  * which owns the d * bits / 32 bytes at L * d * bits / 32:
  *     K, lane (q, r): slot r, dims 32 k + 8 q + j (k < d/32, j < 8) at
- *         q8_0 byte 8 k + j; q4_0 byte 4 k + j/2, low nibble for even j;
+ *         q8_0 byte 8 k + j; q4_0 byte 4 k + j % 4, low nibble for j < 4;
  *     V, lane (q, r): dim 16 t + r of slots 4 q + i (t < d/16, i < 4) at
  *         q8_0 byte 4 t + i; q4_0 byte 4 (t/2) + i, low nibble for even t.
  * q8_0 codes are two's-complement bytes, q4_0 codes are stored as c + 8.

@@ -149,18 +149,22 @@ __device__ __forceinline__ void zero_v_tail(kv_regs<D>& cur, int valid, int quad
 // Online-softmax step on the 4 scores s of the lane's tokens quad*4 + i:
 // masks the slots past `valid`, raises the running maximum when a score
 // exceeds it by more than the slack (rescaling l and O), and returns the
-// weights 2^(s * scale_log2 - m_run) (0 for masked slots).
+// weights 2^(s * scale_log2 - m_run) (0 for masked slots).  scale_log2 > 0
+// (the callers reject other scales), so the maximum of the scaled scores is
+// the scaled maximum; a full block (valid = 16) needs no slot test.
 template <int D>
 __device__ __forceinline__ void softmax_step(const f32x4_t& s, int valid, int quad, float scale_log2, f32x4_t* o,
                                              float& m_run, float& l_lane, float (&pv)[4]) {
-  float sv[4];
-  float mb = -INFINITY;
+  float sm[4] = {s[0], s[1], s[2], s[3]};
+  if (valid < 16) {  // wave uniform; the empty asm keeps this a branch, not per-slot selects
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sv[i] = (quad * 4 + i < valid) ? s[i] * scale_log2 : -INFINITY;
-    mb = fmaxf(mb, sv[i]);
+    for (int i = 0; i < 4; ++i) {
+      sm[i] = quad * 4 + i < valid ? sm[i] : -INFINITY;
+      asm volatile("" : "+v"(sm[i]));
+    }
   }
-  mb = max_xor32(max_xor16(mb));
+  float mb = fmaxf(fmaxf(-INFINITY, fmaxf(sm[0], sm[1])), fmaxf(sm[2], sm[3]));
+  mb = max_xor32(max_xor16(mb)) * scale_log2;
   const bool grow = mb > m_run + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch
     const float m_new = grow ? mb : m_run;
@@ -170,8 +174,11 @@ __device__ __forceinline__ void softmax_step(const f32x4_t& s, int valid, int qu
     for (int i = 0; i < D / 16; ++i) o[i] *= alpha;
     m_run = m_new;
   }
+  // a masked slot (-inf) gets 2^-inf = 0; while m_run is still -inf every
+  // slot of the column is masked and the offset 0 keeps that finite
+  const float nm = m_run == -INFINITY ? 0.f : -m_run;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pv[i] = (sv[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_run);
+  for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm[i], scale_log2, nm));
 }
 
 template <int D>
@@ -216,7 +223,7 @@ __device__ __forceinline__ void attend_block(kv_regs<D>& cur, const bf16x8_t* qo
 // halves ([slot][group]).  Codes are arranged per MFMA lane: lane l = 16 q + r
 // owns D*bits/32 contiguous bytes at l * D*bits/32.
 //   K, lane (q, r): token r, dims 32 kk + 8 q + j (kk < D/32, j < 8);
-//     q8: byte 8 kk + j; q4: byte 4 kk + j/2, nibble j % 2 (low = even j).
+//     q8: byte 8 kk + j; q4: byte 4 kk + j % 4, nibble j / 4 (low = j < 4).
 //   V, lane (q, r): dim 16 t + r of tokens 4 q + i (t < D/16, i < 4);
 //     q8: byte 4 t + i; q4: byte 4 (t/2) + i, nibble t % 2.
 // A q8 code is stored as a two's-complement byte, a q4 code as code + 8.
@@ -302,55 +309,61 @@ __device__ __forceinline__ float sbyte_f32(uint32_t w, int k) {
   return static_cast<float>(static_cast<signed char>(w >> (8 * k)));
 }
 
-// Value of one code unit in the operand tiles below: q8_0 tiles hold the codes
-// c, q4_0 tiles hold 16 c (a nibble placed in the top of a byte), so the
-// scale applied to a tile's products is s * kCodeUnit.
-template <int FMT>
-constexpr float code_unit() { return FMT == kFmtQ4 ? 1.f / 16.f : 1.f; }
+// q4_0 operands carry a bias: the nibble u = c + 8 becomes the bf16 value
+// 128 + u = c + kQ4Bias (bit pattern 0x4300 | u, exact), so that one byte
+// permute makes two operand values.  The attention step removes the bias:
+// for K through the accumulator the products start from (-kQ4Bias times the
+// group's query sum), for V by a second product with the constant operand
+// -kQ4Bias (bf16 0xc308) on the same weights.
+constexpr float kQ4Bias = 136.f;
+constexpr uint32_t kQ4NegBiasPair = 0xc308c308u;
+
+// bf16 pair (128 + b0, 128 + b1) of bytes b0 = bytes[sel], b1 = bytes[sel + 1]
+// (each < 16): the permute takes 0x43 from its first operand for the high
+// byte of each half.
+template <int SEL>
+__device__ __forceinline__ uint32_t q4_pair(uint32_t bytes) {
+  constexpr uint32_t sel = 0x04000400u | static_cast<uint32_t>(SEL) | (static_cast<uint32_t>(SEL + 1) << 16);
+  return __builtin_amdgcn_perm(0x43434343u, bytes, sel);
+}
 
 // The codes of a raw block as the bf16 operand tiles of the decode kernel,
 // exact (integers of at most 8 significant bits).  q8_0: each two's-complement
-// byte converts directly.  q4_0: nibbles hold c + 8; flipping their top bit
-// gives c as a 4-bit two's complement, and moving it to the top of a byte
-// gives the signed byte 16 c; the factor 16 goes into the scale (code_unit).
+// byte converts directly.  q4_0: the low and the high nibbles of the four
+// bytes of a word, spread into bytes, give four bias pairs each (above).
 // The scales themselves are applied in float32 by the attention step.
 template <int D, int FMT>
 __device__ __forceinline__ void codes_block(const kv_qregs<D, FMT>& r, kv_regs<D>& out) {
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
-    float v[8];
     if constexpr (FMT == kFmtQ8) {
+      float v[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         v[k] = sbyte_f32(r.kc[2 * kk], k);
         v[4 + k] = sbyte_f32(r.kc[2 * kk + 1], k);
       }
+      out.k[kk] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                             pack_bf16x2(v[6], v[7]));
     } else {
-      const uint32_t x = r.kc[kk] ^ 0x88888888u;
-      const uint32_t lo = (x << 4) & 0xf0f0f0f0u;  // j = 0, 2, 4, 6
-      const uint32_t hi = x & 0xf0f0f0f0u;         // j = 1, 3, 5, 7
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[2 * k] = sbyte_f32(lo, k);
-        v[2 * k + 1] = sbyte_f32(hi, k);
-      }
+      const uint32_t lo = r.kc[kk] & 0x0f0f0f0fu;         // j = 0 .. 3
+      const uint32_t hi = (r.kc[kk] >> 4) & 0x0f0f0f0fu;  // j = 4 .. 7
+      out.k[kk] = make_uint4(q4_pair<0>(lo), q4_pair<2>(lo), q4_pair<0>(hi), q4_pair<2>(hi));
     }
-    out.k[kk] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                           pack_bf16x2(v[6], v[7]));
   }
   // V: tile t gives the 16x16x16 operand of dims 16 t + r for the lane's 4 tokens
   uint32_t half_words[D / 16][2];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    uint32_t bytes;
     if constexpr (FMT == kFmtQ8) {
-      bytes = r.vc[t];
+      const uint32_t bytes = r.vc[t];
+      half_words[t][0] = pack_bf16x2(sbyte_f32(bytes, 0), sbyte_f32(bytes, 1));
+      half_words[t][1] = pack_bf16x2(sbyte_f32(bytes, 2), sbyte_f32(bytes, 3));
     } else {
-      const uint32_t x = r.vc[t >> 1] ^ 0x88888888u;
-      bytes = (t & 1) ? (x & 0xf0f0f0f0u) : ((x << 4) & 0xf0f0f0f0u);
+      const uint32_t bytes = (t & 1) ? ((r.vc[t >> 1] >> 4) & 0x0f0f0f0fu) : (r.vc[t >> 1] & 0x0f0f0f0fu);
+      half_words[t][0] = q4_pair<0>(bytes);
+      half_words[t][1] = q4_pair<2>(bytes);
     }
-    half_words[t][0] = pack_bf16x2(sbyte_f32(bytes, 0), sbyte_f32(bytes, 1));
-    half_words[t][1] = pack_bf16x2(sbyte_f32(bytes, 2), sbyte_f32(bytes, 3));
   }
 #pragma unroll
   for (int pp = 0; pp < D / 32; ++pp)

@@ -167,7 +167,8 @@ __global__ void __launch_bounds__(256) quantize_cache_kernel(const uint16_t* __r
       } else {
         uint32_t w = 0u;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w |= static_cast<uint32_t>(static_cast<int>(c[q * 8 + j]) + 8) << (4 * j);
+        for (int j = 0; j < 8; ++j)
+          w |= static_cast<uint32_t>(static_cast<int>(c[q * 8 + j]) + 8) << (8 * (j % 4) + 4 * (j / 4));
         *reinterpret_cast<uint32_t*>(dst + grp * 4) = w;
       }
     }
@@ -461,36 +462,35 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(attn_args a) {
 //   O      += sum_r  p(r) * sV(r, g) * codes_V(r, dims of group g),
 // so the only rounding beyond float32 is that of the weight p * sV to bf16
 // (the unquantised path rounds p alone).  l sums the unrounded weights.
+// q4_0 tiles hold code + kQ4Bias: kbias[kk] (-kQ4Bias times the sum of the
+// query over group kk, per column) starts each score product, and every V
+// product is followed by one with the constant -kQ4Bias on the same weights,
+// so both cancel within the tile (products of bf16 values are exact, the
+// accumulation is float32).  q8_0 passes zeros.
 template <int D, int FMT>
 __device__ __forceinline__ void attend_qblock(const kv_regs<D>& cur, const kv_qregs<D, FMT>& raw,
-                                              const bf16x8_t* qop, int valid, int quad, float scale_log2,
-                                              f32x4_t* o, float& m_run, float& l_lane) {
-  // the scores come out code_unit^-1 times too large (the tiles hold codes in
-  // units of code_unit); that power of two goes into the softmax scale, so
+                                              const bf16x8_t* qop, const f32x4_t* kbias, int valid, int quad,
+                                              float scale_log2, f32x4_t* o, float& m_run, float& l_lane) {
   // each product is one mixed-precision fma on the half scale
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {  // one group of 32 dims per instruction
     const f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[kk]), qop[kk],
-                                                               f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                                                               kbias[kk], 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = __builtin_fmaf(scale_at<D>(raw.ks, i, kk), t[i], s[i]);
   }
   float pv[4];
-  softmax_step<D>(s, valid, quad, scale_log2 * code_unit<FMT>(), o, m_run, l_lane, pv);
+  softmax_step<D>(s, valid, quad, scale_log2, o, m_run, l_lane, pv);
   l_lane += (pv[0] + pv[1]) + (pv[2] + pv[3]);
   // O^T += V^T . (P * sV)^T, one weight operand per group.  The weight is one
-  // mixed-precision fma (p * code_unit) * sV + 0; a masked slot (only in a
-  // partial tile) gets weight 0 by selection, as its scale and codes may be
-  // anything
-  float pu[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pu[i] = pv[i] * code_unit<FMT>();
+  // mixed-precision fma p * sV + 0; a masked slot (only in a partial tile)
+  // gets weight 0 by selection, as its scale and codes may be anything
 #pragma unroll
   for (int pp = 0; pp < D / 32; ++pp) {
     float w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = __builtin_fmaf(scale_at<D>(raw.vs, i, pp), pu[i], 0.f);
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_fmaf(scale_at<D>(raw.vs, i, pp), pv[i], 0.f);
     if (valid < 16) {  // wave uniform
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = pv[i] == 0.f ? 0.f : w[i];
@@ -501,6 +501,11 @@ __device__ __forceinline__ void attend_qblock(const kv_regs<D>& cur, const kv_qr
                                                           0, 0, 0);
     o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[1]), pop,
                                                               o[2 * pp + 1], 0, 0, 0);
+    if constexpr (FMT == kFmtQ4) {
+      const s16x4_t nb = __builtin_bit_cast(s16x4_t, make_uint2(kQ4NegBiasPair, kQ4NegBiasPair));
+      o[2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nb, pop, o[2 * pp], 0, 0, 0);
+      o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nb, pop, o[2 * pp + 1], 0, 0, 0);
+    }
   }
 }
 
@@ -817,6 +822,9 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
   int unit_idx = 0;   // index of the current unit within the run
   int seg_j0 = first.j;
   bf16x8_t qop[D / 32];
+  f32x4_t kbias[D / 32];  // q4_0: the score accumulators' start (zeros otherwise)
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) kbias[kk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // queries of the idx-th unit of the run: always read from LDS (a unit past
   // the staged ones is first copied into the slot of an earlier, finished
   // unit), so the query registers never wait on global loads in the loop
@@ -834,6 +842,18 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
       qop[kk] = *reinterpret_cast<const bf16x8_t*>(q_wave + slot * G * D + hg * D + kk * 32 + quad * 8);
+    if constexpr (FMT == kFmtQ4) {  // -kQ4Bias times the query's sum over each group (all four quads)
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const uint4 w = __builtin_bit_cast(uint4, qop[kk]);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        float part = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) part += __uint_as_float(ws[k] << 16) + __uint_as_float(ws[k] & 0xffff0000u);
+        const float b = -kQ4Bias * sum_xor32(sum_xor16(part));
+        kbias[kk] = f32x4_t{b, b, b, b};
+      }
+    }
   };
   fetch_q(0);
 
@@ -894,7 +914,7 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
         } else {
           kv_regs<D> tile;
           codes_block<D, FMT>(buf[u], tile);
-          attend_qblock<D, FMT>(tile, buf[u], qop, valid, quad, a.scale_log2, o, m_run, l_lane);
+          attend_qblock<D, FMT>(tile, buf[u], qop, kbias, valid, quad, a.scale_log2, o, m_run, l_lane);
         }
         if (cs.j == cs.nb - 1 || k == n_blk - 1) {  // end of this unit's run
           finish();

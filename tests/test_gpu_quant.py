@@ -61,8 +61,8 @@ def decode_tiles(raw, fmt, num_blocks, hkv, d):
                     if bits == 8:
                         k[:, :, r, dim] = lane[..., 8 * kk + j].astype(np.int8)
                     else:
-                        byte = lane[..., 4 * kk + j // 2]
-                        nib = (byte >> 4) if j % 2 else (byte & 0x0F)
+                        byte = lane[..., 4 * kk + j % 4]
+                        nib = (byte >> 4) if j >= 4 else (byte & 0x0F)
                         k[:, :, r, dim] = nib.astype(np.int16) - 8
             # V: lane (q, r) holds dim 16 t + r of tokens 4 q + i
             for t in range(d // 16):
