@@ -625,13 +625,13 @@ attn_cascade_kernel(cs_args a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t >= ntiles) continue;
-      mb[t] = max_xor16(fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
+      mb[t] = maxn_xor16(maxn(maxn3(sc[t][0], sc[t][1], sc[t][2]), sc[t][3]));
     }
     bool grow_any = false;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t >= ntiles) continue;
-      mb[t] = max_xor32(mb[t]) * a.scale_log2;
+      mb[t] = maxn_xor32(mb[t]) * a.scale_log2;
       grow_any |= mb[t] > m_run[t] + kRescaleSlack;
     }
     // one wave-uniform branch for every column tile's rescale (rare: the

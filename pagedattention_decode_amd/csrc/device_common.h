@@ -36,6 +36,21 @@ __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// The same maxima with NaN-propagating semantics: gfx950's v_maximum3_f32
+// takes its inputs as they are, where fmaxf (NaN-ignoring) first quiets every
+// input that is not known to be canonical (matrix-core results, lane swaps) with
+// one more instruction each.  For softmax maxima over scores, where a NaN score
+// poisons its row through the weights anyway.
+__device__ __forceinline__ float maxn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float maxn3(float a, float b, float c) { return maxn(maxn(a, b), c); }
+__device__ __forceinline__ float maxn_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return maxn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float maxn_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return maxn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float sum_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -163,8 +178,8 @@ __device__ __forceinline__ void softmax_step(const f32x4_t& s, int valid, int qu
       asm volatile("" : "+v"(sm[i]));
     }
   }
-  float mb = fmaxf(fmaxf(-INFINITY, fmaxf(sm[0], sm[1])), fmaxf(sm[2], sm[3]));
-  mb = max_xor32(max_xor16(mb)) * scale_log2;
+  float mb = maxn(maxn3(sm[0], sm[1], sm[2]), sm[3]);
+  mb = maxn_xor32(maxn_xor16(mb)) * scale_log2;
   const bool grow = mb > m_run + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch
     const float m_new = grow ? mb : m_run;

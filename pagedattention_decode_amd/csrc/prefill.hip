@@ -173,9 +173,9 @@ __device__ __forceinline__ void attend_pair(const QOp& qop, const KOp& kop, cons
         if (quad * 4 + i >= lim_b[cg]) sb[cg][i] = -INFINITY;
       }
     }
-    float m = fmaxf(fmaxf(fmaxf(sa[cg][0], sa[cg][1]), fmaxf(sa[cg][2], sa[cg][3])),
-                    fmaxf(fmaxf(sb[cg][0], sb[cg][1]), fmaxf(sb[cg][2], sb[cg][3])));
-    m = max_xor32(max_xor16(m));
+    float m = maxn3(maxn3(sa[cg][0], sa[cg][1], sa[cg][2]), maxn3(sa[cg][3], sb[cg][0], sb[cg][1]),
+                    maxn(sb[cg][2], sb[cg][3]));
+    m = maxn_xor32(maxn_xor16(m));
     mb[cg] = m * c;
     grow_any |= mb[cg] > m_run[cg] + kRescaleSlack;
   }
@@ -532,6 +532,7 @@ attn_prefill_lds_kernel(pf_args a) {
   typedef const __attribute__((address_space(4))) int32_t ctable_t;
   ctable_t* trow = (ctable_t*)(a.tables + static_cast<int64_t>(a.table_rows ? a.table_rows[s] : s) * a.max_blocks);
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   extern __shared__ __align__(16) u32x4_t pf_kv_lds[];
   u32x4_t* ring = pf_kv_lds + grp * S * (kChunks * 64);  // this group's S slots
 
@@ -576,6 +577,13 @@ attn_prefill_lds_kernel(pf_args a) {
   bool poisoned = false;
   const float c = a.scale_log2;
   auto qop = [&](int cg, int kk) __attribute__((always_inline)) { return qreg[cg][kk]; };
+  // The V operands of a pair take the two blocks' halves side by side, so
+  // each lane reads them as four 8-byte pieces straight into place.  The high
+  // halves go through an offset of 8 that the compiler cannot see through;
+  // otherwise it merges each two 8-byte reads back into one 16-byte read and
+  // then moves the halves into the operands with one instruction per dword.
+  int hi8;
+  asm("v_mov_b32 %0, 8" : "=v"(hi8));
 
 #pragma unroll
   for (int kp = 0; kp < S - 1; ++kp) copy_pair(kp);
@@ -595,7 +603,8 @@ attn_prefill_lds_kernel(pf_args a) {
       poisoned |= bad_a || (has_b && bad_b);
       const int valid_a = bad_a ? 0 : min(16, sq.n - b * 16);
       const int valid_b = (!has_b || bad_b) ? 0 : min(16, sq.n - (b + 1) * 16);
-      const v_tail_mask vm(valid_a, valid_b, quad);
+      // only a pair reaching past the context has V slots to clear
+      const bool vtail = valid_a < 16 || valid_b < 16;
       // operands read from the slot when the matrix instructions need them
       auto kop = [&](int kk, uint4& ka, uint4& kb) __attribute__((always_inline)) {
         const u32x4_t x = sl[(0 * (D / 32) + kk) * 64 + lane];
@@ -603,15 +612,27 @@ attn_prefill_lds_kernel(pf_args a) {
         ka = make_uint4(x[0], x[1], x[2], x[3]);
         kb = make_uint4(y[0], y[1], y[2], y[3]);
       };
-      // (the operands regroup the two blocks' halves, so the registers are
-      // written anyway: the tail mask costs nothing extra.  The slot is read
-      // through the same pointer type the copies write, or the compiler makes
-      // the reads wait for every copy in flight)
+      // (the slot is read through the same pointer type the copies write, or
+      // the compiler makes the reads wait for every copy in flight.  The tail
+      // branch is wave uniform; the empty asm keeps it a branch rather than
+      // per-dword selects on every pair)
       auto vop = [&](int pp, uint4& v0, uint4& v1) __attribute__((always_inline)) {
-        const u32x4_t va = sl[(2 * (D / 32) + pp) * 64 + lane];
-        const u32x4_t vb = sl[(3 * (D / 32) + pp) * 64 + lane];
-        v0 = vm.apply(make_uint4(va[0], va[1], vb[0], vb[1]));
-        v1 = vm.apply(make_uint4(va[2], va[3], vb[2], vb[3]));
+        const char* va = reinterpret_cast<const char*>(sl + (2 * (D / 32) + pp) * 64 + lane);
+        const char* vb = reinterpret_cast<const char*>(sl + (3 * (D / 32) + pp) * 64 + lane);
+        const u32x2_t a0 = *reinterpret_cast<const u32x2_t*>(va), b0 = *reinterpret_cast<const u32x2_t*>(vb);
+        const u32x2_t a1 = *reinterpret_cast<const u32x2_t*>(va + hi8);
+        const u32x2_t b1 = *reinterpret_cast<const u32x2_t*>(vb + hi8);
+        v0 = make_uint4(a0[0], a0[1], b0[0], b0[1]);
+        v1 = make_uint4(a1[0], a1[1], b1[0], b1[1]);
+        if (vtail) {
+          int va_n = valid_a, vb_n = valid_b;  // defined here, so the mask's compares stay in the branch
+          asm volatile("" : "+s"(va_n), "+s"(vb_n));
+          const v_tail_mask vm(va_n, vb_n, quad);
+          v0 = vm.apply(v0);
+          v1 = vm.apply(v1);
+          asm volatile("" : "+v"(v0.x), "+v"(v0.y), "+v"(v0.z), "+v"(v0.w));
+          asm volatile("" : "+v"(v1.x), "+v"(v1.y), "+v"(v1.z), "+v"(v1.w));
+        }
       };
       const bool masked = valid_a < 16 || valid_b < 16 || b * 16 + 31 > pos_min;
       int lim_a[NCG], lim_b[NCG];
