@@ -82,6 +82,7 @@ struct cs_args {
   int acol;                // columns of a prefix unit's partial rows (column tiles x 16)
   int wa, wb, wu;          // work-split cost of a prefix partition, a suffix partition, a unit's start
   int aslot, bslot;        // elements of a wave's prefix and suffix query slots
+  int aslot2;              // elements of a wave's second prefix slot (0: none)
   float scale_log2;
 };
 
@@ -421,8 +422,9 @@ attn_cascade_kernel(cs_args a) {
   // tile's loads -- so the wait for them is the tile's own -- and written to
   // the suffix slot when that tile is consumed.
   uint16_t* a_slot = reinterpret_cast<uint16_t*>(cs_smem + cs_lds_ints(V, n)) +
-                     static_cast<int64_t>(wave) * (a.aslot + a.bslot);
-  uint16_t* b_slot = a_slot + a.aslot;
+                     static_cast<int64_t>(wave) * (a.aslot + a.aslot2 + a.bslot);
+  uint16_t* a_slot2 = a_slot + a.aslot;  // the next prefix unit's, when a run reaches into it
+  uint16_t* b_slot = a_slot2 + a.aslot2;
   // columns sit kQStride = D + 8 elements apart: the 16 lanes of a quarter
   // wave read 16 consecutive columns, which a stride of D would put in one
   // LDS bank (a 16-way conflict on every operand read)
@@ -434,7 +436,7 @@ attn_cascade_kernel(cs_args a) {
   // all are written, so the copy waits out one memory latency.  (Copies
   // straight from global memory to LDS are avoided everywhere in this kernel:
   // the compiler would then make every LDS read wait for all loads.)
-  auto stage_prefix = [&](const cs_cursor& c) __attribute__((always_inline)) {
+  auto stage_prefix = [&](const cs_cursor& c, uint16_t* dst) __attribute__((always_inline)) {
     const uint16_t* qg = static_cast<const uint16_t*>(a.q);
     const int elems = c.cnt * G * D;  // <= NT x 16 columns
     constexpr int kPieces = NT * 16 * D / 512;
@@ -454,7 +456,7 @@ attn_cascade_kernel(cs_args a) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
       const int e = (i * 64 + lane) * 8;
-      if (e < elems) *reinterpret_cast<uint4*>(a_slot + padded(e)) = v[i];
+      if (e < elems) *reinterpret_cast<uint4*>(dst + padded(e)) = v[i];
     }
   };
 
@@ -503,7 +505,23 @@ attn_cascade_kernel(cs_args a) {
     }
   };
 
-  if (first.sp == 0) stage_prefix(first);
+  // A run that reaches from its first prefix unit into the next one stages
+  // that unit's queries too, now, while the registers are free: copied when
+  // the unit starts, they would cost one memory latency per piece, each
+  // waiting for the whole ring.
+  bool staged2 = false;
+  if (first.sp == 0) {
+    stage_prefix(first, a_slot);
+    if (a.aslot2 > 0 && (last.item != first.item || last.kvh != first.kvh)) {
+      cs_cursor c2 = first;
+      c2.j = c2.nb - 1;
+      advance(c2);  // the first tile of the next unit
+      if (c2.sp == 0) {
+        stage_prefix(c2, a_slot2);
+        staged2 = true;
+      }
+    }
+  }
   stage_regs buf[STAGES];
   {
     int pre[STAGES];
@@ -535,7 +553,10 @@ attn_cascade_kernel(cs_args a) {
     uint16_t* slot;
     if (cs.sp == 0) {
       slot = a_slot;
-      if (ua++ > 0) {
+      if (ua == 1 && staged2) {
+        slot = a_slot2;  // staged when the run started
+        ++ua;
+      } else if (ua++ > 0) {
         // a later prefix unit (rare: prefix units are long): copy its queries
         // now, piece by piece through registers, waiting for everything in
         // flight (no copy straight to LDS here: the compiler would then make
@@ -898,7 +919,7 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cs_args a) {
 // ---- host side ---------------------------------------------------------------
 
 struct cs_plan {
-  int nt, acol, mc, cpg, na, aslot, bslot, part_blocks, wa, wb, wu;
+  int nt, acol, mc, cpg, na, aslot, aslot2, bslot, part_blocks, wa, wb, wu;
   int64_t waves;
   uint64_t lds;
   uint64_t a_m, a_l, a_o, b_m, b_l, b_o, cum_parts, cum_cost, member, mdesc, total;  // workspace offsets
@@ -952,6 +973,11 @@ kv_status cs_resolve(const kv_pool* pool, int n_seqs, int n_groups, int max_grou
                                     "(pass the largest group size as max_group)");
   p.mc = mc;
   p.aslot = static_cast<int>(mc * G * stride);
+  // a second prefix slot per wave where the LDS holds it (a run reaching into
+  // a second prefix unit stages its queries at the start)
+  const int64_t lds_one = static_cast<int64_t>(cs_lds_ints(n_groups * ((nt_cap + mc - 1) / mc) + n_seqs, n_seqs)) * 4 +
+                          static_cast<int64_t>(kCsWaves) * (p.aslot + qb * p.bslot) * 2;
+  p.aslot2 = lds_one + static_cast<int64_t>(kCsWaves) * p.aslot * 2 <= lds_max ? p.aslot : 0;
   // work-split weights, in quarters of a suffix tile (one column tile): a
   // tile attended by a full chunk's ct column tiles costs about 3 + ct, the
   // start of a unit about 6
@@ -965,7 +991,7 @@ kv_status cs_resolve(const kv_pool* pool, int n_seqs, int n_groups, int max_grou
       std::numeric_limits<int32_t>::max())
     return fail(KV_ERR_UNSUPPORTED, "too many sequences x blocks for the cascade decode's plan");
   p.lds = static_cast<uint64_t>(cs_lds_ints(p.na + n_seqs, n_seqs)) * 4 +
-          static_cast<uint64_t>(kCsWaves) * (p.aslot + qb * p.bslot) * 2;
+          static_cast<uint64_t>(kCsWaves) * (p.aslot + p.aslot2 + qb * p.bslot) * 2;
   const uint64_t Hkv = c.num_kv_heads;
   const uint64_t a_rows = (static_cast<uint64_t>(p.waves) + p.na * Hkv) * p.acol;
   const uint64_t b_rows = (static_cast<uint64_t>(p.waves) + n_seqs * Hkv) * G;
@@ -1084,6 +1110,7 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   a.wb = p.wb;
   a.wu = p.wu;
   a.aslot = p.aslot;
+  a.aslot2 = p.aslot2;
   a.bslot = p.bslot;
   a.scale_log2 = p.scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
