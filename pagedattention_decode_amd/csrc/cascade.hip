@@ -86,10 +86,25 @@ struct cs_args {
   float scale_log2;
 };
 
-// LDS ints of the plan over V items (n_a prefix chunks, then n members):
-// cum_t, cum_p, cum_c (V + 1 each), ctx_n and j0 (n each), rounded up to 16
-// bytes; the staged queries follow.
-__host__ __device__ constexpr int cs_lds_ints(int V, int n) { return (3 * (V + 1) + 2 * n + 3) & ~3; }
+// LDS ints of the plan over V items (n_a prefix chunks, then n members) of
+// ng groups: cum_t, cum_p, cum_c (V + 1 each), ctx_n and j0 (n each), the
+// group starts (ng + 1), rounded up to 16 bytes; the staged queries follow.
+__host__ __device__ constexpr int cs_lds_ints(int V, int n, int ng) { return (3 * (V + 1) + 2 * n + ng + 1 + 3) & ~3; }
+
+// Sum of x over lanes 0 .. l of the wave, at lane l (every lane active): DPP
+// row shifts by 1, 2, 4 and 8 within each 16-lane row (lanes shifted in from
+// outside the row read 0), then each row adds the totals of the rows before
+// it, read from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
 
 // In place over cum_b (tiles per item on entry): exclusive prefix sums of the
 // tiles, of the partitions ceil(tiles / pb) and of the work-split cost
@@ -105,16 +120,7 @@ __device__ void cs_scan(int* cum_b, int* cum_p, int* cum_c, int n, int pb, int n
     const int t = i < n ? cum_b[i] : 0;
     const int p = (t + pb - 1) / pb;
     const int c = p > 0 ? p * (i < na ? wa : wb) + wu : 0;
-    int ib = t, ip = p, ic = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int yb = __shfl_up(ib, off), yp = __shfl_up(ip, off), yc = __shfl_up(ic, off);
-      if (lane >= off) {
-        ib += yb;
-        ip += yp;
-        ic += yc;
-      }
-    }
+    const int ib = wave_incl_scan(t), ip = wave_incl_scan(p), ic = wave_incl_scan(c);
     if (lane == 63) {
       wsum[0][wv] = ib;
       wsum[1][wv] = ip;
@@ -229,6 +235,7 @@ attn_cascade_kernel(cs_args a) {
   int* cum_c = cum_p + V + 1;    // [V + 1] work-split cost before each item, per kv head
   int* ctx_n = cum_c + V + 1;    // [n] clamped context tokens
   int* j0s = ctx_n + n;          // [n] first tile of each member's suffix (-1: NaN row)
+  int* gsl = j0s + n;            // [n_groups + 1] group starts
   __shared__ int malformed;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int Hkv = a.n_kv_heads;
@@ -255,7 +262,7 @@ attn_cascade_kernel(cs_args a) {
       j0s[s] = -1;
       ctx_n[s] = max(min(a.ctx_lens[s], cap), 0);
     }
-    if (s <= a.n_groups) gst[s] = a.group_start[s];
+    if (s <= a.n_groups) gst[s] = gsl[s] = a.group_start[s];
     if (s < a.n_groups) gS[s] = a.shared[s];
   }
   for (int v = tid; v < na; v += kCsWaves * 64) cum_t[v] = 0;  // prefix tiles per chunk
@@ -352,7 +359,7 @@ attn_cascade_kernel(cs_args a) {
     c.nb = rfl(cum_t[c.item + 1]) - rfl(cum_t[c.item]);
     if (c.item < na) {
       const int g = c.item / a.cpg, ch = c.item % a.cpg;
-      const int first = cload(a.group_start, g), end = cload(a.group_start, g + 1);
+      const int first = rfl(gsl[g]), end = rfl(gsl[g + 1]);
       c.sp = 0;
       c.trow = first;
       c.j0 = 0;
@@ -421,7 +428,7 @@ attn_cascade_kernel(cs_args a) {
   // stage of the unit's first tile), issued by the load side just before that
   // tile's loads -- so the wait for them is the tile's own -- and written to
   // the suffix slot when that tile is consumed.
-  uint16_t* a_slot = reinterpret_cast<uint16_t*>(cs_smem + cs_lds_ints(V, n)) +
+  uint16_t* a_slot = reinterpret_cast<uint16_t*>(cs_smem + cs_lds_ints(V, n, a.n_groups)) +
                      static_cast<int64_t>(wave) * (a.aslot + a.aslot2 + a.bslot);
   uint16_t* a_slot2 = a_slot + a.aslot;  // the next prefix unit's, when a run reaches into it
   uint16_t* b_slot = a_slot2 + a.aslot2;
@@ -505,6 +512,17 @@ attn_cascade_kernel(cs_args a) {
     }
   };
 
+  // the table entries of the first ring fill, read together (and before the
+  // queries are staged, so that the two memory latencies overlap)
+  int pre[STAGES];
+  {
+    cs_cursor c = ld;
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      pre[u] = entry_of(c);
+      if (u + 1 < n_blk) advance(c);
+    }
+  }
   // A run that reaches from its first prefix unit into the next one stages
   // that unit's queries too, now, while the registers are free: copied when
   // the unit starts, they would cost one memory latency per piece, each
@@ -523,17 +541,8 @@ attn_cascade_kernel(cs_args a) {
     }
   }
   stage_regs buf[STAGES];
-  {
-    int pre[STAGES];
-    cs_cursor c = ld;
 #pragma unroll
-    for (int u = 0; u < STAGES; ++u) {
-      pre[u] = entry_of(c);
-      if (u + 1 < n_blk) advance(c);
-    }
-#pragma unroll
-    for (int u = 0; u < STAGES; ++u) issue(buf[u], u, pre[u]);
-  }
+  for (int u = 0; u < STAGES; ++u) issue(buf[u], u, pre[u]);
 
   // ---- consume side ----
   cs_cursor cs = first;
@@ -964,7 +973,7 @@ kv_status cs_resolve(const kv_pool* pool, int n_seqs, int n_groups, int max_grou
   const int nt_cap = std::min(max_group, n_seqs);
   for (; mc >= 1; --mc) {
     const int na = n_groups * ((nt_cap + mc - 1) / mc);
-    const int64_t lds = static_cast<int64_t>(cs_lds_ints(na + n_seqs, n_seqs)) * 4 +
+    const int64_t lds = static_cast<int64_t>(cs_lds_ints(na + n_seqs, n_seqs, n_groups)) * 4 +
                         static_cast<int64_t>(kCsWaves) * (mc * G * stride + qb * p.bslot) * 2;
     if (lds <= lds_max) break;
   }
@@ -975,7 +984,7 @@ kv_status cs_resolve(const kv_pool* pool, int n_seqs, int n_groups, int max_grou
   p.aslot = static_cast<int>(mc * G * stride);
   // a second prefix slot per wave where the LDS holds it (a run reaching into
   // a second prefix unit stages its queries at the start)
-  const int64_t lds_one = static_cast<int64_t>(cs_lds_ints(n_groups * ((nt_cap + mc - 1) / mc) + n_seqs, n_seqs)) * 4 +
+  const int64_t lds_one = static_cast<int64_t>(cs_lds_ints(n_groups * ((nt_cap + mc - 1) / mc) + n_seqs, n_seqs, n_groups)) * 4 +
                           static_cast<int64_t>(kCsWaves) * (p.aslot + qb * p.bslot) * 2;
   p.aslot2 = lds_one + static_cast<int64_t>(kCsWaves) * p.aslot * 2 <= lds_max ? p.aslot : 0;
   // work-split weights, in quarters of a suffix tile (one column tile): a
@@ -990,7 +999,7 @@ kv_status cs_resolve(const kv_pool* pool, int n_seqs, int n_groups, int max_grou
   if (static_cast<int64_t>(p.na + n_seqs) * (static_cast<int64_t>(max_blocks) * std::max(p.wa, p.wb) + p.wu) >
       std::numeric_limits<int32_t>::max())
     return fail(KV_ERR_UNSUPPORTED, "too many sequences x blocks for the cascade decode's plan");
-  p.lds = static_cast<uint64_t>(cs_lds_ints(p.na + n_seqs, n_seqs)) * 4 +
+  p.lds = static_cast<uint64_t>(cs_lds_ints(p.na + n_seqs, n_seqs, n_groups)) * 4 +
           static_cast<uint64_t>(kCsWaves) * (p.aslot + p.aslot2 + qb * p.bslot) * 2;
   const uint64_t Hkv = c.num_kv_heads;
   const uint64_t a_rows = (static_cast<uint64_t>(p.waves) + p.na * Hkv) * p.acol;
