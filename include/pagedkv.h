@@ -389,7 +389,18 @@ typedef enum {
                             quantised pools (the codes, exact in bf16, are the
                             matrix operands and the group scales are applied in
                             float32: the result is the attention over
-                            code x scale) */
+                            code x scale) */,
+  KV_KERNEL_MFMA_STAGED_TABLE = 3 /* the matrix-core kernel (bf16, B = 16 only)
+                            with each wave's block-table entries copied into
+                            an LDS slice when its run starts (straight from
+                            global memory, one wait) and read from there per
+                            tile, instead of one scalar load per tile.  The
+                            pages describe warps that load the block pointers
+                            into shared memory or registers ([KVM]
+                            PagedAttention virtual memory model); this
+                            variant measures that choice against the scalar
+                            loads of KV_KERNEL_MFMA.  Same results, bit for
+                            bit */
 } kv_kernel;
 
 /* Optional timing of an attention call.  Each field is a hipEvent_t that

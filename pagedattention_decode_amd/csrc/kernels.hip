@@ -651,10 +651,16 @@ struct sk_cursor {
 // slots (V).  In every case a lane's 16-byte pieces of one tile are exactly its
 // matrix operands (the tile layout of the pool puts, for B >= 16, each
 // quarter-wave's 16 pieces in one 256-byte run).
-template <int D, int STAGES, int WAVES_PER_SIMD, int FMT, int BS>
+// TBL = 1 (bf16, B = 16): the block-table entries of a wave's run are copied
+// into an LDS slice of up to kSkTblMax entries when the run starts and read
+// from there per tile; 0: one scalar load per tile.
+constexpr int kSkTblMax = 2048;
+
+template <int D, int STAGES, int WAVES_PER_SIMD, int FMT, int BS, int TBL = 0>
 __global__ void __launch_bounds__(kSkWaves * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD)))
 attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ tables) {
   static_assert(FMT == kFmtBf16 || BS == 16, "quantised tiles are 16 tokens");
+  static_assert(TBL == 0 || (FMT == kFmtBf16 && BS == 16), "LDS-staged table entries: bf16, B = 16");
   static_assert(BS == 4 || BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size");
   extern __shared__ __align__(16) int sk_smem[];
   int* cum_b = sk_smem;                       // n_seqs + 1
@@ -726,8 +732,40 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     } while (c.seq < a.n_seqs - 1 && cb(c.seq + 1) == cb(c.seq));
     c.nb = cb(c.seq + 1) - cb(c.seq);
     c.n = cn(c.seq);
-    c.trow = a.table_rows ? a.table_rows[c.seq] : c.seq;
+    c.trow = a.table_rows ? ((const __attribute__((address_space(4))) int32_t*)a.table_rows)[c.seq] : c.seq;
   };
+
+  // TBL = 1: the table entries of the run's first tbl_n blocks, block k of the
+  // run at tbl_wave[k].  The lanes copy consecutive entries of each unit of
+  // the run straight from global memory into the slice (no registers), and
+  // the wave waits for them once, before the ring is first filled.
+  int* tbl_wave = nullptr;
+  int tbl_n = 0;
+  if constexpr (TBL != 0) {
+    tbl_wave = reinterpret_cast<int*>(q_s + static_cast<int64_t>(kSkWaves) * a.q_units * G * D) + wave * kSkTblMax;
+    tbl_n = min(n_blk, kSkTblMax);
+    sk_cursor c = first;
+    for (int k0 = 0; k0 < tbl_n;) {
+      const int cnt = min(c.nb - c.j, tbl_n - k0);  // the unit's blocks in the staged part of the run
+      for (int i = 0; i < cnt; i += 64) {
+        if (lane < cnt - i) {
+          if (c.trow >= 0) {
+            const int32_t* src = tables + static_cast<int64_t>(c.trow) * a.max_blocks + c.j + i + lane;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                             (__attribute__((address_space(3))) void*)(tbl_wave + k0 + i), 4, 0, 0);
+          } else {
+            tbl_wave[k0 + i + lane] = -1;  // a row without valid entries
+          }
+        }
+      }
+      k0 += cnt;
+      if (k0 < tbl_n) {
+        c.j = c.nb - 1;
+        advance(c);  // the next unit
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every counter: the copies and the stores have landed
+  }
 
   // ring entries: bf16 operand tiles, or raw quantised tiles (codes and scales) converted on use
   using ring_t = typename std::conditional<FMT == kFmtBf16, kv_regs<D>, kv_qregs<D, FMT>>::type;
@@ -759,7 +797,14 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     } else if constexpr (BS >= 16) {
       // tile j is sub-tile j % (BS/16) of entry j / (BS/16)
       constexpr int kSub = BS / 16;
-      const int phys = ld.trow >= 0 ? tables[row + ld.j / kSub] : -1;
+      // (the table through the constant address space: after the copies into
+      // LDS the compiler would otherwise turn these uniform reads into vector
+      // loads, whose waits drain the ring)
+      int phys;
+      if (TBL != 0 && ld_k < tbl_n)
+        phys = __builtin_amdgcn_readfirstlane(tbl_wave[ld_k]);
+      else
+        phys = ld.trow >= 0 ? ((const __attribute__((address_space(4))) int32_t*)tables)[row + ld.j / kSub] : -1;
       const bool bad = phys < 0 || phys >= a.num_blocks;
       bad_ring[u] = bad;
       const int p = bad ? 0 : phys;
@@ -1242,6 +1287,7 @@ constexpr int sk_stages() {
 
 struct resolved {
   int kernel;
+  bool staged_table = false;  // KV_KERNEL_MFMA_STAGED_TABLE (kernel is then KV_KERNEL_MFMA)
   int partition;   // tokens
   int max_parts;   // generic kernel: partitions of the longest context
   int64_t groups;  // split-K kernel: persistent workgroups
@@ -1258,9 +1304,18 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
   if (n_seqs < 0 || max_blocks <= 0) return fail(KV_ERR_INVALID, "n_seqs must be >= 0 and max_blocks_per_seq > 0");
   kv_attention_options o{0.f, 0, KV_KERNEL_AUTO, nullptr};
   if (opts) o = *opts;
-  if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_GENERIC && o.kernel != KV_KERNEL_MFMA)
+  if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_GENERIC && o.kernel != KV_KERNEL_MFMA &&
+      o.kernel != KV_KERNEL_MFMA_STAGED_TABLE)
     return fail(KV_ERR_INVALID, "unknown kernel selector");
+  r.staged_table = o.kernel == KV_KERNEL_MFMA_STAGED_TABLE;
+  if (r.staged_table) {
+    if (c.dtype != KV_BF16 || c.block_size != 16)
+      return fail(KV_ERR_UNSUPPORTED, "the LDS-staged table variant reads bf16 pools with B = 16");
+    o.kernel = KV_KERNEL_MFMA;
+  }
   const bool mfma_ok = decode_mfma_supported(c, G) && n_seqs <= kSkMaxSeqs && sk_q_units(n_seqs, G, c.head_dim) >= 1;
+  if (r.staged_table && (!mfma_ok || sk_lds_bytes(n_seqs, G, c.head_dim) + kSkWaves * kSkTblMax * 4 > max_lds_per_block()))
+    return fail(KV_ERR_UNSUPPORTED, "the LDS-staged table variant does not fit this call");
   if (o.kernel == KV_KERNEL_MFMA && !mfma_ok)
     return fail(KV_ERR_UNSUPPORTED,
                 "the matrix-core kernel needs bf16 with B in {4, 8, 16, 32, 64} or q8_0/q4_0 with B = 16, d in "
@@ -1306,9 +1361,16 @@ uint64_t workspace_for(const kv_pool_config& c, int n_seqs, int num_q_heads, con
 
 template <int D, int FMT, int BS = 16>
 hipError_t launch_mfma(const sk_args& a, const int32_t* ctx_lens, const int32_t* tables, int64_t groups, int G,
-                       hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+                       hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, bool staged_table = false) {
   constexpr int kStages = sk_stages<D, FMT>();
   constexpr int kWps = sk_waves_per_simd(D, FMT);
+  if constexpr (FMT == kFmtBf16 && BS == 16) {
+    if (staged_table)
+      return launch_timed(attn_mfma_kernel<D, kStages, kWps, FMT, BS, 1>, dim3(static_cast<unsigned>(groups)),
+                          dim3(kSkWaves * 64),
+                          static_cast<uint32_t>(sk_lds_bytes(a.n_seqs, G, D) + kSkWaves * kSkTblMax * 4), st, ev0,
+                          ev1, a, ctx_lens, tables);
+  }
   return launch_timed(attn_mfma_kernel<D, kStages, kWps, FMT, BS>, dim3(static_cast<unsigned>(groups)),
                       dim3(kSkWaves * 64), static_cast<uint32_t>(sk_lds_bytes(a.n_seqs, G, D)), st, ev0, ev1, a,
                       ctx_lens, tables);
@@ -1359,9 +1421,9 @@ kv_status decode_launch(const kv_pool* pool, int layer, const void* q, void* out
       constexpr int F = decltype(fmt)::value;
       constexpr int BS = decltype(bs)::value;
       switch (c.head_dim) {
-        case 64: return launch_mfma<64, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
-        case 128: return launch_mfma<128, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
-        default: return launch_mfma<256, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop);
+        case 64: return launch_mfma<64, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop, r.staged_table);
+        case 128: return launch_mfma<128, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop, r.staged_table);
+        default: return launch_mfma<256, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop, r.staged_table);
       }
     };
     using B16 = std::integral_constant<int, 16>;
