@@ -133,9 +133,11 @@ def parse():
                     help="decode through paged_attention_decode_cascade (shared prefixes read once per group)")
     ap.add_argument("--layers", type=int, default=0, help="layer buffers (0 = workload default)")
     ap.add_argument("--partition", type=int, default=-1, help="partition tokens (-1 = workload default)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "generic", "mfma_staged_table"],
+    ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "generic", "mfma_staged_table", "valu"],
                     help="mfma_staged_table: the matrix-core kernel with each wave's block-table entries staged in "
-                         "LDS (bf16, B = 16), for comparison with the scalar table reads of mfma")
+                         "LDS (bf16, B = 16), for comparison with the scalar table reads of mfma; valu: the same "
+                         "split-K kernel with vector-ALU dot products instead of matrix instructions (bf16, B = 16, "
+                         "d = 128, G = 4 or 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--seed", type=int, default=0, help="0 = the workload's seed")
@@ -227,7 +229,7 @@ def main():
     seed = args.seed or base.seed
     partition = base.partition_tokens if args.partition < 0 else args.partition
     kernel = {"auto": B.KV_KERNEL_AUTO, "mfma": B.KV_KERNEL_MFMA, "generic": B.KV_KERNEL_GENERIC,
-              "mfma_staged_table": B.KV_KERNEL_MFMA_STAGED_TABLE}[args.kernel]
+              "mfma_staged_table": B.KV_KERNEL_MFMA_STAGED_TABLE, "valu": B.KV_KERNEL_VALU}[args.kernel]
     opts = B.attention_options(partition_tokens=partition, kernel=kernel)
     Hq, Hkv, d, Bs = base.num_q_heads, base.num_kv_heads, base.head_dim, base.block_size
 

@@ -400,7 +400,16 @@ typedef enum {
                             PagedAttention virtual memory model); this
                             variant measures that choice against the scalar
                             loads of KV_KERNEL_MFMA.  Same results, bit for
-                            bit */
+                            bit */,
+  KV_KERNEL_VALU = 4     /* the same split-K kernel (runs, register ring,
+                            merge) with vector-ALU arithmetic instead of matrix
+                            instructions: v_dot2_f32_bf16 scores over each
+                            lane's dims summed by lane swaps, DPP row maxima,
+                            weights gathered across lanes and v_dot2 over token
+                            pairs for the values.  bf16, B = 16, d = 128,
+                            G = 4 or 8.  It measures whether the matrix
+                            instructions pay on a GQA group of at most 8 query
+                            rows, which the pages leave open */
 } kv_kernel;
 
 /* Optional timing of an attention call.  Each field is a hipEvent_t that

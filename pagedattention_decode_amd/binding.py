@@ -19,7 +19,7 @@ from .build import LIB_PATH
 KV_OK, KV_ERR_OOM, KV_ERR_INVALID, KV_ERR_STATE, KV_ERR_HIP, KV_ERR_UNSUPPORTED = range(6)
 KV_F32, KV_BF16, KV_Q8_0, KV_Q4_0 = 0, 1, 2, 3
 DTYPE_CODES = {"f32": KV_F32, "bf16": KV_BF16, "q8_0": KV_Q8_0, "q4_0": KV_Q4_0}
-KV_KERNEL_AUTO, KV_KERNEL_GENERIC, KV_KERNEL_MFMA, KV_KERNEL_MFMA_STAGED_TABLE = 0, 1, 2, 3
+KV_KERNEL_AUTO, KV_KERNEL_GENERIC, KV_KERNEL_MFMA, KV_KERNEL_MFMA_STAGED_TABLE, KV_KERNEL_VALU = 0, 1, 2, 3, 4
 
 
 class KVError(RuntimeError):

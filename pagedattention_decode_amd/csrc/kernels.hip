@@ -510,6 +510,123 @@ __device__ __forceinline__ void attend_qblock(const kv_regs<D>& cur, const kv_qr
 }
 
 // ---------------------------------------------------------------------------
+// The same decode step with vector-ALU dot products instead of matrix
+// instructions (bf16, B = 16, GT query heads per KV head, compile time), on
+// the tile exactly as the ring loads it: lane (r, q) = (lane % 16, lane / 16)
+// holds D/4 dims of key r (k[kk]: dims 32 kk + 8 q .. + 8) and, for every
+// 16-dim tile t, the values of tokens 4q .. 4q+3 in dim 16 t + r (v[t / 2],
+// 8-byte half t % 2).
+//   scores   s(r, h): 4 v_dot2_f32_bf16 per 8 dims against the unit's queries
+//            (LDS, broadcast reads), then summed over the four quads by the
+//            two lane swaps, so every quad holds the scores of key r;
+//   softmax  the block maximum per head over the 16 keys of a row (DPP within
+//            the row), the same lazy rescale and bf16 weights as the matrix
+//            path; the weights of keys (r, r + 1) are packed in lane r;
+//   values   lane (r, q) fetches the packed weights of its tokens 4q .. 4q+3
+//            (two ds_bpermute per head) and adds them into acc[h][t] with two
+//            v_dot2_f32_bf16 per head and tile.
+// acc[h][t] sums over the lane's token slots only; the four quads' sums are
+// added when the unit's run ends.  l[h] sums, per lane, the weights of key r
+// (the quads hold copies; a row's 16 lanes are added at the end).
+// ---------------------------------------------------------------------------
+template <int D, int GT>
+struct valu_state {
+  float acc[GT][D / 16];
+  float m[GT];
+  float l[GT];
+};
+
+template <int D, int GT>
+__device__ __forceinline__ void valu_reset(valu_state<D, GT>& st) {
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) st.acc[h][t] = 0.f;
+    st.m[h] = -INFINITY;
+    st.l[h] = 0.f;
+  }
+}
+
+// maximum over the 16 lanes of each row (every lane gets its row's)
+__device__ __forceinline__ float row_max16(float x) {
+  x = maxn(x, dpp_f32<kDppXor1>(x));
+  x = maxn(x, dpp_f32<kDppXor2>(x));
+  x = maxn(x, dpp_f32<kDppHalfMirror>(x));
+  return maxn(x, dpp_f32<kDppMirror>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<kDppXor1>(x);
+  x += dpp_f32<kDppXor2>(x);
+  x += dpp_f32<kDppHalfMirror>(x);
+  return x + dpp_f32<kDppMirror>(x);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int D, int GT>
+__device__ __forceinline__ void attend_block_valu(kv_regs<D>& cur, const uint16_t* qs, int valid, int lane,
+                                                  float scale_log2, valu_state<D, GT>& st) {
+  const int r = lane & 15, q = lane >> 4;
+  // the values of out-of-range slots are zeroed (their memory may hold anything)
+  if (valid < 16) zero_v_tail<D>(cur, valid, q);
+  float s[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) s[h] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const uint4 k4 = cur.k[kk];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const uint4 q4 = *reinterpret_cast<const uint4*>(qs + h * D + kk * 32 + q * 8);
+      s[h] = dot2_bf16(k4.x, q4.x, s[h]);
+      s[h] = dot2_bf16(k4.y, q4.y, s[h]);
+      s[h] = dot2_bf16(k4.z, q4.z, s[h]);
+      s[h] = dot2_bf16(k4.w, q4.w, s[h]);
+    }
+  }
+  bool grow = false;
+  float mb[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    s[h] = sum_xor32(sum_xor16(s[h]));
+    if (valid < 16) s[h] = r < valid ? s[h] : -INFINITY;  // wave uniform
+    mb[h] = row_max16(s[h]) * scale_log2;
+    grow |= mb[h] > st.m[h] + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform branch, rare after the first blocks
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const float m_new = mb[h] > st.m[h] + kRescaleSlack ? mb[h] : st.m[h];
+      const float alpha = __builtin_amdgcn_exp2f(st.m[h] - m_new);  // 0 when m = -inf, 1 when kept
+      st.l[h] *= alpha;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) st.acc[h][t] *= alpha;
+      st.m[h] = m_new;
+    }
+  }
+  // the source lanes of this row's tokens 4q, 4q+1 and 4q+2, 4q+3 (bytes)
+  const int src01 = (16 * q + 4 * q) * 4, src23 = src01 + 8;
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const float nm = st.m[h] == -INFINITY ? 0.f : -st.m[h];
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h], scale_log2, nm));
+    const float pn = dpp_f32<kDppXor1>(p);  // key r ^ 1
+    const uint32_t pair = pack_bf16x2(p, pn);  // at even r: keys r (low) and r + 1 (high)
+    st.l[h] += __uint_as_float(pair << 16);     // the rounded weight of key r
+    const uint32_t w01 = __builtin_amdgcn_ds_bpermute(src01, pair);
+    const uint32_t w23 = __builtin_amdgcn_ds_bpermute(src23, pair);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const uint2 vh = reinterpret_cast<const uint2*>(&cur.v[t / 2])[t % 2];
+      st.acc[h][t] = dot2_bf16(vh.x, w01, st.acc[h][t]);
+      st.acc[h][t] = dot2_bf16(vh.y, w23, st.acc[h][t]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Split-K over partitions, one contiguous run of partitions per wave.
 //
 // Units are (sequence, kv head) pairs in sequence-major order; every unit is
@@ -656,11 +773,14 @@ struct sk_cursor {
 // from there per tile; 0: one scalar load per tile.
 constexpr int kSkTblMax = 2048;
 
-template <int D, int STAGES, int WAVES_PER_SIMD, int FMT, int BS, int TBL = 0>
+// MATH = 1 (bf16, B = 16): the vector-ALU step attend_block_valu with GT query
+// heads per KV head instead of the matrix instructions; 0: matrix instructions.
+template <int D, int STAGES, int WAVES_PER_SIMD, int FMT, int BS, int TBL = 0, int MATH = 0, int GT = 1>
 __global__ void __launch_bounds__(kSkWaves * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD)))
 attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ tables) {
   static_assert(FMT == kFmtBf16 || BS == 16, "quantised tiles are 16 tokens");
   static_assert(TBL == 0 || (FMT == kFmtBf16 && BS == 16), "LDS-staged table entries: bf16, B = 16");
+  static_assert(MATH == 0 || (FMT == kFmtBf16 && BS == 16 && TBL == 0), "vector-ALU step: bf16, B = 16");
   static_assert(BS == 4 || BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size");
   extern __shared__ __align__(16) int sk_smem[];
   int* cum_b = sk_smem;                       // n_seqs + 1
@@ -873,8 +993,10 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
   // queries of the idx-th unit of the run: always read from LDS (a unit past
   // the staged ones is first copied into the slot of an earlier, finished
   // unit), so the query registers never wait on global loads in the loop
+  int q_slot = 0;  // LDS slot of the current unit's queries
   auto fetch_q = [&](int idx) {
     const int slot = idx % a.q_units;
+    q_slot = slot;
     if (idx >= a.q_units) {
       const uint16_t* qg = static_cast<const uint16_t*>(a.q) +
                            (static_cast<int64_t>(cs.seq) * a.n_q_heads + cs.kvh * G) * D;
@@ -908,8 +1030,51 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
   float m_run = -INFINITY, l_lane = 0.f;
   bool poisoned = false;
 
+  // vector-ALU step: its own state and result layout (lane (r, q) ends with
+  // O[h][16 t + r] for every head once the quads are added; quad q writes the
+  // tiles t = 2q, 2q + 1 of D = 128, in general t = q, q + 4, ...)
+  valu_state<D, GT> vst;
+  if constexpr (MATH == 1) valu_reset(vst);
+  auto finish_valu = [&]() {
+    const int r = lane & 15;
+    const float nan = __builtin_nanf("");
+    const bool whole = seg_j0 == 0 && cs.j == cs.nb - 1;
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const float l = row_sum16(vst.l[h]);
+      const int head = cs.kvh * G + h;
+      float* po = nullptr;
+      uint16_t* orow = nullptr;
+      const int64_t prow = (wid + static_cast<int64_t>(cs.seq) * Hkv + cs.kvh) * G + h;
+      if (whole)
+        orow = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(cs.seq) * a.n_q_heads + head) * D;
+      else
+        po = a.part_o + prow * D;
+      const float inv = poisoned ? 0.f : 1.f / l;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const float v = sum_xor32(sum_xor16(vst.acc[h][t]));
+        if (t % 4 != quad) continue;
+        if (whole)
+          orow[16 * t + r] = poisoned ? static_cast<uint16_t>(0x7fc0) : f32_to_bf16(v * inv);
+        else
+          po[16 * t + r] = poisoned ? nan : v;
+      }
+      if (!whole && lane == 0) {
+        a.part_m[prow] = poisoned ? nan : vst.m[h];
+        a.part_l[prow] = poisoned ? nan : l;
+      }
+    }
+    valu_reset(vst);
+    poisoned = false;
+  };
+
   // writes the result of the current unit's run and resets the state
   auto finish = [&]() {
+    if constexpr (MATH == 1) {
+      finish_valu();
+      return;
+    }
     const float l = sum_xor32(sum_xor16(l_lane));
     const int h = cs.kvh * G + hg;
     const float nan = __builtin_nanf("");
@@ -954,7 +1119,9 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
         const bool bad = bad_ring[u];
         poisoned |= bad;
         const int valid = bad ? 0 : min(16, cs.n - cs.j * 16);
-        if constexpr (FMT == kFmtBf16) {
+        if constexpr (MATH == 1) {
+          attend_block_valu<D, GT>(buf[u], q_wave + q_slot * G * D, valid, lane, a.scale_log2, vst);
+        } else if constexpr (FMT == kFmtBf16) {
           attend_block<D>(buf[u], qop, valid, quad, a.scale_log2, o, m_run, l_lane);
         } else {
           kv_regs<D> tile;
@@ -1288,6 +1455,7 @@ constexpr int sk_stages() {
 struct resolved {
   int kernel;
   bool staged_table = false;  // KV_KERNEL_MFMA_STAGED_TABLE (kernel is then KV_KERNEL_MFMA)
+  bool valu = false;          // KV_KERNEL_VALU (kernel is then KV_KERNEL_MFMA)
   int partition;   // tokens
   int max_parts;   // generic kernel: partitions of the longest context
   int64_t groups;  // split-K kernel: persistent workgroups
@@ -1305,8 +1473,15 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
   kv_attention_options o{0.f, 0, KV_KERNEL_AUTO, nullptr};
   if (opts) o = *opts;
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_GENERIC && o.kernel != KV_KERNEL_MFMA &&
-      o.kernel != KV_KERNEL_MFMA_STAGED_TABLE)
+      o.kernel != KV_KERNEL_MFMA_STAGED_TABLE && o.kernel != KV_KERNEL_VALU)
     return fail(KV_ERR_INVALID, "unknown kernel selector");
+  r.valu = o.kernel == KV_KERNEL_VALU;
+  if (r.valu) {
+    if (c.dtype != KV_BF16 || c.block_size != 16 || c.head_dim != 128 || (G != 4 && G != 8))
+      return fail(KV_ERR_UNSUPPORTED, "the vector-ALU split-K kernel reads bf16 pools with B = 16, d = 128, "
+                                      "G = 4 or 8");
+    o.kernel = KV_KERNEL_MFMA;
+  }
   r.staged_table = o.kernel == KV_KERNEL_MFMA_STAGED_TABLE;
   if (r.staged_table) {
     if (c.dtype != KV_BF16 || c.block_size != 16)
@@ -1361,9 +1536,21 @@ uint64_t workspace_for(const kv_pool_config& c, int n_seqs, int num_q_heads, con
 
 template <int D, int FMT, int BS = 16>
 hipError_t launch_mfma(const sk_args& a, const int32_t* ctx_lens, const int32_t* tables, int64_t groups, int G,
-                       hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, bool staged_table = false) {
+                       hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, bool staged_table = false,
+                       bool valu = false) {
   constexpr int kStages = sk_stages<D, FMT>();
   constexpr int kWps = sk_waves_per_simd(D, FMT);
+  if constexpr (FMT == kFmtBf16 && BS == 16 && D == 128) {
+    // the vector-ALU variant: a 4-deep ring (3 at G = 8) beside its G x D / 16 accumulators per lane
+    const uint32_t lds = static_cast<uint32_t>(sk_lds_bytes(a.n_seqs, G, D));
+    if (valu && G == 4)
+      return launch_timed(attn_mfma_kernel<D, 4, 1, FMT, BS, 0, 1, 4>, dim3(static_cast<unsigned>(groups)),
+                          dim3(kSkWaves * 64), lds, st, ev0, ev1, a, ctx_lens, tables);
+    if (valu && G == 8)
+      return launch_timed(attn_mfma_kernel<D, 3, 1, FMT, BS, 0, 1, 8>, dim3(static_cast<unsigned>(groups)),
+                          dim3(kSkWaves * 64), lds, st, ev0, ev1, a, ctx_lens, tables);
+  }
+  if (valu) return hipErrorInvalidValue;
   if constexpr (FMT == kFmtBf16 && BS == 16) {
     if (staged_table)
       return launch_timed(attn_mfma_kernel<D, kStages, kWps, FMT, BS, 1>, dim3(static_cast<unsigned>(groups)),
@@ -1421,9 +1608,9 @@ kv_status decode_launch(const kv_pool* pool, int layer, const void* q, void* out
       constexpr int F = decltype(fmt)::value;
       constexpr int BS = decltype(bs)::value;
       switch (c.head_dim) {
-        case 64: return launch_mfma<64, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop, r.staged_table);
-        case 128: return launch_mfma<128, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop, r.staged_table);
-        default: return launch_mfma<256, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop, r.staged_table);
+        case 64: return launch_mfma<64, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop, r.staged_table, r.valu);
+        case 128: return launch_mfma<128, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop, r.staged_table, r.valu);
+        default: return launch_mfma<256, F, BS>(a, d_context_lens, d_block_tables, r.groups, G, st, ev.start, ev.kernel_stop, r.staged_table, r.valu);
       }
     };
     using B16 = std::integral_constant<int, 16>;
