@@ -1073,7 +1073,8 @@ def summarize_activity(a):
         line = bench_line(os.path.join(d, f"act_{kind}_1.log"))
         cfg = line["config"]
         tiles = cfg["sequences"] * cfg["context_tokens_first_step"] / 16 * 8  # 8 kv heads
-        wps = 1 if kind == "bf16" else 2
+        kv = kind.split("-")[0]
+        wps = 1 if kv == "bf16" else 2
         valu_share = per["SQ_ACTIVE_INST_VALU"] / per["SQ_WAVE_CYCLES"]
         rows_md.append(f"| {kind} | {n_disp} | {per['SQ_INSTS_VALU'] / tiles:.1f} | {per['SQ_INSTS_MFMA'] / tiles:.1f} | "
                        f"{valu_share:.3f} | {wps} | {valu_share * wps:.2f} | "
@@ -1083,15 +1084,17 @@ def summarize_activity(a):
           "Commands (from the repository root; two passes per storage kind <kind>, each a run of its own):", "",
           "```"]
     for kind in a.summary_kinds.split(","):
+        kv, _, kern = kind.partition("-")  # <storage>[-<kernel>]
+        kern_arg = f" --kernel {kern}" if kern else ""
         for i, pas in enumerate(ACTIVITY_PASSES, 1):
             md.append(f"timeout -s KILL 200 rocprofv3 --pmc {pas} --output-format csv -d <dir>/act_{kind}_{i} -o run "
-                      f"-- python3 bench.py {bench_args} --kv {kind} --steps 2 --warmup 1")
+                      f"-- python3 bench.py {bench_args} --kv {kv}{kern_arg} --steps 2 --warmup 1")
     md += ["```", "", f"Summarised by `{summary_command()}` (each run's stdout in `<dir>/act_<kind>_<pass>.log`).", "",
            "Per 16-token tile of one kv head (a wave's unit of work) in `attn_mfma_kernel`. `SQ_ACTIVE_INST_VALU` "
            "over `SQ_WAVE_CYCLES` is the share of a wave's cycles spent issuing vector-ALU instructions; times the "
            "waves per SIMD it estimates how busy each SIMD's vector ALU is. `SQ_WAIT_INST_ANY` over `SQ_WAVE_CYCLES` "
            "is the share spent waiting (mostly on memory).", "",
-           "| storage | dispatches | VALU instructions per tile | MFMA per tile | VALU share of wave cycles | "
+           "| storage[-kernel] | dispatches | VALU instructions per tile | MFMA per tile | VALU share of wave cycles | "
            "waves per SIMD | SIMD VALU busy (est.) | waiting share | kernel us (this run) |",
            "|---|---|---|---|---|---|---|---|---|"] + rows_md
     out_md = os.path.join(ROOT, "profiles", f"{a.summary_file}.md")
