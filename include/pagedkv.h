@@ -381,8 +381,10 @@ typedef enum {
   KV_KERNEL_AUTO = 0,    /* the matrix-core kernel where it applies, else generic */
   KV_KERNEL_GENERIC = 1, /* vector-ALU kernel: f32 or bf16, any B, d; G <= 16 */
   KV_KERNEL_MFMA = 2     /* bf16 with B in {4, 8, 16, 32, 64}, or q8_0 / q4_0
-                            with B = 16; d in {64, 128, 256}, G <= 16, at most
-                            4095 sequences per call.  It works in 16-token
+                            with B = 16; d in {64, 128, 256}, G <= 16.  A call
+                            of more than 4095 sequences runs as consecutive
+                            launches over slices of at most 4095 (the
+                            workspace holds one slice).  It works in 16-token
                             tiles: B/16 tiles per table entry for B > 16, 16/B
                             entries per tile for B < 16 (entries past a
                             context are never read).  The only kernel for
@@ -422,7 +424,9 @@ typedef enum {
  *                partition kernel of paged_attention_decode and the
  *                multi-query kernel of paged_attention_prefill (both the
  *                call's first kernel, so start .. kernel_stop is that kernel
- *                alone), the fused prefix-and-suffix kernel of the cascade
+ *                alone; when a decode of more than 4095 sequences runs
+ *                as several launches, start .. kernel_stop spans them),
+ *                the fused prefix-and-suffix kernel of the cascade
  *                (also its first kernel), the
  *                last decode kernel of the row-wise prefill path (after its
  *                row-length kernel and any earlier batches);

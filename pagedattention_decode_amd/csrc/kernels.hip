@@ -1488,16 +1488,19 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
       return fail(KV_ERR_UNSUPPORTED, "the LDS-staged table variant reads bf16 pools with B = 16");
     o.kernel = KV_KERNEL_MFMA;
   }
-  const bool mfma_ok = decode_mfma_supported(c, G) && n_seqs <= kSkMaxSeqs && sk_q_units(n_seqs, G, c.head_dim) >= 1;
-  if (r.staged_table && (!mfma_ok || sk_lds_bytes(n_seqs, G, c.head_dim) + kSkWaves * kSkTblMax * 4 > max_lds_per_block()))
+  // a batch of more than kSkMaxSeqs sequences runs as consecutive launches of
+  // at most kSkMaxSeqs (the kernel keeps per-sequence prefix sums in LDS)
+  const int launch_seqs = std::min(n_seqs, kSkMaxSeqs);
+  const bool mfma_ok = decode_mfma_supported(c, G) && sk_q_units(launch_seqs, G, c.head_dim) >= 1;
+  if (r.staged_table &&
+      (!mfma_ok || sk_lds_bytes(launch_seqs, G, c.head_dim) + kSkWaves * kSkTblMax * 4 > max_lds_per_block()))
     return fail(KV_ERR_UNSUPPORTED, "the LDS-staged table variant does not fit this call");
   if (o.kernel == KV_KERNEL_MFMA && !mfma_ok)
     return fail(KV_ERR_UNSUPPORTED,
                 "the matrix-core kernel needs bf16 with B in {4, 8, 16, 32, 64} or q8_0/q4_0 with B = 16, d in "
-                "{64, 128, 256} and at most 4095 sequences");
+                "{64, 128, 256}");
   if (is_quantized(c.dtype) && (o.kernel == KV_KERNEL_GENERIC || !mfma_ok))
-    return fail(KV_ERR_UNSUPPORTED, "a quantised pool is read by the matrix-core kernel only (at most 4095 "
-                                    "sequences, G <= 16)");
+    return fail(KV_ERR_UNSUPPORTED, "a quantised pool is read by the matrix-core kernel only (G <= 16)");
   r.kernel = o.kernel == KV_KERNEL_AUTO ? (mfma_ok ? KV_KERNEL_MFMA : KV_KERNEL_GENERIC) : o.kernel;
   if (o.partition_tokens < 0 || (o.partition_tokens > 0 && o.partition_tokens % c.block_size != 0))
     return fail(KV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of the block size");
@@ -1524,10 +1527,11 @@ kv_status resolve(const kv_pool* pool, int n_seqs, int num_q_heads, int max_bloc
 // Split-K kernel: m, l [slots][G], o [slots][G][d], slots = waves + units,
 // then the partition prefix [n_seqs + 1].
 uint64_t workspace_for(const kv_pool_config& c, int n_seqs, int num_q_heads, const resolved& r) {
-  if (r.kernel == KV_KERNEL_MFMA) {
+  if (r.kernel == KV_KERNEL_MFMA) {  // one launch's worth: at most kSkMaxSeqs sequences
     const int G = num_q_heads / c.num_kv_heads;
-    const uint64_t slots = static_cast<uint64_t>(r.groups) * kSkWaves + static_cast<uint64_t>(n_seqs) * c.num_kv_heads;
-    return 2 * up256(slots * G * 4) + up256(slots * G * c.head_dim * 4) + up256((n_seqs + 1) * 4ull);
+    const int n = std::min(n_seqs, kSkMaxSeqs);
+    const uint64_t slots = static_cast<uint64_t>(r.groups) * kSkWaves + static_cast<uint64_t>(n) * c.num_kv_heads;
+    return 2 * up256(slots * G * 4) + up256(slots * G * c.head_dim * 4) + up256((n + 1) * 4ull);
   }
   if (r.max_parts <= 1) return 0;
   const uint64_t rows = static_cast<uint64_t>(n_seqs) * num_q_heads * r.max_parts;
@@ -1909,8 +1913,30 @@ kv_status paged_attention_decode(kv_pool* pool, int32_t layer, const void* q, vo
     return fail(KV_ERR_INVALID, "workspace too small: need " + std::to_string(need) + " bytes");
   if (need > 0 && (reinterpret_cast<uintptr_t>(d_workspace) & 255))
     return fail(KV_ERR_INVALID, "workspace must be 256-byte aligned");
-  return decode_launch(pool, layer, q, out, d_block_tables, d_context_lens, nullptr, n_seqs, max_blocks_per_seq,
-                       num_q_heads, r, d_workspace, static_cast<hipStream_t>(hip_stream), events_of(opts));
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const call_events ev = events_of(opts);
+  if (r.kernel != KV_KERNEL_MFMA || n_seqs <= kSkMaxSeqs)
+    return decode_launch(pool, layer, q, out, d_block_tables, d_context_lens, nullptr, n_seqs, max_blocks_per_seq,
+                         num_q_heads, r, d_workspace, st, ev);
+  // more sequences than one launch takes: consecutive launches over slices of
+  // the batch, reusing the workspace (stream order separates them); the timing
+  // events go to the first launch's start and the last launch's ends
+  const int64_t row_bytes = static_cast<int64_t>(num_q_heads) * c.head_dim * 2;  // bf16 q / out rows
+  for (int b0 = 0; b0 < n_seqs; b0 += kSkMaxSeqs) {
+    const int n = std::min(kSkMaxSeqs, n_seqs - b0);
+    const bool last = b0 + kSkMaxSeqs >= n_seqs;
+    call_events e;
+    e.start = b0 == 0 ? ev.start : nullptr;
+    e.kernel_stop = last ? ev.kernel_stop : nullptr;
+    e.stop = last ? ev.stop : nullptr;
+    if (kv_status s = decode_launch(pool, layer, static_cast<const char*>(q) + b0 * row_bytes,
+                                    static_cast<char*>(out) + b0 * row_bytes,
+                                    d_block_tables + static_cast<int64_t>(b0) * max_blocks_per_seq,
+                                    d_context_lens + b0, nullptr, n, max_blocks_per_seq, num_q_heads, r, d_workspace,
+                                    st, e))
+      return s;
+  }
+  return KV_OK;
 }
 
 kv_status paged_attention_decode_static(kv_pool* pool, int32_t layer, const void* q, void* out,

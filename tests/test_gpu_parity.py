@@ -456,3 +456,20 @@ def test_timing_events_leave_results_unchanged(kernel):
         assert 0.0 < k_ms <= c_ms
     got = bits_to_float_tensor(out0, wl.dtype).double().cpu().numpy()
     check_outputs(got, ref.attention(0, 0), wl.dtype, "decode")
+
+
+def test_more_sequences_than_one_launch_takes():
+    announce("5000 sequences (more than the 4095 one split-K launch takes), Hq=8 Hkv=2 d=64, lengths 1..40: "
+             "consecutive launches, automatic and matrix-core selection")
+    rng = np.random.default_rng(77)
+    lengths = [int(x) for x in rng.integers(1, 41, size=5000)]
+    wl = ragged_workload(8, 2, 64, lengths, seed=41)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1, opts=B.attention_options(kernel=B.KV_KERNEL_MFMA)).run()
+    compare_all_decodes(run, ref)
+    rec = run.decodes[0]
+    tables = torch.from_numpy(rec["tables"]).cuda()
+    lens = torch.from_numpy(rec["lengths"]).cuda()
+    auto = run.decode(0, 0, tables, lens, len(lengths), opts=B.attention_options())
+    mfma = run.decode(0, 0, tables, lens, len(lengths), opts=B.attention_options(kernel=B.KV_KERNEL_MFMA))
+    assert torch.equal(auto, mfma), "the automatic choice is not the matrix-core kernel above 4095 sequences"
