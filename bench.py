@@ -305,8 +305,8 @@ def main():
     else:
         ws_bytes = pool.workspace_bytes(S, Hq, max_blocks, opts)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    # one upload per step: slot mapping (int64), tables, lengths and the cascade plan (int32)
-    # packed in one pinned buffer and copied to one device buffer in a single transfer
+    # the step's host data: slot mapping (int64), tables, lengths and the cascade plan (int32)
+    # packed in one pinned buffer; a step sends what changed since the last upload
     off_t = 8 * S
     off_l = off_t + 4 * S * max_blocks
     off_p = off_l + 4 * S
@@ -327,6 +327,11 @@ def main():
     h_plan = [h[off_p:].view(np.int32) for h in h_np]
     ring_ev = [None] * ring
     seq_arr = np.asarray(decode_seqs, np.int64)
+    # what the device holds from the previous upload: only the parts that changed are sent
+    # (the block tables change when a sequence crosses a block or copies on write; the slot
+    # mapping and the lengths with every appended token)
+    dev_tables = [None]
+    dev_tail = [None]
     stream = torch.cuda.current_stream()
 
     logical_bytes = [0]
@@ -373,7 +378,16 @@ def main():
             read_tokens = int(sb.astype(np.int64).sum()) * Bs + int((lens.astype(np.int64) - shared_tok).sum())
         else:
             read_tokens = int(lens.astype(np.int64).sum())
-        d_up.copy_(h_up[slot], non_blocking=True)
+        if dev_tables[0] is None or not np.array_equal(h_tables[slot], dev_tables[0]):
+            d_up.copy_(h_up[slot], non_blocking=True)
+            dev_tables[0] = h_tables[slot].copy()
+            dev_tail[0] = h_np[slot][off_l:].copy()
+        else:
+            if step_appends:
+                d_up[:off_t].copy_(h_up[slot][:off_t], non_blocking=True)
+            if not np.array_equal(h_np[slot][off_l:], dev_tail[0]):
+                d_up[off_l:].copy_(h_up[slot][off_l:], non_blocking=True)
+                dev_tail[0] = h_np[slot][off_l:].copy()
         ev = torch.cuda.Event()
         ev.record(stream)
         ring_ev[slot] = ev
