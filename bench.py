@@ -120,7 +120,7 @@ def parse():
     ap.add_argument("--workload", default="gqa70b_12x131072", choices=list(DECODE_LAYERS),
                     help="the decode workload of --op decode")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "q8_0", "q4_0"],
-                    help="storage of the KV pool for --op decode: bf16, or q8_0 / q4_0 codes with one 2-byte "
+                    help="storage of the KV pool (decode, prefill, verify): bf16, or q8_0 / q4_0 codes with one 2-byte "
                          "scale per 32 values (written by reshape_and_cache, dequantised in the kernel)")
     ap.add_argument("--block-size", type=int, default=0,
                     help="--op decode: tokens per block of the pool (0 = the workload's, 16); bf16 pools of block "
@@ -551,6 +551,8 @@ def multi_query_bench(args):
     from pagedattention_decode_amd.pool import PagedKVPool
     from synth import draws, workloads
 
+    from dataclasses import replace
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     prefill = args.op == "prefill"
@@ -564,7 +566,7 @@ def multi_query_bench(args):
     S, c = len(seqs), counts[0]
     opts = B.attention_options(partition_tokens=max(args.partition, 0))
 
-    pool = PagedKVPool(L, base.num_blocks, Bs, Hkv, d, "bf16", free_order=draws.free_order(seed, base.num_blocks))
+    pool = PagedKVPool(L, base.num_blocks, Bs, Hkv, d, args.kv, free_order=draws.free_order(seed, base.num_blocks))
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
 
@@ -623,7 +625,10 @@ def multi_query_bench(args):
     n = lens.astype(np.int64)
     pairs = int(sum(c * (int(x) - c) + c * (c + 1) // 2 for x in n))  # query-key pairs per head
     flops = 4 * d * Hq * pairs                                          # QK^T and PV, per layer call
-    kv_bytes = int(n.sum()) * 2 * Hkv * d * 2                           # each sequence's keys and values
+    # each sequence's keys and values as stored (codes and scales for a quantised pool)
+    kv_per_tok = 2 * Hkv * (d * 2 if args.kv == "bf16" else d * (8 if args.kv == "q8_0" else 4) // 8 + d // 16)
+    kv_bytes = int(n.sum()) * kv_per_tok
+    quant = args.kv != "bf16"  # raw tiles: the multi-query kernel for quantised pools
     ideal_bytes = kv_bytes + 2 * total_q * Hq * d * 2 + 4 * int(np.ceil(n / Bs).sum())
     calls = args.steps * L
     result = {
@@ -648,6 +653,8 @@ def multi_query_bench(args):
             "chunk_tokens": c,
             "history_tokens": int(hist[0]),
             "partition_tokens": args.partition if args.partition > 0 else "auto",
+            "kv_storage": args.kv,
+            "kv_bytes_per_token_per_layer": kv_per_tok,
             "step": f"{L} x (reshape_and_cache of the chunk + paged_attention_prefill)",
         },
         "attn_call_us": round(attn_s * 1e6, 2),
@@ -663,8 +670,9 @@ def multi_query_bench(args):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(flops / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(base.name, PREFILL_SOURCES),
-            "kernel": "attn_prefill_lds_kernel (multi-query kernel)",
+            "traffic": None if quant else measured_traffic(base.name, PREFILL_SOURCES),
+            "kernel": ("attn_prefill_q_kernel (multi-query kernel, quantised tiles)" if quant
+                       else "attn_prefill_lds_kernel (multi-query kernel)"),
             "duration_us": round(kern_s * 1e6, 2),
             "algorithmic_flops_per_launch": flops,
         } if prefill else {
@@ -673,14 +681,16 @@ def multi_query_bench(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ideal_bytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(base.name, PREFILL_SOURCES),
-            "kernel": "attn_prefill_lds_kernel (multi-query kernel)",
+            "traffic": None if quant else measured_traffic(base.name, PREFILL_SOURCES),
+            "kernel": ("attn_prefill_q_kernel (multi-query kernel, quantised tiles)" if quant
+                       else "attn_prefill_lds_kernel (multi-query kernel)"),
             "duration_us": round(kern_s * 1e6, 2),
             "algorithmic_bytes_per_launch": ideal_bytes,
         }),
         "call_frac": round((flops / attn_s / 1e12 / MFMA_BF16_PEAK_TFLOPS) if prefill
                            else (ideal_bytes / attn_s / 1e9 / HBM_PEAK_GBS), 4),
-        "cpu_baseline": None if args.no_cpu_baseline else multi_query_cpu_baseline(args, base),
+        "cpu_baseline": None if args.no_cpu_baseline else multi_query_cpu_baseline(
+            args, base if args.kv == "bf16" else replace(base, kv_format=args.kv)),
     }
     print(json.dumps(result), flush=True)
 

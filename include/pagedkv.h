@@ -564,18 +564,22 @@ uint64_t paged_prefill_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int3
  * A table entry outside [0, N) is never dereferenced: every row whose visible
  * keys include it is written as NaN, and so may be the other rows of its
  * query tile (16 consecutive columns of (row, head)) on the multi-query
- * kernel.  Two paths:
- *   multi-query kernel: bf16 pools with B = 16, d in {64, 128, 256}, G <= 16
+ * kernels.  Two paths:
+ *   multi-query kernels: bf16 pools with B = 16, d in {64, 128, 256}, and
+ *     q8_0 / q4_0 pools with B = 16, d in {64, 128}; G <= 16
  *     (KV_KERNEL_AUTO or KV_KERNEL_MFMA); one tile of columns reads each
- *     block once for all its rows;
- *   row-wise: every other pool, and any pool with KV_KERNEL_GENERIC -- each
- *     chunk row is a decode query over its n - c + j + 1 keys, through the
- *     decode kernels (the matrix-core split-K kernel, in batches of at most
- *     4095 rows, for quantised pools and bf16 pools of block size 4, 8, 32 or
- *     64; the generic kernel for f32 pools and other block sizes), so the
- *     history is read once per row.  Rows no sequence owns are written
- *     as zero rows.  KV_KERNEL_MFMA on a pool no matrix-core kernel reads
- *     gives KV_ERR_UNSUPPORTED.
+ *     block once for all its rows.  Over a quantised pool the codes are the
+ *     matrix operands (exact in bf16) and the group scales are applied in
+ *     float32, as in paged_attention_decode ([INF] §8.4.2);
+ *   row-wise: every other pool (f32, other block sizes, quantised at
+ *     d = 256), and any pool with KV_KERNEL_GENERIC -- each chunk row is a
+ *     decode query over its n - c + j + 1 keys, through the decode kernels
+ *     (the matrix-core split-K kernel, in batches of at most 4095 rows, for
+ *     quantised pools and bf16 pools of block size 4, 8, 32 or 64; the
+ *     generic kernel for f32 pools and other block sizes), so the history is
+ *     read once per row.  Rows no sequence owns are written as zero rows.
+ *     KV_KERNEL_MFMA on a pool no matrix-core kernel reads gives
+ *     KV_ERR_UNSUPPORTED.
  * opts->partition_tokens splits every tile's (row's) keys into partitions
  * merged with the [KVM] recurrences (0 = the library's choice). */
 kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, void* out,

@@ -424,6 +424,317 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-query attention over a quantised pool (q8_0 / q4_0, B = 16, d <= 128)
+// ([INF] §8.4.2: the stored value of a group stands for its code times the
+// group's half scale).  The register-ring kernel above with raw tiles in the
+// ring: per block pair the codes become exact bf16 operands (codes_block, as
+// in the decode kernel), and the scales are applied in float32:
+//   score(r, col) = sum_g sK(r, g) * (codes_K(r, group g) . q_col(group g)),
+//   O^T          += sum_r  p(r) sV(r, g) codes_V(r, dims of group g),
+// so the only rounding beyond float32 is that of each weight p * sV to bf16.
+// l sums the unrounded weights.  q4_0 codes carry the bias kQ4Bias: kb[cg][kk]
+// (-kQ4Bias times the column's query sum over group kk) starts each score
+// product, and every V product is followed by one with the constant operand
+// -kQ4Bias on the same weights.
+// ---------------------------------------------------------------------------
+template <int D, int FMT>
+struct kv_qpair {
+  kv_qregs<D, FMT> a, b;
+};
+
+// One block pair against the NCG column groups: the steps of attend_pair on
+// the dequantised pair.  A masked slot (outside the context, or past a
+// column's position) gets score -inf and then weight 0 by selection: its
+// scale and codes may be anything.
+template <int D, int NCG, int FMT, class QOp>
+__device__ __forceinline__ void attend_qpair(const QOp& qop, const kv_qpair<D, FMT>& raw,
+                                             const float (&kb)[NCG][D / 32], bool masked, const int* lim_a,
+                                             const int* lim_b, int quad, float c, f32x4_t (&o)[NCG][D / 16],
+                                             float* m_run, float* l_lane) {
+  kv_regs<D> ta, tb;
+  codes_block<D, FMT>(raw.a, ta);
+  codes_block<D, FMT>(raw.b, tb);
+  f32x4_t sa[NCG], sb[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    sa[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sb[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const bf16x8_t qk = qop(cg, kk);
+      const f32x4_t b0 = {kb[cg][kk], kb[cg][kk], kb[cg][kk], kb[cg][kk]};
+      const f32x4_t xa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ta.k[kk]), qk, b0, 0, 0, 0);
+      const f32x4_t xb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tb.k[kk]), qk, b0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa[cg][i] = __builtin_fmaf(scale_at<D>(raw.a.ks, i, kk), xa[i], sa[cg][i]);
+        sb[cg][i] = __builtin_fmaf(scale_at<D>(raw.b.ks, i, kk), xb[i], sb[cg][i]);
+      }
+    }
+  }
+  float mb[NCG];
+  bool grow_any = false;
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    if (masked) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (quad * 4 + i >= lim_a[cg]) sa[cg][i] = -INFINITY;
+        if (quad * 4 + i >= lim_b[cg]) sb[cg][i] = -INFINITY;
+      }
+    }
+    float m = maxn3(maxn3(sa[cg][0], sa[cg][1], sa[cg][2]), maxn3(sa[cg][3], sb[cg][0], sb[cg][1]),
+                    maxn(sb[cg][2], sb[cg][3]));
+    m = maxn_xor32(maxn_xor16(m));
+    mb[cg] = m * c;
+    grow_any |= mb[cg] > m_run[cg] + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow_any)) {  // wave-uniform branch, rare after the first blocks
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const float m_new = mb[cg] > m_run[cg] + kRescaleSlack ? mb[cg] : m_run[cg];
+      const float alpha = __builtin_amdgcn_exp2f(m_run[cg] - m_new);  // 0 when m_run = -inf, 1 when kept
+      l_lane[cg] *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) o[cg][i] *= alpha;
+      m_run[cg] = m_new;
+    }
+  }
+  float pa[NCG][4], pb[NCG][4];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const float nm = m_run[cg] == -INFINITY ? 0.f : -m_run[cg];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pa[cg][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[cg][i], c, nm));
+      pb[cg][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[cg][i], c, nm));
+    }
+    l_lane[cg] += ((pa[cg][0] + pa[cg][1]) + (pa[cg][2] + pa[cg][3])) +
+                  ((pb[cg][0] + pb[cg][1]) + (pb[cg][2] + pb[cg][3]));
+  }
+  // O^T += V^T . (P * sV)^T over the 32 tokens of the pair, one weight operand
+  // per group of 32 dims (d-tiles 2 pp and 2 pp + 1); the V operand of d-tile
+  // t is block a's 4 slots of the lane then block b's (as kv_pair::v)
+#pragma unroll
+  for (int pp = 0; pp < D / 32; ++pp) {
+    const uint4 v0 = make_uint4(ta.v[pp].x, ta.v[pp].y, tb.v[pp].x, tb.v[pp].y);
+    const uint4 v1 = make_uint4(ta.v[pp].z, ta.v[pp].w, tb.v[pp].z, tb.v[pp].w);
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      float w[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[i] = __builtin_fmaf(scale_at<D>(raw.a.vs, i, pp), pa[cg][i], 0.f);
+        w[4 + i] = __builtin_fmaf(scale_at<D>(raw.b.vs, i, pp), pb[cg][i], 0.f);
+      }
+      if (masked) {  // wave uniform
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w[i] = pa[cg][i] == 0.f ? 0.f : w[i];
+          w[4 + i] = pb[cg][i] == 0.f ? 0.f : w[4 + i];
+        }
+      }
+      const bf16x8_t pop = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                               pack_bf16x2(w[6], w[7])));
+      o[cg][2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v0), pop, o[cg][2 * pp],
+                                                              0, 0, 0);
+      o[cg][2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v1), pop,
+                                                                  o[cg][2 * pp + 1], 0, 0, 0);
+      if constexpr (FMT == kFmtQ4) {
+        const bf16x8_t nb = __builtin_bit_cast(bf16x8_t, make_uint4(kQ4NegBiasPair, kQ4NegBiasPair, kQ4NegBiasPair,
+                                                                    kQ4NegBiasPair));
+        o[cg][2 * pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nb, pop, o[cg][2 * pp], 0, 0, 0);
+        o[cg][2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nb, pop, o[cg][2 * pp + 1], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// The register-ring multi-query kernel over a quantised pool: work split,
+// queries in LDS, masks, partials and output exactly as attn_prefill_kernel;
+// the ring holds STAGES raw block pairs (codes and scales of K and V).
+template <int D, int NCG, int FMT, int STAGES>
+__global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_q_kernel(pf_args a) {
+  static_assert(FMT == kFmtQ8 || FMT == kFmtQ4, "quantised pools");
+  static_assert(D <= 128, "d <= 128");
+  constexpr int NC = 16 * NCG;
+  const int lane = threadIdx.x & 63;
+  const int quad = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int bid = blockIdx.x;
+  const int pg = bid % a.part_groups;
+  bid /= a.part_groups;
+  const int tg = bid % a.tile_groups;
+  bid /= a.tile_groups;
+  const int g = bid % a.n_kv_heads;
+  const int s = bid / a.n_kv_heads;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int tile = tg * a.wt + wave % a.wt;
+  const int part = pg * (kPfWaves / a.wt) + wave / a.wt;
+
+  const pf_seq sq = pf_locate(a, s);
+  if (sq.c <= 0 || sq.q0 < 0 || sq.q0 + sq.c > a.total_q) return;  // nothing, or rows outside the output
+  const int cols = sq.c * G;
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  if (part >= a.max_parts) return;
+  if (sq.bad) {  // one wave per unit marks the unit's rows
+    if (part == 0 && tile == 0)
+      for (int i = lane; i < cols * D; i += 64) {
+        const int f = i / D, e = i % D;
+        out[(static_cast<int64_t>(sq.q0 + f / G) * a.n_q_heads + g * G + f % G) * D + e] = 0x7fc0;
+      }
+    return;
+  }
+  if (tile * NC >= cols) return;
+  const int kend = pf_tile_keys(a, sq, G, tile, NC);
+  const int P = a.part_blocks * 16;
+  const int k_begin = part * P;
+  if (k_begin >= kend) return;
+  const int n_parts = (kend + P - 1) / P;
+  const int b_begin = k_begin >> 4;
+  const int b_end = (min(kend, k_begin + P) + 15) >> 4;
+  const int f0 = tile * NC;
+
+  // the Q^T operands of the wave's tile to its LDS slice in operand order,
+  // and for q4_0 each column's bias term per group of 32 dims (the lane holds
+  // 8 of the group's dims; the four quads hold the rest)
+  extern __shared__ __align__(16) bf16x8_t pf_q_lds[];
+  bf16x8_t* q_lds = pf_q_lds + wave * (NCG * (D / 32) * 64);
+  int pos[NCG];
+  float kb[NCG][D / 32];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int f = f0 + cg * 16 + (lane & 15);
+    const bool live = f < cols;
+    const int j = live ? f / G : 0;
+    const int hg = live ? f % G : 0;
+    pos[cg] = live ? (a.causal ? sq.h + j : sq.n - 1) : -1;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<int64_t>(sq.q0 + j) * a.n_q_heads + g * G + hg) * D + quad * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const bf16x8_t qv = live ? *reinterpret_cast<const bf16x8_t*>(qp + kk * 32) : bf16x8_t{};
+      q_lds[(cg * (D / 32) + kk) * 64 + lane] = qv;
+      kb[cg][kk] = 0.f;
+      if constexpr (FMT == kFmtQ4) {
+        const uint4 w = __builtin_bit_cast(uint4, qv);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        float part_sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          part_sum += __uint_as_float(ws[k] << 16) + __uint_as_float(ws[k] & 0xffff0000u);
+        kb[cg][kk] = -kQ4Bias * sum_xor32(sum_xor16(part_sum));
+      }
+    }
+  }
+  const int pos_min = a.causal ? sq.h + f0 / G : sq.n - 1;
+
+  const unsigned char* kbase = static_cast<const unsigned char*>(a.k_layer);
+  const unsigned char* vbase = static_cast<const unsigned char*>(a.v_layer);
+  constexpr int64_t kTileBytes = q_tile_bytes<D, FMT>();
+  const int32_t* trow = a.tables + static_cast<int64_t>(a.table_rows ? a.table_rows[s] : s) * a.max_blocks;
+  // ring of STAGES raw block pairs; loads past the run repeat its last block (L2 hits)
+  kv_qpair<D, FMT> buf[STAGES];
+  int phys_a[STAGES], phys_b[STAGES];
+  auto issue = [&](int u, int b) {
+    const int pa = trow[min(b, b_end - 1)];
+    const int pb = trow[min(b + 1, b_end - 1)];
+    phys_a[u] = pa;
+    phys_b[u] = pb;
+    const int qa = (pa < 0 || pa >= a.num_blocks) ? 0 : pa;  // never dereferenced out of range
+    const int qb = (pb < 0 || pb >= a.num_blocks) ? 0 : pb;
+    const int64_t ta = (static_cast<int64_t>(qa) * a.n_kv_heads + g) * kTileBytes;
+    const int64_t tb = (static_cast<int64_t>(qb) * a.n_kv_heads + g) * kTileBytes;
+    load_qblock<D, FMT>(buf[u].a, kbase + ta, vbase + ta, lane);
+    load_qblock<D, FMT>(buf[u].b, kbase + tb, vbase + tb, lane);
+  };
+
+  f32x4_t o[NCG][D / 16];
+  float m_run[NCG], l_lane[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) o[cg][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[cg] = -INFINITY;
+    l_lane[cg] = 0.f;
+  }
+  bool poisoned = false;
+  const float c = a.scale_log2;
+
+#pragma unroll
+  for (int u = 0; u < STAGES; ++u) issue(u, b_begin + 2 * u);
+  for (int b0 = b_begin; b0 < b_end; b0 += 2 * STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      const int b = b0 + 2 * u;
+      // (an index the compiler takes to depend on b keeps the LDS reads of
+      // Q^T inside the loop, as in attn_prefill_kernel)
+      int ql;
+      asm("" : "=v"(ql) : "0"(lane), "s"(b));
+      if (b < b_end) {
+        const bool has_b = b + 1 < b_end;  // else the second block is outside the partition: all masked
+        const bool bad_a = phys_a[u] < 0 || phys_a[u] >= a.num_blocks;
+        const bool bad_b = phys_b[u] < 0 || phys_b[u] >= a.num_blocks;
+        poisoned |= bad_a || (has_b && bad_b);
+        const int valid_a = bad_a ? 0 : min(16, sq.n - b * 16);
+        const int valid_b = (!has_b || bad_b) ? 0 : min(16, sq.n - (b + 1) * 16);
+        auto qop = [&](int cg, int kk) { return q_lds[(cg * (D / 32) + kk) * 64 + ql]; };
+        if (valid_a == 16 && valid_b == 16 && b * 16 + 31 <= pos_min) {
+          attend_qpair<D, NCG, FMT>(qop, buf[u], kb, false, nullptr, nullptr, quad, c, o, m_run, l_lane);
+        } else {
+          int lim_a[NCG], lim_b[NCG];
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) {
+            lim_a[cg] = min(max(pos[cg] - b * 16 + 1, 0), valid_a);
+            lim_b[cg] = min(max(pos[cg] - (b + 1) * 16 + 1, 0), valid_b);
+          }
+          attend_qpair<D, NCG, FMT>(qop, buf[u], kb, true, lim_a, lim_b, quad, c, o, m_run, l_lane);
+        }
+      }
+      issue(u, b + 2 * STAGES);
+    }
+  }
+
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const float l = sum_xor32(sum_xor16(l_lane[cg]));
+    const int f = f0 + cg * 16 + (lane & 15);
+    if (f >= cols) continue;
+    const int64_t row = static_cast<int64_t>(sq.q0 + f / G) * a.n_q_heads + g * G + f % G;
+    if (n_parts == 1 && !a.force_partial) {
+      const float inv = 1.f / l;
+      uint16_t* orow = out + row * D;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = poisoned ? nan : o[cg][nt][i] * inv;
+        *reinterpret_cast<uint2*>(orow + nt * 16 + quad * 4) =
+            make_uint2(static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16),
+                       static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16));
+      }
+    } else {
+      const int64_t pi = row * a.max_parts + part;
+      float* po = a.part_o + pi * D;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt)
+        *reinterpret_cast<float4*>(po + nt * 16 + quad * 4) =
+            poisoned ? make_float4(nan, nan, nan, nan)
+                     : make_float4(o[cg][nt][0], o[cg][nt][1], o[cg][nt][2], o[cg][nt][3]);
+      if (quad == 0) {
+        a.part_m[pi] = poisoned ? nan : m_run[cg];
+        a.part_l[pi] = poisoned ? nan : l;
+      }
+    }
+  }
+}
+
 // The same attention with the K/V of each block pair shared through LDS by the
 // WT waves of a partition group (consecutive tiles of one unit, one partition):
 // the group's waves copy disjoint 1 KiB chunks of the pair (K and V tiles of
@@ -828,8 +1139,10 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   if (opts) o = *opts;
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_MFMA)
     return fail(KV_ERR_UNSUPPORTED, "multi-query attention has only the matrix-core kernel");
-  if (!mfma_supported(c, G) || c.dtype != KV_BF16)
-    return fail(KV_ERR_UNSUPPORTED, "multi-query attention needs a bf16 pool, B = 16, d in {64, 128, 256} and G <= 16");
+  const bool quant = is_quantized(c.dtype);
+  if (!mfma_supported(c, G) || (quant && c.head_dim > 128))
+    return fail(KV_ERR_UNSUPPORTED, "the multi-query kernel needs B = 16, G <= 16 and d in {64, 128, 256} (bf16) or "
+                                    "{64, 128} (q8_0 / q4_0)");
   if (o.partition_tokens < 0 || o.partition_tokens % 16 != 0)
     return fail(KV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of the block size");
   if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
@@ -852,7 +1165,7 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
     // Beyond that, one partition per tile.
     const int64_t waves = static_cast<int64_t>(n_seqs) * c.num_kv_heads * p.tiles;
     int64_t want = 8LL * device_cus();
-    if (p.wt >= 2 && c.head_dim <= 128) {
+    if (p.wt >= 2 && c.head_dim <= 128 && !quant) {
       const int64_t ring = static_cast<int64_t>(kPfWaves / p.wt) * (p.wt == 2 ? 3 : 4) * 4 * 16 * c.head_dim * 2;
       const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(2, max_lds_per_cu() / ring));
       want = kPfWaves * per_cu * device_cus();
@@ -903,8 +1216,24 @@ hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st, hipEvent_t 
                       static_cast<uint32_t>(kLds), st, ev0, ev1, a);
 }
 
+// Quantised pools: the register-ring kernel with raw tiles, ring depth 2 pairs.
+template <int D, int NCG, int FMT>
+hipError_t pf_launch_q(const pf_args& a, int64_t grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  constexpr size_t kLds = static_cast<size_t>(kPfWaves) * NCG * (D / 32) * 64 * 16;  // Q^T operands per wave
+  return launch_timed(attn_prefill_q_kernel<D, NCG, FMT, 2>, dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64),
+                      static_cast<uint32_t>(kLds), st, ev0, ev1, a);
+}
+
 template <int D>
-hipError_t pf_launch_d(const pf_args& a, int ncg, int64_t grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t pf_launch_d(const pf_args& a, int ncg, int32_t dtype, int64_t grid, hipStream_t st, hipEvent_t ev0,
+                       hipEvent_t ev1) {
+  if constexpr (D <= 128) {
+    if (dtype == KV_Q8_0)
+      return ncg == 1 ? pf_launch_q<D, 1, kFmtQ8>(a, grid, st, ev0, ev1) : pf_launch_q<D, 2, kFmtQ8>(a, grid, st, ev0, ev1);
+    if (dtype == KV_Q4_0)
+      return ncg == 1 ? pf_launch_q<D, 1, kFmtQ4>(a, grid, st, ev0, ev1) : pf_launch_q<D, 2, kFmtQ4>(a, grid, st, ev0, ev1);
+  }
+  if (dtype != KV_BF16) return hipErrorInvalidValue;
   if (ncg == 1) return pf_launch<D, 1>(a, grid, st, ev0, ev1);
   if constexpr (D <= 128)
     if (ncg == 2) return pf_launch<D, 2>(a, grid, st, ev0, ev1);
@@ -920,13 +1249,14 @@ hipError_t pf_merge(const pf_args& a, hipStream_t st, hipEvent_t ev1) {
 }
 
 // Whether a call goes to the row-wise path (one decode query per chunk row):
-// the generic kernel asked for, or a pool the multi-query kernel does not read
-// (f32, quantised, B != 16, other head sizes).
+// the generic kernel asked for, or a pool the multi-query kernels do not read
+// (f32, B != 16, other head sizes, quantised at d = 256).
 bool rowwise(const kv_pool* pool, int num_q_heads, const kv_attention_options* opts) {
   if (!pool || num_q_heads <= 0 || num_q_heads % pool->cfg.num_kv_heads != 0) return false;
   const int G = num_q_heads / pool->cfg.num_kv_heads;
   if (opts && opts->kernel == KV_KERNEL_GENERIC) return true;
-  return !(mfma_supported(pool->cfg, G) && pool->cfg.dtype == KV_BF16);
+  const kv_pool_config& c = pool->cfg;
+  return !(mfma_supported(c, G) && (c.dtype == KV_BF16 || c.head_dim <= 128));
 }
 
 }  // namespace
@@ -1019,9 +1349,9 @@ kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, v
   const call_events ev = events_of(opts);
   hipError_t e;
   switch (c.head_dim) {
-    case 64: e = pf_launch_d<64>(a, p.ncg, grid, st, ev.start, ev.kernel_stop); break;
-    case 128: e = pf_launch_d<128>(a, p.ncg, grid, st, ev.start, ev.kernel_stop); break;
-    default: e = pf_launch_d<256>(a, p.ncg, grid, st, ev.start, ev.kernel_stop); break;
+    case 64: e = pf_launch_d<64>(a, p.ncg, c.dtype, grid, st, ev.start, ev.kernel_stop); break;
+    case 128: e = pf_launch_d<128>(a, p.ncg, c.dtype, grid, st, ev.start, ev.kernel_stop); break;
+    default: e = pf_launch_d<256>(a, p.ncg, c.dtype, grid, st, ev.start, ev.kernel_stop); break;
   }
   if (kv_status s = hip_check(e, "paged_attention_prefill launch")) return s;
   if (p.max_parts > 1) {

@@ -1,8 +1,8 @@
 """GPU parity of the row-wise multi-query path against the float64 oracle.
 
-paged_attention_prefill sends the pools its multi-query kernel does not read --
-f32, bf16 with B != 16, quantised q8_0 / q4_0 pools -- and calls that ask for
-the generic kernel through one decode query per chunk row: row j of a chunk of
+paged_attention_prefill sends the pools its multi-query kernels do not read --
+f32, bf16 with B != 16, quantised q8_0 / q4_0 pools with d = 256 -- and calls
+that ask for the generic kernel through one decode query per chunk row: row j of a chunk of
 c rows over a context of n tokens reads the first n - c + j + 1 keys.  Bars:
 f32 within 1e-5 max abs; bf16 (and bf16 queries over quantised pools, against
 the oracle's attention over code x scale) within 2e-2 max abs and 5e-3 per-row
@@ -91,16 +91,16 @@ def test_generic_kernel_asked_for():
 
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
 def test_quantised_pools(fmt):
-    announce(f"{fmt} pool: chunks of 16 over histories, through the matrix-core decode kernel")
-    wl = chunk_wl((40, 33, 1), 16, (100, 17, 64), kv_format=fmt)
+    announce(f"{fmt} pool, d = 256: chunks of 16 over histories, through the matrix-core decode kernel")
+    wl = chunk_wl((40, 33, 1), 16, (100, 17, 64), hq=16, hkv=4, d=256, kv_format=fmt)
     ref = OracleReplay(wl).run()
     run = GpuRun(wl, ref=ref).run()
     compare_all(run, ref, draws.BF16, fmt)
 
 
 def test_quantised_rows_in_batches():
-    announce("q8_0 pool, one chunk of 4200 rows (two launches of the decode kernel), sampled rows")
-    wl = chunk_wl((2100, 2100), 2100, (64, 30), kv_format="q8_0")
+    announce("q8_0 pool, d = 256, one chunk of 4200 rows (two launches of the decode kernel), sampled rows")
+    wl = chunk_wl((2100, 2100), 2100, (64, 30), hq=16, hkv=4, d=256, kv_format="q8_0")
     ref = OracleReplay(wl).run()
     run = GpuRun(wl, ref=ref).run()
     got = run.prefill_outputs[0][0].double().cpu().numpy()
