@@ -123,8 +123,9 @@ def parse():
                     help="storage of the KV pool (decode, prefill, verify): bf16, or q8_0 / q4_0 codes with one 2-byte "
                          "scale per 32 values (written by reshape_and_cache, dequantised in the kernel)")
     ap.add_argument("--block-size", type=int, default=0,
-                    help="--op decode: tokens per block of the pool (0 = the workload's, 16); bf16 pools of block "
-                         "size 4, 8, 32 and 64 are read by the matrix-core kernel too")
+                    help="tokens per block of the pool (0 = the workload's, 16); decode reads bf16 pools of block "
+                         "size 4, 8, 32 and 64 with the matrix-core kernel too, --op prefill / verify those of 32 "
+                         "and 64 with the multi-query kernels (4 and 8 row by row)")
     ap.add_argument("--swap-seqs", type=int, default=8, help="--op swap: sequences swapped out and back in per step")
     ap.add_argument("--op", default="decode", choices=["decode", "prefill", "verify", "swap"],
                     help="decode: the decode step of --workload; prefill: the last 512-token chunk of 16 "
@@ -557,6 +558,11 @@ def multi_query_bench(args):
     torch.cuda.set_device(dev)
     prefill = args.op == "prefill"
     base = workloads.prefill_last_chunk() if prefill else workloads.verify_drafts()
+    if args.block_size and args.block_size != base.block_size:
+        # the same tokens in blocks of another size (plus one partly filled block per sequence)
+        n_seq = len(next(op for op in base.ops if op[0] == "prefill")[1])
+        base = replace(base, block_size=args.block_size,
+                       num_blocks=-(-base.num_blocks * base.block_size // args.block_size) + n_seq)
     L = args.layers or (1 if prefill else 4)
     seed = args.seed or base.seed
     Hq, Hkv, d, Bs = base.num_q_heads, base.num_kv_heads, base.head_dim, base.block_size
@@ -655,6 +661,7 @@ def multi_query_bench(args):
             "partition_tokens": args.partition if args.partition > 0 else "auto",
             "kv_storage": args.kv,
             "kv_bytes_per_token_per_layer": kv_per_tok,
+            "block_size": Bs,
             "step": f"{L} x (reshape_and_cache of the chunk + paged_attention_prefill)",
         },
         "attn_call_us": round(attn_s * 1e6, 2),

@@ -56,6 +56,7 @@ struct pf_args {
   float* part_o;            // [total_q * Hq][max_parts][D]
   int n_seqs, total_q, max_q_len, max_blocks, n_q_heads, n_kv_heads, num_blocks;
   int part_blocks, max_parts, cols_per_tile;
+  int block_size;                // B: tokens per table entry (the kernels work in 16-token tiles)
   int wt;                        // tiles per workgroup (1, 2 or 4); the other factor of 4 is partitions
   int tile_groups, part_groups;  // workgroups per unit along tiles and along partitions
   float scale_log2;
@@ -81,17 +82,20 @@ struct kv_pair {
   uint4 v[D / 16];
 };
 
-template <int D>
+// The lane's pieces: K piece i of a tile at kta[i * STRIDE], V piece i at
+// vta[i * STRIDE] (the pointers already hold the lane's offset; STRIDE = 4 B
+// in 16-byte units for block size B, 64 for B = 16).
+template <int D, int STRIDE>
 __device__ __forceinline__ void load_pair(kv_pair<D>& r, const uint4* kta, const uint4* vta, const uint4* ktb,
-                                          const uint4* vtb, int lane) {
+                                          const uint4* vtb) {
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) r.ka[i] = kta[i * 64 + lane];
+  for (int i = 0; i < D / 32; ++i) r.ka[i] = kta[i * STRIDE];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) r.kb[i] = ktb[i * 64 + lane];
+  for (int i = 0; i < D / 32; ++i) r.kb[i] = ktb[i * STRIDE];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
-    const uint2* va = reinterpret_cast<const uint2*>(vta + i * 64 + lane);
-    const uint2* vb = reinterpret_cast<const uint2*>(vtb + i * 64 + lane);
+    const uint2* va = reinterpret_cast<const uint2*>(vta + i * STRIDE);
+    const uint2* vb = reinterpret_cast<const uint2*>(vtb + i * STRIDE);
     const uint2 a0 = va[0], a1 = va[1], b0 = vb[0], b1 = vb[1];
     r.v[2 * i] = make_uint4(a0.x, a0.y, b0.x, b0.y);
     r.v[2 * i + 1] = make_uint4(a1.x, a1.y, b1.x, b1.y);
@@ -236,7 +240,7 @@ __device__ __forceinline__ pf_seq pf_locate(const pf_args& a, int s) {
   pf_seq r;
   r.q0 = a.q_indptr[s];
   r.c = a.q_indptr[s + 1] - r.q0;
-  r.n = min(a.ctx_lens[s], a.max_blocks * 16);
+  r.n = min(a.ctx_lens[s], a.max_blocks * a.block_size);
   r.h = r.n - r.c;
   r.bad = r.c > a.max_q_len || (a.causal && r.c > r.n);
   return r;
@@ -250,8 +254,14 @@ __device__ __forceinline__ int pf_tile_keys(const pf_args& a, const pf_seq& q, i
   return q.h + f_last / G + 1;
 }
 
-template <int D, int NCG, int STAGES>
+// BS is the pool's block size B (16, 32 or 64): 16-token tile j is sub-tile
+// j % (B/16) of table entry j / (B/16), and in the pool's tile layout a lane's
+// K pieces of it start at quad * B + lane % 16 + 16 * sub (16-byte units
+// inside the entry), its V pieces at lane + 64 * sub, piece i 4 B further.
+template <int D, int NCG, int STAGES, int BS = 16>
 __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) {
+  static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
+  constexpr int kSub = BS / 16;
   constexpr int NC = 16 * NCG;
   const int lane = threadIdx.x & 63;
   const int quad = lane >> 4;
@@ -313,21 +323,25 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
 
   const uint4* kpool = static_cast<const uint4*>(a.k_layer);
   const uint4* vpool = static_cast<const uint4*>(a.v_layer);
-  constexpr int kTileVec = 16 * D * 2 / 16;  // 16-byte vectors per tile
+  constexpr int kEntryVec = BS * D * 2 / 16;  // 16-byte vectors per (entry, kv head)
+  const int k_lane = BS == 16 ? lane : quad * BS + (lane & 15);
   const int32_t* trow = a.tables + static_cast<int64_t>(a.table_rows ? a.table_rows[s] : s) * a.max_blocks;
   // ring of STAGES block pairs; loads past the run repeat its last block (L2 hits)
   kv_pair<D> buf[STAGES];
   int phys_a[STAGES], phys_b[STAGES];
   auto issue = [&](int u, int b) {
-    const int pa = trow[min(b, b_end - 1)];
-    const int pb = trow[min(b + 1, b_end - 1)];
+    const int ja = min(b, b_end - 1), jb = min(b + 1, b_end - 1);
+    const int pa = trow[ja / kSub];
+    const int pb = trow[jb / kSub];
     phys_a[u] = pa;
     phys_b[u] = pb;
     const int qa = (pa < 0 || pa >= a.num_blocks) ? 0 : pa;  // never dereferenced out of range
     const int qb = (pb < 0 || pb >= a.num_blocks) ? 0 : pb;
-    const int64_t ta = (static_cast<int64_t>(qa) * a.n_kv_heads + g) * kTileVec;
-    const int64_t tb = (static_cast<int64_t>(qb) * a.n_kv_heads + g) * kTileVec;
-    load_pair<D>(buf[u], kpool + ta, vpool + ta, kpool + tb, vpool + tb, lane);
+    const int64_t ta = (static_cast<int64_t>(qa) * a.n_kv_heads + g) * kEntryVec;
+    const int64_t tb = (static_cast<int64_t>(qb) * a.n_kv_heads + g) * kEntryVec;
+    const int sa = ja % kSub, sb = jb % kSub;
+    load_pair<D, 4 * BS>(buf[u], kpool + ta + 16 * sa + k_lane, vpool + ta + 64 * sa + lane,
+                         kpool + tb + 16 * sb + k_lane, vpool + tb + 64 * sb + lane);
   };
 
   f32x4_t o[NCG][D / 16];
@@ -752,9 +766,14 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_q_kernel(pf_args a
 // so the wait count is a constant.  The loop count is uniform over the
 // workgroup (the largest partition of its groups); a wave with no columns or
 // no keys left copies and waits but does not attend.  D <= 128.
-template <int D, int NCG, int WT, int S>
+// BS: the pool's block size (16, 32 or 64), as for attn_prefill_kernel; the
+// copies put every 16-token tile into its slot in the B = 16 order.
+template <int D, int NCG, int WT, int S, int BS = 16>
 __global__ void __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_prefill_lds_kernel(pf_args a) {
+  static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
+  constexpr int kSub = BS / 16;
+  constexpr int kEntryVec = BS * D * 2 / 16;  // 16-byte vectors per (entry, kv head)
   constexpr int NC = 16 * NCG;
   constexpr int kTileVec = 16 * D * 2 / 16;    // 16-byte vectors per K or V tile
   constexpr int kChunks = 4 * kTileVec / 64;   // 1 KiB chunks per pair: Ka, Kb, Va, Vb
@@ -851,22 +870,34 @@ attn_prefill_lds_kernel(pf_args a) {
   // for a group with no pair) into slot kp mod S.  Chunk c of a pair: tile
   // c / (D/32) (0 Ka, 1 Kb, 2 Va, 3 Vb), 1 KiB piece c % (D/32).
   auto copy_pair = [&](int kp) __attribute__((always_inline)) {
-    int qa = 0, qb = 0;
+    int qa = 0, qb = 0, sa = 0, sb = 0;
     if (my_pairs > 0) {
       const int b = b_begin + 2 * min(kp, my_pairs - 1);
-      const int pa = trow[min(b, grp_b_end - 1)];
-      const int pb = trow[min(b + 1, grp_b_end - 1)];
+      const int ja = min(b, grp_b_end - 1), jb = min(b + 1, grp_b_end - 1);
+      const int pa = trow[ja / kSub];
+      const int pb = trow[jb / kSub];
       qa = (pa < 0 || pa >= a.num_blocks) ? 0 : pa;  // never dereferenced out of range
       qb = (pb < 0 || pb >= a.num_blocks) ? 0 : pb;
+      sa = ja % kSub;
+      sb = jb % kSub;
     }
-    const int64_t ta = (static_cast<int64_t>(qa) * a.n_kv_heads + g) * kTileVec;
-    const int64_t tb = (static_cast<int64_t>(qb) * a.n_kv_heads + g) * kTileVec;
+    const int64_t ta = (static_cast<int64_t>(qa) * a.n_kv_heads + g) * kEntryVec;
+    const int64_t tb = (static_cast<int64_t>(qb) * a.n_kv_heads + g) * kEntryVec;
     u32x4_t* slot = ring + (kp % S) * (kChunks * 64);
 #pragma unroll
     for (int j = 0; j < kMine; ++j) {
       const int c = tw + j * WT;
       const int t = c / (D / 32), i = c % (D / 32);
-      const uint4* src = (t < 2 ? kpool : vpool) + ((t & 1) ? tb : ta) + i * 64 + lane;
+      // the lane's 16-byte piece i of tile t (Ka, Kb, Va, Vb): for B = 16 one
+      // 1 KiB run per piece; for B > 16 the sub-tile's piece in the entry
+      const uint4* src;
+      if constexpr (BS == 16) {
+        src = (t < 2 ? kpool : vpool) + ((t & 1) ? tb : ta) + i * 64 + lane;
+      } else {
+        const int sub = (t & 1) ? sb : sa;
+        src = t < 2 ? kpool + ((t & 1) ? tb : ta) + 16 * sub + i * 4 * BS + quad * BS + (lane & 15)
+                    : vpool + ((t & 1) ? tb : ta) + 64 * sub + i * 4 * BS + lane;
+      }
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
                                        (__attribute__((address_space(3))) void*)(slot + c * 64), 16, 0, 0);
     }
@@ -906,8 +937,8 @@ attn_prefill_lds_kernel(pf_args a) {
     const bool mine = b < b_end;
     if (mine) {
       const u32x4_t* sl = ring + (k % S) * (kChunks * 64);
-      const int pa = trow[b];
-      const int pb = trow[min(b + 1, b_end - 1)];
+      const int pa = trow[b / kSub];
+      const int pb = trow[min(b + 1, b_end - 1) / kSub];
       const bool has_b = b + 1 < b_end;
       const bool bad_a = pa < 0 || pa >= a.num_blocks;
       const bool bad_b = pb < 0 || pb >= a.num_blocks;
@@ -1126,6 +1157,14 @@ int64_t max_lds_per_cu() {
   return bytes;
 }
 
+// The pools the multi-query kernels read: bf16 with B in {16, 32, 64} and d in
+// {64, 128, 256}; q8_0 / q4_0 with B = 16 and d in {64, 128}; G <= 16.
+bool pf_supported(const kv_pool_config& c, int G) {
+  if (G < 1 || G > kMaxGroup || (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256)) return false;
+  if (c.dtype == KV_BF16) return c.block_size == 16 || c.block_size == 32 || c.block_size == 64;
+  return is_quantized(c.dtype) && c.block_size == 16 && c.head_dim <= 128;
+}
+
 kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len, int num_q_heads, int max_blocks,
                      const kv_attention_options* opts, pf_plan& p) {
   if (!pool) return fail(KV_ERR_INVALID, "pool is NULL");
@@ -1140,9 +1179,9 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_MFMA)
     return fail(KV_ERR_UNSUPPORTED, "multi-query attention has only the matrix-core kernel");
   const bool quant = is_quantized(c.dtype);
-  if (!mfma_supported(c, G) || (quant && c.head_dim > 128))
-    return fail(KV_ERR_UNSUPPORTED, "the multi-query kernel needs B = 16, G <= 16 and d in {64, 128, 256} (bf16) or "
-                                    "{64, 128} (q8_0 / q4_0)");
+  if (!pf_supported(c, G))
+    return fail(KV_ERR_UNSUPPORTED, "the multi-query kernels need G <= 16 and bf16 with B in {16, 32, 64}, d in {64, "
+                                    "128, 256}, or q8_0 / q4_0 with B = 16, d in {64, 128}");
   if (o.partition_tokens < 0 || o.partition_tokens % 16 != 0)
     return fail(KV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of the block size");
   if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
@@ -1155,7 +1194,7 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   p.tiles = static_cast<int>((cols + 16 * p.ncg - 1) / (16 * p.ncg));
   p.wt = p.tiles >= 4 ? 4 : (p.tiles >= 2 ? 2 : 1);
   p.tile_groups = (p.tiles + p.wt - 1) / p.wt;
-  const int64_t max_ctx = static_cast<int64_t>(max_blocks) * 16;
+  const int64_t max_ctx = static_cast<int64_t>(max_blocks) * c.block_size;
   if (o.partition_tokens > 0) {
     p.partition = o.partition_tokens;
   } else {
@@ -1194,7 +1233,7 @@ uint64_t pf_workspace(const kv_pool_config& c, int total_q, int num_q_heads, con
 
 // Ring depth in block pairs: the wider tiles hold more accumulators and fewer
 // blocks in flight.
-template <int D, int NCG>
+template <int D, int NCG, int BS>
 hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr size_t kPair = 4 * 16 * D * 2;  // Ka, Kb, Va, Vb
   // several tiles per partition: share each block pair through LDS; ring
@@ -1202,17 +1241,17 @@ hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st, hipEvent_t 
   // per CU), 3 for two groups (96 KiB, one workgroup per CU)
   if constexpr (D <= 128) {
     if (a.wt == 2 && (kPfWaves / 2) * 3 * kPair <= max_lds_per_block()) {
-      return launch_timed(attn_prefill_lds_kernel<D, NCG, 2, 3>, dim3(static_cast<unsigned>(grid)),
+      return launch_timed(attn_prefill_lds_kernel<D, NCG, 2, 3, BS>, dim3(static_cast<unsigned>(grid)),
                           dim3(kPfWaves * 64), (kPfWaves / 2) * 3 * kPair, st, ev0, ev1, a);
     }
     if (a.wt == 4 && (kPfWaves / 4) * 4 * kPair <= max_lds_per_block()) {
-      return launch_timed(attn_prefill_lds_kernel<D, NCG, 4, 4>, dim3(static_cast<unsigned>(grid)),
+      return launch_timed(attn_prefill_lds_kernel<D, NCG, 4, 4, BS>, dim3(static_cast<unsigned>(grid)),
                           dim3(kPfWaves * 64), (kPfWaves / 4) * 4 * kPair, st, ev0, ev1, a);
     }
   }
   constexpr int kStages = D >= 256 ? 1 : 2;
   constexpr size_t kLds = static_cast<size_t>(kPfWaves) * NCG * (D / 32) * 64 * 16;  // Q^T operands per wave
-  return launch_timed(attn_prefill_kernel<D, NCG, kStages>, dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64),
+  return launch_timed(attn_prefill_kernel<D, NCG, kStages, BS>, dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64),
                       static_cast<uint32_t>(kLds), st, ev0, ev1, a);
 }
 
@@ -1234,9 +1273,24 @@ hipError_t pf_launch_d(const pf_args& a, int ncg, int32_t dtype, int64_t grid, h
       return ncg == 1 ? pf_launch_q<D, 1, kFmtQ4>(a, grid, st, ev0, ev1) : pf_launch_q<D, 2, kFmtQ4>(a, grid, st, ev0, ev1);
   }
   if (dtype != KV_BF16) return hipErrorInvalidValue;
-  if (ncg == 1) return pf_launch<D, 1>(a, grid, st, ev0, ev1);
-  if constexpr (D <= 128)
-    if (ncg == 2) return pf_launch<D, 2>(a, grid, st, ev0, ev1);
+  if (ncg == 1) {
+    switch (a.block_size) {
+      case 16: return pf_launch<D, 1, 16>(a, grid, st, ev0, ev1);
+      case 32: return pf_launch<D, 1, 32>(a, grid, st, ev0, ev1);
+      case 64: return pf_launch<D, 1, 64>(a, grid, st, ev0, ev1);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if constexpr (D <= 128) {
+    if (ncg == 2) {
+      switch (a.block_size) {
+        case 16: return pf_launch<D, 2, 16>(a, grid, st, ev0, ev1);
+        case 32: return pf_launch<D, 2, 32>(a, grid, st, ev0, ev1);
+        case 64: return pf_launch<D, 2, 64>(a, grid, st, ev0, ev1);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   return hipErrorInvalidValue;
 }
 
@@ -1250,13 +1304,12 @@ hipError_t pf_merge(const pf_args& a, hipStream_t st, hipEvent_t ev1) {
 
 // Whether a call goes to the row-wise path (one decode query per chunk row):
 // the generic kernel asked for, or a pool the multi-query kernels do not read
-// (f32, B != 16, other head sizes, quantised at d = 256).
+// (f32, B = 4 or 8 and other block sizes, quantised at d = 256).
 bool rowwise(const kv_pool* pool, int num_q_heads, const kv_attention_options* opts) {
   if (!pool || num_q_heads <= 0 || num_q_heads % pool->cfg.num_kv_heads != 0) return false;
   const int G = num_q_heads / pool->cfg.num_kv_heads;
   if (opts && opts->kernel == KV_KERNEL_GENERIC) return true;
-  const kv_pool_config& c = pool->cfg;
-  return !(mfma_supported(c, G) && (c.dtype == KV_BF16 || c.head_dim <= 128));
+  return !pf_supported(pool->cfg, G);
 }
 
 }  // namespace
@@ -1342,6 +1395,7 @@ kv_status paged_attention_prefill(kv_pool* pool, int32_t layer, const void* q, v
   a.tile_groups = p.tile_groups;
   a.part_groups = p.part_groups;
   a.cols_per_tile = 16 * p.ncg;
+  a.block_size = c.block_size;
   a.scale_log2 = p.scale * kLog2e;
   a.causal = 1;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);

@@ -9,6 +9,7 @@ multiple of 16.  The block-size trade-off ([KVM] block-size trade-off; [BT] §09
 makes B a deployment choice, so the fast kernel has to take every common one.
 """
 
+import dataclasses
 import math
 
 import numpy as np
@@ -108,3 +109,91 @@ def test_qwen3_8b_37x2304_at_block_size_32():
     ref = OracleReplay(wl).run()
     run = GpuRun(wl, ref=ref).run()
     check(run.decode_outputs[0][0].double().cpu().numpy(), ref.attention(0, 0), "37 x 2304, B=32")
+
+
+# ---- multi-query attention (chunked prefill) over pools of block size 32 and 64 ----
+# The multi-query kernels read 16-token tiles: tile j is sub-tile j % (B/16) of
+# table entry j / (B/16).  Partitions of 48 tokens make pairs of tiles that
+# straddle two entries.
+
+def chunks_b(bs, prompts, chunk, history, hq=32, hkv=8, d=128, seed=47):
+    seqs = tuple(range(len(prompts)))
+    ops = [("add", s) for s in seqs]
+    grow = tuple(s for s in seqs if history[s])
+    if grow:
+        ops.append(("append", grow, tuple(history[s] for s in grow)))
+    done = [0] * len(prompts)
+    while any(x < p for x, p in zip(done, prompts)):
+        ids = tuple(s for s in seqs if done[s] < prompts[s])
+        counts = tuple(min(chunk, prompts[s] - done[s]) for s in ids)
+        ops.append(("prefill", ids, counts))
+        for s, c in zip(ids, counts):
+            done[s] += c
+    blocks = sum(-(-(p + h) // bs) for p, h in zip(prompts, history)) + 7
+    return workloads.Workload(f"chunks_b{bs}", seed, draws.BF16, 1, hq, hkv, d, bs, blocks, ops)
+
+
+def compare_prefills(run, ref, what):
+    for i in range(len(ref.prefills)):
+        expect = ref.prefill_attention(i, 0)
+        got = run.prefill_outputs[i][0].double().cpu().numpy()
+        first = np.concatenate([[0], np.cumsum(ref.prefills[i]["counts"])])
+        for b in expect:
+            check(got[first[b]:first[b + 1]], expect[b], f"{what} prefill {i} seq {ref.prefills[i]['seq_ids'][b]}")
+
+
+@pytest.mark.parametrize("bs", (32, 64))
+@pytest.mark.parametrize("partition", [0, 16, 48, 4096])
+def test_multi_query_ragged_chunks(bs, partition):
+    announce(f"multi-query, B={bs}: prompts (700, 33, 1, 517, 16, 130) in chunks of 100, partition {partition}")
+    wl = chunks_b(bs, (700, 33, 1, 517, 16, 130), 100, (0, 40, 3, 17, 0, 1))
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1, opts=B.attention_options(partition_tokens=partition)).run()
+    compare_prefills(run, ref, f"B={bs} P={partition}")
+
+
+@pytest.mark.parametrize("bs", (32, 64))
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (64, 8, 128), (16, 1, 128), (32, 8, 64), (16, 4, 256),
+                                      (12, 4, 64)])
+def test_multi_query_head_shapes(bs, hq, hkv, d):
+    announce(f"multi-query, B={bs}, Hq={hq} Hkv={hkv} d={d}: prompts (97, 16, 5) in chunks of 40")
+    wl = chunks_b(bs, (97, 16, 5), 40, (20, 0, 300), hq=hq, hkv=hkv, d=d)
+    ref = OracleReplay(wl).run()
+    for part in (0, 32):
+        run = GpuRun(wl, ref=ref, fill=-1, opts=B.attention_options(partition_tokens=part)).run()
+        compare_prefills(run, ref, f"B={bs} P={part}")
+
+
+@pytest.mark.parametrize("bs", (32, 64))
+def test_multi_query_last_chunk_of_8k_prompts_sampled(bs):
+    announce(f"multi-query, B={bs}: 16 x (7680 cached + 512-token chunk), default launch, rows sampled")
+    base = workloads.prefill_last_chunk()
+    wl = dataclasses.replace(base, block_size=bs, num_blocks=-(-base.num_blocks * 16 // bs) + 16)
+    sample = [0, 7, 15]
+    ref = OracleReplay(wl, writers=sample).run()
+    run = GpuRun(wl, ref=ref, writers=sample).run()
+    got = run.prefill_outputs[0][0].double().cpu().numpy()
+    picks = [(b, j) for b in sample for j in (0, 1, 15, 16, 63, 64, 255, 256, 510, 511)]
+    rows = [b * 512 + j for b, j in picks]
+    check(got[rows], ref.prefill_rows(0, 0, picks), f"B={bs} last chunk sampled")
+
+
+def test_multi_query_bad_entry_b32():
+    announce("multi-query, B=32: a table entry outside [0, N) gives NaN rows for the rows that see it")
+    wl = chunks_b(32, (40, 40), 40, (10, 50))
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()
+    rec = run.prefills[0]
+    tables = torch.from_numpy(rec["tables"]).cuda()
+    lens = torch.from_numpy(rec["lengths"]).cuda()
+    tables[1, 2] = wl.num_blocks + 3  # sequence 1: positions 64..95 (history 50, rows j >= 14 see them)
+    indptr = torch.tensor([0, 40, 80], dtype=torch.int32, device="cuda")
+    out = run.prefill(0, 0, indptr, tables, lens, 40).double().cpu().numpy()
+    expect = ref.prefill_attention(0, 0)
+    check(out[0:40], expect[0], "sequence 0 unaffected")
+    assert np.isnan(out[40 + 14:80]).all()
+    for j in range(14):
+        row = out[40 + j]
+        if not np.isnan(row).all():
+            check(row[None], expect[1][j][None], f"sequence 1 row {j}")
+    torch.cuda.synchronize()
