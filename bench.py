@@ -124,8 +124,8 @@ def parse():
                          "scale per 32 values (written by reshape_and_cache, dequantised in the kernel)")
     ap.add_argument("--block-size", type=int, default=0,
                     help="tokens per block of the pool (0 = the workload's, 16); decode reads bf16 pools of block "
-                         "size 4, 8, 32 and 64 with the matrix-core kernel too, --op prefill / verify those of 32 "
-                         "and 64 with the multi-query kernels (4 and 8 row by row)")
+                         "size 4, 8, 32 and 64 with the matrix-core kernel too, --op prefill / verify with the "
+                         "multi-query kernels")
     ap.add_argument("--swap-seqs", type=int, default=8, help="--op swap: sequences swapped out and back in per step")
     ap.add_argument("--op", default="decode", choices=["decode", "prefill", "verify", "swap"],
                     help="decode: the decode step of --workload; prefill: the last 512-token chunk of 16 "

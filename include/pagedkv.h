@@ -565,14 +565,14 @@ uint64_t paged_prefill_workspace_bytes(const kv_pool* pool, int32_t n_seqs, int3
  * keys include it is written as NaN, and so may be the other rows of its
  * query tile (16 consecutive columns of (row, head)) on the multi-query
  * kernels.  Two paths:
- *   multi-query kernels: bf16 pools with B in {16, 32, 64}, d in {64, 128,
- *     256}, and q8_0 / q4_0 pools with B = 16, d in {64, 128}; G <= 16
+ *   multi-query kernels: bf16 pools with B in {4, 8, 16, 32, 64}, d in {64,
+ *     128, 256}, and q8_0 / q4_0 pools with B = 16, d in {64, 128}; G <= 16
  *     (KV_KERNEL_AUTO or KV_KERNEL_MFMA); one tile of columns reads each
  *     block once for all its rows.  Over a quantised pool the codes are the
  *     matrix operands (exact in bf16) and the group scales are applied in
  *     float32, as in paged_attention_decode ([INF] §8.4.2);
- *   row-wise: every other pool (f32, bf16 with B = 4 or 8, quantised at
- *     d = 256), and any pool with KV_KERNEL_GENERIC -- each chunk row is a
+ *   row-wise: every other pool (f32, quantised at d = 256), and any pool
+ *     with KV_KERNEL_GENERIC -- each chunk row is a
  *     decode query over its n - c + j + 1 keys, through the decode kernels
  *     (the matrix-core split-K kernel, in batches of at most 4095 rows, for
  *     quantised pools and bf16 pools of block size 4, 8, 32 or 64; the

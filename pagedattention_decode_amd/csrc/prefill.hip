@@ -230,6 +230,41 @@ __device__ __forceinline__ void attend_pair(const QOp& qop, const KOp& kop, cons
   }
 }
 
+// The lane's K and V piece bases of 16-token tile j for a pool of block size
+// BS < 16 (16-byte units from the pool base of the layer): the tile gathers
+// 16/BS consecutive table entries, and a lane's K pieces lie in the entry of
+// its key (lane % 16), its V pieces in the entry of its 4 value slots.  Only
+// entries that hold tokens of the context (< n) are read -- the last tile of a
+// context may reach past the table's row.  Returns whether a needed entry lies
+// outside [0, num_blocks) (such an entry is never dereferenced).  TP: the
+// table row's pointer type (a constant-address-space pointer keeps the reads
+// scalar where the caller's copies into LDS would otherwise hide that the
+// table is read-only).
+template <int D, int BS, class TP>
+__device__ __forceinline__ bool gather_tile(TP trow, int j, int n, int num_blocks, int n_kv_heads, int g,
+                                            int lane, const uint4*& kp, const uint4*& vp, const uint4* kpool,
+                                            const uint4* vpool) {
+  static_assert(BS == 4 || BS == 8, "a tile gathers entries");
+  constexpr int kPer = 16 / BS;
+  constexpr int kEntryVec = BS * D * 2 / 16;
+  const int quad = lane >> 4, r = lane & 15;
+  int pk = 0, pv = 0;
+  bool bad = false;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const bool needed = j * 16 + e * BS < n;
+    const int ph = needed ? trow[j * kPer + e] : 0;
+    const bool b = ph < 0 || ph >= num_blocks;
+    bad |= b;
+    const int q = b ? 0 : ph;
+    pk = r / BS == e ? q : pk;
+    pv = quad * 4 / BS == e ? q : pv;
+  }
+  kp = kpool + (static_cast<int64_t>(pk) * n_kv_heads + g) * kEntryVec + quad * BS + r % BS;
+  vp = vpool + (static_cast<int64_t>(pv) * n_kv_heads + g) * kEntryVec + (quad * 4 % BS / 4) * 16 + r;
+  return bad;
+}
+
 // Where a sequence's queries are and whether its arguments are usable.
 struct pf_seq {
   int q0, c, n, h;  // first query row, chunk length, context, history
@@ -254,14 +289,15 @@ __device__ __forceinline__ int pf_tile_keys(const pf_args& a, const pf_seq& q, i
   return q.h + f_last / G + 1;
 }
 
-// BS is the pool's block size B (16, 32 or 64): 16-token tile j is sub-tile
-// j % (B/16) of table entry j / (B/16), and in the pool's tile layout a lane's
-// K pieces of it start at quad * B + lane % 16 + 16 * sub (16-byte units
-// inside the entry), its V pieces at lane + 64 * sub, piece i 4 B further.
+// BS is the pool's block size B (4 .. 64): for B >= 16, 16-token tile j is
+// sub-tile j % (B/16) of table entry j / (B/16), and in the pool's tile layout
+// a lane's K pieces of it start at quad * B + lane % 16 + 16 * sub (16-byte
+// units inside the entry), its V pieces at lane + 64 * sub, piece i 4 B
+// further; for B < 16 a tile gathers 16/B entries (gather_tile).
 template <int D, int NCG, int STAGES, int BS = 16>
 __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) {
-  static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
-  constexpr int kSub = BS / 16;
+  static_assert(BS == 4 || BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size");
+  constexpr int kSub = BS >= 16 ? BS / 16 : 1;
   constexpr int NC = 16 * NCG;
   const int lane = threadIdx.x & 63;
   const int quad = lane >> 4;
@@ -331,6 +367,13 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_kernel(pf_args a) 
   int phys_a[STAGES], phys_b[STAGES];
   auto issue = [&](int u, int b) {
     const int ja = min(b, b_end - 1), jb = min(b + 1, b_end - 1);
+    if constexpr (BS < 16) {
+      const uint4 *ka, *va, *kb, *vb;
+      phys_a[u] = gather_tile<D, BS>(trow, ja, sq.n, a.num_blocks, a.n_kv_heads, g, lane, ka, va, kpool, vpool) ? -1 : 0;
+      phys_b[u] = gather_tile<D, BS>(trow, jb, sq.n, a.num_blocks, a.n_kv_heads, g, lane, kb, vb, kpool, vpool) ? -1 : 0;
+      load_pair<D, 4 * BS>(buf[u], ka, va, kb, vb);
+      return;
+    }
     const int pa = trow[ja / kSub];
     const int pb = trow[jb / kSub];
     phys_a[u] = pa;
@@ -766,13 +809,13 @@ __global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_q_kernel(pf_args a
 // so the wait count is a constant.  The loop count is uniform over the
 // workgroup (the largest partition of its groups); a wave with no columns or
 // no keys left copies and waits but does not attend.  D <= 128.
-// BS: the pool's block size (16, 32 or 64), as for attn_prefill_kernel; the
+// BS: the pool's block size (4 .. 64), as for attn_prefill_kernel; the
 // copies put every 16-token tile into its slot in the B = 16 order.
 template <int D, int NCG, int WT, int S, int BS = 16>
 __global__ void __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_prefill_lds_kernel(pf_args a) {
-  static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
-  constexpr int kSub = BS / 16;
+  static_assert(BS == 4 || BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size");
+  constexpr int kSub = BS >= 16 ? BS / 16 : 1;
   constexpr int kEntryVec = BS * D * 2 / 16;  // 16-byte vectors per (entry, kv head)
   constexpr int NC = 16 * NCG;
   constexpr int kTileVec = 16 * D * 2 / 16;    // 16-byte vectors per K or V tile
@@ -870,6 +913,26 @@ attn_prefill_lds_kernel(pf_args a) {
   // for a group with no pair) into slot kp mod S.  Chunk c of a pair: tile
   // c / (D/32) (0 Ka, 1 Kb, 2 Va, 3 Vb), 1 KiB piece c % (D/32).
   auto copy_pair = [&](int kp) __attribute__((always_inline)) {
+    if constexpr (BS < 16) {
+      // every lane's pieces from the entries its key and value slots lie in
+      const uint4 *ka = kpool, *va = vpool, *kb = kpool, *vb = vpool;
+      if (my_pairs > 0) {
+        const int b = b_begin + 2 * min(kp, my_pairs - 1);
+        const int ja = min(b, grp_b_end - 1), jb = min(b + 1, grp_b_end - 1);
+        gather_tile<D, BS>(trow, ja, sq.n, a.num_blocks, a.n_kv_heads, g, lane, ka, va, kpool, vpool);
+        gather_tile<D, BS>(trow, jb, sq.n, a.num_blocks, a.n_kv_heads, g, lane, kb, vb, kpool, vpool);
+      }
+      u32x4_t* slot = ring + (kp % S) * (kChunks * 64);
+#pragma unroll
+      for (int j = 0; j < kMine; ++j) {
+        const int c = tw + j * WT;
+        const int t = c / (D / 32), i = c % (D / 32);
+        const uint4* base = t == 0 ? ka : (t == 1 ? kb : (t == 2 ? va : vb));
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + i * 4 * BS),
+                                         (__attribute__((address_space(3))) void*)(slot + c * 64), 16, 0, 0);
+      }
+      return;
+    }
     int qa = 0, qb = 0, sa = 0, sb = 0;
     if (my_pairs > 0) {
       const int b = b_begin + 2 * min(kp, my_pairs - 1);
@@ -937,11 +1000,19 @@ attn_prefill_lds_kernel(pf_args a) {
     const bool mine = b < b_end;
     if (mine) {
       const u32x4_t* sl = ring + (k % S) * (kChunks * 64);
-      const int pa = trow[b / kSub];
-      const int pb = trow[min(b + 1, b_end - 1) / kSub];
       const bool has_b = b + 1 < b_end;
-      const bool bad_a = pa < 0 || pa >= a.num_blocks;
-      const bool bad_b = pb < 0 || pb >= a.num_blocks;
+      bool bad_a, bad_b;
+      if constexpr (BS < 16) {
+        const uint4 *k0, *v0;
+        bad_a = gather_tile<D, BS>(trow, b, sq.n, a.num_blocks, a.n_kv_heads, g, lane, k0, v0, kpool, vpool);
+        bad_b = gather_tile<D, BS>(trow, min(b + 1, b_end - 1), sq.n, a.num_blocks, a.n_kv_heads, g, lane, k0, v0,
+                                   kpool, vpool);
+      } else {
+        const int pa = trow[b / kSub];
+        const int pb = trow[min(b + 1, b_end - 1) / kSub];
+        bad_a = pa < 0 || pa >= a.num_blocks;
+        bad_b = pb < 0 || pb >= a.num_blocks;
+      }
       poisoned |= bad_a || (has_b && bad_b);
       const int valid_a = bad_a ? 0 : min(16, sq.n - b * 16);
       const int valid_b = (!has_b || bad_b) ? 0 : min(16, sq.n - (b + 1) * 16);
@@ -1157,11 +1228,12 @@ int64_t max_lds_per_cu() {
   return bytes;
 }
 
-// The pools the multi-query kernels read: bf16 with B in {16, 32, 64} and d in
+// The pools the multi-query kernels read: bf16 with B in {4, 8, 16, 32, 64} and d in
 // {64, 128, 256}; q8_0 / q4_0 with B = 16 and d in {64, 128}; G <= 16.
 bool pf_supported(const kv_pool_config& c, int G) {
   if (G < 1 || G > kMaxGroup || (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256)) return false;
-  if (c.dtype == KV_BF16) return c.block_size == 16 || c.block_size == 32 || c.block_size == 64;
+  if (c.dtype == KV_BF16)
+    return c.block_size == 4 || c.block_size == 8 || c.block_size == 16 || c.block_size == 32 || c.block_size == 64;
   return is_quantized(c.dtype) && c.block_size == 16 && c.head_dim <= 128;
 }
 
@@ -1180,7 +1252,7 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
     return fail(KV_ERR_UNSUPPORTED, "multi-query attention has only the matrix-core kernel");
   const bool quant = is_quantized(c.dtype);
   if (!pf_supported(c, G))
-    return fail(KV_ERR_UNSUPPORTED, "the multi-query kernels need G <= 16 and bf16 with B in {16, 32, 64}, d in {64, "
+    return fail(KV_ERR_UNSUPPORTED, "the multi-query kernels need G <= 16 and bf16 with B in {4, 8, 16, 32, 64}, d in {64, "
                                     "128, 256}, or q8_0 / q4_0 with B = 16, d in {64, 128}");
   if (o.partition_tokens < 0 || o.partition_tokens % 16 != 0)
     return fail(KV_ERR_INVALID, "partition_tokens must be 0 or a positive multiple of the block size");
@@ -1275,6 +1347,8 @@ hipError_t pf_launch_d(const pf_args& a, int ncg, int32_t dtype, int64_t grid, h
   if (dtype != KV_BF16) return hipErrorInvalidValue;
   if (ncg == 1) {
     switch (a.block_size) {
+      case 4: return pf_launch<D, 1, 4>(a, grid, st, ev0, ev1);
+      case 8: return pf_launch<D, 1, 8>(a, grid, st, ev0, ev1);
       case 16: return pf_launch<D, 1, 16>(a, grid, st, ev0, ev1);
       case 32: return pf_launch<D, 1, 32>(a, grid, st, ev0, ev1);
       case 64: return pf_launch<D, 1, 64>(a, grid, st, ev0, ev1);
@@ -1284,6 +1358,8 @@ hipError_t pf_launch_d(const pf_args& a, int ncg, int32_t dtype, int64_t grid, h
   if constexpr (D <= 128) {
     if (ncg == 2) {
       switch (a.block_size) {
+        case 4: return pf_launch<D, 2, 4>(a, grid, st, ev0, ev1);
+        case 8: return pf_launch<D, 2, 8>(a, grid, st, ev0, ev1);
         case 16: return pf_launch<D, 2, 16>(a, grid, st, ev0, ev1);
         case 32: return pf_launch<D, 2, 32>(a, grid, st, ev0, ev1);
         case 64: return pf_launch<D, 2, 64>(a, grid, st, ev0, ev1);
@@ -1304,7 +1380,7 @@ hipError_t pf_merge(const pf_args& a, hipStream_t st, hipEvent_t ev1) {
 
 // Whether a call goes to the row-wise path (one decode query per chunk row):
 // the generic kernel asked for, or a pool the multi-query kernels do not read
-// (f32, B = 4 or 8 and other block sizes, quantised at d = 256).
+// (f32, other block sizes, quantised at d = 256).
 bool rowwise(const kv_pool* pool, int num_q_heads, const kv_attention_options* opts) {
   if (!pool || num_q_heads <= 0 || num_q_heads % pool->cfg.num_kv_heads != 0) return false;
   const int G = num_q_heads / pool->cfg.num_kv_heads;

@@ -1,5 +1,6 @@
-"""GPU parity of the matrix-core decode over bf16 pools whose block size is not
-16 (B = 4, 8, 32, 64), against the float64 oracle at the bf16 bar.
+"""GPU parity of the matrix-core decode and of the multi-query kernels (chunked
+prefill) over bf16 pools whose block size is not 16 (B = 4, 8, 32, 64), against
+the float64 oracle at the bf16 bar.
 
 For B > 16 the kernel reads each table entry as B/16 tiles of 16 tokens; for
 B < 16 a tile gathers 16/B entries, and only the entries holding tokens of the
@@ -111,10 +112,10 @@ def test_qwen3_8b_37x2304_at_block_size_32():
     check(run.decode_outputs[0][0].double().cpu().numpy(), ref.attention(0, 0), "37 x 2304, B=32")
 
 
-# ---- multi-query attention (chunked prefill) over pools of block size 32 and 64 ----
-# The multi-query kernels read 16-token tiles: tile j is sub-tile j % (B/16) of
-# table entry j / (B/16).  Partitions of 48 tokens make pairs of tiles that
-# straddle two entries.
+# ---- multi-query attention (chunked prefill) over pools of block size 4 .. 64 ----
+# The multi-query kernels read 16-token tiles: for B > 16 tile j is sub-tile
+# j % (B/16) of table entry j / (B/16) (partitions of 48 tokens make pairs of
+# tiles that straddle two entries); for B < 16 a tile gathers 16/B entries.
 
 def chunks_b(bs, prompts, chunk, history, hq=32, hkv=8, d=128, seed=47):
     seqs = tuple(range(len(prompts)))
@@ -142,7 +143,7 @@ def compare_prefills(run, ref, what):
             check(got[first[b]:first[b + 1]], expect[b], f"{what} prefill {i} seq {ref.prefills[i]['seq_ids'][b]}")
 
 
-@pytest.mark.parametrize("bs", (32, 64))
+@pytest.mark.parametrize("bs", (4, 8, 32, 64))
 @pytest.mark.parametrize("partition", [0, 16, 48, 4096])
 def test_multi_query_ragged_chunks(bs, partition):
     announce(f"multi-query, B={bs}: prompts (700, 33, 1, 517, 16, 130) in chunks of 100, partition {partition}")
@@ -152,7 +153,7 @@ def test_multi_query_ragged_chunks(bs, partition):
     compare_prefills(run, ref, f"B={bs} P={partition}")
 
 
-@pytest.mark.parametrize("bs", (32, 64))
+@pytest.mark.parametrize("bs", (4, 8, 32, 64))
 @pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (64, 8, 128), (16, 1, 128), (32, 8, 64), (16, 4, 256),
                                       (12, 4, 64)])
 def test_multi_query_head_shapes(bs, hq, hkv, d):
@@ -164,7 +165,7 @@ def test_multi_query_head_shapes(bs, hq, hkv, d):
         compare_prefills(run, ref, f"B={bs} P={part}")
 
 
-@pytest.mark.parametrize("bs", (32, 64))
+@pytest.mark.parametrize("bs", (4, 8, 32, 64))
 def test_multi_query_last_chunk_of_8k_prompts_sampled(bs):
     announce(f"multi-query, B={bs}: 16 x (7680 cached + 512-token chunk), default launch, rows sampled")
     base = workloads.prefill_last_chunk()
@@ -178,15 +179,16 @@ def test_multi_query_last_chunk_of_8k_prompts_sampled(bs):
     check(got[rows], ref.prefill_rows(0, 0, picks), f"B={bs} last chunk sampled")
 
 
-def test_multi_query_bad_entry_b32():
-    announce("multi-query, B=32: a table entry outside [0, N) gives NaN rows for the rows that see it")
-    wl = chunks_b(32, (40, 40), 40, (10, 50))
+@pytest.mark.parametrize("bs", (8, 32))
+def test_multi_query_bad_entry(bs):
+    announce(f"multi-query, B={bs}: a table entry outside [0, N) gives NaN rows for the rows that see it")
+    wl = chunks_b(bs, (40, 40), 40, (10, 50))
     ref = OracleReplay(wl).run()
     run = GpuRun(wl, ref=ref, fill=-1).run()
     rec = run.prefills[0]
     tables = torch.from_numpy(rec["tables"]).cuda()
     lens = torch.from_numpy(rec["lengths"]).cuda()
-    tables[1, 2] = wl.num_blocks + 3  # sequence 1: positions 64..95 (history 50, rows j >= 14 see them)
+    tables[1, 64 // bs] = wl.num_blocks + 3  # sequence 1: positions from 64 (history 50, rows j >= 14 see them)
     indptr = torch.tensor([0, 40, 80], dtype=torch.int32, device="cuda")
     out = run.prefill(0, 0, indptr, tables, lens, 40).double().cpu().numpy()
     expect = ref.prefill_attention(0, 0)

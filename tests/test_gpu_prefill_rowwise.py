@@ -1,8 +1,9 @@
 """GPU parity of the row-wise multi-query path against the float64 oracle.
 
 paged_attention_prefill sends the pools its multi-query kernels do not read --
-f32, bf16 with B != 16, quantised q8_0 / q4_0 pools with d = 256 -- and calls
-that ask for the generic kernel through one decode query per chunk row: row j of a chunk of
+f32, quantised q8_0 / q4_0 pools with d = 256 -- and calls that ask for the
+generic kernel (here also on bf16 pools of block size 4 and 8) through one
+decode query per chunk row: row j of a chunk of
 c rows over a context of n tokens reads the first n - c + j + 1 keys.  Bars:
 f32 within 1e-5 max abs; bf16 (and bf16 queries over quantised pools, against
 the oracle's attention over code x scale) within 2e-2 max abs and 5e-3 per-row
@@ -74,10 +75,10 @@ def test_f32_pool():
 
 @pytest.mark.parametrize("bs", [4, 8])
 def test_bf16_other_block_sizes(bs):
-    announce(f"bf16 pool with B = {bs}, Hq=8 Hkv=2 d=64: chunks of 24")
+    announce(f"bf16 pool with B = {bs}, Hq=8 Hkv=2 d=64, the generic kernel asked for: chunks of 24")
     wl = chunk_wl((50, 24, 3), 24, (40, 17, 0), hq=8, hkv=2, d=64, bs=bs)
     ref = OracleReplay(wl).run()
-    run = GpuRun(wl, ref=ref, fill=-1).run()
+    run = GpuRun(wl, ref=ref, fill=-1, opts=B.attention_options(kernel=B.KV_KERNEL_GENERIC)).run()
     compare_all(run, ref, draws.BF16, f"bf16 B={bs}")
 
 
@@ -111,10 +112,11 @@ def test_quantised_rows_in_batches():
 
 
 def test_contract_violations():
-    announce("row-wise path: c > n, c > max_q_len and a bad table entry give NaN rows, nothing else")
+    announce("row-wise path (generic kernel asked for, B = 8): c > n, c > max_q_len and a bad table entry give "
+             "NaN rows, nothing else")
     wl = chunk_wl((40, 40, 40), 40, (10, 10, 10), hq=8, hkv=2, d=64, bs=8)
     ref = OracleReplay(wl).run()
-    run = GpuRun(wl, ref=ref, fill=-1).run()
+    run = GpuRun(wl, ref=ref, fill=-1, opts=B.attention_options(kernel=B.KV_KERNEL_GENERIC)).run()
     rec = run.prefills[0]
     tables = torch.from_numpy(rec["tables"]).cuda()
     lens = torch.from_numpy(rec["lengths"]).cuda()
