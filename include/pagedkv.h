@@ -510,14 +510,18 @@ kv_status paged_attention_decode_static(kv_pool* pool, int32_t layer, const void
  * result equals paged_attention_decode; the shared blocks are read once per
  * group instead of once per member.  One persistent kernel streams a single
  * work list of prefix units (a group's shared blocks against the queries of
- * up to 64 query columns: members x their G heads) and suffix units (a
+ * up to 64 query columns -- 32 over a quantised pool, 32 and 16 at d = 256:
+ * members x their G heads) and suffix units (a
  * member's remaining blocks against its G heads), cut into per-wave runs by
  * estimated cost; a second kernel folds each member's prefix and suffix
  * partials with the [KVM] recurrences.
  * A member whose shared entries differ from the first member's, or whose
  * context (or the first member's) does not cover them, gets a NaN row (checked
- * on the device); so do the members of a group larger than max_group.  bf16 pools with the
- * matrix-core kernel only (KV_ERR_UNSUPPORTED otherwise).
+ * on the device); so do the members of a group larger than max_group.  bf16,
+ * q8_0 and q4_0 pools (B = 16) with the matrix-core kernel only
+ * (KV_ERR_UNSUPPORTED otherwise); over a quantised pool the codes are the
+ * matrix operands and the group scales are applied in float32, as in
+ * paged_attention_decode ([INF] §8.4.2).
  *   d_group_start:   device int32[n_groups + 1], group_start[0] = 0,
  *                    non-decreasing, group_start[n_groups] = n_seqs.
  *   d_shared_blocks: device int32[n_groups] (0 = no shared prefix).

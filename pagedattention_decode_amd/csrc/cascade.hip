@@ -44,12 +44,13 @@ namespace {
 constexpr int kCsWaves = 4;  // waves per workgroup, one per SIMD
 
 // Column tiles of a prefix unit: 4 (64 query columns) up to d = 128, 2 at
-// d = 256 (register budget of one wave per SIMD).
-template <int D>
+// d = 256 (register budget of one wave per SIMD); over a quantised pool half
+// as many (the raw tiles and their conversion take the registers).
+template <int D, int FMT>
 constexpr int cs_tiles() {
-  return D <= 128 ? 4 : 2;
+  return (D <= 128 ? 4 : 2) / (FMT == kFmtBf16 ? 1 : 2);
 }
-inline int cs_tiles_rt(int d) { return d <= 128 ? 4 : 2; }
+inline int cs_tiles_rt(int d, int32_t dtype) { return (d <= 128 ? 4 : 2) / (dtype == KV_BF16 ? 1 : 2); }
 
 // Register-ring depth: the deepest whose registers fit beside the accumulators
 // of the column tiles and a suffix unit's queries (qpl 16-byte pieces per
@@ -222,10 +223,14 @@ struct cs_cursor {
   int sp, item, kvh, j, nb, trow, j0, n, m0, cnt;
 };
 
-template <int D, int STAGES, int QPL>
+// FMT: bf16, or a quantised pool (q8_0 / q4_0) read as in the decode kernel --
+// the ring holds raw tiles, whose codes become exact bf16 operands per tile;
+// each 32-dim group's score product is scaled by its K scale in float32 and
+// each V group's weights by its V scale ([INF] §8.4.2).
+template <int D, int STAGES, int QPL, int FMT = kFmtBf16>
 __global__ void __launch_bounds__(kCsWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_cascade_kernel(cs_args a) {
-  constexpr int NT = cs_tiles<D>();
+  constexpr int NT = cs_tiles<D, FMT>();
   extern __shared__ __align__(16) int cs_smem[];
   const int n = a.n_seqs;
   const int na = a.n_groups * a.cpg;
@@ -477,8 +482,9 @@ attn_cascade_kernel(cs_args a) {
   int chk_ring[STAGES];   // prefix tiles: lane i < cnt holds member m0 + i's entry of the tile
   // a ring stage: the tile's K/V operands and, when a suffix unit starts at
   // the tile, the unit's queries
+  using ring_t = typename std::conditional<FMT == kFmtBf16, kv_regs<D>, kv_qregs<D, FMT>>::type;
   struct stage_regs {
-    kv_regs<D> kv;
+    ring_t kv;
     uint4 q[QPL];
   };
   // the table entry of the tile at cursor c; the caller reads it and hands it
@@ -503,8 +509,14 @@ attn_cascade_kernel(cs_args a) {
     if (ld.sp == 0 && lane < ld.cnt)
       chk_ring[u] = a.tables[static_cast<int64_t>(ld.m0 + lane) * a.max_blocks + jt];
     const int p = bad ? 0 : phys;  // never dereferenced out of range
-    const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * kTileVec;
-    load_block<D>(sr.kv, kpool + t, vpool + t, lane);
+    if constexpr (FMT == kFmtBf16) {
+      const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * kTileVec;
+      load_block<D>(sr.kv, kpool + t, vpool + t, lane);
+    } else {
+      const int64_t t = (static_cast<int64_t>(p) * Hkv + ld.kvh) * q_tile_bytes<D, FMT>();
+      load_qblock<D, FMT>(sr.kv, static_cast<const unsigned char*>(a.k_layer) + t,
+                          static_cast<const unsigned char*>(a.v_layer) + t, lane);
+    }
     if (++ld_k < n_blk) {
       const int item = ld.item, kvh = ld.kvh;
       advance(ld);
@@ -556,6 +568,9 @@ attn_cascade_kernel(cs_args a) {
   constexpr bool kQRegs = D <= 128;
   bf16x8_t qf[kQRegs ? NT : 1][kQRegs ? D / 32 : 1];
   const uint16_t* q_lane[NT];
+  // q4_0: -kQ4Bias times each column's query sum over group kk (the start of
+  // that group's score product, which cancels the code bias)
+  float kb[FMT == kFmtQ4 ? NT : 1][FMT == kFmtQ4 ? D / 32 : 1];
   int ntiles = 1, ncols = G;
   // a unit's first tile, at ring stage u: its queries into place
   auto start_unit = [&](const stage_regs& sr) __attribute__((always_inline)) {
@@ -599,6 +614,17 @@ attn_cascade_kernel(cs_args a) {
       if constexpr (kQRegs) {
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) qf[t][kk] = *reinterpret_cast<const bf16x8_t*>(q_lane[t] + kk * 32);
+      }
+      if constexpr (FMT == kFmtQ4) {
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+          const uint4 w = *reinterpret_cast<const uint4*>(q_lane[t] + kk * 32);
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+          float part = 0.f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) part += __uint_as_float(ws[k] << 16) + __uint_as_float(ws[k] & 0xffff0000u);
+          kb[t][kk] = -kQ4Bias * sum_xor32(sum_xor16(part));
+        }
       }
     }
   };
@@ -712,6 +738,99 @@ attn_cascade_kernel(cs_args a) {
       for (int i = 0; i < D / 16; ++i) asm volatile("" : "+a"(o[t][i]));
   };
 
+  // The same step on a raw quantised tile: the codes as exact bf16 operands,
+  // each group's score product scaled by the tile's K scale of that group and
+  // slot, the V scales folded into one weight operand per group (a slot past
+  // `valid` gets weight 0 by selection: its scale and codes may be anything);
+  // l sums the unrounded weights, as the decode kernel's quantised step.
+  auto attend_tiles_q = [&](const auto& raw, int valid) __attribute__((always_inline)) {
+    kv_regs<D> cur;
+    codes_block<D, FMT>(raw, cur);
+    f32x4_t sc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntiles) continue;  // wave uniform
+      sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const float b0 = FMT == kFmtQ4 ? kb[FMT == kFmtQ4 ? t : 0][FMT == kFmtQ4 ? kk : 0] : 0.f;
+        const f32x4_t x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, cur.k[kk]),
+            kQRegs ? qf[kQRegs ? t : 0][kQRegs ? kk : 0] : *reinterpret_cast<const bf16x8_t*>(q_lane[t] + kk * 32),
+            (f32x4_t{b0, b0, b0, b0}), 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[t][i] = __builtin_fmaf(scale_at<D>(raw.ks, i, kk), x[i], sc[t][i]);
+      }
+    }
+    if (valid < 16) {  // wave uniform
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t >= ntiles) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (quad * 4 + i >= valid) sc[t][i] = -INFINITY;
+      }
+    }
+    float mb[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntiles) continue;
+      mb[t] = maxn_xor16(maxn(maxn3(sc[t][0], sc[t][1], sc[t][2]), sc[t][3]));
+    }
+    bool grow_any = false;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntiles) continue;
+      mb[t] = maxn_xor32(mb[t]) * a.scale_log2;
+      grow_any |= mb[t] > m_run[t] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow_any)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t >= ntiles) continue;
+        const float m_new = mb[t] > m_run[t] + kRescaleSlack ? mb[t] : m_run[t];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);
+        l_lane[t] *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) o[t][i] *= alpha;
+        m_run[t] = m_new;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntiles) continue;
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][i], a.scale_log2, -m_run[t]));
+      l_lane[t] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+#pragma unroll
+      for (int pp = 0; pp < D / 32; ++pp) {
+        float w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __builtin_fmaf(scale_at<D>(raw.vs, i, pp), pv[i], 0.f);
+        if (valid < 16) {  // wave uniform
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = pv[i] == 0.f ? 0.f : w[i];
+        }
+        const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])));
+        const uint2* halves = reinterpret_cast<const uint2*>(&cur.v[pp]);
+        o[t][2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[0]), pop,
+                                                                 o[t][2 * pp], 0, 0, 0);
+        o[t][2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, halves[1]), pop,
+                                                                     o[t][2 * pp + 1], 0, 0, 0);
+        if constexpr (FMT == kFmtQ4) {
+          const s16x4_t nb = __builtin_bit_cast(s16x4_t, make_uint2(kQ4NegBiasPair, kQ4NegBiasPair));
+          o[t][2 * pp] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nb, pop, o[t][2 * pp], 0, 0, 0);
+          o[t][2 * pp + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(nb, pop, o[t][2 * pp + 1], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) asm volatile("" : "+a"(o[t][i]));
+  };
+
   // writes the partial of the current unit's run and resets the state
   auto finish = [&]() __attribute__((always_inline)) {
     const int64_t unit = static_cast<int64_t>(cs.item) * Hkv + cs.kvh;
@@ -760,7 +879,10 @@ attn_cascade_kernel(cs_args a) {
         if (cs.sp == 0)
           bad_members |= __builtin_amdgcn_ballot_w64(lane < cs.cnt && chk_ring[u] != phys_ring[u]);
         const int valid = bad ? 0 : min(16, cs.n - (cs.j0 + cs.j) * 16);
-        attend_tiles(buf[u].kv, valid);
+        if constexpr (FMT == kFmtBf16)
+          attend_tiles(buf[u].kv, valid);
+        else
+          attend_tiles_q(buf[u].kv, valid);
         if (cs.j == cs.nb - 1 || k == n_blk - 1) {  // end of this unit's run
           finish();
           if (k + 1 < n_blk) {
@@ -946,9 +1068,9 @@ kv_status cs_resolve(const kv_pool* pool, int n_seqs, int n_groups, int max_grou
   if (opts) o = *opts;
   if (o.kernel != KV_KERNEL_AUTO && o.kernel != KV_KERNEL_MFMA && o.kernel != KV_KERNEL_GENERIC)
     return fail(KV_ERR_INVALID, "unknown kernel selector");
-  if (c.dtype != KV_BF16 || !mfma_supported(c, G) || o.kernel == KV_KERNEL_GENERIC)
-    return fail(KV_ERR_UNSUPPORTED, "the cascade decode needs a bf16 pool with B = 16, d in {64, 128, 256}, G <= 16 "
-                                    "and the matrix-core kernel");
+  if (!mfma_supported(c, G) || o.kernel == KV_KERNEL_GENERIC)
+    return fail(KV_ERR_UNSUPPORTED, "the cascade decode needs a bf16, q8_0 or q4_0 pool with B = 16, d in {64, 128, "
+                                    "256}, G <= 16 and the matrix-core kernel");
   if (n_seqs < 1 || max_blocks <= 0) return fail(KV_ERR_INVALID, "n_seqs and max_blocks_per_seq must be positive");
   if (n_groups < 1 || n_groups > n_seqs || max_group < 1)
     return fail(KV_ERR_INVALID, "need 1 <= n_groups <= n_seqs and max_group >= 1");
@@ -957,7 +1079,7 @@ kv_status cs_resolve(const kv_pool* pool, int n_seqs, int n_groups, int max_grou
   if (!(o.scale >= 0.f) || std::isinf(o.scale)) return fail(KV_ERR_INVALID, "scale must be finite and >= 0");
   p.scale = o.scale > 0.f ? o.scale : 1.f / std::sqrt(static_cast<float>(c.head_dim));
   p.part_blocks = o.partition_tokens ? o.partition_tokens / 16 : 1;
-  p.nt = cs_tiles_rt(c.head_dim);
+  p.nt = cs_tiles_rt(c.head_dim, c.dtype);
   p.acol = 16 * p.nt;
   p.waves = static_cast<int64_t>(kCsWaves) * device_cus();
   // LDS: the plan, then per wave a prefix slot of mc members' queries and a
@@ -1024,26 +1146,33 @@ kv_status cs_resolve(const kv_pool* pool, int n_seqs, int n_groups, int max_grou
   return KV_OK;
 }
 
-template <int D, int QPL>
+template <int D, int QPL, int FMT>
 hipError_t cs_launch_q(const cs_args& a, const cs_plan& p, hipStream_t st, const call_events& ev) {
-  return launch_timed(attn_cascade_kernel<D, cs_stages(D, QPL), QPL>, dim3(static_cast<unsigned>(p.waves / kCsWaves)),
+  return launch_timed(attn_cascade_kernel<D, cs_stages(D, QPL), QPL, FMT>, dim3(static_cast<unsigned>(p.waves / kCsWaves)),
                       dim3(kCsWaves * 64), static_cast<uint32_t>(p.lds), st, ev.start, ev.kernel_stop, a);
 }
 
-template <int D>
+template <int D, int FMT>
 hipError_t cs_launch(const cs_args& a, const cs_plan& p, hipStream_t st, const call_events& ev) {
   // 16-byte pieces per lane of a suffix unit's G x D queries
   const int qpl = (a.n_q_heads / a.n_kv_heads * D + 511) / 512;
   hipError_t e;
   // (G <= 16: at most 16 D / 512 pieces)
-  if (qpl <= 1) e = cs_launch_q<D, 1>(a, p, st, ev);
-  else if (qpl <= 2 || D == 64) e = cs_launch_q<D, 2>(a, p, st, ev);
-  else if (qpl <= 4 || D == 128) e = cs_launch_q<D, std::min(4, 16 * D / 512)>(a, p, st, ev);
-  else e = cs_launch_q<D, 16 * D / 512>(a, p, st, ev);
+  if (qpl <= 1) e = cs_launch_q<D, 1, FMT>(a, p, st, ev);
+  else if (qpl <= 2 || D == 64) e = cs_launch_q<D, 2, FMT>(a, p, st, ev);
+  else if (qpl <= 4 || D == 128) e = cs_launch_q<D, std::min(4, 16 * D / 512), FMT>(a, p, st, ev);
+  else e = cs_launch_q<D, 16 * D / 512, FMT>(a, p, st, ev);
   if (e != hipSuccess) return e;
   const int64_t items = static_cast<int64_t>(a.n_seqs) * a.n_q_heads;
   return launch_timed(cascade_merge_kernel<D>, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), 0u, st,
                       nullptr, ev.stop, a);
+}
+
+template <int D>
+hipError_t cs_dispatch(int32_t dtype, const cs_args& a, const cs_plan& p, hipStream_t st, const call_events& ev) {
+  if (dtype == KV_Q8_0) return cs_launch<D, kFmtQ8>(a, p, st, ev);
+  if (dtype == KV_Q4_0) return cs_launch<D, kFmtQ4>(a, p, st, ev);
+  return cs_launch<D, kFmtBf16>(a, p, st, ev);
 }
 
 }  // namespace
@@ -1126,9 +1255,9 @@ kv_status paged_attention_decode_cascade(kv_pool* pool, int32_t layer, const voi
   const call_events ev = events_of(opts);
   hipError_t e;
   switch (c.head_dim) {
-    case 64: e = cs_launch<64>(a, p, st, ev); break;
-    case 128: e = cs_launch<128>(a, p, st, ev); break;
-    default: e = cs_launch<256>(a, p, st, ev); break;
+    case 64: e = cs_dispatch<64>(c.dtype, a, p, st, ev); break;
+    case 128: e = cs_dispatch<128>(c.dtype, a, p, st, ev); break;
+    default: e = cs_dispatch<256>(c.dtype, a, p, st, ev); break;
   }
   return hip_check(e, "cascade decode launch");
 }

@@ -1,10 +1,13 @@
 """GPU parity of the read-once decode over shared prefixes (cascade) against the
-float64 oracle, bf16 bar.  The groups come from the library's own plan of the
+float64 oracle, bf16 bar (over q8_0 / q4_0 pools against the oracle's attention
+over code x scale).  The groups come from the library's own plan of the
 host tables unless a test gives them; outputs and workspace start as NaN bytes.
 The fork workload (4 roots x 16 forks, 512 steps, 36 layers) is checked with
 the read-once decode beside the plain one in test_gpu_parity.py
 (test_agentic_fork_sampled), so that its long replay runs once.
 """
+
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -114,13 +117,6 @@ def test_contract_violations_give_nan_rows():
     out = run.decode_cascade(0, 0, max_group=2).double().cpu().numpy()
     assert np.isnan(out[:3]).all()
     check(out[3:5], expect[3:5], "group 1")
-    # quantised pools are refused
-    qwl = fork_workload([(40, [0, 2])])
-    from dataclasses import replace
-    qrun = GpuRun(replace(qwl, kv_format="q8_0")).run()
-    with pytest.raises(B.KVError) as e:
-        qrun.decode_cascade(0, 0)
-    assert e.value.status == B.KV_ERR_UNSUPPORTED
     torch.cuda.synchronize()
 
 
@@ -152,3 +148,57 @@ def test_timing_events_leave_results_unchanged():
         k_ms, c_ms = evs[0].elapsed_time(evs[1]), evs[0].elapsed_time(evs[2])
         print(f"  preparation + prefix {k_ms * 1e3:.1f} us, call {c_ms * 1e3:.1f} us", flush=True)
         assert 0.0 < k_ms <= c_ms
+
+
+# ---- quantised pools (q8_0 / q4_0): the read-once kernel with raw tiles ----
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("partition", [0, 64, 512])
+def test_quantised_ragged_groups(fmt, partition):
+    announce(f"{fmt}: ragged fork groups, empty suffixes and singletons, partition {partition}, NaN background")
+    groups = [(32, [0, 0, 5]), (100, [1, 17, 300, 0]), (7, [20]), (512, [16, 16, 16, 16, 33, 1000]), (48, [0])]
+    wl = replace(fork_workload(groups), kv_format=fmt)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()
+    out = run.decode_cascade(0, 0, opts=B.attention_options(partition_tokens=partition)).double().cpu().numpy()
+    check(out, ref.attention(0, 0), f"{fmt} ragged groups P={partition}")
+    plain = run.decode_outputs[0][0].double().cpu().numpy()
+    assert np.abs(out - plain).max() <= 2 * BF16_ABS, "read-once and plain decode of the same pool"
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_quantised_shared_prefix_16x8448_full(fmt):
+    announce(f"{fmt}: 16 x 8448 tokens sharing 6144, read-once decode vs oracle")
+    wl = replace(workloads.shared_prefix(), kv_format=fmt)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref).run()
+    out = run.decode_cascade(0, 0).double().cpu().numpy()
+    check(out, ref.attention(0, 0), f"{fmt} 16 x 8448")
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 64), (16, 2, 256), (64, 4, 128)])
+def test_quantised_head_shapes(fmt, hq, hkv, d):
+    announce(f"{fmt}: read-once decode, Hq={hq} Hkv={hkv} d={d}, two groups and a singleton")
+    wl = replace(fork_workload([(96, [0, 5, 40]), (33, [0]), (300, [17, 1])], hq=hq, hkv=hkv, d=d, seed=67),
+                 kv_format=fmt)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()
+    out = run.decode_cascade(0, 0).double().cpu().numpy()
+    check(out, ref.attention(0, 0), f"{fmt} Hq={hq} Hkv={hkv} d={d}")
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_quantised_mismatched_member_gives_nan_row(fmt):
+    announce(f"{fmt}: a member whose shared table entry differs gets a NaN row, the others are exact")
+    wl = replace(fork_workload([(64, [0, 3, 20]), (80, [2, 2])]), kv_format=fmt)
+    ref = OracleReplay(wl).run()
+    run = GpuRun(wl, ref=ref, fill=-1).run()
+    rec = run.decodes[0]
+    expect = ref.attention(0, 0)
+    tables = rec["tables"].copy()
+    tables[2, 0] = tables[2, 1]
+    out = run.decode_cascade(0, 0, tables=tables).double().cpu().numpy()
+    assert np.isnan(out[2]).all()
+    check(out[[0, 1, 3, 4]], expect[[0, 1, 3, 4]], f"{fmt} other members")
+    torch.cuda.synchronize()
