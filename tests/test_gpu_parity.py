@@ -135,11 +135,10 @@ def test_tiny_fp32_5_7_9():
     compare_all_decodes(run, ref)
 
 
-@pytest.mark.parametrize("kernel", [B.KV_KERNEL_GENERIC, B.KV_KERNEL_MFMA])
-@pytest.mark.parametrize("dtype", [draws.BF16, draws.F32])
-def test_small_fork_workload(kernel, dtype):
-    if kernel == B.KV_KERNEL_MFMA and dtype == draws.F32:
-        pytest.skip("the matrix-core kernel is bf16 only")
+# (the matrix-core kernel reads bf16 and quantised pools, not f32 ones)
+@pytest.mark.parametrize("dtype,kernel", [(draws.BF16, B.KV_KERNEL_GENERIC), (draws.BF16, B.KV_KERNEL_MFMA),
+                                          (draws.F32, B.KV_KERNEL_GENERIC)])
+def test_small_fork_workload(dtype, kernel):
     announce(f"small fork workload with CoW: {dtype}, kernel {kernel}")
     wl = small_fork_workload(dtype, 16, 128)
     ref = OracleReplay(wl).run()
