@@ -21,6 +21,10 @@
 // where it ends inside a unit; cascade_merge_kernel folds, per (member, query
 // head), the partials of its prefix unit and of its suffix unit.
 //
+// Over a quantised pool (q8_0 / q4_0) the ring holds raw tiles and the codes
+// feed the matrix instructions, the group scales applied in float32 ([INF]
+// §8.4.2); a prefix unit then carries 2 column tiles instead of 4.
+//
 // The contract is checked on the device: a member whose shared table entries
 // differ from the first member's (compared tile by tile as the prefix
 // streams), whose context or whose first member's context does not cover

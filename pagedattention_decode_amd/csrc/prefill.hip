@@ -29,6 +29,11 @@
 // its last visible position.  A tile whose keys fit one partition writes its
 // final rows; otherwise every partition writes (m, l, O) and merge_prefill
 // folds them with the running-max recurrences.
+// The kernels work in 16-token tiles whatever the pool's block size B (4 ..
+// 64: a table entry holds B/16 tiles, or a tile gathers 16/B entries), and a
+// quantised pool (q8_0 / q4_0, B = 16, d <= 128) has a kernel of its own that
+// feeds the codes to the matrix instructions and applies the group scales in
+// float32 ([INF] §8.4.2).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
