@@ -65,3 +65,23 @@ def test_roofline_never_above_peak(args):
 def test_verify_line():
     d = run_bench("--op", "verify", "--steps", "2", "--warmup", "1", "--no-cpu-baseline")
     assert d["roofline"]["bound"] == "hbm" and 0 < d["roofline"]["frac"] <= 1 and d["value"] > 0
+
+
+@pytest.mark.parametrize("args", [
+    ("--op", "prefill", "--kv", "q8_0"),
+    ("--op", "verify", "--kv", "q4_0"),
+    ("--op", "prefill", "--block-size", "32"),
+    ("--op", "verify", "--block-size", "8"),
+    ("--workload", "shared_prefix_16x8448", "--cascade", "--kv", "q8_0"),
+])
+def test_other_storage_and_block_sizes(args):
+    """The multi-query lines over quantised pools and other block sizes, and the
+    read-once decode over a quantised pool: one JSON line whose config names
+    the storage / block size, the roofline within the peak."""
+    d = run_bench(*args, "--steps", "2", "--warmup", "1", "--no-cpu-baseline")
+    r = d["roofline"]
+    assert 0 < r["frac"] <= 1 and d["value"] > 0, r
+    if "--kv" in args:
+        assert d["config"]["kv_storage"] == args[args.index("--kv") + 1]
+    if "--block-size" in args:
+        assert d["config"]["block_size"] == int(args[args.index("--block-size") + 1])
