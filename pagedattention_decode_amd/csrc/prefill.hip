@@ -619,9 +619,12 @@ __device__ __forceinline__ void attend_qpair(const QOp& qop, const kv_qpair<D, F
 
 // The register-ring multi-query kernel over a quantised pool: work split,
 // queries in LDS, masks, partials and output exactly as attn_prefill_kernel;
-// the ring holds STAGES raw block pairs (codes and scales of K and V).
+// the ring holds STAGES raw block pairs (codes and scales of K and V).  Two
+// waves per SIMD: the code conversion and scaling are vector work that one
+// wave's own dependency chains leave idle; the launch takes one column group
+// per wave (the registers of two column groups do not fit beside a second wave).
 template <int D, int NCG, int FMT, int STAGES>
-__global__ void __launch_bounds__(kPfWaves * 64) attn_prefill_q_kernel(pf_args a) {
+__global__ void __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_prefill_q_kernel(pf_args a) {
   static_assert(FMT == kFmtQ8 || FMT == kFmtQ4, "quantised pools");
   static_assert(D <= 128, "d <= 128");
   constexpr int NC = 16 * NCG;
@@ -1267,7 +1270,7 @@ kv_status pf_resolve(const kv_pool* pool, int n_seqs, int total_q, int max_q_len
   // 16-column groups per wave: two when there are enough columns for several
   // two-group tiles (the LDS-sharing kernel then reads each pair from LDS once
   // per 32 columns instead of 16); one otherwise, and at d = 256
-  p.ncg = (c.head_dim <= 128 && cols > 64) ? 2 : 1;
+  p.ncg = (c.head_dim <= 128 && cols > 64 && !quant) ? 2 : 1;
   p.tiles = static_cast<int>((cols + 16 * p.ncg - 1) / (16 * p.ncg));
   p.wt = p.tiles >= 4 ? 4 : (p.tiles >= 2 ? 2 : 1);
   p.tile_groups = (p.tiles + p.wt - 1) / p.wt;
@@ -1332,11 +1335,12 @@ hipError_t pf_launch(const pf_args& a, int64_t grid, hipStream_t st, hipEvent_t 
                       static_cast<uint32_t>(kLds), st, ev0, ev1, a);
 }
 
-// Quantised pools: the register-ring kernel with raw tiles, ring depth 2 pairs.
+// Quantised pools: the register-ring kernel with raw tiles, one column group
+// per wave, two waves per SIMD; ring depth 2 pairs (1 at d = 128).
 template <int D, int NCG, int FMT>
 hipError_t pf_launch_q(const pf_args& a, int64_t grid, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr size_t kLds = static_cast<size_t>(kPfWaves) * NCG * (D / 32) * 64 * 16;  // Q^T operands per wave
-  return launch_timed(attn_prefill_q_kernel<D, NCG, FMT, 2>, dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64),
+  return launch_timed(attn_prefill_q_kernel<D, NCG, FMT, D >= 128 ? 1 : 2>, dim3(static_cast<unsigned>(grid)), dim3(kPfWaves * 64),
                       static_cast<uint32_t>(kLds), st, ev0, ev1, a);
 }
 
@@ -1344,10 +1348,8 @@ template <int D>
 hipError_t pf_launch_d(const pf_args& a, int ncg, int32_t dtype, int64_t grid, hipStream_t st, hipEvent_t ev0,
                        hipEvent_t ev1) {
   if constexpr (D <= 128) {
-    if (dtype == KV_Q8_0)
-      return ncg == 1 ? pf_launch_q<D, 1, kFmtQ8>(a, grid, st, ev0, ev1) : pf_launch_q<D, 2, kFmtQ8>(a, grid, st, ev0, ev1);
-    if (dtype == KV_Q4_0)
-      return ncg == 1 ? pf_launch_q<D, 1, kFmtQ4>(a, grid, st, ev0, ev1) : pf_launch_q<D, 2, kFmtQ4>(a, grid, st, ev0, ev1);
+    if (dtype == KV_Q8_0) return pf_launch_q<D, 1, kFmtQ8>(a, grid, st, ev0, ev1);
+    if (dtype == KV_Q4_0) return pf_launch_q<D, 1, kFmtQ4>(a, grid, st, ev0, ev1);
   }
   if (dtype != KV_BF16) return hipErrorInvalidValue;
   if (ncg == 1) {
