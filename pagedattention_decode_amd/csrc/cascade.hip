@@ -187,17 +187,17 @@ struct cs_split {
     return static_cast<int64_t>(Hkv) * cb + kvh * uc + (weighted ? (k ? wu + static_cast<int64_t>(k) * w : 0) : k);
   }
   // the wave that takes a partition starting at cost st
-  __device__ int64_t owner(int64_t st) const { return ((st + 1) * W - 1) / C; }
+  __device__ int64_t owner(int64_t st) const { return div_nn((st + 1) * W - 1, C); }
   // with item (whose cost range holds c), its partitions np, costs before cb
   // and per kv head uc, partitions before pb: the first partition (global
   // index) whose starting cost is >= c
   __device__ int64_t first_at(int64_t c, int item, int np, int64_t cb, int64_t uc, int64_t pb) const {
     const int64_t r = c - static_cast<int64_t>(Hkv) * cb;
-    const int64_t h = r / uc, r2 = r % uc;
+    const int64_t h = div_nn(r, uc), r2 = r - h * uc;
     int64_t k;
     if (weighted) {
       const int w = item < na ? wa : wb;
-      k = r2 == 0 ? 0 : (r2 <= wu ? 1 : (r2 - wu + w - 1) / w);
+      k = r2 == 0 ? 0 : (r2 <= wu ? 1 : div_nn(r2 - wu + w - 1, w));
     } else {
       k = r2;
     }
@@ -360,7 +360,7 @@ attn_cascade_kernel(cs_args a) {
       a.mdesc[i] = d;
     }
   }
-  const int64_t p_begin = first_at(wid * split.C / W), p_end = first_at((wid + 1) * split.C / W);
+  const int64_t p_begin = first_at(div_nn(wid * split.C, W)), p_end = first_at(div_nn((wid + 1) * split.C, W));
   if (p_begin >= p_end) return;
 
   // unit data that depends on the item
@@ -399,8 +399,9 @@ attn_cascade_kernel(cs_args a) {
     c.item = max(passed - 1, 0);
     const int np = rfl(cum_p[c.item + 1]) - rfl(cum_p[c.item]);
     const int64_t r = pp - static_cast<int64_t>(Hkv) * rfl(cum_p[c.item]);
-    c.kvh = static_cast<int>(r / np);
-    c.j = static_cast<int>(r % np) * a.part_blocks;
+    const int64_t h = div_nn(r, np);
+    c.kvh = static_cast<int>(h);
+    c.j = static_cast<int>(r - h * np) * a.part_blocks;
     fill_unit(c);
   };
   auto flat = [&](const cs_cursor& c) __attribute__((always_inline)) -> int64_t {
@@ -942,7 +943,7 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(cs_args a) {
     const bool pre = i < n_a;
     const int64_t w = pre ? wFA + i : wFB + (i - n_a);
     row = pre ? (w + uA) * a.acol + col_a : (w + uB) * G + hg;
-    return split.weighted || w * split.C / W < (w + 1) * split.C / W;
+    return split.weighted || div_nn(w * split.C, W) < div_nn((w + 1) * split.C, W);
   };
   auto entry = [&](int i, float& m, float& l, int64_t& row) {
     const bool pre = i < n_a;

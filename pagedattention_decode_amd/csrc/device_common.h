@@ -73,6 +73,15 @@ __device__ __forceinline__ float dpp_f32(float x) {
 // gets the result): a butterfly in which every step pairs disjoint lane
 // groups -- DPP within a row, then the permlane swaps across rows -- so no
 // step goes through the LDS pipe.
+// a / b for a >= 0, b > 0: in 32-bit arithmetic when both fit in 32 bits
+// (every work-split quotient of the workloads here), which takes a small
+// fraction of the instructions of the 64-bit division sequence.
+__device__ __forceinline__ int64_t div_nn(int64_t a, int64_t b) {
+  if (((static_cast<uint64_t>(a) | static_cast<uint64_t>(b)) >> 32) == 0)
+    return static_cast<int64_t>(static_cast<uint32_t>(a) / static_cast<uint32_t>(b));
+  return a / b;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp_f32<kDppXor1>(x));
   x = fmaxf(x, dpp_f32<kDppXor2>(x));

@@ -806,8 +806,8 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
   // this wave's run of partitions
   const int64_t total_parts = static_cast<int64_t>(Hkv) * cp(a.n_seqs);
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * kSkWaves + wave;
-  const int64_t p_begin = wid * total_parts / a.n_waves;
-  const int64_t p_end = (wid + 1) * total_parts / a.n_waves;
+  const int64_t p_begin = div_nn(wid * total_parts, a.n_waves);
+  const int64_t p_end = div_nn((wid + 1) * total_parts, a.n_waves);
   if (p_begin >= p_end) return;
 
   // partition index -> (sequence, kv head, first block).  The sequence is the
@@ -826,8 +826,9 @@ attn_mfma_kernel(sk_args a, const int32_t* __restrict__ ctx_lens, const int32_t*
     c.seq = lo;
     const int np = cp(lo + 1) - cp(lo);
     const int64_t r = pp - static_cast<int64_t>(Hkv) * cp(lo);
-    c.kvh = static_cast<int>(r / np);
-    c.j = static_cast<int>(r % np) * a.part_blocks;
+    const int64_t h = div_nn(r, np);
+    c.kvh = static_cast<int>(h);
+    c.j = static_cast<int>(r - h * np) * a.part_blocks;
     c.nb = cb(lo + 1) - cb(lo);
     c.n = cn(lo);
     c.trow = a.table_rows ? a.table_rows[lo] : lo;
@@ -1175,8 +1176,8 @@ __global__ void __launch_bounds__(kMergeItems * 64) merge_sk_kernel(sk_args a) {
   const int64_t total = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[a.n_seqs];
   const int64_t W = a.n_waves;
   const int64_t first = static_cast<int64_t>(a.n_kv_heads) * a.cum_parts[seq] + static_cast<int64_t>(kvh) * np;
-  auto wave_of = [&](int64_t pp) { return ((pp + 1) * W - 1) / total; };
-  auto run_begin = [&](int64_t w) { return w * total / W; };
+  auto wave_of = [&](int64_t pp) { return div_nn((pp + 1) * W - 1, total); };
+  auto run_begin = [&](int64_t w) { return div_nn(w * total, W); };
   const int64_t wF = wave_of(first), wL = wave_of(first + np - 1);
   if (wF == wL) return;  // one wave wrote the final row
   const int n_w = static_cast<int>(wL - wF + 1);
